@@ -1,0 +1,270 @@
+"""CPU oracle for the Rotated Runtime Smooth (RRS) A4W4 linear layer.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it. It shares no code with the HIP
+path (``rotated_runtime_activation_amd``) and imports nothing from it.
+
+Plain, slow, obviously correct: NumPy in float64, steps in the order the pages
+give them, no blocking or fusion. Sources ("pages"):
+
+* [RRS-summary]  atlas.scime.ai summary of "Rotated Runtime Smooth:
+  Training-Free Activation Smoother for accurate INT4 inference",
+  paragraphs "Approach" and "Problem".
+* [RRS-rebuttal] paperhub.cn page of the same paper (authors' rebuttal):
+  "Novelty" answer (reorder + group-wise scales aligned with the GEMM),
+  "Description of the reorder process" answer (equation Y = X W^T as a sum of
+  per-channel outer products, invariant under a consistent channel reorder).
+* [RRS-groovesquid] groovesquid.com summary, medium-difficulty summary
+  (RS smooths with runtime maxima; the rotation narrows spike outliers).
+* [AGC-OR] paperpeel.com page of "Understanding LLM Quantization through
+  Activation-Guided Compensation and Orthogonal Residuals": Sec. 3.1 (output
+  preserving transform Z = XP, V = W P^-T; per-token quantiser Q_A), Sec. 3.2
+  (normalised Hadamard), App. B.1 (Delta_t = ||Z_t||_inf / q_A,
+  q_A = 2^(b-1) - 1), Sec. 5 "Quantization and calibration" (per-token
+  symmetric activations, per-output-channel symmetric weights).
+
+Readings taken where the pages are silent (numbered as in the design notes):
+R1 group scale = max over the group's channels of the per-channel max over
+tokens; R2 the max runs over all tokens of the call; R3/R4 Sylvester Hadamard
+in natural order, unnormalised, with the exact 1/K folded into the output;
+R5 rotate, then reorder, then smooth; R6 round half to even; R7 no clipping;
+R8 codes in [-7, 7]; R9 zero group -> scale 1, zero row -> codes 0 and scale 0;
+R10 nibble pack, low nibble first, two's complement; R11 weights RTN per output
+channel; R12 the group scale multiplies each group's integer partial.
+
+Every function below is pinned by ``tests/test_oracle_*.py`` against something
+other than itself (explicit Hadamard matrices, scipy's Hadamard, closed forms,
+a hand-worked example in ``tests/golden/``, int64 brute force, invariants).
+"""
+from __future__ import annotations
+
+from typing import Dict
+
+import numpy as np
+
+QMAX = 7  # q_A = 2^(4-1) - 1 for 4-bit symmetric codes ([AGC-OR] App. B.1)
+
+
+# ----------------------------------------------------------------- rotation
+def fwht(x: np.ndarray) -> np.ndarray:
+    """Unnormalised Sylvester Walsh-Hadamard transform along the last axis,
+    in float64: returns x @ H_n with H_n[i, j] = (-1)^popcount(i & j).
+
+    The rotation of [RRS-summary] "Approach" / [RRS-groovesquid]; normalised
+    form in [AGC-OR] Sec. 3.2 (the 1/sqrt(n) is applied by the callers as an
+    exact 1/n on the output, reading R3).
+
+    Exact for fp16 inputs: every fp16 value is an integer multiple of 2^-24
+    below 2^16 in magnitude, so every +-1 partial sum of n <= 2^13 of them is a
+    multiple of 2^-24 below 2^29 and fits float64's 53-bit significand; no
+    butterfly rounds.
+    """
+    y = np.array(x, dtype=np.float64, copy=True)
+    n = y.shape[-1]
+    if n & (n - 1):
+        raise ValueError("length must be a power of two")
+    lead = y.shape[:-1]
+    h = 1
+    while h < n:
+        y = y.reshape(lead + (n // (2 * h), 2, h))
+        a = y[..., 0, :]
+        b = y[..., 1, :]
+        y = np.stack((a + b, a - b), axis=-2)
+        h *= 2
+    return y.reshape(lead + (n,))
+
+
+# ------------------------------------------------------------------ reorder
+def calibrate_perm(x_cal: np.ndarray) -> np.ndarray:
+    """Fixed channel order from a calibration batch (reading R5/R15).
+
+    Rotate the calibration activations, take each channel's |max| over the
+    calibration tokens, and order channels by that max, largest first, ties
+    by lower channel index. perm[j] is the source channel of position j, so
+    outlier channels gather into the leading groups and normal channels into
+    the rest ([RRS-rebuttal] "Novelty": reorder to collect outliers and normal
+    values).
+    """
+    c = np.max(np.abs(fwht(x_cal)), axis=0)
+    return np.argsort(-c, kind="stable").astype(np.int32)
+
+
+def invert_perm(perm: np.ndarray) -> np.ndarray:
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(perm.size, dtype=perm.dtype)
+    return inv
+
+
+# ---------------------------------------------------------------- quantizer
+def rtn_codes(v: np.ndarray) -> np.ndarray:
+    """Round half to even, clamp to [-7, 7] (R6, R8)."""
+    return np.clip(np.rint(v), -QMAX, QMAX).astype(np.int8)
+
+
+def prepare_weights(W: np.ndarray, perm: np.ndarray) -> Dict[str, np.ndarray]:
+    """Offline weight side for Y = X W with W [K, N].
+
+    Output-preserving transform ([AGC-OR] Sec. 3.1): rotating the activations
+    by H is undone by H^T applied to the weights, and H is symmetric, so the
+    rotated weight is Wz = H W (each column transformed). The reorder applies
+    the same permutation to the weight rows ([RRS-rebuttal], reorder answer).
+    Each output channel is quantised symmetric per channel with
+    Delta_w = max|col| / 7 ([AGC-OR] Sec. 5; R11).
+
+    Returns qw int8 [N, K] (K in permuted order), a = max|Wp| per output
+    channel (float64 [N]), dw = a / 7, and the pre-rounding values uw [N, K].
+    """
+    W = np.asarray(W)
+    Wz_t = fwht(W.T)                    # [N, K]: row n is (H W)[:, n]
+    Wp_t = Wz_t[:, perm]                # Wp[j, n] = Wz[perm[j], n]
+    a = np.max(np.abs(Wp_t), axis=1)    # per output channel
+    safe = np.where(a > 0, a, 1.0)
+    uw = np.where(a[:, None] > 0, QMAX * Wp_t / safe[:, None], 0.0)
+    qw = rtn_codes(uw)
+    return {"qw": qw, "a": a, "dw": a / QMAX, "uw": uw, "Wp_t": Wp_t}
+
+
+def frontend(X: np.ndarray, perm: np.ndarray, G: int, *, rotate: bool = True,
+             smooth: bool = True) -> Dict[str, np.ndarray]:
+    """Activation side: rotate, reorder, runtime group-wise smoothing,
+    per-token symmetric INT4 ([RRS-summary] "Approach"; [RRS-rebuttal]
+    "Novelty"; [AGC-OR] Sec. 3.1 and App. B.1).
+
+    Steps, in the pages' order:
+      Z  = X H                                   (rotation)
+      Zp[:, j] = Z[:, perm[j]]                   (fixed reorder)
+      c_j = max_t |Zp[t, j]|                     (runtime channel max, R1/R2)
+      S_g = max_{j in group g} c_j, 0 -> 1       (group-wise scale, R9)
+      U  = Zp / S_g(j)                           (smoothing divide)
+      r_t = max_j |U[t, j]|; Delta_t = r_t / 7   (per-token scale)
+      v  = 7 U / r_t;  q = clamp(rne(v), -7, 7)  (codes; zero row -> 0)
+
+    ``rotate=False`` gives Runtime Smooth without rotation and
+    ``smooth=False`` gives rotation only (S = 1): the ablations of
+    [RRS-rebuttal] "Incomplete ablation study".
+    """
+    X = np.asarray(X)
+    M, K = X.shape
+    if K % G:
+        raise ValueError("G must divide K")
+    Z = fwht(X) if rotate else X.astype(np.float64)
+    Zp = Z[:, perm]
+    c = np.max(np.abs(Zp), axis=0) if M else np.zeros(K)
+    if smooth:
+        S = np.max(c.reshape(K // G, G), axis=1)
+        S = np.where(S > 0, S, 1.0)
+    else:
+        S = np.ones(K // G)
+    U = Zp / np.repeat(S, G)[None, :]
+    r = np.max(np.abs(U), axis=1) if K else np.zeros(M)
+    safe = np.where(r > 0, r, 1.0)
+    v = np.where(r[:, None] > 0, QMAX * U / safe[:, None], 0.0)
+    q = rtn_codes(v)
+    return {"Z": Z, "Zp": Zp, "c": c, "S": S, "U": U, "r": r, "dx": r / QMAX,
+            "v": v, "q": q}
+
+
+# --------------------------------------------------------------------- GEMM
+def group_partials(q: np.ndarray, qw: np.ndarray, G: int) -> np.ndarray:
+    """Exact per-group integer partials P[t, n, g] = sum_{j in g} q[t,j] qw[n,j].
+
+    Computed as float64 matmuls on integer-valued operands: every partial sum
+    is an integer of magnitude <= 49 * G < 2^53, so the result is exact in any
+    summation order. Pinned against an int64 brute force in the tests.
+    """
+    M, K = q.shape
+    N = qw.shape[0]
+    ng = K // G
+    qa = q.astype(np.float64).reshape(M, ng, G)
+    qb = qw.astype(np.float64).reshape(N, ng, G)
+    P = np.empty((M, N, ng), dtype=np.int64)
+    for g in range(ng):
+        P[:, :, g] = np.rint(qa[:, g, :] @ qb[:, g, :].T).astype(np.int64)
+    return P
+
+
+def group_partials_int64(q: np.ndarray, qw: np.ndarray, G: int) -> np.ndarray:
+    """Brute-force int64 version of ``group_partials`` (small inputs)."""
+    M, K = q.shape
+    N = qw.shape[0]
+    P = np.zeros((M, N, K // G), dtype=np.int64)
+    for t in range(M):
+        for n in range(N):
+            prod = q[t].astype(np.int64) * qw[n].astype(np.int64)
+            P[t, n] = prod.reshape(K // G, G).sum(axis=1)
+    return P
+
+
+def linear_out(q: np.ndarray, dx: np.ndarray, S: np.ndarray, qw: np.ndarray,
+               dw: np.ndarray, G: int) -> Dict[str, np.ndarray]:
+    """Output of the A4W4 GEMM with group rescale (reading R12):
+
+      Y[t, n] = (1/K) * dx_t * dw_n * sum_g S_g * P[t, n, g]
+
+    (1/K is the product of the two 1/sqrt(K) normalisations of H, R3.)
+    Also returns the cancellation-free magnitude
+      C[t, n] = (1/K) * |dx_t| * |dw_n| * sum_g S_g * |P[t, n, g]|
+    used by the output tolerance (R13). Accumulates over groups without
+    materialising P for all groups at once.
+    """
+    M, K = q.shape
+    N = qw.shape[0]
+    ng = K // G
+    qa = q.astype(np.float64).reshape(M, ng, G)
+    qb = qw.astype(np.float64).reshape(N, ng, G)
+    acc = np.zeros((M, N))
+    mag = np.zeros((M, N))
+    for g in range(ng):
+        P = qa[:, g, :] @ qb[:, g, :].T   # exact integers
+        acc += S[g] * P
+        mag += S[g] * np.abs(P)
+    scale = (dx[:, None] * dw[None, :]) / K
+    return {"Y": scale * acc, "C": np.abs(scale) * mag}
+
+
+def rrs_linear(X: np.ndarray, W: np.ndarray, perm: np.ndarray, G: int) -> Dict[str, np.ndarray]:
+    """The whole RRS A4W4 linear: weights prepared offline, then the runtime
+    front end and the grouped integer GEMM."""
+    wp = prepare_weights(W, perm)
+    fe = frontend(X, perm, G)
+    out = linear_out(fe["q"], fe["dx"], fe["S"], wp["qw"], wp["dw"], G)
+    return {"fe": fe, "wp": wp, **out}
+
+
+# ----------------------------------------------------------------- packing
+def pack_codes(q: np.ndarray) -> np.ndarray:
+    """Nibble pack along the last axis (reading R10): byte i holds code 2i in
+    its low nibble and code 2i+1 in its high nibble, two's complement."""
+    q = np.asarray(q).astype(np.int16)
+    lo = q[..., 0::2] & 0xF
+    hi = q[..., 1::2] & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_codes(b: np.ndarray) -> np.ndarray:
+    b = np.asarray(b).astype(np.int16)
+    lo = b & 0xF
+    hi = (b >> 4) & 0xF
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+# ---------------------------------------------------------- parity helpers
+def near_half(v: np.ndarray, window: float = 1e-5) -> np.ndarray:
+    """Codes whose pre-rounding value lies within ``window`` of a .5 boundary:
+    either neighbouring integer is an acceptable code there."""
+    a = np.abs(v)
+    return np.abs(a - (np.floor(a) + 0.5)) < window
+
+
+def scale_match_u(t: np.ndarray) -> np.ndarray:
+    """u = max|t| / RMS(t) along the last axis: equals 1 when a row is
+    perfectly flat ([RRS-rebuttal] "Experimental support for claims (W4)")."""
+    t = np.asarray(t, dtype=np.float64)
+    rms = np.sqrt(np.mean(t * t, axis=-1))
+    return np.max(np.abs(t), axis=-1) / np.where(rms > 0, rms, 1.0)

@@ -1,0 +1,252 @@
+"""Pins of the CPU oracle against the pages' definitions, closed forms,
+invariants, a hand-worked example and brute force (CPU only)."""
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+import workloads
+from tests import pins
+
+
+# ------------------------------------------------------------------ FWHT
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 64, 256, 1024])
+def test_hadamard_orthogonality(n):
+    H = pins.hadamard_popcount(n)
+    assert np.array_equal(H @ H.T, n * np.eye(n))
+
+
+@pytest.mark.parametrize("n", [2, 8, 64, 512])
+def test_popcount_matrix_is_scipy_sylvester(n):
+    assert np.array_equal(pins.hadamard_popcount(n), scipy.linalg.hadamard(n))
+
+
+def test_fwht_bit_exact_vs_explicit_matmul():
+    assert pins.fwht_matches_explicit(oracle.fwht)
+
+
+def test_fwht_unit_vectors():
+    assert pins.fwht_unit_vectors(oracle.fwht)
+
+
+@pytest.mark.parametrize("n", [4096, 8192])
+def test_fwht_sampled_columns_large(n):
+    g = np.random.default_rng(n)
+    x = (g.standard_normal((3, n)) * np.where(g.random(n) < 0.01, 300, 1)).astype(np.float16)
+    z = oracle.fwht(x)
+    for j in g.choice(n, size=6, replace=False):
+        col = pins.hadamard_column(n, int(j))
+        assert np.array_equal(z[:, j], x.astype(np.float64) @ col)
+
+
+def test_fwht_involution_and_parseval():
+    g = np.random.default_rng(3)
+    x = g.standard_normal((4, 2048)).astype(np.float16).astype(np.float64)
+    z = oracle.fwht(x)
+    assert np.array_equal(oracle.fwht(z), 2048 * x)
+    assert np.allclose((z * z).sum(1), 2048 * (x * x).sum(1), rtol=1e-13)
+
+
+def test_fwht_rejects_non_power_of_two():
+    with pytest.raises(ValueError):
+        oracle.fwht(np.ones((2, 12)))
+
+
+# -------------------------------------------------------------- front end
+def test_frontend_golden():
+    assert pins.frontend_matches_golden(oracle.frontend)
+
+
+def test_weights_golden():
+    assert pins.weights_match_golden(oracle.prepare_weights)
+
+
+def test_gemm_golden():
+    assert pins.gemm_matches_golden(oracle.group_partials, oracle.linear_out)
+
+
+def test_pack_golden_and_roundtrip():
+    assert pins.pack_matches_golden(oracle.pack_codes)
+    q = np.random.default_rng(0).integers(-7, 8, size=(5, 64)).astype(np.int8)
+    assert np.array_equal(oracle.unpack_codes(oracle.pack_codes(q)), q)
+
+
+def test_unrounded_output_equals_xw():
+    assert pins.unrounded_output_is_xw(oracle.frontend, oracle.prepare_weights, oracle.linear_out)
+
+
+def _case(seed=5, M=40, K=512, G=64):
+    wl = workloads.WORKLOADS["tiny"]
+    x, xc, w = workloads.random_case(seed, M, K, 16)
+    perm = oracle.calibrate_perm(xc)
+    return x, perm, G
+
+
+def test_invariants_I1_I2_I3_I4():
+    x, perm, G = _case()
+    fe = oracle.frontend(x, perm, G)
+    U, r, q, S = fe["U"], fe["r"], fe["q"], fe["S"]
+    K = x.shape[1]
+    # I1: every group reaches |U| == 1 exactly (x / x == 1 in IEEE).
+    Ug = np.abs(U).reshape(U.shape[0], K // G, G)
+    assert np.all(Ug.max(axis=(0, 2)) == 1.0)
+    # I2: smoothing bounds every entry by 1.
+    assert np.abs(U).max() <= 1.0
+    # I3: each nonzero row has a +-7 code at its |U| argmax.
+    am = np.argmax(np.abs(U), axis=1)
+    assert np.all(np.abs(q[np.arange(len(q)), am]) == 7)
+    # I4: RTN error at most half a step.
+    err = np.abs(U - (r[:, None] / 7) * q)
+    assert np.all(err <= r[:, None] / 14 * (1 + 1e-12))
+
+
+def test_I5_single_group_is_per_token_rtn():
+    """G = K: S is one scalar, so the codes are plain per-token symmetric RTN
+    of the rotated, reordered row ([AGC-OR] Sec. 3.1 quantiser)."""
+    x, perm, _ = _case()
+    K = x.shape[1]
+    fe = oracle.frontend(x, perm, K)
+    Zp = pins.hadamard_popcount(K)
+    Zp = (x.astype(np.float64) @ Zp)[:, perm]
+    delta = np.abs(Zp).max(axis=1) / 7
+    ref = np.clip(np.rint(Zp / delta[:, None]), -7, 7)
+    # the two formulas differ by float64 rounding of the divide chain; compare
+    # away from .5 boundaries
+    ok = ~oracle.near_half(fe["v"], 1e-9)
+    assert np.array_equal(fe["q"][ok], ref[ok])
+
+
+def test_I6_single_token():
+    x, perm, G = _case(M=1)
+    fe = oracle.frontend(x[:1], perm, G)
+    assert fe["r"][0] == 1.0
+
+
+def test_unsmoothing_roundtrip_exact_for_power_of_two_scales():
+    # Group maxima that are powers of two make U * S == Zp exact (the
+    # rotation is switched off so the smoothed values are chosen directly).
+    K, G = 64, 16
+    g = np.random.default_rng(9)
+    X = g.integers(-31, 32, size=(6, K)).astype(np.float64) / 64.0
+    X[0, ::G] = [1.0, 2.0, 0.5, 4.0]   # one power-of-two maximum per group
+    X = X.astype(np.float16)
+    perm = np.arange(K, dtype=np.int32)
+    fe = oracle.frontend(X, perm, G, rotate=False)
+    assert np.array_equal(fe["S"], [1.0, 2.0, 0.5, 4.0])
+    assert np.array_equal(fe["U"] * np.repeat(fe["S"], G), fe["Zp"])
+
+
+def test_unsmoothing_roundtrip_one_ulp_general():
+    x, perm, G = _case(seed=11)
+    fe = oracle.frontend(x, perm, G)
+    back = fe["U"] * np.repeat(fe["S"], G)
+    assert np.all(np.abs(back - fe["Zp"]) <= np.spacing(np.abs(fe["Zp"])) + 0)
+
+
+def test_reorder_identity():
+    """sum_j Zp[:, j] Wp[j, :] / K == X W  ([RRS-rebuttal] reorder answer)."""
+    g = np.random.default_rng(2)
+    K, N = 256, 10
+    x = g.standard_normal((7, K)).astype(np.float16)
+    W = (g.standard_normal((K, N)) * 0.02).astype(np.float16)
+    perm = g.permutation(K).astype(np.int32)
+    Zp = oracle.fwht(x)[:, perm]
+    Wp_t = oracle.prepare_weights(W, perm)["Wp_t"]
+    lhs = Zp @ Wp_t.T / K
+    assert np.allclose(lhs, x.astype(np.float64) @ W.astype(np.float64), rtol=1e-12, atol=1e-15)
+
+
+def test_zero_row_and_zero_group_guards():
+    K, G = 128, 32
+    x = np.zeros((3, K), dtype=np.float16)
+    x[1, 5] = 2.0
+    perm = np.arange(K, dtype=np.int32)
+    fe = oracle.frontend(x, perm, G, rotate=False)
+    # groups 1..3 are all zero over all tokens -> scale 1 (R9)
+    assert np.array_equal(fe["S"], [2.0, 1.0, 1.0, 1.0])
+    assert fe["r"][0] == 0 and fe["dx"][0] == 0 and not fe["q"][0].any()
+    assert fe["q"][1, 5] == 7
+
+
+def test_ablation_switches():
+    x, perm, G = _case()
+    fe = oracle.frontend(x, perm, G, rotate=False)
+    assert np.array_equal(fe["Z"], x.astype(np.float64))
+    fe = oracle.frontend(x, perm, G, smooth=False)
+    assert np.all(fe["S"] == 1.0)
+
+
+def test_calibrate_perm_order_brute_force():
+    g = np.random.default_rng(4)
+    K = 32
+    xc = g.integers(-3, 4, size=(6, K)).astype(np.float16)   # many ties
+    perm = oracle.calibrate_perm(xc)
+    c = np.abs(xc.astype(np.float64) @ pins.hadamard_popcount(K)).max(axis=0)
+    ref = sorted(range(K), key=lambda k: (-c[k], k))
+    assert list(perm) == ref
+
+
+def test_weights_per_channel_properties():
+    g = np.random.default_rng(6)
+    K, N = 256, 9
+    W = (g.standard_normal((K, N)) * 0.02).astype(np.float16)
+    W[:, 3] = 0
+    perm = g.permutation(K).astype(np.int32)
+    wp = oracle.prepare_weights(W, perm)
+    qw = wp["qw"]
+    assert not qw[3].any() and wp["dw"][3] == 0
+    nz = [n for n in range(N) if n != 3]
+    assert np.all(np.abs(qw[nz]).max(axis=1) == 7)
+    assert np.all(np.abs(qw) <= 7)
+
+
+# ------------------------------------------------------------------- GEMM
+def test_partials_vs_int64_brute_force():
+    g = np.random.default_rng(7)
+    for (M, N, K, G) in [(5, 7, 64, 32), (3, 4, 256, 128), (2, 3, 128, 128)]:
+        q = g.integers(-7, 8, size=(M, K)).astype(np.int8)
+        qw = g.integers(-7, 8, size=(N, K)).astype(np.int8)
+        q[0] = 7
+        qw[0] = -7     # extreme partials
+        P = oracle.group_partials(q, qw, G)
+        assert np.array_equal(P, oracle.group_partials_int64(q, qw, G))
+        assert np.abs(P).max() <= 49 * G
+        assert P[0, 0, 0] == -49 * G
+
+
+def test_output_magnitude_bounds_output():
+    g = np.random.default_rng(8)
+    q = g.integers(-7, 8, size=(4, 128)).astype(np.int8)
+    qw = g.integers(-7, 8, size=(5, 128)).astype(np.int8)
+    out = oracle.linear_out(q, g.random(4), g.random(2) + 0.5, qw, g.random(5), 64)
+    assert np.all(np.abs(out["Y"]) <= out["C"] * (1 + 1e-12))
+
+
+def test_quantisation_error_is_bounded_and_rrs_beats_rs_on_spikes():
+    """Non-gating context check of the pages' qualitative claim: on spiky
+    synthetic activations, rotation + runtime smooth at G=128 has lower output
+    error than runtime smooth without rotation ([RRS-summary] "Surprising
+    findings"; reported, asserted only as an ordering)."""
+    wl = workloads.WORKLOADS["tiny"]
+    x = workloads.runtime_x(wl)
+    w = workloads.weights(wl)
+    perm = oracle.calibrate_perm(workloads.calib_x(wl))
+    ref = x.astype(np.float64) @ w.astype(np.float64)
+    res = oracle.rrs_linear(x, w, perm, 128)
+    err_rrs = np.linalg.norm(res["Y"] - ref) / np.linalg.norm(ref)
+    # RS without rotation: identity "rotation" on both sides.
+    fe = oracle.frontend(x, perm, 128, rotate=False)
+    Wp = w.astype(np.float64).T[:, perm]
+    a = np.abs(Wp).max(axis=1)
+    qw = oracle.rtn_codes(7 * Wp / a[:, None])
+    y_rs = oracle.linear_out(fe["q"], fe["dx"], fe["S"], qw, a / 7, 128)["Y"] * x.shape[1]
+    err_rs = np.linalg.norm(y_rs - ref) / np.linalg.norm(ref)
+    assert err_rrs < 0.2
+    assert err_rrs < err_rs
+
+
+def test_scale_match_statistic():
+    assert oracle.scale_match_u(np.ones(16)) == 1.0
+    t = np.zeros(16)
+    t[0] = 4.0
+    assert oracle.scale_match_u(t) == 4.0

@@ -1,0 +1,107 @@
+"""Planted mistakes in the oracle (CPU only): each plausible slip must make at
+least one pin fail, so the pins are shown to be sensitive to it."""
+import numpy as np
+
+import oracle
+from oracle import rrs_ref
+from tests import pins
+
+
+def _fwht_wrong_sign(x):
+    y = np.array(x, dtype=np.float64, copy=True)
+    n = y.shape[-1]
+    lead = y.shape[:-1]
+    h = 1
+    while h < n:
+        y = y.reshape(lead + (n // (2 * h), 2, h))
+        a, b = y[..., 0, :], y[..., 1, :]
+        y = np.stack((a + b, b - a), axis=-2)        # slip: b - a
+        h *= 2
+    return y.reshape(lead + (n,))
+
+
+def _fwht_bit_reversed(x):
+    # a valid Hadamard-type transform, but outputs in bit-reversed order
+    z = oracle.fwht(x)
+    n = z.shape[-1]
+    bits = n.bit_length() - 1
+    idx = [int(format(i, f"0{bits}b")[::-1], 2) if bits else 0 for i in range(n)]
+    return z[..., idx]
+
+
+def test_fwht_mutants_fail():
+    assert not pins.fwht_matches_explicit(_fwht_wrong_sign)
+    assert not pins.fwht_unit_vectors(_fwht_wrong_sign)
+    # bit-reversal keeps e_0 -> ones but fails the explicit matrix check
+    assert not pins.fwht_matches_explicit(_fwht_bit_reversed)
+
+
+def _with(monkeypatch, name, fn):
+    monkeypatch.setattr(rrs_ref, name, fn)
+
+
+def test_inverse_perm_mutant_fails():
+    def frontend_inv(X, perm, G, **kw):
+        return rrs_ref.frontend.__wrapped__(X, oracle.invert_perm(perm), G, **kw)
+    rrs_ref.frontend.__wrapped__ = rrs_ref.frontend
+    try:
+        assert not pins.frontend_matches_golden(frontend_inv)
+    finally:
+        del rrs_ref.frontend.__wrapped__
+
+
+def test_round_half_away_mutant_fails(monkeypatch):
+    _with(monkeypatch, "rtn_codes",
+          lambda v: np.clip(np.sign(v) * np.floor(np.abs(v) + 0.5), -7, 7).astype(np.int8))
+    assert not pins.frontend_matches_golden(rrs_ref.frontend)
+
+
+def test_mean_instead_of_max_group_scale_fails():
+    def frontend_mean(X, perm, G, **kw):
+        fe = oracle.frontend(X, perm, G, **kw)
+        K = X.shape[1]
+        S = fe["c"].reshape(K // G, G).mean(axis=1)
+        U = fe["Zp"] / np.repeat(S, G)
+        r = np.abs(U).max(axis=1)
+        v = 7 * U / r[:, None]
+        return {**fe, "S": S, "U": U, "r": r, "dx": r / 7, "v": v, "q": oracle.rtn_codes(v)}
+    # the golden case has constant groups (mean == max); the invariants catch it
+    assert pins.frontend_invariants(oracle.frontend)
+    assert not pins.frontend_invariants(frontend_mean)
+
+
+def test_dropped_output_scale_fails():
+    def linear_out_no_invK(q, dx, S, qw, dw, G):
+        out = oracle.linear_out(q, dx, S, qw, dw, G)
+        return {"Y": out["Y"] * q.shape[1], "C": out["C"]}
+    assert not pins.unrounded_output_is_xw(oracle.frontend, oracle.prepare_weights, linear_out_no_invK)
+    assert not pins.gemm_matches_golden(oracle.group_partials, linear_out_no_invK)
+
+
+def test_weight_scale_not_divided_by_7_fails():
+    def prep_bad(W, perm):
+        wp = oracle.prepare_weights(W, perm)
+        return {**wp, "dw": wp["a"]}
+    assert not pins.weights_match_golden(prep_bad)
+    assert not pins.unrounded_output_is_xw(oracle.frontend, prep_bad, oracle.linear_out)
+
+
+def test_weight_rows_not_reordered_fails():
+    def prep_noperm(W, perm):
+        return oracle.prepare_weights(W, np.arange(len(perm), dtype=np.int32))
+    assert not pins.weights_match_golden(prep_noperm)
+    assert not pins.unrounded_output_is_xw(oracle.frontend, prep_noperm, oracle.linear_out)
+
+
+def test_transposed_partials_fail():
+    def partials_t(q, qw, G):
+        P = oracle.group_partials(q, qw, G)
+        return P[:, :, ::-1]                    # groups in the wrong order
+    assert not pins.gemm_matches_golden(partials_t, oracle.linear_out)
+
+
+def test_swapped_nibbles_fail():
+    def pack_swapped(q):
+        q = np.asarray(q).astype(np.int16)
+        return ((q[..., 1::2] & 0xF) | ((q[..., 0::2] & 0xF) << 4)).astype(np.uint8)
+    assert not pins.pack_matches_golden(pack_swapped)

@@ -1,0 +1,142 @@
+"""Seeded synthetic workloads for the RRS A4W4 linear layer.
+
+This module only draws random numbers and lays them out; it holds none of the
+method's arithmetic (no rotation, no smoothing, no quantisation). Both the CPU
+oracle (``oracle/``) and the HIP path draw their inputs from here, so that the
+two sides see the same bits.
+
+The recipes mirror the two outlier kinds the Rotated Runtime Smooth pages
+describe: channel-wise outliers (a few channels that are large for every
+token) and spike outliers (isolated huge entries) -- see the RRS summary page
+(atlas.scime.ai), "Problem" paragraph, and the RRS rebuttal page
+(paperhub.cn), the answer on Figure 1 (c). The pages evaluate on WikiText-2
+and common-sense QA activations of LLaMA/Qwen/Mistral models; no dataset or
+checkpoint is available here, so these seeded inputs stand in for them.
+
+Seeds: ``seed = 1000 * cfg_index + role`` with role 0 = outlier-channel
+choice, 1 = calibration batch, 2 = runtime activations, 3 = weights, and
+``numpy.random.Generator(PCG64(seed))`` as the generator.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+ROLE_OUTLIER_CHANNELS = 0
+ROLE_CALIB = 1
+ROLE_X = 2
+ROLE_W = 3
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """Shape and outlier recipe of one synthetic RRS linear workload."""
+
+    index: int            # config index, used in the seeds
+    name: str
+    M: int                # tokens
+    K: int                # input channels (power of two; Hadamard size)
+    N: int                # output channels
+    G: Tuple[int, ...]    # smoothing group size(s)
+    n_outlier_ch: int     # channel-wise outliers
+    outlier_factor: float
+    spike_mode: str       # "count" | "fraction" | "per_token"
+    spike_param: float    # count, fraction of entries, or spikes per token
+    spike_value: float
+    w_std: float
+    calib_tokens: int
+
+    @property
+    def seed_base(self) -> int:
+        return 1000 * self.index
+
+
+# The five configurations: tiny correctness case, LLaMA-3-8B o_proj prefill,
+# gate||up prefill, weight-bandwidth-bound decode, Mistral-like G sweep.
+WORKLOADS: Dict[str, Workload] = {
+    "tiny": Workload(0, "tiny", 16, 256, 256, (128,), 4, 30.0, "count", 3, 300.0, 0.02, 128),
+    "o_proj": Workload(1, "o_proj", 2048, 4096, 4096, (128,), 16, 20.0, "fraction", 1e-4, 500.0, 0.02, 512),
+    "gate_up": Workload(2, "gate_up", 4096, 4096, 28672, (128,), 16, 20.0, "fraction", 1e-4, 500.0, 0.02, 512),
+    "decode": Workload(3, "decode", 64, 8192, 8192, (128,), 32, 20.0, "per_token", 2, 500.0, 0.015, 512),
+    "g_sweep": Workload(4, "g_sweep", 4096, 4096, 14336, (32, 128, 512), 16, 20.0, "fraction", 1e-4, 500.0, 0.02, 512),
+}
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def outlier_channels(wl: Workload) -> np.ndarray:
+    """Sorted indices of the channel-wise outlier channels (shared by the
+    calibration batch and the runtime batch)."""
+    g = rng(wl.seed_base + ROLE_OUTLIER_CHANNELS)
+    return np.sort(g.choice(wl.K, size=wl.n_outlier_ch, replace=False))
+
+
+def make_activations(wl: Workload, tokens: int, seed: int,
+                     channels: Optional[np.ndarray] = None) -> np.ndarray:
+    """fp16 activations [tokens, K]: N(0,1) drawn in fp64, outlier columns
+    multiplied by ``outlier_factor``, spike entries overwritten with
+    +-``spike_value`` (random sign), then cast to fp16."""
+    g = rng(seed)
+    K = wl.K
+    x = g.standard_normal((tokens, K))
+    ch = outlier_channels(wl) if channels is None else channels
+    x[:, ch] *= wl.outlier_factor
+    if wl.spike_mode == "count":
+        n = int(wl.spike_param)
+        flat = g.choice(tokens * K, size=min(n, tokens * K), replace=False)
+        rows, cols = np.divmod(flat, K)
+    elif wl.spike_mode == "fraction":
+        n = int(round(wl.spike_param * tokens * K))
+        flat = g.choice(tokens * K, size=n, replace=False)
+        rows, cols = np.divmod(flat, K)
+    elif wl.spike_mode == "per_token":
+        per = int(wl.spike_param)
+        rows = np.repeat(np.arange(tokens), per)
+        cols = np.concatenate([g.choice(K, size=per, replace=False) for _ in range(tokens)])
+    else:  # pragma: no cover - recipe table above is closed
+        raise ValueError(wl.spike_mode)
+    signs = np.where(g.random(len(rows)) < 0.5, -1.0, 1.0)
+    x[rows, cols] = signs * wl.spike_value
+    return x.astype(np.float16)
+
+
+def runtime_x(wl: Workload, tokens: Optional[int] = None) -> np.ndarray:
+    return make_activations(wl, wl.M if tokens is None else tokens, wl.seed_base + ROLE_X)
+
+
+def calib_x(wl: Workload) -> np.ndarray:
+    return make_activations(wl, wl.calib_tokens, wl.seed_base + ROLE_CALIB)
+
+
+def weights(wl: Workload, N: Optional[int] = None) -> np.ndarray:
+    """fp16 weights [K, N] ~ N(0, w_std) (drawn in fp32 to bound memory on
+    the widest configuration, then cast)."""
+    g = rng(wl.seed_base + ROLE_W)
+    n = wl.N if N is None else N
+    w = g.standard_normal((wl.K, n), dtype=np.float32)
+    w *= np.float32(wl.w_std)
+    return w.astype(np.float16)
+
+
+def random_case(seed: int, M: int, K: int, N: int, *, n_outlier_ch: int = 4,
+                outlier_factor: float = 20.0, n_spikes: int = 3,
+                spike_value: float = 500.0, w_std: float = 0.02):
+    """Small random case (for parity sweeps over odd shapes): returns
+    (X fp16 [M,K], X_cal fp16 [max(M,32),K], W fp16 [K,N])."""
+    wl = Workload(10_000 + seed, "random", M, K, N, (K,), min(n_outlier_ch, K),
+                  outlier_factor, "count", n_spikes, spike_value, w_std, max(M, 32))
+    x = make_activations(wl, M, wl.seed_base + ROLE_X)
+    xc = make_activations(wl, wl.calib_tokens, wl.seed_base + ROLE_CALIB)
+    w = weights(wl)
+    return x, xc, w
+
+
+def shuffled_perm(K: int, seed: int) -> np.ndarray:
+    """A seeded random permutation of range(K) (int32). Any permutation is a
+    valid reorder input; this one exercises the gather independently of any
+    calibration statistic."""
+    return rng(seed).permutation(K).astype(np.int32)
