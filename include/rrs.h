@@ -1,0 +1,146 @@
+/*
+ * rrs.h -- C ABI of the MI355X (gfx950) Rotated Runtime Smooth A4W4 linear.
+ *
+ * The layer computes Y = X W for fp16 activations X [M, K] and fp16 weights
+ * W [K, N] through the Rotated Runtime Smooth (RRS) recipe:
+ *
+ *   1. rotate every activation row by the Sylvester Hadamard matrix H_K
+ *      (RRS summary page, atlas.scime.ai, "Approach"; normalised Hadamard in
+ *      the AGC-OR page, paperpeel.com, Sec. 3.2);
+ *   2. reorder the channels by a fixed permutation and divide each group of
+ *      G reordered channels by its runtime maximum over the call's tokens
+ *      (RRS rebuttal page, paperhub.cn, "Novelty" answer and the reorder
+ *      answer Y = X W^T = sum_i X_i W_i^T);
+ *   3. quantise each token to symmetric 4-bit codes in [-7, 7] with scale
+ *      max|row| / 7 (AGC-OR page, Sec. 3.1 and App. B.1, q_A = 2^(b-1) - 1)
+ *      and pack two codes per byte;
+ *   4. multiply against offline rotated, reordered, per-output-channel 4-bit
+ *      weights, rescaling each K-group's integer partial sum by its group
+ *      scale before fp32 accumulation.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All data pointers are DEVICE pointers (hipMalloc / torch CUDA tensors)
+ *   unless stated otherwise. The caller allocates and owns every buffer; the
+ *   library never allocates, frees or synchronises, and keeps no global
+ *   mutable state.
+ * - Every call is asynchronous on the given stream `s` (0 = null stream).
+ * - Arguments are validated on the host before any launch; a failing check
+ *   returns RRS_EINVAL (or RRS_EUNSUPPORTED for legal but unbuilt shapes) and
+ *   launches nothing. A failed launch returns RRS_EHIP.
+ * - Shapes: K is a power of two with 64 <= K <= 8192; G is a power of two
+ *   with 32 <= G <= K (so G divides K); M >= 1, N >= 1 (M = 0 is accepted by
+ *   the entry points that take M and is a no-op).
+ * - Layouts: X fp16 [M, K] row-major; W fp16 [K, N] row-major (the
+ *   transpose of nn.Linear.weight); Y fp32 [M, N] row-major.
+ * - Packed codes: byte i of a row holds code 2i in its low nibble and code
+ *   2i+1 in its high nibble, two's complement; K runs in reordered order.
+ * - Scales are reported in the unnormalised-Hadamard convention:
+ *     dx[t] = r_t / 7 with r_t = max_j |Zp[t,j] / S_g(j)|,
+ *     S[g]  = max over tokens and the group's channels of |Zp|,
+ *     dw[n] = max_j |Wp[j,n]| / 7,
+ *   so that Y[t,n] = (1/K) dx[t] dw[n] sum_g S[g] P_g[t,n].
+ * - `perm` (int32 [K], device) must be a permutation of 0..K-1 (not checked
+ *   on the device): position j of the reordered row takes rotated channel
+ *   perm[j].
+ * - Non-finite inputs are outside the contract.
+ */
+#ifndef RRS_H_
+#define RRS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RRS_OK = 0,
+  RRS_EINVAL = -1,       /* bad argument (shape, null pointer, short buffer) */
+  RRS_EUNSUPPORTED = -2, /* legal request this build does not serve */
+  RRS_EHIP = -3          /* a HIP launch or runtime call failed */
+} rrs_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* rrs_status_string(int status);
+
+/* Library version string, e.g. "rrs-gfx950 1.0". */
+const char* rrs_version(void);
+
+/* Bytes of the opaque prepared-weight buffer for a [K, N] weight: the packed
+ * codes wq [N][K/2] followed (256-byte aligned) by dw fp32 [N]. Returns 0 for
+ * an invalid shape. */
+size_t rrs_weight_bytes(int K, int N);
+
+/* Bytes of the workspace that rrs_linear needs for M tokens: a small
+ * synchronisation block, then xq [M][K/2], dx [M] and S [K/G], each 256-byte
+ * aligned. rrs_frontend needs only rrs_sync_bytes(K, G) of it. Returns 0 for
+ * an invalid shape. */
+size_t rrs_workspace_bytes(int M, int K, int G);
+size_t rrs_sync_bytes(int K, int G);
+
+/* Zero the synchronisation block at the start of `ws` (a fill kernel on `s`;
+ * no hipMemset, so it is safe under stream capture). Call once for a fresh
+ * workspace before its first use; every later call leaves the block zeroed.
+ * Two calls that share one workspace must not overlap in time. */
+int rrs_workspace_init(void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Calibration reorder (RRS rebuttal page, "Novelty": reorder collects outlier
+ * and normal channels). Rotates the T calibration rows X_cal fp16 [T, K],
+ * takes each channel's |max| over them and writes perm int32 [K] = channels
+ * sorted by that max, largest first, ties by lower channel index.
+ * `ws` needs rrs_calibrate_workspace_bytes(K) bytes; it need not be zeroed. */
+size_t rrs_calibrate_workspace_bytes(int K);
+int rrs_calibrate_perm(const void* X_cal_fp16, int T, int K, int32_t* perm,
+                       void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Offline weight preparation (output-preserving transform of the AGC-OR page,
+ * Sec. 3.1; reorder answer of the RRS rebuttal page; per-output-channel
+ * symmetric 4-bit weights, AGC-OR Sec. 5): Wz = H_K W, rows reordered by
+ * perm, each output channel quantised with dw[n] = max|col|/7, codes
+ * rne(7 Wp/max|col|). Writes the opaque buffer `wq` (rrs_weight_bytes(K, N)
+ * bytes). Independent of G: one buffer serves every group size. */
+int rrs_prepare_weights(const void* W_fp16, int K, int N, const int32_t* perm,
+                        void* wq, hipStream_t s);
+
+/* The RRS A4W4 linear layer: Y fp32 [M, N] = RRS(X) against prepared weights.
+ * `ws` holds rrs_workspace_bytes(M, K, G) bytes, initialised once with
+ * rrs_workspace_init. Y is fully overwritten. Runs the front end (rotation,
+ * reorder, runtime group smoothing, per-token quantise and pack) and the
+ * grouped integer GEMM on `s`. */
+int rrs_linear(const void* X_fp16, int M, int K, int N, int G,
+               const int32_t* perm, const void* wq, float* Y, void* ws,
+               size_t ws_bytes, hipStream_t s);
+
+/* Front end alone (same kernels as rrs_linear): writes xq uint8 [M][K/2],
+ * dx fp32 [M] and S fp32 [K/G] (zero groups reported as 1). `ws` holds at
+ * least rrs_sync_bytes(K, G) bytes, initialised once with
+ * rrs_workspace_init. `flags` selects the ablations of the RRS rebuttal page
+ * ("Incomplete ablation study"): RRS_FLAG_NO_ROTATE skips the rotation
+ * (Runtime Smooth alone), RRS_FLAG_NO_SMOOTH forces S = 1 (rotation alone);
+ * 0 is the full method. */
+#define RRS_FLAG_NO_ROTATE 1
+#define RRS_FLAG_NO_SMOOTH 2
+int rrs_frontend(const void* X_fp16, int M, int K, int G, const int32_t* perm,
+                 uint8_t* xq, float* dx, float* S, void* ws, size_t ws_bytes,
+                 int flags, hipStream_t s);
+
+/* Grouped integer GEMM alone (same kernel as rrs_linear): Y = (1/K) dx dw
+ * sum_g S_g P_g with P_g the int32 group partials of the 4-bit codes. */
+int rrs_gemm(const uint8_t* xq, const float* dx, const float* S, int M, int K,
+             int N, int G, const void* wq, float* Y, hipStream_t s);
+
+/* The int32 group partials P[t-m0][n-n0][g] = sum_{j in group g} q[t,j]
+ * qw[n,j] for m0 <= t < m1, n0 <= n < n1, computed by the same main loop as
+ * rrs_gemm (for exactness checks). P is int32 [m1-m0][n1-n0][K/G]. */
+int rrs_gemm_partials(const uint8_t* xq, int M, int K, int N, int G,
+                      const void* wq, int m0, int m1, int n0, int n1,
+                      int32_t* P, hipStream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RRS_H_ */

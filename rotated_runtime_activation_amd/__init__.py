@@ -1,0 +1,228 @@
+"""Python binding of librrs, the gfx950 Rotated Runtime Smooth A4W4 linear.
+
+Argument marshalling only: every function below checks tensor dtypes,
+shapes, devices and contiguity, takes raw device pointers and the current
+HIP stream, and calls the C entry point of the same name declared in
+``include/rrs.h``. All arithmetic runs in the HIP kernels of librrs; there is
+no fallback. If the library has not been built the import still succeeds but
+every call raises ``RRSLibraryMissing``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "lib", "librrs.so")
+
+RRS_OK, RRS_EINVAL, RRS_EUNSUPPORTED, RRS_EHIP = 0, -1, -2, -3
+RRS_FLAG_NO_ROTATE = 1
+RRS_FLAG_NO_SMOOTH = 2
+
+# every symbol include/rrs.h declares
+EXPORTS = (
+    "rrs_status_string", "rrs_version", "rrs_weight_bytes", "rrs_workspace_bytes",
+    "rrs_sync_bytes", "rrs_workspace_init", "rrs_calibrate_workspace_bytes",
+    "rrs_calibrate_perm", "rrs_prepare_weights", "rrs_linear", "rrs_frontend", "rrs_gemm",
+    "rrs_gemm_partials",
+)
+
+
+class RRSLibraryMissing(RuntimeError):
+    pass
+
+
+class RRSError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def _declare(lib):
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "rrs_status_string": (ctypes.c_char_p, [i]),
+        "rrs_version": (ctypes.c_char_p, []),
+        "rrs_weight_bytes": (sz, [i, i]),
+        "rrs_workspace_bytes": (sz, [i, i, i]),
+        "rrs_sync_bytes": (sz, [i, i]),
+        "rrs_workspace_init": (i, [vp, sz, vp]),
+        "rrs_calibrate_workspace_bytes": (sz, [i]),
+        "rrs_calibrate_perm": (i, [vp, i, i, vp, vp, sz, vp]),
+        "rrs_prepare_weights": (i, [vp, i, i, vp, vp, vp]),
+        "rrs_linear": (i, [vp, i, i, i, i, vp, vp, vp, vp, sz, vp]),
+        "rrs_frontend": (i, [vp, i, i, i, vp, vp, vp, vp, vp, sz, i, vp]),
+        "rrs_gemm": (i, [vp, vp, vp, i, i, i, i, vp, vp, vp]),
+        "rrs_gemm_partials": (i, [vp, i, i, i, i, vp, i, i, i, i, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+def lib():
+    """The loaded librrs (ctypes). Raises RRSLibraryMissing if not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RRSLibraryMissing(
+                f"{LIB_PATH} is missing: build it with `python -m rotated_runtime_activation_amd.build`")
+        _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != RRS_OK:
+        raise RRSError(fn, status, lib().rrs_status_string(status).decode())
+
+
+# ------------------------------------------------------------ size queries
+def rrs_weight_bytes(K: int, N: int) -> int:
+    return int(lib().rrs_weight_bytes(K, N))
+
+
+def rrs_workspace_bytes(M: int, K: int, G: int) -> int:
+    return int(lib().rrs_workspace_bytes(M, K, G))
+
+
+def rrs_sync_bytes(K: int, G: int) -> int:
+    return int(lib().rrs_sync_bytes(K, G))
+
+
+def rrs_calibrate_workspace_bytes(K: int) -> int:
+    return int(lib().rrs_calibrate_workspace_bytes(K))
+
+
+def rrs_status_string(status: int) -> str:
+    return lib().rrs_status_string(status).decode()
+
+
+def rrs_version() -> str:
+    return lib().rrs_version().decode()
+
+
+# ---------------------------------------------------------- marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtype, name: str, shape: Optional[tuple] = None, min_numel: int = 0):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.numel() * t.element_size() < min_numel:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {min_numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+# ----------------------------------------------------------- entry points
+def rrs_workspace_init(ws, stream=None) -> None:
+    _check("rrs_workspace_init", lib().rrs_workspace_init(_dev(ws, None, "ws"), _nbytes(ws), _stream(stream)))
+
+
+def rrs_calibrate_perm(X_cal, perm, ws, stream=None) -> None:
+    torch = _torch()
+    T, K = X_cal.shape
+    _check("rrs_calibrate_perm", lib().rrs_calibrate_perm(
+        _dev(X_cal, torch.float16, "X_cal"), T, K, _dev(perm, torch.int32, "perm", (K,)),
+        _dev(ws, None, "ws"), _nbytes(ws), _stream(stream)))
+
+
+def rrs_prepare_weights(W, perm, wq, stream=None) -> None:
+    torch = _torch()
+    K, N = W.shape
+    _check("rrs_prepare_weights", lib().rrs_prepare_weights(
+        _dev(W, torch.float16, "W"), K, N, _dev(perm, torch.int32, "perm", (K,)),
+        _dev(wq, torch.uint8, "wq", min_numel=rrs_weight_bytes(K, N)), _stream(stream)))
+
+
+def rrs_linear(X, G: int, perm, wq, Y, ws, stream=None) -> None:
+    torch = _torch()
+    M, K = X.shape
+    N = Y.shape[1]
+    _check("rrs_linear", lib().rrs_linear(
+        _dev(X, torch.float16, "X"), M, K, N, G, _dev(perm, torch.int32, "perm", (K,)),
+        _dev(wq, torch.uint8, "wq", min_numel=rrs_weight_bytes(K, N)),
+        _dev(Y, torch.float32, "Y", (M, N)), _dev(ws, None, "ws"), _nbytes(ws), _stream(stream)))
+
+
+def rrs_frontend(X, G: int, perm, xq, dx, S, ws, flags: int = 0, stream=None) -> None:
+    torch = _torch()
+    M, K = X.shape
+    _check("rrs_frontend", lib().rrs_frontend(
+        _dev(X, torch.float16, "X"), M, K, G, _dev(perm, torch.int32, "perm", (K,)),
+        _dev(xq, torch.uint8, "xq", (M, K // 2)), _dev(dx, torch.float32, "dx", (M,)),
+        _dev(S, torch.float32, "S", (K // G,)), _dev(ws, None, "ws"), _nbytes(ws), flags,
+        _stream(stream)))
+
+
+def rrs_gemm(xq, dx, S, G: int, wq, Y, stream=None) -> None:
+    torch = _torch()
+    M, Kh = xq.shape
+    K = 2 * Kh
+    N = Y.shape[1]
+    _check("rrs_gemm", lib().rrs_gemm(
+        _dev(xq, torch.uint8, "xq"), _dev(dx, torch.float32, "dx", (M,)),
+        _dev(S, torch.float32, "S", (K // G,)), M, K, N, G,
+        _dev(wq, torch.uint8, "wq", min_numel=rrs_weight_bytes(K, N)),
+        _dev(Y, torch.float32, "Y", (M, N)), _stream(stream)))
+
+
+def rrs_gemm_partials(xq, N: int, G: int, wq, m0: int, m1: int, n0: int, n1: int, P,
+                      stream=None) -> None:
+    torch = _torch()
+    M, Kh = xq.shape
+    K = 2 * Kh
+    _check("rrs_gemm_partials", lib().rrs_gemm_partials(
+        _dev(xq, torch.uint8, "xq"), M, K, N, G,
+        _dev(wq, torch.uint8, "wq", min_numel=rrs_weight_bytes(K, N)), m0, m1, n0, n1,
+        _dev(P, torch.int32, "P", (m1 - m0, n1 - n0, K // G)), _stream(stream)))
+
+
+# ----------------------------------------------------------- conveniences
+def weight_views(wq, K: int, N: int):
+    """(codes uint8 [N, K/2], dw float32 [N]) views into a prepared-weight
+    buffer (layout documented in include/rrs.h)."""
+    off = ((N * (K // 2)) + 255) // 256 * 256
+    codes = wq[: N * (K // 2)].view(N, K // 2)
+    dw = wq[off: off + 4 * N].view(_torch().float32)
+    return codes, dw
+
+
+def workspace_views(ws, M: int, K: int, G: int):
+    """(xq [M, K/2], dx [M], S [K/G]) views into an rrs_linear workspace."""
+    torch = _torch()
+    a = lambda x: (x + 255) // 256 * 256
+    sync = a(4 * (64 + K // G))
+    xq_off = sync
+    dx_off = xq_off + a(M * (K // 2))
+    s_off = dx_off + a(4 * M)
+    return (ws[xq_off: xq_off + M * (K // 2)].view(M, K // 2),
+            ws[dx_off: dx_off + 4 * M].view(torch.float32),
+            ws[s_off: s_off + 4 * (K // G)].view(torch.float32))

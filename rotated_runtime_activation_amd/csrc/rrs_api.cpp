@@ -1,0 +1,156 @@
+// Host side of the C ABI declared in include/rrs.h: argument validation,
+// buffer carving and kernel launches. Validation happens before any HIP call,
+// so a rejected call touches neither the device nor the runtime.
+
+#include "rrs.h"
+#include "rrs_internal.h"
+
+#define RRS_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using rrs::align256;
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int x) { return 31 - __builtin_clz(static_cast<unsigned>(x)); }
+
+bool valid_K(int K) {
+  return pow2(K) && ilog2(K) >= rrs::kMinLog2K && ilog2(K) <= rrs::kMaxLog2K;
+}
+bool valid_G(int G, int K) { return pow2(G) && G >= rrs::kMinG && G <= K; }
+
+// Largest synchronisation block over all legal (K, G): 64 + 8192/32 words.
+constexpr size_t kMaxSyncBytes = sizeof(uint32_t) * (rrs::kSyncGroups + (1 << rrs::kMaxLog2K) / rrs::kMinG);
+
+size_t sync_bytes(int K, int G) {
+  return align256(sizeof(uint32_t) * (rrs::kSyncGroups + K / G));
+}
+
+struct WsLayout {
+  size_t sync, xq, dx, S, total;
+};
+
+WsLayout ws_layout(int M, int K, int G) {
+  WsLayout l{};
+  l.sync = 0;
+  l.xq = sync_bytes(K, G);
+  l.dx = l.xq + align256(static_cast<size_t>(M) * (K / 2));
+  l.S = l.dx + align256(sizeof(float) * static_cast<size_t>(M));
+  l.total = l.S + align256(sizeof(float) * static_cast<size_t>(K / G));
+  return l;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? RRS_OK : RRS_EHIP; }
+
+}  // namespace
+
+RRS_API const char* rrs_status_string(int status) {
+  switch (status) {
+    case RRS_OK: return "RRS_OK";
+    case RRS_EINVAL: return "RRS_EINVAL: invalid argument";
+    case RRS_EUNSUPPORTED: return "RRS_EUNSUPPORTED: unsupported configuration";
+    case RRS_EHIP: return "RRS_EHIP: HIP runtime or launch failure";
+    default: return "RRS: unknown status";
+  }
+}
+
+RRS_API const char* rrs_version(void) { return "rrs-gfx950 1.0"; }
+
+RRS_API size_t rrs_weight_bytes(int K, int N) {
+  if (!valid_K(K) || N < 1) return 0;
+  return align256(static_cast<size_t>(N) * (K / 2)) + align256(sizeof(float) * static_cast<size_t>(N));
+}
+
+RRS_API size_t rrs_sync_bytes(int K, int G) {
+  if (!valid_K(K) || !valid_G(G, K)) return 0;
+  return sync_bytes(K, G);
+}
+
+RRS_API size_t rrs_workspace_bytes(int M, int K, int G) {
+  if (M < 0 || !valid_K(K) || !valid_G(G, K)) return 0;
+  return ws_layout(M, K, G).total;
+}
+
+RRS_API size_t rrs_calibrate_workspace_bytes(int K) {
+  if (!valid_K(K)) return 0;
+  return align256(sizeof(uint32_t) * static_cast<size_t>(K));
+}
+
+RRS_API int rrs_workspace_init(void* ws, size_t ws_bytes, hipStream_t s) {
+  if (ws == nullptr || ws_bytes < 256 || ws_bytes % 4) return RRS_EINVAL;
+  const size_t n = (ws_bytes < kMaxSyncBytes ? ws_bytes : kMaxSyncBytes) / sizeof(uint32_t);
+  return hip_status(rrs::launch_zero_u32(static_cast<uint32_t*>(ws), n, s));
+}
+
+RRS_API int rrs_calibrate_perm(const void* X_cal_fp16, int T, int K, int32_t* perm, void* ws,
+                               size_t ws_bytes, hipStream_t s) {
+  if (X_cal_fp16 == nullptr || perm == nullptr || ws == nullptr) return RRS_EINVAL;
+  if (T < 1 || !valid_K(K)) return RRS_EINVAL;
+  if (ws_bytes < rrs_calibrate_workspace_bytes(K)) return RRS_EINVAL;
+  return hip_status(rrs::launch_calibrate(static_cast<const uint16_t*>(X_cal_fp16), T, ilog2(K), perm,
+                                          static_cast<uint32_t*>(ws), s));
+}
+
+RRS_API int rrs_prepare_weights(const void* W_fp16, int K, int N, const int32_t* perm, void* wq,
+                                hipStream_t s) {
+  if (W_fp16 == nullptr || perm == nullptr || wq == nullptr) return RRS_EINVAL;
+  if (!valid_K(K) || N < 1) return RRS_EINVAL;
+  uint8_t* codes = static_cast<uint8_t*>(wq);
+  float* dw = reinterpret_cast<float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
+  return hip_status(rrs::launch_weight_prep(static_cast<const uint16_t*>(W_fp16), ilog2(K), N, perm,
+                                            codes, dw, s));
+}
+
+RRS_API int rrs_frontend(const void* X_fp16, int M, int K, int G, const int32_t* perm, uint8_t* xq,
+                         float* dx, float* S, void* ws, size_t ws_bytes, int flags, hipStream_t s) {
+  if (M < 0 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;
+  if (flags & ~(RRS_FLAG_NO_ROTATE | RRS_FLAG_NO_SMOOTH)) return RRS_EINVAL;
+  if (perm == nullptr || S == nullptr || ws == nullptr) return RRS_EINVAL;
+  if (M > 0 && (X_fp16 == nullptr || xq == nullptr || dx == nullptr)) return RRS_EINVAL;
+  if (ws_bytes < sync_bytes(K, G)) return RRS_EINVAL;
+  if (M == 0) return RRS_OK;
+  return hip_status(rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, ilog2(K), G, perm, xq,
+                                         dx, S, static_cast<uint32_t*>(ws), flags, s));
+}
+
+RRS_API int rrs_gemm(const uint8_t* xq, const float* dx, const float* S, int M, int K, int N, int G,
+                     const void* wq, float* Y, hipStream_t s) {
+  if (M < 0 || N < 1 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;
+  if (S == nullptr || wq == nullptr) return RRS_EINVAL;
+  if (M > 0 && (xq == nullptr || dx == nullptr || Y == nullptr)) return RRS_EINVAL;
+  if (M == 0) return RRS_OK;
+  const uint8_t* codes = static_cast<const uint8_t*>(wq);
+  const float* dw = reinterpret_cast<const float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
+  return hip_status(rrs::launch_gemm(xq, dx, S, M, ilog2(K), N, G, codes, dw, Y, nullptr, 0, 0, 0, 0, s));
+}
+
+RRS_API int rrs_gemm_partials(const uint8_t* xq, int M, int K, int N, int G, const void* wq, int m0,
+                              int m1, int n0, int n1, int32_t* P, hipStream_t s) {
+  if (M < 1 || N < 1 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;
+  if (xq == nullptr || wq == nullptr || P == nullptr) return RRS_EINVAL;
+  if (m0 < 0 || m1 > M || m0 >= m1 || n0 < 0 || n1 > N || n0 >= n1) return RRS_EINVAL;
+  const uint8_t* codes = static_cast<const uint8_t*>(wq);
+  const float* dw = reinterpret_cast<const float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
+  return hip_status(rrs::launch_gemm(xq, nullptr, nullptr, M, ilog2(K), N, G, codes, dw, nullptr, P, m0,
+                                     m1, n0, n1, s));
+}
+
+RRS_API int rrs_linear(const void* X_fp16, int M, int K, int N, int G, const int32_t* perm,
+                       const void* wq, float* Y, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (M < 0 || N < 1 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;
+  if (perm == nullptr || wq == nullptr || ws == nullptr) return RRS_EINVAL;
+  if (M > 0 && (X_fp16 == nullptr || Y == nullptr)) return RRS_EINVAL;
+  const WsLayout l = ws_layout(M, K, G);
+  if (ws_bytes < l.total) return RRS_EINVAL;
+  if (M == 0) return RRS_OK;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* xq = base + l.xq;
+  float* dx = reinterpret_cast<float*>(base + l.dx);
+  float* S = reinterpret_cast<float*>(base + l.S);
+  hipError_t e = rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, ilog2(K), G, perm, xq, dx, S,
+                                      reinterpret_cast<uint32_t*>(base + l.sync), 0, s);
+  if (e != hipSuccess) return RRS_EHIP;
+  const uint8_t* codes = static_cast<const uint8_t*>(wq);
+  const float* dw = reinterpret_cast<const float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
+  return hip_status(rrs::launch_gemm(xq, dx, S, M, ilog2(K), N, G, codes, dw, Y, nullptr, 0, 0, 0, 0, s));
+}

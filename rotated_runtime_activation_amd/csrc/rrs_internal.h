@@ -1,0 +1,51 @@
+// Internal declarations shared by the HIP translation units of librrs.
+// Not part of the public ABI (that is include/rrs.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rrs {
+
+// Largest and smallest supported Hadamard sizes / group sizes.
+constexpr int kMinLog2K = 6;
+constexpr int kMaxLog2K = 13;
+constexpr int kMinG = 32;
+
+// Layout of the synchronisation block at the start of a workspace (all
+// uint32): [0] done-counter of the quantise kernel, [1] grid barrier word,
+// [2] error flag, [3..63] reserved, [64 .. 64 + K/G) running group maxima as
+// float bits. Every front-end call leaves the block zeroed.
+constexpr int kSyncCounter = 0;
+constexpr int kSyncBarrier = 1;
+constexpr int kSyncError = 2;
+constexpr int kSyncGroups = 64;
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Front end (activation rows): stats pass then quantise pass.
+//   flags: bit0 = skip rotation, bit1 = skip smoothing (S = 1).
+hipError_t launch_frontend(const uint16_t* X, int M, int log2K, int G, const int32_t* perm,
+                           uint8_t* xq, float* dx, float* S_out, uint32_t* sync, int flags,
+                           hipStream_t s);
+
+// Offline weight preparation: W [K, N] row-major fp16 -> wq [N][K/2] + dw [N].
+hipError_t launch_weight_prep(const uint16_t* W, int log2K, int N, const int32_t* perm,
+                              uint8_t* wq, float* dw, hipStream_t s);
+
+// Calibration permutation: per-channel |max| of the rotated rows, then a
+// stable descending rank. ws holds K uint32.
+hipError_t launch_calibrate(const uint16_t* Xc, int T, int log2K, int32_t* perm, uint32_t* ws,
+                            hipStream_t s);
+
+// Zero n uint32 words (fill kernel; used instead of hipMemsetAsync).
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
+
+// Grouped INT4 GEMM. Y = (1/K) dx dw sum_g S_g P_g. If P != nullptr the
+// kernel instead writes the int32 partials of the window [m0,m1) x [n0,n1).
+hipError_t launch_gemm(const uint8_t* xq, const float* dx, const float* S, int M, int log2K,
+                       int N, int G, const uint8_t* wq, const float* dw, float* Y, int32_t* P,
+                       int m0, int m1, int n0, int n1, hipStream_t s);
+
+}  // namespace rrs

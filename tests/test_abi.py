@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import rotated_runtime_activation_amd as rra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(rra.LIB_PATH),
+                                reason="librrs.so not built (run __graft_entry__.build())")
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "rrs.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rrs_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(rra.EXPORTS) == header_functions()
+
+
+def test_library_exports_every_header_symbol():
+    lib = ctypes.CDLL(rra.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    assert rra.rrs_status_string(0) == "RRS_OK"
+    assert "EINVAL" in rra.rrs_status_string(-1)
+    assert "EUNSUPPORTED" in rra.rrs_status_string(-2)
+    assert "EHIP" in rra.rrs_status_string(-3)
+    assert "unknown" in rra.rrs_status_string(42)
+    assert rra.rrs_version().startswith("rrs-gfx950")
+
+
+def test_size_queries():
+    # weights: N*K/2 codes + 4N scales, each section 256-byte aligned
+    assert rra.rrs_weight_bytes(4096, 4096) == 4096 * 2048 + 4096 * 4
+    assert rra.rrs_weight_bytes(256, 3) == 512 + 256
+    assert rra.rrs_weight_bytes(100, 4) == 0      # K not a power of two
+    assert rra.rrs_weight_bytes(32, 4) == 0       # K < 64
+    assert rra.rrs_weight_bytes(16384, 4) == 0    # K > 8192
+    assert rra.rrs_weight_bytes(256, 0) == 0
+    # workspace: sync block + xq + dx + S
+    sync = rra.rrs_sync_bytes(4096, 128)
+    # 64 control words + one word per group, rounded up to 256 bytes
+    assert sync == 512 and rra.rrs_sync_bytes(8192, 32) == 1280
+    assert rra.rrs_workspace_bytes(2048, 4096, 128) == sync + 2048 * 2048 + 2048 * 4 + 256
+    assert rra.rrs_workspace_bytes(1, 64, 32) == 512 + 256 + 256 + 256
+    assert rra.rrs_workspace_bytes(16, 256, 16) == 0   # G < 32
+    assert rra.rrs_workspace_bytes(16, 256, 512) == 0  # G > K
+    assert rra.rrs_workspace_bytes(16, 256, 96) == 0   # G not a power of two
+    assert rra.rrs_workspace_bytes(-1, 256, 128) == 0
+    assert rra.rrs_calibrate_workspace_bytes(8192) == 32768
+
+
+# Invalid calls return RRS_EINVAL from the host-side checks; nothing is
+# launched, so they run without a GPU. Pointers are dummies that would fault
+# if ever dereferenced.
+DUMMY = ctypes.c_void_p(0x1000)
+NULL = None
+
+
+def _lin(**kw):
+    a = dict(X=DUMMY, M=16, K=256, N=256, G=128, perm=DUMMY, wq=DUMMY, Y=DUMMY, ws=DUMMY,
+             ws_bytes=1 << 20, s=NULL)
+    a.update(kw)
+    return rra.lib().rrs_linear(a["X"], a["M"], a["K"], a["N"], a["G"], a["perm"], a["wq"],
+                                a["Y"], a["ws"], a["ws_bytes"], a["s"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(K=100), dict(K=32), dict(K=16384), dict(G=16), dict(G=96), dict(G=512),
+    dict(M=-1), dict(N=0), dict(X=NULL), dict(perm=NULL), dict(wq=NULL), dict(Y=NULL),
+    dict(ws=NULL), dict(ws_bytes=100),
+])
+def test_linear_rejects(kw):
+    assert _lin(**kw) == rra.RRS_EINVAL
+
+
+def test_linear_zero_tokens_is_noop():
+    assert _lin(M=0, X=NULL, Y=NULL) == rra.RRS_OK
+
+
+def test_frontend_rejects():
+    L = rra.lib()
+    ok = dict(X=DUMMY, M=4, K=256, G=64, perm=DUMMY, xq=DUMMY, dx=DUMMY, S=DUMMY, ws=DUMMY,
+              ws_bytes=4096, flags=0)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return L.rrs_frontend(a["X"], a["M"], a["K"], a["G"], a["perm"], a["xq"], a["dx"], a["S"],
+                              a["ws"], a["ws_bytes"], a["flags"], NULL)
+    assert call(flags=4) == rra.RRS_EINVAL
+    assert call(ws_bytes=255) == rra.RRS_EINVAL
+    assert call(S=NULL) == rra.RRS_EINVAL
+    assert call(xq=NULL) == rra.RRS_EINVAL
+    assert call(G=512) == rra.RRS_EINVAL
+    assert call(M=0, X=NULL, xq=NULL, dx=NULL) == rra.RRS_OK
+
+
+def test_gemm_and_partials_reject():
+    L = rra.lib()
+    assert L.rrs_gemm(DUMMY, DUMMY, DUMMY, 4, 256, 0, 128, DUMMY, DUMMY, NULL) == rra.RRS_EINVAL
+    assert L.rrs_gemm(DUMMY, DUMMY, NULL, 4, 256, 8, 128, DUMMY, DUMMY, NULL) == rra.RRS_EINVAL
+    assert L.rrs_gemm(NULL, NULL, DUMMY, 0, 256, 8, 128, DUMMY, NULL, NULL) == rra.RRS_OK
+    # partial windows must lie inside [0, M) x [0, N) and be non-empty
+    for m0, m1, n0, n1 in [(0, 5, 0, 4), (2, 2, 0, 4), (0, 4, -1, 4), (0, 4, 0, 9), (3, 1, 0, 4)]:
+        assert L.rrs_gemm_partials(DUMMY, 4, 256, 8, 128, DUMMY, m0, m1, n0, n1, DUMMY, NULL) == rra.RRS_EINVAL
+
+
+def test_weights_calibrate_init_reject():
+    L = rra.lib()
+    assert L.rrs_prepare_weights(DUMMY, 96, 8, DUMMY, DUMMY, NULL) == rra.RRS_EINVAL
+    assert L.rrs_prepare_weights(DUMMY, 256, 0, DUMMY, DUMMY, NULL) == rra.RRS_EINVAL
+    assert L.rrs_prepare_weights(DUMMY, 256, 8, NULL, DUMMY, NULL) == rra.RRS_EINVAL
+    assert L.rrs_calibrate_perm(DUMMY, 0, 256, DUMMY, DUMMY, 1024, NULL) == rra.RRS_EINVAL
+    assert L.rrs_calibrate_perm(DUMMY, 8, 256, DUMMY, DUMMY, 1000, NULL) == rra.RRS_EINVAL
+    assert L.rrs_workspace_init(NULL, 1024, NULL) == rra.RRS_EINVAL
+    assert L.rrs_workspace_init(DUMMY, 100, NULL) == rra.RRS_EINVAL
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(rra, "_lib", None)
+    monkeypatch.setattr(rra, "LIB_PATH", "/nonexistent/librrs.so")
+    with pytest.raises(rra.RRSLibraryMissing):
+        rra.rrs_weight_bytes(256, 4)

@@ -1,0 +1,217 @@
+"""GPU parity of each stage of the HIP path against the CPU oracle, on small
+and ragged shapes that span several tiles (run on an MI355X: -m gpu)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rotated_runtime_activation_amd as rra
+import workloads
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+# (M, K, G): K sweep 64..8192, G sweep 32..K, ragged token counts (not a
+# multiple of the rows a wavefront handles when K < 4096, or of the GEMM tile)
+FE_SHAPES = [
+    (16, 256, 128), (1, 64, 32), (3, 64, 64), (17, 128, 32), (64, 256, 256), (5, 512, 128),
+    (33, 1024, 1024), (7, 2048, 64), (2, 4096, 128), (9, 4096, 4096), (3, 4096, 32),
+    (3, 8192, 128), (65, 8192, 32), (2, 8192, 8192), (300, 512, 64),
+]
+
+
+def _case(M, K, N=8, seed=None):
+    seed = seed if seed is not None else M * 7919 + K
+    x, xc, w = workloads.random_case(seed, M, K, N)
+    perm = oracle.calibrate_perm(xc)
+    return x, w, perm
+
+
+@pytest.mark.parametrize("M,K,G", FE_SHAPES)
+def test_frontend(M, K, G):
+    gu.log(f"[frontend] M={M} K={K} G={G}")
+    x, _, perm = _case(M, K)
+    gu.check_frontend(x, perm, G)
+
+
+@pytest.mark.parametrize("M,K,G", [(40, 512, 64), (5, 4096, 128), (3, 8192, 256)])
+@pytest.mark.parametrize("flags", [rra.RRS_FLAG_NO_ROTATE, rra.RRS_FLAG_NO_SMOOTH,
+                                   rra.RRS_FLAG_NO_ROTATE | rra.RRS_FLAG_NO_SMOOTH])
+def test_frontend_ablations(M, K, G, flags):
+    gu.log(f"[frontend ablation] flags={flags} M={M} K={K} G={G}")
+    x, _, perm = _case(M, K)
+    gu.check_frontend(x, perm, G, flags)
+
+
+def test_frontend_random_perm():
+    gu.log("[frontend] shuffled permutation M=50 K=1024 G=128")
+    x, _, _ = _case(50, 1024)
+    gu.check_frontend(x, workloads.shuffled_perm(1024, 3), 128)
+
+
+def test_frontend_zero_rows_and_groups():
+    gu.log("[frontend] zero rows / all-zero input")
+    K, G = 512, 64
+    x, _, perm = _case(12, K)
+    x[[0, 5, 11]] = 0
+    fe, xq, dx, S, q, _ = gu.check_frontend(x, perm, G)
+    assert np.all(dx[[0, 5, 11]] == 0) and not q[[0, 5, 11]].any()
+    # all zero: every group scale guarded to 1, all codes 0
+    z = np.zeros((7, K), dtype=np.float16)
+    xq, dx, S = gu.frontend(z, perm, G)
+    assert not xq.any() and not dx.any() and np.all(S == 1.0)
+    # zero groups without rotation: groups with no nonzero channel -> 1
+    z[:, perm[:G]] = 1.5
+    gu.check_frontend(z, perm, G, rra.RRS_FLAG_NO_ROTATE)
+
+
+def test_frontend_extreme_values():
+    """fp16 extremes: spikes at +-65504 on two tokens (the two-outlier-token
+    case the RRS summary lists as a limitation) and subnormal inputs."""
+    gu.log("[frontend] fp16 extremes")
+    K, G = 4096, 128
+    x, _, perm = _case(20, K)
+    x[3, 17] = np.float16(65504)
+    x[11, 2000] = np.float16(-65504)
+    x[5] = np.float16(6e-8)        # subnormal row
+    gu.check_frontend(x, perm, G)
+
+
+@pytest.mark.parametrize("K,N", [(256, 256), (64, 7), (512, 130), (4096, 300), (8192, 129)])
+def test_prepare_weights(K, N):
+    gu.log(f"[weights] K={K} N={N}")
+    _, w, perm = _case(4, K, N)
+    wq = gu.prepare_weights(w, perm)
+    torch.cuda.synchronize()
+    codes, dw = rra.weight_views(wq, K, N)
+    ref = oracle.prepare_weights(w, perm)
+    gu.compare_codes(oracle.unpack_codes(codes.cpu().numpy()), ref["qw"], ref["uw"], "weight codes")
+    gu.rel_close(dw.cpu().numpy(), ref["dw"], gu.SCALE_TOL, "dw")
+
+
+def test_prepare_weights_zero_column():
+    gu.log("[weights] zero column")
+    _, w, perm = _case(4, 512, 9)
+    w[:, 4] = 0
+    wq = gu.prepare_weights(w, perm)
+    codes, dw = rra.weight_views(wq, 512, 9)
+    torch.cuda.synchronize()
+    assert not codes[4].any().item() and dw[4].item() == 0.0
+
+
+# (M, N, K, G) for the grouped GEMM, fed oracle codes
+GEMM_SHAPES = [
+    (16, 256, 256, 128), (1, 1, 64, 32), (130, 200, 512, 32), (64, 64, 64, 64),
+    (257, 129, 1024, 256), (128, 128, 4096, 4096), (33, 300, 2048, 128), (5, 17, 8192, 512),
+]
+
+
+def _random_codes(seed, M, N, K):
+    g = np.random.default_rng(seed)
+    q = g.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = g.integers(-7, 8, size=(N, K)).astype(np.int8)
+    q[0, :] = 7      # extreme partials +-49 G
+    qw[0, :] = -7
+    return q, qw
+
+
+@pytest.mark.parametrize("M,N,K,G", GEMM_SHAPES)
+def test_gemm_partials_exact(M, N, K, G):
+    gu.log(f"[gemm partials] M={M} N={N} K={K} G={G}")
+    q, qw = _random_codes(M + N + K, M, N, K)
+    xq = gu.to_dev(oracle.pack_codes(q))
+    wq = gu.weight_buffer_from_codes(oracle.pack_codes(qw), np.ones(N))
+    ref = oracle.group_partials(q, qw, G)
+    for (m0, m1, n0, n1) in {(0, M, 0, N), (M // 2, M, N // 3, N), (M - 1, M, N - 1, N)}:
+        P = torch.empty(m1 - m0, n1 - n0, K // G, dtype=torch.int32, device=gu.DEV)
+        rra.rrs_gemm_partials(xq, N, G, wq, m0, m1, n0, n1, P)
+        torch.cuda.synchronize()
+        got = P.cpu().numpy()
+        assert np.array_equal(got, ref[m0:m1, n0:n1]), \
+            f"partials differ in window {(m0, m1, n0, n1)}: {int((got != ref[m0:m1, n0:n1]).sum())} entries"
+
+
+@pytest.mark.parametrize("M,N,K,G", GEMM_SHAPES)
+def test_gemm_output(M, N, K, G):
+    gu.log(f"[gemm Y] M={M} N={N} K={K} G={G}")
+    q, qw = _random_codes(M * 3 + N + K, M, N, K)
+    g = np.random.default_rng(K + M)
+    dx = (g.random(M) + 0.1).astype(np.float32)
+    dw = (g.random(N) * 0.01 + 1e-3).astype(np.float32)
+    S = (g.random(K // G) * 100 + 1).astype(np.float32)
+    ref = oracle.linear_out(q, dx.astype(np.float64), S.astype(np.float64), qw, dw.astype(np.float64), G)
+    Y = torch.empty(M, N, dtype=torch.float32, device=gu.DEV)
+    rra.rrs_gemm(gu.to_dev(oracle.pack_codes(q)), gu.to_dev(dx), gu.to_dev(S), G,
+                 gu.weight_buffer_from_codes(oracle.pack_codes(qw), dw), Y)
+    torch.cuda.synchronize()
+    err = gu.y_error(Y.cpu().numpy(), ref)
+    gu.log(f"  Y err/C = {err:.3e}")
+    assert err <= gu.Y_TOL
+
+
+@pytest.mark.parametrize("M,K,N,G", [(16, 256, 256, 128), (45, 1024, 300, 64), (3, 8192, 129, 32),
+                                     (130, 4096, 260, 4096), (1, 64, 1, 32)])
+def test_linear_end_to_end(M, K, N, G):
+    gu.log(f"[linear] M={M} K={K} N={N} G={G}")
+    x, w, perm = _case(M, K, N)
+    ref = oracle.rrs_linear(x, w, perm, G)
+    wq = gu.prepare_weights(w, perm)
+    ws = torch.zeros(rra.rrs_workspace_bytes(M, K, G), dtype=torch.uint8, device=gu.DEV)
+    rra.rrs_workspace_init(ws)
+    Y = torch.empty(M, N, dtype=torch.float32, device=gu.DEV)
+    rra.rrs_linear(gu.to_dev(x), G, gu.to_dev(perm), wq, Y, ws)
+    torch.cuda.synchronize()
+    xq, dx, S = rra.workspace_views(ws, M, K, G)
+    q_gpu = oracle.unpack_codes(xq.cpu().numpy())
+    gu.compare_codes(q_gpu, ref["fe"]["q"], ref["fe"]["v"], "linear codes")
+    codes, dw = rra.weight_views(wq, K, N)
+    qw_gpu = oracle.unpack_codes(codes.cpu().numpy())
+    gu.compare_codes(qw_gpu, ref["wp"]["qw"], ref["wp"]["uw"], "weight codes")
+    Yg = Y.cpu().numpy().astype(np.float64)
+    err = np.abs(Yg - ref["Y"])
+    bound = gu.Y_TOL * ref["C"] + (1 + 1e-6) * gu.flip_bound(
+        q_gpu, ref["fe"]["q"], qw_gpu, ref["wp"]["qw"], ref["fe"]["dx"], ref["fe"]["S"], ref["wp"]["dw"], G)
+    gu.log(f"  Y max err/C = {gu.y_error(Yg, ref):.3e}")
+    assert np.all(err <= bound)
+
+
+def test_determinism():
+    gu.log("[determinism] two identical rrs_linear calls")
+    M, K, N, G = 200, 4096, 512, 128
+    x, w, perm = _case(M, K, N)
+    wq = gu.prepare_weights(w, perm)
+    ws = torch.zeros(rra.rrs_workspace_bytes(M, K, G), dtype=torch.uint8, device=gu.DEV)
+    rra.rrs_workspace_init(ws)
+    X, P = gu.to_dev(x), gu.to_dev(perm)
+    Y1 = torch.empty(M, N, dtype=torch.float32, device=gu.DEV)
+    Y2 = torch.empty_like(Y1)
+    rra.rrs_linear(X, G, P, wq, Y1, ws)
+    xq1 = rra.workspace_views(ws, M, K, G)[0].clone()
+    rra.rrs_linear(X, G, P, wq, Y2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)
+    assert torch.equal(xq1, rra.workspace_views(ws, M, K, G)[0])
+
+
+@pytest.mark.parametrize("T,K", [(128, 256), (512, 4096), (100, 8192), (3, 64)])
+def test_calibrate_perm(T, K):
+    gu.log(f"[calibrate] T={T} K={K}")
+    wl = workloads.Workload(20_000 + K, "cal", T, K, 8, (K,), 8, 20.0, "count", 3, 500.0, 0.02, T)
+    xc = workloads.make_activations(wl, T, wl.seed_base + workloads.ROLE_CALIB)
+    ref = oracle.calibrate_perm(xc)
+    perm = torch.empty(K, dtype=torch.int32, device=gu.DEV)
+    ws = torch.empty(rra.rrs_calibrate_workspace_bytes(K), dtype=torch.uint8, device=gu.DEV)
+    rra.rrs_calibrate_perm(gu.to_dev(xc), perm, ws)
+    torch.cuda.synchronize()
+    got = perm.cpu().numpy()
+    assert np.array_equal(np.sort(got), np.arange(K))
+    # the order is unique where channel maxima differ by more than fp32
+    # rounding of the rotation; near-ties may swap
+    c = np.abs(oracle.fwht(xc)).max(axis=0)
+    cs = c[got]
+    assert np.all(cs[:-1] >= cs[1:] * (1 - 1e-5) - 1e-30)
+    same = got == ref
+    if not same.all():
+        idx = np.nonzero(~same)[0]
+        assert np.all(np.abs(c[got[idx]] - c[ref[idx]]) <= 1e-5 * c[ref[idx]])
+    gu.log(f"  perm positions differing from the oracle (near-ties): {int((~same).sum())}")
