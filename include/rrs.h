@@ -33,8 +33,16 @@
  *   the entry points that take M and is a no-op).
  * - Layouts: X fp16 [M, K] row-major; W fp16 [K, N] row-major (the
  *   transpose of nn.Linear.weight); Y fp32 [M, N] row-major.
- * - Packed codes: byte i of a row holds code 2i in its low nibble and code
- *   2i+1 in its high nibble, two's complement; K runs in reordered order.
+ * - Packed codes: 4-bit sign-magnitude, K in reordered order, 8 codes per
+ *   little-endian 32-bit word (4 bytes). With a_j = code 2j and b_j = code
+ *   2j+1 of a word, byte j holds |a_j| in bits 0-2, |b_j| in bits 4-6, the
+ *   sign of a_j in bit 7 and the sign of b_{(j-1) mod 4} in bit 3. Masking a
+ *   word with 0x87878787 then gives its four a codes, and rotating it right
+ *   by 4 bits before the same mask its four b codes, each as an fp8 e4m3
+ *   byte whose value is exactly code * 2^-9 (a subnormal), which the matrix
+ *   cores consume directly. A zero code may carry either sign bit (a
+ *   negative value that rounds to 0 keeps its sign); readers take any zero
+ *   magnitude as 0. The pages fix no storage layout.
  * - Scales are reported in the unnormalised-Hadamard convention:
  *     dx[t] = r_t / 7 with r_t = max_j |Zp[t,j] / S_g(j)|,
  *     S[g]  = max over tokens and the group's channels of |Zp|,

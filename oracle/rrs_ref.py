@@ -30,7 +30,8 @@ tokens; R2 the max runs over all tokens of the call; R3/R4 Sylvester Hadamard
 in natural order, unnormalised, with the exact 1/K folded into the output;
 R5 rotate, then reorder, then smooth; R6 round half to even; R7 no clipping;
 R8 codes in [-7, 7]; R9 zero group -> scale 1, zero row -> codes 0 and scale 0;
-R10 nibble pack, low nibble first, two's complement; R11 weights RTN per output
+R10 4-bit sign-magnitude packing, 8 codes per 32-bit word (layout in
+``pack_codes``); R11 weights RTN per output
 channel; R12 the group scale multiplies each group's integer partial.
 
 Every function below is pinned by ``tests/test_oracle_*.py`` against something
@@ -234,24 +235,36 @@ def rrs_linear(X: np.ndarray, W: np.ndarray, perm: np.ndarray, G: int) -> Dict[s
 
 # ----------------------------------------------------------------- packing
 def pack_codes(q: np.ndarray) -> np.ndarray:
-    """Nibble pack along the last axis (reading R10): byte i holds code 2i in
-    its low nibble and code 2i+1 in its high nibble, two's complement."""
+    """4-bit sign-magnitude packing along the last axis (reading R10; the
+    pages fix no layout). Codes come in words of 8 (4 bytes, little endian);
+    with a_j = code 2j and b_j = code 2j+1 of a word, byte j holds
+      bits 0-2: |a_j|,  bit 7: sign of a_j,
+      bits 4-6: |b_j|,  and bit 3 of byte (j+1) mod 4 holds the sign of b_j.
+    Zero is stored with a clear sign bit; the last axis must be a multiple
+    of 8."""
     q = np.asarray(q).astype(np.int16)
-    lo = q[..., 0::2] & 0xF
-    hi = q[..., 1::2] & 0xF
-    return (lo | (hi << 4)).astype(np.uint8)
+    if q.shape[-1] % 8:
+        raise ValueError("code rows must be a multiple of 8")
+    w = q.reshape(q.shape[:-1] + (q.shape[-1] // 8, 4, 2))
+    a, b = w[..., 0], w[..., 1]
+    sa = (a < 0).astype(np.int16)
+    sb = (b < 0).astype(np.int16)
+    byte = np.abs(a) | (np.abs(b) << 4) | (sa << 7) | (np.roll(sb, 1, axis=-1) << 3)
+    return byte.reshape(q.shape[:-1] + (q.shape[-1] // 2,)).astype(np.uint8)
 
 
-def unpack_codes(b: np.ndarray) -> np.ndarray:
-    b = np.asarray(b).astype(np.int16)
-    lo = b & 0xF
-    hi = (b >> 4) & 0xF
-    lo = np.where(lo >= 8, lo - 16, lo)
-    hi = np.where(hi >= 8, hi - 16, hi)
-    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.int8)
-    out[..., 0::2] = lo
-    out[..., 1::2] = hi
-    return out
+def unpack_codes(bts: np.ndarray) -> np.ndarray:
+    """Inverse of ``pack_codes`` (a stored sign on a zero magnitude reads as
+    zero)."""
+    bts = np.asarray(bts).astype(np.int16)
+    w = bts.reshape(bts.shape[:-1] + (bts.shape[-1] // 4, 4))
+    ma, mb = w & 7, (w >> 4) & 7
+    sa = (w >> 7) & 1
+    sb = np.roll((w >> 3) & 1, -1, axis=-1)
+    a = np.where(sa == 1, -ma, ma)
+    b = np.where(sb == 1, -mb, mb)
+    out = np.stack((a, b), axis=-1).reshape(bts.shape[:-1] + (2 * bts.shape[-1],))
+    return out.astype(np.int8)
 
 
 # ---------------------------------------------------------- parity helpers

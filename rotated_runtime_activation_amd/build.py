@@ -36,6 +36,9 @@ def command(out: str = LIB) -> list:
         "-fvisibility=hidden",
         # packed fp32 VALU forms are kept out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # matrix-core accumulators in VGPRs: the group rescale multiplies them
+        # with ordinary VALU instructions
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         *[os.path.join(CSRC, s) for s in SOURCES],
         "-o", out,

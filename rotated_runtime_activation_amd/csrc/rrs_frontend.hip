@@ -31,9 +31,9 @@ namespace rrs {
 namespace {
 
 constexpr int kWave = 64;
-// Adding 1.5 * 2^23 to |x| < 2^22 rounds x to the nearest integer (ties to
-// even, the default mode) and leaves it in the low mantissa bits in two's
-// complement: the low nibble of the result bits is the 4-bit code.
+// Adding 1.5 * 2^23 to 0 <= x < 2^22 rounds x to the nearest integer (ties
+// to even, the default mode) and leaves it in the low mantissa bits: for a
+// code magnitude (<= 7) the low 3 bits of the result are the magnitude.
 constexpr float kMagic = 12582912.0f;
 
 enum Mode { kStats = 0, kQuant = 1, kWeight = 2, kColmax = 3 };
@@ -95,16 +95,30 @@ __device__ __forceinline__ void butterfly(float (&v)[E], int h) {
   }
 }
 
-// Eight 4-bit codes (low nibbles of b[0..7]) -> one packed word, code 2i in
-// the low nibble of byte i and code 2i+1 in its high nibble.
-__device__ __forceinline__ uint32_t pack8(const uint32_t* b) {
-  const uint32_t e0 = __builtin_amdgcn_perm(b[2], b[0], 0x0c0c0400u);
-  const uint32_t e1 = __builtin_amdgcn_perm(b[6], b[4], 0x0c0c0400u);
-  const uint32_t ev = __builtin_amdgcn_perm(e1, e0, 0x05040100u);
-  const uint32_t o0 = __builtin_amdgcn_perm(b[3], b[1], 0x0c0c0400u);
-  const uint32_t o1 = __builtin_amdgcn_perm(b[7], b[5], 0x0c0c0400u);
-  const uint32_t od = __builtin_amdgcn_perm(o1, o0, 0x05040100u);
-  return (ev & 0x0f0f0f0fu) | ((od << 4) & 0xf0f0f0f0u);
+// Byte 0 (resp. byte 3) of four words, gathered into one word.
+__device__ __forceinline__ uint32_t gather_b0(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
+  const uint32_t t01 = __builtin_amdgcn_perm(x1, x0, 0x0c0c0400u);
+  const uint32_t t23 = __builtin_amdgcn_perm(x3, x2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t gather_b3(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
+  const uint32_t t01 = __builtin_amdgcn_perm(x1, x0, 0x0c0c0703u);
+  const uint32_t t23 = __builtin_amdgcn_perm(x3, x2, 0x0c0c0703u);
+  return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+}
+
+// Eight codes -> one packed word. mag[i] holds |code i| in its low 3 bits,
+// sgn[i] the float whose sign is the sign of code i. Layout (8 codes per
+// little-endian word, a_j = code 2j, b_j = code 2j+1): byte j carries |a_j|
+// in bits 0-2, |b_j| in bits 4-6 and sign(a_j) in bit 7; bit 3 of byte
+// (j+1) mod 4 carries sign(b_j). With it, w & 0x87878787 and
+// rotr(w, 4) & 0x87878787 are the a- and b-codes as fp8 e4m3 subnormals.
+__device__ __forceinline__ uint32_t pack8(const uint32_t* mag, const uint32_t* sgn) {
+  const uint32_t ma = gather_b0(mag[0], mag[2], mag[4], mag[6]);
+  const uint32_t mb = gather_b0(mag[1], mag[3], mag[5], mag[7]);
+  const uint32_t sa = gather_b3(sgn[0], sgn[2], sgn[4], sgn[6]);
+  const uint32_t sb = gather_b3(sgn[7], sgn[1], sgn[3], sgn[5]);
+  return ma | (mb << 4) | (sa & 0x80808080u) | ((sb >> 4) & 0x08080808u);
 }
 
 template <int LOG2K, int MODE, bool ROTATE>
@@ -296,11 +310,14 @@ frontend_kernel(FeArgs a) {
         uint32_t packed[E / 8];
 #pragma unroll
         for (int o = 0; o < E / 8; ++o) {
-          uint32_t b[8];
+          uint32_t mag[8], sgn[8];
           const float ks = inv[(8 * o) / 32] * k7;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) b[e] = __float_as_uint(fmaf(v[8 * o + e], ks, kMagic));
-          packed[o] = pack8(b);
+          for (int e = 0; e < 8; ++e) {
+            mag[e] = __float_as_uint(fmaf(fabsf(v[8 * o + e]), ks, kMagic));
+            sgn[e] = __float_as_uint(v[8 * o + e]);
+          }
+          packed[o] = pack8(mag, sgn);
         }
         if (row_ok) {
           uint8_t* dst = a.codes + static_cast<size_t>(row0 + rl) * (K / 2) + j0 / 2;

@@ -1,35 +1,54 @@
 // Grouped INT4 x INT4 GEMM of the RRS A4W4 linear on gfx950.
 //
 // Y[t, n] = (1/K) dx[t] dw[n] sum_g S[g] P_g[t, n],
-// P_g[t, n] = sum_{j in group g} q[t, j] qw[n, j]    (exact int32)
+// P_g[t, n] = sum_{j in group g} q[t, j] qw[n, j]    (exact integers)
 //
 // The group scale multiplies each group's integer partial before the fp32
 // accumulation: the smoothing is not migrated into the weights (RRS summary
 // page, atlas.scime.ai, "Approach"), and grouping the scales along K keeps
-// the contraction in wide integer tiles (RRS rebuttal page, paperhub.cn,
-// "Novelty": per-channel scales do not fit the hardware's tiled scheme).
+// the contraction in wide tiles (RRS rebuttal page, paperhub.cn, "Novelty":
+// per-channel scales do not fit the hardware's tiled scheme).
 //
-// gfx950 has no 4-bit integer matrix instruction, so codes are widened to
-// int8 on their way into LDS and multiplied with v_mfma_i32_16x16x64_i8
-// (v_mfma_i32_16x16x32_i8 when G = 32). The widening keeps each code in the
-// high nibble of its byte (16 q, one AND per four codes), so every product
-// carries a factor 256 that the epilogue removes exactly.
+// gfx950 has no 4-bit integer matrix instruction. Each 4-bit code widens to
+// an fp8 e4m3 subnormal, +-|q| * 2^-9, which the matrix core multiplies
+// exactly; products (+-|q_a q_b| * 2^-18) and group sums (< 2^24 units) are
+// exact in the fp32 accumulator, so the group partials are the exact
+// integers scaled by 2^-18. The packing puts each code's sign and magnitude
+// where one AND (even codes) or a rotate and an AND (odd codes) yields the
+// e4m3 byte: 3 VALU operations per 8 codes.
 //
-// Both operands are K-contiguous ("NT"): xq [M][K/2], wq [N][K/2]. Within a
-// packed 32-bit word the widening emits the even codes then the odd codes;
-// A and B are widened the same way, so the contraction pairs equal K
-// indices and each 16-byte chunk stays inside one group (G >= 32).
+// The group rescale runs inside the accumulator: after group g the MFMA
+// accumulator holds (sum_{g' <= g} S_g' P_g') / S_g, so entering group g+1
+// costs one multiply by S_g / S_{g+1} per output and the products of the
+// next group accumulate on top. No separate integer accumulator is kept.
+//
+// Tiles: 256 output channels x 128 tokens per workgroup, 4 waves of
+// 128 x 64. The MFMA A operand is the weight tile (rows n), the B operand the
+// activation tile (rows t), so a lane's four accumulators are four
+// consecutive output channels of one token: one 16-byte store per tile.
+// K advances in stages of 128 codes (64 packed bytes per row): direct
+// global -> LDS loads into 3-slot rings (two stages in flight), then
+// per-wave widening of the packed fragments -> MFMA. Two sets of 4 waves
+// split K and add their partial sums at the end.
+// v_mfma_f32_16x16x128_f8f6f4 serves G >= 128; v_mfma_f32_16x16x32_fp8_fp8
+// serves G = 32 and 64.
 
 #include "rrs_internal.h"
 
 namespace rrs {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128;
-constexpr int kBN = 128;
-constexpr int kThreads = 256;
+constexpr int kTN = 256;       // output channels per workgroup tile
+constexpr int kTT = 128;       // tokens per workgroup tile
+constexpr int kThreads = 256;  // 4 waves: 2 (n) x 2 (t), each 128 x 64
+constexpr int kRowB = 64;      // packed bytes per row per stage (128 codes)
+constexpr int kWB = kTN * kRowB;
+constexpr int kXB = kTT * kRowB;
+constexpr int kStageB = kWB + kXB;
+constexpr float kUnit = 262144.0f;  // 2^18: one integer product in accumulator units
 
 struct GemmArgs {
   const uint8_t* xq;
@@ -38,189 +57,356 @@ struct GemmArgs {
   const uint8_t* wq;
   const float* dw;
   float* Y;
-  int32_t* P;       // partials window (null: normal output)
+  int32_t* P;  // partials window (partials variant)
   int M, N, K, log2G;
   int pm0, pm1, pn0, pn1;
-  float out_scale;  // 1 / (256 K)
+  int tiles_t, tiles_n;
 };
 
-// 16 packed bytes (32 codes) -> 32 int8 bytes holding 16 * code.
-__device__ __forceinline__ void widen16(const uint4 p, uint32_t (&o)[8]) {
-  const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+// a-codes (even) and b-codes (odd) of a packed word as e4m3 subnormals
+__device__ __forceinline__ uint32_t ecodes(uint32_t w) { return w & 0x87878787u; }
+__device__ __forceinline__ uint32_t ocodes(uint32_t w) {
+  return __builtin_amdgcn_alignbit(w, w, 4) & 0x87878787u;
+}
+
+template <int KM>
+struct Mma;
+
+template <>
+struct Mma<128> {  // 32 codes (16 packed bytes) per lane
+  typedef v8i frag;
+  static constexpr int kSteps = 1;  // MFMA k-steps per stage
+  __device__ static frag load(const uint8_t* p) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    return v8i{(int)ecodes(w.x), (int)ocodes(w.x), (int)ecodes(w.y), (int)ocodes(w.y),
+               (int)ecodes(w.z), (int)ocodes(w.z), (int)ecodes(w.w), (int)ocodes(w.w)};
+  }
+  __device__ static v4f mma(frag a, frag b, v4f c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mma<32> {  // 8 codes (4 packed bytes) per lane
+  typedef long frag;
+  static constexpr int kSteps = 4;
+  __device__ static frag load(const uint8_t* p) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+    return static_cast<long>(static_cast<uint64_t>(ecodes(w)) | (static_cast<uint64_t>(ocodes(w)) << 32));
+  }
+  __device__ static v4f mma(frag a, frag b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+  }
+};
+
+// Split K: the workgroup is two sets of 4 waves over the same output tile;
+// set 0 runs the first half of K, set 1 the second, and their partial sums
+// meet in LDS at the end. Two waves per SIMD let one wave's widening and
+// rescale overlap the other's matrix instructions.
+constexpr int kSets = 2;
+constexpr int kThreadsWG = kSets * kThreads;
+
+// LDS rings, one per set, three slots each (two stages in flight). Separate
+// arrays let the compiler tell which direct-to-LDS load a fragment read
+// depends on (with one array it would wait for every load in flight).
+constexpr int kRing = 3;
+__shared__ __attribute__((aligned(1024))) uint8_t s_r00[kStageB];
+__shared__ __attribute__((aligned(1024))) uint8_t s_r01[kStageB];
+__shared__ __attribute__((aligned(1024))) uint8_t s_r02[kStageB];
+__shared__ __attribute__((aligned(1024))) uint8_t s_r10[kStageB];
+__shared__ __attribute__((aligned(1024))) uint8_t s_r11[kStageB];
+__shared__ __attribute__((aligned(1024))) uint8_t s_r12[kStageB];
+
+template <int SET, int SLOT>
+__device__ __forceinline__ uint8_t* ring() {
+  if (SET == 0) return SLOT == 0 ? s_r00 : SLOT == 1 ? s_r01 : s_r02;
+  return SLOT == 0 ? s_r10 : SLOT == 1 ? s_r11 : s_r12;
+}
+
+// 1-KiB chunk c (0 <= c < 144) of the six ring buffers, used to park the
+// second set's partial sums once the rings are idle
+__device__ __forceinline__ float* park_chunk(int c) {
+  uint8_t* b;
+  switch (c / 24) {
+    case 0: b = s_r00; break;
+    case 1: b = s_r01; break;
+    case 2: b = s_r02; break;
+    case 3: b = s_r10; break;
+    case 4: b = s_r11; break;
+    default: b = s_r12; break;
+  }
+  return reinterpret_cast<float*>(b + (c % 24) * 1024);
+}
+
+// vmcnt(n) and lgkmcnt(0), expcnt unconstrained (gfx9 s_waitcnt encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] in bits 15:14). The
+// barrier that follows then also publishes this wave's LDS stores.
+#define RRS_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0070)
+
+template <int KM, bool PARTIALS>
+struct GemmCtx {
+  using Mm = Mma<KM>;
+  static constexpr int kDmaPerWave = (kStageB / 1024) / (kThreads / 64);  // 6
+
+  const GemmArgs& a;
+  int lane, wn, wt, n0, t0, Kb, nstage, log2spg, ngroups;
+  int st0, st1;                      // this set's stage range [st0, st1)
+  const uint8_t* gsrc[kDmaPerWave];  // this lane's row pointer for each of its DMA blocks
+  int goff[kDmaPerWave];             // byte offset of its 16-byte piece
+  int lblk[kDmaPerWave];             // LDS offset of each block in a stage
+  int fW, fX;
+  v4f acc[8][4];
+  const float* rat;
+
+  __device__ GemmCtx(const GemmArgs& args, const float* s_rat) : a(args), rat(s_rat) {}
+
+  template <int SET, int SLOT>
+  __device__ __forceinline__ void issue(int st) {
+    uint8_t* base = ring<SET, SLOT>();
+    const int kb = st * kRowB;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    o[2 * i] = (w[i] << 4) & 0xf0f0f0f0u;   // even codes
-    o[2 * i + 1] = w[i] & 0xf0f0f0f0u;      // odd codes
+    for (int d = 0; d < kDmaPerWave; ++d) {
+      // a piece past the end of a row (K = 64) re-reads the row's first
+      // bytes: in bounds, and never multiplied (only K codes are used)
+      const int off = kb + goff[d] < Kb ? kb + goff[d] : goff[d] & 15;
+      __builtin_amdgcn_global_load_lds(gsrc[d] + off, (__attribute__((address_space(3))) void*)(base + lblk[d]), 16, 0, 0);
+    }
+  }
+
+  template <int SET, int SLOT>
+  __device__ __forceinline__ void compute(int st) {
+    const uint8_t* stage = ring<SET, SLOT>();
+#pragma unroll
+    for (int ks = 0; ks < Mm::kSteps; ++ks) {
+      const int step = st * Mm::kSteps + ks;
+      if (step << (KM == 128 ? 7 : 5) >= a.K) break;  // K = 64: half a stage
+      const int gs = step & ((1 << log2spg) - 1);
+      typename Mm::frag fx[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fx[j] = Mm::load(stage + fX + j * 16 * kRowB + ks * 16);
+      if (gs == 0 && step > st0 * Mm::kSteps) {
+        if (PARTIALS) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        } else {
+          const float r = rat[step >> log2spg];
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] *= r;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const typename Mm::frag fw = Mm::load(stage + fW + i * 16 * kRowB + ks * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = Mm::mma(fw, fx[j], acc[i][j]);
+      }
+      if (PARTIALS && gs == (1 << log2spg) - 1) dump(step >> log2spg);
+    }
+  }
+
+  __device__ void dump(int g) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = t0 + wt * 64 + j * 16 + (lane & 15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int n = n0 + wn * 128 + i * 16 + (lane >> 4) * 4 + e;
+          if (t >= a.pm0 && t < a.pm1 && n >= a.pn0 && n < a.pn1) {
+            const size_t o = (static_cast<size_t>(t - a.pm0) * (a.pn1 - a.pn0) + (n - a.pn0)) * ngroups + g;
+            a.P[o] = static_cast<int32_t>(acc[i][j][e] * kUnit);
+          }
+        }
+      }
+  }
+
+  // One ring revolution: stages st .. st+2 in slots 0..2; stage s+2 is
+  // fetched into the slot that stage s-1 just released. Both sets run the
+  // same number of steps (the barrier is workgroup wide) and every step
+  // issues the same number of loads (past the set's last stage it re-reads
+  // that stage into the released slot, which is never read again), so the
+  // wait is constant.
+  template <int SET, int SLOT>
+  __device__ __forceinline__ void step(int st) {
+    // this stage's blocks have landed once at most one newer stage of this
+    // wave is in flight; the barrier publishes all waves' blocks and frees
+    // the slot of stage st - 1
+    RRS_WAIT_VM(kDmaPerWave);
+    __builtin_amdgcn_s_barrier();
+    issue<SET, (SLOT + kRing - 1) % kRing>(min(st + kRing - 1, st1 - 1));
+    if (st < st1) compute<SET, SLOT>(st);
+  }
+
+  template <int SET>
+  __device__ void run(int nsteps) {
+    // prologue: the set's first two stages in flight (the first barrier also
+    // publishes the ratio table)
+    issue<SET, 0>(st0);
+    issue<SET, 1>(min(st0 + 1, st1 - 1));
+    int s = 0;
+    for (; s + kRing <= nsteps; s += kRing) {
+      step<SET, 0>(st0 + s);
+      step<SET, 1>(st0 + s + 1);
+      step<SET, 2>(st0 + s + 2);
+    }
+    if (s < nsteps) step<SET, 0>(st0 + s);
+    if (s + 1 < nsteps) step<SET, 1>(st0 + s + 1);
+    RRS_WAIT_VM(0);
+  }
+};
+
+template <int KM, bool PARTIALS>
+__global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
+  __shared__ float s_rat[(1 << kMaxLog2K) / kMinG];
+  GemmCtx<KM, PARTIALS> c(a, s_rat);
+  const int tid = threadIdx.x;
+  const int set = tid / kThreads;
+  const int stid = tid % kThreads;
+  c.lane = stid & 63;
+  const int wave = stid >> 6;
+  c.wn = wave >> 1;
+  c.wt = wave & 1;
+
+  // XCD-aware tile order: consecutive workgroup ids land on different XCDs,
+  // so give each XCD a contiguous run of the tile sequence; inside bands of
+  // 8 output tiles the token tile runs fastest (neighbours share weights).
+  const int ntiles = a.tiles_t * a.tiles_n;
+  int wg = blockIdx.x;
+  if ((ntiles & 7) == 0) wg = (wg & 7) * (ntiles >> 3) + (wg >> 3);
+  const int band = 8 * a.tiles_t;
+  const int bi = wg / band, bo = wg % band;
+  const int bn = min(8, a.tiles_n - bi * 8);
+  c.n0 = (bi * 8 + bo % bn) * kTN;
+  c.t0 = (bo / bn) * kTT;
+
+  c.Kb = a.K / 2;
+  c.nstage = (a.K + 127) / 128;
+  c.log2spg = a.log2G - (KM == 128 ? 7 : 5);
+  c.ngroups = a.K >> a.log2G;
+  // K halves (the partials dump keeps whole groups in one set)
+  const int half = PARTIALS ? c.nstage : (c.nstage + 1) / 2;
+  c.st0 = set == 0 ? 0 : half;
+  c.st1 = set == 0 ? half : c.nstage;
+  const int nsteps = half;  // both sets step in lockstep
+
+  if (!PARTIALS) {
+    // s_rat[g] = S[g-1] / S[g]: entering group g rescales the accumulator
+    for (int g = tid; g < c.ngroups; g += kThreadsWG) s_rat[g] = g > 0 ? a.S[g - 1] / a.S[g] : 1.f;
+  }
+
+  // DMA blocks of a stage: 1 KiB = 16 rows x 64 B; blocks 0..15 hold the
+  // weight rows, 16..23 the activation rows; wave w moves blocks 6w..6w+5,
+  // lane i the 16-byte piece i & 3 of row 16b + i / 4 (rows clamped to the
+  // matrix; clamped rows only feed outputs that are never stored)
+#pragma unroll
+  for (int d = 0; d < GemmCtx<KM, PARTIALS>::kDmaPerWave; ++d) {
+    const int blk = wave * GemmCtx<KM, PARTIALS>::kDmaPerWave + d;
+    const int r = (blk & 15) * 16 + (c.lane >> 2);
+    c.goff[d] = (c.lane & 3) * 16;
+    c.lblk[d] = blk * 1024;
+    if (blk < 16) {
+      const int n = min(c.n0 + r, a.N - 1);
+      c.gsrc[d] = a.wq + static_cast<size_t>(n) * c.Kb;
+    } else {
+      const int t = min(c.t0 + r, a.M - 1);
+      c.gsrc[d] = a.xq + static_cast<size_t>(t) * c.Kb;
+    }
+  }
+
+  // fragment offsets: row (lane & 15) of each 16-row tile; K bytes
+  // (lane >> 4) * 16 (KM = 128) or ks * 16 + (lane >> 4) * 4 (KM = 32)
+  const int fbyte = (KM == 128) ? (c.lane >> 4) * 16 : (c.lane >> 4) * 4;
+  c.fW = (c.wn * 128 + (c.lane & 15)) * kRowB + fbyte;
+  c.fX = kWB + (c.wt * 64 + (c.lane & 15)) * kRowB + fbyte;
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c.acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  if (set == 0) {
+    c.template run<0>(nsteps);
+  } else if (c.st1 > c.st0) {
+    c.template run<1>(nsteps);
+  } else {
+    // no second half (K <= 128 or the partials dump): keep step with set 0
+    for (int s = 0; s < nsteps; ++s) __builtin_amdgcn_s_barrier();
+  }
+  if (PARTIALS) return;
+
+  // ---- combine the halves ------------------------------------------------
+  // With two or more groups the halves meet on a group boundary (K / 2 is a
+  // multiple of G), so each half is a finished sum over whole groups: set 1
+  // parks its sum made absolute (times its last group's scale) and set 0
+  // adds its own. With one group (G = K) the two halves are integer parts of
+  // the same group partial: they are added exactly first and scaled once,
+  // so a partial that cancels to zero stays exactly zero.
+  const bool one_group = c.ngroups == 1;
+  const float s_end = a.S[((c.st1 * 128 > a.K ? a.K : c.st1 * 128) - 1) >> a.log2G];
+  __syncthreads();  // all rings idle: park set 1's 4 x 32 tiles of 1 KiB there
+  if (set == 1) {
+    const float m1 = one_group ? 1.f : s_end;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        reinterpret_cast<v4f*>(park_chunk(wave * 32 + i * 4 + j))[c.lane] =
+            c.st1 > c.st0 ? c.acc[i][j] * m1 : v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();
+  if (set == 1) return;
+  const float m0 = one_group ? 1.f : s_end;  // set 0's own last group
+  const float fin = one_group ? s_end : 1.f;
+
+  // ---- epilogue: Y[t, n..n+3] = (both halves, absolute) 2^18 / K dx[t] dw[n]
+  const float base = kUnit / static_cast<float>(a.K);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int n = c.n0 + c.wn * 128 + i * 16 + (c.lane >> 4) * 4;
+    if (n >= a.N) continue;
+    float4 dwv;
+    if (n + 3 < a.N) {
+      dwv = *reinterpret_cast<const float4*>(a.dw + n);
+    } else {
+      dwv.x = a.dw[n];
+      dwv.y = n + 1 < a.N ? a.dw[n + 1] : 0.f;
+      dwv.z = n + 2 < a.N ? a.dw[n + 2] : 0.f;
+      dwv.w = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = c.t0 + c.wt * 64 + j * 16 + (c.lane & 15);
+      if (t >= a.M) continue;
+      const float rs = a.dx[t] * base;
+      float* y = a.Y + static_cast<size_t>(t) * a.N + n;
+      const v4f v = (c.acc[i][j] * m0 + reinterpret_cast<const v4f*>(park_chunk(wave * 32 + i * 4 + j))[c.lane]) * fin;
+      const float v0 = v[0] * rs * dwv.x, v1 = v[1] * rs * dwv.y;
+      const float v2 = v[2] * rs * dwv.z, v3 = v[3] * rs * dwv.w;
+      if (n + 3 < a.N && (a.N & 3) == 0) {
+        *reinterpret_cast<float4*>(y) = make_float4(v0, v1, v2, v3);
+      } else {
+        y[0] = v0;
+        if (n + 1 < a.N) y[1] = v1;
+        if (n + 2 < a.N) y[2] = v2;
+        if (n + 3 < a.N) y[3] = v3;
+      }
+    }
   }
 }
 
-template <int KS>
-struct Step;
-template <>
-struct Step<64> {  // 16x16x64 i8: 16 bytes of K per lane
-  static constexpr int kPackedRowBytes = 32;
-  typedef v4i frag;
-  __device__ static v4i mma(v4i a, v4i b, v4i c) {
-    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
-  }
-};
-template <>
-struct Step<32> {  // 16x16x32 i8: 8 bytes of K per lane
-  static constexpr int kPackedRowBytes = 16;
-  typedef long frag;
-  __device__ static v4i mma(long a, long b, v4i c) {
-    return __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, c, 0, 0, 0);
-  }
-};
-
-template <int KS>
-__global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs a) {
-  using St = Step<KS>;
-  constexpr int ROWB = KS + 16;  // LDS row stride (bytes): widened step + pad
-  constexpr int PRB = St::kPackedRowBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][kBM * ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][kBN * ROWB];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * kBM;
-  const int n0 = blockIdx.x * kBN;
-  const int Kb = a.K / 2;  // packed bytes per row
-  const int nsteps = a.K / KS;
-  const int steps_per_group = (1 << a.log2G) / KS;
-
-  // global -> register staging: each thread moves PRB/2 packed bytes of one
-  // A row and of one B row per step (KS=64: 16 B; KS=32: 8 B)
-  const int ld_row = tid >> 1;
-  const int ld_off = (tid & 1) * (PRB / 2);
-  const bool a_ok = m0 + ld_row < a.M;
-  const bool b_ok = n0 + ld_row < a.N;
-  const uint8_t* gA = a.xq + static_cast<size_t>(m0 + ld_row) * Kb + ld_off;
-  const uint8_t* gB = a.wq + static_cast<size_t>(n0 + ld_row) * Kb + ld_off;
-
-  auto load = [&](int step, uint4& ra, uint4& rb) {
-    ra = make_uint4(0, 0, 0, 0);
-    rb = make_uint4(0, 0, 0, 0);
-    const int kb = step * PRB;
-    if constexpr (KS == 64) {
-      if (a_ok) ra = *reinterpret_cast<const uint4*>(gA + kb);
-      if (b_ok) rb = *reinterpret_cast<const uint4*>(gB + kb);
-    } else {
-      if (a_ok) { const uint2 t = *reinterpret_cast<const uint2*>(gA + kb); ra.x = t.x; ra.y = t.y; }
-      if (b_ok) { const uint2 t = *reinterpret_cast<const uint2*>(gB + kb); rb.x = t.x; rb.y = t.y; }
-    }
-  };
-  auto store = [&](int buf, const uint4& ra, const uint4& rb) {
-    uint32_t oa[8], ob[8];
-    widen16(ra, oa);
-    widen16(rb, ob);
-    uint8_t* pa = &sA[buf][ld_row * ROWB + ld_off * 2];
-    uint8_t* pb = &sB[buf][ld_row * ROWB + ld_off * 2];
-    if constexpr (KS == 64) {
-      reinterpret_cast<uint4*>(pa)[0] = make_uint4(oa[0], oa[1], oa[2], oa[3]);
-      reinterpret_cast<uint4*>(pa)[1] = make_uint4(oa[4], oa[5], oa[6], oa[7]);
-      reinterpret_cast<uint4*>(pb)[0] = make_uint4(ob[0], ob[1], ob[2], ob[3]);
-      reinterpret_cast<uint4*>(pb)[1] = make_uint4(ob[4], ob[5], ob[6], ob[7]);
-    } else {
-      reinterpret_cast<uint4*>(pa)[0] = make_uint4(oa[0], oa[1], oa[2], oa[3]);
-      reinterpret_cast<uint4*>(pb)[0] = make_uint4(ob[0], ob[1], ob[2], ob[3]);
-    }
-  };
-
-  v4i acc[4][4];
-  float accf[4][4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[i][j] = v4i{0, 0, 0, 0};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) accf[i][j][e] = 0.f;
-    }
-
-  uint4 ra, rb;
-  load(0, ra, rb);
-  store(0, ra, rb);
-  __syncthreads();
-
-  // MFMA operand addresses: lane -> row/col (lane & 15), K bytes
-  // (lane >> 4) * (KS / 4)
-  const int fr = lane & 15;
-  const int fk = (lane >> 4) * (KS / 4);
-
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    const bool more = step + 1 < nsteps;
-    if (more) load(step + 1, ra, rb);
-
-    typename St::frag fa[4], fb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa[i] = *reinterpret_cast<const typename St::frag*>(&sA[buf][(wm * 64 + i * 16 + fr) * ROWB + fk]);
-      fb[i] = *reinterpret_cast<const typename St::frag*>(&sB[buf][(wn * 64 + i * 16 + fr) * ROWB + fk]);
-    }
-    const int gs = step % steps_per_group;
-    if (gs == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = St::mma(fa[i], fb[j], v4i{0, 0, 0, 0});
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = St::mma(fa[i], fb[j], acc[i][j]);
-    }
-
-    if (gs == steps_per_group - 1) {
-      const int g = step / steps_per_group;
-      if (a.P == nullptr) {
-        const float sg = a.S[g];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) accf[i][j][e] = fmaf(sg, static_cast<float>(acc[i][j][e]), accf[i][j][e]);
-      } else {
-        const int ng = a.K >> a.log2G;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int row = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
-              const int col = n0 + wn * 64 + j * 16 + (lane & 15);
-              if (row >= a.pm0 && row < a.pm1 && col >= a.pn0 && col < a.pn1) {
-                const size_t o = (static_cast<size_t>(row - a.pm0) * (a.pn1 - a.pn0) + (col - a.pn0)) * ng + g;
-                a.P[o] = acc[i][j][e] >> 8;
-              }
-            }
-      }
-    }
-
-    if (more) store(buf ^ 1, ra, rb);
-    __syncthreads();
-  }
-
-  if (a.P != nullptr) return;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
-      if (row >= a.M) continue;
-      const float rs = a.dx[row] * a.out_scale;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 64 + j * 16 + (lane & 15);
-        if (col < a.N) a.Y[static_cast<size_t>(row) * a.N + col] = accf[i][j][e] * rs * a.dw[col];
-      }
-    }
-  }
+template <int KM>
+hipError_t launch_km(const GemmArgs& a, bool partials, hipStream_t s) {
+  const dim3 grid(a.tiles_t * a.tiles_n);
+  if (partials)
+    hipLaunchKernelGGL((gemm_kernel<KM, true>), grid, dim3(kThreadsWG), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<KM, false>), grid, dim3(kThreadsWG), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -241,18 +427,11 @@ hipError_t launch_gemm(const uint8_t* xq, const float* dx, const float* S, int M
   a.K = 1 << log2K;
   a.log2G = __builtin_ctz(static_cast<unsigned>(G));
   a.pm0 = m0; a.pm1 = m1; a.pn0 = n0; a.pn1 = n1;
-  a.out_scale = 1.0f / (256.0f * static_cast<float>(a.K));
   if (M == 0 || N == 0) return hipSuccess;
-  dim3 grid((N + kBN - 1) / kBN, (M + kBM - 1) / kBM);
-  if (P != nullptr) {
-    // only the tiles that cover the window
-    grid = dim3((n1 - 1) / kBN + 1, (m1 - 1) / kBM + 1);
-  }
-  if (G == 32)
-    hipLaunchKernelGGL(gemm_kernel<32>, grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(gemm_kernel<64>, grid, dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  a.tiles_t = (M + kTT - 1) / kTT;
+  a.tiles_n = (N + kTN - 1) / kTN;
+  const bool partials = P != nullptr;
+  return G >= 128 ? launch_km<128>(a, partials, s) : launch_km<32>(a, partials, s);
 }
 
 }  // namespace rrs

@@ -250,3 +250,22 @@ def test_scale_match_statistic():
     t = np.zeros(16)
     t[0] = 4.0
     assert oracle.scale_match_u(t) == 4.0
+
+
+def test_pack_layout_feeds_fp8_subnormals():
+    """The packing reading R10 is chosen so that, per 32-bit word, w & 0x87878787
+    and rotr(w, 4) & 0x87878787 are the even and odd codes as sign-magnitude
+    bytes (fp8 e4m3 subnormals +-|q| * 2^-9); checked on every code pair."""
+    g = np.random.default_rng(12)
+    q = g.integers(-7, 8, size=(64, 8)).astype(np.int8)
+    b = oracle.pack_codes(q)
+    w = b.view("<u4")[:, 0].astype(np.uint64)
+    lo = w & 0x87878787
+    hi = (((w >> 4) | (w << 28)) & 0xFFFFFFFF) & 0x87878787
+
+    def dec(x, j):
+        byte = (x >> (8 * j)) & 0xFF
+        return np.where(byte & 0x80, -(byte & 7).astype(np.int64), (byte & 7).astype(np.int64))
+    for j in range(4):
+        assert np.array_equal(dec(lo, j), q[:, 2 * j])
+        assert np.array_equal(dec(hi, j), q[:, 2 * j + 1])

@@ -105,3 +105,13 @@ def test_swapped_nibbles_fail():
         q = np.asarray(q).astype(np.int16)
         return ((q[..., 1::2] & 0xF) | ((q[..., 0::2] & 0xF) << 4)).astype(np.uint8)
     assert not pins.pack_matches_golden(pack_swapped)
+
+
+def test_odd_sign_in_own_byte_fails():
+    def pack_no_roll(q):
+        q = np.asarray(q).astype(np.int16)
+        w = q.reshape(q.shape[:-1] + (q.shape[-1] // 8, 4, 2))
+        a, b = w[..., 0], w[..., 1]
+        byte = np.abs(a) | (np.abs(b) << 4) | ((a < 0) << 7) | ((b < 0) << 3)
+        return byte.reshape(q.shape[:-1] + (q.shape[-1] // 2,)).astype(np.uint8)
+    assert not pins.pack_matches_golden(pack_no_roll)
