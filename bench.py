@@ -8,9 +8,16 @@ LLaMA-3-8B o_proj prefill shape, M=2048 tokens, K=N=4096, G=128.
 
 Prints one JSON line: effective int TOPS of the whole layer (2MNK per step),
 the front end's GB/s, a roofline object for the dominant kernel (the GEMM,
-against the int8 MFMA peak) and one for the front end (against HBM peak),
-each kernel timed alone with HIP events on the stream it runs on, and the
-CPU oracle timed on the host as a reported baseline.
+whose int4 x int4 products run on fp8 matrix cores, against the dense fp8
+peak, which equals the dense int8 peak) and one for the front end (against
+HBM peak), each kernel timed alone with HIP events on the stream it runs on,
+and the CPU oracle timed on the host as a reported baseline.
+
+HBM traffic per launch ("traffic") comes from rocprofv3 FETCH_SIZE and
+WRITE_SIZE counter runs recorded in profiles/traffic.txt, scaled by the
+same counters read for a plain copy of known size (``--copy-probe``); it is
+reported only while the kernel's source file still hashes to the value the
+counters were taken with, else null.
 
 To keep the 256 MB Infinity Cache from serving repeated inputs, the timed
 loops rotate over enough independent input/weight/output sets to exceed it.
@@ -28,7 +35,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_I8_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_MFMA_TOPS = 5000.0      # MI355X dense fp8 (and int8) MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 MALL_BYTES = 256 << 20
 
@@ -43,7 +50,48 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-gemm-only", action="store_true",
                     help="run only the GEMM loop (for counter collection)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB a few times "
+                         "(reference dispatch for scaling HBM counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
+CSRC = os.path.join(ROOT, "rotated_runtime_activation_amd", "csrc")
+
+
+def source_hash(name):
+    import hashlib
+    with open(os.path.join(CSRC, name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(kernel, source, workload):
+    """Bytes per launch (fetch + write) recorded for this kernel and workload
+    with the current source, or None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    sha = source_hash(source)
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) == 6 and parts[0] == kernel and parts[1] == workload and parts[2] == sha:
+                return {"fetch_bytes": int(parts[3]), "write_bytes": int(parts[4]),
+                        "bytes": int(parts[3]) + int(parts[4]), "copy_scale": float(parts[5]),
+                        "source": f"{source}@{sha}"}
+    return None
+
+
+def copy_probe(mib):
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
 
 
 def main():
@@ -53,6 +101,10 @@ def main():
               "(the layer shards by output channels with no exchange, see the design notes)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     import torch
     import rotated_runtime_activation_amd as rra
@@ -136,6 +188,7 @@ def main():
     gemm_tops = ops / (ms_gemm * 1e-3) / 1e12
     fe_bytes = 2 * M * K + M * K // 2 + 4 * M + 4 * (K // G)
     fe_gbs = fe_bytes / (ms_fe * 1e-3) / 1e9
+    gemm_bytes = M * K // 2 + K * N // 2 + 4 * (M + N) + 4 * (K // G) + 4 * M * N
 
     out = {
         "metric": "rrs_linear effective int TOPS + front-end GB/s at M=2048,K=N=4096,G=128",
@@ -148,7 +201,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8",
+        "dtype": "fp8",
         "data": "synthetic (seeded outlier recipe; stands in for WikiText-2 / QA activations)",
         "config": {"workload": wl.name, "M": M, "K": K, "N": N, "G": G, "input_sets": nsets},
         "frontend_gbs": round(fe_gbs, 2),
@@ -157,11 +210,13 @@ def main():
             "kernel": "rrs_a4w4_gemm",
             "bound": "mfma",
             "achieved": round(gemm_tops, 3),
-            "peak": PEAK_I8_TOPS,
+            "peak": PEAK_MFMA_TOPS,
             "unit": "TFLOP/s",
-            "op_kind": "int8 MFMA ops (multiply-add = 2), against the dense int8 peak 5.0 POP/s",
-            "frac": round(gemm_tops / PEAK_I8_TOPS, 4),
-            "traffic": None,
+            "op_kind": "2MNK ops of int4 codes on fp8 e4m3 MFMA (exact), against the dense fp8 peak 5.0 PFLOP/s",
+            "frac": round(gemm_tops / PEAK_MFMA_TOPS, 4),
+            "traffic": (recorded_traffic("gemm", "rrs_gemm.hip", wl.name) or {}).get("bytes"),
+            "traffic_detail": recorded_traffic("gemm", "rrs_gemm.hip", wl.name),
+            "algorithmic_bytes": gemm_bytes,
             "ms_per_launch": round(ms_gemm, 5),
         },
         "roofline_frontend": {
@@ -171,7 +226,8 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(fe_gbs / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": (recorded_traffic("frontend", "rrs_frontend.hip", wl.name) or {}).get("bytes"),
+            "traffic_detail": recorded_traffic("frontend", "rrs_frontend.hip", wl.name),
             "algorithmic_bytes": fe_bytes,
             "ms_per_call": round(ms_fe, 5),
         },
@@ -184,25 +240,37 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(x, w, xc, G):
-    """The CPU oracle as it stands, on the host cores: one full layer step
+def cpu_baseline(x, w, xc, G, budget_s=10.0):
+    """The CPU oracle as it stands, on the host cores: full layer steps
     (front end of all tokens + the grouped GEMM output), weights prepared
-    beforehand as on the GPU side. Reported for context only."""
+    beforehand as on the GPU side, repeated until about ``budget_s`` seconds
+    of CPU work. Reported for context only."""
     import oracle
     perm = oracle.calibrate_perm(xc)
     wp = oracle.prepare_weights(w, perm)
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas = 1
+    reps = 0
     t0 = time.perf_counter()
-    fe = oracle.frontend(x, perm, G)
-    oracle.linear_out(fe["q"], fe["dx"], fe["S"], wp["qw"], wp["dw"], G)
-    dt = time.perf_counter() - t0
+    while True:
+        fe = oracle.frontend(x, perm, G)
+        oracle.linear_out(fe["q"], fe["dx"], fe["S"], wp["qw"], wp["dw"], G)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / reps
     M, K = x.shape
     N = w.shape[1]
     return {
         "value": round(2.0 * M * N * K / dt / 1e12, 6),
         "unit": "TOPS",
-        "cores": len(os.sched_getaffinity(0)),
+        "cores": blas,
         "kind": "oracle",
-        "sample": f"one full step (M={M}, K={K}, N={N}, G={G}) in float64 NumPy: {dt:.2f} s",
+        "sample": (f"{reps} full steps of the same workload (M={M}, K={K}, N={N}, G={G}) in float64 "
+                   f"NumPy, {dt:.2f} s each; front end single-threaded, group GEMMs on {blas} BLAS threads"),
     }
 
 
