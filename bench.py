@@ -183,6 +183,7 @@ def main():
     ms_fe, _ = timed(fe_step, args.steps, args.warmup)
     ms_gemm, _ = timed(gemm_step, args.steps, args.warmup)
 
+    fe_launches = rra.rrs_frontend_passes(M, K, 0)
     ops = 2.0 * M * N * K
     tops = ops / (ms_step * 1e-3) / 1e12
     gemm_tops = ops / (ms_gemm * 1e-3) / 1e12
@@ -220,7 +221,9 @@ def main():
             "ms_per_launch": round(ms_gemm, 5),
         },
         "roofline_frontend": {
-            "kernel": "rrs_fwht_colmax + rrs_smooth_quant_pack",
+            "kernel": ("fused_kernel (rotate, reorder, group max, grid-wide wait, quantise, pack)"
+                       if fe_launches == 1 else "frontend_kernel stats pass + quantise pass"),
+            "launches": fe_launches,
             "bound": "hbm",
             "achieved": round(fe_gbs, 2),
             "peak": PEAK_HBM_GBS,

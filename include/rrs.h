@@ -82,17 +82,22 @@ const char* rrs_version(void);
  * an invalid shape. */
 size_t rrs_weight_bytes(int K, int N);
 
-/* Bytes of the workspace that rrs_linear needs for M tokens: a small
- * synchronisation block, then xq [M][K/2], dx [M] and S [K/G], each 256-byte
- * aligned. rrs_frontend needs only rrs_sync_bytes(K, G) of it. Returns 0 for
- * an invalid shape. */
+/* Bytes of the workspace that rrs_linear needs for M tokens: a
+ * synchronisation block (rrs_sync_bytes(K, G): control words, per-workgroup
+ * arrival flags and a row of K/G group maxima for each of up to 512
+ * workgroups), then xq [M][K/2], dx [M] and S [K/G], each 256-byte aligned.
+ * rrs_frontend needs only the synchronisation block. Returns 0 for an
+ * invalid shape. */
 size_t rrs_workspace_bytes(int M, int K, int G);
 size_t rrs_sync_bytes(int K, int G);
 
-/* Zero the synchronisation block at the start of `ws` (a fill kernel on `s`;
- * no hipMemset, so it is safe under stream capture). Call once for a fresh
- * workspace before its first use; every later call leaves the block zeroed.
- * Two calls that share one workspace must not overlap in time. */
+/* Initialise the synchronisation block at the start of `ws` (zeroes its
+ * first 3328 bytes, or all of `ws` if smaller, with a fill kernel on `s`; no
+ * hipMemset, so it is safe under stream capture). Call once for a fresh
+ * workspace before its first use; every later call leaves the block ready
+ * for the next one (the one-launch front end counts calls in it instead of
+ * clearing it). Two calls that share one workspace must not overlap in
+ * time. */
 int rrs_workspace_init(void* ws, size_t ws_bytes, hipStream_t s);
 
 /* Calibration reorder (RRS rebuttal page, "Novelty": reorder collects outlier
@@ -128,12 +133,32 @@ int rrs_linear(const void* X_fp16, int M, int K, int N, int G,
  * rrs_workspace_init. `flags` selects the ablations of the RRS rebuttal page
  * ("Incomplete ablation study"): RRS_FLAG_NO_ROTATE skips the rotation
  * (Runtime Smooth alone), RRS_FLAG_NO_SMOOTH forces S = 1 (rotation alone);
- * 0 is the full method. */
+ * 0 is the full method. RRS_FLAG_TWO_PASS changes no result: it makes the
+ * smoothed front end use two launches (group maxima, then quantise,
+ * reading X twice), the form rrs_linear falls back to when the one-launch
+ * form does not fit on the device at once.
+ *
+ * The one-launch form keeps every rotated row on chip while the workgroups
+ * combine their group maxima, so all its workgroups must be resident
+ * together; rrs_linear and rrs_frontend check that against the device's
+ * occupancy before choosing it. Its wait is bounded: if the workgroups never
+ * all arrive (for example when another such call on another stream holds
+ * part of the device), the kernel still ends, with wrong codes, and sets
+ * word 2 of the workspace (the error word) to nonzero; the word stays set
+ * until rrs_workspace_init. */
 #define RRS_FLAG_NO_ROTATE 1
 #define RRS_FLAG_NO_SMOOTH 2
+#define RRS_FLAG_TWO_PASS 4
 int rrs_frontend(const void* X_fp16, int M, int K, int G, const int32_t* perm,
                  uint8_t* xq, float* dx, float* S, void* ws, size_t ws_bytes,
                  int flags, hipStream_t s);
+
+/* Number of launches (1 or 2) the front end of rrs_linear / rrs_frontend
+ * uses for M tokens of length K with these flags on the current device:
+ * 1 when the one-launch form fits on the device at once (or without
+ * smoothing), 2 otherwise. A host-side query; RRS_EINVAL for bad arguments,
+ * RRS_EHIP if the device cannot be queried. */
+int rrs_frontend_passes(int M, int K, int flags);
 
 /* Grouped integer GEMM alone (same kernel as rrs_linear): Y = (1/K) dx dw
  * sum_g S_g P_g with P_g the int32 group partials of the 4-bit codes. */

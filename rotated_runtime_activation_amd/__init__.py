@@ -19,13 +19,14 @@ LIB_PATH = os.path.join(PKG, "lib", "librrs.so")
 RRS_OK, RRS_EINVAL, RRS_EUNSUPPORTED, RRS_EHIP = 0, -1, -2, -3
 RRS_FLAG_NO_ROTATE = 1
 RRS_FLAG_NO_SMOOTH = 2
+RRS_FLAG_TWO_PASS = 4
 
 # every symbol include/rrs.h declares
 EXPORTS = (
     "rrs_status_string", "rrs_version", "rrs_weight_bytes", "rrs_workspace_bytes",
     "rrs_sync_bytes", "rrs_workspace_init", "rrs_calibrate_workspace_bytes",
     "rrs_calibrate_perm", "rrs_prepare_weights", "rrs_linear", "rrs_frontend", "rrs_gemm",
-    "rrs_gemm_partials",
+    "rrs_gemm_partials", "rrs_frontend_passes",
 )
 
 
@@ -58,6 +59,7 @@ def _declare(lib):
         "rrs_frontend": (i, [vp, i, i, i, vp, vp, vp, vp, vp, sz, i, vp]),
         "rrs_gemm": (i, [vp, vp, vp, i, i, i, i, vp, vp, vp]),
         "rrs_gemm_partials": (i, [vp, i, i, i, i, vp, i, i, i, i, vp, vp]),
+        "rrs_frontend_passes": (i, [i, i, i]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -97,6 +99,14 @@ def rrs_sync_bytes(K: int, G: int) -> int:
 
 def rrs_calibrate_workspace_bytes(K: int) -> int:
     return int(lib().rrs_calibrate_workspace_bytes(K))
+
+
+def rrs_frontend_passes(M: int, K: int, flags: int = 0) -> int:
+    """Launches (1 or 2) the front end uses for M tokens on the current device."""
+    n = int(lib().rrs_frontend_passes(M, K, flags))
+    if n < 0:
+        _check("rrs_frontend_passes", n)
+    return n
 
 
 def rrs_status_string(status: int) -> str:
@@ -219,8 +229,7 @@ def workspace_views(ws, M: int, K: int, G: int):
     """(xq [M, K/2], dx [M], S [K/G]) views into an rrs_linear workspace."""
     torch = _torch()
     a = lambda x: (x + 255) // 256 * 256
-    sync = a(4 * (64 + K // G))
-    xq_off = sync
+    xq_off = rrs_sync_bytes(K, G)
     dx_off = xq_off + a(M * (K // 2))
     s_off = dx_off + a(4 * M)
     return (ws[xq_off: xq_off + M * (K // 2)].view(M, K // 2),

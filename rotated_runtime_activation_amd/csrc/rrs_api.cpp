@@ -19,11 +19,12 @@ bool valid_K(int K) {
 }
 bool valid_G(int G, int K) { return pow2(G) && G >= rrs::kMinG && G <= K; }
 
-// Largest synchronisation block over all legal (K, G): 64 + 8192/32 words.
-constexpr size_t kMaxSyncBytes = sizeof(uint32_t) * (rrs::kSyncGroups + (1 << rrs::kMaxLog2K) / rrs::kMinG);
+// Words of the synchronisation block that must start at zero (all control
+// words, the two-launch maxima and the one-launch flags).
+constexpr size_t kInitSyncBytes = sizeof(uint32_t) * rrs::kSyncPartials;
 
 size_t sync_bytes(int K, int G) {
-  return align256(sizeof(uint32_t) * (rrs::kSyncGroups + K / G));
+  return align256(sizeof(uint32_t) * (rrs::kSyncPartials + static_cast<size_t>(rrs::kMaxFusedWG) * (K / G)));
 }
 
 struct WsLayout {
@@ -78,7 +79,7 @@ RRS_API size_t rrs_calibrate_workspace_bytes(int K) {
 
 RRS_API int rrs_workspace_init(void* ws, size_t ws_bytes, hipStream_t s) {
   if (ws == nullptr || ws_bytes < 256 || ws_bytes % 4) return RRS_EINVAL;
-  const size_t n = (ws_bytes < kMaxSyncBytes ? ws_bytes : kMaxSyncBytes) / sizeof(uint32_t);
+  const size_t n = (ws_bytes < kInitSyncBytes ? ws_bytes : kInitSyncBytes) / sizeof(uint32_t);
   return hip_status(rrs::launch_zero_u32(static_cast<uint32_t*>(ws), n, s));
 }
 
@@ -104,13 +105,20 @@ RRS_API int rrs_prepare_weights(const void* W_fp16, int K, int N, const int32_t*
 RRS_API int rrs_frontend(const void* X_fp16, int M, int K, int G, const int32_t* perm, uint8_t* xq,
                          float* dx, float* S, void* ws, size_t ws_bytes, int flags, hipStream_t s) {
   if (M < 0 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;
-  if (flags & ~(RRS_FLAG_NO_ROTATE | RRS_FLAG_NO_SMOOTH)) return RRS_EINVAL;
+  if (flags & ~(RRS_FLAG_NO_ROTATE | RRS_FLAG_NO_SMOOTH | RRS_FLAG_TWO_PASS)) return RRS_EINVAL;
   if (perm == nullptr || S == nullptr || ws == nullptr) return RRS_EINVAL;
   if (M > 0 && (X_fp16 == nullptr || xq == nullptr || dx == nullptr)) return RRS_EINVAL;
   if (ws_bytes < sync_bytes(K, G)) return RRS_EINVAL;
   if (M == 0) return RRS_OK;
   return hip_status(rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, ilog2(K), G, perm, xq,
                                          dx, S, static_cast<uint32_t*>(ws), flags, s));
+}
+
+RRS_API int rrs_frontend_passes(int M, int K, int flags) {
+  if (M < 1 || !valid_K(K)) return RRS_EINVAL;
+  if (flags & ~(RRS_FLAG_NO_ROTATE | RRS_FLAG_NO_SMOOTH | RRS_FLAG_TWO_PASS)) return RRS_EINVAL;
+  const int n = rrs::frontend_launches(M, ilog2(K), flags);
+  return n > 0 ? n : RRS_EHIP;
 }
 
 RRS_API int rrs_gemm(const uint8_t* xq, const float* dx, const float* S, int M, int K, int N, int G,

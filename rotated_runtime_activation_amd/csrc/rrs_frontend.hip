@@ -24,8 +24,17 @@
 // The Sylvester transform is unnormalised (sums and differences only); the
 // exact 1/K of the normalised pair is applied once in the GEMM epilogue and
 // cancels out of the codes.
+//
+// The group scales need every token of the call before any token can be
+// quantised. The one-launch form (fused_kernel) keeps each wave's rotated,
+// reordered rows in registers across one grid-wide wait on the group
+// maxima, so X is read from memory once; it is used whenever all its
+// workgroups fit on the device together. Otherwise a stats launch and a
+// quantise launch each rotate the rows (X is read twice).
 
 #include "rrs_internal.h"
+
+#include <atomic>
 
 namespace rrs {
 namespace {
@@ -121,45 +130,230 @@ __device__ __forceinline__ uint32_t pack8(const uint32_t* mag, const uint32_t* s
   return ma | (mb << 4) | (sa & 0x80808080u) | ((sb >> 4) & 0x08080808u);
 }
 
+// ---------------------------------------------------------------- row steps
+// The steps below work on one wavefront's block of B = max(K, 4096)
+// elements: lane L holds E = B/64 values in v[].
+
+// s_tab[gpos(l, r)] = gather-buffer address of the element that lane l,
+// register r needs after the reorder: position p = E*l + r of the block, row
+// p / K, reordered column p % K, source channel perm[p % K].
+template <int LOG2K, bool ROTATE>
+__device__ __forceinline__ void build_table(uint32_t* s_tab, const int32_t* perm, int tid, int nthreads) {
+  using C = Cfg<LOG2K>;
+  constexpr int K = 1 << LOG2K;
+  for (int idx = tid; idx < C::kB; idx += nthreads) {
+    const int c4 = idx >> 8, l = (idx >> 2) & 63, rr = idx & 3;
+    const int p = C::kE * l + (c4 << 2) + rr;
+    const int f = ((p >> LOG2K) << LOG2K) | perm[p & (K - 1)];
+    int sl, sr;
+    if (ROTATE) {
+      sl = (f & 7) | (((f >> 9) & 7) << 3);
+      sr = ((f >> 3) & 63) | ((f >> 12) << 6);
+    } else {
+      sl = (f >> 3) & 63;
+      sr = (f & 7) | ((f >> 9) << 3);
+    }
+    s_tab[idx] = static_cast<uint32_t>(gpos(sl, sr));
+  }
+}
+
+// fp16 words of a block of activation rows X [rows][K]: element
+// f = 8L + 512i + e of the block lands in word w[i], half e. Rows past the
+// last read as zero.
+template <int LOG2K>
+__device__ __forceinline__ void load_block(uint4 (&w)[Cfg<LOG2K>::kChunks], const uint16_t* src, int rows,
+                                           int row0, int lane) {
+  constexpr int K = 1 << LOG2K;
+#pragma unroll
+  for (int i = 0; i < Cfg<LOG2K>::kChunks; ++i) {
+    const int f0 = 8 * lane + 512 * i;
+    if (row0 + (f0 >> LOG2K) < rows)
+      w[i] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(row0) * K + f0);
+    else
+      w[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+template <int LOG2K>
+__device__ __forceinline__ void widen_block(float (&v)[Cfg<LOG2K>::kE], const uint4 (&w)[Cfg<LOG2K>::kChunks]) {
+#pragma unroll
+  for (int i = 0; i < Cfg<LOG2K>::kChunks; ++i) {
+    const uint32_t q[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[8 * i + 2 * e] = h2f(q[e] & 0xffffu);
+      v[8 * i + 2 * e + 1] = h2f(q[e] >> 16);
+    }
+  }
+}
+
+// Sylvester rotation of every row of the block (unnormalised): phase 1 over
+// the register-index bits of f (bits 0-2 and 9..), a padded LDS transpose,
+// phase 2 over f bits 3-8. Leaves element f in lane (f & 7) | ((f >> 9) & 7)
+// << 3, register ((f >> 3) & 63) | (f >> 12) << 6.
+template <int LOG2K>
+__device__ __forceinline__ void rotate_block(float (&v)[Cfg<LOG2K>::kE], float* wb, int lane) {
+  using C = Cfg<LOG2K>;
+  constexpr int E = C::kE;
+#pragma unroll
+  for (int rb = 0; rb < C::kLog2E; ++rb) {
+    const int fb = rb < 3 ? rb : rb + 6;
+    if (fb < LOG2K) butterfly<E>(v, 1 << rb);
+  }
+#pragma unroll
+  for (int i = 0; i < C::kChunks; ++i) {
+    const int t = tpos(8 * lane + 512 * i);
+    *reinterpret_cast<float4*>(wb + t) = make_float4(v[8 * i], v[8 * i + 1], v[8 * i + 2], v[8 * i + 3]);
+    *reinterpret_cast<float4*>(wb + t + 4) = make_float4(v[8 * i + 4], v[8 * i + 5], v[8 * i + 6], v[8 * i + 7]);
+  }
+  lds_fence();
+  {
+    const int base = (lane & 7) + (lane >> 3) * (512 + 8);
+#pragma unroll
+    for (int r = 0; r < E; ++r) v[r] = wb[base + 8 * (r & 63) + (4096 + 64) * (r >> 6)];
+  }
+  lds_fence();
+#pragma unroll
+  for (int rb = 0; rb < 6; ++rb) {
+    if (rb + 3 < LOG2K) butterfly<E>(v, 1 << rb);
+  }
+}
+
+// Reorder: scatter the registers to LDS, gather the reordered positions
+// through the table. Afterwards v[r] is position p = E*lane + r of the block.
+template <int LOG2K>
+__device__ __forceinline__ void reorder_block(float (&v)[Cfg<LOG2K>::kE], float* wb, const uint32_t* s_tab,
+                                              int lane) {
+  constexpr int E = Cfg<LOG2K>::kE;
+#pragma unroll
+  for (int c = 0; c < E / 4; ++c)
+    *reinterpret_cast<float4*>(wb + gpos(lane, 4 * c)) = make_float4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
+  lds_fence();
+#pragma unroll
+  for (int c = 0; c < E / 4; ++c) {
+    const uint4 ad = reinterpret_cast<const uint4*>(s_tab)[c * 64 + lane];
+    v[4 * c] = wb[ad.x];
+    v[4 * c + 1] = wb[ad.y];
+    v[4 * c + 2] = wb[ad.z];
+    v[4 * c + 3] = wb[ad.w];
+  }
+  lds_fence();
+}
+
+// Per-lane |max| of each 32-wide sub-segment, merged so that m[s] is the
+// max over the whole group (of the lane's row) the sub-segment belongs to.
+template <int LOG2K>
+__device__ __forceinline__ void group_max(const float (&v)[Cfg<LOG2K>::kE], float (&m)[Cfg<LOG2K>::kE / 32],
+                                          int G) {
+  constexpr int E = Cfg<LOG2K>::kE, NS = E / 32;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    float x = fabsf(v[32 * s]);
+#pragma unroll
+    for (int r = 1; r < 32; ++r) x = fmaxf(x, fabsf(v[32 * s + r]));
+    m[s] = x;
+  }
+#pragma unroll
+  for (int st = 1; st < NS; st <<= 1) {
+    if (G > 32 * st) {
+      float t[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) t[s] = fmaxf(m[s], m[s ^ st]);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) m[s] = t[s];
+    }
+  }
+  for (int d = 1; d * E < G; d <<= 1) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) m[s] = fmaxf(m[s], __shfl_xor(m[s], d));
+  }
+}
+
+// Fold the block's per-row group maxima into the workgroup's LDS maxima.
+template <int LOG2K>
+__device__ __forceinline__ void fold_group_max(const float (&m)[Cfg<LOG2K>::kE / 32], float* s_grp, int log2G,
+                                               int rows, int row0, int lane) {
+  constexpr int K = 1 << LOG2K, E = Cfg<LOG2K>::kE;
+  const int rl = (E * lane) >> LOG2K;
+  const int j0 = (E * lane) & (K - 1);
+  const int G = 1 << log2G;
+#pragma unroll
+  for (int s = 0; s < E / 32; ++s) {
+    const int j = j0 + 32 * s;
+    if (row0 + rl < rows && (j & (G - 1)) == 0 && m[s] > 0.f)
+      atomicMax(reinterpret_cast<uint32_t*>(&s_grp[j >> log2G]), __float_as_uint(m[s]));
+  }
+}
+
+// Per-token scale, codes and packing of one block. s_inv[g] = 1 / S_g (or
+// 1 without smoothing). Writes codes [rows][K/2] and scale[row] = r / 7.
+template <int LOG2K>
+__device__ __forceinline__ void quantise_block(const float (&v)[Cfg<LOG2K>::kE],
+                                               const float (&m)[Cfg<LOG2K>::kE / 32], const float* s_inv,
+                                               int log2G, uint8_t* codes, float* scale, int rows, int row0,
+                                               int lane) {
+  constexpr int K = 1 << LOG2K, E = Cfg<LOG2K>::kE, NS = E / 32;
+  const int rl = (E * lane) >> LOG2K;
+  const int j0 = (E * lane) & (K - 1);
+  float inv[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) inv[s] = s_inv[(j0 + 32 * s) >> log2G];
+  float rmax = 0.f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) rmax = fmaxf(rmax, m[s] * inv[s]);
+  for (int d = 1; d * E < K; d <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, d));
+  const float k7 = rmax > 0.f ? 7.f / rmax : 0.f;
+  uint32_t packed[E / 8];
+#pragma unroll
+  for (int o = 0; o < E / 8; ++o) {
+    uint32_t mag[8], sgn[8];
+    const float ks = inv[(8 * o) / 32] * k7;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      mag[e] = __float_as_uint(fmaf(fabsf(v[8 * o + e]), ks, kMagic));
+      sgn[e] = __float_as_uint(v[8 * o + e]);
+    }
+    packed[o] = pack8(mag, sgn);
+  }
+  if (row0 + rl < rows) {
+    uint8_t* dst = codes + static_cast<size_t>(row0 + rl) * (K / 2) + j0 / 2;
+#pragma unroll
+    for (int o = 0; o < E / 32; ++o)
+      reinterpret_cast<uint4*>(dst)[o] = make_uint4(packed[4 * o], packed[4 * o + 1], packed[4 * o + 2], packed[4 * o + 3]);
+    if (j0 == 0) scale[row0 + rl] = rmax / 7.f;
+  }
+}
+
+// ----------------------------------------------------------- one-pass kernels
+// Stats and quantise passes of the two-launch front end, the offline weight
+// preparation (columns of W as rows) and the calibration channel maxima.
 template <int LOG2K, int MODE, bool ROTATE>
 __global__ void __launch_bounds__(Cfg<LOG2K>::kThreads)
 frontend_kernel(FeArgs a) {
   using C = Cfg<LOG2K>;
   constexpr int K = 1 << LOG2K;
-  constexpr int B = C::kB, E = C::kE, WAVES = C::kWaves;
-  constexpr int NS = E / 32;  // 32-wide sub-segments per lane (G >= 32)
+  constexpr int E = C::kE, WAVES = C::kWaves;
 
   __shared__ float s_buf[WAVES][C::kBufFloats];
-  __shared__ uint32_t s_tab[B];                 // gather table, or channel max
+  __shared__ uint32_t s_tab[C::kB];             // gather table, or channel max
   __shared__ float s_grp[K / 32];               // group max (stats) / 1/S (quant)
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
-  const int G = 1 << a.log2G;
   const int ngroups = K >> a.log2G;
+  const int blk = blockIdx.x * WAVES + wave;
+  const int row0 = blk * C::kRows;
+
+  // activation rows: start the loads before the set-up
+  uint4 w[C::kChunks];
+  if constexpr (MODE != kWeight) load_block<LOG2K>(w, a.src, a.rows, row0, lane);
 
   // ---- per-workgroup set-up -------------------------------------------
   if constexpr (MODE == kColmax) {
     for (int k = tid; k < K; k += C::kThreads) s_tab[k] = 0u;
   } else {
-    // s_tab[gpos(l, r)] = gather-buffer address of the element that lane l,
-    // register r needs: position p = E*l + r of the block, row p / K,
-    // reordered column p % K, source channel perm[p % K].
-    for (int idx = tid; idx < B; idx += C::kThreads) {
-      const int c4 = idx >> 8, l = (idx >> 2) & 63, rr = idx & 3;
-      const int p = E * l + (c4 << 2) + rr;
-      const int f = ((p >> LOG2K) << LOG2K) | a.perm[p & (K - 1)];
-      int sl, sr;
-      if (ROTATE) {
-        sl = (f & 7) | (((f >> 9) & 7) << 3);
-        sr = ((f >> 3) & 63) | ((f >> 12) << 6);
-      } else {
-        sl = (f >> 3) & 63;
-        sr = (f & 7) | ((f >> 9) << 3);
-      }
-      s_tab[idx] = static_cast<uint32_t>(gpos(sl, sr));
-    }
+    build_table<LOG2K, ROTATE>(s_tab, a.perm, tid, C::kThreads);
     if constexpr (MODE == kStats) {
       for (int g = tid; g < ngroups; g += C::kThreads) s_grp[g] = 0.f;
     } else if constexpr (MODE == kQuant) {
@@ -171,69 +365,35 @@ frontend_kernel(FeArgs a) {
         }
         s_grp[g] = 1.f / sg;
       }
+    } else {
+      for (int g = tid; g < ngroups; g += C::kThreads) s_grp[g] = 1.f;
     }
   }
   __syncthreads();
 
-  const int blk = blockIdx.x * WAVES + wave;
-  const int row0 = blk * C::kRows;
   if (row0 < a.rows) {
-    // ---- load ------------------------------------------------------------
-    float v[E];
+    if constexpr (MODE == kWeight) {
+      // column `row` of W [K][ldw], channels k0..k0+7
 #pragma unroll
-    for (int i = 0; i < C::kChunks; ++i) {
-      const int f0 = 8 * lane + 512 * i;
-      const int row = row0 + (f0 >> LOG2K);
-      uint32_t w[4] = {0u, 0u, 0u, 0u};
-      if (row < a.rows) {
-        if constexpr (MODE == kWeight) {
-          // column `row` of W [K][ldw], channels k0..k0+7
+      for (int i = 0; i < C::kChunks; ++i) {
+        const int f0 = 8 * lane + 512 * i;
+        const int row = row0 + (f0 >> LOG2K);
+        uint32_t q[4] = {0u, 0u, 0u, 0u};
+        if (row < a.rows) {
           const int k0 = f0 & (K - 1);
           const uint16_t* p = a.src + static_cast<size_t>(k0) * a.ldw + row;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            w[e] = static_cast<uint32_t>(p[(2 * e) * static_cast<size_t>(a.ldw)]) |
+            q[e] = static_cast<uint32_t>(p[(2 * e) * static_cast<size_t>(a.ldw)]) |
                    (static_cast<uint32_t>(p[(2 * e + 1) * static_cast<size_t>(a.ldw)]) << 16);
-        } else {
-          const uint4 q = *reinterpret_cast<const uint4*>(a.src + static_cast<size_t>(row0) * K + f0);
-          w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
         }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[8 * i + 2 * e] = h2f(w[e] & 0xffffu);
-        v[8 * i + 2 * e + 1] = h2f(w[e] >> 16);
+        w[i] = make_uint4(q[0], q[1], q[2], q[3]);
       }
     }
-
+    float v[E];
+    widen_block<LOG2K>(v, w);
     float* wb = s_buf[wave];
-    if constexpr (ROTATE) {
-      // ---- rotation, phase 1: register bits <-> f bits 0-2, 9.. --------
-#pragma unroll
-      for (int rb = 0; rb < C::kLog2E; ++rb) {
-        const int fb = rb < 3 ? rb : rb + 6;
-        if (fb < LOG2K) butterfly<E>(v, 1 << rb);
-      }
-      // ---- transpose ---------------------------------------------------
-#pragma unroll
-      for (int i = 0; i < C::kChunks; ++i) {
-        const int t = tpos(8 * lane + 512 * i);
-        *reinterpret_cast<float4*>(wb + t) = make_float4(v[8 * i], v[8 * i + 1], v[8 * i + 2], v[8 * i + 3]);
-        *reinterpret_cast<float4*>(wb + t + 4) = make_float4(v[8 * i + 4], v[8 * i + 5], v[8 * i + 6], v[8 * i + 7]);
-      }
-      lds_fence();
-      {
-        const int base = (lane & 7) + (lane >> 3) * (512 + 8);
-#pragma unroll
-        for (int r = 0; r < E; ++r) v[r] = wb[base + 8 * (r & 63) + (4096 + 64) * (r >> 6)];
-      }
-      lds_fence();
-      // ---- rotation, phase 2: f bits 3-8 -------------------------------
-#pragma unroll
-      for (int rb = 0; rb < 6; ++rb) {
-        if (rb + 3 < LOG2K) butterfly<E>(v, 1 << rb);
-      }
-    }
+    if constexpr (ROTATE) rotate_block<LOG2K>(v, wb, lane);
 
     if constexpr (MODE == kColmax) {
       // channel |max| over the block's rows (LDS), folded into global below
@@ -244,89 +404,13 @@ frontend_kernel(FeArgs a) {
           atomicMax(&s_tab[f & (K - 1)], __float_as_uint(fabsf(v[r])));
       }
     } else {
-      // ---- reorder: scatter registers, gather reordered positions ------
-#pragma unroll
-      for (int c = 0; c < E / 4; ++c)
-        *reinterpret_cast<float4*>(wb + gpos(lane, 4 * c)) = make_float4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
-      lds_fence();
-#pragma unroll
-      for (int c = 0; c < E / 4; ++c) {
-        const uint4 ad = reinterpret_cast<const uint4*>(s_tab)[c * 64 + lane];
-        v[4 * c] = wb[ad.x];
-        v[4 * c + 1] = wb[ad.y];
-        v[4 * c + 2] = wb[ad.z];
-        v[4 * c + 3] = wb[ad.w];
-      }
-      lds_fence();
-
-      // v[r] = Zp of block position p = E*lane + r: row rl, column j0 + r
-      const int rl = (E * lane) >> LOG2K;
-      const int j0 = (E * lane) & (K - 1);
-      const bool row_ok = row0 + rl < a.rows;
-
-      // ---- per-row group |max| -----------------------------------------
-      float m[NS];
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        float x = fabsf(v[32 * s]);
-#pragma unroll
-        for (int r = 1; r < 32; ++r) x = fmaxf(x, fabsf(v[32 * s + r]));
-        m[s] = x;
-      }
-      // merge sub-segments of the same group inside the lane
-#pragma unroll
-      for (int st = 1; st < NS; st <<= 1) {
-        if (G > 32 * st) {
-          float t[NS];
-#pragma unroll
-          for (int s = 0; s < NS; ++s) t[s] = fmaxf(m[s], m[s ^ st]);
-#pragma unroll
-          for (int s = 0; s < NS; ++s) m[s] = t[s];
-        }
-      }
-      // and across the G / E lanes of a group
-      for (int d = 1; d * E < G; d <<= 1) {
-#pragma unroll
-        for (int s = 0; s < NS; ++s) m[s] = fmaxf(m[s], __shfl_xor(m[s], d));
-      }
-
-      if constexpr (MODE == kStats) {
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const int j = j0 + 32 * s;
-          if (row_ok && (j & (G - 1)) == 0 && m[s] > 0.f)
-            atomicMax(reinterpret_cast<uint32_t*>(&s_grp[j >> a.log2G]), __float_as_uint(m[s]));
-        }
-      } else {
-        // ---- per-token scale, codes, pack ------------------------------
-        float inv[NS];
-#pragma unroll
-        for (int s = 0; s < NS; ++s) inv[s] = (MODE == kQuant) ? s_grp[(j0 + 32 * s) >> a.log2G] : 1.f;
-        float rmax = 0.f;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) rmax = fmaxf(rmax, m[s] * inv[s]);
-        for (int d = 1; d * E < K; d <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, d));
-        const float k7 = rmax > 0.f ? 7.f / rmax : 0.f;
-        uint32_t packed[E / 8];
-#pragma unroll
-        for (int o = 0; o < E / 8; ++o) {
-          uint32_t mag[8], sgn[8];
-          const float ks = inv[(8 * o) / 32] * k7;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            mag[e] = __float_as_uint(fmaf(fabsf(v[8 * o + e]), ks, kMagic));
-            sgn[e] = __float_as_uint(v[8 * o + e]);
-          }
-          packed[o] = pack8(mag, sgn);
-        }
-        if (row_ok) {
-          uint8_t* dst = a.codes + static_cast<size_t>(row0 + rl) * (K / 2) + j0 / 2;
-#pragma unroll
-          for (int o = 0; o < E / 32; ++o)
-            reinterpret_cast<uint4*>(dst)[o] = make_uint4(packed[4 * o], packed[4 * o + 1], packed[4 * o + 2], packed[4 * o + 3]);
-          if (j0 == 0) a.scale[row0 + rl] = rmax / 7.f;
-        }
-      }
+      reorder_block<LOG2K>(v, wb, s_tab, lane);
+      float m[E / 32];
+      group_max<LOG2K>(v, m, 1 << a.log2G);
+      if constexpr (MODE == kStats)
+        fold_group_max<LOG2K>(m, s_grp, a.log2G, a.rows, row0, lane);
+      else
+        quantise_block<LOG2K>(v, m, s_grp, a.log2G, a.codes, a.scale, a.rows, row0, lane);
     }
   }
 
@@ -365,6 +449,136 @@ frontend_kernel(FeArgs a) {
       if (tid == 0) a.sync[kSyncCounter] = 0u;
     }
   }
+}
+
+// ------------------------------------------------------------- fused kernel
+// Bounded spin: every wait below gives up after this many polls (seconds of
+// polling), raises the error word and lets the kernel run to its end, so
+// every wave exits whatever happens to the other workgroups.
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+// The whole activation front end in one launch: each wave rotates, reorders
+// and reduces R blocks and keeps them in registers; each workgroup stores
+// its group maxima in its own row of the synchronisation block and raises
+// its arrival flag to this call's epoch; once every flag shows the epoch,
+// each workgroup reduces all rows itself and smooths, quantises and packs
+// its blocks from its registers. X is read once, and no two workgroups ever
+// update the same word (same-address atomics from every XCD serialise).
+// All workgroups must be resident at once; the launcher checks the grid
+// against the device's occupancy.
+template <int LOG2K, bool ROTATE, int R>
+__global__ void __launch_bounds__(Cfg<LOG2K>::kThreads)
+fused_kernel(FeArgs a) {
+  using C = Cfg<LOG2K>;
+  constexpr int K = 1 << LOG2K;
+  constexpr int E = C::kE, WAVES = C::kWaves;
+
+  __shared__ float s_buf[WAVES][C::kBufFloats];
+  __shared__ uint32_t s_tab[C::kB];
+  __shared__ float s_grp[K / 32];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int ngroups = K >> a.log2G;
+  const int nwg = gridDim.x;
+  int row0[R];
+#pragma unroll
+  for (int q = 0; q < R; ++q) row0[q] = ((blockIdx.x * R + q) * WAVES + wave) * C::kRows;
+
+  uint4 w[R][C::kChunks];
+#pragma unroll
+  for (int q = 0; q < R; ++q) load_block<LOG2K>(w[q], a.src, a.rows, row0[q], lane);
+  // every workgroup reads the epoch before raising its flag, so none can
+  // see the next call's value
+  const uint32_t epoch =
+      __hip_atomic_load(&a.sync[kSyncEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+
+  build_table<LOG2K, ROTATE>(s_tab, a.perm, tid, C::kThreads);
+  for (int g = tid; g < ngroups; g += C::kThreads) s_grp[g] = 0.f;
+  __syncthreads();
+
+  // ---- rotate, reorder, group maxima; the blocks stay in registers --------
+  float v[R][E];
+  float m[R][E / 32];
+  float* wb = s_buf[wave];
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    widen_block<LOG2K>(v[q], w[q]);
+    if constexpr (ROTATE) rotate_block<LOG2K>(v[q], wb, lane);
+    reorder_block<LOG2K>(v[q], wb, s_tab, lane);
+    group_max<LOG2K>(v[q], m[q], 1 << a.log2G);
+    fold_group_max<LOG2K>(m[q], s_grp, a.log2G, a.rows, row0[q], lane);
+  }
+  __syncthreads();
+
+  // ---- publish this workgroup's maxima, wait for everyone's ---------------
+  // Every cross-workgroup word is written and read with relaxed agent-scope
+  // atomics, which go to the device-coherent level directly (no L2
+  // write-back or invalidate, which acquire/release would add per access).
+  // The order "maxima before flag" comes from waiting for the maxima stores
+  // to complete before the flag store is issued; on the reading side the
+  // maxima are loaded only after every flag has been seen.
+  uint32_t* part = a.sync + kSyncPartials;
+  uint32_t* flags = a.sync + kSyncFlags;
+  for (int g = tid; g < ngroups; g += C::kThreads)
+    __hip_atomic_store(&part[blockIdx.x * ngroups + g], __float_as_uint(s_grp[g]), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's stores are complete
+  __syncthreads();
+  if (tid == 0) __hip_atomic_store(&flags[blockIdx.x], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = tid; i < nwg; i += C::kThreads) {
+    uint32_t it = 0;
+    while (__hip_atomic_load(&flags[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+      if (++it == kSpinLimit) {
+        atomicOr(&a.sync[kSyncError], 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  for (int g = tid; g < ngroups; g += C::kThreads) s_grp[g] = 0.f;
+  __syncthreads();
+  if (blockIdx.x == 0 && tid == 0)
+    __hip_atomic_store(&a.sync[kSyncEpoch], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // ---- S_g = max over the workgroups' rows (loads issued in batches) -------
+  {
+    constexpr int kBatch = 8;
+    const int n = nwg * ngroups;
+    const bool same_group = C::kThreads % ngroups == 0;  // thread always on group tid % ngroups
+    uint32_t mx = 0u;
+    for (int base = tid; base < n; base += C::kThreads * kBatch) {
+      uint32_t b[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int idx = base + k * C::kThreads;
+        b[k] = idx < n ? __hip_atomic_load(&part[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        if (same_group) {
+          mx = max(mx, b[k]);
+        } else if (b[k]) {
+          atomicMax(reinterpret_cast<uint32_t*>(&s_grp[(base + k * C::kThreads) % ngroups]), b[k]);
+        }
+      }
+    }
+    if (same_group && mx) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[tid % ngroups]), mx);
+  }
+  __syncthreads();
+  for (int g = tid; g < ngroups; g += C::kThreads) {
+    float sg = s_grp[g];
+    if (!(sg > 0.f)) sg = 1.f;  // all-zero group over every token
+    if (blockIdx.x == 0) a.S_out[g] = sg;
+    s_grp[g] = 1.f / sg;
+  }
+  __syncthreads();
+
+  // ---- smooth, quantise, pack ------------------------------------------------
+#pragma unroll
+  for (int q = 0; q < R; ++q)
+    quantise_block<LOG2K>(v[q], m[q], s_grp, a.log2G, a.codes, a.scale, a.rows, row0[q], lane);
 }
 
 // Stable descending rank: perm[rank(j)] = j with rank(j) = #{i : c_i > c_j}
@@ -415,6 +629,86 @@ hipError_t dispatch_k(int log2K, const FeArgs& a, hipStream_t s) {
   }
 }
 
+// Workgroups of fused_kernel<LOG2K, ROTATE, R> that the current device holds
+// at once (occupancy per CU x CUs), cached per device; -1 if unknown.
+constexpr int kMaxDevices = 64;
+
+template <int LOG2K, bool ROTATE, int R>
+int fused_capacity() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  int cap = cache[dev].load(std::memory_order_relaxed);
+  if (cap == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<LOG2K, ROTATE, R>,
+                                                     Cfg<LOG2K>::kThreads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        per_cu <= 0 || cus <= 0) {
+      cap = -1;
+    } else {
+      cap = per_cu * cus;
+    }
+    cache[dev].store(cap, std::memory_order_relaxed);
+  }
+  return cap;
+}
+
+// Launch the fused front end with R blocks per wave if its grid fits on the
+// device at once; returns false (nothing launched) otherwise.
+template <int LOG2K, bool ROTATE, int R>
+bool try_fused(const FeArgs& a, hipStream_t s, hipError_t* err) {
+  using C = Cfg<LOG2K>;
+  const int nblk = (a.rows + C::kRows - 1) / C::kRows;
+  const int grid = (nblk + C::kWaves * R - 1) / (C::kWaves * R);
+  const int cap = fused_capacity<LOG2K, ROTATE, R>();
+  if (cap <= 0 || grid > cap || grid > kMaxFusedWG) return false;
+  hipLaunchKernelGGL((fused_kernel<LOG2K, ROTATE, R>), dim3(grid), dim3(C::kThreads), 0, s, a);
+  *err = hipGetLastError();
+  return true;
+}
+
+// Blocks per wave of the one-launch form for `rows` rows (1 or 2), or 0
+// when its grid does not fit on the current device at once.
+template <int LOG2K, bool ROTATE>
+int fused_blocks_per_wave(int rows) {
+  using C = Cfg<LOG2K>;
+  const int nblk = (rows + C::kRows - 1) / C::kRows;
+  const int g1 = (nblk + C::kWaves - 1) / C::kWaves;
+  int cap = fused_capacity<LOG2K, ROTATE, 1>();
+  if (cap > 0 && g1 <= cap && g1 <= kMaxFusedWG) return 1;
+  if constexpr (LOG2K <= 12) {
+    const int g2 = (nblk + 2 * C::kWaves - 1) / (2 * C::kWaves);
+    cap = fused_capacity<LOG2K, ROTATE, 2>();
+    if (cap > 0 && g2 <= cap && g2 <= kMaxFusedWG) return 2;
+  }
+  return 0;
+}
+
+template <int LOG2K, bool ROTATE>
+bool launch_fused(const FeArgs& a, hipStream_t s, hipError_t* err) {
+  if (try_fused<LOG2K, ROTATE, 1>(a, s, err)) return true;
+  if constexpr (LOG2K <= 12) {
+    if (try_fused<LOG2K, ROTATE, 2>(a, s, err)) return true;
+  }
+  return false;
+}
+
+template <bool ROTATE>
+bool fused_k(int log2K, const FeArgs& a, hipStream_t s, hipError_t* err) {
+  switch (log2K) {
+    case 6: return launch_fused<6, ROTATE>(a, s, err);
+    case 7: return launch_fused<7, ROTATE>(a, s, err);
+    case 8: return launch_fused<8, ROTATE>(a, s, err);
+    case 9: return launch_fused<9, ROTATE>(a, s, err);
+    case 10: return launch_fused<10, ROTATE>(a, s, err);
+    case 11: return launch_fused<11, ROTATE>(a, s, err);
+    case 12: return launch_fused<12, ROTATE>(a, s, err);
+    case 13: return launch_fused<13, ROTATE>(a, s, err);
+    default: return false;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_frontend(const uint16_t* X, int M, int log2K, int G, const int32_t* perm,
@@ -431,12 +725,28 @@ hipError_t launch_frontend(const uint16_t* X, int M, int log2K, int G, const int
   a.scale = dx;
   a.S_out = S_out;
   const bool rotate = !(flags & 1);
-  hipError_t e;
+  hipError_t e = hipSuccess;
   if (a.smooth) {
+    // one launch when every workgroup fits on the device at once
+    if (!(flags & 4) && (rotate ? fused_k<true>(log2K, a, s, &e) : fused_k<false>(log2K, a, s, &e))) return e;
     e = rotate ? dispatch_k<kStats, true>(log2K, a, s) : dispatch_k<kStats, false>(log2K, a, s);
     if (e != hipSuccess) return e;
   }
   return rotate ? dispatch_k<kQuant, true>(log2K, a, s) : dispatch_k<kQuant, false>(log2K, a, s);
+}
+
+int frontend_launches(int M, int log2K, int flags) {
+  if (flags & 2) return 1;
+  if (flags & 4) return 2;
+  const bool rotate = !(flags & 1);
+  int r = 0;
+  switch (log2K) {
+#define RRS_CASE(L) case L: r = rotate ? fused_blocks_per_wave<L, true>(M) : fused_blocks_per_wave<L, false>(M); break;
+    RRS_CASE(6) RRS_CASE(7) RRS_CASE(8) RRS_CASE(9) RRS_CASE(10) RRS_CASE(11) RRS_CASE(12) RRS_CASE(13)
+#undef RRS_CASE
+    default: return -1;
+  }
+  return r > 0 ? 1 : 2;
 }
 
 hipError_t launch_weight_prep(const uint16_t* W, int log2K, int N, const int32_t* perm,

@@ -13,22 +13,40 @@ constexpr int kMinLog2K = 6;
 constexpr int kMaxLog2K = 13;
 constexpr int kMinG = 32;
 
-// Layout of the synchronisation block at the start of a workspace (all
-// uint32): [0] done-counter of the quantise kernel, [1] grid barrier word,
-// [2] error flag, [3..63] reserved, [64 .. 64 + K/G) running group maxima as
-// float bits. Every front-end call leaves the block zeroed.
+// Layout of the synchronisation block at the start of a workspace (uint32
+// words unless noted):
+//   [0]    done-counter of the two-launch front end's quantise pass
+//   [2]    error word: nonzero once a bounded wait gave up (only
+//          rrs_workspace_init clears it)
+//   [3]    epoch of the one-launch front end (calls so far, mod 2^32)
+//   [64, 64 + K/G)       running group maxima of the two-launch front end
+//                        (float bits; left zero by every call)
+//   [320, 320 + 512)     one-launch arrival flags, one per workgroup: the
+//                        epoch of the call that last passed through it
+//   [832, 832 + 512 K/G) one-launch group maxima, one row of K/G floats per
+//                        workgroup (never needs clearing)
+// rrs_workspace_init zeroes words [0, 832).
 constexpr int kSyncCounter = 0;
-constexpr int kSyncBarrier = 1;
 constexpr int kSyncError = 2;
+constexpr int kSyncEpoch = 3;
 constexpr int kSyncGroups = 64;
+constexpr int kSyncFlags = 320;
+constexpr int kMaxFusedWG = 512;
+constexpr int kSyncPartials = kSyncFlags + kMaxFusedWG;  // 832
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Front end (activation rows): stats pass then quantise pass.
-//   flags: bit0 = skip rotation, bit1 = skip smoothing (S = 1).
+// Front end (activation rows): one launch when its workgroups all fit on
+// the device at once, else a stats pass then a quantise pass.
+//   flags: bit0 = skip rotation, bit1 = skip smoothing (S = 1),
+//          bit2 = always use the two launches.
 hipError_t launch_frontend(const uint16_t* X, int M, int log2K, int G, const int32_t* perm,
                            uint8_t* xq, float* dx, float* S_out, uint32_t* sync, int flags,
                            hipStream_t s);
+
+// Launches the front end would use for M rows on the current device (1 or
+// 2), -1 for an unsupported K.
+int frontend_launches(int M, int log2K, int flags);
 
 // Offline weight preparation: W [K, N] row-major fp16 -> wq [N][K/2] + dw [N].
 hipError_t launch_weight_prep(const uint16_t* W, int log2K, int N, const int32_t* perm,

@@ -62,9 +62,19 @@ def frontend(x: np.ndarray, perm: np.ndarray, G: int, flags: int = 0):
     ws = torch.zeros(rra.rrs_sync_bytes(K, G), dtype=torch.uint8, device=DEV)
     rra.rrs_frontend(X, G, to_dev(perm), xq, dx, S, ws, flags)
     torch.cuda.synchronize()
-    # the call must leave its synchronisation block zeroed
-    assert int(ws.count_nonzero()) == 0, "front end left the sync block dirty"
+    check_sync_block(ws, K, G)
     return xq.cpu().numpy(), dx.cpu().numpy(), S.cpu().numpy()
+
+
+def check_sync_block(ws, K: int, G: int, calls: int = 1):
+    """After `calls` front-end calls on a freshly initialised workspace: the
+    error word is clear, the two-launch counter and maxima are back to zero,
+    and the one-launch epoch counted the one-launch calls (0 or `calls`)."""
+    words = ws[: rra.rrs_sync_bytes(K, G)].view(torch.int32).cpu().numpy()
+    assert words[2] == 0, "a bounded wait gave up (error word set)"
+    assert words[0] == 0, "two-launch done-counter left nonzero"
+    assert not words[64:64 + K // G].any(), "two-launch group maxima left nonzero"
+    assert words[3] in (0, calls), f"epoch {words[3]} after {calls} call(s)"
 
 
 def compare_codes(q_gpu: np.ndarray, q_ref: np.ndarray, v_ref: np.ndarray, what: str) -> dict:

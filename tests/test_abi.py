@@ -49,10 +49,12 @@ def test_size_queries():
     assert rra.rrs_weight_bytes(256, 0) == 0
     # workspace: sync block + xq + dx + S
     sync = rra.rrs_sync_bytes(4096, 128)
-    # 64 control words + one word per group, rounded up to 256 bytes
-    assert sync == 512 and rra.rrs_sync_bytes(8192, 32) == 1280
+    # 832 words (control, two-launch maxima, 512 arrival flags) + a row of
+    # K/G maxima for each of 512 workgroups, rounded up to 256 bytes
+    assert sync == 4 * (832 + 512 * 32) and rra.rrs_sync_bytes(8192, 32) == 4 * (832 + 512 * 256)
+    assert rra.rrs_sync_bytes(64, 32) == 4 * (832 + 512 * 2)
     assert rra.rrs_workspace_bytes(2048, 4096, 128) == sync + 2048 * 2048 + 2048 * 4 + 256
-    assert rra.rrs_workspace_bytes(1, 64, 32) == 512 + 256 + 256 + 256
+    assert rra.rrs_workspace_bytes(1, 64, 32) == 7424 + 256 + 256 + 256
     assert rra.rrs_workspace_bytes(16, 256, 16) == 0   # G < 32
     assert rra.rrs_workspace_bytes(16, 256, 512) == 0  # G > K
     assert rra.rrs_workspace_bytes(16, 256, 96) == 0   # G not a power of two
@@ -91,18 +93,28 @@ def test_linear_zero_tokens_is_noop():
 def test_frontend_rejects():
     L = rra.lib()
     ok = dict(X=DUMMY, M=4, K=256, G=64, perm=DUMMY, xq=DUMMY, dx=DUMMY, S=DUMMY, ws=DUMMY,
-              ws_bytes=4096, flags=0)
+              ws_bytes=1 << 20, flags=0)
 
     def call(**kw):
         a = {**ok, **kw}
         return L.rrs_frontend(a["X"], a["M"], a["K"], a["G"], a["perm"], a["xq"], a["dx"], a["S"],
                               a["ws"], a["ws_bytes"], a["flags"], NULL)
-    assert call(flags=4) == rra.RRS_EINVAL
+    assert call(flags=8) == rra.RRS_EINVAL
     assert call(ws_bytes=255) == rra.RRS_EINVAL
     assert call(S=NULL) == rra.RRS_EINVAL
     assert call(xq=NULL) == rra.RRS_EINVAL
     assert call(G=512) == rra.RRS_EINVAL
     assert call(M=0, X=NULL, xq=NULL, dx=NULL) == rra.RRS_OK
+
+
+def test_frontend_passes_rejects():
+    L = rra.lib()
+    assert L.rrs_frontend_passes(0, 4096, 0) == rra.RRS_EINVAL
+    assert L.rrs_frontend_passes(16, 100, 0) == rra.RRS_EINVAL
+    assert L.rrs_frontend_passes(16, 4096, 8) == rra.RRS_EINVAL
+    # answered without a device when the flags fix the form
+    assert L.rrs_frontend_passes(16, 4096, rra.RRS_FLAG_NO_SMOOTH) == 1
+    assert L.rrs_frontend_passes(16, 4096, rra.RRS_FLAG_TWO_PASS) == 2
 
 
 def test_gemm_and_partials_reject():

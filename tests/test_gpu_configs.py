@@ -68,6 +68,8 @@ def test_workload(name):
         rra.rrs_linear(X, G, P, wq, Y, ws)
         rra.rrs_linear(X, G, P, wq, Y, ws)     # second call on the same workspace
         torch.cuda.synchronize()
+        gu.check_sync_block(ws, K, G, calls=2)
+        gu.log(f"  front end: {rra.rrs_frontend_passes(M, K, 0)} launch(es)")
         xq, dx, S = rra.workspace_views(ws, M, K, G)
         fe = oracle.frontend(x, perm_ref, G)
         q_gpu = oracle.unpack_codes(xq.cpu().numpy())
