@@ -526,10 +526,10 @@ fused_kernel(FeArgs a) {
                        __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's stores are complete
   __syncthreads();
-  if (tid == 0) __hip_atomic_store(&flags[blockIdx.x], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(&flags[blockIdx.x * kFlagStride], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (int i = tid; i < nwg; i += C::kThreads) {
     uint32_t it = 0;
-    while (__hip_atomic_load(&flags[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+    while (__hip_atomic_load(&flags[i * kFlagStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
       if (++it == kSpinLimit) {
         atomicOr(&a.sync[kSyncError], 1u);
         break;
@@ -544,7 +544,7 @@ fused_kernel(FeArgs a) {
 
   // ---- S_g = max over the workgroups' rows (loads issued in batches) -------
   {
-    constexpr int kBatch = 8;
+    constexpr int kBatch = 16;
     const int n = nwg * ngroups;
     const bool same_group = C::kThreads % ngroups == 0;  // thread always on group tid % ngroups
     uint32_t mx = 0u;

@@ -21,18 +21,21 @@ constexpr int kMinG = 32;
 //   [3]    epoch of the one-launch front end (calls so far, mod 2^32)
 //   [64, 64 + K/G)       running group maxima of the two-launch front end
 //                        (float bits; left zero by every call)
-//   [320, 320 + 512)     one-launch arrival flags, one per workgroup: the
-//                        epoch of the call that last passed through it
-//   [832, 832 + 512 K/G) one-launch group maxima, one row of K/G floats per
-//                        workgroup (never needs clearing)
-// rrs_workspace_init zeroes words [0, 832).
+//   [1024, 1024 + 32*512) one-launch arrival flags, one per workgroup, each
+//                        alone in its 128-byte line (pollers of different
+//                        flags then do not queue on one line): the epoch of
+//                        the call that last passed through it
+//   [17408, 17408 + 512 K/G) one-launch group maxima, one row of K/G floats
+//                        per workgroup (never needs clearing)
+// rrs_workspace_init zeroes words [0, 17408).
 constexpr int kSyncCounter = 0;
 constexpr int kSyncError = 2;
 constexpr int kSyncEpoch = 3;
 constexpr int kSyncGroups = 64;
-constexpr int kSyncFlags = 320;
+constexpr int kSyncFlags = 1024;
+constexpr int kFlagStride = 32;
 constexpr int kMaxFusedWG = 512;
-constexpr int kSyncPartials = kSyncFlags + kMaxFusedWG;  // 832
+constexpr int kSyncPartials = kSyncFlags + kFlagStride * kMaxFusedWG;  // 17408
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
