@@ -154,7 +154,7 @@ struct GemmCtx {
   const uint8_t* gsrc[kDmaPerWave];  // this lane's row pointer for each of its DMA blocks
   int goff[kDmaPerWave];             // byte offset of its 16-byte piece
   int lblk[kDmaPerWave];             // LDS offset of each block in a stage
-  int fW, fX;
+  int fW, fX, fsw;
   v4f acc[8][4];
   const float* rat;
 
@@ -182,30 +182,44 @@ struct GemmCtx {
       if (step << (KM == 128 ? 7 : 5) >= a.K) break;  // K = 64: half a stage
       const int gs = step & ((1 << log2spg) - 1);
       typename Mm::frag fx[4];
+      const int koff = KM == 128 ? 0 : ((ks * 16) ^ fsw);  // swizzled 16-byte chunk ks
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fx[j] = Mm::load(stage + fX + j * 16 * kRowB + ks * 16);
+      for (int j = 0; j < 4; ++j) fx[j] = Mm::load(stage + fX + j * 16 * kRowB + koff);
+      // Entering a new group rescales the accumulator by S_{g-1} / S_g.
+      // Set 0 does it just before the group's first products, set 1 right
+      // after the previous group's last ones: after each barrier one wave of
+      // every SIMD pair then multiplies while the other feeds the matrix
+      // core, instead of both multiplying at once.
       if (gs == 0 && step > st0 * Mm::kSteps) {
         if (PARTIALS) {
 #pragma unroll
           for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-        } else {
-          const float r = rat[step >> log2spg];
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] *= r;
+        } else if (SET == 0) {
+          rescale(rat[step >> log2spg]);
         }
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const typename Mm::frag fw = Mm::load(stage + fW + i * 16 * kRowB + ks * 16);
+        const typename Mm::frag fw = Mm::load(stage + fW + i * 16 * kRowB + koff);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = Mm::mma(fw, fx[j], acc[i][j]);
       }
       if (PARTIALS && gs == (1 << log2spg) - 1) dump(step >> log2spg);
+      if (!PARTIALS && SET == 1) {
+        const int nx = step + 1;
+        if ((nx & ((1 << log2spg) - 1)) == 0 && nx < st1 * Mm::kSteps && (nx << (KM == 128 ? 7 : 5)) < a.K)
+          rescale(rat[nx >> log2spg]);
+      }
     }
+  }
+
+  __device__ __forceinline__ void rescale(float r) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] *= r;
   }
 
   __device__ void dump(int g) {
@@ -300,14 +314,18 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
   }
 
   // DMA blocks of a stage: 1 KiB = 16 rows x 64 B; blocks 0..15 hold the
-  // weight rows, 16..23 the activation rows; wave w moves blocks 6w..6w+5,
-  // lane i the 16-byte piece i & 3 of row 16b + i / 4 (rows clamped to the
-  // matrix; clamped rows only feed outputs that are never stored)
+  // weight rows, 16..23 the activation rows; wave w moves blocks 6w..6w+5.
+  // Lane i fills 16-byte slot i of the block: row r = i / 4 (16b + r of the
+  // matrix, clamped to it; clamped rows only feed outputs that are never
+  // stored), 16-byte chunk (i & 3) ^ ((r >> 1) & 3) of that row. The XOR
+  // swizzle spreads the eight rows a fragment read serves at once over all
+  // 32 LDS banks (rows 64 bytes apart would otherwise hit the same banks
+  // every two rows).
 #pragma unroll
   for (int d = 0; d < GemmCtx<KM, PARTIALS>::kDmaPerWave; ++d) {
     const int blk = wave * GemmCtx<KM, PARTIALS>::kDmaPerWave + d;
     const int r = (blk & 15) * 16 + (c.lane >> 2);
-    c.goff[d] = (c.lane & 3) * 16;
+    c.goff[d] = ((c.lane & 3) ^ ((c.lane >> 3) & 3)) * 16;
     c.lblk[d] = blk * 1024;
     if (blk < 16) {
       const int n = min(c.n0 + r, a.N - 1);
@@ -318,9 +336,12 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
     }
   }
 
-  // fragment offsets: row (lane & 15) of each 16-row tile; K bytes
-  // (lane >> 4) * 16 (KM = 128) or ks * 16 + (lane >> 4) * 4 (KM = 32)
-  const int fbyte = (KM == 128) ? (c.lane >> 4) * 16 : (c.lane >> 4) * 4;
+  // fragment offsets: row (lane & 15) of each 16-row tile; logical 16-byte
+  // chunk lane >> 4 (KM = 128) or ks with bytes (lane >> 4) * 4 inside it
+  // (KM = 32), stored at chunk position logical ^ ((row >> 1) & 3)
+  const int sw = (((c.lane & 15) >> 1) & 3) * 16;
+  const int fbyte = (KM == 128) ? (((c.lane >> 4) * 16) ^ sw) : (c.lane >> 4) * 4;
+  c.fsw = KM == 128 ? 0 : sw;
   c.fW = (c.wn * 128 + (c.lane & 15)) * kRowB + fbyte;
   c.fX = kWB + (c.wt * 64 + (c.lane & 15)) * kRowB + fbyte;
 
@@ -347,7 +368,32 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
   // the same group partial: they are added exactly first and scaled once,
   // so a partial that cancels to zero stays exactly zero.
   const bool one_group = c.ngroups == 1;
+  // Epilogue operands go into registers before any store: Y may alias them
+  // as far as the compiler knows, so loads left between the Y stores would
+  // each wait out a full memory latency in turn.
   const float s_end = a.S[((c.st1 * 128 > a.K ? a.K : c.st1 * 128) - 1) >> a.log2G];
+  const float base = kUnit / static_cast<float>(a.K);
+  float rsv[4];
+  float4 dwv[8];
+  if (set == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = c.t0 + c.wt * 64 + j * 16 + (c.lane & 15);
+      rsv[j] = t < a.M ? a.dx[t] * base : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n = c.n0 + c.wn * 128 + i * 16 + (c.lane >> 4) * 4;
+      if (n + 3 < a.N) {
+        dwv[i] = *reinterpret_cast<const float4*>(a.dw + n);
+      } else {
+        dwv[i].x = n < a.N ? a.dw[n] : 0.f;
+        dwv[i].y = n + 1 < a.N ? a.dw[n + 1] : 0.f;
+        dwv[i].z = n + 2 < a.N ? a.dw[n + 2] : 0.f;
+        dwv[i].w = 0.f;
+      }
+    }
+  }
   __syncthreads();  // all rings idle: park set 1's 4 x 32 tiles of 1 KiB there
   if (set == 1) {
     const float m1 = one_group ? 1.f : s_end;
@@ -364,29 +410,19 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
   const float fin = one_group ? s_end : 1.f;
 
   // ---- epilogue: Y[t, n..n+3] = (both halves, absolute) 2^18 / K dx[t] dw[n]
-  const float base = kUnit / static_cast<float>(a.K);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int n = c.n0 + c.wn * 128 + i * 16 + (c.lane >> 4) * 4;
     if (n >= a.N) continue;
-    float4 dwv;
-    if (n + 3 < a.N) {
-      dwv = *reinterpret_cast<const float4*>(a.dw + n);
-    } else {
-      dwv.x = a.dw[n];
-      dwv.y = n + 1 < a.N ? a.dw[n + 1] : 0.f;
-      dwv.z = n + 2 < a.N ? a.dw[n + 2] : 0.f;
-      dwv.w = 0.f;
-    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int t = c.t0 + c.wt * 64 + j * 16 + (c.lane & 15);
       if (t >= a.M) continue;
-      const float rs = a.dx[t] * base;
       float* y = a.Y + static_cast<size_t>(t) * a.N + n;
-      const v4f v = (c.acc[i][j] * m0 + reinterpret_cast<const v4f*>(park_chunk(wave * 32 + i * 4 + j))[c.lane]) * fin;
-      const float v0 = v[0] * rs * dwv.x, v1 = v[1] * rs * dwv.y;
-      const float v2 = v[2] * rs * dwv.z, v3 = v[3] * rs * dwv.w;
+      const v4f v = (c.acc[i][j] * m0 + reinterpret_cast<const v4f*>(park_chunk(wave * 32 + i * 4 + j))[c.lane]) *
+                    (fin * rsv[j]);
+      const float v0 = v[0] * dwv[i].x, v1 = v[1] * dwv[i].y;
+      const float v2 = v[2] * dwv[i].z, v3 = v[3] * dwv[i].w;
       if (n + 3 < a.N && (a.N & 3) == 0) {
         *reinterpret_cast<float4*>(y) = make_float4(v0, v1, v2, v3);
       } else {
