@@ -124,8 +124,15 @@ __device__ __forceinline__ uint8_t* ring() {
 }
 
 // 1-KiB chunk c (0 <= c < 144) of the six ring buffers, used to park the
-// second set's partial sums once the rings are idle
+// second set's partial sums once the rings are idle. c is wave-uniform.
+// The compiler places the six arrays back to back in declaration order;
+// the address arithmetic then needs no branch (the test folds to a
+// constant, the switch only stands in if the layout ever differs).
 __device__ __forceinline__ float* park_chunk(int c) {
+  uint8_t* b0 = s_r00;
+  if (s_r01 == b0 + kStageB && s_r02 == b0 + 2 * kStageB && s_r10 == b0 + 3 * kStageB &&
+      s_r11 == b0 + 4 * kStageB && s_r12 == b0 + 5 * kStageB)
+    return reinterpret_cast<float*>(b0 + c * 1024);
   uint8_t* b;
   switch (c / 24) {
     case 0: b = s_r00; break;
@@ -277,12 +284,15 @@ struct GemmCtx {
 template <int KM, bool PARTIALS>
 __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
   __shared__ float s_rat[(1 << kMaxLog2K) / kMinG];
+  __shared__ float s_rs[kTT];       // dx[t] 2^18 / K of the tile's tokens
+  __shared__ float s_dw[kTN];       // dw[n] of the tile's output channels
+  __shared__ float s_send[kSets];   // each set's last group scale
   GemmCtx<KM, PARTIALS> c(a, s_rat);
   const int tid = threadIdx.x;
   const int set = tid / kThreads;
   const int stid = tid % kThreads;
   c.lane = stid & 63;
-  const int wave = stid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(stid >> 6);  // uniform, for scalar addressing
   c.wn = wave >> 1;
   c.wt = wave & 1;
 
@@ -311,6 +321,19 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
   if (!PARTIALS) {
     // s_rat[g] = S[g-1] / S[g]: entering group g rescales the accumulator
     for (int g = tid; g < c.ngroups; g += kThreadsWG) s_rat[g] = g > 0 ? a.S[g - 1] / a.S[g] : 1.f;
+    // epilogue operands, read now so their latency hides behind the main
+    // loop (zero past the matrix edge; those outputs are never stored)
+    const float base = kUnit / static_cast<float>(a.K);
+    if (tid < kTT) {
+      const int t = c.t0 + tid;
+      s_rs[tid] = t < a.M ? a.dx[t] * base : 0.f;
+    } else if (tid < kTT + kTN) {
+      const int n = c.n0 + tid - kTT;
+      s_dw[tid - kTT] = n < a.N ? a.dw[n] : 0.f;
+    } else if (tid < kTT + kTN + kSets) {
+      const int st_end = tid - kTT - kTN == 0 ? half : c.nstage;  // end stage of set 0 / set 1
+      s_send[tid - kTT - kTN] = a.S[((st_end * 128 > a.K ? a.K : st_end * 128) - 1) >> a.log2G];
+    }
   }
 
   // DMA blocks of a stage: 1 KiB = 16 rows x 64 B; blocks 0..15 hold the
@@ -368,41 +391,15 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
   // the same group partial: they are added exactly first and scaled once,
   // so a partial that cancels to zero stays exactly zero.
   const bool one_group = c.ngroups == 1;
-  // Epilogue operands go into registers before any store: Y may alias them
-  // as far as the compiler knows, so loads left between the Y stores would
-  // each wait out a full memory latency in turn.
-  const float s_end = a.S[((c.st1 * 128 > a.K ? a.K : c.st1 * 128) - 1) >> a.log2G];
-  const float base = kUnit / static_cast<float>(a.K);
-  float rsv[4];
-  float4 dwv[8];
-  if (set == 0) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = c.t0 + c.wt * 64 + j * 16 + (c.lane & 15);
-      rsv[j] = t < a.M ? a.dx[t] * base : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int n = c.n0 + c.wn * 128 + i * 16 + (c.lane >> 4) * 4;
-      if (n + 3 < a.N) {
-        dwv[i] = *reinterpret_cast<const float4*>(a.dw + n);
-      } else {
-        dwv[i].x = n < a.N ? a.dw[n] : 0.f;
-        dwv[i].y = n + 1 < a.N ? a.dw[n + 1] : 0.f;
-        dwv[i].z = n + 2 < a.N ? a.dw[n + 2] : 0.f;
-        dwv[i].w = 0.f;
-      }
-    }
-  }
+  const float s_end = s_send[set];
   __syncthreads();  // all rings idle: park set 1's 4 x 32 tiles of 1 KiB there
   if (set == 1) {
-    const float m1 = one_group ? 1.f : s_end;
+    // no second half (K <= 128): park zeros
+    const float m1 = c.st1 > c.st0 ? (one_group ? 1.f : s_end) : 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        reinterpret_cast<v4f*>(park_chunk(wave * 32 + i * 4 + j))[c.lane] =
-            c.st1 > c.st0 ? c.acc[i][j] * m1 : v4f{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 4; ++j) reinterpret_cast<v4f*>(park_chunk(wave * 32 + i * 4 + j))[c.lane] = c.acc[i][j] * m1;
   }
   __syncthreads();
   if (set == 1) return;
@@ -410,26 +407,40 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
   const float fin = one_group ? s_end : 1.f;
 
   // ---- epilogue: Y[t, n..n+3] = (both halves, absolute) 2^18 / K dx[t] dw[n]
+  const bool full = c.t0 + kTT <= a.M && c.n0 + kTN <= a.N && (a.N & 3) == 0;  // uniform
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int nl = c.wn * 128 + i * 16 + (c.lane >> 4) * 4;
+      const float4 dwv = *reinterpret_cast<const float4*>(s_dw + nl);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tl = c.wt * 64 + j * 16 + (c.lane & 15);
+        const v4f v = (c.acc[i][j] * m0 + reinterpret_cast<const v4f*>(park_chunk(wave * 32 + i * 4 + j))[c.lane]) *
+                      (fin * s_rs[tl]);
+        *reinterpret_cast<float4*>(a.Y + static_cast<size_t>(c.t0 + tl) * a.N + c.n0 + nl) =
+            make_float4(v[0] * dwv.x, v[1] * dwv.y, v[2] * dwv.z, v[3] * dwv.w);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int n = c.n0 + c.wn * 128 + i * 16 + (c.lane >> 4) * 4;
-    if (n >= a.N) continue;
+    const int nl = c.wn * 128 + i * 16 + (c.lane >> 4) * 4;  // column in the tile
+    const int n = c.n0 + nl;
+    const float4 dwv = *reinterpret_cast<const float4*>(s_dw + nl);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int t = c.t0 + c.wt * 64 + j * 16 + (c.lane & 15);
-      if (t >= a.M) continue;
-      float* y = a.Y + static_cast<size_t>(t) * a.N + n;
+      const int tl = c.wt * 64 + j * 16 + (c.lane & 15);
+      const int t = c.t0 + tl;
       const v4f v = (c.acc[i][j] * m0 + reinterpret_cast<const v4f*>(park_chunk(wave * 32 + i * 4 + j))[c.lane]) *
-                    (fin * rsv[j]);
-      const float v0 = v[0] * dwv[i].x, v1 = v[1] * dwv[i].y;
-      const float v2 = v[2] * dwv[i].z, v3 = v[3] * dwv[i].w;
-      if (n + 3 < a.N && (a.N & 3) == 0) {
-        *reinterpret_cast<float4*>(y) = make_float4(v0, v1, v2, v3);
-      } else {
-        y[0] = v0;
-        if (n + 1 < a.N) y[1] = v1;
-        if (n + 2 < a.N) y[2] = v2;
-        if (n + 3 < a.N) y[3] = v3;
+                    (fin * s_rs[tl]);
+      if (t < a.M && n < a.N) {
+        float* y = a.Y + static_cast<size_t>(t) * a.N + n;
+        y[0] = v[0] * dwv.x;
+        if (n + 1 < a.N) y[1] = v[1] * dwv.y;
+        if (n + 2 < a.N) y[2] = v[2] * dwv.z;
+        if (n + 3 < a.N) y[3] = v[3] * dwv.w;
       }
     }
   }
