@@ -167,21 +167,29 @@ struct GemmCtx {
 
   __device__ GemmCtx(const GemmArgs& args, const float* s_rat) : a(args), rat(s_rat) {}
 
+  // DMA block d of stage st into ring slot SLOT
   template <int SET, int SLOT>
-  __device__ __forceinline__ void issue(int st) {
+  __device__ __forceinline__ void issue_one(int st, int d) {
     uint8_t* base = ring<SET, SLOT>();
     const int kb = st * kRowB;
-#pragma unroll
-    for (int d = 0; d < kDmaPerWave; ++d) {
-      // a piece past the end of a row (K = 64) re-reads the row's first
-      // bytes: in bounds, and never multiplied (only K codes are used)
-      const int off = kb + goff[d] < Kb ? kb + goff[d] : goff[d] & 15;
-      __builtin_amdgcn_global_load_lds(gsrc[d] + off, (__attribute__((address_space(3))) void*)(base + lblk[d]), 16, 0, 0);
-    }
+    // a piece past the end of a row (K = 64) re-reads the row's first
+    // bytes: in bounds, and never multiplied (only K codes are used)
+    const int off = kb + goff[d] < Kb ? kb + goff[d] : goff[d] & 15;
+    __builtin_amdgcn_global_load_lds(gsrc[d] + off, (__attribute__((address_space(3))) void*)(base + lblk[d]), 16, 0, 0);
   }
 
   template <int SET, int SLOT>
-  __device__ __forceinline__ void compute(int st) {
+  __device__ __forceinline__ void issue(int st) {
+#pragma unroll
+    for (int d = 0; d < kDmaPerWave; ++d) issue_one<SET, SLOT>(st, d);
+  }
+
+  // One stage of products; the DMA of stage nst into slot NSLOT is issued
+  // one block after each of the first rows of products, so the address
+  // unit's work for it spreads over the stage instead of stalling every
+  // wave right after the barrier.
+  template <int SET, int SLOT, int NSLOT>
+  __device__ __forceinline__ void compute(int st, int nst) {
     const uint8_t* stage = ring<SET, SLOT>();
 #pragma unroll
     for (int ks = 0; ks < Mm::kSteps; ++ks) {
@@ -192,18 +200,14 @@ struct GemmCtx {
       const int koff = KM == 128 ? 0 : ((ks * 16) ^ fsw);  // swizzled 16-byte chunk ks
 #pragma unroll
       for (int j = 0; j < 4; ++j) fx[j] = Mm::load(stage + fX + j * 16 * kRowB + koff);
-      // Entering a new group rescales the accumulator by S_{g-1} / S_g.
-      // Set 0 does it just before the group's first products, set 1 right
-      // after the previous group's last ones: after each barrier one wave of
-      // every SIMD pair then multiplies while the other feeds the matrix
-      // core, instead of both multiplying at once.
+      // entering a new group rescales the accumulator by S_{g-1} / S_g
       if (gs == 0 && step > st0 * Mm::kSteps) {
         if (PARTIALS) {
 #pragma unroll
           for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-        } else if (SET == 0) {
+        } else {
           rescale(rat[step >> log2spg]);
         }
       }
@@ -212,13 +216,9 @@ struct GemmCtx {
         const typename Mm::frag fw = Mm::load(stage + fW + i * 16 * kRowB + koff);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = Mm::mma(fw, fx[j], acc[i][j]);
+        if (ks == 0 && i < kDmaPerWave) issue_one<SET, NSLOT>(nst, i);
       }
       if (PARTIALS && gs == (1 << log2spg) - 1) dump(step >> log2spg);
-      if (!PARTIALS && SET == 1) {
-        const int nx = step + 1;
-        if ((nx & ((1 << log2spg) - 1)) == 0 && nx < st1 * Mm::kSteps && (nx << (KM == 128 ? 7 : 5)) < a.K)
-          rescale(rat[nx >> log2spg]);
-      }
     }
   }
 
@@ -259,8 +259,12 @@ struct GemmCtx {
     // the slot of stage st - 1
     RRS_WAIT_VM(kDmaPerWave);
     __builtin_amdgcn_s_barrier();
-    issue<SET, (SLOT + kRing - 1) % kRing>(min(st + kRing - 1, st1 - 1));
-    if (st < st1) compute<SET, SLOT>(st);
+    constexpr int kNext = (SLOT + kRing - 1) % kRing;
+    const int nst = min(st + kRing - 1, st1 - 1);
+    if (st < st1)
+      compute<SET, SLOT, kNext>(st, nst);
+    else
+      issue<SET, kNext>(nst);
   }
 
   template <int SET>
