@@ -110,6 +110,7 @@ constexpr int kThreadsWG = kSets * kThreads;
 // arrays let the compiler tell which direct-to-LDS load a fragment read
 // depends on (with one array it would wait for every load in flight).
 constexpr int kRing = 3;
+constexpr uint32_t kBarSpinLimit = 1u << 22;  // polls before a set barrier gives up
 __shared__ __attribute__((aligned(1024))) uint8_t s_r00[kStageB];
 __shared__ __attribute__((aligned(1024))) uint8_t s_r01[kStageB];
 __shared__ __attribute__((aligned(1024))) uint8_t s_r02[kStageB];
@@ -164,6 +165,8 @@ struct GemmCtx {
   int fW, fX, fsw;
   v4f acc[8][4];
   const float* rat;
+  uint32_t* sbar;   // this set's arrival counter (LDS)
+  uint32_t nbar = 0;
 
   __device__ GemmCtx(const GemmArgs& args, const float* s_rat) : a(args), rat(s_rat) {}
 
@@ -246,6 +249,30 @@ struct GemmCtx {
       }
   }
 
+  // Barrier of the set's four waves only: an LDS arrival counter that every
+  // wave bumps once per stage, then polls until all four have (bounded
+  // poll; the count only grows within a launch). The caller has waited for
+  // its own loads and LDS accesses, so after the wait every block of the
+  // stage is in LDS and every read of the slot about to be refilled is
+  // done. The two sets of a workgroup never wait for each other, so they
+  // drift apart and one set's waits overlap the other's matrix work.
+  // The counter is accessed in inline assembly that waits for its own
+  // result: as plain LDS accesses the compiler cannot tell them apart from
+  // the direct-to-LDS loads in flight and would drain all of them first.
+  __device__ __forceinline__ void set_barrier() {
+    nbar += 4;
+    typedef __attribute__((address_space(3))) uint32_t lds_u32;
+    const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u32*)sbar));
+    const uint32_t one = 1u;
+    if (lane == 0) asm volatile("ds_add_u32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(addr), "v"(one) : "memory");
+    for (uint32_t it = 0; it < kBarSpinLimit; ++it) {
+      uint32_t n;
+      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(n) : "v"(addr) : "memory");
+      if (__builtin_amdgcn_readfirstlane(n) >= nbar) break;
+      __builtin_amdgcn_s_sleep(0);
+    }
+  }
+
   // One ring revolution: stages st .. st+2 in slots 0..2; stage s+2 is
   // fetched into the slot that stage s-1 just released. Both sets run the
   // same number of steps (the barrier is workgroup wide) and every step
@@ -258,7 +285,7 @@ struct GemmCtx {
     // wave is in flight; the barrier publishes all waves' blocks and frees
     // the slot of stage st - 1
     RRS_WAIT_VM(kDmaPerWave);
-    __builtin_amdgcn_s_barrier();
+    set_barrier();
     constexpr int kNext = (SLOT + kRing - 1) % kRing;
     const int nst = min(st + kRing - 1, st1 - 1);
     if (st < st1)
@@ -269,8 +296,7 @@ struct GemmCtx {
 
   template <int SET>
   __device__ void run(int nsteps) {
-    // prologue: the set's first two stages in flight (the first barrier also
-    // publishes the ratio table)
+    // prologue: the set's first two stages in flight
     issue<SET, 0>(st0);
     issue<SET, 1>(min(st0 + 1, st1 - 1));
     int s = 0;
@@ -288,6 +314,7 @@ struct GemmCtx {
 template <int KM, bool PARTIALS>
 __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
   __shared__ float s_rat[(1 << kMaxLog2K) / kMinG];
+  __shared__ uint32_t s_bar[kSets];
   __shared__ float s_rs[kTT];       // dx[t] 2^18 / K of the tile's tokens
   __shared__ float s_dw[kTN];       // dw[n] of the tile's output channels
   __shared__ float s_send[kSets];   // each set's last group scale
@@ -377,14 +404,14 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) c.acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  if (tid < kSets) s_bar[tid] = 0u;
+  c.sbar = &s_bar[set];
+  __syncthreads();  // tables and counters published
   if (set == 0) {
     c.template run<0>(nsteps);
   } else if (c.st1 > c.st0) {
     c.template run<1>(nsteps);
-  } else {
-    // no second half (K <= 128 or the partials dump): keep step with set 0
-    for (int s = 0; s < nsteps; ++s) __builtin_amdgcn_s_barrier();
-  }
+  }  // else: no second half (K <= 128 or the partials dump)
   if (PARTIALS) return;
 
   // ---- combine the halves ------------------------------------------------
