@@ -24,14 +24,17 @@
 //
 // Tiles: 256 output channels x 128 tokens per workgroup, 4 waves of
 // 128 x 64. The MFMA A operand is the weight tile (rows n), the B operand the
-// activation tile (rows t), so a lane's four accumulators are four
-// consecutive output channels of one token: one 16-byte store per tile.
+// activation tile (rows t), so runs of four accumulator registers are four
+// consecutive output channels of one token: 16-byte stores.
 // K advances in stages of 128 codes (64 packed bytes per row): direct
 // global -> LDS loads into 3-slot rings (two stages in flight), then
 // per-wave widening of the packed fragments -> MFMA. Two sets of 4 waves
 // split K and add their partial sums at the end.
-// v_mfma_f32_16x16x128_f8f6f4 serves G >= 128; v_mfma_f32_16x16x32_fp8_fp8
-// serves G = 32 and 64.
+// v_mfma_f32_32x32x64_f8f6f4 serves G >= 128, v_mfma_f32_16x16x32_fp8_fp8
+// G = 32 and 64. The 32 x 32 shape is chosen for its length: an MFMA hides
+// only a few VALU issue slots of the widening and rescale that go with it,
+// and a 64-cycle 32 x 32 x 64 MFMA hides about three times as many as a
+// 32-cycle 16 x 16 x 128 one for the same products.
 
 #include "rrs_internal.h"
 
@@ -40,6 +43,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kTN = 256;       // output channels per workgroup tile
 constexpr int kTT = 128;       // tokens per workgroup tile
@@ -69,34 +73,57 @@ __device__ __forceinline__ uint32_t ocodes(uint32_t w) {
   return __builtin_amdgcn_alignbit(w, w, 4) & 0x87878787u;
 }
 
+// MFMA shapes. KM: codes of K per instruction; BR: rows (and columns) of an
+// accumulator block; NQ: runs of four consecutive output channels per lane
+// in a block. Lane l's fragment holds row l % BR of a block; its codes sit
+// at logical 16-byte chunk chunk(ks, l) of the stage row plus byte inner(l).
 template <int KM>
 struct Mma;
 
 template <>
-struct Mma<128> {  // 32 codes (16 packed bytes) per lane
+struct Mma<64> {  // 32 x 32 x 64: 32 codes (16 packed bytes) per lane
   typedef v8i frag;
-  static constexpr int kSteps = 1;  // MFMA k-steps per stage
+  typedef v16f acc_t;
+  static constexpr int BR = 32, NQ = 4, kSteps = 2, kLog2K = 6;
+  __device__ static int chunk(int ks, int l) { return ks * 2 + (l >> 5); }
+  __device__ static int inner(int) { return 0; }
+  // register r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+  __device__ static int qrow(int q, int l) { return 8 * q + 4 * (l >> 5); }
   __device__ static frag load(const uint8_t* p) {
     const uint4 w = *reinterpret_cast<const uint4*>(p);
     return v8i{(int)ecodes(w.x), (int)ocodes(w.x), (int)ecodes(w.y), (int)ocodes(w.y),
                (int)ecodes(w.z), (int)ocodes(w.z), (int)ecodes(w.w), (int)ocodes(w.w)};
   }
-  __device__ static v4f mma(frag a, frag b, v4f c) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  __device__ static acc_t mma(frag a, frag b, acc_t c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
   }
+  __device__ static acc_t zero() {
+    acc_t z;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) z[e] = 0.f;
+    return z;
+  }
+  __device__ static v4f quad(const acc_t& c, int q) { return v4f{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]}; }
 };
 
 template <>
-struct Mma<32> {  // 8 codes (4 packed bytes) per lane
+struct Mma<32> {  // 16 x 16 x 32: 8 codes (4 packed bytes) per lane
   typedef long frag;
-  static constexpr int kSteps = 4;
+  typedef v4f acc_t;
+  static constexpr int BR = 16, NQ = 1, kSteps = 4, kLog2K = 5;
+  __device__ static int chunk(int ks, int) { return ks; }
+  __device__ static int inner(int l) { return (l >> 4) * 4; }
+  // register r of lane l: row 4 (l / 16) + r, column l % 16
+  __device__ static int qrow(int, int l) { return 4 * (l >> 4); }
   __device__ static frag load(const uint8_t* p) {
     const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
     return static_cast<long>(static_cast<uint64_t>(ecodes(w)) | (static_cast<uint64_t>(ocodes(w)) << 32));
   }
-  __device__ static v4f mma(frag a, frag b, v4f c) {
+  __device__ static acc_t mma(frag a, frag b, acc_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
   }
+  __device__ static acc_t zero() { return v4f{0.f, 0.f, 0.f, 0.f}; }
+  __device__ static v4f quad(const acc_t& c, int) { return c; }
 };
 
 // Split K: the workgroup is two sets of 4 waves over the same output tile;
@@ -151,7 +178,7 @@ __device__ __forceinline__ float* park_chunk(int c) {
 // barrier that follows then also publishes this wave's LDS stores.
 #define RRS_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0070)
 
-template <int KM, bool PARTIALS>
+template <int KM, bool PARTIALS, int SPG>
 struct GemmCtx {
   using Mm = Mma<KM>;
   static constexpr int kDmaPerWave = (kStageB / 1024) / (kThreads / 64);  // 6
@@ -162,18 +189,18 @@ struct GemmCtx {
   const uint8_t* gsrc[kDmaPerWave];  // this lane's row pointer for each of its DMA blocks
   int goff[kDmaPerWave];             // byte offset of its 16-byte piece
   int lblk[kDmaPerWave];             // LDS offset of each block in a stage
-  int fW, fX, fsw;
-  v4f acc[8][4];
+  static constexpr int TI = 128 / Mm::BR;  // accumulator blocks per wave along n
+  static constexpr int TJ = 64 / Mm::BR;   // and along t
+  int fW, fX, swz;
+  typename Mm::acc_t acc[TI][TJ];
   const float* rat;
   uint32_t* sbar;   // this set's arrival counter (LDS)
   uint32_t nbar = 0;
 
   __device__ GemmCtx(const GemmArgs& args, const float* s_rat) : a(args), rat(s_rat) {}
 
-  // DMA block d of stage st into ring slot SLOT
-  template <int SET, int SLOT>
-  __device__ __forceinline__ void issue_one(int st, int d) {
-    uint8_t* base = ring<SET, SLOT>();
+  // DMA block d of stage st into ring slot `base`
+  __device__ __forceinline__ void issue_one(uint8_t* base, int st, int d) {
     const int kb = st * kRowB;
     // a piece past the end of a row (K = 64) re-reads the row's first
     // bytes: in bounds, and never multiplied (only K codes are used)
@@ -181,69 +208,86 @@ struct GemmCtx {
     __builtin_amdgcn_global_load_lds(gsrc[d] + off, (__attribute__((address_space(3))) void*)(base + lblk[d]), 16, 0, 0);
   }
 
-  template <int SET, int SLOT>
-  __device__ __forceinline__ void issue(int st) {
+  __device__ __forceinline__ void issue(uint8_t* base, int st) {
 #pragma unroll
-    for (int d = 0; d < kDmaPerWave; ++d) issue_one<SET, SLOT>(st, d);
+    for (int d = 0; d < kDmaPerWave; ++d) issue_one(base, st, d);
   }
 
   // One stage of products; the DMA of stage nst into slot NSLOT is issued
   // one block after each of the first rows of products, so the address
   // unit's work for it spreads over the stage instead of stalling every
   // wave right after the barrier.
-  template <int SET, int SLOT, int NSLOT>
-  __device__ __forceinline__ void compute(int st, int nst) {
-    const uint8_t* stage = ring<SET, SLOT>();
+  __device__ __forceinline__ void compute(const uint8_t* stage, uint8_t* next, int st, int nst) {
 #pragma unroll
     for (int ks = 0; ks < Mm::kSteps; ++ks) {
       const int step = st * Mm::kSteps + ks;
-      if (step << (KM == 128 ? 7 : 5) >= a.K) break;  // K = 64: half a stage
+      if (step << Mm::kLog2K >= a.K) break;  // K = 64: half a stage
       const int gs = step & ((1 << log2spg) - 1);
-      typename Mm::frag fx[4];
-      const int koff = KM == 128 ? 0 : ((ks * 16) ^ fsw);  // swizzled 16-byte chunk ks
+      // logical chunk of this k-step, stored at chunk position logical ^ swizzle
+      const int koff = ((Mm::chunk(ks, lane) * 16) ^ swz) + Mm::inner(lane);
+      typename Mm::frag fx[TJ];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fx[j] = Mm::load(stage + fX + j * 16 * kRowB + koff);
-      // entering a new group rescales the accumulator by S_{g-1} / S_g
-      if (gs == 0 && step > st0 * Mm::kSteps) {
-        if (PARTIALS) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < TJ; ++j) fx[j] = Mm::load(stage + fX + j * Mm::BR * kRowB + koff);
+      // Entering a new group rescales the accumulator by S_{g-1} / S_g (the
+      // partials dump clears it instead). With SPG (MFMA k-steps per group)
+      // known at compile time, each block is multiplied just before its
+      // first product of the group: its previous product was issued a full
+      // row of blocks earlier and has retired, so neither the multiplies nor
+      // the matrix core wait on each other. Otherwise (G > 128, one group
+      // over several stages) the whole accumulator is scaled at the group's
+      // first k-step.
+      if constexpr (SPG > 0 && !PARTIALS) {
+        if (ks % SPG == 0) {  // folds: ks is an unrolled index
+          const float r = step > st0 * Mm::kSteps ? rat[step >> log2spg] : 1.f;
+          products<true>(stage, next, koff, fx, r, ks, nst);
         } else {
-          rescale(rat[step >> log2spg]);
+          products<false>(stage, next, koff, fx, 1.f, ks, nst);
         }
-      }
+      } else {
+        if (gs == 0 && step > st0 * Mm::kSteps) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const typename Mm::frag fw = Mm::load(stage + fW + i * 16 * kRowB + koff);
+          for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = Mm::mma(fw, fx[j], acc[i][j]);
-        if (ks == 0 && i < kDmaPerWave) issue_one<SET, NSLOT>(nst, i);
+            for (int j = 0; j < TJ; ++j) acc[i][j] = PARTIALS ? Mm::zero() : acc[i][j] * rat[step >> log2spg];
+        }
+        products<false>(stage, next, koff, fx, 1.f, ks, nst);
       }
       if (PARTIALS && gs == (1 << log2spg) - 1) dump(step >> log2spg);
     }
   }
 
-  __device__ __forceinline__ void rescale(float r) {
+  // The products of one k-step; RS: multiply each accumulator block by r
+  // right before its product. One DMA block of the next stage goes out after
+  // each row of products.
+  template <bool RS>
+  __device__ __forceinline__ void products(const uint8_t* stage, uint8_t* next, int koff,
+                                           const typename Mm::frag (&fx)[TJ], float r, int ks, int nst) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < TI; ++i) {
+      const typename Mm::frag fw = Mm::load(stage + fW + i * Mm::BR * kRowB + koff);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] *= r;
+      for (int j = 0; j < TJ; ++j) acc[i][j] = Mm::mma(fw, fx[j], RS ? acc[i][j] * r : acc[i][j]);
+      const int d = ks * TI + i;
+      if (d < kDmaPerWave) issue_one(next, nst, d);
+    }
   }
 
   __device__ void dump(int g) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = t0 + wt * 64 + j * 16 + (lane & 15);
+      for (int j = 0; j < TJ; ++j) {
+        const int t = t0 + wt * 64 + j * Mm::BR + (lane % Mm::BR);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int n = n0 + wn * 128 + i * 16 + (lane >> 4) * 4 + e;
-          if (t >= a.pm0 && t < a.pm1 && n >= a.pn0 && n < a.pn1) {
-            const size_t o = (static_cast<size_t>(t - a.pm0) * (a.pn1 - a.pn0) + (n - a.pn0)) * ngroups + g;
-            a.P[o] = static_cast<int32_t>(acc[i][j][e] * kUnit);
+        for (int q = 0; q < Mm::NQ; ++q) {
+          const v4f v = Mm::quad(acc[i][j], q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int n = n0 + wn * 128 + i * Mm::BR + Mm::qrow(q, lane) + e;
+            if (t >= a.pm0 && t < a.pm1 && n >= a.pn0 && n < a.pn1) {
+              const size_t o = (static_cast<size_t>(t - a.pm0) * (a.pn1 - a.pn0) + (n - a.pn0)) * ngroups + g;
+              a.P[o] = static_cast<int32_t>(v[e] * kUnit);
+            }
           }
         }
       }
@@ -273,54 +317,64 @@ struct GemmCtx {
     }
   }
 
-  // One ring revolution: stages st .. st+2 in slots 0..2; stage s+2 is
-  // fetched into the slot that stage s-1 just released. Both sets run the
-  // same number of steps (the barrier is workgroup wide) and every step
-  // issues the same number of loads (past the set's last stage it re-reads
-  // that stage into the released slot, which is never read again), so the
-  // wait is constant.
-  template <int SET, int SLOT>
-  __device__ __forceinline__ void step(int st) {
+  // One stage: stage st is read from slot `cur`, stage st + 2 is fetched
+  // into `next`, the slot stage st - 1 just released. Every step issues the
+  // same number of loads (past the set's last stage it re-reads that stage
+  // into the released slot, which is never read again), so the wait is
+  // constant.
+  __device__ __forceinline__ void step(const uint8_t* cur, uint8_t* next, int st) {
     // this stage's blocks have landed once at most one newer stage of this
-    // wave is in flight; the barrier publishes all waves' blocks and frees
+    // wave is in flight; the barrier publishes the set's blocks and frees
     // the slot of stage st - 1
     RRS_WAIT_VM(kDmaPerWave);
     set_barrier();
-    constexpr int kNext = (SLOT + kRing - 1) % kRing;
     const int nst = min(st + kRing - 1, st1 - 1);
     if (st < st1)
-      compute<SET, SLOT, kNext>(st, nst);
+      compute(cur, next, st, nst);
     else
-      issue<SET, kNext>(nst);
+      issue(next, st);
+  }
+
+  // Steps s .. s + n - 1 (n <= 3) of the set, the ring slots passed as
+  // distinct restrict pointers: inlined, they give every direct-to-LDS load
+  // and every fragment read an alias scope, from which the compiler's wait
+  // insertion tells which loads in flight a read depends on. Without scopes
+  // it makes each fragment read wait for every load in flight, the one
+  // fetched two stages ahead included.
+  __device__ __forceinline__ void revolution(int s, int n, uint8_t* __restrict__ r0, uint8_t* __restrict__ r1,
+                                             uint8_t* __restrict__ r2) {
+    step(r0, r2, st0 + s);
+    if (n > 1) step(r1, r0, st0 + s + 1);
+    if (n > 2) step(r2, r1, st0 + s + 2);
   }
 
   template <int SET>
   __device__ void run(int nsteps) {
+    uint8_t* r0 = ring<SET, 0>();
+    uint8_t* r1 = ring<SET, 1>();
+    uint8_t* r2 = ring<SET, 2>();
     // prologue: the set's first two stages in flight
-    issue<SET, 0>(st0);
-    issue<SET, 1>(min(st0 + 1, st1 - 1));
+    issue(r0, st0);
+    issue(r1, min(st0 + 1, st1 - 1));
     int s = 0;
-    for (; s + kRing <= nsteps; s += kRing) {
-      step<SET, 0>(st0 + s);
-      step<SET, 1>(st0 + s + 1);
-      step<SET, 2>(st0 + s + 2);
-    }
-    if (s < nsteps) step<SET, 0>(st0 + s);
-    if (s + 1 < nsteps) step<SET, 1>(st0 + s + 1);
+    for (; s + kRing <= nsteps; s += kRing) revolution(s, kRing, r0, r1, r2);
+    if (s < nsteps) revolution(s, nsteps - s, r0, r1, r2);
     RRS_WAIT_VM(0);
   }
 };
 
-template <int KM, bool PARTIALS>
+// SPG: MFMA k-steps per group when a group is a whole number of k-steps
+// that divides a stage (the rescale then folds into the product loop), else 0
+template <int KM, bool PARTIALS, int SPG>
 __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
   __shared__ float s_rat[(1 << kMaxLog2K) / kMinG];
   __shared__ uint32_t s_bar[kSets];
   __shared__ float s_rs[kTT];       // dx[t] 2^18 / K of the tile's tokens
   __shared__ float s_dw[kTN];       // dw[n] of the tile's output channels
   __shared__ float s_send[kSets];   // each set's last group scale
-  GemmCtx<KM, PARTIALS> c(a, s_rat);
+  GemmCtx<KM, PARTIALS, SPG> c(a, s_rat);
   const int tid = threadIdx.x;
-  const int set = tid / kThreads;
+  const int set = __builtin_amdgcn_readfirstlane(tid / kThreads);  // uniform: stage bounds stay scalar
   const int stid = tid % kThreads;
   c.lane = stid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(stid >> 6);  // uniform, for scalar addressing
@@ -341,7 +395,7 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
 
   c.Kb = a.K / 2;
   c.nstage = (a.K + 127) / 128;
-  c.log2spg = a.log2G - (KM == 128 ? 7 : 5);
+  c.log2spg = a.log2G - Mma<KM>::kLog2K;  // MFMA k-steps per group
   c.ngroups = a.K >> a.log2G;
   // K halves (the partials dump keeps whole groups in one set)
   const int half = PARTIALS ? c.nstage : (c.nstage + 1) / 2;
@@ -376,8 +430,8 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
   // 32 LDS banks (rows 64 bytes apart would otherwise hit the same banks
   // every two rows).
 #pragma unroll
-  for (int d = 0; d < GemmCtx<KM, PARTIALS>::kDmaPerWave; ++d) {
-    const int blk = wave * GemmCtx<KM, PARTIALS>::kDmaPerWave + d;
+  for (int d = 0; d < GemmCtx<KM, PARTIALS, SPG>::kDmaPerWave; ++d) {
+    const int blk = wave * GemmCtx<KM, PARTIALS, SPG>::kDmaPerWave + d;
     const int r = (blk & 15) * 16 + (c.lane >> 2);
     c.goff[d] = ((c.lane & 3) ^ ((c.lane >> 3) & 3)) * 16;
     c.lblk[d] = blk * 1024;
@@ -390,19 +444,18 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
     }
   }
 
-  // fragment offsets: row (lane & 15) of each 16-row tile; logical 16-byte
-  // chunk lane >> 4 (KM = 128) or ks with bytes (lane >> 4) * 4 inside it
-  // (KM = 32), stored at chunk position logical ^ ((row >> 1) & 3)
-  const int sw = (((c.lane & 15) >> 1) & 3) * 16;
-  const int fbyte = (KM == 128) ? (((c.lane >> 4) * 16) ^ sw) : (c.lane >> 4) * 4;
-  c.fsw = KM == 128 ? 0 : sw;
-  c.fW = (c.wn * 128 + (c.lane & 15)) * kRowB + fbyte;
-  c.fX = kWB + (c.wt * 64 + (c.lane & 15)) * kRowB + fbyte;
+  // fragment rows: row lane % BR of each BR-row block; the swizzle of the
+  // row's 16-row DMA block is ((row & 15) >> 1) & 3
+  constexpr int BR = Mma<KM>::BR;
+  c.swz = (((c.lane & 15) >> 1) & 3) * 16;
+  c.fW = (c.wn * 128 + (c.lane % BR)) * kRowB;
+  c.fX = kWB + (c.wt * 64 + (c.lane % BR)) * kRowB;
+  constexpr int TI = GemmCtx<KM, PARTIALS, SPG>::TI, TJ = GemmCtx<KM, PARTIALS, SPG>::TJ, NQ = Mma<KM>::NQ;
 
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) c.acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TJ; ++j) c.acc[i][j] = Mma<KM>::zero();
 
   if (tid < kSets) s_bar[tid] = 0u;
   c.sbar = &s_bar[set];
@@ -423,14 +476,19 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
   // so a partial that cancels to zero stays exactly zero.
   const bool one_group = c.ngroups == 1;
   const float s_end = s_send[set];
+  // park chunk of run q of block (i, j) of this wave (32 chunks of 1 KiB)
+  auto chunk_of = [&](int i, int j, int q) { return wave * 32 + (i * TJ + j) * NQ + q; };
   __syncthreads();  // all rings idle: park set 1's 4 x 32 tiles of 1 KiB there
   if (set == 1) {
     // no second half (K <= 128): park zeros
     const float m1 = c.st1 > c.st0 ? (one_group ? 1.f : s_end) : 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) reinterpret_cast<v4f*>(park_chunk(wave * 32 + i * 4 + j))[c.lane] = c.acc[i][j] * m1;
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+          reinterpret_cast<v4f*>(park_chunk(chunk_of(i, j, q)))[c.lane] = Mma<KM>::quad(c.acc[i][j], q) * m1;
   }
   __syncthreads();
   if (set == 1) return;
@@ -439,51 +497,41 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
 
   // ---- epilogue: Y[t, n..n+3] = (both halves, absolute) 2^18 / K dx[t] dw[n]
   const bool full = c.t0 + kTT <= a.M && c.n0 + kTN <= a.N && (a.N & 3) == 0;  // uniform
-  if (full) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int nl = c.wn * 128 + i * 16 + (c.lane >> 4) * 4;
-      const float4 dwv = *reinterpret_cast<const float4*>(s_dw + nl);
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tl = c.wt * 64 + j * 16 + (c.lane & 15);
-        const v4f v = (c.acc[i][j] * m0 + reinterpret_cast<const v4f*>(park_chunk(wave * 32 + i * 4 + j))[c.lane]) *
-                      (fin * s_rs[tl]);
-        *reinterpret_cast<float4*>(a.Y + static_cast<size_t>(c.t0 + tl) * a.N + c.n0 + nl) =
-            make_float4(v[0] * dwv.x, v[1] * dwv.y, v[2] * dwv.z, v[3] * dwv.w);
-      }
-    }
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int nl = c.wn * 128 + i * 16 + (c.lane >> 4) * 4;  // column in the tile
-    const int n = c.n0 + nl;
-    const float4 dwv = *reinterpret_cast<const float4*>(s_dw + nl);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tl = c.wt * 64 + j * 16 + (c.lane & 15);
+    for (int j = 0; j < TJ; ++j) {
+      const int tl = c.wt * 64 + j * BR + (c.lane % BR);  // token in the tile
       const int t = c.t0 + tl;
-      const v4f v = (c.acc[i][j] * m0 + reinterpret_cast<const v4f*>(park_chunk(wave * 32 + i * 4 + j))[c.lane]) *
-                    (fin * s_rs[tl]);
-      if (t < a.M && n < a.N) {
-        float* y = a.Y + static_cast<size_t>(t) * a.N + n;
-        y[0] = v[0] * dwv.x;
-        if (n + 1 < a.N) y[1] = v[1] * dwv.y;
-        if (n + 2 < a.N) y[2] = v[2] * dwv.z;
-        if (n + 3 < a.N) y[3] = v[3] * dwv.w;
+      const float rs = fin * s_rs[tl];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int nl = c.wn * 128 + i * BR + Mma<KM>::qrow(q, c.lane);  // first of 4 channels
+        const int n = c.n0 + nl;
+        const float4 dwv = *reinterpret_cast<const float4*>(s_dw + nl);
+        const v4f v = (Mma<KM>::quad(c.acc[i][j], q) * m0 +
+                       reinterpret_cast<const v4f*>(park_chunk(chunk_of(i, j, q)))[c.lane]) * rs;
+        if (full) {
+          *reinterpret_cast<float4*>(a.Y + static_cast<size_t>(t) * a.N + n) =
+              make_float4(v[0] * dwv.x, v[1] * dwv.y, v[2] * dwv.z, v[3] * dwv.w);
+        } else if (t < a.M && n < a.N) {
+          float* y = a.Y + static_cast<size_t>(t) * a.N + n;
+          y[0] = v[0] * dwv.x;
+          if (n + 1 < a.N) y[1] = v[1] * dwv.y;
+          if (n + 2 < a.N) y[2] = v[2] * dwv.z;
+          if (n + 3 < a.N) y[3] = v[3] * dwv.w;
+        }
       }
     }
-  }
 }
 
-template <int KM>
+template <int KM, int SPG>
 hipError_t launch_km(const GemmArgs& a, bool partials, hipStream_t s) {
   const dim3 grid(a.tiles_t * a.tiles_n);
   if (partials)
-    hipLaunchKernelGGL((gemm_kernel<KM, true>), grid, dim3(kThreadsWG), 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<KM, true, 0>), grid, dim3(kThreadsWG), 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_kernel<KM, false>), grid, dim3(kThreadsWG), 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<KM, false, SPG>), grid, dim3(kThreadsWG), 0, s, a);
   return hipGetLastError();
 }
 
@@ -509,7 +557,12 @@ hipError_t launch_gemm(const uint8_t* xq, const float* dx, const float* S, int M
   a.tiles_t = (M + kTT - 1) / kTT;
   a.tiles_n = (N + kTN - 1) / kTN;
   const bool partials = P != nullptr;
-  return G >= 128 ? launch_km<128>(a, partials, s) : launch_km<32>(a, partials, s);
+  switch (G) {
+    case 32: return launch_km<32, 1>(a, partials, s);
+    case 64: return launch_km<32, 2>(a, partials, s);
+    case 128: return launch_km<64, 2>(a, partials, s);
+    default: return launch_km<64, 0>(a, partials, s);
+  }
 }
 
 }  // namespace rrs
