@@ -554,9 +554,10 @@ hipError_t launch_gemm(const uint8_t* xq, const float* dx, const float* S, int M
   a.log2G = __builtin_ctz(static_cast<unsigned>(G));
   a.pm0 = m0; a.pm1 = m1; a.pn0 = n0; a.pn1 = n1;
   if (M == 0 || N == 0) return hipSuccess;
+  const bool partials = P != nullptr;
+  if (!partials && gemm_small_applies(M, log2K, G)) return launch_gemm_small(xq, dx, S, M, log2K, N, G, wq, dw, Y, s);
   a.tiles_t = (M + kTT - 1) / kTT;
   a.tiles_n = (N + kTN - 1) / kTN;
-  const bool partials = P != nullptr;
   switch (G) {
     case 32: return launch_km<32, 1>(a, partials, s);
     case 64: return launch_km<32, 2>(a, partials, s);

@@ -1,0 +1,238 @@
+// Grouped INT4 x INT4 GEMM of the RRS A4W4 linear for few tokens (M <= 64,
+// decode-shaped calls), on gfx950.
+//
+// Same arithmetic as the tiled kernel (Y[t, n] = (1/K) dx[t] dw[n]
+// sum_g S[g] P_g[t, n], group scales applied to each group's exact integer
+// partial before fp32 accumulation; RRS summary page, atlas.scime.ai,
+// "Approach"; RRS rebuttal page, paperhub.cn, "Novelty"), shaped for the
+// case where the packed weights are the only large operand and the run time
+// is the time to stream them from HBM once.
+//
+// One workgroup owns 32 output channels and every token (one 32 x 32
+// accumulator block per 32 tokens, v_mfma_f32_32x32x64_f8f6f4 on codes
+// widened to exact fp8 subnormals as in the tiled kernel). Its 8 waves
+// split K into equal runs of k-steps (64 codes); each wave rescales its
+// accumulator when it enters a new group, makes its sum absolute at the end
+// (times the scale of its last group), and the 8 sums are added in LDS in a
+// fixed order. A group cut between two waves is thus scaled in two exact
+// integer pieces: the same sum up to one fp32 rounding per piece.
+//
+// Loads: a wave reads its operands a round (4 k-steps, one 128-byte line of
+// every row) at a time with whole-line coalesced loads into registers, two
+// rounds ahead; at its turn a round goes through a wave-private LDS buffer
+// (row-major, 16-byte chunks XOR-swizzled by row) that turns it into MFMA
+// fragments. With N / 32 workgroups (256 at N = 8192) every CU streams its
+// own slice of the weights.
+
+#include <type_traits>
+
+#include "rrs_internal.h"
+
+namespace rrs {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTN = 32;      // output channels per workgroup
+constexpr int kRound = 4;    // k-steps per round (128 bytes of a row)
+constexpr int kRows = 128;   // bytes of a row per round
+constexpr float kUnit = 262144.0f;  // 2^18: one integer product in accumulator units
+
+struct SmallArgs {
+  const uint8_t* xq;
+  const float* dx;
+  const float* S;
+  const uint8_t* wq;
+  const float* dw;
+  float* Y;
+  int M, N, K, log2G;
+};
+
+// a-codes (even) and b-codes (odd) of a packed word as e4m3 subnormals
+__device__ __forceinline__ uint32_t ecodes(uint32_t w) { return w & 0x87878787u; }
+__device__ __forceinline__ uint32_t ocodes(uint32_t w) { return __builtin_amdgcn_alignbit(w, w, 4) & 0x87878787u; }
+__device__ __forceinline__ v8i widen(v4u w) {
+  return v8i{(int)ecodes(w.x), (int)ocodes(w.x), (int)ecodes(w.y), (int)ocodes(w.y),
+             (int)ecodes(w.z), (int)ocodes(w.z), (int)ecodes(w.w), (int)ocodes(w.w)};
+}
+
+// byte offset of 16-byte chunk c of row r in a wave's round buffer
+__device__ __forceinline__ int swz(int r, int c) { return r * kRows + ((c ^ (r & 7)) << 4); }
+
+// TJ: 32-token blocks (1 for M <= 32, 2 for M <= 64); NR: rounds of loads
+// in flight (1 or 2; divides the wave's round count); KS: min(k-steps per
+// group, kRound), the spacing of possible group starts inside a round.
+template <int TJ, int NR, int KS>
+__global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
+  constexpr int kWL = 4;            // W loads per lane per round (32 rows / 8)
+  constexpr int kXL = 4 * TJ;       // X loads per lane per round
+  constexpr int kBuf = (32 + 32 * TJ) * kRows;  // round buffer bytes per wave
+  static_assert(TJ * 16 * 64 * 4 <= kBuf, "a wave's sums fit its round buffer");
+  __shared__ float s_rat[(1 << kMaxLog2K) / 64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[kWaves][kBuf];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * kTN;
+  const int Kb = a.K / 2;
+  const int ngroups = a.K >> a.log2G;
+  const int log2spg = a.log2G - 6;
+  const int kspg = 1 << log2spg;      // k-steps per group (G >= 64)
+  const int kpw = (a.K >> 6) / kWaves;  // k-steps per wave (a multiple of kRound)
+  const int ks0 = wave * kpw;
+  const int rounds = kpw / kRound;
+
+  for (int g = tid; g < ngroups; g += kThreads) s_rat[g] = g > 0 ? a.S[g - 1] / a.S[g] : 1.f;
+  __syncthreads();
+
+  // coalesced load i of a round: row 8 i + lane / 8, chunk lane % 8 (rows
+  // clamped to the matrix; clamped rows feed outputs that are never stored)
+  const int lr = lane >> 3, lc = lane & 7;
+  const uint8_t* wsrc[kWL];
+  const uint8_t* xsrc[kXL];
+#pragma unroll
+  for (int i = 0; i < kWL; ++i)
+    wsrc[i] = a.wq + static_cast<size_t>(min(n0 + 8 * i + lr, a.N - 1)) * Kb + ks0 * 32 + lc * 16;
+#pragma unroll
+  for (int i = 0; i < kXL; ++i)
+    xsrc[i] = a.xq + static_cast<size_t>(min(8 * i + lr, a.M - 1)) * Kb + ks0 * 32 + lc * 16;
+
+  uint8_t* buf = s_buf[wave];
+  v4u rw[NR][kWL], rx[NR][kXL];
+  v16f acc[TJ];
+#pragma unroll
+  for (int j = 0; j < TJ; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+
+#pragma unroll
+  for (int s = 0; s < NR; ++s) {
+    const int off = min(s, rounds - 1) * kRows;
+#pragma unroll
+    for (int i = 0; i < kWL; ++i) rw[s][i] = *reinterpret_cast<const v4u*>(wsrc[i] + off);
+#pragma unroll
+    for (int i = 0; i < kXL; ++i) rx[s][i] = *reinterpret_cast<const v4u*>(xsrc[i] + off);
+  }
+  for (int r0 = 0; r0 < rounds; r0 += NR) {
+#pragma unroll
+    for (int s = 0; s < NR; ++s) {
+      const int r = r0 + s;
+      // round -> LDS: W rows 0..31, then X rows 32.. (in-order LDS within
+      // the wave: these writes land after the previous round's fragment
+      // reads)
+#pragma unroll
+      for (int i = 0; i < kWL; ++i) *reinterpret_cast<v4u*>(buf + swz(8 * i + lr, lc)) = rw[s][i];
+#pragma unroll
+      for (int i = 0; i < kXL; ++i) *reinterpret_cast<v4u*>(buf + swz(32 + 8 * i + lr, lc)) = rx[s][i];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // refill the slot with the round NR ahead (past the end: the last
+      // round again, so every iteration issues the same loads)
+      const int off = min(r + NR, rounds - 1) * kRows;
+#pragma unroll
+      for (int i = 0; i < kWL; ++i) rw[s][i] = *reinterpret_cast<const v4u*>(wsrc[i] + off);
+#pragma unroll
+      for (int i = 0; i < kXL; ++i) rx[s][i] = *reinterpret_cast<const v4u*>(xsrc[i] + off);
+#pragma unroll
+      for (int u = 0; u < kRound; ++u) {
+        const int ks = r * kRound + u;
+        // entering a new group: the accumulator goes from units of S_{g-1}
+        // to units of S_g. Group starts fall only on k-steps with
+        // u % KS == 0; the multiply there is unconditional (by 1 when no
+        // group starts, and at the wave's first k-step, whose sum so far is
+        // empty).
+        if (u % KS == 0) {
+          const int kg = ks0 + ks;
+          const float rg = s_rat[kg >> log2spg];
+          const float f = (ks > 0 && (kg & (kspg - 1)) == 0) ? rg : 1.f;
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) acc[j] *= f;
+        }
+        const int c = 2 * u + (lane >> 5);
+        const v8i fw = widen(*reinterpret_cast<const v4u*>(buf + swz(lane & 31, c)));
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const v8i fx = widen(*reinterpret_cast<const v4u*>(buf + swz(32 + 32 * j + (lane & 31), c)));
+          acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw, fx, acc[j], 0, 0, 0, 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // absolute sums, times the scale of the group of the wave's last k-step,
+  // into the wave's own buffer (its fragment reads are done: in-order LDS)
+  const float s_last = a.S[(ks0 + kpw - 1) >> log2spg];
+  float* part = reinterpret_cast<float*>(buf);
+#pragma unroll
+  for (int j = 0; j < TJ; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) part[(j * 16 + e) * 64 + lane] = acc[j][e] * s_last;
+  __syncthreads();
+
+  // output element (token t, channel n0 + nl): register e = (nl / 8) * 4 +
+  // nl % 4 of lane t % 32 + 32 ((nl / 4) % 2) in block t / 32
+  const float base = kUnit / static_cast<float>(a.K);
+  for (int id = tid; id < TJ * 32 * kTN; id += kThreads) {
+    const int t = id / kTN, nl = id % kTN;
+    const int n = n0 + nl;
+    if (t >= a.M || n >= a.N) continue;
+    const int j = t >> 5, e = (nl >> 3) * 4 + (nl & 3), l = (t & 31) + 32 * ((nl >> 2) & 1);
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) v += reinterpret_cast<const float*>(s_buf[w])[(j * 16 + e) * 64 + l];
+    a.Y[static_cast<size_t>(t) * a.N + n] = v * (a.dx[t] * base) * a.dw[n];
+  }
+}
+
+}  // namespace
+
+// K >= 2048: every wave gets at least one whole round
+bool gemm_small_applies(int M, int log2K, int G) { return M >= 1 && M <= 64 && G >= 64 && log2K >= 11; }
+
+hipError_t launch_gemm_small(const uint8_t* xq, const float* dx, const float* S, int M, int log2K, int N, int G,
+                             const uint8_t* wq, const float* dw, float* Y, hipStream_t s) {
+  if (!gemm_small_applies(M, log2K, G)) return hipErrorInvalidValue;
+  SmallArgs a{};
+  a.xq = xq;
+  a.dx = dx;
+  a.S = S;
+  a.wq = wq;
+  a.dw = dw;
+  a.Y = Y;
+  a.M = M;
+  a.N = N;
+  a.K = 1 << log2K;
+  a.log2G = __builtin_ctz(static_cast<unsigned>(G));
+  const dim3 grid((N + kTN - 1) / kTN);
+  const int rounds = (a.K >> 6) / kWaves / kRound;  // 1, 2, 4 for K = 2048, 4096, 8192
+  const int spg = G >> 6;
+  const int ks = spg < kRound ? spg : kRound;
+  // instantiations: TJ in {1, 2}, NR in {1, 2}, KS in {1, 2, 4}
+  auto go = [&](auto tj, auto nr) {
+    constexpr int TJ = decltype(tj)::value, NR = decltype(nr)::value;
+    switch (ks) {
+      case 1: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 1>), grid, dim3(kThreads), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 2>), grid, dim3(kThreads), 0, s, a); break;
+      default: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, kRound>), grid, dim3(kThreads), 0, s, a); break;
+    }
+  };
+  auto by_rounds = [&](auto tj) {
+    if (rounds == 1)
+      go(tj, std::integral_constant<int, 1>{});
+    else
+      go(tj, std::integral_constant<int, 2>{});
+  };
+  if (M <= 32)
+    by_rounds(std::integral_constant<int, 1>{});
+  else
+    by_rounds(std::integral_constant<int, 2>{});
+  return hipGetLastError();
+}
+
+}  // namespace rrs

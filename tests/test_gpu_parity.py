@@ -115,10 +115,14 @@ def test_prepare_weights_zero_column():
     assert not codes[4].any().item() and dw[4].item() == 0.0
 
 
-# (M, N, K, G) for the grouped GEMM, fed oracle codes
+# (M, N, K, G) for the grouped GEMM, fed oracle codes. M <= 64 with G >= 64
+# runs the few-token kernel (K split over 8 waves, groups cut between
+# waves: (32, 40, 128, 64), (48, 70, 1024, 256), (64, 33, 4096, 4096)).
 GEMM_SHAPES = [
     (16, 256, 256, 128), (1, 1, 64, 32), (130, 200, 512, 32), (64, 64, 64, 64),
     (257, 129, 1024, 256), (128, 128, 4096, 4096), (33, 300, 2048, 128), (5, 17, 8192, 512),
+    (1, 4096, 8192, 128), (32, 40, 128, 64), (48, 70, 1024, 256), (64, 33, 4096, 4096),
+    (17, 257, 512, 64),
 ]
 
 
