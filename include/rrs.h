@@ -21,7 +21,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All data pointers are DEVICE pointers (hipMalloc / torch CUDA tensors)
- *   unless stated otherwise. The caller allocates and owns every buffer; the
+ *   unless stated otherwise, each 16-byte aligned (the kernels move data in
+ *   16-byte accesses; a misaligned pointer is rejected with RRS_EINVAL). The caller allocates and owns every buffer; the
  *   library never allocates, frees or synchronises, and keeps no global
  *   mutable state.
  * - Every call is asynchronous on the given stream `s` (0 = null stream).

@@ -19,6 +19,11 @@ bool valid_K(int K) {
 }
 bool valid_G(int G, int K) { return pow2(G) && G >= rrs::kMinG && G <= K; }
 
+// every device pointer argument is read or written with 16-byte accesses
+bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+template <typename... P>
+bool all_a16(const P*... p) { return (a16(p) && ...); }
+
 // Words of the synchronisation block that must start at zero (all control
 // words, the two-launch maxima and the one-launch flags).
 constexpr size_t kInitSyncBytes = sizeof(uint32_t) * rrs::kSyncPartials;
@@ -78,7 +83,7 @@ RRS_API size_t rrs_calibrate_workspace_bytes(int K) {
 }
 
 RRS_API int rrs_workspace_init(void* ws, size_t ws_bytes, hipStream_t s) {
-  if (ws == nullptr || ws_bytes < 256 || ws_bytes % 4) return RRS_EINVAL;
+  if (ws == nullptr || ws_bytes < 256 || ws_bytes % 4 || !a16(ws)) return RRS_EINVAL;
   const size_t n = (ws_bytes < kInitSyncBytes ? ws_bytes : kInitSyncBytes) / sizeof(uint32_t);
   return hip_status(rrs::launch_zero_u32(static_cast<uint32_t*>(ws), n, s));
 }
@@ -88,6 +93,7 @@ RRS_API int rrs_calibrate_perm(const void* X_cal_fp16, int T, int K, int32_t* pe
   if (X_cal_fp16 == nullptr || perm == nullptr || ws == nullptr) return RRS_EINVAL;
   if (T < 1 || !valid_K(K)) return RRS_EINVAL;
   if (ws_bytes < rrs_calibrate_workspace_bytes(K)) return RRS_EINVAL;
+  if (!all_a16(X_cal_fp16, perm, ws)) return RRS_EINVAL;
   return hip_status(rrs::launch_calibrate(static_cast<const uint16_t*>(X_cal_fp16), T, ilog2(K), perm,
                                           static_cast<uint32_t*>(ws), s));
 }
@@ -96,6 +102,7 @@ RRS_API int rrs_prepare_weights(const void* W_fp16, int K, int N, const int32_t*
                                 hipStream_t s) {
   if (W_fp16 == nullptr || perm == nullptr || wq == nullptr) return RRS_EINVAL;
   if (!valid_K(K) || N < 1) return RRS_EINVAL;
+  if (!all_a16(W_fp16, perm, wq)) return RRS_EINVAL;
   uint8_t* codes = static_cast<uint8_t*>(wq);
   float* dw = reinterpret_cast<float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
   return hip_status(rrs::launch_weight_prep(static_cast<const uint16_t*>(W_fp16), ilog2(K), N, perm,
@@ -109,6 +116,7 @@ RRS_API int rrs_frontend(const void* X_fp16, int M, int K, int G, const int32_t*
   if (perm == nullptr || S == nullptr || ws == nullptr) return RRS_EINVAL;
   if (M > 0 && (X_fp16 == nullptr || xq == nullptr || dx == nullptr)) return RRS_EINVAL;
   if (ws_bytes < sync_bytes(K, G)) return RRS_EINVAL;
+  if (!all_a16(X_fp16, perm, xq, dx, S, ws)) return RRS_EINVAL;
   if (M == 0) return RRS_OK;
   return hip_status(rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, ilog2(K), G, perm, xq,
                                          dx, S, static_cast<uint32_t*>(ws), flags, s));
@@ -126,6 +134,7 @@ RRS_API int rrs_gemm(const uint8_t* xq, const float* dx, const float* S, int M, 
   if (M < 0 || N < 1 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;
   if (S == nullptr || wq == nullptr) return RRS_EINVAL;
   if (M > 0 && (xq == nullptr || dx == nullptr || Y == nullptr)) return RRS_EINVAL;
+  if (!all_a16(xq, dx, S, wq, Y)) return RRS_EINVAL;
   if (M == 0) return RRS_OK;
   const uint8_t* codes = static_cast<const uint8_t*>(wq);
   const float* dw = reinterpret_cast<const float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
@@ -137,6 +146,7 @@ RRS_API int rrs_gemm_partials(const uint8_t* xq, int M, int K, int N, int G, con
   if (M < 1 || N < 1 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;
   if (xq == nullptr || wq == nullptr || P == nullptr) return RRS_EINVAL;
   if (m0 < 0 || m1 > M || m0 >= m1 || n0 < 0 || n1 > N || n0 >= n1) return RRS_EINVAL;
+  if (!all_a16(xq, wq, P)) return RRS_EINVAL;
   const uint8_t* codes = static_cast<const uint8_t*>(wq);
   const float* dw = reinterpret_cast<const float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
   return hip_status(rrs::launch_gemm(xq, nullptr, nullptr, M, ilog2(K), N, G, codes, dw, nullptr, P, m0,
@@ -150,6 +160,7 @@ RRS_API int rrs_linear(const void* X_fp16, int M, int K, int N, int G, const int
   if (M > 0 && (X_fp16 == nullptr || Y == nullptr)) return RRS_EINVAL;
   const WsLayout l = ws_layout(M, K, G);
   if (ws_bytes < l.total) return RRS_EINVAL;
+  if (!all_a16(X_fp16, perm, wq, Y, ws)) return RRS_EINVAL;
   if (M == 0) return RRS_OK;
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint8_t* xq = base + l.xq;

@@ -138,22 +138,45 @@ __device__ __forceinline__ uint32_t pack8(const uint32_t* mag, const uint32_t* s
 // register r needs after the reorder: position p = E*l + r of the block, row
 // p / K, reordered column p % K, source channel perm[p % K].
 template <int LOG2K, bool ROTATE>
-__device__ __forceinline__ void build_table(uint32_t* s_tab, const int32_t* perm, int tid, int nthreads) {
+__device__ __forceinline__ void build_table(uint32_t* s_tab, const int32_t* perm, int tid) {
   using C = Cfg<LOG2K>;
   constexpr int K = 1 << LOG2K;
-  for (int idx = tid; idx < C::kB; idx += nthreads) {
-    const int c4 = idx >> 8, l = (idx >> 2) & 63, rr = idx & 3;
-    const int p = C::kE * l + (c4 << 2) + rr;
-    const int f = ((p >> LOG2K) << LOG2K) | perm[p & (K - 1)];
-    int sl, sr;
-    if (ROTATE) {
-      sl = (f & 7) | (((f >> 9) & 7) << 3);
-      sr = ((f >> 3) & 63) | ((f >> 12) << 6);
-    } else {
-      sl = (f >> 3) & 63;
-      sr = (f & 7) | ((f >> 9) << 3);
+  // entries 4j .. 4j+3 share lane and chunk and take four consecutive
+  // positions, so their channels are one 16-byte load of perm; every
+  // thread issues all of its loads before it uses any
+  constexpr int kQuads = C::kB / 4;
+  constexpr int kIt = (kQuads + C::kThreads - 1) / C::kThreads;
+  int4 pv[kIt];
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int j = tid + it * C::kThreads;
+    if (j < kQuads) {
+      const int idx = 4 * j;
+      const int p = C::kE * ((idx >> 2) & 63) + ((idx >> 8) << 2);
+      pv[it] = *reinterpret_cast<const int4*>(perm + (p & (K - 1)));
     }
-    s_tab[idx] = static_cast<uint32_t>(gpos(sl, sr));
+  }
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int j = tid + it * C::kThreads;
+    if (j < kQuads) {
+      const int idx = 4 * j;
+      const int p = C::kE * ((idx >> 2) & 63) + ((idx >> 8) << 2);
+      const int ch[4] = {pv[it].x, pv[it].y, pv[it].z, pv[it].w};
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int f = ((p >> LOG2K) << LOG2K) | ch[rr];
+        int sl, sr;
+        if (ROTATE) {
+          sl = (f & 7) | (((f >> 9) & 7) << 3);
+          sr = ((f >> 3) & 63) | ((f >> 12) << 6);
+        } else {
+          sl = (f >> 3) & 63;
+          sr = (f & 7) | ((f >> 9) << 3);
+        }
+        s_tab[idx + rr] = static_cast<uint32_t>(gpos(sl, sr));
+      }
+    }
   }
 }
 
@@ -353,7 +376,7 @@ frontend_kernel(FeArgs a) {
   if constexpr (MODE == kColmax) {
     for (int k = tid; k < K; k += C::kThreads) s_tab[k] = 0u;
   } else {
-    build_table<LOG2K, ROTATE>(s_tab, a.perm, tid, C::kThreads);
+    build_table<LOG2K, ROTATE>(s_tab, a.perm, tid);
     if constexpr (MODE == kStats) {
       for (int g = tid; g < ngroups; g += C::kThreads) s_grp[g] = 0.f;
     } else if constexpr (MODE == kQuant) {
@@ -494,7 +517,7 @@ fused_kernel(FeArgs a) {
   const uint32_t epoch =
       __hip_atomic_load(&a.sync[kSyncEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
 
-  build_table<LOG2K, ROTATE>(s_tab, a.perm, tid, C::kThreads);
+  build_table<LOG2K, ROTATE>(s_tab, a.perm, tid);
   for (int g = tid; g < ngroups; g += C::kThreads) s_grp[g] = 0.f;
   __syncthreads();
 

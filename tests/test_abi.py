@@ -138,6 +138,22 @@ def test_weights_calibrate_init_reject():
     assert L.rrs_workspace_init(DUMMY, 100, NULL) == rra.RRS_EINVAL
 
 
+def test_misaligned_pointers_rejected():
+    """Every device pointer must be 16-byte aligned (the kernels move data in
+    16-byte accesses); the host check rejects any other address."""
+    L = rra.lib()
+    odd = ctypes.c_void_p(0x1004)
+    for key in ("X", "perm", "wq", "Y", "ws"):
+        assert _lin(**{key: odd}) == rra.RRS_EINVAL, key
+    assert L.rrs_gemm(odd, DUMMY, DUMMY, 4, 256, 8, 128, DUMMY, DUMMY, NULL) == rra.RRS_EINVAL
+    assert L.rrs_gemm(DUMMY, DUMMY, DUMMY, 4, 256, 8, 128, DUMMY, odd, NULL) == rra.RRS_EINVAL
+    assert L.rrs_gemm_partials(DUMMY, 4, 256, 8, 128, odd, 0, 4, 0, 8, DUMMY, NULL) == rra.RRS_EINVAL
+    assert L.rrs_frontend(DUMMY, 4, 256, 64, odd, DUMMY, DUMMY, DUMMY, DUMMY, 1 << 20, 0, NULL) == rra.RRS_EINVAL
+    assert L.rrs_prepare_weights(odd, 256, 8, DUMMY, DUMMY, NULL) == rra.RRS_EINVAL
+    assert L.rrs_calibrate_perm(DUMMY, 8, 256, odd, DUMMY, 1024, NULL) == rra.RRS_EINVAL
+    assert L.rrs_workspace_init(odd, 1024, NULL) == rra.RRS_EINVAL
+
+
 def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(rra, "_lib", None)
     monkeypatch.setattr(rra, "LIB_PATH", "/nonexistent/librrs.so")
