@@ -161,14 +161,25 @@ int rrs_frontend(const void* X_fp16, int M, int K, int G, const int32_t* perm,
  * RRS_EHIP if the device cannot be queried. */
 int rrs_frontend_passes(int M, int K, int flags);
 
-/* Grouped integer GEMM alone (same kernel as rrs_linear): Y = (1/K) dx dw
+/* Grouped integer GEMM alone (same kernels as rrs_linear): Y = (1/K) dx dw
  * sum_g S_g P_g with P_g the int32 group partials of the 4-bit codes. */
 int rrs_gemm(const uint8_t* xq, const float* dx, const float* S, int M, int K,
              int N, int G, const void* wq, float* Y, hipStream_t s);
 
+/* Which GEMM kernel rrs_gemm and rrs_linear run for M tokens of length K
+ * with group size G: RRS_GEMM_TILED (256 x 128 output tiles, every shape)
+ * or RRS_GEMM_FEW_TOKENS (one workgroup per 32 output channels streaming
+ * the weights once; M <= 64, G >= 64, K >= 2048). Both apply the same
+ * arithmetic (group partials exact, rescaled in fp32). A host-side query;
+ * RRS_EINVAL for bad arguments. */
+#define RRS_GEMM_TILED 1
+#define RRS_GEMM_FEW_TOKENS 2
+int rrs_gemm_form(int M, int K, int G);
+
 /* The int32 group partials P[t-m0][n-n0][g] = sum_{j in group g} q[t,j]
- * qw[n,j] for m0 <= t < m1, n0 <= n < n1, computed by the same main loop as
- * rrs_gemm (for exactness checks). P is int32 [m1-m0][n1-n0][K/G]. */
+ * qw[n,j] for m0 <= t < m1, n0 <= n < n1, computed by the main loop of the
+ * tiled kernel (for exactness checks; at every M). P is int32
+ * [m1-m0][n1-n0][K/G]. */
 int rrs_gemm_partials(const uint8_t* xq, int M, int K, int N, int G,
                       const void* wq, int m0, int m1, int n0, int n1,
                       int32_t* P, hipStream_t s);

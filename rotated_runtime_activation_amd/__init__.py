@@ -26,7 +26,7 @@ EXPORTS = (
     "rrs_status_string", "rrs_version", "rrs_weight_bytes", "rrs_workspace_bytes",
     "rrs_sync_bytes", "rrs_workspace_init", "rrs_calibrate_workspace_bytes",
     "rrs_calibrate_perm", "rrs_prepare_weights", "rrs_linear", "rrs_frontend", "rrs_gemm",
-    "rrs_gemm_partials", "rrs_frontend_passes",
+    "rrs_gemm_partials", "rrs_frontend_passes", "rrs_gemm_form",
 )
 
 
@@ -60,6 +60,7 @@ def _declare(lib):
         "rrs_gemm": (i, [vp, vp, vp, i, i, i, i, vp, vp, vp]),
         "rrs_gemm_partials": (i, [vp, i, i, i, i, vp, i, i, i, i, vp, vp]),
         "rrs_frontend_passes": (i, [i, i, i]),
+        "rrs_gemm_form": (i, [i, i, i]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -106,6 +107,19 @@ def rrs_frontend_passes(M: int, K: int, flags: int = 0) -> int:
     n = int(lib().rrs_frontend_passes(M, K, flags))
     if n < 0:
         _check("rrs_frontend_passes", n)
+    return n
+
+
+RRS_GEMM_TILED = 1
+RRS_GEMM_FEW_TOKENS = 2
+
+
+def rrs_gemm_form(M: int, K: int, G: int) -> int:
+    """GEMM kernel rrs_gemm / rrs_linear run for (M, K, G): RRS_GEMM_TILED or
+    RRS_GEMM_FEW_TOKENS."""
+    n = int(lib().rrs_gemm_form(M, K, G))
+    if n < 0:
+        _check("rrs_gemm_form", n)
     return n
 
 

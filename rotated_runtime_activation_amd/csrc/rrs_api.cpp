@@ -141,6 +141,11 @@ RRS_API int rrs_gemm(const uint8_t* xq, const float* dx, const float* S, int M, 
   return hip_status(rrs::launch_gemm(xq, dx, S, M, ilog2(K), N, G, codes, dw, Y, nullptr, 0, 0, 0, 0, s));
 }
 
+RRS_API int rrs_gemm_form(int M, int K, int G) {
+  if (M < 1 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;
+  return rrs::gemm_small_applies(M, ilog2(K), G) ? RRS_GEMM_FEW_TOKENS : RRS_GEMM_TILED;
+}
+
 RRS_API int rrs_gemm_partials(const uint8_t* xq, int M, int K, int N, int G, const void* wq, int m0,
                               int m1, int n0, int n1, int32_t* P, hipStream_t s) {
   if (M < 1 || N < 1 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;

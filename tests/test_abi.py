@@ -117,6 +117,20 @@ def test_frontend_passes_rejects():
     assert L.rrs_frontend_passes(16, 4096, rra.RRS_FLAG_TWO_PASS) == 2
 
 
+def test_gemm_form():
+    """Few-token kernel for M <= 64, G >= 64, K >= 2048; tiled otherwise."""
+    assert rra.rrs_gemm_form(64, 8192, 128) == rra.RRS_GEMM_FEW_TOKENS
+    assert rra.rrs_gemm_form(1, 2048, 64) == rra.RRS_GEMM_FEW_TOKENS
+    assert rra.rrs_gemm_form(1, 8192, 8192) == rra.RRS_GEMM_FEW_TOKENS
+    assert rra.rrs_gemm_form(65, 8192, 128) == rra.RRS_GEMM_TILED
+    assert rra.rrs_gemm_form(64, 1024, 128) == rra.RRS_GEMM_TILED
+    assert rra.rrs_gemm_form(64, 4096, 32) == rra.RRS_GEMM_TILED
+    L = rra.lib()
+    assert L.rrs_gemm_form(0, 4096, 128) == rra.RRS_EINVAL
+    assert L.rrs_gemm_form(4, 4096, 8192) == rra.RRS_EINVAL
+    assert L.rrs_gemm_form(4, 100, 32) == rra.RRS_EINVAL
+
+
 def test_gemm_and_partials_reject():
     L = rra.lib()
     assert L.rrs_gemm(DUMMY, DUMMY, DUMMY, 4, 256, 0, 128, DUMMY, DUMMY, NULL) == rra.RRS_EINVAL
