@@ -104,6 +104,108 @@ __device__ __forceinline__ void butterfly(float (&v)[E], int h) {
   }
 }
 
+// ---- matrix-core form of the rotation for K = 4096 -----------------------
+// H_4096 factors over any split of the 12 index bits of f into two sets,
+// H_4096 = H_64(f bits 0-2, 8-10) (x) H_64(f bits 3-7, 11). The load
+// layout (element f = 8L + 512i + e in half e of chunk i of lane L) already
+// is the A operand of v_mfma_f32_32x32x16_f16 with row = f bits 3-7 (lane %
+// 32), k = f bits 0-2 (half e), 8 (lane / 32) and 9-10 (k-step = i % 4), and
+// a second tile for f bit 11 (i / 4): so the first factor is 16 fp16 MFMAs
+// against a +-1 matrix (exact products of the fp16 inputs, fp32 sums), with
+// no widening. The accumulators hold column n = f bits (0-2, 8-10) in lane
+// % 32 and the tile index, row bits f3, f4, f6, f7 in the register and f5
+// in lane / 32 (32 x 32 accumulator layout); the second factor is five
+// in-register butterfly levels and one level across the lane halves with
+// v_permlane32_swap, which trades register bit 0 (f3) and lane bit 5 (f5).
+// Element f then sits in lane m12_lane(f), register m12_reg(f).
+__device__ __forceinline__ constexpr int m12_lane(int f) {
+  return (f & 7) | (((f >> 8) & 1) << 3) | (((f >> 9) & 1) << 4) | (((f >> 3) & 1) << 5);
+}
+__device__ __forceinline__ constexpr int m12_reg(int f) {
+  return ((f >> 5) & 1) | (((f >> 4) & 1) << 1) | (((f >> 6) & 1) << 2) | (((f >> 7) & 1) << 3) |
+         (((f >> 10) & 1) << 4) | (((f >> 11) & 1) << 5);
+}
+__device__ __forceinline__ constexpr int m12_elem(int lane, int r) {
+  return (lane & 7) | (((lane >> 5) & 1) << 3) | (((r >> 1) & 1) << 4) | ((r & 1) << 5) |
+         (((r >> 2) & 1) << 6) | (((r >> 3) & 1) << 7) | (((lane >> 3) & 1) << 8) |
+         (((lane >> 4) & 1) << 9) | (((r >> 4) & 1) << 10) | (((r >> 5) & 1) << 11);
+}
+constexpr bool m12_bijective() {
+  for (int f = 0; f < 4096; ++f) {
+    const int l = m12_lane(f), r = m12_reg(f);
+    if (l < 0 || l > 63 || r < 0 || r > 63 || m12_elem(l, r) != f) return false;
+  }
+  return true;
+}
+static_assert(m12_bijective(), "lane/register layout of the matrix-core rotation is a bijection");
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void rotate_block_mfma12(float (&v)[64], const uint4 (&w)[8], int lane) {
+  // B operand of k-step ks, column tile tj: lane l, half e holds H_64[k][n]
+  // with k = e + 8 (l / 32) + 16 ks and n = l % 32 + 32 tj, read as 6-bit
+  // labels of f bits (0, 1, 2, 8, 9, 10); sign = parity of popcount(k & n)
+  // = parity(e & l % 8) xor (l / 32 & l bit 3) xor parity(ks & (l bit 4 |
+  // tj << 1)).
+  const uint32_t a = lane & 7;
+  v4u base;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t s0 = __builtin_popcount((2 * d) & a) & 1u;
+    const uint32_t s1 = __builtin_popcount((2 * d + 1) & a) & 1u;
+    base[d] = 0x3c003c00u | (s0 << 15) | (s1 << 31);
+  }
+  const uint32_t hn3 = ((lane >> 5) & (lane >> 3)) & 1u;
+  const uint32_t n4 = (lane >> 4) & 1u;
+  v16f acc[2][2];
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+    for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[ti][tj][e] = 0.f;
+#pragma unroll
+  for (int tj = 0; tj < 2; ++tj) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint32_t c = hn3 ^ (__builtin_popcount(static_cast<uint32_t>(ks) & (n4 | (tj << 1))) & 1u);
+      const uint32_t m = (0u - c) & 0x80008000u;
+      const v4u b = base ^ m;
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) {
+        const v4u x = {w[4 * ti + ks].x, w[4 * ti + ks].y, w[4 * ti + ks].z, w[4 * ti + ks].w};
+        acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, x), __builtin_bit_cast(v8h, b),
+                                                             acc[ti][tj], 0, 0, 0);
+      }
+    }
+  }
+  // v[32 ti + 16 tj + r] = accumulator register r of tile (ti, tj):
+  // register bits f3, f4, f6, f7, then f10 (tj), f11 (ti)
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+    for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[32 * ti + 16 * tj + r] = acc[ti][tj][r];
+  butterfly<64>(v, 1);   // f3
+  butterfly<64>(v, 2);   // f4
+  butterfly<64>(v, 4);   // f6
+  butterfly<64>(v, 8);   // f7
+  butterfly<64>(v, 32);  // f11
+  // f5 across the lane halves: after the swap, v[R] holds (lanes 0-31)
+  // register R and (lanes 32-63) register R + 1 of the lower half, v[R + 1]
+  // the same of the upper half; one butterfly finishes the level
+#pragma unroll
+  for (int R = 0; R < 64; R += 2) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[R]), __float_as_uint(v[R + 1]), false, false);
+    const float x = __uint_as_float(sw[0]), y = __uint_as_float(sw[1]);
+    v[R] = x + y;
+    v[R + 1] = x - y;
+  }
+}
+
 // Byte 0 (resp. byte 3) of four words, gathered into one word.
 __device__ __forceinline__ uint32_t gather_b0(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
   const uint32_t t01 = __builtin_amdgcn_perm(x1, x0, 0x0c0c0400u);
@@ -167,7 +269,10 @@ __device__ __forceinline__ void build_table(uint32_t* s_tab, const int32_t* perm
       for (int rr = 0; rr < 4; ++rr) {
         const int f = ((p >> LOG2K) << LOG2K) | ch[rr];
         int sl, sr;
-        if (ROTATE) {
+        if (ROTATE && LOG2K == 12) {
+          sl = m12_lane(f);
+          sr = m12_reg(f);
+        } else if (ROTATE) {
           sl = (f & 7) | (((f >> 9) & 7) << 3);
           sr = ((f >> 3) & 63) | ((f >> 12) << 6);
         } else {
@@ -414,15 +519,20 @@ frontend_kernel(FeArgs a) {
       }
     }
     float v[E];
-    widen_block<LOG2K>(v, w);
     float* wb = s_buf[wave];
-    if constexpr (ROTATE) rotate_block<LOG2K>(v, wb, lane);
+    if constexpr (ROTATE && LOG2K == 12) {
+      rotate_block_mfma12(v, w, lane);
+    } else {
+      widen_block<LOG2K>(v, w);
+      if constexpr (ROTATE) rotate_block<LOG2K>(v, wb, lane);
+    }
 
     if constexpr (MODE == kColmax) {
       // channel |max| over the block's rows (LDS), folded into global below
 #pragma unroll
       for (int r = 0; r < E; ++r) {
-        const int f = (lane & 7) | ((r & 63) << 3) | ((lane >> 3) << 9) | ((r >> 6) << 12);
+        const int f = LOG2K == 12 ? m12_elem(lane, r)
+                                  : (lane & 7) | ((r & 63) << 3) | ((lane >> 3) << 9) | ((r >> 6) << 12);
         if (row0 + (f >> LOG2K) < a.rows)
           atomicMax(&s_tab[f & (K - 1)], __float_as_uint(fabsf(v[r])));
       }
@@ -527,8 +637,12 @@ fused_kernel(FeArgs a) {
   float* wb = s_buf[wave];
 #pragma unroll
   for (int q = 0; q < R; ++q) {
-    widen_block<LOG2K>(v[q], w[q]);
-    if constexpr (ROTATE) rotate_block<LOG2K>(v[q], wb, lane);
+    if constexpr (ROTATE && LOG2K == 12) {
+      rotate_block_mfma12(v[q], w[q], lane);
+    } else {
+      widen_block<LOG2K>(v[q], w[q]);
+      if constexpr (ROTATE) rotate_block<LOG2K>(v[q], wb, lane);
+    }
     reorder_block<LOG2K>(v[q], wb, s_tab, lane);
     group_max<LOG2K>(v[q], m[q], 1 << a.log2G);
     fold_group_max<LOG2K>(m[q], s_grp, a.log2G, a.rows, row0[q], lane);
