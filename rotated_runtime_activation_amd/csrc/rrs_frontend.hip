@@ -239,35 +239,48 @@ __device__ __forceinline__ uint32_t pack8(const uint32_t* mag, const uint32_t* s
 // s_tab[gpos(l, r)] = gather-buffer address of the element that lane l,
 // register r needs after the reorder: position p = E*l + r of the block, row
 // p / K, reordered column p % K, source channel perm[p % K].
-template <int LOG2K, bool ROTATE>
-__device__ __forceinline__ void build_table(uint32_t* s_tab, const int32_t* perm, int tid) {
-  using C = Cfg<LOG2K>;
+// The table is built in two parts so that a kernel can issue the perm
+// loads first, then its activation loads, and fill the table while the
+// activations are in flight. Entries 4j .. 4j+3 share lane and chunk and
+// take four consecutive positions, so their channels are one 16-byte load.
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+template <int LOG2K>
+struct TableLoads {
+  static constexpr int kQuads = Cfg<LOG2K>::kB / 4;
+  static constexpr int kIt = (kQuads + Cfg<LOG2K>::kThreads - 1) / Cfg<LOG2K>::kThreads;
+  v4i pv[kIt];
+};
+
+template <int LOG2K>
+__device__ __forceinline__ constexpr int table_pos(int idx) {  // position p of entry idx (rr = 0)
+  return Cfg<LOG2K>::kE * ((idx >> 2) & 63) + ((idx >> 8) << 2);
+}
+
+template <int LOG2K>
+__device__ __forceinline__ void table_loads(TableLoads<LOG2K>& t, const int32_t* perm, int tid) {
+  using T = TableLoads<LOG2K>;
   constexpr int K = 1 << LOG2K;
-  // entries 4j .. 4j+3 share lane and chunk and take four consecutive
-  // positions, so their channels are one 16-byte load of perm; every
-  // thread issues all of its loads before it uses any
-  constexpr int kQuads = C::kB / 4;
-  constexpr int kIt = (kQuads + C::kThreads - 1) / C::kThreads;
-  int4 pv[kIt];
 #pragma unroll
-  for (int it = 0; it < kIt; ++it) {
-    const int j = tid + it * C::kThreads;
-    if (j < kQuads) {
-      const int idx = 4 * j;
-      const int p = C::kE * ((idx >> 2) & 63) + ((idx >> 8) << 2);
-      pv[it] = *reinterpret_cast<const int4*>(perm + (p & (K - 1)));
-    }
+  for (int it = 0; it < T::kIt; ++it) {
+    const int j = tid + it * Cfg<LOG2K>::kThreads;
+    if (j < T::kQuads) t.pv[it] = *reinterpret_cast<const v4i*>(perm + (table_pos<LOG2K>(4 * j) & (K - 1)));
   }
+}
+
+template <int LOG2K, bool ROTATE>
+__device__ __forceinline__ void table_fill(uint32_t* s_tab, const TableLoads<LOG2K>& t, int tid) {
+  using T = TableLoads<LOG2K>;
+  constexpr int K = 1 << LOG2K;
 #pragma unroll
-  for (int it = 0; it < kIt; ++it) {
-    const int j = tid + it * C::kThreads;
-    if (j < kQuads) {
+  for (int it = 0; it < T::kIt; ++it) {
+    const int j = tid + it * Cfg<LOG2K>::kThreads;
+    if (j < T::kQuads) {
       const int idx = 4 * j;
-      const int p = C::kE * ((idx >> 2) & 63) + ((idx >> 8) << 2);
-      const int ch[4] = {pv[it].x, pv[it].y, pv[it].z, pv[it].w};
+      const int p = table_pos<LOG2K>(idx);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int f = ((p >> LOG2K) << LOG2K) | ch[rr];
+        const int f = ((p >> LOG2K) << LOG2K) | t.pv[it][rr];
         int sl, sr;
         if (ROTATE && LOG2K == 12) {
           sl = m12_lane(f);
@@ -287,7 +300,8 @@ __device__ __forceinline__ void build_table(uint32_t* s_tab, const int32_t* perm
 
 // fp16 words of a block of activation rows X [rows][K]: element
 // f = 8L + 512i + e of the block lands in word w[i], half e. Rows past the
-// last read as zero.
+// last read the last row instead (every load is unconditional, so wait
+// counts stay exact); no result of such a row is ever stored or reduced.
 template <int LOG2K>
 __device__ __forceinline__ void load_block(uint4 (&w)[Cfg<LOG2K>::kChunks], const uint16_t* src, int rows,
                                            int row0, int lane) {
@@ -295,10 +309,8 @@ __device__ __forceinline__ void load_block(uint4 (&w)[Cfg<LOG2K>::kChunks], cons
 #pragma unroll
   for (int i = 0; i < Cfg<LOG2K>::kChunks; ++i) {
     const int f0 = 8 * lane + 512 * i;
-    if (row0 + (f0 >> LOG2K) < rows)
-      w[i] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(row0) * K + f0);
-    else
-      w[i] = make_uint4(0u, 0u, 0u, 0u);
+    const int row = min(row0 + (f0 >> LOG2K), rows - 1);
+    w[i] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(row) * K + (f0 & (K - 1)));
   }
 }
 
@@ -473,15 +485,18 @@ frontend_kernel(FeArgs a) {
   const int blk = blockIdx.x * WAVES + wave;
   const int row0 = blk * C::kRows;
 
-  // activation rows: start the loads before the set-up
+  // table loads, then the activation rows, both before the set-up
+  TableLoads<LOG2K> tl;
+  if constexpr (MODE != kColmax) table_loads<LOG2K>(tl, a.perm, tid);
   uint4 w[C::kChunks];
   if constexpr (MODE != kWeight) load_block<LOG2K>(w, a.src, a.rows, row0, lane);
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- per-workgroup set-up -------------------------------------------
   if constexpr (MODE == kColmax) {
     for (int k = tid; k < K; k += C::kThreads) s_tab[k] = 0u;
   } else {
-    build_table<LOG2K, ROTATE>(s_tab, a.perm, tid);
+    table_fill<LOG2K, ROTATE>(s_tab, tl, tid);
     if constexpr (MODE == kStats) {
       for (int g = tid; g < ngroups; g += C::kThreads) s_grp[g] = 0.f;
     } else if constexpr (MODE == kQuant) {
@@ -619,15 +634,20 @@ fused_kernel(FeArgs a) {
 #pragma unroll
   for (int q = 0; q < R; ++q) row0[q] = ((blockIdx.x * R + q) * WAVES + wave) * C::kRows;
 
+  TableLoads<LOG2K> tl;
+  table_loads<LOG2K>(tl, a.perm, tid);
   uint4 w[R][C::kChunks];
 #pragma unroll
   for (int q = 0; q < R; ++q) load_block<LOG2K>(w[q], a.src, a.rows, row0[q], lane);
+  // every load is issued before the table is filled: waiting for the perm
+  // loads then leaves the activation loads in flight
+  __builtin_amdgcn_sched_barrier(0);
   // every workgroup reads the epoch before raising its flag, so none can
   // see the next call's value
   const uint32_t epoch =
       __hip_atomic_load(&a.sync[kSyncEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
 
-  build_table<LOG2K, ROTATE>(s_tab, a.perm, tid);
+  table_fill<LOG2K, ROTATE>(s_tab, tl, tid);
   for (int g = tid; g < ngroups; g += C::kThreads) s_grp[g] = 0.f;
   __syncthreads();
 
