@@ -195,6 +195,7 @@ struct GemmCtx {
   typename Mm::acc_t acc[TI][TJ];
   const float* rat;
   uint32_t* sbar;   // this set's arrival counter (LDS)
+  uint32_t* sbar_o;  // the other set's arrival counter (LDS)
   uint32_t nbar = 0;
 
   __device__ GemmCtx(const GemmArgs& args, const float* s_rat) : a(args), rat(s_rat) {}
@@ -315,6 +316,17 @@ struct GemmCtx {
       if (__builtin_amdgcn_readfirstlane(n) >= nbar) break;
       __builtin_amdgcn_s_sleep(0);
     }
+    // Balance the sets: wave w of each set shares a SIMD, and with equal
+    // priorities the older wave (set 0) wins every issue conflict, so set 1
+    // would finish its half of K several microseconds late. A wave whose set
+    // is a stage or more behind the other set raises its priority.
+    const uint32_t addr_o = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u32*)sbar_o));
+    uint32_t no;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(no) : "v"(addr_o) : "memory");
+    if (__builtin_amdgcn_readfirstlane(no) > nbar)
+      __builtin_amdgcn_s_setprio(2);
+    else
+      __builtin_amdgcn_s_setprio(0);
   }
 
   // One stage: stage st is read from slot `cur`, stage st + 2 is fetched
@@ -459,6 +471,7 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
 
   if (tid < kSets) s_bar[tid] = 0u;
   c.sbar = &s_bar[set];
+  c.sbar_o = &s_bar[1 - set];
   __syncthreads();  // tables and counters published
   if (set == 0) {
     c.template run<0>(nsteps);
