@@ -13,11 +13,14 @@
 // contiguous elements, i.e. one row, or 4096/K whole rows when K < 4096):
 //   * load: lane L takes 16-byte chunks, element f = 8L + 512i + e of the
 //     block sits in register 8i + e (coalesced 1 KiB per load instruction);
-//   * rotation phase 1: butterflies over the in-register index bits
-//     (f bits 0-2 and 9..);
-//   * transpose through LDS so f bits 3-8 become register bits (lane
-//     l = (f & 7) | ((f >> 9) & 7) << 3, register (f >> 3) & 63 | (f >> 12) << 6);
-//   * rotation phase 2: butterflies over f bits 3-8;
+//   * rotation, K = 4096 and 8192: the load layout is the A operand of the
+//     fp16 32 x 32 x 16 MFMA, so one 64-point factor of the Sylvester
+//     transform runs on the matrix cores against a +-1 fragment and the
+//     other in registers (plus one lane-half level); see rotate_block_mfma;
+//   * rotation, K <= 2048: phase 1 butterflies over the in-register index
+//     bits (f bits 0-2 and 9..), a transpose through LDS so f bits 3-8
+//     become register bits (lane l = (f & 7) | ((f >> 9) & 7) << 3,
+//     register (f >> 3) & 63 | (f >> 12) << 6), phase 2 over f bits 3-8;
 //   * reorder: registers go back to LDS (conflict-free b128) and every lane
 //     gathers its E = B/64 consecutive reordered positions through a
 //     per-workgroup address table built from perm.
@@ -143,12 +146,16 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void rotate_block_mfma12(float (&v)[64], const uint4 (&w)[8], int lane) {
-  // B operand of k-step ks, column tile tj: lane l, half e holds H_64[k][n]
-  // with k = e + 8 (l / 32) + 16 ks and n = l % 32 + 32 tj, read as 6-bit
-  // labels of f bits (0, 1, 2, 8, 9, 10); sign = parity of popcount(k & n)
-  // = parity(e & l % 8) xor (l / 32 & l bit 3) xor parity(ks & (l bit 4 |
-  // tj << 1)).
+// B operand of k-step ks, column tile tj: lane l, half e holds H_64[k][n]
+// with k = e + 8 (l / 32) + 16 ks and n = l % 32 + 32 tj, read as 6-bit
+// labels of f bits (0, 1, 2, 8, 9, 10); sign = parity of popcount(k & n)
+// = parity(e & l % 8) xor (l / 32 & l bit 3) xor parity(ks & (l bit 4 |
+// tj << 1)).
+struct HFrags {
+  v4u b[2][4];  // [tj][ks]
+};
+
+__device__ __forceinline__ HFrags h64_frags(int lane) {
   const uint32_t a = lane & 7;
   v4u base;
 #pragma unroll
@@ -159,6 +166,21 @@ __device__ __forceinline__ void rotate_block_mfma12(float (&v)[64], const uint4 
   }
   const uint32_t hn3 = ((lane >> 5) & (lane >> 3)) & 1u;
   const uint32_t n4 = (lane >> 4) & 1u;
+  HFrags h;
+#pragma unroll
+  for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint32_t c = hn3 ^ (__builtin_popcount(static_cast<uint32_t>(ks) & (n4 | (tj << 1))) & 1u);
+      h.b[tj][ks] = base ^ ((0u - c) & 0x80008000u);
+    }
+  return h;
+}
+
+// Rotate the 4096 elements in chunks w[C0 .. C0+7] into v[V0 .. V0+63]
+// (layout m12_lane / m12_reg).
+template <int C0, int V0, int NC, int NV>
+__device__ __forceinline__ void rotate4096_mfma(float (&v)[NV], const uint4 (&w)[NC], const HFrags& h) {
   v16f acc[2][2];
 #pragma unroll
   for (int ti = 0; ti < 2; ++ti)
@@ -170,41 +192,69 @@ __device__ __forceinline__ void rotate_block_mfma12(float (&v)[64], const uint4 
   for (int tj = 0; tj < 2; ++tj) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const uint32_t c = hn3 ^ (__builtin_popcount(static_cast<uint32_t>(ks) & (n4 | (tj << 1))) & 1u);
-      const uint32_t m = (0u - c) & 0x80008000u;
-      const v4u b = base ^ m;
 #pragma unroll
       for (int ti = 0; ti < 2; ++ti) {
-        const v4u x = {w[4 * ti + ks].x, w[4 * ti + ks].y, w[4 * ti + ks].z, w[4 * ti + ks].w};
-        acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, x), __builtin_bit_cast(v8h, b),
-                                                             acc[ti][tj], 0, 0, 0);
+        const uint4 c = w[C0 + 4 * ti + ks];
+        const v4u x = {c.x, c.y, c.z, c.w};
+        acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, x),
+                                                             __builtin_bit_cast(v8h, h.b[tj][ks]), acc[ti][tj], 0, 0, 0);
       }
     }
   }
-  // v[32 ti + 16 tj + r] = accumulator register r of tile (ti, tj):
+  // v[V0 + 32 ti + 16 tj + r] = accumulator register r of tile (ti, tj):
   // register bits f3, f4, f6, f7, then f10 (tj), f11 (ti)
+  float u[64];
 #pragma unroll
   for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
     for (int tj = 0; tj < 2; ++tj)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v[32 * ti + 16 * tj + r] = acc[ti][tj][r];
-  butterfly<64>(v, 1);   // f3
-  butterfly<64>(v, 2);   // f4
-  butterfly<64>(v, 4);   // f6
-  butterfly<64>(v, 8);   // f7
-  butterfly<64>(v, 32);  // f11
-  // f5 across the lane halves: after the swap, v[R] holds (lanes 0-31)
-  // register R and (lanes 32-63) register R + 1 of the lower half, v[R + 1]
+      for (int r = 0; r < 16; ++r) u[32 * ti + 16 * tj + r] = acc[ti][tj][r];
+  butterfly<64>(u, 1);   // f3
+  butterfly<64>(u, 2);   // f4
+  butterfly<64>(u, 4);   // f6
+  butterfly<64>(u, 8);   // f7
+  butterfly<64>(u, 32);  // f11
+  // f5 across the lane halves: after the swap, u[R] holds (lanes 0-31)
+  // register R and (lanes 32-63) register R + 1 of the lower half, u[R + 1]
   // the same of the upper half; one butterfly finishes the level
 #pragma unroll
   for (int R = 0; R < 64; R += 2) {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[R]), __float_as_uint(v[R + 1]), false, false);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(u[R]), __float_as_uint(u[R + 1]), false, false);
     const float x = __uint_as_float(sw[0]), y = __uint_as_float(sw[1]);
-    v[R] = x + y;
-    v[R + 1] = x - y;
+    v[V0 + R] = x + y;
+    v[V0 + R + 1] = x - y;
   }
 }
+
+// Whole-block rotation on the matrix cores for K = 4096 and 8192 (two
+// 4096 halves, then one butterfly level over f bit 12 = register bit 6).
+template <int LOG2K>
+__device__ __forceinline__ void rotate_block_mfma(float (&v)[Cfg<LOG2K>::kE], const uint4 (&w)[Cfg<LOG2K>::kChunks],
+                                                  int lane) {
+  static_assert(LOG2K == 12 || LOG2K == 13, "matrix-core rotation: K = 4096 or 8192");
+  constexpr int E = Cfg<LOG2K>::kE, NC = Cfg<LOG2K>::kChunks;
+  const HFrags h = h64_frags(lane);
+  rotate4096_mfma<0, 0, NC, E>(v, w, h);
+  if constexpr (LOG2K == 13) {
+    rotate4096_mfma<8, 64, NC, E>(v, w, h);
+    butterfly<E>(v, 64);
+  }
+}
+
+// (lane, register) of element f after rotate_block_mfma, and back
+template <int LOG2K>
+__device__ __forceinline__ constexpr int mfma_lane(int f) { return m12_lane(f & 4095); }
+template <int LOG2K>
+__device__ __forceinline__ constexpr int mfma_reg(int f) { return m12_reg(f & 4095) | ((f >> 12) << 6); }
+template <int LOG2K>
+__device__ __forceinline__ constexpr int mfma_elem(int lane, int r) { return m12_elem(lane, r & 63) | ((r >> 6) << 12); }
+constexpr bool mfma13_bijective() {
+  for (int f = 0; f < 8192; ++f)
+    if (mfma_elem<13>(mfma_lane<13>(f), mfma_reg<13>(f)) != f || mfma_reg<13>(f) > 127) return false;
+  return true;
+}
+static_assert(mfma13_bijective(), "lane/register layout of the K = 8192 matrix-core rotation is a bijection");
 
 // Byte 0 (resp. byte 3) of four words, gathered into one word.
 __device__ __forceinline__ uint32_t gather_b0(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
@@ -282,9 +332,9 @@ __device__ __forceinline__ void table_fill(uint32_t* s_tab, const TableLoads<LOG
       for (int rr = 0; rr < 4; ++rr) {
         const int f = ((p >> LOG2K) << LOG2K) | t.pv[it][rr];
         int sl, sr;
-        if (ROTATE && LOG2K == 12) {
-          sl = m12_lane(f);
-          sr = m12_reg(f);
+        if (ROTATE && LOG2K >= 12) {
+          sl = mfma_lane<LOG2K>(f);
+          sr = mfma_reg<LOG2K>(f);
         } else if (ROTATE) {
           sl = (f & 7) | (((f >> 9) & 7) << 3);
           sr = ((f >> 3) & 63) | ((f >> 12) << 6);
@@ -535,8 +585,8 @@ frontend_kernel(FeArgs a) {
     }
     float v[E];
     float* wb = s_buf[wave];
-    if constexpr (ROTATE && LOG2K == 12) {
-      rotate_block_mfma12(v, w, lane);
+    if constexpr (ROTATE && LOG2K >= 12) {
+      rotate_block_mfma<LOG2K>(v, w, lane);
     } else {
       widen_block<LOG2K>(v, w);
       if constexpr (ROTATE) rotate_block<LOG2K>(v, wb, lane);
@@ -546,7 +596,7 @@ frontend_kernel(FeArgs a) {
       // channel |max| over the block's rows (LDS), folded into global below
 #pragma unroll
       for (int r = 0; r < E; ++r) {
-        const int f = LOG2K == 12 ? m12_elem(lane, r)
+        const int f = LOG2K >= 12 ? mfma_elem<LOG2K>(lane, r)
                                   : (lane & 7) | ((r & 63) << 3) | ((lane >> 3) << 9) | ((r >> 6) << 12);
         if (row0 + (f >> LOG2K) < a.rows)
           atomicMax(&s_tab[f & (K - 1)], __float_as_uint(fabsf(v[r])));
@@ -657,8 +707,8 @@ fused_kernel(FeArgs a) {
   float* wb = s_buf[wave];
 #pragma unroll
   for (int q = 0; q < R; ++q) {
-    if constexpr (ROTATE && LOG2K == 12) {
-      rotate_block_mfma12(v[q], w[q], lane);
+    if constexpr (ROTATE && LOG2K >= 12) {
+      rotate_block_mfma<LOG2K>(v[q], w[q], lane);
     } else {
       widen_block<LOG2K>(v[q], w[q]);
       if constexpr (ROTATE) rotate_block<LOG2K>(v[q], wb, lane);
