@@ -32,7 +32,11 @@ R5 rotate, then reorder, then smooth; R6 round half to even; R7 no clipping;
 R8 codes in [-7, 7]; R9 zero group -> scale 1, zero row -> codes 0 and scale 0;
 R10 4-bit sign-magnitude packing, 8 codes per 32-bit word (layout in
 ``pack_codes``); R11 weights RTN per output
-channel; R12 the group scale multiplies each group's integer partial.
+channel; R12 the group scale multiplies each group's integer partial;
+R16 the signed rotation variant is Z = X D H with D = diag(d), d in {+1, -1}^K
+given by the caller, and the weights take H D W ([AGC-OR] Sec. 4.1, the
+transform family P = Lambda^-1 D H^T with Lambda = I; Sec. 4.6 "Signed online
+rotation": sign flips before the online Hadamard rotation).
 
 Every function below is pinned by ``tests/test_oracle_*.py`` against something
 other than itself (explicit Hadamard matrices, scipy's Hadamard, closed forms,
@@ -76,18 +80,41 @@ def fwht(x: np.ndarray) -> np.ndarray:
     return y.reshape(lead + (n,))
 
 
+def rotate_rows(x: np.ndarray, d=None) -> np.ndarray:
+    """The online rotation of the activations: x H, or with a sign vector d
+    (+1 / -1 per input channel) the signed rotation x D H of [AGC-OR]
+    Sec. 4.1 / Sec. 4.6 (reading R16). Flipping signs of fp16 values is exact,
+    so this is as exact as ``fwht``."""
+    x = np.asarray(x, dtype=np.float64)
+    if d is None:
+        return fwht(x)
+    d = np.asarray(d, dtype=np.float64)
+    if d.shape != (x.shape[-1],) or not np.all(np.abs(d) == 1.0):
+        raise ValueError("d must be a +-1 vector over the channels")
+    return fwht(x * d)
+
+
+def signs_from_bits(bits: np.ndarray, K: int) -> np.ndarray:
+    """+-1 vector from the boundary's sign bitmask (K bits, little-endian
+    32-bit words; bit j set means d_j = -1)."""
+    b = np.asarray(bits, dtype=np.uint32)
+    j = np.arange(K)
+    neg = (b[j // 32] >> (j % 32).astype(np.uint32)) & 1
+    return np.where(neg == 1, -1.0, 1.0)
+
+
 # ------------------------------------------------------------------ reorder
-def calibrate_perm(x_cal: np.ndarray) -> np.ndarray:
+def calibrate_perm(x_cal: np.ndarray, d=None) -> np.ndarray:
     """Fixed channel order from a calibration batch (reading R5/R15).
 
-    Rotate the calibration activations, take each channel's |max| over the
-    calibration tokens, and order channels by that max, largest first, ties
-    by lower channel index. perm[j] is the source channel of position j, so
-    outlier channels gather into the leading groups and normal channels into
-    the rest ([RRS-rebuttal] "Novelty": reorder to collect outliers and normal
-    values).
+    Rotate the calibration activations (with the layer's sign vector, if
+    any), take each channel's |max| over the calibration tokens, and order
+    channels by that max, largest first, ties by lower channel index. perm[j]
+    is the source channel of position j, so outlier channels gather into the
+    leading groups and normal channels into the rest ([RRS-rebuttal]
+    "Novelty": reorder to collect outliers and normal values).
     """
-    c = np.max(np.abs(fwht(x_cal)), axis=0)
+    c = np.max(np.abs(rotate_rows(x_cal, d)), axis=0)
     return np.argsort(-c, kind="stable").astype(np.int32)
 
 
@@ -103,12 +130,13 @@ def rtn_codes(v: np.ndarray) -> np.ndarray:
     return np.clip(np.rint(v), -QMAX, QMAX).astype(np.int8)
 
 
-def prepare_weights(W: np.ndarray, perm: np.ndarray) -> Dict[str, np.ndarray]:
+def prepare_weights(W: np.ndarray, perm: np.ndarray, d=None) -> Dict[str, np.ndarray]:
     """Offline weight side for Y = X W with W [K, N].
 
     Output-preserving transform ([AGC-OR] Sec. 3.1): rotating the activations
     by H is undone by H^T applied to the weights, and H is symmetric, so the
-    rotated weight is Wz = H W (each column transformed). The reorder applies
+    rotated weight is Wz = H W (each column transformed); with signs
+    (Z = X D H) it is Wz = H D W, since D D = I (reading R16). The reorder applies
     the same permutation to the weight rows ([RRS-rebuttal], reorder answer).
     Each output channel is quantised symmetric per channel with
     Delta_w = max|col| / 7 ([AGC-OR] Sec. 5; R11).
@@ -117,7 +145,7 @@ def prepare_weights(W: np.ndarray, perm: np.ndarray) -> Dict[str, np.ndarray]:
     channel (float64 [N]), dw = a / 7, and the pre-rounding values uw [N, K].
     """
     W = np.asarray(W)
-    Wz_t = fwht(W.T)                    # [N, K]: row n is (H W)[:, n]
+    Wz_t = rotate_rows(W.T, d)          # [N, K]: row n is (H D W)[:, n]
     Wp_t = Wz_t[:, perm]                # Wp[j, n] = Wz[perm[j], n]
     a = np.max(np.abs(Wp_t), axis=1)    # per output channel
     safe = np.where(a > 0, a, 1.0)
@@ -127,7 +155,7 @@ def prepare_weights(W: np.ndarray, perm: np.ndarray) -> Dict[str, np.ndarray]:
 
 
 def frontend(X: np.ndarray, perm: np.ndarray, G: int, *, rotate: bool = True,
-             smooth: bool = True) -> Dict[str, np.ndarray]:
+             smooth: bool = True, d=None) -> Dict[str, np.ndarray]:
     """Activation side: rotate, reorder, runtime group-wise smoothing,
     per-token symmetric INT4 ([RRS-summary] "Approach"; [RRS-rebuttal]
     "Novelty"; [AGC-OR] Sec. 3.1 and App. B.1).
@@ -143,13 +171,14 @@ def frontend(X: np.ndarray, perm: np.ndarray, G: int, *, rotate: bool = True,
 
     ``rotate=False`` gives Runtime Smooth without rotation and
     ``smooth=False`` gives rotation only (S = 1): the ablations of
-    [RRS-rebuttal] "Incomplete ablation study".
+    [RRS-rebuttal] "Incomplete ablation study". ``d`` (a +-1 vector) makes
+    the rotation the signed one, Z = X D H (reading R16).
     """
     X = np.asarray(X)
     M, K = X.shape
     if K % G:
         raise ValueError("G must divide K")
-    Z = fwht(X) if rotate else X.astype(np.float64)
+    Z = rotate_rows(X, d) if rotate else X.astype(np.float64)
     Zp = Z[:, perm]
     c = np.max(np.abs(Zp), axis=0) if M else np.zeros(K)
     if smooth:
@@ -224,11 +253,11 @@ def linear_out(q: np.ndarray, dx: np.ndarray, S: np.ndarray, qw: np.ndarray,
     return {"Y": scale * acc, "C": np.abs(scale) * mag}
 
 
-def rrs_linear(X: np.ndarray, W: np.ndarray, perm: np.ndarray, G: int) -> Dict[str, np.ndarray]:
+def rrs_linear(X: np.ndarray, W: np.ndarray, perm: np.ndarray, G: int, d=None) -> Dict[str, np.ndarray]:
     """The whole RRS A4W4 linear: weights prepared offline, then the runtime
-    front end and the grouped integer GEMM."""
-    wp = prepare_weights(W, perm)
-    fe = frontend(X, perm, G)
+    front end and the grouped integer GEMM (signed rotation when d is given)."""
+    wp = prepare_weights(W, perm, d)
+    fe = frontend(X, perm, G, d=d)
     out = linear_out(fe["q"], fe["dx"], fe["S"], wp["qw"], wp["dw"], G)
     return {"fe": fe, "wp": wp, **out}
 

@@ -14,6 +14,7 @@ import json
 import os
 
 import numpy as np
+import scipy.linalg
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -144,3 +145,27 @@ def frontend_invariants(frontend, seed=5, M=40, K=512, G=64) -> bool:
                 and np.abs(U).max() <= 1.0
                 and np.all(np.abs(q[np.arange(M), am]) == 7)
                 and np.all(np.abs(U - (r[:, None] / 7) * q) <= r[:, None] / 14 * (1 + 1e-12)))
+
+
+def signed_rotation_matches_explicit(rotate_rows, sizes=(2, 8, 64, 256), seed=3) -> bool:
+    """Signed rotation x D H against the explicit product with scipy's
+    Sylvester Hadamard and diag(d) ([AGC-OR] Sec. 4.1; reading R16). fp16
+    inputs make both sides exact in float64."""
+    g = np.random.default_rng(seed)
+    for n in sizes:
+        x = g.standard_normal((5, n)).astype(np.float16)
+        d = np.where(g.random(n) < 0.5, -1.0, 1.0)
+        ref = (x.astype(np.float64) * d) @ scipy.linalg.hadamard(n).astype(np.float64)
+        if not np.array_equal(rotate_rows(x, d), ref):
+            return False
+    return True
+
+
+def signed_rotation_inverts(rotate_rows, n=512, seed=4) -> bool:
+    """(x D H) H / n then D gives x back exactly (H H = n I, D D = I)."""
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((3, n)).astype(np.float16).astype(np.float64)
+    d = np.where(g.random(n) < 0.5, -1.0, 1.0)
+    z = rotate_rows(x, d)
+    back = (z @ scipy.linalg.hadamard(n).astype(np.float64)) / n * d
+    return bool(np.array_equal(back, x))

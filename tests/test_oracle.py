@@ -269,3 +269,47 @@ def test_pack_layout_feeds_fp8_subnormals():
     for j in range(4):
         assert np.array_equal(dec(lo, j), q[:, 2 * j])
         assert np.array_equal(dec(hi, j), q[:, 2 * j + 1])
+
+
+# ---- signed rotation (x D H; [AGC-OR] Sec. 4.1 / Sec. 4.6, reading R16)
+def test_signed_rotation_explicit_and_inverse():
+    assert pins.signed_rotation_matches_explicit(oracle.rotate_rows)
+    assert pins.signed_rotation_inverts(oracle.rotate_rows)
+
+
+def test_signed_rotation_all_plus_is_plain():
+    x, perm, G = _case()
+    K = x.shape[1]
+    assert np.array_equal(oracle.rotate_rows(x, np.ones(K)), oracle.fwht(x))
+    a = oracle.frontend(x, perm, G)
+    b = oracle.frontend(x, perm, G, d=np.ones(K))
+    assert np.array_equal(a["q"], b["q"]) and np.array_equal(a["S"], b["S"])
+
+
+def test_signed_unrounded_output_equals_xw():
+    import functools
+    d = np.where(np.random.default_rng(9).random(128) < 0.5, -1.0, 1.0)
+    fe = functools.partial(oracle.frontend, d=d)
+    pw = functools.partial(oracle.prepare_weights, d=d)
+    assert pins.unrounded_output_is_xw(fe, pw, oracle.linear_out)
+
+
+def test_signed_weights_are_h_d_w():
+    g = np.random.default_rng(11)
+    K, N = 64, 6
+    W = (g.standard_normal((K, N)) * 0.05).astype(np.float16)
+    d = np.where(g.random(K) < 0.5, -1.0, 1.0)
+    perm = g.permutation(K).astype(np.int32)
+    wp = oracle.prepare_weights(W, perm, d)
+    ref = scipy.linalg.hadamard(K).astype(np.float64) @ (d[:, None] * W.astype(np.float64))
+    assert np.array_equal(wp["Wp_t"], ref[perm, :].T)
+
+
+def test_signs_from_bits_brute_force():
+    g = np.random.default_rng(12)
+    K = 96
+    bits = g.integers(0, 2**32, size=K // 32, dtype=np.uint64).astype(np.uint32)
+    d = oracle.signs_from_bits(bits, K)
+    for j in range(K):
+        word = int(bits[j // 32])
+        assert d[j] == (-1.0 if (word >> (j % 32)) & 1 else 1.0)

@@ -115,3 +115,15 @@ def test_odd_sign_in_own_byte_fails():
         byte = np.abs(a) | (np.abs(b) << 4) | ((a < 0) << 7) | ((b < 0) << 3)
         return byte.reshape(q.shape[:-1] + (q.shape[-1] // 2,)).astype(np.uint8)
     assert not pins.pack_matches_golden(pack_no_roll)
+
+
+def test_signs_after_rotation_mutant_fails():
+    # slip: x H D instead of x D H
+    def rot_after(x, d=None):
+        z = oracle.fwht(x)
+        return z if d is None else z * np.asarray(d, dtype=np.float64)
+    assert not pins.signed_rotation_matches_explicit(rot_after)
+
+
+def test_signs_ignored_mutant_fails():
+    assert not pins.signed_rotation_matches_explicit(lambda x, d=None: oracle.fwht(x))
