@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="o_proj")
     ap.add_argument("--G", type=int, default=None)
+    ap.add_argument("--signed", action="store_true",
+                    help="time the signed rotation X D H (random sign mask) instead of X H")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-gemm-only", action="store_true",
                     help="run only the GEMM loop (for counter collection)")
@@ -127,7 +129,15 @@ def main():
     cws = torch.empty(rra.rrs_calibrate_workspace_bytes(K), dtype=torch.uint8, device=dev)
     rra.rrs_calibrate_perm(torch.from_numpy(xc).to(dev), perm, cws)
     wq0 = torch.empty(rra.rrs_weight_bytes(K, N), dtype=torch.uint8, device=dev)
-    rra.rrs_prepare_weights(W0, perm, wq0)
+    dsign = None
+    if args.signed:
+        import numpy as np
+        bits = np.random.default_rng(1234).integers(0, 2**32, size=K // 32, dtype=np.uint64).astype(np.uint32)
+        dsign = torch.from_numpy(bits.view(np.int32)).to(dev)
+        rra.rrs_calibrate_perm_signed(torch.from_numpy(xc).to(dev), dsign, perm, cws)
+        rra.rrs_prepare_weights_signed(W0, perm, dsign, wq0)
+    else:
+        rra.rrs_prepare_weights(W0, perm, wq0)
     del W0
 
     ws_bytes = rra.rrs_workspace_bytes(M, K, G)
@@ -145,12 +155,18 @@ def main():
 
     def step(i):
         s = sets[i % nsets]
-        rra.rrs_linear(s["X"], G, perm, s["wq"], s["Y"], s["ws"], stream)
+        if dsign is None:
+            rra.rrs_linear(s["X"], G, perm, s["wq"], s["Y"], s["ws"], stream)
+        else:
+            rra.rrs_linear_signed(s["X"], G, perm, dsign, s["wq"], s["Y"], s["ws"], stream)
 
     def fe_step(i):
         s = sets[i % nsets]
         xq, dx, S = s["views"]
-        rra.rrs_frontend(s["X"], G, perm, xq, dx, S, s["ws"], 0, stream)
+        if dsign is None:
+            rra.rrs_frontend(s["X"], G, perm, xq, dx, S, s["ws"], 0, stream)
+        else:
+            rra.rrs_frontend_signed(s["X"], G, perm, dsign, xq, dx, S, s["ws"], 0, stream)
 
     def gemm_step(i):
         s = sets[i % nsets]
@@ -234,7 +250,8 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8",
         "data": "synthetic (seeded outlier recipe; stands in for WikiText-2 / QA activations)",
-        "config": {"workload": wl.name, "M": M, "K": K, "N": N, "G": G, "input_sets": nsets},
+        "config": {"workload": wl.name, "M": M, "K": K, "N": N, "G": G, "input_sets": nsets,
+                   "rotation": "signed X D H" if dsign is not None else "X H"},
         "frontend_gbs": round(fe_gbs, 2),
         "gemm_tops": round(gemm_tops, 3),
         "roofline": gemm_roofline,

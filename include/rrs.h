@@ -52,6 +52,15 @@
  * - `perm` (int32 [K], device) must be a permutation of 0..K-1 (not checked
  *   on the device): position j of the reordered row takes rotated channel
  *   perm[j].
+ * - Signed rotation (the `_signed` entry points): the rotation becomes
+ *   Z = X D H_K with D = diag(d), d_j = -1 where bit j of the sign mask
+ *   `dsign` is set (uint32 [K/32] words, device, little-endian: bit j % 32
+ *   of word j / 32; K >= 64 so at least two words) and +1 elsewhere, and
+ *   the weights take H_K D W (the transform family P = D H^T of the AGC-OR
+ *   page, Sec. 4.1, with unit channel scaling; the signed online rotation
+ *   of its Sec. 4.6). Calibration, weight preparation and the front end of
+ *   one layer must use the same mask. `dsign` must not be NULL (use the
+ *   plain entry points for D = I).
  * - Non-finite inputs are outside the contract.
  */
 #ifndef RRS_H_
@@ -109,6 +118,10 @@ int rrs_workspace_init(void* ws, size_t ws_bytes, hipStream_t s);
 size_t rrs_calibrate_workspace_bytes(int K);
 int rrs_calibrate_perm(const void* X_cal_fp16, int T, int K, int32_t* perm,
                        void* ws, size_t ws_bytes, hipStream_t s);
+/* Same with the signed rotation X_cal D H_K. */
+int rrs_calibrate_perm_signed(const void* X_cal_fp16, int T, int K,
+                              const uint32_t* dsign, int32_t* perm, void* ws,
+                              size_t ws_bytes, hipStream_t s);
 
 /* Offline weight preparation (output-preserving transform of the AGC-OR page,
  * Sec. 3.1; reorder answer of the RRS rebuttal page; per-output-channel
@@ -118,6 +131,10 @@ int rrs_calibrate_perm(const void* X_cal_fp16, int T, int K, int32_t* perm,
  * bytes). Independent of G: one buffer serves every group size. */
 int rrs_prepare_weights(const void* W_fp16, int K, int N, const int32_t* perm,
                         void* wq, hipStream_t s);
+/* Same with Wz = H_K D W (the weight side of the signed rotation). */
+int rrs_prepare_weights_signed(const void* W_fp16, int K, int N,
+                               const int32_t* perm, const uint32_t* dsign,
+                               void* wq, hipStream_t s);
 
 /* The RRS A4W4 linear layer: Y fp32 [M, N] = RRS(X) against prepared weights.
  * `ws` holds rrs_workspace_bytes(M, K, G) bytes, initialised once with
@@ -127,6 +144,11 @@ int rrs_prepare_weights(const void* W_fp16, int K, int N, const int32_t* perm,
 int rrs_linear(const void* X_fp16, int M, int K, int N, int G,
                const int32_t* perm, const void* wq, float* Y, void* ws,
                size_t ws_bytes, hipStream_t s);
+/* Same with the signed rotation X D H_K (wq from rrs_prepare_weights_signed
+ * with the same mask). */
+int rrs_linear_signed(const void* X_fp16, int M, int K, int N, int G,
+                      const int32_t* perm, const uint32_t* dsign, const void* wq,
+                      float* Y, void* ws, size_t ws_bytes, hipStream_t s);
 
 /* Front end alone (same kernels as rrs_linear): writes xq uint8 [M][K/2],
  * dx fp32 [M] and S fp32 [K/G] (zero groups reported as 1). `ws` holds at
@@ -153,6 +175,12 @@ int rrs_linear(const void* X_fp16, int M, int K, int N, int G,
 int rrs_frontend(const void* X_fp16, int M, int K, int G, const int32_t* perm,
                  uint8_t* xq, float* dx, float* S, void* ws, size_t ws_bytes,
                  int flags, hipStream_t s);
+/* Same with the signed rotation X D H_K. The signs belong to the rotation:
+ * RRS_FLAG_NO_ROTATE together with a sign mask is rejected (RRS_EINVAL). */
+int rrs_frontend_signed(const void* X_fp16, int M, int K, int G,
+                        const int32_t* perm, const uint32_t* dsign, uint8_t* xq,
+                        float* dx, float* S, void* ws, size_t ws_bytes,
+                        int flags, hipStream_t s);
 
 /* Number of launches (1 or 2) the front end of rrs_linear / rrs_frontend
  * uses for M tokens of length K with these flags on the current device:

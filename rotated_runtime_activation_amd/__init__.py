@@ -27,6 +27,8 @@ EXPORTS = (
     "rrs_sync_bytes", "rrs_workspace_init", "rrs_calibrate_workspace_bytes",
     "rrs_calibrate_perm", "rrs_prepare_weights", "rrs_linear", "rrs_frontend", "rrs_gemm",
     "rrs_gemm_partials", "rrs_frontend_passes", "rrs_gemm_form",
+    "rrs_calibrate_perm_signed", "rrs_prepare_weights_signed", "rrs_linear_signed",
+    "rrs_frontend_signed",
 )
 
 
@@ -61,6 +63,10 @@ def _declare(lib):
         "rrs_gemm_partials": (i, [vp, i, i, i, i, vp, i, i, i, i, vp, vp]),
         "rrs_frontend_passes": (i, [i, i, i]),
         "rrs_gemm_form": (i, [i, i, i]),
+        "rrs_calibrate_perm_signed": (i, [vp, i, i, vp, vp, vp, sz, vp]),
+        "rrs_prepare_weights_signed": (i, [vp, i, i, vp, vp, vp, vp]),
+        "rrs_linear_signed": (i, [vp, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]),
+        "rrs_frontend_signed": (i, [vp, i, i, i, vp, vp, vp, vp, vp, vp, sz, i, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -201,6 +207,47 @@ def rrs_frontend(X, G: int, perm, xq, dx, S, ws, flags: int = 0, stream=None) ->
     M, K = X.shape
     _check("rrs_frontend", lib().rrs_frontend(
         _dev(X, torch.float16, "X"), M, K, G, _dev(perm, torch.int32, "perm", (K,)),
+        _dev(xq, torch.uint8, "xq", (M, K // 2)), _dev(dx, torch.float32, "dx", (M,)),
+        _dev(S, torch.float32, "S", (K // G,)), _dev(ws, None, "ws"), _nbytes(ws), flags,
+        _stream(stream)))
+
+
+# signed rotation X D H: dsign is int32 [K/32] holding the K-bit sign mask
+# (bit j set: channel j negated)
+def rrs_calibrate_perm_signed(X_cal, dsign, perm, ws, stream=None) -> None:
+    torch = _torch()
+    T, K = X_cal.shape
+    _check("rrs_calibrate_perm_signed", lib().rrs_calibrate_perm_signed(
+        _dev(X_cal, torch.float16, "X_cal"), T, K, _dev(dsign, torch.int32, "dsign", (K // 32,)),
+        _dev(perm, torch.int32, "perm", (K,)), _dev(ws, None, "ws"), _nbytes(ws), _stream(stream)))
+
+
+def rrs_prepare_weights_signed(W, perm, dsign, wq, stream=None) -> None:
+    torch = _torch()
+    K, N = W.shape
+    _check("rrs_prepare_weights_signed", lib().rrs_prepare_weights_signed(
+        _dev(W, torch.float16, "W"), K, N, _dev(perm, torch.int32, "perm", (K,)),
+        _dev(dsign, torch.int32, "dsign", (K // 32,)),
+        _dev(wq, torch.uint8, "wq", min_numel=rrs_weight_bytes(K, N)), _stream(stream)))
+
+
+def rrs_linear_signed(X, G: int, perm, dsign, wq, Y, ws, stream=None) -> None:
+    torch = _torch()
+    M, K = X.shape
+    N = Y.shape[1]
+    _check("rrs_linear_signed", lib().rrs_linear_signed(
+        _dev(X, torch.float16, "X"), M, K, N, G, _dev(perm, torch.int32, "perm", (K,)),
+        _dev(dsign, torch.int32, "dsign", (K // 32,)),
+        _dev(wq, torch.uint8, "wq", min_numel=rrs_weight_bytes(K, N)),
+        _dev(Y, torch.float32, "Y", (M, N)), _dev(ws, None, "ws"), _nbytes(ws), _stream(stream)))
+
+
+def rrs_frontend_signed(X, G: int, perm, dsign, xq, dx, S, ws, flags: int = 0, stream=None) -> None:
+    torch = _torch()
+    M, K = X.shape
+    _check("rrs_frontend_signed", lib().rrs_frontend_signed(
+        _dev(X, torch.float16, "X"), M, K, G, _dev(perm, torch.int32, "perm", (K,)),
+        _dev(dsign, torch.int32, "dsign", (K // 32,)),
         _dev(xq, torch.uint8, "xq", (M, K // 2)), _dev(dx, torch.float32, "dx", (M,)),
         _dev(S, torch.float32, "S", (K // G,)), _dev(ws, None, "ws"), _nbytes(ws), flags,
         _stream(stream)))

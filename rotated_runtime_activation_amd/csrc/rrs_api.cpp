@@ -88,38 +88,98 @@ RRS_API int rrs_workspace_init(void* ws, size_t ws_bytes, hipStream_t s) {
   return hip_status(rrs::launch_zero_u32(static_cast<uint32_t*>(ws), n, s));
 }
 
-RRS_API int rrs_calibrate_perm(const void* X_cal_fp16, int T, int K, int32_t* perm, void* ws,
-                               size_t ws_bytes, hipStream_t s) {
+namespace {
+
+int calibrate_impl(const void* X_cal_fp16, int T, int K, const uint32_t* dsign, int32_t* perm, void* ws,
+                   size_t ws_bytes, hipStream_t s) {
   if (X_cal_fp16 == nullptr || perm == nullptr || ws == nullptr) return RRS_EINVAL;
   if (T < 1 || !valid_K(K)) return RRS_EINVAL;
   if (ws_bytes < rrs_calibrate_workspace_bytes(K)) return RRS_EINVAL;
-  if (!all_a16(X_cal_fp16, perm, ws)) return RRS_EINVAL;
-  return hip_status(rrs::launch_calibrate(static_cast<const uint16_t*>(X_cal_fp16), T, ilog2(K), perm,
+  if (!all_a16(X_cal_fp16, perm, ws, dsign)) return RRS_EINVAL;
+  return hip_status(rrs::launch_calibrate(static_cast<const uint16_t*>(X_cal_fp16), T, ilog2(K), dsign, perm,
                                           static_cast<uint32_t*>(ws), s));
+}
+
+int prepare_impl(const void* W_fp16, int K, int N, const int32_t* perm, const uint32_t* dsign, void* wq,
+                 hipStream_t s) {
+  if (W_fp16 == nullptr || perm == nullptr || wq == nullptr) return RRS_EINVAL;
+  if (!valid_K(K) || N < 1) return RRS_EINVAL;
+  if (!all_a16(W_fp16, perm, wq, dsign)) return RRS_EINVAL;
+  uint8_t* codes = static_cast<uint8_t*>(wq);
+  float* dw = reinterpret_cast<float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
+  return hip_status(rrs::launch_weight_prep(static_cast<const uint16_t*>(W_fp16), ilog2(K), N, perm, dsign,
+                                            codes, dw, s));
+}
+
+int frontend_impl(const void* X_fp16, int M, int K, int G, const int32_t* perm, const uint32_t* dsign,
+                  uint8_t* xq, float* dx, float* S, void* ws, size_t ws_bytes, int flags, hipStream_t s) {
+  if (M < 0 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;
+  if (flags & ~(RRS_FLAG_NO_ROTATE | RRS_FLAG_NO_SMOOTH | RRS_FLAG_TWO_PASS)) return RRS_EINVAL;
+  if (dsign != nullptr && (flags & RRS_FLAG_NO_ROTATE)) return RRS_EINVAL;  // the signs belong to the rotation
+  if (perm == nullptr || S == nullptr || ws == nullptr) return RRS_EINVAL;
+  if (M > 0 && (X_fp16 == nullptr || xq == nullptr || dx == nullptr)) return RRS_EINVAL;
+  if (ws_bytes < sync_bytes(K, G)) return RRS_EINVAL;
+  if (!all_a16(X_fp16, perm, xq, dx, S, ws, dsign)) return RRS_EINVAL;
+  if (M == 0) return RRS_OK;
+  return hip_status(rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, ilog2(K), G, perm, dsign, xq,
+                                         dx, S, static_cast<uint32_t*>(ws), flags, s));
+}
+
+int linear_impl(const void* X_fp16, int M, int K, int N, int G, const int32_t* perm, const uint32_t* dsign,
+                const void* wq, float* Y, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (M < 0 || N < 1 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;
+  if (perm == nullptr || wq == nullptr || ws == nullptr) return RRS_EINVAL;
+  if (M > 0 && (X_fp16 == nullptr || Y == nullptr)) return RRS_EINVAL;
+  const WsLayout l = ws_layout(M, K, G);
+  if (ws_bytes < l.total) return RRS_EINVAL;
+  if (!all_a16(X_fp16, perm, wq, Y, ws, dsign)) return RRS_EINVAL;
+  if (M == 0) return RRS_OK;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* xq = base + l.xq;
+  float* dx = reinterpret_cast<float*>(base + l.dx);
+  float* S = reinterpret_cast<float*>(base + l.S);
+  hipError_t e = rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, ilog2(K), G, perm, dsign, xq, dx,
+                                      S, reinterpret_cast<uint32_t*>(base + l.sync), 0, s);
+  if (e != hipSuccess) return RRS_EHIP;
+  const uint8_t* codes = static_cast<const uint8_t*>(wq);
+  const float* dw = reinterpret_cast<const float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
+  return hip_status(rrs::launch_gemm(xq, dx, S, M, ilog2(K), N, G, codes, dw, Y, nullptr, 0, 0, 0, 0, s));
+}
+
+}  // namespace
+
+RRS_API int rrs_calibrate_perm(const void* X_cal_fp16, int T, int K, int32_t* perm, void* ws,
+                               size_t ws_bytes, hipStream_t s) {
+  return calibrate_impl(X_cal_fp16, T, K, nullptr, perm, ws, ws_bytes, s);
+}
+
+RRS_API int rrs_calibrate_perm_signed(const void* X_cal_fp16, int T, int K, const uint32_t* dsign, int32_t* perm,
+                                      void* ws, size_t ws_bytes, hipStream_t s) {
+  if (dsign == nullptr) return RRS_EINVAL;
+  return calibrate_impl(X_cal_fp16, T, K, dsign, perm, ws, ws_bytes, s);
 }
 
 RRS_API int rrs_prepare_weights(const void* W_fp16, int K, int N, const int32_t* perm, void* wq,
                                 hipStream_t s) {
-  if (W_fp16 == nullptr || perm == nullptr || wq == nullptr) return RRS_EINVAL;
-  if (!valid_K(K) || N < 1) return RRS_EINVAL;
-  if (!all_a16(W_fp16, perm, wq)) return RRS_EINVAL;
-  uint8_t* codes = static_cast<uint8_t*>(wq);
-  float* dw = reinterpret_cast<float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
-  return hip_status(rrs::launch_weight_prep(static_cast<const uint16_t*>(W_fp16), ilog2(K), N, perm,
-                                            codes, dw, s));
+  return prepare_impl(W_fp16, K, N, perm, nullptr, wq, s);
+}
+
+RRS_API int rrs_prepare_weights_signed(const void* W_fp16, int K, int N, const int32_t* perm,
+                                       const uint32_t* dsign, void* wq, hipStream_t s) {
+  if (dsign == nullptr) return RRS_EINVAL;
+  return prepare_impl(W_fp16, K, N, perm, dsign, wq, s);
 }
 
 RRS_API int rrs_frontend(const void* X_fp16, int M, int K, int G, const int32_t* perm, uint8_t* xq,
                          float* dx, float* S, void* ws, size_t ws_bytes, int flags, hipStream_t s) {
-  if (M < 0 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;
-  if (flags & ~(RRS_FLAG_NO_ROTATE | RRS_FLAG_NO_SMOOTH | RRS_FLAG_TWO_PASS)) return RRS_EINVAL;
-  if (perm == nullptr || S == nullptr || ws == nullptr) return RRS_EINVAL;
-  if (M > 0 && (X_fp16 == nullptr || xq == nullptr || dx == nullptr)) return RRS_EINVAL;
-  if (ws_bytes < sync_bytes(K, G)) return RRS_EINVAL;
-  if (!all_a16(X_fp16, perm, xq, dx, S, ws)) return RRS_EINVAL;
-  if (M == 0) return RRS_OK;
-  return hip_status(rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, ilog2(K), G, perm, xq,
-                                         dx, S, static_cast<uint32_t*>(ws), flags, s));
+  return frontend_impl(X_fp16, M, K, G, perm, nullptr, xq, dx, S, ws, ws_bytes, flags, s);
+}
+
+RRS_API int rrs_frontend_signed(const void* X_fp16, int M, int K, int G, const int32_t* perm,
+                                const uint32_t* dsign, uint8_t* xq, float* dx, float* S, void* ws,
+                                size_t ws_bytes, int flags, hipStream_t s) {
+  if (dsign == nullptr) return RRS_EINVAL;
+  return frontend_impl(X_fp16, M, K, G, perm, dsign, xq, dx, S, ws, ws_bytes, flags, s);
 }
 
 RRS_API int rrs_frontend_passes(int M, int K, int flags) {
@@ -160,21 +220,12 @@ RRS_API int rrs_gemm_partials(const uint8_t* xq, int M, int K, int N, int G, con
 
 RRS_API int rrs_linear(const void* X_fp16, int M, int K, int N, int G, const int32_t* perm,
                        const void* wq, float* Y, void* ws, size_t ws_bytes, hipStream_t s) {
-  if (M < 0 || N < 1 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;
-  if (perm == nullptr || wq == nullptr || ws == nullptr) return RRS_EINVAL;
-  if (M > 0 && (X_fp16 == nullptr || Y == nullptr)) return RRS_EINVAL;
-  const WsLayout l = ws_layout(M, K, G);
-  if (ws_bytes < l.total) return RRS_EINVAL;
-  if (!all_a16(X_fp16, perm, wq, Y, ws)) return RRS_EINVAL;
-  if (M == 0) return RRS_OK;
-  uint8_t* base = static_cast<uint8_t*>(ws);
-  uint8_t* xq = base + l.xq;
-  float* dx = reinterpret_cast<float*>(base + l.dx);
-  float* S = reinterpret_cast<float*>(base + l.S);
-  hipError_t e = rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, ilog2(K), G, perm, xq, dx, S,
-                                      reinterpret_cast<uint32_t*>(base + l.sync), 0, s);
-  if (e != hipSuccess) return RRS_EHIP;
-  const uint8_t* codes = static_cast<const uint8_t*>(wq);
-  const float* dw = reinterpret_cast<const float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
-  return hip_status(rrs::launch_gemm(xq, dx, S, M, ilog2(K), N, G, codes, dw, Y, nullptr, 0, 0, 0, 0, s));
+  return linear_impl(X_fp16, M, K, N, G, perm, nullptr, wq, Y, ws, ws_bytes, s);
+}
+
+RRS_API int rrs_linear_signed(const void* X_fp16, int M, int K, int N, int G, const int32_t* perm,
+                              const uint32_t* dsign, const void* wq, float* Y, void* ws, size_t ws_bytes,
+                              hipStream_t s) {
+  if (dsign == nullptr) return RRS_EINVAL;
+  return linear_impl(X_fp16, M, K, N, G, perm, dsign, wq, Y, ws, ws_bytes, s);
 }

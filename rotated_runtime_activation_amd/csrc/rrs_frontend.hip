@@ -76,6 +76,7 @@ struct FeArgs {
   float* scale;         // [rows]
   float* S_out;         // [K/G]
   uint32_t* colmax;     // [K] (calibration)
+  const uint8_t* dsign; // signed rotation: K-bit mask, bit j set -> channel j negated (nullptr: none)
 };
 
 __device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
@@ -364,6 +365,34 @@ __device__ __forceinline__ void load_block(uint4 (&w)[Cfg<LOG2K>::kChunks], cons
   }
 }
 
+// Signed rotation (x D H, D = diag(+-1)): the mask byte of the 8 channels
+// of each 16-byte chunk, loaded with the block; flipping an fp16 sign bit
+// is exact. Rows of the block share the channels of their column offset.
+template <int LOG2K>
+struct SignLoads {
+  uint32_t b[Cfg<LOG2K>::kChunks];
+};
+
+template <int LOG2K>
+__device__ __forceinline__ void sign_loads(SignLoads<LOG2K>& sl, const uint8_t* dsign, int lane) {
+  constexpr int K = 1 << LOG2K;
+#pragma unroll
+  for (int i = 0; i < Cfg<LOG2K>::kChunks; ++i)
+    sl.b[i] = dsign ? static_cast<uint32_t>(dsign[((8 * lane + 512 * i) & (K - 1)) >> 3]) : 0u;
+}
+
+template <int LOG2K>
+__device__ __forceinline__ void apply_signs(uint4 (&w)[Cfg<LOG2K>::kChunks], const SignLoads<LOG2K>& sl) {
+#pragma unroll
+  for (int i = 0; i < Cfg<LOG2K>::kChunks; ++i) {
+    const uint32_t b = sl.b[i];  // bit e: half e of the chunk
+    w[i].x ^= ((b & 1u) << 15) | ((b & 2u) << 30);
+    w[i].y ^= ((b & 4u) << 13) | ((b & 8u) << 28);
+    w[i].z ^= ((b & 16u) << 11) | ((b & 32u) << 26);
+    w[i].w ^= ((b & 64u) << 9) | ((b & 128u) << 24);
+  }
+}
+
 template <int LOG2K>
 __device__ __forceinline__ void widen_block(float (&v)[Cfg<LOG2K>::kE], const uint4 (&w)[Cfg<LOG2K>::kChunks]) {
 #pragma unroll
@@ -540,6 +569,8 @@ frontend_kernel(FeArgs a) {
   if constexpr (MODE != kColmax) table_loads<LOG2K>(tl, a.perm, tid);
   uint4 w[C::kChunks];
   if constexpr (MODE != kWeight) load_block<LOG2K>(w, a.src, a.rows, row0, lane);
+  SignLoads<LOG2K> sg;
+  if constexpr (ROTATE) sign_loads<LOG2K>(sg, a.dsign, lane);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- per-workgroup set-up -------------------------------------------
@@ -585,6 +616,9 @@ frontend_kernel(FeArgs a) {
     }
     float v[E];
     float* wb = s_buf[wave];
+    if constexpr (ROTATE) {
+      if (a.dsign) apply_signs<LOG2K>(w, sg);
+    }
     if constexpr (ROTATE && LOG2K >= 12) {
       rotate_block_mfma<LOG2K>(v, w, lane);
     } else {
@@ -689,6 +723,8 @@ fused_kernel(FeArgs a) {
   uint4 w[R][C::kChunks];
 #pragma unroll
   for (int q = 0; q < R; ++q) load_block<LOG2K>(w[q], a.src, a.rows, row0[q], lane);
+  SignLoads<LOG2K> sg;
+  if constexpr (ROTATE) sign_loads<LOG2K>(sg, a.dsign, lane);
   // every load is issued before the table is filled: waiting for the perm
   // loads then leaves the activation loads in flight
   __builtin_amdgcn_sched_barrier(0);
@@ -707,6 +743,9 @@ fused_kernel(FeArgs a) {
   float* wb = s_buf[wave];
 #pragma unroll
   for (int q = 0; q < R; ++q) {
+    if constexpr (ROTATE) {
+      if (a.dsign) apply_signs<LOG2K>(w[q], sg);
+    }
     if constexpr (ROTATE && LOG2K >= 12) {
       rotate_block_mfma<LOG2K>(v[q], w[q], lane);
     } else {
@@ -919,9 +958,10 @@ bool fused_k(int log2K, const FeArgs& a, hipStream_t s, hipError_t* err) {
 }  // namespace
 
 hipError_t launch_frontend(const uint16_t* X, int M, int log2K, int G, const int32_t* perm,
-                           uint8_t* xq, float* dx, float* S_out, uint32_t* sync, int flags,
-                           hipStream_t s) {
+                           const uint32_t* dsign, uint8_t* xq, float* dx, float* S_out, uint32_t* sync,
+                           int flags, hipStream_t s) {
   FeArgs a{};
+  a.dsign = reinterpret_cast<const uint8_t*>(dsign);
   a.src = X;
   a.rows = M;
   a.log2G = __builtin_ctz(static_cast<unsigned>(G));
@@ -957,8 +997,9 @@ int frontend_launches(int M, int log2K, int flags) {
 }
 
 hipError_t launch_weight_prep(const uint16_t* W, int log2K, int N, const int32_t* perm,
-                              uint8_t* wq, float* dw, hipStream_t s) {
+                              const uint32_t* dsign, uint8_t* wq, float* dw, hipStream_t s) {
   FeArgs a{};
+  a.dsign = reinterpret_cast<const uint8_t*>(dsign);
   a.src = W;
   a.rows = N;
   a.ldw = N;
@@ -970,8 +1011,8 @@ hipError_t launch_weight_prep(const uint16_t* W, int log2K, int N, const int32_t
   return dispatch_k<kWeight, true>(log2K, a, s);
 }
 
-hipError_t launch_calibrate(const uint16_t* Xc, int T, int log2K, int32_t* perm, uint32_t* ws,
-                            hipStream_t s) {
+hipError_t launch_calibrate(const uint16_t* Xc, int T, int log2K, const uint32_t* dsign, int32_t* perm,
+                            uint32_t* ws, hipStream_t s) {
   const int K = 1 << log2K;
   hipError_t e = launch_zero_u32(ws, static_cast<size_t>(K), s);
   if (e != hipSuccess) return e;
@@ -980,6 +1021,7 @@ hipError_t launch_calibrate(const uint16_t* Xc, int T, int log2K, int32_t* perm,
   a.rows = T;
   a.log2G = log2K;
   a.colmax = ws;
+  a.dsign = reinterpret_cast<const uint8_t*>(dsign);
   e = dispatch_k<kColmax, true>(log2K, a, s);
   if (e != hipSuccess) return e;
   const int grid = (K + 1023) / 1024;

@@ -43,22 +43,25 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // the device at once, else a stats pass then a quantise pass.
 //   flags: bit0 = skip rotation, bit1 = skip smoothing (S = 1),
 //          bit2 = always use the two launches.
+//   dsign: signed rotation x D H, K-bit mask (bit j set: channel j negated),
+//          or nullptr for the plain rotation.
 hipError_t launch_frontend(const uint16_t* X, int M, int log2K, int G, const int32_t* perm,
-                           uint8_t* xq, float* dx, float* S_out, uint32_t* sync, int flags,
-                           hipStream_t s);
+                           const uint32_t* dsign, uint8_t* xq, float* dx, float* S_out, uint32_t* sync,
+                           int flags, hipStream_t s);
 
 // Launches the front end would use for M rows on the current device (1 or
 // 2), -1 for an unsupported K.
 int frontend_launches(int M, int log2K, int flags);
 
-// Offline weight preparation: W [K, N] row-major fp16 -> wq [N][K/2] + dw [N].
+// Offline weight preparation: W [K, N] row-major fp16 -> wq [N][K/2] + dw [N]
+// (H D W with a sign mask, H W without).
 hipError_t launch_weight_prep(const uint16_t* W, int log2K, int N, const int32_t* perm,
-                              uint8_t* wq, float* dw, hipStream_t s);
+                              const uint32_t* dsign, uint8_t* wq, float* dw, hipStream_t s);
 
 // Calibration permutation: per-channel |max| of the rotated rows, then a
 // stable descending rank. ws holds K uint32.
-hipError_t launch_calibrate(const uint16_t* Xc, int T, int log2K, int32_t* perm, uint32_t* ws,
-                            hipStream_t s);
+hipError_t launch_calibrate(const uint16_t* Xc, int T, int log2K, const uint32_t* dsign, int32_t* perm,
+                            uint32_t* ws, hipStream_t s);
 
 // Zero n uint32 words (fill kernel; used instead of hipMemsetAsync).
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);

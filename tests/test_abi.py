@@ -168,6 +168,26 @@ def test_misaligned_pointers_rejected():
     assert L.rrs_workspace_init(odd, 1024, NULL) == rra.RRS_EINVAL
 
 
+def test_signed_entry_points_reject():
+    """The signed entry points need a 16-byte aligned, non-null sign mask,
+    and the front end rejects signs without the rotation."""
+    L = rra.lib()
+    odd = ctypes.c_void_p(0x1004)
+    for dsign in (NULL, odd):
+        assert L.rrs_linear_signed(DUMMY, 16, 256, 256, 128, DUMMY, dsign, DUMMY, DUMMY, DUMMY, 1 << 20,
+                                   NULL) == rra.RRS_EINVAL
+        assert L.rrs_prepare_weights_signed(DUMMY, 256, 8, DUMMY, dsign, DUMMY, NULL) == rra.RRS_EINVAL
+        assert L.rrs_calibrate_perm_signed(DUMMY, 8, 256, dsign, DUMMY, DUMMY, 1024, NULL) == rra.RRS_EINVAL
+        assert L.rrs_frontend_signed(DUMMY, 4, 256, 64, DUMMY, dsign, DUMMY, DUMMY, DUMMY, DUMMY, 1 << 20, 0,
+                                     NULL) == rra.RRS_EINVAL
+    assert L.rrs_frontend_signed(DUMMY, 4, 256, 64, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 1 << 20,
+                                 rra.RRS_FLAG_NO_ROTATE, NULL) == rra.RRS_EINVAL
+    assert L.rrs_frontend_signed(NULL, 0, 256, 64, DUMMY, DUMMY, NULL, NULL, DUMMY, DUMMY, 1 << 20, 0,
+                                 NULL) == rra.RRS_OK
+    assert L.rrs_linear_signed(NULL, 0, 256, 256, 128, DUMMY, DUMMY, DUMMY, NULL, DUMMY, 1 << 20,
+                               NULL) == rra.RRS_OK
+
+
 def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(rra, "_lib", None)
     monkeypatch.setattr(rra, "LIB_PATH", "/nonexistent/librrs.so")
