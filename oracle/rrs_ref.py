@@ -33,7 +33,7 @@ R8 codes in [-7, 7]; R9 zero group -> scale 1, zero row -> codes 0 and scale 0;
 R10 4-bit sign-magnitude packing, 8 codes per 32-bit word (layout in
 ``pack_codes``); R11 weights RTN per output
 channel; R12 the group scale multiplies each group's integer partial;
-R16 the signed rotation variant is Z = X D H with D = diag(d), d in {+1, -1}^K
+R18 the signed rotation variant is Z = X D H with D = diag(d), d in {+1, -1}^K
 given by the caller, and the weights take H D W ([AGC-OR] Sec. 4.1, the
 transform family P = Lambda^-1 D H^T with Lambda = I; Sec. 4.6 "Signed online
 rotation": sign flips before the online Hadamard rotation).
@@ -83,7 +83,7 @@ def fwht(x: np.ndarray) -> np.ndarray:
 def rotate_rows(x: np.ndarray, d=None) -> np.ndarray:
     """The online rotation of the activations: x H, or with a sign vector d
     (+1 / -1 per input channel) the signed rotation x D H of [AGC-OR]
-    Sec. 4.1 / Sec. 4.6 (reading R16). Flipping signs of fp16 values is exact,
+    Sec. 4.1 / Sec. 4.6 (reading R18). Flipping signs of fp16 values is exact,
     so this is as exact as ``fwht``."""
     x = np.asarray(x, dtype=np.float64)
     if d is None:
@@ -136,7 +136,7 @@ def prepare_weights(W: np.ndarray, perm: np.ndarray, d=None) -> Dict[str, np.nda
     Output-preserving transform ([AGC-OR] Sec. 3.1): rotating the activations
     by H is undone by H^T applied to the weights, and H is symmetric, so the
     rotated weight is Wz = H W (each column transformed); with signs
-    (Z = X D H) it is Wz = H D W, since D D = I (reading R16). The reorder applies
+    (Z = X D H) it is Wz = H D W, since D D = I (reading R18). The reorder applies
     the same permutation to the weight rows ([RRS-rebuttal], reorder answer).
     Each output channel is quantised symmetric per channel with
     Delta_w = max|col| / 7 ([AGC-OR] Sec. 5; R11).
@@ -172,7 +172,7 @@ def frontend(X: np.ndarray, perm: np.ndarray, G: int, *, rotate: bool = True,
     ``rotate=False`` gives Runtime Smooth without rotation and
     ``smooth=False`` gives rotation only (S = 1): the ablations of
     [RRS-rebuttal] "Incomplete ablation study". ``d`` (a +-1 vector) makes
-    the rotation the signed one, Z = X D H (reading R16).
+    the rotation the signed one, Z = X D H (reading R18).
     """
     X = np.asarray(X)
     M, K = X.shape

@@ -149,7 +149,7 @@ def frontend_invariants(frontend, seed=5, M=40, K=512, G=64) -> bool:
 
 def signed_rotation_matches_explicit(rotate_rows, sizes=(2, 8, 64, 256), seed=3) -> bool:
     """Signed rotation x D H against the explicit product with scipy's
-    Sylvester Hadamard and diag(d) ([AGC-OR] Sec. 4.1; reading R16). fp16
+    Sylvester Hadamard and diag(d) ([AGC-OR] Sec. 4.1; reading R18). fp16
     inputs make both sides exact in float64."""
     g = np.random.default_rng(seed)
     for n in sizes:

@@ -1,5 +1,5 @@
 """GPU parity of the signed rotation X D H (AGC-OR page, Sec. 4.1 / Sec. 4.6;
-reading R16) against the oracle: front end (both forms, butterfly and
+reading R18) against the oracle: front end (both forms, butterfly and
 matrix-core rotations), weight preparation H D W, calibration and the whole
 layer (run on an MI355X: -m gpu)."""
 import numpy as np

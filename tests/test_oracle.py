@@ -271,7 +271,7 @@ def test_pack_layout_feeds_fp8_subnormals():
         assert np.array_equal(dec(hi, j), q[:, 2 * j + 1])
 
 
-# ---- signed rotation (x D H; [AGC-OR] Sec. 4.1 / Sec. 4.6, reading R16)
+# ---- signed rotation (x D H; [AGC-OR] Sec. 4.1 / Sec. 4.6, reading R18)
 def test_signed_rotation_explicit_and_inverse():
     assert pins.signed_rotation_matches_explicit(oracle.rotate_rows)
     assert pins.signed_rotation_inverts(oracle.rotate_rows)
