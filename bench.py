@@ -43,8 +43,9 @@ MALL_BYTES = 256 << 20
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps first: the shader clock needs tens of milliseconds of load to settle")
     ap.add_argument("--workload", default="o_proj")
     ap.add_argument("--G", type=int, default=None)
     ap.add_argument("--signed", action="store_true",
