@@ -36,7 +36,12 @@ channel; R12 the group scale multiplies each group's integer partial;
 R18 the signed rotation variant is Z = X D H with D = diag(d), d in {+1, -1}^K
 given by the caller, and the weights take H D W ([AGC-OR] Sec. 4.1, the
 transform family P = Lambda^-1 D H^T with Lambda = I; Sec. 4.6 "Signed online
-rotation": sign flips before the online Hadamard rotation).
+rotation": sign flips before the online Hadamard rotation);
+R19 for K = m 2^k with m in {12, 20, 28} (no power of two) the rotation is
+the Kronecker product H_K = H_m (x) H_{2^k}, H_m from Paley's constructions
+(I for q = 11, 19; II for q = 13) and Sylvester H_{2^k}; x indexed i 2^k + j
+(i < m). H_m need not be symmetric, so the weights take H_K^T W (which is
+W^T H_K row by row: the same row transform as the activations).
 
 Every function below is pinned by ``tests/test_oracle_*.py`` against something
 other than itself (explicit Hadamard matrices, scipy's Hadamard, closed forms,
@@ -80,18 +85,84 @@ def fwht(x: np.ndarray) -> np.ndarray:
     return y.reshape(lead + (n,))
 
 
+KRON_ORDERS = (12, 20, 28)
+
+
+def _legendre(a: int, q: int) -> int:
+    a %= q
+    if a == 0:
+        return 0
+    return 1 if pow(a, (q - 1) // 2, q) == 1 else -1
+
+
+def hadamard_paley(m: int) -> np.ndarray:
+    """A Hadamard matrix of order m in {12, 20, 28} (reading R19), from
+    Paley's constructions with the quadratic character chi of GF(q), q prime:
+    construction I for q = m - 1 = 11, 19 (q = 3 mod 4): with the Jacobsthal
+    matrix Q[i, j] = chi(j - i), H = I + [[0, 1^T], [-1, Q]]; construction II
+    for q = 13 (q = 1 mod 4), m = 2 (q + 1): with the symmetric conference
+    matrix C = [[0, 1^T], [1, Q]], H = [[C + I, C - I], [C - I, -C - I]].
+    Pinned by H H^T = m I in the tests."""
+    if m in (12, 20):
+        q = m - 1
+        Q = np.array([[_legendre(j - i, q) for j in range(q)] for i in range(q)], dtype=np.float64)
+        S = np.zeros((m, m))
+        S[0, 1:] = 1.0
+        S[1:, 0] = -1.0
+        S[1:, 1:] = Q
+        return np.eye(m) + S
+    if m == 28:
+        q = 13
+        Q = np.array([[_legendre(j - i, q) for j in range(q)] for i in range(q)], dtype=np.float64)
+        C = np.zeros((q + 1, q + 1))
+        C[0, 1:] = 1.0
+        C[1:, 0] = 1.0
+        C[1:, 1:] = Q
+        I = np.eye(q + 1)
+        return np.block([[C + I, C - I], [C - I, -C - I]])
+    raise ValueError("Hadamard orders built here: 12, 20, 28")
+
+
+def kron_split(K: int):
+    """(m, n) with K = m n, n a power of two and m = 1 (K a power of two) or
+    m in KRON_ORDERS; ValueError otherwise."""
+    if K > 0 and K & (K - 1) == 0:
+        return 1, K
+    for m in KRON_ORDERS:
+        if K % m == 0:
+            n = K // m
+            if n & (n - 1) == 0:
+                return m, n
+    raise ValueError(f"K = {K} is neither a power of two nor m 2^k with m in {KRON_ORDERS}")
+
+
+def hadamard_rows(x: np.ndarray) -> np.ndarray:
+    """x @ H_K along the last axis: Sylvester H_K for a power of two (``fwht``),
+    else H_m (x) H_n with K = m n (reading R19): H_n over each run of n
+    consecutive channels, then H_m across the runs."""
+    x = np.asarray(x, dtype=np.float64)
+    K = x.shape[-1]
+    m, n = kron_split(K)
+    if m == 1:
+        return fwht(x)
+    lead = x.shape[:-1]
+    y = fwht(x.reshape(lead + (m, n)))                 # sum_j x[i, j] H_n[j, b]
+    y = np.einsum("...ib,ia->...ab", y, hadamard_paley(m))  # sum_i (.)[i, b] H_m[i, a]
+    return y.reshape(lead + (K,))
+
+
 def rotate_rows(x: np.ndarray, d=None) -> np.ndarray:
     """The online rotation of the activations: x H, or with a sign vector d
     (+1 / -1 per input channel) the signed rotation x D H of [AGC-OR]
-    Sec. 4.1 / Sec. 4.6 (reading R18). Flipping signs of fp16 values is exact,
-    so this is as exact as ``fwht``."""
+    Sec. 4.1 / Sec. 4.6 (reading R18); H = H_K of ``hadamard_rows``.
+    Flipping signs of fp16 values is exact."""
     x = np.asarray(x, dtype=np.float64)
     if d is None:
-        return fwht(x)
+        return hadamard_rows(x)
     d = np.asarray(d, dtype=np.float64)
     if d.shape != (x.shape[-1],) or not np.all(np.abs(d) == 1.0):
         raise ValueError("d must be a +-1 vector over the channels")
-    return fwht(x * d)
+    return hadamard_rows(x * d)
 
 
 def signs_from_bits(bits: np.ndarray, K: int) -> np.ndarray:

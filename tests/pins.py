@@ -169,3 +169,28 @@ def signed_rotation_inverts(rotate_rows, n=512, seed=4) -> bool:
     z = rotate_rows(x, d)
     back = (z @ scipy.linalg.hadamard(n).astype(np.float64)) / n * d
     return bool(np.array_equal(back, x))
+
+
+def paley_is_hadamard(hadamard_paley, orders=(12, 20, 28)) -> bool:
+    """H H^T = m I with +-1 entries: the defining property of a Hadamard matrix
+    (reading R19)."""
+    for m in orders:
+        H = hadamard_paley(m)
+        if H.shape != (m, m) or not np.all(np.abs(H) == 1.0):
+            return False
+        if not np.array_equal(H @ H.T, m * np.eye(m)):
+            return False
+    return True
+
+
+def kron_rotation_matches_explicit(hadamard_rows, hadamard_paley, cases=((12, 64), (20, 64), (28, 64), (12, 128)),
+                                   seed=13) -> bool:
+    """x H_K for K = m n against the explicit dense Kronecker product
+    kron(H_m, H_n) with scipy's Sylvester H_n (fp16 inputs: exact)."""
+    g = np.random.default_rng(seed)
+    for m, n in cases:
+        x = g.standard_normal((4, m * n)).astype(np.float16)
+        ref = x.astype(np.float64) @ np.kron(hadamard_paley(m), scipy.linalg.hadamard(n).astype(np.float64))
+        if not np.array_equal(hadamard_rows(x), ref):
+            return False
+    return True

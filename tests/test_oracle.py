@@ -313,3 +313,36 @@ def test_signs_from_bits_brute_force():
     for j in range(K):
         word = int(bits[j // 32])
         assert d[j] == (-1.0 if (word >> (j % 32)) & 1 else 1.0)
+
+
+# ---- Kronecker rotation for K = m 2^k (reading R19)
+def test_paley_orders_are_hadamard():
+    assert pins.paley_is_hadamard(oracle.hadamard_paley)
+
+
+def test_kron_rotation_explicit():
+    assert pins.kron_rotation_matches_explicit(oracle.hadamard_rows, oracle.hadamard_paley)
+
+
+def test_kron_split():
+    assert oracle.kron_split(4096) == (1, 4096)
+    assert oracle.kron_split(14336) == (28, 512)
+    assert oracle.kron_split(768) == (12, 64)
+    assert oracle.kron_split(5120) == (20, 256)
+    for bad in (100, 11008, 14 * 3):
+        with pytest.raises(ValueError):
+            oracle.kron_split(bad)
+
+
+@pytest.mark.parametrize("K,G", [(768, 64), (1792, 128)])
+def test_kron_unrounded_output_equals_xw(K, G):
+    assert pins.unrounded_output_is_xw(oracle.frontend, oracle.prepare_weights, oracle.linear_out, K=K, G=G)
+
+
+def test_kron_signed_rotation_explicit():
+    g = np.random.default_rng(14)
+    m, n = 20, 64
+    x = g.standard_normal((3, m * n)).astype(np.float16)
+    d = np.where(g.random(m * n) < 0.5, -1.0, 1.0)
+    ref = (x.astype(np.float64) * d) @ np.kron(oracle.hadamard_paley(m), scipy.linalg.hadamard(n).astype(np.float64))
+    assert np.array_equal(oracle.rotate_rows(x, d), ref)

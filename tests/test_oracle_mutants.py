@@ -127,3 +127,27 @@ def test_signs_after_rotation_mutant_fails():
 
 def test_signs_ignored_mutant_fails():
     assert not pins.signed_rotation_matches_explicit(lambda x, d=None: oracle.fwht(x))
+
+
+def test_kron_order_mutant_fails():
+    # slip: H_n (x) H_m instead of H_m (x) H_n
+    def rows_swapped(x):
+        x = np.asarray(x, dtype=np.float64)
+        m, n = oracle.kron_split(x.shape[-1])
+        y = np.einsum("...ij,ja->...ia", x.reshape(x.shape[:-1] + (n, m)), oracle.hadamard_paley(m))
+        return oracle.fwht(np.swapaxes(y, -1, -2)).swapaxes(-1, -2).reshape(x.shape)
+    assert not pins.kron_rotation_matches_explicit(rows_swapped, oracle.hadamard_paley)
+
+
+def test_kron_transposed_factor_mutant_fails():
+    # slip: H_m^T in place of H_m (Paley I matrices are not symmetric)
+    assert not pins.kron_rotation_matches_explicit(oracle.hadamard_rows, lambda m: oracle.hadamard_paley(m).T)
+
+
+def test_paley_wrong_character_mutant_fails():
+    # slip: Jacobsthal matrix with chi(i - j) and no border sign change
+    def bad(m):
+        H = oracle.hadamard_paley(m)
+        H[1:, 0] = 1.0
+        return H
+    assert not pins.paley_is_hadamard(bad, orders=(12,))
