@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "librrs.so")
-SOURCES = ["rrs_frontend.hip", "rrs_gemm.hip", "rrs_gemm_small.hip", "rrs_api.cpp"]
+SOURCES = ["rrs_frontend.hip", "rrs_frontend_kron.hip", "rrs_gemm.hip", "rrs_gemm_small.hip", "rrs_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -14,10 +14,15 @@ using rrs::align256;
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 int ilog2(int x) { return 31 - __builtin_clz(static_cast<unsigned>(x)); }
 
+// K: a power of two in [64, 8192], or m 2^k with m in {12, 20, 28} (the
+// Kronecker rotation; see rrs::kron_split)
 bool valid_K(int K) {
-  return pow2(K) && ilog2(K) >= rrs::kMinLog2K && ilog2(K) <= rrs::kMaxLog2K;
+  if (K <= 0) return false;
+  if (pow2(K)) return ilog2(K) >= rrs::kMinLog2K && ilog2(K) <= rrs::kMaxLog2K;
+  int m = 0, ln = 0;
+  return rrs::kron_split(K, &m, &ln);
 }
-bool valid_G(int G, int K) { return pow2(G) && G >= rrs::kMinG && G <= K; }
+bool valid_G(int G, int K) { return pow2(G) && G >= rrs::kMinG && G <= K && K % G == 0; }
 
 // every device pointer argument is read or written with 16-byte accesses
 bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -96,7 +101,7 @@ int calibrate_impl(const void* X_cal_fp16, int T, int K, const uint32_t* dsign, 
   if (T < 1 || !valid_K(K)) return RRS_EINVAL;
   if (ws_bytes < rrs_calibrate_workspace_bytes(K)) return RRS_EINVAL;
   if (!all_a16(X_cal_fp16, perm, ws, dsign)) return RRS_EINVAL;
-  return hip_status(rrs::launch_calibrate(static_cast<const uint16_t*>(X_cal_fp16), T, ilog2(K), dsign, perm,
+  return hip_status(rrs::launch_calibrate(static_cast<const uint16_t*>(X_cal_fp16), T, K, dsign, perm,
                                           static_cast<uint32_t*>(ws), s));
 }
 
@@ -107,7 +112,7 @@ int prepare_impl(const void* W_fp16, int K, int N, const int32_t* perm, const ui
   if (!all_a16(W_fp16, perm, wq, dsign)) return RRS_EINVAL;
   uint8_t* codes = static_cast<uint8_t*>(wq);
   float* dw = reinterpret_cast<float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
-  return hip_status(rrs::launch_weight_prep(static_cast<const uint16_t*>(W_fp16), ilog2(K), N, perm, dsign,
+  return hip_status(rrs::launch_weight_prep(static_cast<const uint16_t*>(W_fp16), K, N, perm, dsign,
                                             codes, dw, s));
 }
 
@@ -121,7 +126,7 @@ int frontend_impl(const void* X_fp16, int M, int K, int G, const int32_t* perm, 
   if (ws_bytes < sync_bytes(K, G)) return RRS_EINVAL;
   if (!all_a16(X_fp16, perm, xq, dx, S, ws, dsign)) return RRS_EINVAL;
   if (M == 0) return RRS_OK;
-  return hip_status(rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, ilog2(K), G, perm, dsign, xq,
+  return hip_status(rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, K, G, perm, dsign, xq,
                                          dx, S, static_cast<uint32_t*>(ws), flags, s));
 }
 
@@ -138,12 +143,12 @@ int linear_impl(const void* X_fp16, int M, int K, int N, int G, const int32_t* p
   uint8_t* xq = base + l.xq;
   float* dx = reinterpret_cast<float*>(base + l.dx);
   float* S = reinterpret_cast<float*>(base + l.S);
-  hipError_t e = rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, ilog2(K), G, perm, dsign, xq, dx,
+  hipError_t e = rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, K, G, perm, dsign, xq, dx,
                                       S, reinterpret_cast<uint32_t*>(base + l.sync), 0, s);
   if (e != hipSuccess) return RRS_EHIP;
   const uint8_t* codes = static_cast<const uint8_t*>(wq);
   const float* dw = reinterpret_cast<const float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
-  return hip_status(rrs::launch_gemm(xq, dx, S, M, ilog2(K), N, G, codes, dw, Y, nullptr, 0, 0, 0, 0, s));
+  return hip_status(rrs::launch_gemm(xq, dx, S, M, K, N, G, codes, dw, Y, nullptr, 0, 0, 0, 0, s));
 }
 
 }  // namespace
@@ -185,7 +190,7 @@ RRS_API int rrs_frontend_signed(const void* X_fp16, int M, int K, int G, const i
 RRS_API int rrs_frontend_passes(int M, int K, int flags) {
   if (M < 1 || !valid_K(K)) return RRS_EINVAL;
   if (flags & ~(RRS_FLAG_NO_ROTATE | RRS_FLAG_NO_SMOOTH | RRS_FLAG_TWO_PASS)) return RRS_EINVAL;
-  const int n = rrs::frontend_launches(M, ilog2(K), flags);
+  const int n = rrs::frontend_launches(M, K, flags);
   return n > 0 ? n : RRS_EHIP;
 }
 
@@ -198,12 +203,12 @@ RRS_API int rrs_gemm(const uint8_t* xq, const float* dx, const float* S, int M, 
   if (M == 0) return RRS_OK;
   const uint8_t* codes = static_cast<const uint8_t*>(wq);
   const float* dw = reinterpret_cast<const float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
-  return hip_status(rrs::launch_gemm(xq, dx, S, M, ilog2(K), N, G, codes, dw, Y, nullptr, 0, 0, 0, 0, s));
+  return hip_status(rrs::launch_gemm(xq, dx, S, M, K, N, G, codes, dw, Y, nullptr, 0, 0, 0, 0, s));
 }
 
 RRS_API int rrs_gemm_form(int M, int K, int G) {
   if (M < 1 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;
-  return rrs::gemm_small_applies(M, ilog2(K), G) ? RRS_GEMM_FEW_TOKENS : RRS_GEMM_TILED;
+  return rrs::gemm_small_applies(M, K, G) ? RRS_GEMM_FEW_TOKENS : RRS_GEMM_TILED;
 }
 
 RRS_API int rrs_gemm_partials(const uint8_t* xq, int M, int K, int N, int G, const void* wq, int m0,
@@ -214,7 +219,7 @@ RRS_API int rrs_gemm_partials(const uint8_t* xq, int M, int K, int N, int G, con
   if (!all_a16(xq, wq, P)) return RRS_EINVAL;
   const uint8_t* codes = static_cast<const uint8_t*>(wq);
   const float* dw = reinterpret_cast<const float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
-  return hip_status(rrs::launch_gemm(xq, nullptr, nullptr, M, ilog2(K), N, G, codes, dw, nullptr, P, m0,
+  return hip_status(rrs::launch_gemm(xq, nullptr, nullptr, M, K, N, G, codes, dw, nullptr, P, m0,
                                      m1, n0, n1, s));
 }
 

@@ -36,6 +36,7 @@
 // quantise launch each rotate the rows (X is read twice).
 
 #include "rrs_internal.h"
+#include "rrs_codes.h"
 
 #include <atomic>
 
@@ -43,10 +44,6 @@ namespace rrs {
 namespace {
 
 constexpr int kWave = 64;
-// Adding 1.5 * 2^23 to 0 <= x < 2^22 rounds x to the nearest integer (ties
-// to even, the default mode) and leaves it in the low mantissa bits: for a
-// code magnitude (<= 7) the low 3 bits of the result are the magnitude.
-constexpr float kMagic = 12582912.0f;
 
 enum Mode { kStats = 0, kQuant = 1, kWeight = 2, kColmax = 3 };
 
@@ -81,9 +78,6 @@ struct FeArgs {
 
 __device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
 
-__device__ __forceinline__ float h2f(uint32_t bits16) {
-  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
-}
 
 // Transpose-buffer address of block element f: 8 floats of padding after
 // every 512 make both the phase-1 writes and the phase-2 reads
@@ -256,32 +250,6 @@ constexpr bool mfma13_bijective() {
   return true;
 }
 static_assert(mfma13_bijective(), "lane/register layout of the K = 8192 matrix-core rotation is a bijection");
-
-// Byte 0 (resp. byte 3) of four words, gathered into one word.
-__device__ __forceinline__ uint32_t gather_b0(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
-  const uint32_t t01 = __builtin_amdgcn_perm(x1, x0, 0x0c0c0400u);
-  const uint32_t t23 = __builtin_amdgcn_perm(x3, x2, 0x0c0c0400u);
-  return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t gather_b3(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
-  const uint32_t t01 = __builtin_amdgcn_perm(x1, x0, 0x0c0c0703u);
-  const uint32_t t23 = __builtin_amdgcn_perm(x3, x2, 0x0c0c0703u);
-  return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
-}
-
-// Eight codes -> one packed word. mag[i] holds |code i| in its low 3 bits,
-// sgn[i] the float whose sign is the sign of code i. Layout (8 codes per
-// little-endian word, a_j = code 2j, b_j = code 2j+1): byte j carries |a_j|
-// in bits 0-2, |b_j| in bits 4-6 and sign(a_j) in bit 7; bit 3 of byte
-// (j+1) mod 4 carries sign(b_j). With it, w & 0x87878787 and
-// rotr(w, 4) & 0x87878787 are the a- and b-codes as fp8 e4m3 subnormals.
-__device__ __forceinline__ uint32_t pack8(const uint32_t* mag, const uint32_t* sgn) {
-  const uint32_t ma = gather_b0(mag[0], mag[2], mag[4], mag[6]);
-  const uint32_t mb = gather_b0(mag[1], mag[3], mag[5], mag[7]);
-  const uint32_t sa = gather_b3(sgn[0], sgn[2], sgn[4], sgn[6]);
-  const uint32_t sb = gather_b3(sgn[7], sgn[1], sgn[3], sgn[5]);
-  return ma | (mb << 4) | (sa & 0x80808080u) | ((sb >> 4) & 0x08080808u);
-}
 
 // ---------------------------------------------------------------- row steps
 // The steps below work on one wavefront's block of B = max(K, 4096)
@@ -830,7 +798,7 @@ fused_kernel(FeArgs a) {
 // Stable descending rank: perm[rank(j)] = j with rank(j) = #{i : c_i > c_j}
 // + #{i < j : c_i == c_j} (values compared as non-negative float bits).
 __global__ void __launch_bounds__(1024) rank_kernel(const uint32_t* c, int K, int32_t* perm) {
-  __shared__ uint32_t s_c[1 << kMaxLog2K];
+  __shared__ uint32_t s_c[kMaxKronK];  // K <= kMaxKronK (>= 2^kMaxLog2K)
   for (int k = threadIdx.x; k < K; k += blockDim.x) s_c[k] = c[k];
   __syncthreads();
   for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < K; j += gridDim.x * blockDim.x) {
@@ -957,9 +925,11 @@ bool fused_k(int log2K, const FeArgs& a, hipStream_t s, hipError_t* err) {
 
 }  // namespace
 
-hipError_t launch_frontend(const uint16_t* X, int M, int log2K, int G, const int32_t* perm,
+hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t* perm,
                            const uint32_t* dsign, uint8_t* xq, float* dx, float* S_out, uint32_t* sync,
                            int flags, hipStream_t s) {
+  if (K & (K - 1)) return launch_frontend_kron(X, M, K, G, perm, dsign, xq, dx, S_out, sync, flags, s);
+  const int log2K = __builtin_ctz(static_cast<unsigned>(K));
   FeArgs a{};
   a.dsign = reinterpret_cast<const uint8_t*>(dsign);
   a.src = X;
@@ -982,7 +952,12 @@ hipError_t launch_frontend(const uint16_t* X, int M, int log2K, int G, const int
   return rotate ? dispatch_k<kQuant, true>(log2K, a, s) : dispatch_k<kQuant, false>(log2K, a, s);
 }
 
-int frontend_launches(int M, int log2K, int flags) {
+int frontend_launches(int M, int K, int flags) {
+  if (K & (K - 1)) {
+    int m = 0, ln = 0;
+    return kron_split(K, &m, &ln) ? kron_frontend_launches(flags) : -1;
+  }
+  const int log2K = __builtin_ctz(static_cast<unsigned>(K));
   if (flags & 2) return 1;
   if (flags & 4) return 2;
   const bool rotate = !(flags & 1);
@@ -996,8 +971,10 @@ int frontend_launches(int M, int log2K, int flags) {
   return r > 0 ? 1 : 2;
 }
 
-hipError_t launch_weight_prep(const uint16_t* W, int log2K, int N, const int32_t* perm,
+hipError_t launch_weight_prep(const uint16_t* W, int K, int N, const int32_t* perm,
                               const uint32_t* dsign, uint8_t* wq, float* dw, hipStream_t s) {
+  if (K & (K - 1)) return launch_weight_prep_kron(W, K, N, perm, dsign, wq, dw, s);
+  const int log2K = __builtin_ctz(static_cast<unsigned>(K));
   FeArgs a{};
   a.dsign = reinterpret_cast<const uint8_t*>(dsign);
   a.src = W;
@@ -1011,18 +988,22 @@ hipError_t launch_weight_prep(const uint16_t* W, int log2K, int N, const int32_t
   return dispatch_k<kWeight, true>(log2K, a, s);
 }
 
-hipError_t launch_calibrate(const uint16_t* Xc, int T, int log2K, const uint32_t* dsign, int32_t* perm,
+hipError_t launch_calibrate(const uint16_t* Xc, int T, int K, const uint32_t* dsign, int32_t* perm,
                             uint32_t* ws, hipStream_t s) {
-  const int K = 1 << log2K;
   hipError_t e = launch_zero_u32(ws, static_cast<size_t>(K), s);
   if (e != hipSuccess) return e;
-  FeArgs a{};
-  a.src = Xc;
-  a.rows = T;
-  a.log2G = log2K;
-  a.colmax = ws;
-  a.dsign = reinterpret_cast<const uint8_t*>(dsign);
-  e = dispatch_k<kColmax, true>(log2K, a, s);
+  if (K & (K - 1)) {
+    e = launch_colmax_kron(Xc, T, K, dsign, ws, s);
+  } else {
+    const int log2K = __builtin_ctz(static_cast<unsigned>(K));
+    FeArgs a{};
+    a.src = Xc;
+    a.rows = T;
+    a.log2G = log2K;
+    a.colmax = ws;
+    a.dsign = reinterpret_cast<const uint8_t*>(dsign);
+    e = dispatch_k<kColmax, true>(log2K, a, s);
+  }
   if (e != hipSuccess) return e;
   const int grid = (K + 1023) / 1024;
   hipLaunchKernelGGL(rank_kernel, dim3(grid), dim3(1024), 0, s, ws, K, perm);

@@ -1,0 +1,431 @@
+// Front end of the RRS A4W4 linear for K = m 2^k, m in {12, 20, 28} (no
+// power of two; e.g. K = 14336 = 28 * 512): the rotation is the Kronecker
+// product H_K = H_m (x) H_n, n = 2^k, with H_m from Paley's constructions
+// and Sylvester H_n; element f = i n + j of a row (i < m, j < n).
+//
+// Method as in rrs_frontend.hip (RRS summary page, atlas.scime.ai,
+// "Approach"; RRS rebuttal page, paperhub.cn, "Novelty"; per-token scale of
+// the AGC-OR page, paperpeel.com, Sec. 3.1 and App. B.1; signed rotation,
+// AGC-OR Sec. 4.1 and 4.6). Hadamard matrices of order 12, 20 and 28 are not
+// Sylvester matrices; QuaRot-style rotations use such Kronecker products for
+// hidden sizes like 14336.
+//
+// One workgroup of 256 threads rotates one row at a time in LDS (fp32):
+// 16-byte loads give each thread 8 consecutive elements (f bits 0-2, three
+// butterfly levels in registers), radix-8 passes over LDS do f bits 3..k-1,
+// and H_m mixes the m runs column by column (m^2 compile-time signed adds
+// per column). Then the row is gathered in reordered order through perm,
+// eight positions (one packed word) per thread and step.
+//
+// The group scales need every token first, so the smoothed front end is
+// three launches: stats (each workgroup's group maxima over its rows into
+// its own row of the synchronisation block, no atomics), reduce (S = max
+// over those rows), quantise (rotate again, smooth, per-token scale, pack).
+// Weight preparation and calibration use the same rotation.
+
+#include "rrs_codes.h"
+#include "rrs_internal.h"
+
+namespace rrs {
+namespace {
+
+constexpr int kKT = 256;  // threads per workgroup
+
+enum KronMode { kKStats = 0, kKQuant = 1, kKWeight = 2, kKColmax = 3 };
+
+// ---- Paley Hadamard matrices H_m[i][a], built at compile time -------------
+constexpr int legendre(int a, int q) {
+  a %= q;
+  if (a < 0) a += q;
+  if (a == 0) return 0;
+  int r = 1, b = a, e = (q - 1) / 2;
+  while (e) {
+    if (e & 1) r = r * b % q;
+    b = b * b % q;
+    e >>= 1;
+  }
+  return r == 1 ? 1 : -1;
+}
+
+// m = 12, 20: construction I with q = m - 1 (q = 3 mod 4), H = I + S,
+// S = [[0, 1^T], [-1, Q]], Q[i][j] = chi(j - i). m = 28: construction II with
+// q = 13 (q = 1 mod 4), C = [[0, 1^T], [1, Q]], H = [[C + I, C - I],
+// [C - I, -C - I]].
+constexpr int paley(int m, int i, int a) {
+  if (m == 12 || m == 20) {
+    if (i == a || i == 0) return 1;
+    if (a == 0) return -1;
+    return legendre(a - i, m - 1);
+  }
+  const int br = i / 14, bc = a / 14, r = i % 14, c = a % 14;
+  const int C = (r == c) ? 0 : (r == 0 || c == 0) ? 1 : legendre(c - r, 13);
+  const int e = r == c ? 1 : 0;
+  if (br == 0 && bc == 0) return C + e;
+  if (br == 1 && bc == 1) return -C - e;
+  return C - e;
+}
+
+template <int M>
+struct PaleyNeg {  // bit i of neg[a]: H_M[i][a] = -1
+  uint32_t neg[M];
+  constexpr PaleyNeg() : neg() {
+    for (int a = 0; a < M; ++a) {
+      uint32_t w = 0;
+      for (int i = 0; i < M; ++i)
+        if (paley(M, i, a) < 0) w |= 1u << i;
+      neg[a] = w;
+    }
+  }
+};
+
+constexpr int popcount32(uint32_t x) {
+  int n = 0;
+  for (; x; x &= x - 1) ++n;
+  return n;
+}
+
+// H^T H = M I: any two distinct columns differ in exactly M / 2 signs
+template <int M>
+constexpr bool paley_orthogonal() {
+  constexpr PaleyNeg<M> P{};
+  for (int a = 0; a < M; ++a)
+    for (int b = a + 1; b < M; ++b)
+      if (2 * popcount32(P.neg[a] ^ P.neg[b]) != M) return false;
+  return true;
+}
+static_assert(paley_orthogonal<12>() && paley_orthogonal<20>() && paley_orthogonal<28>(),
+              "Paley matrices are Hadamard");
+
+struct KronArgs {
+  const uint16_t* src;  // X [rows][K], or W [K][ldw] (weights)
+  int rows;
+  int ldw;
+  int log2G;
+  int smooth;
+  int rotate;
+  const int32_t* perm;
+  const uint8_t* dsign;  // K-bit sign mask or nullptr
+  const float* S_in;     // quant: group scales from the reduce pass
+  uint32_t* part;        // stats: [gridDim.x][K/G] partial maxima (float bits)
+  uint8_t* codes;        // [rows][K/2]
+  float* scale;          // [rows]
+  float* S_out;          // [K/G] (quant without smoothing: 1)
+  uint32_t* colmax;      // [K] (calibration)
+};
+
+__device__ __forceinline__ void bfly(float& x, float& y) {
+  const float a = x, b = y;
+  x = a + b;
+  y = a - b;
+}
+
+// Butterflies over R bits of f starting at bit B, in LDS (every run of n = 2^LOG2N).
+template <int K, int B, int R>
+__device__ __forceinline__ void lds_pass(float* row, int tid) {
+  constexpr int P = 1 << R;
+  for (int t = tid; t < (K >> R); t += kKT) {
+    const int lo = t & ((1 << B) - 1), hi = t >> B;
+    const int base = (hi << (B + R)) | lo;
+    float v[P];
+#pragma unroll
+    for (int u = 0; u < P; ++u) v[u] = row[base + (u << B)];
+#pragma unroll
+    for (int h = 1; h < P; h <<= 1)
+#pragma unroll
+      for (int u = 0; u < P; ++u)
+        if (!(u & h)) bfly(v[u], v[u + h]);
+#pragma unroll
+    for (int u = 0; u < P; ++u) row[base + (u << B)] = v[u];
+  }
+  __syncthreads();
+}
+
+template <int K, int B, int LOG2N>
+__device__ __forceinline__ void lds_passes(float* row, int tid) {
+  if constexpr (B < LOG2N) {
+    constexpr int R = (LOG2N - B) < 3 ? (LOG2N - B) : 3;
+    lds_pass<K, B, R>(row, tid);
+    lds_passes<K, B + R, LOG2N>(row, tid);
+  }
+}
+
+// The row (already in LDS, f bits 0-2 transformed) through the rest of H_K.
+template <int M, int LOG2N>
+__device__ __forceinline__ void rotate_rest(float* row, int tid) {
+  constexpr int N = 1 << LOG2N, K = M * N;
+  lds_passes<K, 3, LOG2N>(row, tid);
+  constexpr PaleyNeg<M> P{};
+  for (int j = tid; j < N; j += kKT) {
+    float x[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) x[i] = row[i * N + j];
+#pragma unroll
+    for (int a = 0; a < M; ++a) {
+      float y = 0.f;
+#pragma unroll
+      for (int i = 0; i < M; ++i) y = ((P.neg[a] >> i) & 1u) ? y - x[i] : y + x[i];
+      row[a * N + j] = y;
+    }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ float block_max(float v, float* s_red, int tid) {
+  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d));
+  if ((tid & 63) == 0) s_red[tid >> 6] = v;
+  __syncthreads();
+  float m = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kKT / 64; ++w) m = fmaxf(m, s_red[w]);
+  __syncthreads();
+  return m;
+}
+
+template <int M, int LOG2N, int MODE>
+__global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
+  constexpr int N = 1 << LOG2N, K = M * N;
+  constexpr int W8 = K / 8;                      // packed words (8 positions) per row
+  constexpr int SW = (W8 + kKT - 1) / kKT;       // words per thread
+  __shared__ __attribute__((aligned(16))) float s_row[K];
+  __shared__ float s_grp[K / 32];                // group maxima, or inverse scales
+  __shared__ float s_red[kKT / 64];
+  const int tid = threadIdx.x;
+  const int ngroups = K >> a.log2G;
+
+  if constexpr (MODE == kKStats) {
+    for (int g = tid; g < ngroups; g += kKT) s_grp[g] = 0.f;
+  } else if constexpr (MODE == kKQuant) {
+    for (int g = tid; g < ngroups; g += kKT) s_grp[g] = a.smooth ? 1.f / a.S_in[g] : 1.f;
+    if (!a.smooth && blockIdx.x == 0)
+      for (int g = tid; g < ngroups; g += kKT) a.S_out[g] = 1.f;
+  } else if constexpr (MODE == kKWeight) {
+    for (int g = tid; g < ngroups; g += kKT) s_grp[g] = 1.f;
+  }
+  __syncthreads();
+
+  for (int row = blockIdx.x; row < a.rows; row += gridDim.x) {
+    // ---- load (signs flip fp16 sign bits), f bits 0-2 in registers, to LDS
+    for (int c = tid; c < W8; c += kKT) {
+      uint32_t q[4];
+      if constexpr (MODE == kKWeight) {
+        const uint16_t* p = a.src + static_cast<size_t>(8 * c) * a.ldw + row;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          q[e] = static_cast<uint32_t>(p[(2 * e) * static_cast<size_t>(a.ldw)]) |
+                 (static_cast<uint32_t>(p[(2 * e + 1) * static_cast<size_t>(a.ldw)]) << 16);
+      } else {
+        const uint4 w = *reinterpret_cast<const uint4*>(a.src + static_cast<size_t>(row) * K + 8 * c);
+        q[0] = w.x; q[1] = w.y; q[2] = w.z; q[3] = w.w;
+      }
+      if (a.dsign) {
+        const uint32_t b = a.dsign[c];
+        q[0] ^= ((b & 1u) << 15) | ((b & 2u) << 30);
+        q[1] ^= ((b & 4u) << 13) | ((b & 8u) << 28);
+        q[2] ^= ((b & 16u) << 11) | ((b & 32u) << 26);
+        q[3] ^= ((b & 64u) << 9) | ((b & 128u) << 24);
+      }
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = h2f(q[e] & 0xffffu);
+        v[2 * e + 1] = h2f(q[e] >> 16);
+      }
+      if (a.rotate) {
+#pragma unroll
+        for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (!(u & h)) bfly(v[u], v[u + h]);
+      }
+      *reinterpret_cast<float4*>(s_row + 8 * c) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(s_row + 8 * c + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    __syncthreads();
+    if (a.rotate) rotate_rest<M, LOG2N>(s_row, tid);
+
+    if constexpr (MODE == kKColmax) {
+      // channel |max| of the rotated rows (calibration; before any reorder)
+      for (int k = tid; k < K; k += kKT) {
+        const uint32_t bits = __float_as_uint(fabsf(s_row[k]));
+        if (bits) atomicMax(&a.colmax[k], bits);
+      }
+    } else {
+      // ---- gather eight reordered positions per word
+      float z[SW][8];
+#pragma unroll
+      for (int s = 0; s < SW; ++s) {
+        const int w = tid + s * kKT;
+        if (w < W8) {
+          const int4 p0 = *reinterpret_cast<const int4*>(a.perm + 8 * w);
+          const int4 p1 = *reinterpret_cast<const int4*>(a.perm + 8 * w + 4);
+          const int pp[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) z[s][e] = s_row[pp[e]];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) z[s][e] = 0.f;
+        }
+      }
+      if constexpr (MODE == kKStats) {
+#pragma unroll
+        for (int s = 0; s < SW; ++s) {
+          const int w = tid + s * kKT;
+          if (w < W8) {
+            float m = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(z[s][e]));
+            if (m > 0.f) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[(8 * w) >> a.log2G]), __float_as_uint(m));
+          }
+        }
+      } else {
+        // per-token (or per-output-channel) scale of the smoothed row
+        float r = 0.f;
+#pragma unroll
+        for (int s = 0; s < SW; ++s) {
+          const int w = tid + s * kKT;
+          if (w < W8) {
+            const float inv = s_grp[(8 * w) >> a.log2G];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) r = fmaxf(r, fabsf(z[s][e]) * inv);
+          }
+        }
+        r = block_max(r, s_red, tid);
+        const float k7 = r > 0.f ? 7.f / r : 0.f;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + static_cast<size_t>(row) * (K / 2));
+#pragma unroll
+        for (int s = 0; s < SW; ++s) {
+          const int w = tid + s * kKT;
+          if (w < W8) {
+            const float ks = s_grp[(8 * w) >> a.log2G] * k7;
+            uint32_t mag[8], sgn[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              mag[e] = __float_as_uint(fmaf(fabsf(z[s][e]), ks, kMagic));
+              sgn[e] = __float_as_uint(z[s][e]);
+            }
+            dst[w] = pack8(mag, sgn);
+          }
+        }
+        if (tid == 0) a.scale[row] = r / 7.f;
+      }
+    }
+    __syncthreads();  // the row buffer is reused by the next row
+  }
+
+  if constexpr (MODE == kKStats) {
+    // this workgroup's maxima over its rows into its own partial row
+    for (int g = tid; g < ngroups; g += kKT) a.part[blockIdx.x * ngroups + g] = __float_as_uint(s_grp[g]);
+  }
+}
+
+// S_g = max over the stats pass's partial rows (zero -> 1).
+__global__ void __launch_bounds__(256) kron_reduce_kernel(const uint32_t* part, int nrows, int ngroups,
+                                                          float* S_out) {
+  for (int g = blockIdx.x * blockDim.x + threadIdx.x; g < ngroups; g += gridDim.x * blockDim.x) {
+    uint32_t m = 0u;
+    for (int r = 0; r < nrows; ++r) m = max(m, part[r * ngroups + g]);
+    const float s = __uint_as_float(m);
+    S_out[g] = s > 0.f ? s : 1.f;
+  }
+}
+
+template <int M, int LOG2N, int MODE>
+hipError_t launch_kron_mode(const KronArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((kron_kernel<M, LOG2N, MODE>), dim3(grid), dim3(kKT), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t dispatch_kron(int m, int log2n, const KronArgs& a, int grid, hipStream_t s) {
+#define RRS_KCASE(MM, LN) \
+  if (m == MM && log2n == LN) return launch_kron_mode<MM, LN, MODE>(a, grid, s);
+  RRS_KCASE(12, 6) RRS_KCASE(12, 7) RRS_KCASE(12, 8) RRS_KCASE(12, 9) RRS_KCASE(12, 10)
+  RRS_KCASE(20, 6) RRS_KCASE(20, 7) RRS_KCASE(20, 8) RRS_KCASE(20, 9)
+  RRS_KCASE(28, 6) RRS_KCASE(28, 7) RRS_KCASE(28, 8) RRS_KCASE(28, 9)
+#undef RRS_KCASE
+  return hipErrorInvalidValue;
+}
+
+constexpr int kKronStatsWG = kMaxFusedWG;  // partial rows the synchronisation block holds
+constexpr int kKronRowsWG = 4096;          // grid cap of the row loops
+
+}  // namespace
+
+bool kron_split(int K, int* m, int* log2n) {
+  for (int mm : {12, 20, 28}) {
+    if (K % mm) continue;
+    const int n = K / mm;
+    if (n < 64 || (n & (n - 1))) continue;
+    const int ln = 31 - __builtin_clz(static_cast<unsigned>(n));
+    if (mm * n > kMaxKronK || (mm == 12 && ln > 10) || (mm != 12 && ln > 9)) continue;
+    *m = mm;
+    *log2n = ln;
+    return true;
+  }
+  return false;
+}
+
+int kron_frontend_launches(int flags) { return (flags & 2) ? 1 : 3; }
+
+hipError_t launch_frontend_kron(const uint16_t* X, int M, int K, int G, const int32_t* perm, const uint32_t* dsign,
+                                uint8_t* xq, float* dx, float* S_out, uint32_t* sync, int flags, hipStream_t s) {
+  int m = 0, log2n = 0;
+  if (!kron_split(K, &m, &log2n)) return hipErrorInvalidValue;
+  KronArgs a{};
+  a.src = X;
+  a.rows = M;
+  a.log2G = __builtin_ctz(static_cast<unsigned>(G));
+  a.smooth = (flags & 2) ? 0 : 1;
+  a.rotate = (flags & 1) ? 0 : 1;
+  a.perm = perm;
+  a.dsign = reinterpret_cast<const uint8_t*>(dsign);
+  a.codes = xq;
+  a.scale = dx;
+  a.S_out = S_out;
+  a.S_in = S_out;
+  a.part = sync + kSyncPartials;
+  const int ngroups = K / G;
+  if (a.smooth) {
+    const int gs = M < kKronStatsWG ? M : kKronStatsWG;
+    hipError_t e = dispatch_kron<kKStats>(m, log2n, a, gs, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kron_reduce_kernel, dim3((ngroups + 255) / 256), dim3(256), 0, s, a.part, gs, ngroups, S_out);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return dispatch_kron<kKQuant>(m, log2n, a, M < kKronRowsWG ? M : kKronRowsWG, s);
+}
+
+hipError_t launch_weight_prep_kron(const uint16_t* W, int K, int N, const int32_t* perm, const uint32_t* dsign,
+                                   uint8_t* wq, float* dw, hipStream_t s) {
+  int m = 0, log2n = 0;
+  if (!kron_split(K, &m, &log2n)) return hipErrorInvalidValue;
+  KronArgs a{};
+  a.src = W;
+  a.rows = N;
+  a.ldw = N;
+  a.log2G = __builtin_ctz(static_cast<unsigned>(K & -K));  // one group: no smoothing
+  a.smooth = 0;
+  a.rotate = 1;
+  a.perm = perm;
+  a.dsign = reinterpret_cast<const uint8_t*>(dsign);
+  a.codes = wq;
+  a.scale = dw;
+  return dispatch_kron<kKWeight>(m, log2n, a, N < kKronRowsWG ? N : kKronRowsWG, s);
+}
+
+hipError_t launch_colmax_kron(const uint16_t* Xc, int T, int K, const uint32_t* dsign, uint32_t* colmax,
+                              hipStream_t s) {
+  int m = 0, log2n = 0;
+  if (!kron_split(K, &m, &log2n)) return hipErrorInvalidValue;
+  KronArgs a{};
+  a.src = Xc;
+  a.rows = T;
+  a.log2G = 5;
+  a.rotate = 1;
+  a.dsign = reinterpret_cast<const uint8_t*>(dsign);
+  a.colmax = colmax;
+  return dispatch_kron<kKColmax>(m, log2n, a, T < 1024 ? T : 1024, s);
+}
+
+}  // namespace rrs

@@ -379,7 +379,7 @@ struct GemmCtx {
 // that divides a stage (the rescale then folds into the product loop), else 0
 template <int KM, bool PARTIALS, int SPG>
 __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
-  __shared__ float s_rat[(1 << kMaxLog2K) / kMinG];
+  __shared__ float s_rat[kMaxKronK / kMinG];  // one per group (K <= kMaxKronK)
   __shared__ uint32_t s_bar[kSets];
   __shared__ float s_rs[kTT];       // dx[t] 2^18 / K of the tile's tokens
   __shared__ float s_dw[kTN];       // dw[n] of the tile's output channels
@@ -409,11 +409,16 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
   c.nstage = (a.K + 127) / 128;
   c.log2spg = a.log2G - Mma<KM>::kLog2K;  // MFMA k-steps per group
   c.ngroups = a.K >> a.log2G;
-  // K halves (the partials dump keeps whole groups in one set)
-  const int half = PARTIALS ? c.nstage : (c.nstage + 1) / 2;
+  // K halves (the partials dump keeps whole groups in one set). With two or
+  // more groups the halves meet on a group boundary: half of the groups when
+  // a group spans whole stages (G >= 128; an odd group count, possible for
+  // K = m 2^k, leaves the larger share to set 1), else half of the stages.
+  int half = (c.nstage + 1) / 2;
+  if (c.ngroups > 1 && a.log2G >= 7) half = (c.ngroups / 2) << (a.log2G - 7);
+  if (PARTIALS) half = c.nstage;
   c.st0 = set == 0 ? 0 : half;
   c.st1 = set == 0 ? half : c.nstage;
-  const int nsteps = half;  // both sets step in lockstep
+  const int nsteps = max(half, c.nstage - half);  // both sets step in lockstep
 
   if (!PARTIALS) {
     // s_rat[g] = S[g-1] / S[g]: entering group g rescales the accumulator
@@ -550,7 +555,7 @@ hipError_t launch_km(const GemmArgs& a, bool partials, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_gemm(const uint8_t* xq, const float* dx, const float* S, int M, int log2K,
+hipError_t launch_gemm(const uint8_t* xq, const float* dx, const float* S, int M, int K,
                        int N, int G, const uint8_t* wq, const float* dw, float* Y, int32_t* P,
                        int m0, int m1, int n0, int n1, hipStream_t s) {
   GemmArgs a{};
@@ -563,12 +568,12 @@ hipError_t launch_gemm(const uint8_t* xq, const float* dx, const float* S, int M
   a.P = P;
   a.M = M;
   a.N = N;
-  a.K = 1 << log2K;
+  a.K = K;
   a.log2G = __builtin_ctz(static_cast<unsigned>(G));
   a.pm0 = m0; a.pm1 = m1; a.pn0 = n0; a.pn1 = n1;
   if (M == 0 || N == 0) return hipSuccess;
   const bool partials = P != nullptr;
-  if (!partials && gemm_small_applies(M, log2K, G)) return launch_gemm_small(xq, dx, S, M, log2K, N, G, wq, dw, Y, s);
+  if (!partials && gemm_small_applies(M, K, G)) return launch_gemm_small(xq, dx, S, M, K, N, G, wq, dw, Y, s);
   a.tiles_t = (M + kTT - 1) / kTT;
   a.tiles_n = (N + kTN - 1) / kTN;
   switch (G) {

@@ -192,12 +192,14 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
 
 }  // namespace
 
-// K >= 2048: every wave gets at least one whole round
-bool gemm_small_applies(int M, int log2K, int G) { return M >= 1 && M <= 64 && G >= 64 && log2K >= 11; }
+// K a power of two >= 2048: every wave gets a whole number of rounds
+bool gemm_small_applies(int M, int K, int G) {
+  return M >= 1 && M <= 64 && G >= 64 && K >= 2048 && (K & (K - 1)) == 0;
+}
 
-hipError_t launch_gemm_small(const uint8_t* xq, const float* dx, const float* S, int M, int log2K, int N, int G,
+hipError_t launch_gemm_small(const uint8_t* xq, const float* dx, const float* S, int M, int K, int N, int G,
                              const uint8_t* wq, const float* dw, float* Y, hipStream_t s) {
-  if (!gemm_small_applies(M, log2K, G)) return hipErrorInvalidValue;
+  if (!gemm_small_applies(M, K, G)) return hipErrorInvalidValue;
   SmallArgs a{};
   a.xq = xq;
   a.dx = dx;
@@ -207,7 +209,7 @@ hipError_t launch_gemm_small(const uint8_t* xq, const float* dx, const float* S,
   a.Y = Y;
   a.M = M;
   a.N = N;
-  a.K = 1 << log2K;
+  a.K = K;
   a.log2G = __builtin_ctz(static_cast<unsigned>(G));
   const dim3 grid((N + kTN - 1) / kTN);
   const int rounds = (a.K >> 6) / kWaves / kRound;  // 1, 2, 4 for K = 2048, 4096, 8192

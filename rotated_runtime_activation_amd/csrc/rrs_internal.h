@@ -45,22 +45,22 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 //          bit2 = always use the two launches.
 //   dsign: signed rotation x D H, K-bit mask (bit j set: channel j negated),
 //          or nullptr for the plain rotation.
-hipError_t launch_frontend(const uint16_t* X, int M, int log2K, int G, const int32_t* perm,
+hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t* perm,
                            const uint32_t* dsign, uint8_t* xq, float* dx, float* S_out, uint32_t* sync,
                            int flags, hipStream_t s);
 
 // Launches the front end would use for M rows on the current device (1 or
-// 2), -1 for an unsupported K.
-int frontend_launches(int M, int log2K, int flags);
+// 2; 3 for a Kronecker K with smoothing), -1 for an unsupported K.
+int frontend_launches(int M, int K, int flags);
 
 // Offline weight preparation: W [K, N] row-major fp16 -> wq [N][K/2] + dw [N]
 // (H D W with a sign mask, H W without).
-hipError_t launch_weight_prep(const uint16_t* W, int log2K, int N, const int32_t* perm,
+hipError_t launch_weight_prep(const uint16_t* W, int K, int N, const int32_t* perm,
                               const uint32_t* dsign, uint8_t* wq, float* dw, hipStream_t s);
 
 // Calibration permutation: per-channel |max| of the rotated rows, then a
 // stable descending rank. ws holds K uint32.
-hipError_t launch_calibrate(const uint16_t* Xc, int T, int log2K, const uint32_t* dsign, int32_t* perm,
+hipError_t launch_calibrate(const uint16_t* Xc, int T, int K, const uint32_t* dsign, int32_t* perm,
                             uint32_t* ws, hipStream_t s);
 
 // Zero n uint32 words (fill kernel; used instead of hipMemsetAsync).
@@ -68,14 +68,26 @@ hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
 
 // Grouped INT4 GEMM. Y = (1/K) dx dw sum_g S_g P_g. If P != nullptr the
 // kernel instead writes the int32 partials of the window [m0,m1) x [n0,n1).
-hipError_t launch_gemm(const uint8_t* xq, const float* dx, const float* S, int M, int log2K,
+hipError_t launch_gemm(const uint8_t* xq, const float* dx, const float* S, int M, int K,
                        int N, int G, const uint8_t* wq, const float* dw, float* Y, int32_t* P,
                        int m0, int m1, int n0, int n1, hipStream_t s);
 
 // Few-token form of the same product (Y only): whether it serves (M, G),
 // and its launch. launch_gemm dispatches to it by itself.
-bool gemm_small_applies(int M, int log2K, int G);
-hipError_t launch_gemm_small(const uint8_t* xq, const float* dx, const float* S, int M, int log2K, int N, int G,
+bool gemm_small_applies(int M, int K, int G);
+hipError_t launch_gemm_small(const uint8_t* xq, const float* dx, const float* S, int M, int K, int N, int G,
                              const uint8_t* wq, const float* dw, float* Y, hipStream_t s);
+
+// Kronecker rotation H_m (x) H_n for K = m n, m in {12, 20, 28}, n = 2^k
+// (64 <= n, K <= kMaxKronK; n <= 1024 for m = 12, n <= 512 otherwise).
+constexpr int kMaxKronK = 16384;
+bool kron_split(int K, int* m, int* log2n);
+int kron_frontend_launches(int flags);
+hipError_t launch_frontend_kron(const uint16_t* X, int M, int K, int G, const int32_t* perm, const uint32_t* dsign,
+                                uint8_t* xq, float* dx, float* S_out, uint32_t* sync, int flags, hipStream_t s);
+hipError_t launch_weight_prep_kron(const uint16_t* W, int K, int N, const int32_t* perm, const uint32_t* dsign,
+                                   uint8_t* wq, float* dw, hipStream_t s);
+hipError_t launch_colmax_kron(const uint16_t* Xc, int T, int K, const uint32_t* dsign, uint32_t* colmax,
+                              hipStream_t s);
 
 }  // namespace rrs

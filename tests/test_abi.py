@@ -117,6 +117,20 @@ def test_frontend_passes_rejects():
     assert L.rrs_frontend_passes(16, 4096, rra.RRS_FLAG_TWO_PASS) == 2
 
 
+def test_kron_shapes_accepted_and_rejected():
+    """K = m 2^k with m in {12, 20, 28} is a valid size (Kronecker rotation);
+    other non-powers of two are not, and G must divide K."""
+    for K in (768, 1792, 3072, 10240, 12288, 14336):
+        assert rra.rrs_weight_bytes(K, 8) > 0, K
+        assert rra.rrs_workspace_bytes(4, K, 128) > 0, K
+    for K in (100, 11008, 28 * 32, 24576, 28 * 1024, 12 * 32):
+        assert rra.rrs_weight_bytes(K, 8) == 0, K
+    assert rra.rrs_workspace_bytes(4, 14336, 4096) == 0   # 4096 does not divide 14336
+    assert rra.rrs_gemm_form(8, 14336, 128) == rra.RRS_GEMM_TILED
+    assert rra.rrs_frontend_passes(8, 14336, 0) == 3
+    assert rra.rrs_frontend_passes(8, 14336, rra.RRS_FLAG_NO_SMOOTH) == 1
+
+
 def test_gemm_form():
     """Few-token kernel for M <= 64, G >= 64, K >= 2048; tiled otherwise."""
     assert rra.rrs_gemm_form(64, 8192, 128) == rra.RRS_GEMM_FEW_TOKENS

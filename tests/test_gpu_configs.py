@@ -1,4 +1,4 @@
-"""GPU parity at the five workload sizes, in the launch configuration the
+"""GPU parity at the workload sizes, in the launch configuration the
 benchmark times (rrs_linear on a workspace initialised once). The oracle
 computes every code and scale at full size; outputs of the two widest
 configurations are compared on sampled rows and columns."""
@@ -14,7 +14,8 @@ from tests import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 # name -> (output rows sampled, output columns sampled); None = all
-SAMPLING = {"tiny": None, "o_proj": None, "decode": None, "gate_up": (96, 384), "g_sweep": (96, 384)}
+SAMPLING = {"tiny": None, "o_proj": None, "decode": None, "gate_up": (96, 384), "g_sweep": (96, 384),
+            "down_proj": (96, 384)}
 
 
 @pytest.mark.parametrize("name", list(workloads.WORKLOADS))
@@ -34,7 +35,7 @@ def test_workload(name):
     rra.rrs_calibrate_perm(gu.to_dev(xc), perm_gpu, cws)
     torch.cuda.synchronize()
     pg = perm_gpu.cpu().numpy()
-    c = np.abs(oracle.fwht(xc)).max(axis=0)
+    c = np.abs(oracle.rotate_rows(xc)).max(axis=0)
     diff = pg != perm_ref
     assert np.all(np.abs(c[pg[diff]] - c[perm_ref[diff]]) <= 1e-5 * c[perm_ref[diff]])
     gu.log(f"  perm: {int(diff.sum())} near-tie positions differ")

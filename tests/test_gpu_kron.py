@@ -1,0 +1,142 @@
+"""GPU parity of the Kronecker rotation H_m (x) H_n for K = m 2^k,
+m in {12, 20, 28} (reading R19), against the oracle: front end (with
+ablations and signs), weight preparation, calibration, the grouped GEMM at
+such K (including an odd number of groups, where the two halves of K meet
+off the middle) and the whole layer (run on an MI355X: -m gpu)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rotated_runtime_activation_amd as rra
+import workloads
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(M, K, N=8):
+    x, xc, w = workloads.random_case(M * 131 + K, M, K, N)
+    perm = oracle.calibrate_perm(xc)
+    return x, w, perm
+
+
+# (M, K, G): every m, n from 64 to the largest built, odd group counts
+KRON_FE = [
+    (16, 768, 64), (5, 1280, 256), (33, 1792, 128), (7, 3072, 1024), (40, 5120, 32),
+    (3, 14336, 128), (130, 14336, 2048), (9, 12288, 4096), (2, 10240, 512), (300, 1536, 64),
+]
+
+
+@pytest.mark.parametrize("M,K,G", KRON_FE)
+def test_frontend_kron(M, K, G):
+    gu.log(f"[frontend kron] M={M} K={K} G={G} (m, n) = {oracle.kron_split(K)}: {rra.rrs_frontend_passes(M, K, 0)} launches")
+    x, _, perm = _case(M, K)
+    gu.check_frontend(x, perm, G)
+
+
+@pytest.mark.parametrize("flags", [rra.RRS_FLAG_NO_ROTATE, rra.RRS_FLAG_NO_SMOOTH])
+def test_frontend_kron_ablations(flags):
+    M, K, G = 21, 3584, 128   # 28 * 128
+    gu.log(f"[frontend kron ablation] flags={flags} M={M} K={K} G={G}")
+    x, _, perm = _case(M, K)
+    gu.check_frontend(x, perm, G, flags)
+
+
+@pytest.mark.parametrize("M,K,G", [(11, 1792, 64), (6, 14336, 256)])
+def test_frontend_kron_signed(M, K, G):
+    gu.log(f"[frontend kron signed] M={M} K={K} G={G}")
+    x, _, perm = _case(M, K)
+    bits = np.random.default_rng(K).integers(0, 2**32, size=K // 32, dtype=np.uint64).astype(np.uint32)
+    d = oracle.signs_from_bits(bits, K)
+    fe = oracle.frontend(x, perm, G, d=d)
+    xq = torch.empty(M, K // 2, dtype=torch.uint8, device=gu.DEV)
+    dx = torch.empty(M, dtype=torch.float32, device=gu.DEV)
+    S = torch.empty(K // G, dtype=torch.float32, device=gu.DEV)
+    ws = torch.zeros(rra.rrs_sync_bytes(K, G), dtype=torch.uint8, device=gu.DEV)
+    rra.rrs_frontend_signed(gu.to_dev(x), G, gu.to_dev(perm), gu.to_dev(bits.view(np.int32)), xq, dx, S, ws)
+    torch.cuda.synchronize()
+    gu.compare_codes(oracle.unpack_codes(xq.cpu().numpy()), fe["q"], fe["v"], "kron signed codes")
+    gu.rel_close(dx.cpu().numpy(), fe["dx"], gu.SCALE_TOL, "kron signed dx")
+    gu.rel_close(S.cpu().numpy(), fe["S"], gu.SCALE_TOL, "kron signed S")
+
+
+@pytest.mark.parametrize("K,N", [(768, 40), (1792, 7), (14336, 96), (12288, 33)])
+def test_prepare_weights_kron(K, N):
+    gu.log(f"[weights kron] K={K} N={N}")
+    _, w, perm = _case(4, K, N)
+    wq = gu.prepare_weights(w, perm)
+    torch.cuda.synchronize()
+    codes, dw = rra.weight_views(wq, K, N)
+    ref = oracle.prepare_weights(w, perm)
+    gu.compare_codes(oracle.unpack_codes(codes.cpu().numpy()), ref["qw"], ref["uw"], "kron weight codes")
+    gu.rel_close(dw.cpu().numpy(), ref["dw"], gu.SCALE_TOL, "kron dw")
+
+
+@pytest.mark.parametrize("T,K", [(64, 768), (200, 14336)])
+def test_calibrate_perm_kron(T, K):
+    gu.log(f"[calibrate kron] T={T} K={K}")
+    wl = workloads.Workload(40_000 + K, "cal", T, K, 8, (K,), 8, 20.0, "count", 3, 500.0, 0.02, T)
+    xc = workloads.make_activations(wl, T, wl.seed_base + workloads.ROLE_CALIB)
+    ref = oracle.calibrate_perm(xc)
+    perm = torch.empty(K, dtype=torch.int32, device=gu.DEV)
+    ws = torch.empty(rra.rrs_calibrate_workspace_bytes(K), dtype=torch.uint8, device=gu.DEV)
+    rra.rrs_calibrate_perm(gu.to_dev(xc), perm, ws)
+    torch.cuda.synchronize()
+    got = perm.cpu().numpy()
+    assert np.array_equal(np.sort(got), np.arange(K))
+    c = np.abs(oracle.rotate_rows(xc)).max(axis=0)
+    cs = c[got]
+    assert np.all(cs[:-1] >= cs[1:] * (1 - 1e-5) - 1e-30)
+    same = got == ref
+    if not same.all():
+        idx = np.nonzero(~same)[0]
+        assert np.all(np.abs(c[got[idx]] - c[ref[idx]]) <= 1e-5 * c[ref[idx]])
+
+
+@pytest.mark.parametrize("M,N,K,G", [(33, 130, 14336, 2048), (130, 64, 1792, 128), (5, 260, 12288, 32),
+                                     (64, 40, 14336, 1024)])
+def test_gemm_kron(M, N, K, G):
+    gu.log(f"[gemm kron] M={M} N={N} K={K} G={G} groups={K // G}")
+    g = np.random.default_rng(M + N + K)
+    q = g.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = g.integers(-7, 8, size=(N, K)).astype(np.int8)
+    dx = (g.random(M) + 0.1).astype(np.float32)
+    dw = (g.random(N) * 0.01 + 1e-3).astype(np.float32)
+    S = (g.random(K // G) * 100 + 1).astype(np.float32)
+    xq = gu.to_dev(oracle.pack_codes(q))
+    wq = gu.weight_buffer_from_codes(oracle.pack_codes(qw), dw)
+    ref = oracle.linear_out(q, dx.astype(np.float64), S.astype(np.float64), qw, dw.astype(np.float64), G)
+    Y = torch.empty(M, N, dtype=torch.float32, device=gu.DEV)
+    rra.rrs_gemm(xq, gu.to_dev(dx), gu.to_dev(S), G, wq, Y)
+    P = torch.empty(M, N, K // G, dtype=torch.int32, device=gu.DEV)
+    rra.rrs_gemm_partials(xq, N, G, wq, 0, M, 0, N, P)
+    torch.cuda.synchronize()
+    assert np.array_equal(P.cpu().numpy(), oracle.group_partials(q, qw, G))
+    err = gu.y_error(Y.cpu().numpy(), ref)
+    gu.log(f"  Y err/C = {err:.3e}")
+    assert err <= gu.Y_TOL
+
+
+@pytest.mark.parametrize("M,K,N,G", [(48, 14336, 130, 128), (7, 1280, 64, 64)])
+def test_linear_kron(M, K, N, G):
+    gu.log(f"[linear kron] M={M} K={K} N={N} G={G}")
+    x, w, perm = _case(M, K, N)
+    ref = oracle.rrs_linear(x, w, perm, G)
+    wq = gu.prepare_weights(w, perm)
+    ws = torch.zeros(rra.rrs_workspace_bytes(M, K, G), dtype=torch.uint8, device=gu.DEV)
+    rra.rrs_workspace_init(ws)
+    Y = torch.empty(M, N, dtype=torch.float32, device=gu.DEV)
+    rra.rrs_linear(gu.to_dev(x), G, gu.to_dev(perm), wq, Y, ws)
+    torch.cuda.synchronize()
+    xq, dx, S = rra.workspace_views(ws, M, K, G)
+    q_gpu = oracle.unpack_codes(xq.cpu().numpy())
+    gu.compare_codes(q_gpu, ref["fe"]["q"], ref["fe"]["v"], "kron linear codes")
+    codes, dw = rra.weight_views(wq, K, N)
+    qw_gpu = oracle.unpack_codes(codes.cpu().numpy())
+    gu.compare_codes(qw_gpu, ref["wp"]["qw"], ref["wp"]["uw"], "kron weight codes")
+    Yg = Y.cpu().numpy().astype(np.float64)
+    bound = gu.Y_TOL * ref["C"] + (1 + 1e-6) * gu.flip_bound(
+        q_gpu, ref["fe"]["q"], qw_gpu, ref["wp"]["qw"], ref["fe"]["dx"], ref["fe"]["S"], ref["wp"]["dw"], G)
+    gu.log(f"  Y max err/C = {gu.y_error(Yg, ref):.3e}")
+    assert np.all(np.abs(Yg - ref["Y"]) <= bound)

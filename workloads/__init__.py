@@ -37,7 +37,7 @@ class Workload:
     index: int            # config index, used in the seeds
     name: str
     M: int                # tokens
-    K: int                # input channels (power of two; Hadamard size)
+    K: int                # input channels (Hadamard size: 2^k, or 12, 20, 28 times 2^k)
     N: int                # output channels
     G: Tuple[int, ...]    # smoothing group size(s)
     n_outlier_ch: int     # channel-wise outliers
@@ -61,6 +61,8 @@ WORKLOADS: Dict[str, Workload] = {
     "gate_up": Workload(2, "gate_up", 4096, 4096, 28672, (128,), 16, 20.0, "fraction", 1e-4, 500.0, 0.02, 512),
     "decode": Workload(3, "decode", 64, 8192, 8192, (128,), 32, 20.0, "per_token", 2, 500.0, 0.015, 512),
     "g_sweep": Workload(4, "g_sweep", 4096, 4096, 14336, (32, 128, 512), 16, 20.0, "fraction", 1e-4, 500.0, 0.02, 512),
+    # LLaMA-3-8B down_proj prefill: K = 14336 = 28 * 512 takes the Kronecker rotation
+    "down_proj": Workload(5, "down_proj", 2048, 14336, 4096, (128,), 16, 20.0, "fraction", 1e-4, 500.0, 0.02, 512),
 }
 
 
