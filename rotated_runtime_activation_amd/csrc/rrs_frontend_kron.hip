@@ -10,17 +10,19 @@
 // Sylvester matrices; QuaRot-style rotations use such Kronecker products for
 // hidden sizes like 14336.
 //
-// One workgroup of 256 threads rotates one row at a time in LDS (fp32):
-// 16-byte loads give each thread 8 consecutive elements (f bits 0-2, three
-// butterfly levels in registers), radix-8 passes over LDS do f bits 3..k-1,
-// and H_m mixes the m runs column by column (m^2 compile-time signed adds
-// per column). Then the row is gathered in reordered order through perm,
-// eight positions (one packed word) per thread and step.
+// One workgroup of 512 threads rotates one row at a time in LDS (loading
+// its next row meanwhile): H_m runs first on the matrix cores
+// (fp16 32 x 32 x 16 MFMA against +-1 H_m^T: exact products, fp32 sums),
+// then H_n runs as radix-8 butterfly passes over the fp32 row. The two
+// factors commute (H_m (x) H_n = (H_m (x) I)(I (x) H_n)). Then the row is
+// gathered in reordered order through perm, eight positions (one packed
+// word) per thread and step.
 //
 // The group scales need every token first, so the smoothed front end is
-// three launches: stats (each workgroup's group maxima over its rows into
-// its own row of the synchronisation block, no atomics), reduce (S = max
-// over those rows), quantise (rotate again, smooth, per-token scale, pack).
+// three launches: stats (each row's group maxima into its own row of a
+// scratch area, the codes buffer, which the quantise pass overwrites later;
+// no atomics), reduce (S = max over those rows), quantise (rotate again,
+// smooth, per-token scale, pack).
 // Weight preparation and calibration use the same rotation.
 
 #include "rrs_codes.h"
@@ -29,7 +31,7 @@
 namespace rrs {
 namespace {
 
-constexpr int kKT = 256;  // threads per workgroup
+constexpr int kKT = 512;  // threads per workgroup
 
 enum KronMode { kKStats = 0, kKQuant = 1, kKWeight = 2, kKColmax = 3 };
 
@@ -119,6 +121,13 @@ __device__ __forceinline__ void bfly(float& x, float& y) {
   y = a - b;
 }
 
+// Row buffer index of element f: one float of padding after every 64, so
+// that the strided accesses of the passes, the matrix-core stores and the
+// gather spread over the LDS banks.
+__device__ __forceinline__ constexpr int rpad(int f) { return f + (f >> 6); }
+template <int K>
+constexpr int kRowFloats = K + K / 64;
+
 // Butterflies over R bits of f starting at bit B, in LDS (every run of n = 2^LOG2N).
 template <int K, int B, int R>
 __device__ __forceinline__ void lds_pass(float* row, int tid) {
@@ -128,14 +137,14 @@ __device__ __forceinline__ void lds_pass(float* row, int tid) {
     const int base = (hi << (B + R)) | lo;
     float v[P];
 #pragma unroll
-    for (int u = 0; u < P; ++u) v[u] = row[base + (u << B)];
+    for (int u = 0; u < P; ++u) v[u] = row[rpad(base + (u << B))];
 #pragma unroll
     for (int h = 1; h < P; h <<= 1)
 #pragma unroll
       for (int u = 0; u < P; ++u)
         if (!(u & h)) bfly(v[u], v[u + h]);
 #pragma unroll
-    for (int u = 0; u < P; ++u) row[base + (u << B)] = v[u];
+    for (int u = 0; u < P; ++u) row[rpad(base + (u << B))] = v[u];
   }
   __syncthreads();
 }
@@ -149,25 +158,74 @@ __device__ __forceinline__ void lds_passes(float* row, int tid) {
   }
 }
 
-// The row (already in LDS, f bits 0-2 transformed) through the rest of H_K.
-template <int M, int LOG2N>
-__device__ __forceinline__ void rotate_rest(float* row, int tid) {
-  constexpr int N = 1 << LOG2N, K = M * N;
-  lds_passes<K, 3, LOG2N>(row, tid);
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// H_m on the matrix cores, on the raw fp16 row: Z1[a][j] = sum_i H_m[i][a]
+// x[i][j] is a 32 x 32 x MP product per tile of 32 columns j, A = H_m^T
+// (+-1, zero-padded to MP = 16 or 32 rows and columns), B = the row read
+// at stride n from the fp16 buffer (8 halves of consecutive i per lane,
+// consecutive lanes on consecutive j). Products are exact, sums fp32. Rows
+// a >= m of a tile are padding and not written.
+template <int M>
+struct HmFrag {
+  static constexpr int MP = M <= 16 ? 16 : 32;
+  static constexpr int KS = MP / 16;  // 16-deep k-steps
+  v4u a[KS];
+};
+
+template <int M>
+__device__ __forceinline__ HmFrag<M> hm_frags(int lane) {
   constexpr PaleyNeg<M> P{};
-  for (int j = tid; j < N; j += kKT) {
-    float x[M];
+  HmFrag<M> h;
+  const int ar = lane & 31;
 #pragma unroll
-    for (int i = 0; i < M; ++i) x[i] = row[i * N + j];
+  for (int ks = 0; ks < HmFrag<M>::KS; ++ks) {
 #pragma unroll
-    for (int a = 0; a < M; ++a) {
-      float y = 0.f;
+    for (int d = 0; d < 4; ++d) {
+      uint32_t w = 0;
 #pragma unroll
-      for (int i = 0; i < M; ++i) y = ((P.neg[a] >> i) & 1u) ? y - x[i] : y + x[i];
-      row[a * N + j] = y;
+      for (int t = 0; t < 2; ++t) {
+        const int k = 16 * ks + 8 * (lane >> 5) + 2 * d + t;  // i
+        uint32_t v = 0;
+        if (k < M && ar < M) v = ((P.neg[ar] >> k) & 1u) ? 0xbc00u : 0x3c00u;
+        w |= v << (16 * t);
+      }
+      h.a[ks][d] = w;
     }
   }
-  __syncthreads();
+  return h;
+}
+
+template <int M, int LOG2N>
+__device__ __forceinline__ void hm_mfma(const uint16_t* x16, float* row, const HmFrag<M>& h, int tid) {
+  constexpr int N = 1 << LOG2N;
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int jt = wave; jt < N / 32; jt += kKT / 64) {
+    const int j = jt * 32 + (lane & 31);
+    v16f acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < HmFrag<M>::KS; ++ks) {
+      // B[i][j] for i = i0 .. i0 + 7: halves n apart in the natural row
+      // (consecutive lanes read consecutive j); rows i >= m read as 0
+      const int i0 = 16 * ks + 8 * (lane >> 5);
+      uint32_t hv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = (i0 + e < M) ? x16[(i0 + e) * N + j] : 0u;
+      const v4u b = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16)};
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, h.a[ks]), __builtin_bit_cast(v8h, b), acc,
+                                                   0, 0, 0);
+    }
+    // register r of lane l: row a = 8 (r / 4) + 4 (l / 32) + r % 4, column j
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ar = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (ar < M) row[rpad(ar * N + j)] = acc[r];
+    }
+  }
 }
 
 __device__ __forceinline__ float block_max(float v, float* s_red, int tid) {
@@ -181,16 +239,35 @@ __device__ __forceinline__ float block_max(float v, float* s_red, int tid) {
   return m;
 }
 
+// 16-byte chunk c (elements 8c .. 8c+7) of row `row`, fp16 bits
+template <int MODE, int K>
+__device__ __forceinline__ uint4 load_chunk(const KronArgs& a, int row, int c) {
+  if constexpr (MODE == kKWeight) {
+    // column `row` of W [K][ldw], channels 8c .. 8c+7
+    const uint16_t* p = a.src + static_cast<size_t>(8 * c) * a.ldw + row;
+    uint32_t q[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      q[e] = static_cast<uint32_t>(p[(2 * e) * static_cast<size_t>(a.ldw)]) |
+             (static_cast<uint32_t>(p[(2 * e + 1) * static_cast<size_t>(a.ldw)]) << 16);
+    return make_uint4(q[0], q[1], q[2], q[3]);
+  } else {
+    return *reinterpret_cast<const uint4*>(a.src + static_cast<size_t>(row) * K + 8 * c);
+  }
+}
+
 template <int M, int LOG2N, int MODE>
 __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
   constexpr int N = 1 << LOG2N, K = M * N;
-  constexpr int W8 = K / 8;                      // packed words (8 positions) per row
-  constexpr int SW = (W8 + kKT - 1) / kKT;       // words per thread
-  __shared__ __attribute__((aligned(16))) float s_row[K];
+  constexpr int W8 = K / 8;                      // 16-byte chunks = packed words (8 positions) per row
+  constexpr int SW = (W8 + kKT - 1) / kKT;       // chunks / words per thread
+  __shared__ __attribute__((aligned(16))) float s_row[kRowFloats<K>];
+  __shared__ __attribute__((aligned(16))) uint16_t s_x16[K];  // the fp16 row (matrix-core input)
   __shared__ float s_grp[K / 32];                // group maxima, or inverse scales
   __shared__ float s_red[kKT / 64];
   const int tid = threadIdx.x;
   const int ngroups = K >> a.log2G;
+  const HmFrag<M> hf = hm_frags<M>(tid & 63);
 
   if constexpr (MODE == kKStats) {
     for (int g = tid; g < ngroups; g += kKT) s_grp[g] = 0.f;
@@ -201,52 +278,78 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
   } else if constexpr (MODE == kKWeight) {
     for (int g = tid; g < ngroups; g += kKT) s_grp[g] = 1.f;
   }
+
+  // the permutation is the same for every row: its row buffer indices stay
+  // in registers; sign-mask bytes likewise
+  int pp[SW][8];
+  uint32_t sb[SW];
+#pragma unroll
+  for (int s = 0; s < SW; ++s) {
+    const int w = tid + s * kKT;
+    sb[s] = (a.dsign && w < W8) ? static_cast<uint32_t>(a.dsign[w]) : 0u;
+    if constexpr (MODE != kKColmax) {
+      if (w < W8) {
+        const int4 p0 = *reinterpret_cast<const int4*>(a.perm + 8 * w);
+        const int4 p1 = *reinterpret_cast<const int4*>(a.perm + 8 * w + 4);
+        pp[s][0] = rpad(p0.x); pp[s][1] = rpad(p0.y); pp[s][2] = rpad(p0.z); pp[s][3] = rpad(p0.w);
+        pp[s][4] = rpad(p1.x); pp[s][5] = rpad(p1.y); pp[s][6] = rpad(p1.z); pp[s][7] = rpad(p1.w);
+      }
+    }
+  }
   __syncthreads();
 
+  // rows blockIdx.x, + gridDim.x, ...: the next row's chunks load while this
+  // one is processed
+  uint4 nxt[SW];
+#pragma unroll
+  for (int s = 0; s < SW; ++s) {
+    const int c = tid + s * kKT;
+    if (c < W8 && blockIdx.x < a.rows) nxt[s] = load_chunk<MODE, K>(a, blockIdx.x, c);
+  }
   for (int row = blockIdx.x; row < a.rows; row += gridDim.x) {
-    // ---- load (signs flip fp16 sign bits), f bits 0-2 in registers, to LDS
-    for (int c = tid; c < W8; c += kKT) {
-      uint32_t q[4];
-      if constexpr (MODE == kKWeight) {
-        const uint16_t* p = a.src + static_cast<size_t>(8 * c) * a.ldw + row;
+    uint4 cur[SW];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          q[e] = static_cast<uint32_t>(p[(2 * e) * static_cast<size_t>(a.ldw)]) |
-                 (static_cast<uint32_t>(p[(2 * e + 1) * static_cast<size_t>(a.ldw)]) << 16);
-      } else {
-        const uint4 w = *reinterpret_cast<const uint4*>(a.src + static_cast<size_t>(row) * K + 8 * c);
-        q[0] = w.x; q[1] = w.y; q[2] = w.z; q[3] = w.w;
-      }
-      if (a.dsign) {
-        const uint32_t b = a.dsign[c];
-        q[0] ^= ((b & 1u) << 15) | ((b & 2u) << 30);
-        q[1] ^= ((b & 4u) << 13) | ((b & 8u) << 28);
-        q[2] ^= ((b & 16u) << 11) | ((b & 32u) << 26);
-        q[3] ^= ((b & 64u) << 9) | ((b & 128u) << 24);
-      }
-      float v[8];
+    for (int s = 0; s < SW; ++s) cur[s] = nxt[s];
+    const int nrow = row + gridDim.x;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[2 * e] = h2f(q[e] & 0xffffu);
-        v[2 * e + 1] = h2f(q[e] >> 16);
-      }
-      if (a.rotate) {
+    for (int s = 0; s < SW; ++s) {
+      const int c = tid + s * kKT;
+      if (c < W8 && nrow < a.rows) nxt[s] = load_chunk<MODE, K>(a, nrow, c);
+    }
+    // ---- signs (fp16 sign bits), then the row into LDS
 #pragma unroll
-        for (int h = 1; h < 8; h <<= 1)
+    for (int s = 0; s < SW; ++s) {
+      const int c = tid + s * kKT;
+      if (c < W8) {
+        uint4 q = cur[s];
+        const uint32_t b = sb[s];
+        q.x ^= ((b & 1u) << 15) | ((b & 2u) << 30);
+        q.y ^= ((b & 4u) << 13) | ((b & 8u) << 28);
+        q.z ^= ((b & 16u) << 11) | ((b & 32u) << 26);
+        q.w ^= ((b & 64u) << 9) | ((b & 128u) << 24);
+        if (a.rotate) {
+          *reinterpret_cast<uint4*>(s_x16 + 8 * c) = q;
+        } else {
+          const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (!(u & h)) bfly(v[u], v[u + h]);
+          for (int e = 0; e < 4; ++e) {
+            s_row[rpad(8 * c + 2 * e)] = h2f(qq[e] & 0xffffu);
+            s_row[rpad(8 * c + 2 * e + 1)] = h2f(qq[e] >> 16);
+          }
+        }
       }
-      *reinterpret_cast<float4*>(s_row + 8 * c) = make_float4(v[0], v[1], v[2], v[3]);
-      *reinterpret_cast<float4*>(s_row + 8 * c + 4) = make_float4(v[4], v[5], v[6], v[7]);
     }
     __syncthreads();
-    if (a.rotate) rotate_rest<M, LOG2N>(s_row, tid);
+    if (a.rotate) {
+      hm_mfma<M, LOG2N>(s_x16, s_row, hf, tid);  // H_m across the runs
+      __syncthreads();
+      lds_passes<K, 0, LOG2N>(s_row, tid);       // H_n along each run
+    }
 
     if constexpr (MODE == kKColmax) {
       // channel |max| of the rotated rows (calibration; before any reorder)
       for (int k = tid; k < K; k += kKT) {
-        const uint32_t bits = __float_as_uint(fabsf(s_row[k]));
+        const uint32_t bits = __float_as_uint(fabsf(s_row[rpad(k)]));
         if (bits) atomicMax(&a.colmax[k], bits);
       }
     } else {
@@ -255,16 +358,8 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
 #pragma unroll
       for (int s = 0; s < SW; ++s) {
         const int w = tid + s * kKT;
-        if (w < W8) {
-          const int4 p0 = *reinterpret_cast<const int4*>(a.perm + 8 * w);
-          const int4 p1 = *reinterpret_cast<const int4*>(a.perm + 8 * w + 4);
-          const int pp[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) z[s][e] = s_row[pp[e]];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) z[s][e] = 0.f;
-        }
+        for (int e = 0; e < 8; ++e) z[s][e] = (w < W8) ? s_row[pp[s][e]] : 0.f;
       }
       if constexpr (MODE == kKStats) {
 #pragma unroll
@@ -309,7 +404,7 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
         if (tid == 0) a.scale[row] = r / 7.f;
       }
     }
-    __syncthreads();  // the row buffer is reused by the next row
+    __syncthreads();  // the row buffers are reused by the next row
   }
 
   if constexpr (MODE == kKStats) {
@@ -318,14 +413,21 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
   }
 }
 
-// S_g = max over the stats pass's partial rows (zero -> 1).
+// S_g = max over the stats pass's partial rows (zero -> 1): one workgroup
+// per group, threads over rows.
 __global__ void __launch_bounds__(256) kron_reduce_kernel(const uint32_t* part, int nrows, int ngroups,
                                                           float* S_out) {
-  for (int g = blockIdx.x * blockDim.x + threadIdx.x; g < ngroups; g += gridDim.x * blockDim.x) {
-    uint32_t m = 0u;
-    for (int r = 0; r < nrows; ++r) m = max(m, part[r * ngroups + g]);
-    const float s = __uint_as_float(m);
-    S_out[g] = s > 0.f ? s : 1.f;
+  __shared__ uint32_t s_m[4];
+  const int g = blockIdx.x, tid = threadIdx.x;
+  uint32_t m = 0u;
+  for (int r = tid; r < nrows; r += 256) m = max(m, part[static_cast<size_t>(r) * ngroups + g]);
+  for (int d = 32; d >= 1; d >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), d)));
+  if ((tid & 63) == 0) s_m[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) {
+    m = max(max(s_m[0], s_m[1]), max(s_m[2], s_m[3]));
+    const float v = __uint_as_float(m);
+    S_out[g] = v > 0.f ? v : 1.f;
   }
 }
 
@@ -346,8 +448,7 @@ hipError_t dispatch_kron(int m, int log2n, const KronArgs& a, int grid, hipStrea
   return hipErrorInvalidValue;
 }
 
-constexpr int kKronStatsWG = kMaxFusedWG;  // partial rows the synchronisation block holds
-constexpr int kKronRowsWG = 4096;          // grid cap of the row loops
+constexpr int kKronRowsWG = 256;  // workgroups of the row loops (one per CU; each prefetches its next row)
 
 }  // namespace
 
@@ -368,7 +469,8 @@ bool kron_split(int K, int* m, int* log2n) {
 int kron_frontend_launches(int flags) { return (flags & 2) ? 1 : 3; }
 
 hipError_t launch_frontend_kron(const uint16_t* X, int M, int K, int G, const int32_t* perm, const uint32_t* dsign,
-                                uint8_t* xq, float* dx, float* S_out, uint32_t* sync, int flags, hipStream_t s) {
+                                uint8_t* xq, float* dx, float* S_out, uint32_t* /*sync: unused*/, int flags,
+                                hipStream_t s) {
   int m = 0, log2n = 0;
   if (!kron_split(K, &m, &log2n)) return hipErrorInvalidValue;
   KronArgs a{};
@@ -383,13 +485,16 @@ hipError_t launch_frontend_kron(const uint16_t* X, int M, int K, int G, const in
   a.scale = dx;
   a.S_out = S_out;
   a.S_in = S_out;
-  a.part = sync + kSyncPartials;
+  // the stats pass's partial rows (one per workgroup, K/G words; at most M
+  // of them) fit the codes buffer (K/2 bytes per token, G >= 32), which the
+  // quantise pass overwrites afterwards
+  a.part = reinterpret_cast<uint32_t*>(xq);
   const int ngroups = K / G;
   if (a.smooth) {
-    const int gs = M < kKronStatsWG ? M : kKronStatsWG;
+    const int gs = M < kKronRowsWG ? M : kKronRowsWG;
     hipError_t e = dispatch_kron<kKStats>(m, log2n, a, gs, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kron_reduce_kernel, dim3((ngroups + 255) / 256), dim3(256), 0, s, a.part, gs, ngroups, S_out);
+    hipLaunchKernelGGL(kron_reduce_kernel, dim3(ngroups), dim3(256), 0, s, a.part, gs, ngroups, S_out);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
