@@ -93,19 +93,20 @@ const char* rrs_version(void);
 size_t rrs_weight_bytes(int K, int N);
 
 /* Bytes of the workspace that rrs_linear needs for M tokens: a
- * synchronisation block (rrs_sync_bytes(K, G): control words, arrival
- * flags in their own 128-byte lines and a row of K/G group maxima for each
- * of up to 512 workgroups), then xq [M][K/2], dx [M] and S [K/G], each 256-byte aligned.
+ * synchronisation block (rrs_sync_bytes(K, G): control words, a reserved
+ * area, and a row of K/G 64-bit group-maximum words, tagged with the call
+ * count, for each of up to 512 workgroups), then xq [M][K/2], dx [M] and
+ * S [K/G], each 256-byte aligned.
  * rrs_frontend needs only the synchronisation block. Returns 0 for an
  * invalid shape. */
 size_t rrs_workspace_bytes(int M, int K, int G);
 size_t rrs_sync_bytes(int K, int G);
 
-/* Initialise the synchronisation block at the start of `ws` (zeroes its
- * first 69632 bytes, or all of `ws` if smaller, with a fill kernel on `s`; no
- * hipMemset, so it is safe under stream capture). Call once for a fresh
- * workspace before its first use; every later call leaves the block ready
- * for the next one (the one-launch front end counts calls in it instead of
+/* Initialise a workspace: zeroes all `ws_bytes` bytes (the synchronisation
+ * block at its start among them) with a fill kernel on `s` (no hipMemset,
+ * so it is safe under stream capture). Call once for a fresh workspace
+ * before its first use; every later call leaves the block ready for the
+ * next one (the one-launch front end counts calls in it instead of
  * clearing it). Two calls that share one workspace must not overlap in
  * time. */
 int rrs_workspace_init(void* ws, size_t ws_bytes, hipStream_t s);

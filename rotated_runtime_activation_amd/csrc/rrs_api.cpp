@@ -29,12 +29,9 @@ bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 template <typename... P>
 bool all_a16(const P*... p) { return (a16(p) && ...); }
 
-// Words of the synchronisation block that must start at zero (all control
-// words, the two-launch maxima and the one-launch flags).
-constexpr size_t kInitSyncBytes = sizeof(uint32_t) * rrs::kSyncPartials;
-
 size_t sync_bytes(int K, int G) {
-  return align256(sizeof(uint32_t) * (rrs::kSyncPartials + static_cast<size_t>(rrs::kMaxFusedWG) * (K / G)));
+  // 64-bit tagged group maxima per workgroup of the one-launch front end
+  return align256(sizeof(uint32_t) * (rrs::kSyncPartials + 2 * static_cast<size_t>(rrs::kMaxFusedWG) * (K / G)));
 }
 
 struct WsLayout {
@@ -89,7 +86,9 @@ RRS_API size_t rrs_calibrate_workspace_bytes(int K) {
 
 RRS_API int rrs_workspace_init(void* ws, size_t ws_bytes, hipStream_t s) {
   if (ws == nullptr || ws_bytes < 256 || ws_bytes % 4 || !a16(ws)) return RRS_EINVAL;
-  const size_t n = (ws_bytes < kInitSyncBytes ? ws_bytes : kInitSyncBytes) / sizeof(uint32_t);
+  // all of it: the tagged maxima of the one-launch front end must not hold
+  // a stale tag from memory that was never initialised
+  const size_t n = ws_bytes / sizeof(uint32_t);
   return hip_status(rrs::launch_zero_u32(static_cast<uint32_t*>(ws), n, s));
 }
 

@@ -726,60 +726,64 @@ fused_kernel(FeArgs a) {
   }
   __syncthreads();
 
-  // ---- publish this workgroup's maxima, wait for everyone's ---------------
+  // ---- publish this workgroup's maxima, read everyone's ---------------------
+  // Each workgroup stores its group maxima in its own row of 64-bit words
+  // tagged with this call's epoch in the high half (single-copy atomic
+  // stores); the readers poll the rows themselves until every word carries
+  // the epoch, so the data and the arrival need one round trip, not two.
   // Every cross-workgroup word is written and read with relaxed agent-scope
   // atomics, which go to the device-coherent level directly (no L2
   // write-back or invalidate, which acquire/release would add per access).
-  // The order "maxima before flag" comes from waiting for the maxima stores
-  // to complete before the flag store is issued; on the reading side the
-  // maxima are loaded only after every flag has been seen.
-  uint32_t* part = a.sync + kSyncPartials;
-  uint32_t* flags = a.sync + kSyncFlags;
+  uint64_t* part = reinterpret_cast<uint64_t*>(a.sync + kSyncPartials);
+  const uint64_t tag = static_cast<uint64_t>(epoch) << 32;
   for (int g = tid; g < ngroups; g += C::kThreads)
-    __hip_atomic_store(&part[blockIdx.x * ngroups + g], __float_as_uint(s_grp[g]), __ATOMIC_RELAXED,
+    __hip_atomic_store(&part[blockIdx.x * ngroups + g], tag | __float_as_uint(s_grp[g]), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's stores are complete
   __syncthreads();
-  if (tid == 0) __hip_atomic_store(&flags[blockIdx.x * kFlagStride], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (int i = tid; i < nwg; i += C::kThreads) {
-    uint32_t it = 0;
-    while (__hip_atomic_load(&flags[i * kFlagStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
-      if (++it == kSpinLimit) {
-        atomicOr(&a.sync[kSyncError], 1u);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-  }
   for (int g = tid; g < ngroups; g += C::kThreads) s_grp[g] = 0.f;
   __syncthreads();
-  if (blockIdx.x == 0 && tid == 0)
-    __hip_atomic_store(&a.sync[kSyncEpoch], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // ---- S_g = max over the workgroups' rows (loads issued in batches) -------
+  // ---- S_g = max over the workgroups' rows (all loads of a poll in flight) --
   {
     constexpr int kBatch = 16;
     const int n = nwg * ngroups;
     const bool same_group = C::kThreads % ngroups == 0;  // thread always on group tid % ngroups
     uint32_t mx = 0u;
     for (int base = tid; base < n; base += C::kThreads * kBatch) {
-      uint32_t b[kBatch];
+      uint64_t b[kBatch];
+      uint32_t it = 0;
+      for (;;) {
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        const int idx = base + k * C::kThreads;
-        b[k] = idx < n ? __hip_atomic_load(&part[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+        for (int k = 0; k < kBatch; ++k) {
+          const int idx = base + k * C::kThreads;
+          b[k] = idx < n ? __hip_atomic_load(&part[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag;
+        }
+        bool all = true;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) all &= (b[k] >> 32) == epoch;
+        if (all) break;
+        if (++it == kSpinLimit) {
+          atomicOr(&a.sync[kSyncError], 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
       }
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
+        const uint32_t v = static_cast<uint32_t>(b[k]);
         if (same_group) {
-          mx = max(mx, b[k]);
-        } else if (b[k]) {
-          atomicMax(reinterpret_cast<uint32_t*>(&s_grp[(base + k * C::kThreads) % ngroups]), b[k]);
+          mx = max(mx, v);
+        } else if (v) {
+          atomicMax(reinterpret_cast<uint32_t*>(&s_grp[(base + k * C::kThreads) % ngroups]), v);
         }
       }
     }
     if (same_group && mx) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[tid % ngroups]), mx);
   }
+  __syncthreads();
+  // every workgroup has read the old epoch (it tagged its row with old + 1)
+  if (blockIdx.x == 0 && tid == 0)
+    __hip_atomic_store(&a.sync[kSyncEpoch], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   for (int g = tid; g < ngroups; g += C::kThreads) {
     float sg = s_grp[g];

@@ -49,12 +49,12 @@ def test_size_queries():
     assert rra.rrs_weight_bytes(256, 0) == 0
     # workspace: sync block + xq + dx + S
     sync = rra.rrs_sync_bytes(4096, 128)
-    # 17408 words (control, two-launch maxima, 512 arrival flags 128 bytes
-    # apart) + a row of K/G maxima for each of 512 workgroups
-    assert sync == 4 * (17408 + 512 * 32) and rra.rrs_sync_bytes(8192, 32) == 4 * (17408 + 512 * 256)
-    assert rra.rrs_sync_bytes(64, 32) == 4 * (17408 + 512 * 2)
+    # 17408 words (control, two-launch maxima, a reserved area) + a row of
+    # K/G 64-bit tagged maxima for each of 512 workgroups
+    assert sync == 4 * (17408 + 2 * 512 * 32) and rra.rrs_sync_bytes(8192, 32) == 4 * (17408 + 2 * 512 * 256)
+    assert rra.rrs_sync_bytes(64, 32) == 4 * (17408 + 2 * 512 * 2)
     assert rra.rrs_workspace_bytes(2048, 4096, 128) == sync + 2048 * 2048 + 2048 * 4 + 256
-    assert rra.rrs_workspace_bytes(1, 64, 32) == 4 * (17408 + 1024) + 256 + 256 + 256
+    assert rra.rrs_workspace_bytes(1, 64, 32) == 4 * (17408 + 2048) + 256 + 256 + 256
     assert rra.rrs_workspace_bytes(16, 256, 16) == 0   # G < 32
     assert rra.rrs_workspace_bytes(16, 256, 512) == 0  # G > K
     assert rra.rrs_workspace_bytes(16, 256, 96) == 0   # G not a power of two
