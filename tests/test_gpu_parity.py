@@ -213,6 +213,32 @@ def test_determinism():
     assert torch.equal(xq1, rra.workspace_views(ws, M, K, G)[0])
 
 
+def test_frontend_workspace_reuse_across_sizes():
+    """One synchronisation block serves calls of different token counts in a
+    row (the one-launch form's grid changes size between calls: rows of
+    workgroups a smaller call does not use keep older epoch tags and must
+    not be read), on both forms and after a smoothing-free call."""
+    K, G = 4096, 128
+    ws = torch.zeros(rra.rrs_sync_bytes(K, G), dtype=torch.uint8, device=gu.DEV)
+    rra.rrs_workspace_init(ws)
+    calls = 0
+    for M, flags in [(2048, 0), (64, 0), (1000, 0), (300, rra.RRS_FLAG_TWO_PASS), (2048, 0),
+                     (5, rra.RRS_FLAG_NO_SMOOTH), (777, 0)]:
+        gu.log(f"[workspace reuse] M={M} flags={flags}")
+        x, _, perm = _case(M, K)
+        fe = oracle.frontend(x, perm, G, smooth=not (flags & 2))
+        xq = torch.empty(M, K // 2, dtype=torch.uint8, device=gu.DEV)
+        dx = torch.empty(M, dtype=torch.float32, device=gu.DEV)
+        S = torch.empty(K // G, dtype=torch.float32, device=gu.DEV)
+        rra.rrs_frontend(gu.to_dev(x), G, gu.to_dev(perm), xq, dx, S, ws, flags)
+        torch.cuda.synchronize()
+        if not flags and rra.rrs_frontend_passes(M, K, 0) == 1:
+            calls += 1
+        gu.check_sync_block(ws, K, G, calls)
+        gu.compare_codes(oracle.unpack_codes(xq.cpu().numpy()), fe["q"], fe["v"], "reuse codes")
+        gu.rel_close(S.cpu().numpy(), fe["S"], gu.SCALE_TOL, "reuse S")
+
+
 @pytest.mark.parametrize("T,K", [(128, 256), (512, 4096), (100, 8192), (3, 64)])
 def test_calibrate_perm(T, K):
     gu.log(f"[calibrate] T={T} K={K}")
