@@ -200,13 +200,29 @@ struct GemmCtx {
 
   __device__ GemmCtx(const GemmArgs& args, const float* s_rat) : a(args), rat(s_rat) {}
 
-  // DMA block d of stage st into ring slot `base`
+  // DMA block d of stage st into ring slot `base`. The load is written in
+  // assembly so that the compiler does not track it: its wait insertion
+  // loses the ring slots' alias scopes across the loop's back edge and then
+  // drains every load in flight (the next stage's included) before a
+  // stage's first fragment read, which leaves one stage of prefetch instead
+  // of two. The kernel orders these loads itself: each wave waits for its
+  // own loads of a stage, then the set barrier, before any fragment read of
+  // it. The instruction writes no register (its data goes to LDS at M0 plus
+  // 16 bytes per lane), so nothing the compiler allocates is overwritten
+  // while it is in flight; M0 is set here for every load (nothing else in
+  // this file uses it).
   __device__ __forceinline__ void issue_one(uint8_t* base, int st, int d) {
     const int kb = st * kRowB;
     // a piece past the end of a row (K = 64) re-reads the row's first
     // bytes: in bounds, and never multiplied (only K codes are used)
     const int off = kb + goff[d] < Kb ? kb + goff[d] : goff[d] & 15;
-    __builtin_amdgcn_global_load_lds(gsrc[d] + off, (__attribute__((address_space(3))) void*)(base + lblk[d]), 16, 0, 0);
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)base)) + lblk[d]);  // uniform
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gsrc[d] + off), "s"(lds)
+                 : "memory");  // M0 is reserved: the compiler keeps no value of its own there
   }
 
   __device__ __forceinline__ void issue(uint8_t* base, int st) {
@@ -361,13 +377,16 @@ struct GemmCtx {
   }
 
   template <int SET>
+  __device__ void prologue() {  // the set's first two stages in flight
+    issue(ring<SET, 0>(), st0);
+    issue(ring<SET, 1>(), min(st0 + 1, st1 - 1));
+  }
+
+  template <int SET>
   __device__ void run(int nsteps) {
     uint8_t* r0 = ring<SET, 0>();
     uint8_t* r1 = ring<SET, 1>();
     uint8_t* r2 = ring<SET, 2>();
-    // prologue: the set's first two stages in flight
-    issue(r0, st0);
-    issue(r1, min(st0 + 1, st1 - 1));
     int s = 0;
     for (; s + kRing <= nsteps; s += kRing) revolution(s, kRing, r0, r1, r2);
     if (s < nsteps) revolution(s, nsteps - s, r0, r1, r2);
@@ -420,24 +439,6 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
   c.st1 = set == 0 ? half : c.nstage;
   const int nsteps = max(half, c.nstage - half);  // both sets step in lockstep
 
-  if (!PARTIALS) {
-    // s_rat[g] = S[g-1] / S[g]: entering group g rescales the accumulator
-    for (int g = tid; g < c.ngroups; g += kThreadsWG) s_rat[g] = g > 0 ? a.S[g - 1] / a.S[g] : 1.f;
-    // epilogue operands, read now so their latency hides behind the main
-    // loop (zero past the matrix edge; those outputs are never stored)
-    const float base = kUnit / static_cast<float>(a.K);
-    if (tid < kTT) {
-      const int t = c.t0 + tid;
-      s_rs[tid] = t < a.M ? a.dx[t] * base : 0.f;
-    } else if (tid < kTT + kTN) {
-      const int n = c.n0 + tid - kTT;
-      s_dw[tid - kTT] = n < a.N ? a.dw[n] : 0.f;
-    } else if (tid < kTT + kTN + kSets) {
-      const int st_end = tid - kTT - kTN == 0 ? half : c.nstage;  // end stage of set 0 / set 1
-      s_send[tid - kTT - kTN] = a.S[((st_end * 128 > a.K ? a.K : st_end * 128) - 1) >> a.log2G];
-    }
-  }
-
   // DMA blocks of a stage: 1 KiB = 16 rows x 64 B; blocks 0..15 hold the
   // weight rows, 16..23 the activation rows; wave w moves blocks 6w..6w+5.
   // Lane i fills 16-byte slot i of the block: row r = i / 4 (16b + r of the
@@ -458,6 +459,32 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
     } else {
       const int t = min(c.t0 + r, a.M - 1);
       c.gsrc[d] = a.xq + static_cast<size_t>(t) * c.Kb;
+    }
+  }
+
+  // the first loads go out before the tables below are read, so the two
+  // latencies overlap
+  if (set == 0) {
+    c.template prologue<0>();
+  } else if (c.st1 > c.st0) {
+    c.template prologue<1>();
+  }
+
+  if (!PARTIALS) {
+    // s_rat[g] = S[g-1] / S[g]: entering group g rescales the accumulator
+    for (int g = tid; g < c.ngroups; g += kThreadsWG) s_rat[g] = g > 0 ? a.S[g - 1] / a.S[g] : 1.f;
+    // epilogue operands, read now so their latency hides behind the main
+    // loop (zero past the matrix edge; those outputs are never stored)
+    const float base = kUnit / static_cast<float>(a.K);
+    if (tid < kTT) {
+      const int t = c.t0 + tid;
+      s_rs[tid] = t < a.M ? a.dx[t] * base : 0.f;
+    } else if (tid < kTT + kTN) {
+      const int n = c.n0 + tid - kTT;
+      s_dw[tid - kTT] = n < a.N ? a.dw[n] : 0.f;
+    } else if (tid < kTT + kTN + kSets) {
+      const int st_end = tid - kTT - kTN == 0 ? half : c.nstage;  // end stage of set 0 / set 1
+      s_send[tid - kTT - kTN] = a.S[((st_end * 128 > a.K ? a.K : st_end * 128) - 1) >> a.log2G];
     }
   }
 
