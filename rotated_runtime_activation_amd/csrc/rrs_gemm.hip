@@ -186,9 +186,11 @@ struct GemmCtx {
   const GemmArgs& a;
   int lane, wn, wt, n0, t0, Kb, nstage, log2spg, ngroups;
   int st0, st1;                      // this set's stage range [st0, st1)
-  const uint8_t* gsrc[kDmaPerWave];  // this lane's row pointer for each of its DMA blocks
-  int goff[kDmaPerWave];             // byte offset of its 16-byte piece
-  int lblk[kDmaPerWave];             // LDS offset of each block in a stage
+  const uint8_t* wbase;               // uniform: weight row n0 of the tile
+  const uint8_t* xbase;               // uniform: activation row t0 of the tile
+  uint32_t voff[kDmaPerWave];         // this lane's offset from its block's base: row and 16-byte piece
+  uint32_t lblk[kDmaPerWave];         // uniform: LDS offset of each block in a stage
+  int wave6;                          // uniform: first DMA block of this wave
   static constexpr int TI = 128 / Mm::BR;  // accumulator blocks per wave along n
   static constexpr int TJ = 64 / Mm::BR;   // and along t
   int fW, fX, swz;
@@ -200,7 +202,9 @@ struct GemmCtx {
 
   __device__ GemmCtx(const GemmArgs& args, const float* s_rat) : a(args), rat(s_rat) {}
 
-  // DMA block d of stage st into ring slot `base`. The load is written in
+  // DMA block d of stage st into ring slot `base`: the scalar base (block
+  // row plus stage) and the lane's fixed offset form the address, so a
+  // stage's loads cost no vector instructions. The load is written in
   // assembly so that the compiler does not track it: its wait insertion
   // loses the ring slots' alias scopes across the loop's back edge and then
   // drains every load in flight (the next stage's included) before a
@@ -212,16 +216,19 @@ struct GemmCtx {
   // while it is in flight; M0 is set here for every load (nothing else in
   // this file uses it).
   __device__ __forceinline__ void issue_one(uint8_t* base, int st, int d) {
-    const int kb = st * kRowB;
-    // a piece past the end of a row (K = 64) re-reads the row's first
-    // bytes: in bounds, and never multiplied (only K codes are used)
-    const int off = kb + goff[d] < Kb ? kb + goff[d] : goff[d] & 15;
     typedef __attribute__((address_space(3))) uint8_t lds_u8;
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(
-        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)base)) + lblk[d]);  // uniform
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+    // both scalar operands are uniform; readfirstlane keeps them in scalar
+    // registers where the compiler cannot prove it (a no-op elsewhere). Its
+    // result is a signed int: widen through uint32_t, never directly.
+    const uint32_t lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+        static_cast<int>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)base)) + lblk[d])));
+    const uint64_t ra = reinterpret_cast<uint64_t>((wave6 + d < 16 ? wbase : xbase) + st * kRowB);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(ra))));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(ra >> 32))));
+    const uint8_t* rows = reinterpret_cast<const uint8_t*>(static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(gsrc[d] + off), "s"(lds)
+                 : "v"(voff[d]), "s"(rows), "s"(lds)
                  : "memory");  // M0 is reserved: the compiler keeps no value of its own there
   }
 
@@ -441,25 +448,29 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
 
   // DMA blocks of a stage: 1 KiB = 16 rows x 64 B; blocks 0..15 hold the
   // weight rows, 16..23 the activation rows; wave w moves blocks 6w..6w+5.
-  // Lane i fills 16-byte slot i of the block: row r = i / 4 (16b + r of the
-  // matrix, clamped to it; clamped rows only feed outputs that are never
-  // stored), 16-byte chunk (i & 3) ^ ((r >> 1) & 3) of that row. The XOR
+  // Lane i fills 16-byte slot i of the block: row 16b + i / 4 of the
+  // matrix (clamped to it; clamped rows only feed outputs that are never
+  // stored), 16-byte chunk (i & 3) ^ ((i >> 3) & 3) of that row. The XOR
   // swizzle spreads the eight rows a fragment read serves at once over all
   // 32 LDS banks (rows 64 bytes apart would otherwise hit the same banks
-  // every two rows).
+  // every two rows). With K = 64 (one stage of 32 bytes per row) the
+  // chunks past the row's end re-read its first bytes: in bounds, and never
+  // multiplied (only K codes are used). Every other K is a multiple of 128.
+  // The tile's first rows (n0 < N, t0 < M) are the scalar bases; a lane's
+  // offset from them stays below 256 rows, so 32 bits hold it.
+  c.wbase = a.wq + static_cast<size_t>(c.n0) * c.Kb;
+  c.xbase = a.xq + static_cast<size_t>(c.t0) * c.Kb;
+  c.wave6 = wave * GemmCtx<KM, PARTIALS, SPG>::kDmaPerWave;
 #pragma unroll
   for (int d = 0; d < GemmCtx<KM, PARTIALS, SPG>::kDmaPerWave; ++d) {
-    const int blk = wave * GemmCtx<KM, PARTIALS, SPG>::kDmaPerWave + d;
-    const int r = (blk & 15) * 16 + (c.lane >> 2);
-    c.goff[d] = ((c.lane & 3) ^ ((c.lane >> 3) & 3)) * 16;
+    const int blk = c.wave6 + d;
+    const bool wrows = blk < 16;
+    const int base_row = wrows ? c.n0 : c.t0;
+    const int row = min(base_row + (blk & 15) * 16 + (c.lane >> 2), (wrows ? a.N : a.M) - 1);
+    int goff = ((c.lane & 3) ^ ((c.lane >> 3) & 3)) * 16;
+    if (goff >= c.Kb) goff &= 15;
+    c.voff[d] = static_cast<uint32_t>((row - base_row) * c.Kb + goff);
     c.lblk[d] = blk * 1024;
-    if (blk < 16) {
-      const int n = min(c.n0 + r, a.N - 1);
-      c.gsrc[d] = a.wq + static_cast<size_t>(n) * c.Kb;
-    } else {
-      const int t = min(c.t0 + r, a.M - 1);
-      c.gsrc[d] = a.xq + static_cast<size_t>(t) * c.Kb;
-    }
   }
 
   // the first loads go out before the tables below are read, so the two
