@@ -628,6 +628,15 @@ frontend_kernel(FeArgs a) {
       if (bits) atomicMax(&a.colmax[k], bits);
     }
   } else if constexpr (MODE == kQuant) {
+    // Without smoothing no maxima were gathered: S = 1 and the
+    // synchronisation block is untouched, so no workgroup has to wait for
+    // the others (a device-scope fence and a same-address counter per
+    // workgroup would cost more than the pass itself).
+    if (!a.smooth) {
+      if (blockIdx.x == 0)
+        for (int g = tid; g < ngroups; g += C::kThreads) a.S_out[g] = 1.f;
+      return;
+    }
     // The last workgroup to finish reading the running maxima publishes the
     // guarded scales and re-zeroes the synchronisation block for the next
     // call (every workgroup copied its scales to LDS before arriving here).
