@@ -258,7 +258,7 @@ def main():
         "roofline": gemm_roofline,
         "roofline_frontend": {
             "kernel": ("fused_kernel (rotate, reorder, group max, grid-wide wait, quantise, pack)"
-                       if fe_launches == 1 else "frontend_kernel stats pass + quantise pass"),
+                       if fe_launches == 1 else "stats pass, group-max reduce, quantise pass"),
             "launches": fe_launches,
             "bound": "hbm",
             "achieved": round(fe_gbs, 2),

@@ -158,9 +158,11 @@ int rrs_linear_signed(const void* X_fp16, int M, int K, int N, int G,
  * ("Incomplete ablation study"): RRS_FLAG_NO_ROTATE skips the rotation
  * (Runtime Smooth alone), RRS_FLAG_NO_SMOOTH forces S = 1 (rotation alone);
  * 0 is the full method. RRS_FLAG_TWO_PASS changes no result: it makes the
- * smoothed front end use two launches (group maxima, then quantise,
- * reading X twice), the form rrs_linear falls back to when the one-launch
- * form does not fit on the device at once.
+ * smoothed front end use three launches (each workgroup's group maxima,
+ * their reduction to S, then quantise; X is read twice), the form
+ * rrs_linear falls back to when the one-launch form does not fit on the
+ * device at once. That form keeps the per-workgroup maxima in xq, which its
+ * last launch then overwrites with the codes.
  *
  * The one-launch form keeps every rotated row on chip while the workgroups
  * combine their group maxima, so all its workgroups must be resident
@@ -183,10 +185,10 @@ int rrs_frontend_signed(const void* X_fp16, int M, int K, int G,
                         float* dx, float* S, void* ws, size_t ws_bytes,
                         int flags, hipStream_t s);
 
-/* Number of launches (1 or 2) the front end of rrs_linear / rrs_frontend
+/* Number of launches (1 or 3) the front end of rrs_linear / rrs_frontend
  * uses for M tokens of length K with these flags on the current device:
  * 1 when the one-launch form fits on the device at once (or without
- * smoothing), 2 otherwise. A host-side query; RRS_EINVAL for bad arguments,
+ * smoothing), 3 otherwise (also for K = m 2^k). A host-side query; RRS_EINVAL for bad arguments,
  * RRS_EHIP if the device cannot be queried. */
 int rrs_frontend_passes(int M, int K, int flags);
 

@@ -109,7 +109,7 @@ def rrs_calibrate_workspace_bytes(K: int) -> int:
 
 
 def rrs_frontend_passes(M: int, K: int, flags: int = 0) -> int:
-    """Launches (1 or 2) the front end uses for M tokens on the current device."""
+    """Launches (1 or 3) the front end uses for M tokens on the current device."""
     n = int(lib().rrs_frontend_passes(M, K, flags))
     if n < 0:
         _check("rrs_frontend_passes", n)

@@ -68,7 +68,8 @@ struct FeArgs {
   int log2G;
   int smooth;           // 0: S = 1 (rotation-only ablation, and weights)
   const int32_t* perm;
-  uint32_t* sync;       // synchronisation block (stats / quant)
+  uint32_t* sync;       // synchronisation block (one-launch form)
+  uint32_t* part;       // stats pass: one row of K/G group maxima per workgroup
   uint8_t* codes;       // [rows][K/2]
   float* scale;         // [rows]
   float* S_out;         // [K/G]
@@ -552,7 +553,7 @@ frontend_kernel(FeArgs a) {
       for (int g = tid; g < ngroups; g += C::kThreads) {
         float sg = 1.f;
         if (a.smooth) {
-          sg = __uint_as_float(a.sync[kSyncGroups + g]);
+          sg = a.S_out[g];            // from the reduce launch
           if (!(sg > 0.f)) sg = 1.f;  // all-zero group over every token
         }
         s_grp[g] = 1.f / sg;
@@ -614,13 +615,13 @@ frontend_kernel(FeArgs a) {
     }
   }
 
-  // ---- fold the workgroup's partial maxima into global memory ----------
+  // ---- the workgroup's partial maxima, the channel maxima ---------------
   if constexpr (MODE == kStats) {
+    // its own row of the partial area: plain stores (same-address atomics
+    // from every workgroup would serialise)
     __syncthreads();
-    for (int g = tid; g < ngroups; g += C::kThreads) {
-      const uint32_t bits = __float_as_uint(s_grp[g]);
-      if (bits) atomicMax(&a.sync[kSyncGroups + g], bits);
-    }
+    for (int g = tid; g < ngroups; g += C::kThreads)
+      a.part[static_cast<size_t>(blockIdx.x) * ngroups + g] = __float_as_uint(s_grp[g]);
   } else if constexpr (MODE == kColmax) {
     __syncthreads();
     for (int k = tid; k < K; k += C::kThreads) {
@@ -628,35 +629,27 @@ frontend_kernel(FeArgs a) {
       if (bits) atomicMax(&a.colmax[k], bits);
     }
   } else if constexpr (MODE == kQuant) {
-    // Without smoothing no maxima were gathered: S = 1 and the
-    // synchronisation block is untouched, so no workgroup has to wait for
-    // the others (a device-scope fence and a same-address counter per
-    // workgroup would cost more than the pass itself).
-    if (!a.smooth) {
-      if (blockIdx.x == 0)
-        for (int g = tid; g < ngroups; g += C::kThreads) a.S_out[g] = 1.f;
-      return;
-    }
-    // The last workgroup to finish reading the running maxima publishes the
-    // guarded scales and re-zeroes the synchronisation block for the next
-    // call (every workgroup copied its scales to LDS before arriving here).
-    __shared__ int s_last;
-    __syncthreads();
-    if (tid == 0) {
-      __threadfence();
-      const uint32_t done = atomicAdd(&a.sync[kSyncCounter], 1u);
-      s_last = done == gridDim.x - 1;
-    }
-    __syncthreads();
-    if (s_last) {
-      __threadfence();
-      for (int g = tid; g < ngroups; g += C::kThreads) {
-        const float sg = __uint_as_float(a.sync[kSyncGroups + g]);
-        a.S_out[g] = (a.smooth && sg > 0.f) ? sg : 1.f;
-        a.sync[kSyncGroups + g] = 0u;
-      }
-      if (tid == 0) a.sync[kSyncCounter] = 0u;
-    }
+    // with smoothing the reduce launch wrote S; without it S = 1
+    if (!a.smooth && blockIdx.x == 0)
+      for (int g = tid; g < ngroups; g += C::kThreads) a.S_out[g] = 1.f;
+  }
+}
+
+// S_g = max over `nrows` partial rows of group maxima (float bits), 1 where
+// every row holds 0: one workgroup per group, threads over rows.
+__global__ void __launch_bounds__(256) group_max_kernel(const uint32_t* part, int nrows, int ngroups,
+                                                        float* S_out) {
+  __shared__ uint32_t s_m[4];
+  const int g = blockIdx.x, tid = threadIdx.x;
+  uint32_t m = 0u;
+  for (int r = tid; r < nrows; r += 256) m = max(m, part[static_cast<size_t>(r) * ngroups + g]);
+  for (int d = 32; d >= 1; d >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), d)));
+  if ((tid & 63) == 0) s_m[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) {
+    m = max(max(s_m[0], s_m[1]), max(s_m[2], s_m[3]));
+    const float v = __uint_as_float(m);
+    S_out[g] = v > 0.f ? v : 1.f;
   }
 }
 
@@ -831,11 +824,21 @@ __global__ void zero_u32_kernel(uint32_t* p, size_t n) {
     p[i] = 0u;
 }
 
+// Workgroups of a one-pass launch over `rows` rows of length 2^log2K
+// (blocks of max(K, 4096) elements, Cfg's waves per workgroup).
+constexpr int pass_grid(int log2K, int rows) {
+  const int log2B = log2K > 12 ? log2K : 12;
+  const int per_block = 1 << (log2B - log2K);
+  const int waves = log2B == 12 ? 8 : 3;
+  return ((rows + per_block - 1) / per_block + waves - 1) / waves;
+}
+
 template <int LOG2K, int MODE, bool ROTATE>
 hipError_t launch_mode(const FeArgs& a, hipStream_t s) {
   using C = Cfg<LOG2K>;
-  const int nblk = (a.rows + C::kRows - 1) / C::kRows;
-  const int grid = (nblk + C::kWaves - 1) / C::kWaves;
+  static_assert(pass_grid(LOG2K, 1000) == ((1000 + C::kRows - 1) / C::kRows + C::kWaves - 1) / C::kWaves,
+                "pass_grid follows Cfg");
+  const int grid = pass_grid(LOG2K, a.rows);
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((frontend_kernel<LOG2K, MODE, ROTATE>), dim3(grid), dim3(C::kThreads), 0, s, a);
   return hipGetLastError();
@@ -938,6 +941,12 @@ bool fused_k(int log2K, const FeArgs& a, hipStream_t s, hipError_t* err) {
 
 }  // namespace
 
+hipError_t launch_group_max(const uint32_t* part, int nrows, int ngroups, float* S_out, hipStream_t s) {
+  if (ngroups <= 0) return hipSuccess;
+  hipLaunchKernelGGL(group_max_kernel, dim3(ngroups), dim3(256), 0, s, part, nrows, ngroups, S_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t* perm,
                            const uint32_t* dsign, uint8_t* xq, float* dx, float* S_out, uint32_t* sync,
                            int flags, hipStream_t s) {
@@ -959,7 +968,18 @@ hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t
   if (a.smooth) {
     // one launch when every workgroup fits on the device at once
     if (!(flags & 4) && (rotate ? fused_k<true>(log2K, a, s, &e) : fused_k<false>(log2K, a, s, &e))) return e;
+    // else stats, reduce, quantise. The stats rows sit in the codes buffer,
+    // which the quantise pass overwrites after the reduce has read them:
+    // pass_grid(log2K, M) rows of K/G words take at most M K / 32 bytes of
+    // its M K / 2 (K/G <= K/32 words, and a workgroup covers at least
+    // 3 rows, or 8 blocks of 4096/K rows when K < 4096).
+    const int ngroups = K / G;
+    const int nrows = pass_grid(log2K, M);
+    if (static_cast<size_t>(nrows) * ngroups * 4 > static_cast<size_t>(M) * (K / 2)) return hipErrorInvalidValue;
+    a.part = reinterpret_cast<uint32_t*>(xq);
     e = rotate ? dispatch_k<kStats, true>(log2K, a, s) : dispatch_k<kStats, false>(log2K, a, s);
+    if (e != hipSuccess) return e;
+    e = launch_group_max(a.part, nrows, ngroups, S_out, s);
     if (e != hipSuccess) return e;
   }
   return rotate ? dispatch_k<kQuant, true>(log2K, a, s) : dispatch_k<kQuant, false>(log2K, a, s);
@@ -972,7 +992,7 @@ int frontend_launches(int M, int K, int flags) {
   }
   const int log2K = __builtin_ctz(static_cast<unsigned>(K));
   if (flags & 2) return 1;
-  if (flags & 4) return 2;
+  if (flags & 4) return 3;
   const bool rotate = !(flags & 1);
   int r = 0;
   switch (log2K) {
@@ -981,7 +1001,7 @@ int frontend_launches(int M, int K, int flags) {
 #undef RRS_CASE
     default: return -1;
   }
-  return r > 0 ? 1 : 2;
+  return r > 0 ? 1 : 3;
 }
 
 hipError_t launch_weight_prep(const uint16_t* W, int K, int N, const int32_t* perm,

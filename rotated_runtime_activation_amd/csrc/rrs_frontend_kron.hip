@@ -413,24 +413,6 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
   }
 }
 
-// S_g = max over the stats pass's partial rows (zero -> 1): one workgroup
-// per group, threads over rows.
-__global__ void __launch_bounds__(256) kron_reduce_kernel(const uint32_t* part, int nrows, int ngroups,
-                                                          float* S_out) {
-  __shared__ uint32_t s_m[4];
-  const int g = blockIdx.x, tid = threadIdx.x;
-  uint32_t m = 0u;
-  for (int r = tid; r < nrows; r += 256) m = max(m, part[static_cast<size_t>(r) * ngroups + g]);
-  for (int d = 32; d >= 1; d >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), d)));
-  if ((tid & 63) == 0) s_m[tid >> 6] = m;
-  __syncthreads();
-  if (tid == 0) {
-    m = max(max(s_m[0], s_m[1]), max(s_m[2], s_m[3]));
-    const float v = __uint_as_float(m);
-    S_out[g] = v > 0.f ? v : 1.f;
-  }
-}
-
 template <int M, int LOG2N, int MODE>
 hipError_t launch_kron_mode(const KronArgs& a, int grid, hipStream_t s) {
   hipLaunchKernelGGL((kron_kernel<M, LOG2N, MODE>), dim3(grid), dim3(kKT), 0, s, a);
@@ -494,8 +476,7 @@ hipError_t launch_frontend_kron(const uint16_t* X, int M, int K, int G, const in
     const int gs = M < kKronRowsWG ? M : kKronRowsWG;
     hipError_t e = dispatch_kron<kKStats>(m, log2n, a, gs, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kron_reduce_kernel, dim3(ngroups), dim3(256), 0, s, a.part, gs, ngroups, S_out);
-    e = hipGetLastError();
+    e = launch_group_max(a.part, gs, ngroups, S_out, s);
     if (e != hipSuccess) return e;
   }
   return dispatch_kron<kKQuant>(m, log2n, a, M < kKronRowsWG ? M : kKronRowsWG, s);

@@ -15,34 +15,26 @@ constexpr int kMinG = 32;
 
 // Layout of the synchronisation block at the start of a workspace (uint32
 // words unless noted):
-//   [0]    done-counter of the two-launch front end's quantise pass
 //   [2]    error word: nonzero once a bounded wait gave up (only
 //          rrs_workspace_init clears it)
 //   [3]    epoch of the one-launch front end (calls so far, mod 2^32)
-//   [64, 64 + K/G)       running group maxima of the two-launch front end
-//                        (float bits; left zero by every call)
-//   [1024, 1024 + 32*512) one-launch arrival flags, one per workgroup, each
-//                        alone in its 128-byte line (pollers of different
-//                        flags then do not queue on one line): the epoch of
-//                        the call that last passed through it
-//   [17408, 17408 + 512 K/G) one-launch group maxima, one row of K/G floats
-//                        per workgroup (never needs clearing)
-// rrs_workspace_init zeroes words [0, 17408).
-constexpr int kSyncCounter = 0;
+//   [17408, 17408 + 2 * 512 K/G) one-launch group maxima: one row of K/G
+//          64-bit words per workgroup, this call's epoch in the high half
+//          and the maximum's float bits in the low half (never needs
+//          clearing)
+// Every other word below 17408 is reserved and stays zero.
+// rrs_workspace_init zeroes the whole block.
 constexpr int kSyncError = 2;
 constexpr int kSyncEpoch = 3;
-constexpr int kSyncGroups = 64;
-constexpr int kSyncFlags = 1024;
-constexpr int kFlagStride = 32;
 constexpr int kMaxFusedWG = 512;
-constexpr int kSyncPartials = kSyncFlags + kFlagStride * kMaxFusedWG;  // 17408
+constexpr int kSyncPartials = 17408;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Front end (activation rows): one launch when its workgroups all fit on
-// the device at once, else a stats pass then a quantise pass.
+// the device at once, else a stats pass, a reduce and a quantise pass.
 //   flags: bit0 = skip rotation, bit1 = skip smoothing (S = 1),
-//          bit2 = always use the two launches.
+//          bit2 = always use the three launches.
 //   dsign: signed rotation x D H, K-bit mask (bit j set: channel j negated),
 //          or nullptr for the plain rotation.
 hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t* perm,
@@ -83,6 +75,10 @@ hipError_t launch_gemm_small(const uint8_t* xq, const float* dx, const float* S,
 constexpr int kMaxKronK = 16384;
 bool kron_split(int K, int* m, int* log2n);
 int kron_frontend_launches(int flags);
+// S_g = max over `nrows` rows of K/G group maxima (float bits) at `part`,
+// 1 where every row holds 0 (the stats passes' reduce).
+hipError_t launch_group_max(const uint32_t* part, int nrows, int ngroups, float* S_out, hipStream_t s);
+
 hipError_t launch_frontend_kron(const uint16_t* X, int M, int K, int G, const int32_t* perm, const uint32_t* dsign,
                                 uint8_t* xq, float* dx, float* S_out, uint32_t* sync, int flags, hipStream_t s);
 hipError_t launch_weight_prep_kron(const uint16_t* W, int K, int N, const int32_t* perm, const uint32_t* dsign,

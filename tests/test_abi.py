@@ -49,7 +49,7 @@ def test_size_queries():
     assert rra.rrs_weight_bytes(256, 0) == 0
     # workspace: sync block + xq + dx + S
     sync = rra.rrs_sync_bytes(4096, 128)
-    # 17408 words (control, two-launch maxima, a reserved area) + a row of
+    # 17408 words (control words and a reserved area) + a row of
     # K/G 64-bit tagged maxima for each of 512 workgroups
     assert sync == 4 * (17408 + 2 * 512 * 32) and rra.rrs_sync_bytes(8192, 32) == 4 * (17408 + 2 * 512 * 256)
     assert rra.rrs_sync_bytes(64, 32) == 4 * (17408 + 2 * 512 * 2)
@@ -114,7 +114,7 @@ def test_frontend_passes_rejects():
     assert L.rrs_frontend_passes(16, 4096, 8) == rra.RRS_EINVAL
     # answered without a device when the flags fix the form
     assert L.rrs_frontend_passes(16, 4096, rra.RRS_FLAG_NO_SMOOTH) == 1
-    assert L.rrs_frontend_passes(16, 4096, rra.RRS_FLAG_TWO_PASS) == 2
+    assert L.rrs_frontend_passes(16, 4096, rra.RRS_FLAG_TWO_PASS) == 3
 
 
 def test_kron_shapes_accepted_and_rejected():

@@ -27,20 +27,20 @@ def _case(M, K, N=8, seed=None):
     return x, w, perm
 
 
-@pytest.mark.parametrize("form", ["one-launch", "two-launch"])
+@pytest.mark.parametrize("form", ["one-launch", "multi-launch"])
 @pytest.mark.parametrize("M,K,G", FE_SHAPES)
 def test_frontend(M, K, G, form):
-    flags = rra.RRS_FLAG_TWO_PASS if form == "two-launch" else 0
+    flags = rra.RRS_FLAG_TWO_PASS if form == "multi-launch" else 0
     passes = rra.rrs_frontend_passes(M, K, flags)
     gu.log(f"[frontend] M={M} K={K} G={G} {form}: {passes} launch(es)")
-    assert passes == (2 if flags else 1)
+    assert passes == (3 if flags else 1)
     x, _, perm = _case(M, K)
     gu.check_frontend(x, perm, G, flags)
 
 
 # Token counts at and past what the one-launch front end holds on chip (two
 # blocks of 4096 elements per wave at K <= 4096, one block of 8192 at
-# K = 8192): past it the same call falls back to two launches.
+# K = 8192): past it the same call falls back to three launches.
 @pytest.mark.parametrize("M,K,G", [(4096, 4096, 128), (4200, 4096, 128), (8300, 2048, 64),
                                    (768, 8192, 128), (800, 8192, 256)])
 def test_frontend_capacity(M, K, G):

@@ -30,11 +30,11 @@ def _case(M, K, N=8):
     return x, w, perm, bits, d
 
 
-@pytest.mark.parametrize("form", ["one-launch", "two-launch"])
+@pytest.mark.parametrize("form", ["one-launch", "multi-launch"])
 @pytest.mark.parametrize("M,K,G", [(16, 256, 64), (7, 2048, 64), (40, 4096, 128), (5, 8192, 256),
                                    (65, 8192, 32), (300, 512, 128)])
 def test_frontend_signed(M, K, G, form):
-    flags = rra.RRS_FLAG_TWO_PASS if form == "two-launch" else 0
+    flags = rra.RRS_FLAG_TWO_PASS if form == "multi-launch" else 0
     gu.log(f"[frontend signed] M={M} K={K} G={G} {form}")
     x, _, perm, bits, d = _case(M, K)
     fe = oracle.frontend(x, perm, G, d=d)
