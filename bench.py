@@ -273,10 +273,27 @@ def main():
         "wall_s_timed_region": round(wall, 4),
     }
 
+    out["device"] = device_info(torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, w, xc, G)
 
     print(json.dumps(out), flush=True)
+
+
+def device_info(torch):
+    """The device and the clock levels rocm-smi shows right after the timed
+    loops (the shader clock ramps under load; these are its levels then)."""
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
+            "rocm_smi_clocks": None}
+    try:
+        import subprocess
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        lines = [l.strip() for l in r.stdout.splitlines() if ("sclk" in l or "mclk" in l or "fclk" in l) and ":" in l]
+        info["rocm_smi_clocks"] = lines[:8] or None
+    except Exception:
+        pass
+    return info
 
 
 def cpu_baseline(x, w, xc, G, budget_s=10.0):
@@ -296,13 +313,17 @@ def cpu_baseline(x, w, xc, G, budget_s=10.0):
     t0 = time.perf_counter()
     while True:
         fe = oracle.frontend(x, perm, G)
-        oracle.linear_out(fe["q"], fe["dx"], fe["S"], wp["qw"], wp["dw"], G)
+        y = oracle.linear_out(fe["q"], fe["dx"], fe["S"], wp["qw"], wp["dw"], G)["Y"]
         reps += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = (time.perf_counter() - t0) / reps
     M, K = x.shape
     N = w.shape[1]
+    # the method's own quantisation error on this workload (outside the timing)
+    import numpy as np
+    ref = x.astype(np.float64) @ w.astype(np.float64)
+    qerr = float(np.linalg.norm(y - ref) / np.linalg.norm(ref))
     return {
         "value": round(2.0 * M * N * K / dt / 1e12, 6),
         "unit": "TOPS",
@@ -310,6 +331,8 @@ def cpu_baseline(x, w, xc, G, budget_s=10.0):
         "kind": "oracle",
         "sample": (f"{reps} full steps of the same workload (M={M}, K={K}, N={N}, G={G}) in float64 "
                    f"NumPy, {dt:.2f} s each; front end single-threaded, group GEMMs on {blas} BLAS threads"),
+        "quant_error": {"rel_fro": round(qerr, 6),
+                        "of": "the oracle's Y against the float64 product X W of the same fp16 inputs"},
     }
 
 
