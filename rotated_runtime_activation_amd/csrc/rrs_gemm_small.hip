@@ -73,6 +73,10 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
   constexpr int kBuf = (32 + 32 * TJ) * kRows;  // round buffer bytes per wave
   static_assert(TJ * 16 * 64 * 4 <= kBuf, "a wave's sums fit its round buffer");
   __shared__ float s_rat[(1 << kMaxLog2K) / 64];
+  __shared__ float s_dx[64];         // dx[t] 2^18 / K (0 past M)
+  __shared__ float s_dw[kTN];        // dw of the workgroup's channels (0 past N)
+  __shared__ float s_last[kWaves];   // scale of each wave's last group
+  __shared__ float s_out[64 * (kTN + 1)];  // the summed tile, token-major, rows padded by one word
   __shared__ __attribute__((aligned(16))) uint8_t s_buf[kWaves][kBuf];
 
   const int tid = threadIdx.x;
@@ -86,9 +90,6 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
   const int kpw = (a.K >> 6) / kWaves;  // k-steps per wave (a multiple of kRound)
   const int ks0 = wave * kpw;
   const int rounds = kpw / kRound;
-
-  for (int g = tid; g < ngroups; g += kThreads) s_rat[g] = g > 0 ? a.S[g - 1] / a.S[g] : 1.f;
-  __syncthreads();
 
   // coalesced load i of a round: row 8 i + lane / 8, chunk lane % 8 (rows
   // clamped to the matrix; clamped rows feed outputs that are never stored)
@@ -118,6 +119,23 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
 #pragma unroll
     for (int i = 0; i < kXL; ++i) rx[s][i] = *reinterpret_cast<const v4u*>(xsrc[i] + off);
   }
+  // the scales the loop and the epilogue need, read up front after the
+  // first rounds' loads: their latency then overlaps those loads instead of
+  // ending the kernel (as plain loads at the end they cost several
+  // microseconds per call)
+  const float base = kUnit / static_cast<float>(a.K);
+  for (int g = tid; g < ngroups; g += kThreads) s_rat[g] = g > 0 ? a.S[g - 1] / a.S[g] : 1.f;
+  if (tid < 64) {
+    s_dx[tid] = tid < a.M ? a.dx[tid] * base : 0.f;
+  } else if (tid < 64 + kTN) {
+    const int n = n0 + tid - 64;
+    s_dw[tid - 64] = n < a.N ? a.dw[n] : 0.f;
+  } else if (tid < 64 + kTN + kWaves) {
+    const int w = tid - 64 - kTN;
+    s_last[w] = a.S[(w * kpw + kpw - 1) >> log2spg];
+  }
+  __syncthreads();
+
   for (int r0 = 0; r0 < rounds; r0 += NR) {
 #pragma unroll
     for (int s = 0; s < NR; ++s) {
@@ -167,26 +185,35 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
 
   // absolute sums, times the scale of the group of the wave's last k-step,
   // into the wave's own buffer (its fragment reads are done: in-order LDS)
-  const float s_last = a.S[(ks0 + kpw - 1) >> log2spg];
+  const float sl = s_last[wave];
   float* part = reinterpret_cast<float*>(buf);
 #pragma unroll
   for (int j = 0; j < TJ; ++j)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) part[(j * 16 + e) * 64 + lane] = acc[j][e] * s_last;
+    for (int e = 0; e < 16; ++e) part[(j * 16 + e) * 64 + lane] = acc[j][e] * sl;
   __syncthreads();
 
-  // output element (token t, channel n0 + nl): register e = (nl / 8) * 4 +
-  // nl % 4 of lane t % 32 + 32 ((nl / 4) % 2) in block t / 32
-  const float base = kUnit / static_cast<float>(a.K);
+  // Sum of the 8 waves' sums in their storage order (consecutive threads
+  // on consecutive words: a token-major walk here would put one token's
+  // channels 64 words apart, all in one LDS bank), into a token-major tile.
+  // Register e of lane l in block j holds token 32 j + l % 32, channel
+  // 8 (e / 4) + 4 (l / 32) + e % 4.
+  for (int idx = tid; idx < TJ * 16 * 64; idx += kThreads) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) v += reinterpret_cast<const float*>(s_buf[w])[idx];
+    const int j = idx >> 10, e = (idx >> 6) & 15, l = idx & 63;
+    const int t = 32 * j + (l & 31);
+    const int nl = 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
+    s_out[t * (kTN + 1) + nl] = v;
+  }
+  __syncthreads();
+  // Y[t, n0 .. n0 + 31]: 128-byte rows
   for (int id = tid; id < TJ * 32 * kTN; id += kThreads) {
     const int t = id / kTN, nl = id % kTN;
     const int n = n0 + nl;
     if (t >= a.M || n >= a.N) continue;
-    const int j = t >> 5, e = (nl >> 3) * 4 + (nl & 3), l = (t & 31) + 32 * ((nl >> 2) & 1);
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += reinterpret_cast<const float*>(s_buf[w])[(j * 16 + e) * 64 + l];
-    a.Y[static_cast<size_t>(t) * a.N + n] = v * (a.dx[t] * base) * a.dw[n];
+    a.Y[static_cast<size_t>(t) * a.N + n] = s_out[t * (kTN + 1) + nl] * s_dx[t] * s_dw[nl];
   }
 }
 
