@@ -121,12 +121,13 @@ __device__ __forceinline__ void bfly(float& x, float& y) {
   y = a - b;
 }
 
-// Row buffer index of element f: one float of padding after every 64, so
+// Row buffer index of element f: four floats of padding after every 64, so
 // that the strided accesses of the passes, the matrix-core stores and the
-// gather spread over the LDS banks.
-__device__ __forceinline__ constexpr int rpad(int f) { return f + (f >> 6); }
+// gather spread over the LDS banks, and every run of 8 elements starting at
+// a multiple of 8 stays one aligned 32-byte piece (two 16-byte accesses).
+__device__ __forceinline__ constexpr int rpad(int f) { return f + 4 * (f >> 6); }
 template <int K>
-constexpr int kRowFloats = K + K / 64;
+constexpr int kRowFloats = K + K / 16;
 
 // Butterflies over R bits of f starting at bit B, in LDS (every run of n = 2^LOG2N).
 template <int K, int B, int R>
@@ -149,11 +150,65 @@ __device__ __forceinline__ void lds_pass(float* row, int tid) {
   __syncthreads();
 }
 
+// The first pass (f bits 0-2): each thread's 8 elements are consecutive,
+// read and written as two 16-byte words (as eight scalar accesses, lanes 8
+// floats apart share LDS banks eight ways).
+template <int K>
+__device__ __forceinline__ void lds_pass_low3(float* row, int tid) {
+  for (int t = tid; t < K / 8; t += kKT) {
+    float4* p = reinterpret_cast<float4*>(row + rpad(8 * t));
+    const float4 lo = p[0], hi = p[1];
+    float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (!(u & h)) bfly(v[u], v[u + h]);
+    p[0] = make_float4(v[0], v[1], v[2], v[3]);
+    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  __syncthreads();
+}
+
+// Later passes (B >= 2): f bits 0-1 take no part, so each thread carries 4
+// adjacent elements (one 16-byte word) through its R levels, 2^R words
+// 2^B apart.
+template <int K, int B, int R>
+__device__ __forceinline__ void lds_pass_vec(float* row, int tid) {
+  static_assert(B >= 2, "bits 0-1 stay inside a 16-byte word");
+  constexpr int P = 1 << R;
+  for (int t = tid; t < (K >> (R + 2)); t += kKT) {
+    const int lo = t & ((1 << (B - 2)) - 1), hi = t >> (B - 2);
+    const int base = (hi << (B + R)) | (lo << 2);
+    float4 v[P];
+#pragma unroll
+    for (int u = 0; u < P; ++u) v[u] = *reinterpret_cast<const float4*>(row + rpad(base + (u << B)));
+#pragma unroll
+    for (int h = 1; h < P; h <<= 1)
+#pragma unroll
+      for (int u = 0; u < P; ++u)
+        if (!(u & h)) {
+          bfly(v[u].x, v[u + h].x);
+          bfly(v[u].y, v[u + h].y);
+          bfly(v[u].z, v[u + h].z);
+          bfly(v[u].w, v[u + h].w);
+        }
+#pragma unroll
+    for (int u = 0; u < P; ++u) *reinterpret_cast<float4*>(row + rpad(base + (u << B))) = v[u];
+  }
+  __syncthreads();
+}
+
 template <int K, int B, int LOG2N>
 __device__ __forceinline__ void lds_passes(float* row, int tid) {
   if constexpr (B < LOG2N) {
     constexpr int R = (LOG2N - B) < 3 ? (LOG2N - B) : 3;
-    lds_pass<K, B, R>(row, tid);
+    if constexpr (B == 0 && R == 3)
+      lds_pass_low3<K>(row, tid);
+    else if constexpr (B >= 2)
+      lds_pass_vec<K, B, R>(row, tid);
+    else
+      lds_pass<K, B, R>(row, tid);
     lds_passes<K, B + R, LOG2N>(row, tid);
   }
 }
