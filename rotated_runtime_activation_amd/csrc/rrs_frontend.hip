@@ -859,6 +859,210 @@ hipError_t dispatch_k(int log2K, const FeArgs& a, hipStream_t s) {
   }
 }
 
+// ------------------------------------------------- one row per workgroup
+// Few tokens (decode-shaped calls, K = 4096 or 8192): the one-wave-per-row
+// kernel above leaves most of the chip idle and runs each row's whole chain
+// on one wave. Here a workgroup of 512 threads owns one row: thread t holds
+// elements E t .. E t + E - 1 (E = K / 512), runs the butterflies over the
+// E-index bits in registers, then three radix-8 passes over the padded row
+// in LDS cover the other nine bits. The reorder reads each output
+// position's source channel straight from the row buffer through perm.
+// Group maxima, the grid-wide wait (same epoch-tagged rows as fused_kernel,
+// one row per workgroup), the per-token scale and the packing follow the
+// kernels above with the same arithmetic.
+constexpr int kRowThreads = 512;
+
+__device__ __forceinline__ constexpr int rowpad(int f) { return f + 4 * (f >> 6); }
+
+template <int LOG2K, int B>
+__device__ __forceinline__ void row_pass8(float* row, int tid) {
+  constexpr int K = 1 << LOG2K;
+  for (int t = tid; t < K / 8; t += kRowThreads) {
+    const int lo = t & ((1 << B) - 1), hi = t >> B;
+    const int base = (hi << (B + 3)) | lo;
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = row[rowpad(base + (u << B))];
+    butterfly<8>(v, 1);
+    butterfly<8>(v, 2);
+    butterfly<8>(v, 4);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) row[rowpad(base + (u << B))] = v[u];
+  }
+  __syncthreads();
+}
+
+template <int LOG2K, bool ROTATE>
+__global__ void __launch_bounds__(kRowThreads) rowsplit_kernel(FeArgs a) {
+  constexpr int K = 1 << LOG2K;
+  constexpr int E = K / kRowThreads;  // 8 or 16
+  constexpr int LOG2E = LOG2K - 9;
+  static_assert(E == 8 || E == 16, "K = 4096 or 8192");
+  __shared__ __attribute__((aligned(16))) float s_row[K + K / 16];
+  __shared__ float s_grp[K / 32];
+  __shared__ float s_red[kRowThreads / 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int row = blockIdx.x;
+  const int ngroups = K >> a.log2G;
+  const int G = 1 << a.log2G;
+  const int p0 = E * tid;  // this thread's first element / output position
+
+  // ---- loads: perm of the outputs, then the activations (and signs)
+  int src[E];
+#pragma unroll
+  for (int c = 0; c < E / 4; ++c) {
+    const int4 q = *reinterpret_cast<const int4*>(a.perm + p0 + 4 * c);
+    src[4 * c] = rowpad(q.x);
+    src[4 * c + 1] = rowpad(q.y);
+    src[4 * c + 2] = rowpad(q.z);
+    src[4 * c + 3] = rowpad(q.w);
+  }
+  uint4 w[E / 8];
+#pragma unroll
+  for (int i = 0; i < E / 8; ++i)
+    w[i] = *reinterpret_cast<const uint4*>(a.src + static_cast<size_t>(row) * K + p0 + 8 * i);
+  if (ROTATE && a.dsign) {
+#pragma unroll
+    for (int i = 0; i < E / 8; ++i) {
+      const uint32_t b = a.dsign[(p0 >> 3) + i];
+      w[i].x ^= ((b & 1u) << 15) | ((b & 2u) << 30);
+      w[i].y ^= ((b & 4u) << 13) | ((b & 8u) << 28);
+      w[i].z ^= ((b & 16u) << 11) | ((b & 32u) << 26);
+      w[i].w ^= ((b & 64u) << 9) | ((b & 128u) << 24);
+    }
+  }
+  const uint32_t epoch =
+      a.smooth ? __hip_atomic_load(&a.sync[kSyncEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u : 0u;
+  for (int g = tid; g < ngroups; g += kRowThreads) s_grp[g] = 0.f;
+
+  // ---- rotate: E-index bits in registers, the other nine bits in LDS
+  float v[E];
+#pragma unroll
+  for (int i = 0; i < E / 8; ++i) {
+    const uint32_t q[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[8 * i + 2 * e] = h2f(q[e] & 0xffffu);
+      v[8 * i + 2 * e + 1] = h2f(q[e] >> 16);
+    }
+  }
+  if (ROTATE) {
+#pragma unroll
+    for (int h = 1; h < E; h <<= 1) butterfly<E>(v, h);
+  }
+#pragma unroll
+  for (int c = 0; c < E / 4; ++c)
+    *reinterpret_cast<float4*>(s_row + rowpad(p0 + 4 * c)) = make_float4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
+  __syncthreads();
+  if (ROTATE) {
+    row_pass8<LOG2K, LOG2E>(s_row, tid);
+    row_pass8<LOG2K, LOG2E + 3>(s_row, tid);
+    row_pass8<LOG2K, LOG2E + 6>(s_row, tid);
+  }
+
+  // ---- reorder, then the group maximum of this row (all E in one group)
+#pragma unroll
+  for (int r = 0; r < E; ++r) v[r] = s_row[src[r]];
+  float m = fabsf(v[0]);
+#pragma unroll
+  for (int r = 1; r < E; ++r) m = fmaxf(m, fabsf(v[r]));
+  const int g0 = p0 >> a.log2G;
+  if (a.smooth) {
+    float mg = m;
+    for (int d = 1; d * E < G && d < 64; d <<= 1) mg = fmaxf(mg, __shfl_xor(mg, d));
+    if ((p0 & (G - 1)) == 0 || (lane == 0)) {
+      if (mg > 0.f) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[g0]), __float_as_uint(mg));
+    }
+    __syncthreads();
+
+    // ---- publish this row's maxima, read every row's (as fused_kernel)
+    uint64_t* part = reinterpret_cast<uint64_t*>(a.sync + kSyncPartials);
+    const uint64_t tag = static_cast<uint64_t>(epoch) << 32;
+    for (int g = tid; g < ngroups; g += kRowThreads)
+      __hip_atomic_store(&part[static_cast<size_t>(row) * ngroups + g], tag | __float_as_uint(s_grp[g]),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    for (int g = tid; g < ngroups; g += kRowThreads) s_grp[g] = 0.f;
+    __syncthreads();
+    {
+      constexpr int kBatch = 8;
+      const int n = static_cast<int>(gridDim.x) * ngroups;
+      for (int base = tid; base < n; base += kRowThreads * kBatch) {
+        uint64_t b[kBatch];
+        uint32_t it = 0;
+        for (;;) {
+#pragma unroll
+          for (int k = 0; k < kBatch; ++k) {
+            const int idx = base + k * kRowThreads;
+            b[k] = idx < n ? __hip_atomic_load(&part[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag;
+          }
+          bool all = true;
+#pragma unroll
+          for (int k = 0; k < kBatch; ++k) all &= (b[k] >> 32) == epoch;
+          if (all) break;
+          if (++it == kSpinLimit) {
+            atomicOr(&a.sync[kSyncError], 1u);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const uint32_t bits = static_cast<uint32_t>(b[k]);
+          if (bits) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[(base + k * kRowThreads) % ngroups]), bits);
+        }
+      }
+    }
+    __syncthreads();
+    // every workgroup has read the old epoch (it tagged its row with old + 1)
+    if (row == 0 && tid == 0)
+      __hip_atomic_store(&a.sync[kSyncEpoch], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int g = tid; g < ngroups; g += kRowThreads) {
+      float sg = s_grp[g];
+      if (!(sg > 0.f)) sg = 1.f;  // all-zero group over every token
+      if (row == 0) a.S_out[g] = sg;
+      s_grp[g] = 1.f / sg;
+    }
+  } else {
+    for (int g = tid; g < ngroups; g += kRowThreads) {
+      if (row == 0) a.S_out[g] = 1.f;
+      s_grp[g] = 1.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- per-token scale (max over the row of |Zp| / S_g), codes, packing
+  const float inv = s_grp[g0];
+  float rmax = m * inv;
+  for (int d = 1; d < 64; d <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, d));
+  if (lane == 0) s_red[tid >> 6] = rmax;
+  __syncthreads();
+  rmax = s_red[0];
+#pragma unroll
+  for (int k = 1; k < kRowThreads / 64; ++k) rmax = fmaxf(rmax, s_red[k]);
+  const float k7 = rmax > 0.f ? 7.f / rmax : 0.f;
+  const float ks = inv * k7;
+  uint32_t packed[E / 8];
+#pragma unroll
+  for (int o = 0; o < E / 8; ++o) {
+    uint32_t mag[8], sgn[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      mag[e] = __float_as_uint(fmaf(fabsf(v[8 * o + e]), ks, kMagic));
+      sgn[e] = __float_as_uint(v[8 * o + e]);
+    }
+    packed[o] = pack8(mag, sgn);
+  }
+  uint8_t* dst = a.codes + static_cast<size_t>(row) * (K / 2) + p0 / 2;
+  if constexpr (E == 16)
+    *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
+  else
+    *reinterpret_cast<uint32_t*>(dst) = packed[0];
+  if (tid == 0) a.scale[row] = rmax / 7.f;
+}
+
 // Workgroups of fused_kernel<LOG2K, ROTATE, R> that the current device holds
 // at once (occupancy per CU x CUs), cached per device; -1 if unknown.
 constexpr int kMaxDevices = 64;
@@ -924,6 +1128,56 @@ bool launch_fused(const FeArgs& a, hipStream_t s, hipError_t* err) {
   return false;
 }
 
+// Workgroups of rowsplit_kernel the device holds at once (cached per device).
+template <int LOG2K, bool ROTATE>
+int rowsplit_capacity() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  int cap = cache[dev].load(std::memory_order_relaxed);
+  if (cap == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rowsplit_kernel<LOG2K, ROTATE>, kRowThreads, 0) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu <= 0 ||
+        cus <= 0) {
+      cap = -1;
+    } else {
+      cap = per_cu * cus;
+    }
+    cache[dev].store(cap, std::memory_order_relaxed);
+  }
+  return cap;
+}
+
+// Token counts up to which one row per workgroup beats one row per wave
+// (measured at K = 4096 and 8192).
+constexpr int kRowSplitMaxRows = 256;
+
+template <int LOG2K, bool ROTATE>
+bool rowsplit_fits(int rows) {
+  if (rows < 1 || rows > kRowSplitMaxRows || rows > kMaxFusedWG) return false;
+  const int cap = rowsplit_capacity<LOG2K, ROTATE>();
+  return cap > 0 && rows <= cap;
+}
+
+bool rowsplit_applies(int log2K, bool rotate, int rows) {
+  if (log2K == 12) return rotate ? rowsplit_fits<12, true>(rows) : rowsplit_fits<12, false>(rows);
+  if (log2K == 13) return rotate ? rowsplit_fits<13, true>(rows) : rowsplit_fits<13, false>(rows);
+  return false;
+}
+
+template <int LOG2K, bool ROTATE>
+hipError_t launch_rowsplit(const FeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((rowsplit_kernel<LOG2K, ROTATE>), dim3(a.rows), dim3(kRowThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t rowsplit_k(int log2K, bool rotate, const FeArgs& a, hipStream_t s) {
+  if (log2K == 12) return rotate ? launch_rowsplit<12, true>(a, s) : launch_rowsplit<12, false>(a, s);
+  return rotate ? launch_rowsplit<13, true>(a, s) : launch_rowsplit<13, false>(a, s);
+}
+
 template <bool ROTATE>
 bool fused_k(int log2K, const FeArgs& a, hipStream_t s, hipError_t* err) {
   switch (log2K) {
@@ -965,6 +1219,8 @@ hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t
   a.S_out = S_out;
   const bool rotate = !(flags & 1);
   hipError_t e = hipSuccess;
+  // few tokens at K = 4096 / 8192: one row per workgroup, one launch
+  if (!(flags & 4) && rowsplit_applies(log2K, rotate, M)) return rowsplit_k(log2K, rotate, a, s);
   if (a.smooth) {
     // one launch when every workgroup fits on the device at once
     if (!(flags & 4) && (rotate ? fused_k<true>(log2K, a, s, &e) : fused_k<false>(log2K, a, s, &e))) return e;
@@ -994,6 +1250,7 @@ int frontend_launches(int M, int K, int flags) {
   if (flags & 2) return 1;
   if (flags & 4) return 3;
   const bool rotate = !(flags & 1);
+  if (rowsplit_applies(log2K, rotate, M)) return 1;
   int r = 0;
   switch (log2K) {
 #define RRS_CASE(L) case L: r = rotate ? fused_blocks_per_wave<L, true>(M) : fused_blocks_per_wave<L, false>(M); break;
