@@ -50,6 +50,42 @@ def test_frontend_capacity(M, K, G):
     gu.check_frontend(x, perm, G)
 
 
+# One row per workgroup (K = 4096 and 8192, up to 256 rows) and the step to
+# one row per wave past it; group sizes from 32 to a single group of K.
+@pytest.mark.parametrize("M,K,G", [(1, 8192, 128), (255, 8192, 32), (256, 8192, 8192), (257, 8192, 128),
+                                   (1, 4096, 4096), (256, 4096, 64), (257, 4096, 128)])
+@pytest.mark.parametrize("flags", [0, rra.RRS_FLAG_NO_SMOOTH, rra.RRS_FLAG_NO_ROTATE])
+def test_frontend_rows_boundary(M, K, G, flags):
+    gu.log(f"[frontend rows] M={M} K={K} G={G} flags={flags}: {rra.rrs_frontend_passes(M, K, flags)} launch(es)")
+    assert rra.rrs_frontend_passes(M, K, flags) == 1
+    x, _, perm = _case(M, K)
+    gu.check_frontend(x, perm, G, flags)
+
+
+def test_frontend_rows_workspace_reuse():
+    """The row-per-workgroup form and the one-row-per-wave form share the
+    synchronisation block's epoch and partial rows: calls of both in a row,
+    with a smoothing-free call between."""
+    K, G = 8192, 128
+    ws = torch.zeros(rra.rrs_sync_bytes(K, G), dtype=torch.uint8, device=gu.DEV)
+    rra.rrs_workspace_init(ws)
+    calls = 0
+    for M, flags in [(64, 0), (700, 0), (3, 0), (64, rra.RRS_FLAG_NO_SMOOTH), (256, 0), (300, 0), (1, 0)]:
+        gu.log(f"[rows workspace reuse] M={M} flags={flags}")
+        x, _, perm = _case(M, K)
+        fe = oracle.frontend(x, perm, G, smooth=not (flags & 2))
+        xq = torch.empty(M, K // 2, dtype=torch.uint8, device=gu.DEV)
+        dx = torch.empty(M, dtype=torch.float32, device=gu.DEV)
+        S = torch.empty(K // G, dtype=torch.float32, device=gu.DEV)
+        rra.rrs_frontend(gu.to_dev(x), G, gu.to_dev(perm), xq, dx, S, ws, flags)
+        torch.cuda.synchronize()
+        if not flags and rra.rrs_frontend_passes(M, K, 0) == 1:
+            calls += 1
+        gu.check_sync_block(ws, K, G, calls)
+        gu.compare_codes(oracle.unpack_codes(xq.cpu().numpy()), fe["q"], fe["v"], "rows reuse codes")
+        gu.rel_close(S.cpu().numpy(), fe["S"], gu.SCALE_TOL, "rows reuse S")
+
+
 @pytest.mark.parametrize("M,K,G", [(40, 512, 64), (5, 4096, 128), (3, 8192, 256)])
 @pytest.mark.parametrize("flags", [rra.RRS_FLAG_NO_ROTATE, rra.RRS_FLAG_NO_SMOOTH,
                                    rra.RRS_FLAG_NO_ROTATE | rra.RRS_FLAG_NO_SMOOTH])
