@@ -257,7 +257,9 @@ def main():
         "gemm_tops": round(gemm_tops, 3),
         "roofline": gemm_roofline,
         "roofline_frontend": {
-            "kernel": ("fused_kernel (rotate, reorder, group max, grid-wide wait, quantise, pack)"
+            "kernel": (("rowsplit_kernel (one row per workgroup: rotate, reorder, group max, grid-wide wait, "
+                        "quantise, pack)" if M <= 256 and K in (4096, 8192) else
+                        "fused_kernel (rotate, reorder, group max, grid-wide wait, quantise, pack)")
                        if fe_launches == 1 else "stats pass, group-max reduce, quantise pass"),
             "launches": fe_launches,
             "bound": "hbm",
