@@ -283,16 +283,21 @@ def main():
 
 
 def device_info(torch):
-    """The device and the clock levels rocm-smi shows right after the timed
-    loops (the shader clock ramps under load; these are its levels then)."""
+    """The device and the clock levels the driver reports right after the
+    timed loops (the shader clock ramps under load; the level marked with *
+    is the one in use). Read from the driver's sysfs tables: no program is
+    started from this GPU process."""
+    import glob
     props = torch.cuda.get_device_properties(0)
     info = {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
-            "rocm_smi_clocks": None}
+            "clocks": None}
     try:
-        import subprocess
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
-        lines = [l.strip() for l in r.stdout.splitlines() if ("sclk" in l or "mclk" in l or "fclk" in l) and ":" in l]
-        info["rocm_smi_clocks"] = lines[:8] or None
+        clocks = {}
+        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_[sm]clk")):
+            cur = [l.strip() for l in open(path) if "*" in l]
+            if cur:
+                clocks[path.split("/")[-3] + ":" + path.rsplit("_", 1)[-1]] = cur[0]
+        info["clocks"] = clocks or None
     except Exception:
         pass
     return info
