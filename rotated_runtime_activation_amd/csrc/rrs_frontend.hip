@@ -32,8 +32,11 @@
 // quantised. The one-launch form (fused_kernel) keeps each wave's rotated,
 // reordered rows in registers across one grid-wide wait on the group
 // maxima, so X is read from memory once; it is used whenever all its
-// workgroups fit on the device together. Otherwise a stats launch and a
-// quantise launch each rotate the rows (X is read twice).
+// workgroups fit on the device together. For few tokens at K = 4096 and
+// 8192 (up to 256 rows) rowsplit_kernel gives each row a whole workgroup
+// instead (one launch as well). Otherwise a stats launch (per-workgroup
+// maxima rows), a reduce launch and a quantise launch; the stats and
+// quantise launches each rotate the rows (X is read twice).
 
 #include "rrs_internal.h"
 #include "rrs_codes.h"
@@ -513,7 +516,7 @@ __device__ __forceinline__ void quantise_block(const float (&v)[Cfg<LOG2K>::kE],
 }
 
 // ----------------------------------------------------------- one-pass kernels
-// Stats and quantise passes of the two-launch front end, the offline weight
+// Stats and quantise passes of the three-launch front end, the offline weight
 // preparation (columns of W as rows) and the calibration channel maxima.
 template <int LOG2K, int MODE, bool ROTATE>
 __global__ void __launch_bounds__(Cfg<LOG2K>::kThreads)
