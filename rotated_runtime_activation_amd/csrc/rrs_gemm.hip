@@ -30,11 +30,12 @@
 // global -> LDS loads into 3-slot rings (two stages in flight), then
 // per-wave widening of the packed fragments -> MFMA. Two sets of 4 waves
 // split K and add their partial sums at the end.
-// v_mfma_f32_32x32x64_f8f6f4 serves G >= 128, v_mfma_f32_16x16x32_fp8_fp8
-// G = 32 and 64. The 32 x 32 shape is chosen for its length: an MFMA hides
-// only a few VALU issue slots of the widening and rescale that go with it,
-// and a 64-cycle 32 x 32 x 64 MFMA hides about three times as many as a
-// 32-cycle 16 x 16 x 128 one for the same products.
+// v_mfma_f32_32x32x64_f8f6f4 serves G >= 64 (one instruction never crosses
+// a group boundary), v_mfma_f32_16x16x32_fp8_fp8 G = 32. The 32 x 32 shape
+// is chosen for its length: an MFMA hides only a few VALU issue slots of the
+// widening and rescale that go with it, and a 64-cycle 32 x 32 x 64 MFMA
+// hides about three times as many as a 32-cycle 16 x 16 x 128 one for the
+// same products.
 
 #include "rrs_internal.h"
 
@@ -616,7 +617,7 @@ hipError_t launch_gemm(const uint8_t* xq, const float* dx, const float* S, int M
   a.tiles_n = (N + kTN - 1) / kTN;
   switch (G) {
     case 32: return launch_km<32, 1>(a, partials, s);
-    case 64: return launch_km<32, 2>(a, partials, s);
+    case 64: return launch_km<64, 1>(a, partials, s);
     case 128: return launch_km<64, 2>(a, partials, s);
     default: return launch_km<64, 0>(a, partials, s);
   }
