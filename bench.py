@@ -100,8 +100,8 @@ def copy_probe(mib):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the layer shards by output channels with no exchange, see the design notes)",
+        print(f"bench.py: runs on one GPU; --gpus {args.gpus} is not supported (the layer would shard "
+              "by output channels with no exchange: each GPU runs these kernels on its N / p channels)",
               file=sys.stderr)
         sys.exit(2)
 

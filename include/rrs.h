@@ -77,7 +77,7 @@ extern "C" {
 typedef enum {
   RRS_OK = 0,
   RRS_EINVAL = -1,       /* bad argument (shape, null pointer, short buffer) */
-  RRS_EUNSUPPORTED = -2, /* legal request this build does not serve */
+  RRS_EUNSUPPORTED = -2, /* legal request the library does not serve */
   RRS_EHIP = -3          /* a HIP launch or runtime call failed */
 } rrs_status;
 

@@ -24,7 +24,7 @@ give them, no blocking or fusion. Sources ("pages"):
   q_A = 2^(b-1) - 1), Sec. 5 "Quantization and calibration" (per-token
   symmetric activations, per-output-channel symmetric weights).
 
-Readings taken where the pages are silent (numbered as in the design notes):
+Readings taken where the pages are silent, each with a label (R1, R2, ...):
 R1 group scale = max over the group's channels of the per-channel max over
 tokens; R2 the max runs over all tokens of the call; R3/R4 Sylvester Hadamard
 in natural order, unnormalised, with the exact 1/K folded into the output;
