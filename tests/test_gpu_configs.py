@@ -16,6 +16,9 @@ pytestmark = pytest.mark.gpu
 # name -> (output rows sampled, output columns sampled); None = all
 SAMPLING = {"tiny": None, "o_proj": None, "decode": None, "gate_up": (96, 384), "g_sweep": (96, 384),
             "down_proj": (96, 384)}
+# group sizes run beyond the workload's own: G = 64 takes its own GEMM
+# schedule (one group per 32x32x64 MFMA K step), G = 256 the generic one
+EXTRA_G = {"g_sweep": (64, 256)}
 
 
 @pytest.mark.parametrize("name", list(workloads.WORKLOADS))
@@ -61,7 +64,7 @@ def test_workload(name):
 
     X = gu.to_dev(x)
     P = gu.to_dev(perm_ref)
-    for G in wl.G:
+    for G in tuple(wl.G) + EXTRA_G.get(name, ()):
         gu.log(f"[workload {name}] rrs_linear G={G}")
         ws = torch.zeros(rra.rrs_workspace_bytes(M, K, G), dtype=torch.uint8, device=gu.DEV)
         rra.rrs_workspace_init(ws)
