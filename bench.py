@@ -260,7 +260,9 @@ def main():
             "kernel": (("rowsplit_kernel (one row per workgroup: rotate, reorder, group max, grid-wide wait, "
                         "quantise, pack)" if M <= 256 and K in (4096, 8192) else
                         "fused_kernel (rotate, reorder, group max, grid-wide wait, quantise, pack)")
-                       if fe_launches == 1 else "stats pass, group-max reduce, quantise pass"),
+                       if fe_launches == 1 else
+                       "stats pass, group-max reduce, quantise pass" if (K & (K - 1)) == 0 else
+                       "stats pass (keeps the rotated rows), group-max reduce, quantise pass over the stored rows"),
             "launches": fe_launches,
             "bound": "hbm",
             "achieved": round(fe_gbs, 2),

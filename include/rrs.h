@@ -96,7 +96,9 @@ size_t rrs_weight_bytes(int K, int N);
  * synchronisation block (rrs_sync_bytes(K, G): control words, a reserved
  * area, and a row of K/G 64-bit group-maximum words, tagged with the call
  * count, for each of up to 512 workgroups), then xq [M][K/2], dx [M] and
- * S [K/G], each 256-byte aligned.
+ * S [K/G], each 256-byte aligned; for K = m 2^k (Kronecker rotation) also a
+ * row area of M x K fp32 (the rotated, reordered rows, kept between the
+ * front end's stats and quantise passes so that each row is rotated once).
  * rrs_frontend needs only the synchronisation block. Returns 0 for an
  * invalid shape. */
 size_t rrs_workspace_bytes(int M, int K, int G);
@@ -163,6 +165,13 @@ int rrs_linear_signed(const void* X_fp16, int M, int K, int N, int G,
  * rrs_linear falls back to when the one-launch form does not fit on the
  * device at once. That form keeps the per-workgroup maxima in xq, which its
  * last launch then overwrites with the codes.
+ *
+ * For K = m 2^k with smoothing and rotation, a `ws` of at least
+ * rrs_workspace_bytes(M, K, G) bytes is taken as an rrs_linear workspace:
+ * its row area keeps the rotated rows between the stats and quantise passes
+ * (as in rrs_linear) unless X, perm, dsign, xq, dx or S lies in that area;
+ * with a smaller `ws` the quantise pass rotates every row again. The results
+ * are the same bits either way.
  *
  * The one-launch form keeps every rotated row on chip while the workgroups
  * combine their group maxima, so all its workgroups must be resident

@@ -35,17 +35,27 @@ size_t sync_bytes(int K, int G) {
 }
 
 struct WsLayout {
-  size_t sync, xq, dx, S, total;
+  size_t sync, xq, dx, S, rows, rows_bytes, total;
 };
 
+// sync | xq | dx | S | rows; the row area (the rotated, reordered fp32 rows
+// the Kronecker front end keeps between its stats and quantise passes) is
+// there only for K = m 2^k
 WsLayout ws_layout(int M, int K, int G) {
   WsLayout l{};
   l.sync = 0;
   l.xq = sync_bytes(K, G);
   l.dx = l.xq + align256(static_cast<size_t>(M) * (K / 2));
   l.S = l.dx + align256(sizeof(float) * static_cast<size_t>(M));
-  l.total = l.S + align256(sizeof(float) * static_cast<size_t>(K / G));
+  l.rows = l.S + align256(sizeof(float) * static_cast<size_t>(K / G));
+  l.rows_bytes = pow2(K) ? 0 : align256(sizeof(float) * static_cast<size_t>(M) * K);
+  l.total = l.rows + l.rows_bytes;
   return l;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? RRS_OK : RRS_EHIP; }
@@ -125,8 +135,22 @@ int frontend_impl(const void* X_fp16, int M, int K, int G, const int32_t* perm, 
   if (ws_bytes < sync_bytes(K, G)) return RRS_EINVAL;
   if (!all_a16(X_fp16, perm, xq, dx, S, ws, dsign)) return RRS_EINVAL;
   if (M == 0) return RRS_OK;
+  // a workspace of rrs_linear's size: the Kronecker front end keeps its rows
+  // in the row area, unless another argument lies there
+  float* zrows = nullptr;
+  const WsLayout l = ws_layout(M, K, G);
+  if (l.rows_bytes && ws_bytes >= l.total) {
+    uint8_t* r = static_cast<uint8_t*>(ws) + l.rows;
+    const size_t mk = static_cast<size_t>(M) * K;
+    if (!overlap(r, l.rows_bytes, X_fp16, 2 * mk) && !overlap(r, l.rows_bytes, xq, mk / 2) &&
+        !overlap(r, l.rows_bytes, dx, 4 * static_cast<size_t>(M)) &&
+        !overlap(r, l.rows_bytes, S, 4 * static_cast<size_t>(K / G)) &&
+        !overlap(r, l.rows_bytes, perm, 4 * static_cast<size_t>(K)) &&
+        (dsign == nullptr || !overlap(r, l.rows_bytes, dsign, static_cast<size_t>(K / 8))))
+      zrows = reinterpret_cast<float*>(r);
+  }
   return hip_status(rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, K, G, perm, dsign, xq,
-                                         dx, S, static_cast<uint32_t*>(ws), flags, s));
+                                         dx, S, static_cast<uint32_t*>(ws), flags, s, zrows));
 }
 
 int linear_impl(const void* X_fp16, int M, int K, int N, int G, const int32_t* perm, const uint32_t* dsign,
@@ -142,8 +166,9 @@ int linear_impl(const void* X_fp16, int M, int K, int N, int G, const int32_t* p
   uint8_t* xq = base + l.xq;
   float* dx = reinterpret_cast<float*>(base + l.dx);
   float* S = reinterpret_cast<float*>(base + l.S);
+  float* zrows = l.rows_bytes ? reinterpret_cast<float*>(base + l.rows) : nullptr;
   hipError_t e = rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, K, G, perm, dsign, xq, dx,
-                                      S, reinterpret_cast<uint32_t*>(base + l.sync), 0, s);
+                                      S, reinterpret_cast<uint32_t*>(base + l.sync), 0, s, zrows);
   if (e != hipSuccess) return RRS_EHIP;
   const uint8_t* codes = static_cast<const uint8_t*>(wq);
   const float* dw = reinterpret_cast<const float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));

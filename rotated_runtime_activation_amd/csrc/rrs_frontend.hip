@@ -1206,8 +1206,8 @@ hipError_t launch_group_max(const uint32_t* part, int nrows, int ngroups, float*
 
 hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t* perm,
                            const uint32_t* dsign, uint8_t* xq, float* dx, float* S_out, uint32_t* sync,
-                           int flags, hipStream_t s) {
-  if (K & (K - 1)) return launch_frontend_kron(X, M, K, G, perm, dsign, xq, dx, S_out, sync, flags, s);
+                           int flags, hipStream_t s, float* zrows) {
+  if (K & (K - 1)) return launch_frontend_kron(X, M, K, G, perm, dsign, xq, dx, S_out, sync, flags, s, zrows);
   const int log2K = __builtin_ctz(static_cast<unsigned>(K));
   FeArgs a{};
   a.dsign = reinterpret_cast<const uint8_t*>(dsign);

@@ -21,8 +21,12 @@
 // The group scales need every token first, so the smoothed front end is
 // three launches: stats (each row's group maxima into its own row of a
 // scratch area, the codes buffer, which the quantise pass overwrites later;
-// no atomics), reduce (S = max over those rows), quantise (rotate again,
-// smooth, per-token scale, pack).
+// no atomics), reduce (S = max over those rows), quantise. Given a row area
+// of 4 M K bytes, the stats pass also stores each rotated, reordered fp32
+// row and the quantise pass streams them back (one workgroup per row);
+// without one it rotates every row again. Both give the same bits: the
+// quantise arithmetic is the same and the rows are those the stats pass
+// reduced.
 // Weight preparation and calibration use the same rotation.
 
 #include "rrs_codes.h"
@@ -113,6 +117,7 @@ struct KronArgs {
   float* scale;          // [rows]
   float* S_out;          // [K/G] (quant without smoothing: 1)
   uint32_t* colmax;      // [K] (calibration)
+  float* zrows;          // stats: [rows][K] rotated, reordered rows, or nullptr
 };
 
 __device__ __forceinline__ void bfly(float& x, float& y) {
@@ -417,6 +422,17 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
         for (int e = 0; e < 8; ++e) z[s][e] = (w < W8) ? s_row[pp[s][e]] : 0.f;
       }
       if constexpr (MODE == kKStats) {
+        if (a.zrows) {
+          float4* zr = reinterpret_cast<float4*>(a.zrows + static_cast<size_t>(row) * K);
+#pragma unroll
+          for (int s = 0; s < SW; ++s) {
+            const int w = tid + s * kKT;
+            if (w < W8) {
+              zr[2 * w] = make_float4(z[s][0], z[s][1], z[s][2], z[s][3]);
+              zr[2 * w + 1] = make_float4(z[s][4], z[s][5], z[s][6], z[s][7]);
+            }
+          }
+        }
 #pragma unroll
         for (int s = 0; s < SW; ++s) {
           const int w = tid + s * kKT;
@@ -468,6 +484,75 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
   }
 }
 
+// Quantise pass over stored rows: one workgroup per row streams the row the
+// stats pass stored and runs the quantise pass's arithmetic on it (smooth,
+// per-token scale, round, pack). SW = packed words per thread.
+template <int SW>
+__global__ void __launch_bounds__(kKT) kron_quant_rows_kernel(KronArgs a, int K) {
+  __shared__ float s_grp[kMaxKronK / 32];  // inverse group scales
+  __shared__ float s_red[kKT / 64];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const int W8 = K / 8;
+  const int ngroups = K >> a.log2G;
+  const float4* zr = reinterpret_cast<const float4*>(a.zrows + static_cast<size_t>(row) * K);
+  float z[SW][8];
+#pragma unroll
+  for (int s = 0; s < SW; ++s) {
+    const int w = tid + s * kKT;
+    float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
+    if (w < W8) {
+      lo = zr[2 * w];
+      hi = zr[2 * w + 1];
+    }
+    z[s][0] = lo.x; z[s][1] = lo.y; z[s][2] = lo.z; z[s][3] = lo.w;
+    z[s][4] = hi.x; z[s][5] = hi.y; z[s][6] = hi.z; z[s][7] = hi.w;
+  }
+  for (int g = tid; g < ngroups; g += kKT) s_grp[g] = 1.f / a.S_in[g];
+  __syncthreads();
+
+  float r = 0.f;
+#pragma unroll
+  for (int s = 0; s < SW; ++s) {
+    const int w = tid + s * kKT;
+    if (w < W8) {
+      const float inv = s_grp[(8 * w) >> a.log2G];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r = fmaxf(r, fabsf(z[s][e]) * inv);
+    }
+  }
+  r = block_max(r, s_red, tid);
+  const float k7 = r > 0.f ? 7.f / r : 0.f;
+  uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + static_cast<size_t>(row) * (K / 2));
+#pragma unroll
+  for (int s = 0; s < SW; ++s) {
+    const int w = tid + s * kKT;
+    if (w < W8) {
+      const float ks = s_grp[(8 * w) >> a.log2G] * k7;
+      uint32_t mag[8], sgn[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        mag[e] = __float_as_uint(fmaf(fabsf(z[s][e]), ks, kMagic));
+        sgn[e] = __float_as_uint(z[s][e]);
+      }
+      dst[w] = pack8(mag, sgn);
+    }
+  }
+  if (tid == 0) a.scale[row] = r / 7.f;
+}
+
+hipError_t launch_quant_rows(const KronArgs& a, int K, hipStream_t s) {
+  const int sw = (K / 8 + kKT - 1) / kKT;
+  switch (sw) {
+    case 1: hipLaunchKernelGGL(kron_quant_rows_kernel<1>, dim3(a.rows), dim3(kKT), 0, s, a, K); break;
+    case 2: hipLaunchKernelGGL(kron_quant_rows_kernel<2>, dim3(a.rows), dim3(kKT), 0, s, a, K); break;
+    case 3: hipLaunchKernelGGL(kron_quant_rows_kernel<3>, dim3(a.rows), dim3(kKT), 0, s, a, K); break;
+    case 4: hipLaunchKernelGGL(kron_quant_rows_kernel<4>, dim3(a.rows), dim3(kKT), 0, s, a, K); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int M, int LOG2N, int MODE>
 hipError_t launch_kron_mode(const KronArgs& a, int grid, hipStream_t s) {
   hipLaunchKernelGGL((kron_kernel<M, LOG2N, MODE>), dim3(grid), dim3(kKT), 0, s, a);
@@ -507,7 +592,7 @@ int kron_frontend_launches(int flags) { return (flags & 2) ? 1 : 3; }
 
 hipError_t launch_frontend_kron(const uint16_t* X, int M, int K, int G, const int32_t* perm, const uint32_t* dsign,
                                 uint8_t* xq, float* dx, float* S_out, uint32_t* /*sync: unused*/, int flags,
-                                hipStream_t s) {
+                                hipStream_t s, float* zrows) {
   int m = 0, log2n = 0;
   if (!kron_split(K, &m, &log2n)) return hipErrorInvalidValue;
   KronArgs a{};
@@ -528,11 +613,15 @@ hipError_t launch_frontend_kron(const uint16_t* X, int M, int K, int G, const in
   a.part = reinterpret_cast<uint32_t*>(xq);
   const int ngroups = K / G;
   if (a.smooth) {
+    // rows kept only when the rotation runs (without it the quantise pass
+    // reads X itself, as cheap as the stored rows)
+    a.zrows = a.rotate ? zrows : nullptr;
     const int gs = M < kKronRowsWG ? M : kKronRowsWG;
     hipError_t e = dispatch_kron<kKStats>(m, log2n, a, gs, s);
     if (e != hipSuccess) return e;
     e = launch_group_max(a.part, gs, ngroups, S_out, s);
     if (e != hipSuccess) return e;
+    if (a.zrows) return launch_quant_rows(a, K, s);
   }
   return dispatch_kron<kKQuant>(m, log2n, a, M < kKronRowsWG ? M : kKronRowsWG, s);
 }

@@ -37,12 +37,15 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 //          bit2 = always use the three launches.
 //   dsign: signed rotation x D H, K-bit mask (bit j set: channel j negated),
 //          or nullptr for the plain rotation.
+//   zrows: Kronecker K only: room for the M x K fp32 rotated, reordered rows
+//          (the quantise pass then streams them instead of rotating again),
+//          or nullptr.
 hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t* perm,
                            const uint32_t* dsign, uint8_t* xq, float* dx, float* S_out, uint32_t* sync,
-                           int flags, hipStream_t s);
+                           int flags, hipStream_t s, float* zrows = nullptr);
 
 // Launches the front end would use for M rows on the current device (1 or
-// 2; 3 for a Kronecker K with smoothing), -1 for an unsupported K.
+// 3), -1 for an unsupported K.
 int frontend_launches(int M, int K, int flags);
 
 // Offline weight preparation: W [K, N] row-major fp16 -> wq [N][K/2] + dw [N]
@@ -80,7 +83,8 @@ int kron_frontend_launches(int flags);
 hipError_t launch_group_max(const uint32_t* part, int nrows, int ngroups, float* S_out, hipStream_t s);
 
 hipError_t launch_frontend_kron(const uint16_t* X, int M, int K, int G, const int32_t* perm, const uint32_t* dsign,
-                                uint8_t* xq, float* dx, float* S_out, uint32_t* sync, int flags, hipStream_t s);
+                                uint8_t* xq, float* dx, float* S_out, uint32_t* sync, int flags, hipStream_t s,
+                                float* zrows);
 hipError_t launch_weight_prep_kron(const uint16_t* W, int K, int N, const int32_t* perm, const uint32_t* dsign,
                                    uint8_t* wq, float* dw, hipStream_t s);
 hipError_t launch_colmax_kron(const uint16_t* Xc, int T, int K, const uint32_t* dsign, uint32_t* colmax,

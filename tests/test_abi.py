@@ -126,6 +126,12 @@ def test_kron_shapes_accepted_and_rejected():
     for K in (100, 11008, 28 * 32, 24576, 28 * 1024, 12 * 32):
         assert rra.rrs_weight_bytes(K, 8) == 0, K
     assert rra.rrs_workspace_bytes(4, 14336, 4096) == 0   # 4096 does not divide 14336
+    # layout sync | xq | dx | S | rows: a Kronecker K adds the M x K fp32 row area
+    a = lambda n: (n + 255) // 256 * 256
+    M, K, G = 2048, 14336, 128
+    base = rra.rrs_sync_bytes(K, G) + a(M * K // 2) + a(4 * M) + a(4 * K // G)
+    assert rra.rrs_workspace_bytes(M, K, G) == base + a(4 * M * K)
+    assert rra.rrs_workspace_bytes(3, 768, 64) == rra.rrs_sync_bytes(768, 64) + a(3 * 384) + 256 + 256 + a(4 * 3 * 768)
     assert rra.rrs_gemm_form(8, 14336, 128) == rra.RRS_GEMM_TILED
     assert rra.rrs_frontend_passes(8, 14336, 0) == 3
     assert rra.rrs_frontend_passes(8, 14336, rra.RRS_FLAG_NO_SMOOTH) == 1

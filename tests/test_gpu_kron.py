@@ -140,3 +140,60 @@ def test_linear_kron(M, K, N, G):
         q_gpu, ref["fe"]["q"], qw_gpu, ref["wp"]["qw"], ref["fe"]["dx"], ref["fe"]["S"], ref["wp"]["dw"], G)
     gu.log(f"  Y max err/C = {gu.y_error(Yg, ref):.3e}")
     assert np.all(np.abs(Yg - ref["Y"]) <= bound)
+
+
+@pytest.mark.parametrize("M,K,G,signed", [(37, 14336, 128, False), (300, 1536, 64, False), (11, 1792, 64, True)])
+def test_frontend_kron_row_area(M, K, G, signed):
+    """With an rrs_linear-sized workspace the stats pass keeps the rotated,
+    reordered rows in its row area and the quantise pass streams them: the
+    same bits as the form that rotates every row twice, the rows themselves
+    close to the exact ones, and no row area used when xq lies in it."""
+    gu.log(f"[frontend kron rows] M={M} K={K} G={G} signed={signed}")
+    x, _, perm = _case(M, K)
+    X, P = gu.to_dev(x), gu.to_dev(perm)
+    dsign_np = (np.random.default_rng(K + M).integers(0, 2**32, size=K // 32, dtype=np.uint64)
+                .astype(np.uint32)) if signed else None
+    D = gu.to_dev(dsign_np.view(np.int32)) if signed else None
+
+    def run(xq, dx, S, ws):
+        if signed:
+            rra.rrs_frontend_signed(X, G, P, D, xq, dx, S, ws)
+        else:
+            rra.rrs_frontend(X, G, P, xq, dx, S, ws)
+        torch.cuda.synchronize()
+
+    # rotate twice: a workspace of the synchronisation block alone
+    xq_a = torch.empty(M, K // 2, dtype=torch.uint8, device=gu.DEV)
+    dx_a = torch.empty(M, dtype=torch.float32, device=gu.DEV)
+    S_a = torch.empty(K // G, dtype=torch.float32, device=gu.DEV)
+    ws_a = torch.zeros(rra.rrs_sync_bytes(K, G), dtype=torch.uint8, device=gu.DEV)
+    run(xq_a, dx_a, S_a, ws_a)
+
+    # stored rows: a whole rrs_linear workspace, outputs in its own views
+    nbytes = rra.rrs_workspace_bytes(M, K, G)
+    ws_b = torch.zeros(nbytes, dtype=torch.uint8, device=gu.DEV)
+    xq_b, dx_b, S_b = rra.workspace_views(ws_b, M, K, G)
+    run(xq_b, dx_b, S_b, ws_b)
+    row_off = nbytes - (4 * M * K + 255) // 256 * 256
+    rows = ws_b[row_off:].view(torch.float32).view(M, K).cpu().numpy().astype(np.float64)
+
+    assert torch.equal(xq_a, xq_b), "codes differ between the two forms"
+    assert torch.equal(dx_a.view(torch.int32), dx_b.view(torch.int32)), "dx differs between the two forms"
+    assert torch.equal(S_a.view(torch.int32), S_b.view(torch.int32)), "S differs between the two forms"
+
+    fe = oracle.frontend(x, perm, G, d=oracle.signs_from_bits(dsign_np, K)) if signed else oracle.frontend(x, perm, G)
+    gu.compare_codes(oracle.unpack_codes(xq_b.cpu().numpy()), fe["q"], fe["v"], "kron rows codes")
+    gu.rel_close(dx_b.cpu().numpy(), fe["dx"], gu.SCALE_TOL, "kron rows dx")
+    gu.rel_close(S_b.cpu().numpy(), fe["S"], gu.SCALE_TOL, "kron rows S")
+    scale = np.maximum(np.abs(fe["Zp"]).max(axis=1, keepdims=True), 1e-30)
+    err = float((np.abs(rows - fe["Zp"]) / scale).max())
+    gu.log(f"  stored rows: max |row - Zp| / max|Zp row| = {err:.3e}")
+    assert err <= 1e-5
+
+    # xq inside the row area: the library must not keep rows there
+    ws_c = torch.zeros(nbytes, dtype=torch.uint8, device=gu.DEV)
+    xq_c = ws_c[row_off: row_off + M * (K // 2)].view(M, K // 2)
+    dx_c = torch.empty(M, dtype=torch.float32, device=gu.DEV)
+    S_c = torch.empty(K // G, dtype=torch.float32, device=gu.DEV)
+    run(xq_c, dx_c, S_c, ws_c)
+    assert torch.equal(xq_a, xq_c) and torch.equal(dx_a, dx_c) and torch.equal(S_a, S_c)
