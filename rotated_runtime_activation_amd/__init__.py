@@ -10,6 +10,7 @@ every call raises ``RRSLibraryMissing``.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional
 
@@ -92,6 +93,7 @@ def _check(fn: str, status: int) -> None:
 
 
 # ------------------------------------------------------------ size queries
+@functools.lru_cache(maxsize=256)
 def rrs_weight_bytes(K: int, N: int) -> int:
     return int(lib().rrs_weight_bytes(K, N))
 
@@ -143,32 +145,35 @@ def _torch():
     return torch
 
 
-def _stream(stream) -> ctypes.c_void_p:
+def _stream(stream) -> int:
     torch = _torch()
     if stream is None:
         stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    return stream.cuda_stream
 
 
-def _dev(t, dtype, name: str, shape: Optional[tuple] = None, min_numel: int = 0):
+def _dev(t, dtype, name: str, shape: Optional[tuple] = None, min_numel: int = 0) -> int:
+    """Device address of a checked tensor argument. The checks use the
+    cheapest tensor attributes: they run on every call, and for small
+    shapes the host time of a call can exceed its GPU time."""
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != shape:
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
-    if t.numel() * t.element_size() < min_numel:
-        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {min_numel}")
-    return ctypes.c_void_p(t.data_ptr())
+    if min_numel and t.nbytes < min_numel:
+        raise ValueError(f"{name} holds {t.nbytes} bytes, needs {min_numel}")
+    return t.data_ptr()
 
 
 def _nbytes(t) -> int:
-    return t.numel() * t.element_size()
+    return t.nbytes
 
 
 # ----------------------------------------------------------- entry points
