@@ -142,7 +142,9 @@ def test_linear_kron(M, K, N, G):
     assert np.all(np.abs(Yg - ref["Y"]) <= bound)
 
 
-@pytest.mark.parametrize("M,K,G,signed", [(37, 14336, 128, False), (300, 1536, 64, False), (11, 1792, 64, True)])
+@pytest.mark.parametrize("M,K,G,signed", [(37, 14336, 128, False), (300, 1536, 64, False), (11, 1792, 64, True),
+                                          (1, 14336, 256, False), (2, 12288, 4096, False), (257, 10240, 512, True),
+                                          (3, 768, 256, False), (40, 5120, 32, False), (64, 7168, 1024, True)])
 def test_frontend_kron_row_area(M, K, G, signed):
     """With an rrs_linear-sized workspace the stats pass keeps the rotated,
     reordered rows in its row area and the quantise pass streams them: the
