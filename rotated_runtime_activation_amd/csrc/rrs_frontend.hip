@@ -518,12 +518,18 @@ __device__ __forceinline__ void quantise_block(const float (&v)[Cfg<LOG2K>::kE],
 // ----------------------------------------------------------- one-pass kernels
 // Stats and quantise passes of the three-launch front end, the offline weight
 // preparation (columns of W as rows) and the calibration channel maxima.
+// Each wave owns the blocks blockIdx.x * WAVES + wave + i * gridDim.x * WAVES:
+// the stats and quantise passes launch at most as many workgroups as the
+// device holds at once, so a workgroup builds its gather table once and
+// each wave loads its next block while it processes the current one (the
+// other modes launch one block per wave).
 template <int LOG2K, int MODE, bool ROTATE>
 __global__ void __launch_bounds__(Cfg<LOG2K>::kThreads)
 frontend_kernel(FeArgs a) {
   using C = Cfg<LOG2K>;
   constexpr int K = 1 << LOG2K;
   constexpr int E = C::kE, WAVES = C::kWaves;
+  constexpr bool kLoop = MODE == kStats || MODE == kQuant;
 
   __shared__ float s_buf[WAVES][C::kBufFloats];
   __shared__ uint32_t s_tab[C::kB];             // gather table, or channel max
@@ -533,14 +539,14 @@ frontend_kernel(FeArgs a) {
   const int wave = tid / kWave;
   const int lane = tid % kWave;
   const int ngroups = K >> a.log2G;
-  const int blk = blockIdx.x * WAVES + wave;
-  const int row0 = blk * C::kRows;
+  const int stride = gridDim.x * WAVES;
+  int blk = blockIdx.x * WAVES + wave;
 
   // table loads, then the activation rows, both before the set-up
   TableLoads<LOG2K> tl;
   if constexpr (MODE != kColmax) table_loads<LOG2K>(tl, a.perm, tid);
   uint4 w[C::kChunks];
-  if constexpr (MODE != kWeight) load_block<LOG2K>(w, a.src, a.rows, row0, lane);
+  if constexpr (MODE != kWeight) load_block<LOG2K>(w, a.src, a.rows, blk * C::kRows, lane);
   SignLoads<LOG2K> sg;
   if constexpr (ROTATE) sign_loads<LOG2K>(sg, a.dsign, lane);
   __builtin_amdgcn_sched_barrier(0);
@@ -567,7 +573,14 @@ frontend_kernel(FeArgs a) {
   }
   __syncthreads();
 
-  if (row0 < a.rows) {
+  for (; blk * C::kRows < a.rows; blk += stride) {
+    const int row0 = blk * C::kRows;
+    // the wave's next block loads while this one is processed
+    uint4 wn[kLoop ? C::kChunks : 1];
+    const bool more = kLoop && (blk + stride) * C::kRows < a.rows;
+    if constexpr (kLoop) {
+      if (more) load_block<LOG2K>(wn, a.src, a.rows, (blk + stride) * C::kRows, lane);
+    }
     if constexpr (MODE == kWeight) {
       // column `row` of W [K][ldw], channels k0..k0+7
 #pragma unroll
@@ -615,6 +628,13 @@ frontend_kernel(FeArgs a) {
         fold_group_max<LOG2K>(m, s_grp, a.log2G, a.rows, row0, lane);
       else
         quantise_block<LOG2K>(v, m, s_grp, a.log2G, a.codes, a.scale, a.rows, row0, lane);
+    }
+    if constexpr (kLoop) {
+      if (!more) break;
+#pragma unroll
+      for (int i = 0; i < C::kChunks; ++i) w[i] = wn[i];
+    } else {
+      break;
     }
   }
 
@@ -836,28 +856,61 @@ constexpr int pass_grid(int log2K, int rows) {
   return ((rows + per_block - 1) / per_block + waves - 1) / waves;
 }
 
+constexpr int kMaxDevices = 64;
+
+// Workgroups of frontend_kernel<LOG2K, MODE, ROTATE> the current device
+// holds at once (occupancy per CU x CUs), cached per device; -1 if unknown.
 template <int LOG2K, int MODE, bool ROTATE>
-hipError_t launch_mode(const FeArgs& a, hipStream_t s) {
+int pass_capacity() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  int cap = cache[dev].load(std::memory_order_relaxed);
+  if (cap == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, frontend_kernel<LOG2K, MODE, ROTATE>,
+                                                     Cfg<LOG2K>::kThreads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        per_cu <= 0 || cus <= 0) {
+      cap = -1;
+    } else {
+      cap = per_cu * cus;
+    }
+    cache[dev].store(cap, std::memory_order_relaxed);
+  }
+  return cap;
+}
+
+// One pass over `a.rows` rows; the stats and quantise passes take at most
+// one workgroup per resident slot (each wave then loops over its blocks).
+// *grid_out (if given) receives the launched grid.
+template <int LOG2K, int MODE, bool ROTATE>
+hipError_t launch_mode(const FeArgs& a, hipStream_t s, int* grid_out) {
   using C = Cfg<LOG2K>;
   static_assert(pass_grid(LOG2K, 1000) == ((1000 + C::kRows - 1) / C::kRows + C::kWaves - 1) / C::kWaves,
                 "pass_grid follows Cfg");
-  const int grid = pass_grid(LOG2K, a.rows);
+  int grid = pass_grid(LOG2K, a.rows);
+  if constexpr (MODE == kStats || MODE == kQuant) {
+    const int cap = pass_capacity<LOG2K, MODE, ROTATE>();
+    if (cap > 0 && grid > cap) grid = cap;
+  }
+  if (grid_out) *grid_out = grid;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((frontend_kernel<LOG2K, MODE, ROTATE>), dim3(grid), dim3(C::kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int MODE, bool ROTATE>
-hipError_t dispatch_k(int log2K, const FeArgs& a, hipStream_t s) {
+hipError_t dispatch_k(int log2K, const FeArgs& a, hipStream_t s, int* grid_out = nullptr) {
   switch (log2K) {
-    case 6: return launch_mode<6, MODE, ROTATE>(a, s);
-    case 7: return launch_mode<7, MODE, ROTATE>(a, s);
-    case 8: return launch_mode<8, MODE, ROTATE>(a, s);
-    case 9: return launch_mode<9, MODE, ROTATE>(a, s);
-    case 10: return launch_mode<10, MODE, ROTATE>(a, s);
-    case 11: return launch_mode<11, MODE, ROTATE>(a, s);
-    case 12: return launch_mode<12, MODE, ROTATE>(a, s);
-    case 13: return launch_mode<13, MODE, ROTATE>(a, s);
+    case 6: return launch_mode<6, MODE, ROTATE>(a, s, grid_out);
+    case 7: return launch_mode<7, MODE, ROTATE>(a, s, grid_out);
+    case 8: return launch_mode<8, MODE, ROTATE>(a, s, grid_out);
+    case 9: return launch_mode<9, MODE, ROTATE>(a, s, grid_out);
+    case 10: return launch_mode<10, MODE, ROTATE>(a, s, grid_out);
+    case 11: return launch_mode<11, MODE, ROTATE>(a, s, grid_out);
+    case 12: return launch_mode<12, MODE, ROTATE>(a, s, grid_out);
+    case 13: return launch_mode<13, MODE, ROTATE>(a, s, grid_out);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1068,8 +1121,6 @@ __global__ void __launch_bounds__(kRowThreads) rowsplit_kernel(FeArgs a) {
 
 // Workgroups of fused_kernel<LOG2K, ROTATE, R> that the current device holds
 // at once (occupancy per CU x CUs), cached per device; -1 if unknown.
-constexpr int kMaxDevices = 64;
-
 template <int LOG2K, bool ROTATE, int R>
 int fused_capacity() {
   static std::atomic<int> cache[kMaxDevices];
@@ -1227,16 +1278,18 @@ hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t
   if (a.smooth) {
     // one launch when every workgroup fits on the device at once
     if (!(flags & 4) && (rotate ? fused_k<true>(log2K, a, s, &e) : fused_k<false>(log2K, a, s, &e))) return e;
-    // else stats, reduce, quantise. The stats rows sit in the codes buffer,
-    // which the quantise pass overwrites after the reduce has read them:
-    // pass_grid(log2K, M) rows of K/G words take at most M K / 32 bytes of
-    // its M K / 2 (K/G <= K/32 words, and a workgroup covers at least
-    // 3 rows, or 8 blocks of 4096/K rows when K < 4096).
+    // else stats, reduce, quantise. The stats rows (one per workgroup) sit
+    // in the codes buffer, which the quantise pass overwrites after the
+    // reduce has read them: at most pass_grid(log2K, M) rows of K/G words
+    // take at most M K / 32 bytes of its M K / 2 (K/G <= K/32 words, and a
+    // workgroup covers at least 3 rows, or 8 blocks of 4096/K rows when
+    // K < 4096).
     const int ngroups = K / G;
-    const int nrows = pass_grid(log2K, M);
-    if (static_cast<size_t>(nrows) * ngroups * 4 > static_cast<size_t>(M) * (K / 2)) return hipErrorInvalidValue;
+    if (static_cast<size_t>(pass_grid(log2K, M)) * ngroups * 4 > static_cast<size_t>(M) * (K / 2))
+      return hipErrorInvalidValue;
     a.part = reinterpret_cast<uint32_t*>(xq);
-    e = rotate ? dispatch_k<kStats, true>(log2K, a, s) : dispatch_k<kStats, false>(log2K, a, s);
+    int nrows = 0;
+    e = rotate ? dispatch_k<kStats, true>(log2K, a, s, &nrows) : dispatch_k<kStats, false>(log2K, a, s, &nrows);
     if (e != hipSuccess) return e;
     e = launch_group_max(a.part, nrows, ngroups, S_out, s);
     if (e != hipSuccess) return e;

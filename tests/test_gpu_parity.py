@@ -40,9 +40,10 @@ def test_frontend(M, K, G, form):
 
 # Token counts at and past what the one-launch front end holds on chip (two
 # blocks of 4096 elements per wave at K <= 4096, one block of 8192 at
-# K = 8192): past it the same call falls back to three launches.
+# K = 8192): past it the same call falls back to three launches, whose
+# passes loop each wave over several blocks (ragged at the end).
 @pytest.mark.parametrize("M,K,G", [(4096, 4096, 128), (4200, 4096, 128), (8300, 2048, 64),
-                                   (768, 8192, 128), (800, 8192, 256)])
+                                   (768, 8192, 128), (800, 8192, 256), (8192, 4096, 128), (2000, 8192, 64)])
 def test_frontend_capacity(M, K, G):
     passes = rra.rrs_frontend_passes(M, K, 0)
     gu.log(f"[frontend capacity] M={M} K={K} G={G}: {passes} launch(es)")
