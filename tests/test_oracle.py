@@ -245,6 +245,23 @@ def test_quantisation_error_is_bounded_and_rrs_beats_rs_on_spikes():
     assert err_rrs < err_rs
 
 
+def test_rotation_spares_the_victims_of_a_spike():
+    """Non-gating context check of the pages' qualitative claim about spike
+    outliers and the victim effect ([RRS-summary] "Approach"; [RRS-rebuttal]
+    "Novelty"): in a token with a spike, smoothing without rotation rounds
+    most of the other channels to code 0, while the rotation spreads the
+    spike over every channel first. Reported, asserted only as an ordering."""
+    wl = workloads.WORKLOADS["tiny"]
+    x = workloads.runtime_x(wl)
+    perm = oracle.calibrate_perm(workloads.calib_x(wl))
+    spiky = np.abs(x.astype(np.float64)).max(axis=1) >= 0.99 * wl.spike_value
+    assert spiky.any()
+    zeros_rrs = int((oracle.frontend(x, perm, 128)["q"][spiky] == 0).sum())
+    zeros_rs = int((oracle.frontend(x, perm, 128, rotate=False)["q"][spiky] == 0).sum())
+    print(f"zero codes in {int(spiky.sum())} spike tokens: {zeros_rrs} with rotation, {zeros_rs} without")
+    assert zeros_rrs < zeros_rs
+
+
 def test_scale_match_statistic():
     assert oracle.scale_match_u(np.ones(16)) == 1.0
     t = np.zeros(16)
