@@ -208,7 +208,7 @@ def main():
     fe_gbs = fe_bytes / (ms_fe * 1e-3) / 1e9
     gemm_bytes = M * K // 2 + K * N // 2 + 4 * (M + N) + 4 * (K // G) + 4 * M * N
 
-    if rra.rrs_gemm_form(M, K, G) == rra.RRS_GEMM_FEW_TOKENS:
+    if rra.rrs_gemm_form(M, K, N, G) == rra.RRS_GEMM_FEW_TOKENS:
         # few tokens: the weights stream from HBM once; bytes bound the kernel
         gemm_gbs = gemm_bytes / (ms_gemm * 1e-3) / 1e9
         gemm_roofline = {

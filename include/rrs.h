@@ -206,15 +206,18 @@ int rrs_frontend_passes(int M, int K, int flags);
 int rrs_gemm(const uint8_t* xq, const float* dx, const float* S, int M, int K,
              int N, int G, const void* wq, float* Y, hipStream_t s);
 
-/* Which GEMM kernel rrs_gemm and rrs_linear run for M tokens of length K
- * with group size G: RRS_GEMM_TILED (256 x 128 output tiles, every shape)
- * or RRS_GEMM_FEW_TOKENS (one workgroup per 32 output channels streaming
- * the weights once; M <= 64, G >= 64, K >= 2048). Both apply the same
- * arithmetic (group partials exact, rescaled in fp32). A host-side query;
- * RRS_EINVAL for bad arguments. */
+/* Which GEMM kernel rrs_gemm and rrs_linear run for M tokens of length K,
+ * N output channels and group size G: RRS_GEMM_TILED (256 x 128 output
+ * tiles, every shape) or RRS_GEMM_FEW_TOKENS (one workgroup per 32 output
+ * channels and 64 tokens, streaming the weights once per 64 tokens; needs
+ * G >= 64 and K a power of two >= 2048, and serves every M <= 64 and, up
+ * to M = 512, the shapes where it needs fewer rounds of workgroups than
+ * the tiled kernel, weighted by their measured cost per round). Both apply
+ * the same arithmetic (group partials exact, rescaled in fp32). A host-side
+ * query; RRS_EINVAL for bad arguments. */
 #define RRS_GEMM_TILED 1
 #define RRS_GEMM_FEW_TOKENS 2
-int rrs_gemm_form(int M, int K, int G);
+int rrs_gemm_form(int M, int K, int N, int G);
 
 /* The int32 group partials P[t-m0][n-n0][g] = sum_{j in group g} q[t,j]
  * qw[n,j] for m0 <= t < m1, n0 <= n < n1, computed by the main loop of the

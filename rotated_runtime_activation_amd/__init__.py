@@ -63,7 +63,7 @@ def _declare(lib):
         "rrs_gemm": (i, [vp, vp, vp, i, i, i, i, vp, vp, vp]),
         "rrs_gemm_partials": (i, [vp, i, i, i, i, vp, i, i, i, i, vp, vp]),
         "rrs_frontend_passes": (i, [i, i, i]),
-        "rrs_gemm_form": (i, [i, i, i]),
+        "rrs_gemm_form": (i, [i, i, i, i]),
         "rrs_calibrate_perm_signed": (i, [vp, i, i, vp, vp, vp, sz, vp]),
         "rrs_prepare_weights_signed": (i, [vp, i, i, vp, vp, vp, vp]),
         "rrs_linear_signed": (i, [vp, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]),
@@ -122,10 +122,10 @@ RRS_GEMM_TILED = 1
 RRS_GEMM_FEW_TOKENS = 2
 
 
-def rrs_gemm_form(M: int, K: int, G: int) -> int:
-    """GEMM kernel rrs_gemm / rrs_linear run for (M, K, G): RRS_GEMM_TILED or
-    RRS_GEMM_FEW_TOKENS."""
-    n = int(lib().rrs_gemm_form(M, K, G))
+def rrs_gemm_form(M: int, K: int, N: int, G: int) -> int:
+    """GEMM kernel rrs_gemm / rrs_linear run for (M, K, N, G): RRS_GEMM_TILED
+    or RRS_GEMM_FEW_TOKENS."""
+    n = int(lib().rrs_gemm_form(M, K, N, G))
     if n < 0:
         _check("rrs_gemm_form", n)
     return n

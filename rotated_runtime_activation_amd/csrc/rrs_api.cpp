@@ -230,9 +230,9 @@ RRS_API int rrs_gemm(const uint8_t* xq, const float* dx, const float* S, int M, 
   return hip_status(rrs::launch_gemm(xq, dx, S, M, K, N, G, codes, dw, Y, nullptr, 0, 0, 0, 0, s));
 }
 
-RRS_API int rrs_gemm_form(int M, int K, int G) {
-  if (M < 1 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;
-  return rrs::gemm_small_applies(M, K, G) ? RRS_GEMM_FEW_TOKENS : RRS_GEMM_TILED;
+RRS_API int rrs_gemm_form(int M, int K, int N, int G) {
+  if (M < 1 || N < 1 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;
+  return rrs::gemm_small_applies(M, K, N, G) ? RRS_GEMM_FEW_TOKENS : RRS_GEMM_TILED;
 }
 
 RRS_API int rrs_gemm_partials(const uint8_t* xq, int M, int K, int N, int G, const void* wq, int m0,

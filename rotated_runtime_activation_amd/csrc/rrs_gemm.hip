@@ -612,7 +612,7 @@ hipError_t launch_gemm(const uint8_t* xq, const float* dx, const float* S, int M
   a.pm0 = m0; a.pm1 = m1; a.pn0 = n0; a.pn1 = n1;
   if (M == 0 || N == 0) return hipSuccess;
   const bool partials = P != nullptr;
-  if (!partials && gemm_small_applies(M, K, G)) return launch_gemm_small(xq, dx, S, M, K, N, G, wq, dw, Y, s);
+  if (!partials && gemm_small_applies(M, K, N, G)) return launch_gemm_small(xq, dx, S, M, K, N, G, wq, dw, Y, s);
   a.tiles_t = (M + kTT - 1) / kTT;
   a.tiles_n = (N + kTN - 1) / kTN;
   switch (G) {

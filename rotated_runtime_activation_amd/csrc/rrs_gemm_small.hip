@@ -1,5 +1,5 @@
-// Grouped INT4 x INT4 GEMM of the RRS A4W4 linear for few tokens (M <= 64,
-// decode-shaped calls), on gfx950.
+// Grouped INT4 x INT4 GEMM of the RRS A4W4 linear for few tokens
+// (decode-shaped calls), on gfx950.
 //
 // Same arithmetic as the tiled kernel (Y[t, n] = (1/K) dx[t] dw[n]
 // sum_g S[g] P_g[t, n], group scales applied to each group's exact integer
@@ -8,21 +8,25 @@
 // case where the packed weights are the only large operand and the run time
 // is the time to stream them from HBM once.
 //
-// One workgroup owns 32 output channels and every token (one 32 x 32
-// accumulator block per 32 tokens, v_mfma_f32_32x32x64_f8f6f4 on codes
+// One workgroup owns 32 output channels and a slice of up to 64 tokens
+// (grid y walks the slices; one 32 x 32 accumulator block per 32 tokens,
+// v_mfma_f32_32x32x64_f8f6f4 on codes
 // widened to exact fp8 subnormals as in the tiled kernel). Its 8 waves
 // split K into equal runs of k-steps (64 codes); each wave rescales its
 // accumulator when it enters a new group, makes its sum absolute at the end
 // (times the scale of its last group), and the 8 sums are added in LDS in a
-// fixed order. A group cut between two waves is thus scaled in two exact
-// integer pieces: the same sum up to one fp32 rounding per piece.
+// fixed order. Runs and groups are powers of two, so either every run holds
+// whole groups or every group holds whole runs; in the second case the
+// runs' sums are exact integer pieces of one group partial, which are added
+// exactly before the group's scale is applied once.
 //
 // Loads: a wave reads its operands a round (4 k-steps, one 128-byte line of
 // every row) at a time with whole-line coalesced loads into registers, two
 // rounds ahead; at its turn a round goes through a wave-private LDS buffer
 // (row-major, 16-byte chunks XOR-swizzled by row) that turns it into MFMA
-// fragments. With N / 32 workgroups (256 at N = 8192) every CU streams its
-// own slice of the weights.
+// fragments. With N / 32 workgroups per token slice (256 at N = 8192) every
+// CU streams its own slice of the weights; further token slices stream them
+// again (from the Infinity Cache when they fit there).
 
 #include <type_traits>
 
@@ -38,6 +42,7 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTN = 32;      // output channels per workgroup
+constexpr int kSmallMaxTokens = 512;  // token count past which the tiled kernel always serves
 constexpr int kRound = 4;    // k-steps per round (128 bytes of a row)
 constexpr int kRows = 128;   // bytes of a row per round
 constexpr float kUnit = 262144.0f;  // 2^18: one integer product in accumulator units
@@ -84,6 +89,12 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n0 = blockIdx.x * kTN;
   const int Kb = a.K / 2;
+  // this workgroup's token slice: rows t0 .. t0 + Mt - 1 of xq, dx and Y
+  const int t0 = blockIdx.y * 64;
+  const int Mt = min(64, a.M - t0);
+  const uint8_t* xq = a.xq + static_cast<size_t>(t0) * Kb;
+  const float* dx = a.dx + t0;
+  float* Y = a.Y + static_cast<size_t>(t0) * a.N;
   const int ngroups = a.K >> a.log2G;
   const int log2spg = a.log2G - 6;
   const int kspg = 1 << log2spg;      // k-steps per group (G >= 64)
@@ -101,7 +112,7 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
     wsrc[i] = a.wq + static_cast<size_t>(min(n0 + 8 * i + lr, a.N - 1)) * Kb + ks0 * 32 + lc * 16;
 #pragma unroll
   for (int i = 0; i < kXL; ++i)
-    xsrc[i] = a.xq + static_cast<size_t>(min(8 * i + lr, a.M - 1)) * Kb + ks0 * 32 + lc * 16;
+    xsrc[i] = xq + static_cast<size_t>(min(8 * i + lr, Mt - 1)) * Kb + ks0 * 32 + lc * 16;
 
   uint8_t* buf = s_buf[wave];
   v4u rw[NR][kWL], rx[NR][kXL];
@@ -126,7 +137,7 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
   const float base = kUnit / static_cast<float>(a.K);
   for (int g = tid; g < ngroups; g += kThreads) s_rat[g] = g > 0 ? a.S[g - 1] / a.S[g] : 1.f;
   if (tid < 64) {
-    s_dx[tid] = tid < a.M ? a.dx[tid] * base : 0.f;
+    s_dx[tid] = tid < Mt ? dx[tid] * base : 0.f;
   } else if (tid < 64 + kTN) {
     const int n = n0 + tid - 64;
     s_dw[tid - 64] = n < a.N ? a.dw[n] : 0.f;
@@ -183,9 +194,14 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
     }
   }
 
-  // absolute sums, times the scale of the group of the wave's last k-step,
-  // into the wave's own buffer (its fragment reads are done: in-order LDS)
-  const float sl = s_last[wave];
+  // When a group spans several waves (kpw < kspg), each wave's run lies in
+  // one group and its sum is an exact integer piece of that group's
+  // partial: the pieces are added exactly first and the group's scale is
+  // applied once. Otherwise every wave holds whole groups: its sum is made
+  // absolute with the scale of its last group.
+  const bool pieces = kpw < kspg;
+  const int wpg = pieces ? kspg / kpw : 1;  // waves per group
+  const float sl = pieces ? 1.f : s_last[wave];
   float* part = reinterpret_cast<float*>(buf);
 #pragma unroll
   for (int j = 0; j < TJ; ++j)
@@ -199,9 +215,25 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
   // Register e of lane l in block j holds token 32 j + l % 32, channel
   // 8 (e / 4) + 4 (l / 32) + e % 4.
   for (int idx = tid; idx < TJ * 16 * 64; idx += kThreads) {
-    float v = 0.f;
+    float pv[kWaves];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += reinterpret_cast<const float*>(s_buf[w])[idx];
+    for (int w = 0; w < kWaves; ++w) pv[w] = reinterpret_cast<const float*>(s_buf[w])[idx];
+    float v = 0.f;
+    if (!pieces) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += pv[w];
+    } else {
+      // p collects one group's exact partial from its waves' pieces
+      float p = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        p += pv[w];
+        if (((w + 1) & (wpg - 1)) == 0) {
+          v += p * s_last[w + 1 - wpg];
+          p = 0.f;
+        }
+      }
+    }
     const int j = idx >> 10, e = (idx >> 6) & 15, l = idx & 63;
     const int t = 32 * j + (l & 31);
     const int nl = 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
@@ -212,21 +244,35 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
   for (int id = tid; id < TJ * 32 * kTN; id += kThreads) {
     const int t = id / kTN, nl = id % kTN;
     const int n = n0 + nl;
-    if (t >= a.M || n >= a.N) continue;
-    a.Y[static_cast<size_t>(t) * a.N + n] = s_out[t * (kTN + 1) + nl] * s_dx[t] * s_dw[nl];
+    if (t >= Mt || n >= a.N) continue;
+    Y[static_cast<size_t>(t) * a.N + n] = s_out[t * (kTN + 1) + nl] * s_dx[t] * s_dw[nl];
   }
 }
 
 }  // namespace
 
-// K a power of two >= 2048: every wave gets a whole number of rounds
-bool gemm_small_applies(int M, int K, int G) {
-  return M >= 1 && M <= 64 && G >= 64 && K >= 2048 && (K & (K - 1)) == 0;
+// K a power of two >= 2048: every wave gets a whole number of rounds. Up to
+// 64 tokens this kernel always serves. Past that it serves while it needs
+// fewer rounds of resident workgroups (one per CU, 256 CUs) than the tiled
+// kernel, weighted by what one round of each costs at this K (measured with
+// both kernels alone at M = 65 .. 512: a tiled round costs about 4.8 times
+// a few-token round at K = 8192, 3.6 times at K = 4096; 3 is assumed at
+// K = 2048).
+bool gemm_small_applies(int M, int K, int N, int G) {
+  if (M < 1 || N < 1 || G < 64 || K < 2048 || (K & (K - 1)) != 0) return false;
+  if (M <= 64) return true;
+  if (M > kSmallMaxTokens) return false;
+  constexpr long kCUs = 256;
+  const long ws = static_cast<long>((N + kTN - 1) / kTN) * ((M + 63) / 64);
+  const long wt = static_cast<long>((N + 255) / 256) * ((M + 127) / 128);
+  const long rs = (ws + kCUs - 1) / kCUs, rt = (wt + kCUs - 1) / kCUs;
+  const long ratio10 = K >= 8192 ? 48 : K >= 4096 ? 36 : 30;  // tenths
+  return rs * 10 < rt * ratio10;
 }
 
 hipError_t launch_gemm_small(const uint8_t* xq, const float* dx, const float* S, int M, int K, int N, int G,
                              const uint8_t* wq, const float* dw, float* Y, hipStream_t s) {
-  if (!gemm_small_applies(M, K, G)) return hipErrorInvalidValue;
+  if (!gemm_small_applies(M, K, N, G)) return hipErrorInvalidValue;
   SmallArgs a{};
   a.xq = xq;
   a.dx = dx;
@@ -238,7 +284,7 @@ hipError_t launch_gemm_small(const uint8_t* xq, const float* dx, const float* S,
   a.N = N;
   a.K = K;
   a.log2G = __builtin_ctz(static_cast<unsigned>(G));
-  const dim3 grid((N + kTN - 1) / kTN);
+  const dim3 grid((N + kTN - 1) / kTN, (M + 63) / 64);
   const int rounds = (a.K >> 6) / kWaves / kRound;  // 1, 2, 4 for K = 2048, 4096, 8192
   const int spg = G >> 6;
   const int ks = spg < kRound ? spg : kRound;

@@ -67,9 +67,9 @@ hipError_t launch_gemm(const uint8_t* xq, const float* dx, const float* S, int M
                        int N, int G, const uint8_t* wq, const float* dw, float* Y, int32_t* P,
                        int m0, int m1, int n0, int n1, hipStream_t s);
 
-// Few-token form of the same product (Y only): whether it serves (M, G),
-// and its launch. launch_gemm dispatches to it by itself.
-bool gemm_small_applies(int M, int K, int G);
+// Few-token form of the same product (Y only): whether it serves
+// (M, K, N, G), and its launch. launch_gemm dispatches to it by itself.
+bool gemm_small_applies(int M, int K, int N, int G);
 hipError_t launch_gemm_small(const uint8_t* xq, const float* dx, const float* S, int M, int K, int N, int G,
                              const uint8_t* wq, const float* dw, float* Y, hipStream_t s);
 

@@ -132,23 +132,38 @@ def test_kron_shapes_accepted_and_rejected():
     base = rra.rrs_sync_bytes(K, G) + a(M * K // 2) + a(4 * M) + a(4 * K // G)
     assert rra.rrs_workspace_bytes(M, K, G) == base + a(4 * M * K)
     assert rra.rrs_workspace_bytes(3, 768, 64) == rra.rrs_sync_bytes(768, 64) + a(3 * 384) + 256 + 256 + a(4 * 3 * 768)
-    assert rra.rrs_gemm_form(8, 14336, 128) == rra.RRS_GEMM_TILED
+    assert rra.rrs_gemm_form(8, 14336, 4096, 128) == rra.RRS_GEMM_TILED
     assert rra.rrs_frontend_passes(8, 14336, 0) == 3
     assert rra.rrs_frontend_passes(8, 14336, rra.RRS_FLAG_NO_SMOOTH) == 1
 
 
 def test_gemm_form():
-    """Few-token kernel for M <= 64, G >= 64, K >= 2048; tiled otherwise."""
-    assert rra.rrs_gemm_form(64, 8192, 128) == rra.RRS_GEMM_FEW_TOKENS
-    assert rra.rrs_gemm_form(1, 2048, 64) == rra.RRS_GEMM_FEW_TOKENS
-    assert rra.rrs_gemm_form(1, 8192, 8192) == rra.RRS_GEMM_FEW_TOKENS
-    assert rra.rrs_gemm_form(65, 8192, 128) == rra.RRS_GEMM_TILED
-    assert rra.rrs_gemm_form(64, 1024, 128) == rra.RRS_GEMM_TILED
-    assert rra.rrs_gemm_form(64, 4096, 32) == rra.RRS_GEMM_TILED
+    """Few-token kernel for M <= 64 (G >= 64, K a power of two >= 2048); up to
+    M = 512 while its rounds of 256 workgroups (N/32 x M/64 of them) stay
+    below the tiled kernel's (N/256 x M/128) times the per-round cost ratio
+    (4.8 at K = 8192, 3.6 at 4096, 3 at 2048); tiled otherwise."""
+    F, T = rra.RRS_GEMM_FEW_TOKENS, rra.RRS_GEMM_TILED
+    assert rra.rrs_gemm_form(64, 8192, 8192, 128) == F
+    assert rra.rrs_gemm_form(1, 2048, 1, 64) == F
+    assert rra.rrs_gemm_form(1, 8192, 4096, 8192) == F
+    assert rra.rrs_gemm_form(64, 1024, 4096, 128) == T      # K < 2048
+    assert rra.rrs_gemm_form(64, 4096, 4096, 32) == T       # G < 64
+    assert rra.rrs_gemm_form(64, 14336, 4096, 128) == T     # K not a power of two
+    # K = N = 8192: 2 .. 4 rounds against one tiled round (x 4.8); 5 is too many
+    assert rra.rrs_gemm_form(65, 8192, 8192, 128) == F
+    assert rra.rrs_gemm_form(256, 8192, 8192, 128) == F
+    assert rra.rrs_gemm_form(257, 8192, 8192, 128) == T
+    # K = N = 4096: up to 3 rounds (x 3.6)
+    assert rra.rrs_gemm_form(384, 4096, 4096, 128) == F
+    assert rra.rrs_gemm_form(385, 4096, 4096, 128) == T
+    # gate/up-sized N: 4 rounds already at M = 65
+    assert rra.rrs_gemm_form(65, 4096, 14336, 128) == T
+    assert rra.rrs_gemm_form(513, 8192, 64, 128) == T       # past 512 tokens
     L = rra.lib()
-    assert L.rrs_gemm_form(0, 4096, 128) == rra.RRS_EINVAL
-    assert L.rrs_gemm_form(4, 4096, 8192) == rra.RRS_EINVAL
-    assert L.rrs_gemm_form(4, 100, 32) == rra.RRS_EINVAL
+    assert L.rrs_gemm_form(0, 4096, 64, 128) == rra.RRS_EINVAL
+    assert L.rrs_gemm_form(4, 4096, 64, 8192) == rra.RRS_EINVAL
+    assert L.rrs_gemm_form(4, 100, 64, 32) == rra.RRS_EINVAL
+    assert L.rrs_gemm_form(4, 4096, 0, 128) == rra.RRS_EINVAL
 
 
 def test_gemm_and_partials_reject():

@@ -160,6 +160,8 @@ GEMM_SHAPES = [
     (257, 129, 1024, 256), (128, 128, 4096, 4096), (33, 300, 2048, 128), (5, 17, 8192, 512),
     (1, 4096, 8192, 128), (32, 40, 128, 64), (48, 70, 1024, 256), (64, 33, 4096, 4096),
     (17, 257, 512, 64),
+    # few-token kernel over several 64-token slices (grid y), ragged last slice
+    (65, 260, 8192, 128), (200, 33, 2048, 64), (256, 300, 4096, 256), (500, 64, 4096, 128),
 ]
 
 
@@ -190,7 +192,7 @@ def test_gemm_partials_exact(M, N, K, G):
 
 @pytest.mark.parametrize("M,N,K,G", GEMM_SHAPES)
 def test_gemm_output(M, N, K, G):
-    gu.log(f"[gemm Y] M={M} N={N} K={K} G={G}")
+    gu.log(f"[gemm Y] M={M} N={N} K={K} G={G} form={rra.rrs_gemm_form(M, K, N, G)}")
     q, qw = _random_codes(M * 3 + N + K, M, N, K)
     g = np.random.default_rng(K + M)
     dx = (g.random(M) + 0.1).astype(np.float32)

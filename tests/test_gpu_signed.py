@@ -111,7 +111,7 @@ def test_calibrate_perm_signed(T, K):
 @pytest.mark.parametrize("M,K,N,G", [(16, 4096, 256, 128), (3, 8192, 129, 128), (130, 1024, 260, 64),
                                      (64, 8192, 96, 256)])
 def test_linear_signed(M, K, N, G):
-    gu.log(f"[linear signed] M={M} K={K} N={N} G={G} form={rra.rrs_gemm_form(M, K, G)}")
+    gu.log(f"[linear signed] M={M} K={K} N={N} G={G} form={rra.rrs_gemm_form(M, K, N, G)}")
     x, w, perm, bits, d = _case(M, K, N)
     ref = oracle.rrs_linear(x, w, perm, G, d)
     db = _dev_bits(bits)
