@@ -77,7 +77,8 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
   constexpr int kXL = 4 * TJ;       // X loads per lane per round
   constexpr int kBuf = (32 + 32 * TJ) * kRows;  // round buffer bytes per wave
   static_assert(TJ * 16 * 64 * 4 <= kBuf, "a wave's sums fit its round buffer");
-  __shared__ float s_rat[(1 << kMaxLog2K) / 64];
+  static_assert(kMaxKronK >= (1 << kMaxLog2K), "group ratio table sized by the largest K");
+  __shared__ float s_rat[kMaxKronK / 64];
   __shared__ float s_dx[64];         // dx[t] 2^18 / K (0 past M)
   __shared__ float s_dw[kTN];        // dw of the workgroup's channels (0 past N)
   __shared__ float s_last[kWaves];   // scale of each wave's last group
@@ -251,15 +252,21 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
 
 }  // namespace
 
-// K a power of two >= 2048: every wave gets a whole number of rounds. Up to
-// 64 tokens this kernel always serves. Past that it serves while it needs
+// K a multiple of 2048 (a power of two, or m 2^k with the Kronecker
+// rotation): every wave gets a whole number of rounds. Its run and the
+// group must nest (one a multiple of the other), so that no group is cut
+// part-way into a wave. Up to 64 tokens this kernel then always serves. Past that it serves while it needs
 // fewer rounds of resident workgroups (one per CU, 256 CUs) than the tiled
 // kernel, weighted by what one round of each costs at this K (measured with
 // both kernels alone at M = 65 .. 512: a tiled round costs about 4.8 times
 // a few-token round at K = 8192, 3.6 times at K = 4096; 3 is assumed at
 // K = 2048).
 bool gemm_small_applies(int M, int K, int N, int G) {
-  if (M < 1 || N < 1 || G < 64 || K < 2048 || (K & (K - 1)) != 0) return false;
+  if (M < 1 || N < 1 || G < 64 || (G & (G - 1)) != 0 || K < 2048 || K % 2048 != 0 || K > kMaxKronK ||
+      K % G != 0)
+    return false;
+  const int kpw = K / 64 / kWaves, kspg = G / 64;  // k-steps per wave, per group
+  if (kpw % kspg != 0 && kspg % kpw != 0) return false;
   if (M <= 64) return true;
   if (M > kSmallMaxTokens) return false;
   constexpr long kCUs = 256;
@@ -285,7 +292,7 @@ hipError_t launch_gemm_small(const uint8_t* xq, const float* dx, const float* S,
   a.K = K;
   a.log2G = __builtin_ctz(static_cast<unsigned>(G));
   const dim3 grid((N + kTN - 1) / kTN, (M + 63) / 64);
-  const int rounds = (a.K >> 6) / kWaves / kRound;  // 1, 2, 4 for K = 2048, 4096, 8192
+  const int rounds = (a.K >> 6) / kWaves / kRound;  // 1, 2, 4 for K = 2048, 4096, 8192; 7 for 14336
   const int spg = G >> 6;
   const int ks = spg < kRound ? spg : kRound;
   // instantiations: TJ in {1, 2}, NR in {1, 2}, KS in {1, 2, 4}
@@ -298,7 +305,7 @@ hipError_t launch_gemm_small(const uint8_t* xq, const float* dx, const float* S,
     }
   };
   auto by_rounds = [&](auto tj) {
-    if (rounds == 1)
+    if (rounds % 2 != 0)  // NR divides the round count
       go(tj, std::integral_constant<int, 1>{});
     else
       go(tj, std::integral_constant<int, 2>{});

@@ -132,13 +132,15 @@ def test_kron_shapes_accepted_and_rejected():
     base = rra.rrs_sync_bytes(K, G) + a(M * K // 2) + a(4 * M) + a(4 * K // G)
     assert rra.rrs_workspace_bytes(M, K, G) == base + a(4 * M * K)
     assert rra.rrs_workspace_bytes(3, 768, 64) == rra.rrs_sync_bytes(768, 64) + a(3 * 384) + 256 + 256 + a(4 * 3 * 768)
-    assert rra.rrs_gemm_form(8, 14336, 4096, 128) == rra.RRS_GEMM_TILED
+    assert rra.rrs_gemm_form(8, 14336, 4096, 128) == rra.RRS_GEMM_FEW_TOKENS
+    assert rra.rrs_gemm_form(8, 14336, 4096, 2048) == rra.RRS_GEMM_TILED
     assert rra.rrs_frontend_passes(8, 14336, 0) == 3
     assert rra.rrs_frontend_passes(8, 14336, rra.RRS_FLAG_NO_SMOOTH) == 1
 
 
 def test_gemm_form():
-    """Few-token kernel for M <= 64 (G >= 64, K a power of two >= 2048); up to
+    """Few-token kernel for M <= 64 (G >= 64, K a multiple of 2048, groups
+    nested in the waves' runs of K/8); up to
     M = 512 while its rounds of 256 workgroups (N/32 x M/64 of them) stay
     below the tiled kernel's (N/256 x M/128) times the per-round cost ratio
     (4.8 at K = 8192, 3.6 at 4096, 3 at 2048); tiled otherwise."""
@@ -148,7 +150,14 @@ def test_gemm_form():
     assert rra.rrs_gemm_form(1, 8192, 4096, 8192) == F
     assert rra.rrs_gemm_form(64, 1024, 4096, 128) == T      # K < 2048
     assert rra.rrs_gemm_form(64, 4096, 4096, 32) == T       # G < 64
-    assert rra.rrs_gemm_form(64, 14336, 4096, 128) == T     # K not a power of two
+    # K = m 2^k: a multiple of 2048 with groups nested in the waves' runs of K/8
+    assert rra.rrs_gemm_form(64, 14336, 4096, 128) == F     # runs of 1792 codes, groups of 128
+    assert rra.rrs_gemm_form(64, 14336, 4096, 256) == F
+    assert rra.rrs_gemm_form(64, 14336, 4096, 512) == T     # 512 does not divide 1792
+    assert rra.rrs_gemm_form(64, 12288, 4096, 512) == F     # runs of 1536
+    assert rra.rrs_gemm_form(64, 10240, 4096, 64) == F
+    assert rra.rrs_gemm_form(64, 3072, 4096, 64) == T       # not a multiple of 2048
+    assert rra.rrs_gemm_form(64, 5120, 4096, 64) == T
     # K = N = 8192: 2 .. 4 rounds against one tiled round (x 4.8); 5 is too many
     assert rra.rrs_gemm_form(65, 8192, 8192, 128) == F
     assert rra.rrs_gemm_form(256, 8192, 8192, 128) == F

@@ -95,9 +95,12 @@ def test_calibrate_perm_kron(T, K):
 
 
 @pytest.mark.parametrize("M,N,K,G", [(33, 130, 14336, 2048), (130, 64, 1792, 128), (5, 260, 12288, 32),
-                                     (64, 40, 14336, 1024)])
+                                     (64, 40, 14336, 1024),
+                                     # few-token kernel at K = m 2^k (odd and even round counts)
+                                     (64, 130, 14336, 128), (1, 33, 14336, 256), (40, 96, 12288, 512),
+                                     (100, 70, 10240, 64), (3, 64, 6144, 128)])
 def test_gemm_kron(M, N, K, G):
-    gu.log(f"[gemm kron] M={M} N={N} K={K} G={G} groups={K // G}")
+    gu.log(f"[gemm kron] M={M} N={N} K={K} G={G} groups={K // G} form={rra.rrs_gemm_form(M, K, N, G)}")
     g = np.random.default_rng(M + N + K)
     q = g.integers(-7, 8, size=(M, K)).astype(np.int8)
     qw = g.integers(-7, 8, size=(N, K)).astype(np.int8)
