@@ -70,7 +70,8 @@ __device__ __forceinline__ int swz(int r, int c) { return r * kRows + ((c ^ (r &
 
 // TJ: 32-token blocks (1 for M <= 32, 2 for M <= 64); NR: rounds of loads
 // in flight (1 or 2; divides the wave's round count); KS: min(k-steps per
-// group, kRound), the spacing of possible group starts inside a round.
+// group, kRound), the spacing of possible group starts inside a round, or 0
+// for G = 32 (two groups in every k-step).
 template <int TJ, int NR, int KS>
 __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
   constexpr int kWL = 4;            // W loads per lane per round (32 rows / 8)
@@ -78,7 +79,7 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
   constexpr int kBuf = (32 + 32 * TJ) * kRows;  // round buffer bytes per wave
   static_assert(TJ * 16 * 64 * 4 <= kBuf, "a wave's sums fit its round buffer");
   static_assert(kMaxKronK >= (1 << kMaxLog2K), "group ratio table sized by the largest K");
-  __shared__ float s_rat[kMaxKronK / 64];
+  __shared__ float s_rat[kMaxKronK / 32];
   __shared__ float s_dx[64];         // dx[t] 2^18 / K (0 past M)
   __shared__ float s_dw[kTN];        // dw of the workgroup's channels (0 past N)
   __shared__ float s_last[kWaves];   // scale of each wave's last group
@@ -97,8 +98,9 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
   const float* dx = a.dx + t0;
   float* Y = a.Y + static_cast<size_t>(t0) * a.N;
   const int ngroups = a.K >> a.log2G;
-  const int log2spg = a.log2G - 6;
-  const int kspg = 1 << log2spg;      // k-steps per group (G >= 64)
+  // k-steps per group for G >= 64 (KS = 0 is G = 32: two groups per k-step)
+  const int log2spg = KS == 0 ? 0 : a.log2G - 6;
+  const int kspg = 1 << log2spg;
   const int kpw = (a.K >> 6) / kWaves;  // k-steps per wave (a multiple of kRound)
   const int ks0 = wave * kpw;
   const int rounds = kpw / kRound;
@@ -144,7 +146,7 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
     s_dw[tid - 64] = n < a.N ? a.dw[n] : 0.f;
   } else if (tid < 64 + kTN + kWaves) {
     const int w = tid - 64 - kTN;
-    s_last[w] = a.S[(w * kpw + kpw - 1) >> log2spg];
+    s_last[w] = a.S[(((w + 1) * kpw) * 64 - 1) >> a.log2G];  // group of the wave's last code
   }
   __syncthreads();
 
@@ -177,19 +179,41 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
         // u % KS == 0; the multiply there is unconditional (by 1 when no
         // group starts, and at the wave's first k-step, whose sum so far is
         // empty).
-        if (u % KS == 0) {
-          const int kg = ks0 + ks;
-          const float rg = s_rat[kg >> log2spg];
-          const float f = (ks > 0 && (kg & (kspg - 1)) == 0) ? rg : 1.f;
-#pragma unroll
-          for (int j = 0; j < TJ; ++j) acc[j] *= f;
-        }
         const int c = 2 * u + (lane >> 5);
         const v8i fw = widen(*reinterpret_cast<const v4u*>(buf + swz(lane & 31, c)));
+        if constexpr (KS == 0) {
+          // G = 32: lanes 0-31 carry codes 0-31 of the k-step (group 2 kg)
+          // and lanes 32-63 codes 32-63 (group 2 kg + 1), for both operands.
+          // Two MFMAs, each with the other lane half of the weights zeroed,
+          // and the rescale into the second group between them.
+          const int kg = ks0 + ks;
+          const float f0 = ks > 0 ? s_rat[2 * kg] : 1.f, f1 = s_rat[2 * kg + 1];
+          const bool lo = lane < 32;
+          const v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
+          const v8i fw0 = lo ? fw : z, fw1 = lo ? z : fw;
+          v8i fx[TJ];
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const v8i fx = widen(*reinterpret_cast<const v4u*>(buf + swz(32 + 32 * j + (lane & 31), c)));
-          acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw, fx, acc[j], 0, 0, 0, 0, 0, 0);
+          for (int j = 0; j < TJ; ++j) fx[j] = widen(*reinterpret_cast<const v4u*>(buf + swz(32 + 32 * j + (lane & 31), c)));
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) {
+            acc[j] *= f0;
+            acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw0, fx[j], acc[j], 0, 0, 0, 0, 0, 0);
+            acc[j] *= f1;
+            acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw1, fx[j], acc[j], 0, 0, 0, 0, 0, 0);
+          }
+        } else {
+          if (u % KS == 0) {
+            const int kg = ks0 + ks;
+            const float rg = s_rat[kg >> log2spg];
+            const float f = (ks > 0 && (kg & (kspg - 1)) == 0) ? rg : 1.f;
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) acc[j] *= f;
+          }
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) {
+            const v8i fx = widen(*reinterpret_cast<const v4u*>(buf + swz(32 + 32 * j + (lane & 31), c)));
+            acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw, fx, acc[j], 0, 0, 0, 0, 0, 0);
+          }
         }
       }
     }
@@ -262,10 +286,10 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
 // a few-token round at K = 8192, 3.6 times at K = 4096; 3 is assumed at
 // K = 2048).
 bool gemm_small_applies(int M, int K, int N, int G) {
-  if (M < 1 || N < 1 || G < 64 || (G & (G - 1)) != 0 || K < 2048 || K % 2048 != 0 || K > kMaxKronK ||
+  if (M < 1 || N < 1 || G < 32 || (G & (G - 1)) != 0 || K < 2048 || K % 2048 != 0 || K > kMaxKronK ||
       K % G != 0)
     return false;
-  const int kpw = K / 64 / kWaves, kspg = G / 64;  // k-steps per wave, per group
+  const int kpw = K / 64 / kWaves, kspg = G >= 64 ? G / 64 : 1;  // k-steps per wave, per group
   if (kpw % kspg != 0 && kspg % kpw != 0) return false;
   if (M <= 64) return true;
   if (M > kSmallMaxTokens) return false;
@@ -294,11 +318,12 @@ hipError_t launch_gemm_small(const uint8_t* xq, const float* dx, const float* S,
   const dim3 grid((N + kTN - 1) / kTN, (M + 63) / 64);
   const int rounds = (a.K >> 6) / kWaves / kRound;  // 1, 2, 4 for K = 2048, 4096, 8192; 7 for 14336
   const int spg = G >> 6;
-  const int ks = spg < kRound ? spg : kRound;
-  // instantiations: TJ in {1, 2}, NR in {1, 2}, KS in {1, 2, 4}
+  const int ks = G == 32 ? 0 : spg < kRound ? spg : kRound;
+  // instantiations: TJ in {1, 2}, NR in {1, 2}, KS in {0 (G = 32), 1, 2, 4}
   auto go = [&](auto tj, auto nr) {
     constexpr int TJ = decltype(tj)::value, NR = decltype(nr)::value;
     switch (ks) {
+      case 0: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 0>), grid, dim3(kThreads), 0, s, a); break;
       case 1: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 1>), grid, dim3(kThreads), 0, s, a); break;
       case 2: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 2>), grid, dim3(kThreads), 0, s, a); break;
       default: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, kRound>), grid, dim3(kThreads), 0, s, a); break;

@@ -139,8 +139,8 @@ def test_kron_shapes_accepted_and_rejected():
 
 
 def test_gemm_form():
-    """Few-token kernel for M <= 64 (G >= 64, K a multiple of 2048, groups
-    nested in the waves' runs of K/8); up to
+    """Few-token kernel for M <= 64 (K a multiple of 2048, groups nested in
+    the waves' runs of K/8); up to
     M = 512 while its rounds of 256 workgroups (N/32 x M/64 of them) stay
     below the tiled kernel's (N/256 x M/128) times the per-round cost ratio
     (4.8 at K = 8192, 3.6 at 4096, 3 at 2048); tiled otherwise."""
@@ -149,7 +149,7 @@ def test_gemm_form():
     assert rra.rrs_gemm_form(1, 2048, 1, 64) == F
     assert rra.rrs_gemm_form(1, 8192, 4096, 8192) == F
     assert rra.rrs_gemm_form(64, 1024, 4096, 128) == T      # K < 2048
-    assert rra.rrs_gemm_form(64, 4096, 4096, 32) == T       # G < 64
+    assert rra.rrs_gemm_form(64, 4096, 4096, 32) == F       # G = 32: two groups per k-step
     # K = m 2^k: a multiple of 2048 with groups nested in the waves' runs of K/8
     assert rra.rrs_gemm_form(64, 14336, 4096, 128) == F     # runs of 1792 codes, groups of 128
     assert rra.rrs_gemm_form(64, 14336, 4096, 256) == F

@@ -162,6 +162,8 @@ GEMM_SHAPES = [
     (17, 257, 512, 64),
     # few-token kernel over several 64-token slices (grid y), ragged last slice
     (65, 260, 8192, 128), (200, 33, 2048, 64), (256, 300, 4096, 256), (500, 64, 4096, 128),
+    # few-token kernel at G = 32 (two groups per k-step)
+    (64, 260, 4096, 32), (130, 64, 8192, 32), (1, 33, 2048, 32),
 ]
 
 
