@@ -166,12 +166,14 @@ int rrs_linear_signed(const void* X_fp16, int M, int K, int N, int G,
  * device at once. That form keeps the per-workgroup maxima in xq, which its
  * last launch then overwrites with the codes.
  *
- * For K = m 2^k with smoothing and rotation, a `ws` of at least
+ * For K = m 2^k with smoothing, up to 256 rows take a one-launch form as
+ * well (one workgroup per row, the same grid-wide wait). With more rows, or
+ * RRS_FLAG_TWO_PASS, and the rotation on, a `ws` of at least
  * rrs_workspace_bytes(M, K, G) bytes is taken as an rrs_linear workspace:
  * its row area keeps the rotated rows between the stats and quantise passes
  * (as in rrs_linear) unless X, perm, dsign, xq, dx or S lies in that area;
  * with a smaller `ws` the quantise pass rotates every row again. The results
- * are the same bits either way.
+ * are the same bits in every form.
  *
  * The one-launch form keeps every rotated row on chip while the workgroups
  * combine their group maxima, so all its workgroups must be resident
@@ -197,7 +199,8 @@ int rrs_frontend_signed(const void* X_fp16, int M, int K, int G,
 /* Number of launches (1 or 3) the front end of rrs_linear / rrs_frontend
  * uses for M tokens of length K with these flags on the current device:
  * 1 when the one-launch form fits on the device at once (or without
- * smoothing), 3 otherwise (also for K = m 2^k). A host-side query; RRS_EINVAL for bad arguments,
+ * smoothing; for K = m 2^k up to 256 rows, one workgroup each), 3
+ * otherwise. A host-side query; RRS_EINVAL for bad arguments,
  * RRS_EHIP if the device cannot be queried. */
 int rrs_frontend_passes(int M, int K, int flags);
 

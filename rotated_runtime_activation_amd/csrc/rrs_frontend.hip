@@ -677,11 +677,6 @@ __global__ void __launch_bounds__(256) group_max_kernel(const uint32_t* part, in
 }
 
 // ------------------------------------------------------------- fused kernel
-// Bounded spin: every wait below gives up after this many polls (seconds of
-// polling), raises the error word and lets the kernel run to its end, so
-// every wave exits whatever happens to the other workgroups.
-constexpr uint32_t kSpinLimit = 1u << 22;
-
 // The whole activation front end in one launch: each wave rotates, reorders
 // and reduces R blocks and keeps them in registers; each workgroup stores
 // its group maxima in its own row of the synchronisation block and raises
@@ -1300,7 +1295,7 @@ hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t
 int frontend_launches(int M, int K, int flags) {
   if (K & (K - 1)) {
     int m = 0, ln = 0;
-    return kron_split(K, &m, &ln) ? kron_frontend_launches(flags) : -1;
+    return kron_split(K, &m, &ln) ? kron_frontend_launches(M, K, flags) : -1;
   }
   const int log2K = __builtin_ctz(static_cast<unsigned>(K));
   if (flags & 2) return 1;

@@ -32,12 +32,14 @@
 #include "rrs_codes.h"
 #include "rrs_internal.h"
 
+#include <atomic>
+
 namespace rrs {
 namespace {
 
 constexpr int kKT = 512;  // threads per workgroup
 
-enum KronMode { kKStats = 0, kKQuant = 1, kKWeight = 2, kKColmax = 3 };
+enum KronMode { kKStats = 0, kKQuant = 1, kKWeight = 2, kKColmax = 3, kKFused = 4 };
 
 // ---- Paley Hadamard matrices H_m[i][a], built at compile time -------------
 constexpr int legendre(int a, int q) {
@@ -118,6 +120,7 @@ struct KronArgs {
   float* S_out;          // [K/G] (quant without smoothing: 1)
   uint32_t* colmax;      // [K] (calibration)
   float* zrows;          // stats: [rows][K] rotated, reordered rows, or nullptr
+  uint32_t* sync;        // one launch: the synchronisation block (epoch, error word, tagged rows)
 };
 
 __device__ __forceinline__ void bfly(float& x, float& y) {
@@ -329,7 +332,7 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
   const int ngroups = K >> a.log2G;
   const HmFrag<M> hf = hm_frags<M>(tid & 63);
 
-  if constexpr (MODE == kKStats) {
+  if constexpr (MODE == kKStats || MODE == kKFused) {
     for (int g = tid; g < ngroups; g += kKT) s_grp[g] = 0.f;
   } else if constexpr (MODE == kKQuant) {
     for (int g = tid; g < ngroups; g += kKT) s_grp[g] = a.smooth ? 1.f / a.S_in[g] : 1.f;
@@ -358,8 +361,14 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
   }
   __syncthreads();
 
+  // one launch: every workgroup reads the epoch before it publishes its row,
+  // so none can see the next call's value
+  uint32_t epoch = 0;
+  if constexpr (MODE == kKFused)
+    epoch = __hip_atomic_load(&a.sync[kSyncEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+
   // rows blockIdx.x, + gridDim.x, ...: the next row's chunks load while this
-  // one is processed
+  // one is processed (one launch: one row per workgroup)
   uint4 nxt[SW];
 #pragma unroll
   for (int s = 0; s < SW; ++s) {
@@ -421,8 +430,8 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) z[s][e] = (w < W8) ? s_row[pp[s][e]] : 0.f;
       }
-      if constexpr (MODE == kKStats) {
-        if (a.zrows) {
+      if constexpr (MODE == kKStats || MODE == kKFused) {
+        if (MODE == kKStats && a.zrows) {
           float4* zr = reinterpret_cast<float4*>(a.zrows + static_cast<size_t>(row) * K);
 #pragma unroll
           for (int s = 0; s < SW; ++s) {
@@ -443,7 +452,62 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
             if (m > 0.f) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[(8 * w) >> a.log2G]), __float_as_uint(m));
           }
         }
-      } else {
+      }
+      if constexpr (MODE == kKFused) {
+        // publish this row's group maxima as 64-bit words tagged with the
+        // epoch (single-copy atomic stores), poll every row until all carry
+        // it, reduce them here; the reordered row stays in registers
+        __syncthreads();
+        uint64_t* part = reinterpret_cast<uint64_t*>(a.sync + kSyncPartials);
+        const uint64_t tag = static_cast<uint64_t>(epoch) << 32;
+        for (int g = tid; g < ngroups; g += kKT)
+          __hip_atomic_store(&part[static_cast<size_t>(row) * ngroups + g], tag | __float_as_uint(s_grp[g]),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        for (int g = tid; g < ngroups; g += kKT) s_grp[g] = 0.f;
+        __syncthreads();
+        {
+          constexpr int kBatch = 8;
+          const int n = static_cast<int>(gridDim.x) * ngroups;
+          for (int base = tid; base < n; base += kKT * kBatch) {
+            uint64_t b[kBatch];
+            uint32_t it = 0;
+            for (;;) {
+#pragma unroll
+              for (int k = 0; k < kBatch; ++k) {
+                const int idx = base + k * kKT;
+                b[k] = idx < n ? __hip_atomic_load(&part[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag;
+              }
+              bool all = true;
+#pragma unroll
+              for (int k = 0; k < kBatch; ++k) all &= (b[k] >> 32) == epoch;
+              if (all) break;
+              if (++it == kSpinLimit) {
+                atomicOr(&a.sync[kSyncError], 1u);
+                break;
+              }
+              __builtin_amdgcn_s_sleep(2);
+            }
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+              const uint32_t bits = static_cast<uint32_t>(b[k]);
+              if (bits) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[(base + k * kKT) % ngroups]), bits);
+            }
+          }
+        }
+        __syncthreads();
+        // every workgroup has read the old epoch (it tagged its row with old + 1)
+        if (row == 0 && tid == 0)
+          __hip_atomic_store(&a.sync[kSyncEpoch], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int g = tid; g < ngroups; g += kKT) {
+          float sg = s_grp[g];
+          if (!(sg > 0.f)) sg = 1.f;  // all-zero group over every token
+          if (row == 0) a.S_out[g] = sg;
+          s_grp[g] = 1.f / sg;
+        }
+        __syncthreads();
+      }
+      if constexpr (MODE != kKStats) {
         // per-token (or per-output-channel) scale of the smoothed row
         float r = 0.f;
 #pragma unroll
@@ -572,6 +636,49 @@ hipError_t dispatch_kron(int m, int log2n, const KronArgs& a, int grid, hipStrea
 
 constexpr int kKronRowsWG = 256;  // workgroups of the row loops (one per CU; each prefetches its next row)
 
+// Workgroups of the one-launch kron_kernel<M, LOG2N, kKFused> the current
+// device holds at once (occupancy per CU x CUs), cached per device; -1 if
+// unknown.
+template <int M, int LOG2N>
+int fused_capacity_mn() {
+  constexpr int kDevices = 64;
+  static std::atomic<int> cache[kDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return -1;
+  int cap = cache[dev].load(std::memory_order_relaxed);
+  if (cap == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kron_kernel<M, LOG2N, kKFused>, kKT, 0) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu <= 0 ||
+        cus <= 0) {
+      cap = -1;
+    } else {
+      cap = per_cu * cus;
+    }
+    cache[dev].store(cap, std::memory_order_relaxed);
+  }
+  return cap;
+}
+
+int kron_fused_capacity(int m, int log2n) {
+#define RRS_KCAP(MM, LN) \
+  if (m == MM && log2n == LN) return fused_capacity_mn<MM, LN>();
+  RRS_KCAP(12, 6) RRS_KCAP(12, 7) RRS_KCAP(12, 8) RRS_KCAP(12, 9) RRS_KCAP(12, 10)
+  RRS_KCAP(20, 6) RRS_KCAP(20, 7) RRS_KCAP(20, 8) RRS_KCAP(20, 9)
+  RRS_KCAP(28, 6) RRS_KCAP(28, 7) RRS_KCAP(28, 8) RRS_KCAP(28, 9)
+#undef RRS_KCAP
+  return -1;
+}
+
+// The smoothed front end fits one launch when every row gets a workgroup
+// and all of them are resident together (they wait for each other).
+bool kron_fused_fits(int M, int m, int log2n) {
+  if (M < 1 || M > kKronRowsWG || M > kMaxFusedWG) return false;
+  const int cap = kron_fused_capacity(m, log2n);
+  return cap > 0 && M <= cap;
+}
+
 }  // namespace
 
 bool kron_split(int K, int* m, int* log2n) {
@@ -588,10 +695,15 @@ bool kron_split(int K, int* m, int* log2n) {
   return false;
 }
 
-int kron_frontend_launches(int flags) { return (flags & 2) ? 1 : 3; }
+int kron_frontend_launches(int M, int K, int flags) {
+  if (flags & 2) return 1;  // no smoothing: the quantise pass alone
+  int m = 0, log2n = 0;
+  if (!kron_split(K, &m, &log2n)) return -1;
+  return (!(flags & 4) && kron_fused_fits(M, m, log2n)) ? 1 : 3;
+}
 
 hipError_t launch_frontend_kron(const uint16_t* X, int M, int K, int G, const int32_t* perm, const uint32_t* dsign,
-                                uint8_t* xq, float* dx, float* S_out, uint32_t* /*sync: unused*/, int flags,
+                                uint8_t* xq, float* dx, float* S_out, uint32_t* sync, int flags,
                                 hipStream_t s, float* zrows) {
   int m = 0, log2n = 0;
   if (!kron_split(K, &m, &log2n)) return hipErrorInvalidValue;
@@ -612,6 +724,12 @@ hipError_t launch_frontend_kron(const uint16_t* X, int M, int K, int G, const in
   // quantise pass overwrites afterwards
   a.part = reinterpret_cast<uint32_t*>(xq);
   const int ngroups = K / G;
+  if (a.smooth && !(flags & 4) && kron_fused_fits(M, m, log2n)) {
+    // few rows: one launch, one row per workgroup, grid-wide wait on the
+    // group maxima in the synchronisation block
+    a.sync = sync;
+    return dispatch_kron<kKFused>(m, log2n, a, M, s);
+  }
   if (a.smooth) {
     // rows kept only when the rotation runs (without it the quantise pass
     // reads X itself, as cheap as the stored rows)

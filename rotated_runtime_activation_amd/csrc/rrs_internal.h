@@ -28,6 +28,10 @@ constexpr int kSyncError = 2;
 constexpr int kSyncEpoch = 3;
 constexpr int kMaxFusedWG = 512;
 constexpr int kSyncPartials = 17408;
+// Bounded spin of the one-launch forms' grid-wide wait: after this many
+// polls (seconds of polling) a workgroup raises the error word and runs to
+// its end, so every wave exits whatever happens to the other workgroups.
+constexpr uint32_t kSpinLimit = 1u << 22;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -77,7 +81,9 @@ hipError_t launch_gemm_small(const uint8_t* xq, const float* dx, const float* S,
 // (64 <= n, K <= kMaxKronK; n <= 1024 for m = 12, n <= 512 otherwise).
 constexpr int kMaxKronK = 16384;
 bool kron_split(int K, int* m, int* log2n);
-int kron_frontend_launches(int flags);
+// Launches of the Kronecker front end for M rows (1 or 3; queries the
+// device's occupancy).
+int kron_frontend_launches(int M, int K, int flags);
 // S_g = max over `nrows` rows of K/G group maxima (float bits) at `part`,
 // 1 where every row holds 0 (the stats passes' reduce).
 hipError_t launch_group_max(const uint32_t* part, int nrows, int ngroups, float* S_out, hipStream_t s);

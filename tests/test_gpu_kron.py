@@ -160,11 +160,13 @@ def test_frontend_kron_row_area(M, K, G, signed):
                 .astype(np.uint32)) if signed else None
     D = gu.to_dev(dsign_np.view(np.int32)) if signed else None
 
-    def run(xq, dx, S, ws):
+    # three launches forced: the row area belongs to that form (few rows
+    # otherwise take the one-launch form, compared with it at the end)
+    def run(xq, dx, S, ws, flags=rra.RRS_FLAG_TWO_PASS):
         if signed:
-            rra.rrs_frontend_signed(X, G, P, D, xq, dx, S, ws)
+            rra.rrs_frontend_signed(X, G, P, D, xq, dx, S, ws, flags)
         else:
-            rra.rrs_frontend(X, G, P, xq, dx, S, ws)
+            rra.rrs_frontend(X, G, P, xq, dx, S, ws, flags)
         torch.cuda.synchronize()
 
     # rotate twice: a workspace of the synchronisation block alone
@@ -202,3 +204,39 @@ def test_frontend_kron_row_area(M, K, G, signed):
     S_c = torch.empty(K // G, dtype=torch.float32, device=gu.DEV)
     run(xq_c, dx_c, S_c, ws_c)
     assert torch.equal(xq_a, xq_c) and torch.equal(dx_a, dx_c) and torch.equal(S_a, S_c)
+
+    # the default form (one launch for up to one row per CU): the same bits
+    ws_d = torch.zeros(nbytes, dtype=torch.uint8, device=gu.DEV)
+    xq_d, dx_d, S_d = rra.workspace_views(ws_d, M, K, G)
+    gu.log(f"  default form: {rra.rrs_frontend_passes(M, K, 0)} launch(es)")
+    run(xq_d, dx_d, S_d, ws_d, 0)
+    assert torch.equal(xq_a, xq_d) and torch.equal(dx_a, dx_d) and torch.equal(S_a, S_d)
+    gu.check_sync_block(ws_d, K, G)
+
+
+def test_frontend_kron_workspace_reuse():
+    """One synchronisation block across Kronecker calls of several sizes,
+    one-launch (few rows) and three-launch (more rows, or forced) mixed: the
+    epoch counts the one-launch calls and every call matches the oracle."""
+    K, G = 1792, 64
+    ws = torch.zeros(rra.rrs_sync_bytes(K, G), dtype=torch.uint8, device=gu.DEV)
+    rra.rrs_workspace_init(ws)
+    one = 0
+    for M, flags in [(5, 0), (200, 0), (1, 0), (300, 0), (64, rra.RRS_FLAG_TWO_PASS), (64, 0), (256, 0)]:
+        passes = rra.rrs_frontend_passes(M, K, flags)
+        gu.log(f"[kron workspace reuse] M={M} flags={flags}: {passes} launch(es)")
+        x, _, perm = _case(M, K)
+        fe = oracle.frontend(x, perm, G)
+        xq = torch.empty(M, K // 2, dtype=torch.uint8, device=gu.DEV)
+        dx = torch.empty(M, dtype=torch.float32, device=gu.DEV)
+        S = torch.empty(K // G, dtype=torch.float32, device=gu.DEV)
+        rra.rrs_frontend(gu.to_dev(x), G, gu.to_dev(perm), xq, dx, S, ws, flags)
+        torch.cuda.synchronize()
+        one += passes == 1
+        gu.compare_codes(oracle.unpack_codes(xq.cpu().numpy()), fe["q"], fe["v"], "kron reuse codes")
+        gu.rel_close(dx.cpu().numpy(), fe["dx"], gu.SCALE_TOL, "kron reuse dx")
+        gu.rel_close(S.cpu().numpy(), fe["S"], gu.SCALE_TOL, "kron reuse S")
+        words = ws.view(torch.int32).cpu().numpy()
+        assert words[2] == 0, "a bounded wait gave up (error word set)"
+        assert words[3] == one, f"epoch {words[3]} after {one} one-launch call(s)"
+    assert one >= 4, "few-row calls take the one-launch form"
