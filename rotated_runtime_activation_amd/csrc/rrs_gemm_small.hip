@@ -39,8 +39,11 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
+// Waves per workgroup: 8 when K is a multiple of 2048; otherwise the
+// largest of 7, 6, 5, 4 that splits K into whole rounds (see small_waves).
+// More than 8 (three waves per SIMD) would cap a wave below the registers
+// the main loop needs.
+constexpr int kMaxWaves = 8;
 constexpr int kTN = 32;      // output channels per workgroup
 constexpr int kSmallMaxTokens = 512;  // token count past which the tiled kernel always serves
 constexpr int kRound = 4;    // k-steps per round (128 bytes of a row)
@@ -71,9 +74,11 @@ __device__ __forceinline__ int swz(int r, int c) { return r * kRows + ((c ^ (r &
 // TJ: 32-token blocks (1 for M <= 32, 2 for M <= 64); NR: rounds of loads
 // in flight (1 or 2; divides the wave's round count); KS: min(k-steps per
 // group, kRound), the spacing of possible group starts inside a round, or 0
-// for G = 32 (two groups in every k-step).
-template <int TJ, int NR, int KS>
-__global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
+// for G = 32 (two groups in every k-step); WV: waves per workgroup.
+template <int TJ, int NR, int KS, int WV>
+__global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
+  constexpr int kWaves = WV, kThreads = WV * 64;
+  static_assert(WV <= kMaxWaves && 64 + kTN + WV <= kThreads, "one thread per scale preloaded");
   constexpr int kWL = 4;            // W loads per lane per round (32 rows / 8)
   constexpr int kXL = 4 * TJ;       // X loads per lane per round
   constexpr int kBuf = (32 + 32 * TJ) * kRows;  // round buffer bytes per wave
@@ -276,20 +281,32 @@ __global__ void __launch_bounds__(kThreads) gemm_small_kernel(SmallArgs a) {
 
 }  // namespace
 
-// K a multiple of 2048 (a power of two, or m 2^k with the Kronecker
-// rotation): every wave gets a whole number of rounds. Its run and the
-// group must nest (one a multiple of the other), so that no group is cut
-// part-way into a wave. Up to 64 tokens this kernel then always serves. Past that it serves while it needs
+// Waves per workgroup for K (0: not served): every wave gets the same whole
+// number of rounds (256 codes each). K a multiple of 2048 takes 8 waves;
+// other K (m 2^k, or 1024) the largest of 7, 6, 5, 4 waves that divides its
+// round count.
+int small_waves(int K) {
+  if (K % 2048 == 0) return 8;
+  if (K % 256 != 0) return 0;
+  const int rounds = K / 256;
+  for (int w : {7, 6, 5, 4})
+    if (rounds % w == 0) return w;
+  return 0;
+}
+
+// A wave's run and the group must nest (one a multiple of the other), so
+// that no group is cut part-way into a wave. Up to 64 tokens this kernel
+// then always serves. Past that it serves while it needs
 // fewer rounds of resident workgroups (one per CU, 256 CUs) than the tiled
 // kernel, weighted by what one round of each costs at this K (measured with
 // both kernels alone at M = 65 .. 512: a tiled round costs about 4.8 times
 // a few-token round at K = 8192, 3.6 times at K = 4096; 3 is assumed at
 // K = 2048).
 bool gemm_small_applies(int M, int K, int N, int G) {
-  if (M < 1 || N < 1 || G < 32 || (G & (G - 1)) != 0 || K < 2048 || K % 2048 != 0 || K > kMaxKronK ||
-      K % G != 0)
-    return false;
-  const int kpw = K / 64 / kWaves, kspg = G >= 64 ? G / 64 : 1;  // k-steps per wave, per group
+  if (M < 1 || N < 1 || G < 32 || (G & (G - 1)) != 0 || K > kMaxKronK || K % G != 0) return false;
+  const int wv = small_waves(K);
+  if (wv == 0) return false;
+  const int kpw = K / 64 / wv, kspg = G >= 64 ? G / 64 : 1;  // k-steps per wave, per group
   if (kpw % kspg != 0 && kspg % kpw != 0) return false;
   if (M <= 64) return true;
   if (M > kSmallMaxTokens) return false;
@@ -316,24 +333,36 @@ hipError_t launch_gemm_small(const uint8_t* xq, const float* dx, const float* S,
   a.K = K;
   a.log2G = __builtin_ctz(static_cast<unsigned>(G));
   const dim3 grid((N + kTN - 1) / kTN, (M + 63) / 64);
-  const int rounds = (a.K >> 6) / kWaves / kRound;  // 1, 2, 4 for K = 2048, 4096, 8192; 7 for 14336
+  const int wv = small_waves(K);
+  const int rounds = (a.K >> 6) / wv / kRound;  // per wave: 1, 2, 4 for K = 2048, 4096, 8192; 7 for 14336
   const int spg = G >> 6;
   const int ks = G == 32 ? 0 : spg < kRound ? spg : kRound;
-  // instantiations: TJ in {1, 2}, NR in {1, 2}, KS in {0 (G = 32), 1, 2, 4}
-  auto go = [&](auto tj, auto nr) {
-    constexpr int TJ = decltype(tj)::value, NR = decltype(nr)::value;
+  // instantiations: TJ in {1, 2}, NR in {1, 2}, KS in {0 (G = 32), 1, 2, 4},
+  // WV in {4, 5, 6, 7, 8}
+  auto go = [&](auto tj, auto nr, auto w) {
+    constexpr int TJ = decltype(tj)::value, NR = decltype(nr)::value, WV = decltype(w)::value;
+    const dim3 block(WV * 64);
     switch (ks) {
-      case 0: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 0>), grid, dim3(kThreads), 0, s, a); break;
-      case 1: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 1>), grid, dim3(kThreads), 0, s, a); break;
-      case 2: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 2>), grid, dim3(kThreads), 0, s, a); break;
-      default: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, kRound>), grid, dim3(kThreads), 0, s, a); break;
+      case 0: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 0, WV>), grid, block, 0, s, a); break;
+      case 1: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 1, WV>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 2, WV>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, kRound, WV>), grid, block, 0, s, a); break;
+    }
+  };
+  auto by_waves = [&](auto tj, auto nr) {
+    switch (wv) {
+      case 4: go(tj, nr, std::integral_constant<int, 4>{}); break;
+      case 5: go(tj, nr, std::integral_constant<int, 5>{}); break;
+      case 6: go(tj, nr, std::integral_constant<int, 6>{}); break;
+      case 7: go(tj, nr, std::integral_constant<int, 7>{}); break;
+      default: go(tj, nr, std::integral_constant<int, 8>{}); break;
     }
   };
   auto by_rounds = [&](auto tj) {
     if (rounds % 2 != 0)  // NR divides the round count
-      go(tj, std::integral_constant<int, 1>{});
+      by_waves(tj, std::integral_constant<int, 1>{});
     else
-      go(tj, std::integral_constant<int, 2>{});
+      by_waves(tj, std::integral_constant<int, 2>{});
   };
   if (M <= 32)
     by_rounds(std::integral_constant<int, 1>{});

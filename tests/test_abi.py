@@ -139,8 +139,8 @@ def test_kron_shapes_accepted_and_rejected():
 
 
 def test_gemm_form():
-    """Few-token kernel for M <= 64 (K a multiple of 2048, groups nested in
-    the waves' runs of K/8); up to
+    """Few-token kernel for M <= 64 (K split into whole 256-code rounds over
+    8 waves, or 7, 6, 5, 4; groups nested in the waves' runs); up to
     M = 512 while its rounds of 256 workgroups (N/32 x M/64 of them) stay
     below the tiled kernel's (N/256 x M/128) times the per-round cost ratio
     (4.8 at K = 8192, 3.6 at 4096, 3 at 2048); tiled otherwise."""
@@ -148,7 +148,9 @@ def test_gemm_form():
     assert rra.rrs_gemm_form(64, 8192, 8192, 128) == F
     assert rra.rrs_gemm_form(1, 2048, 1, 64) == F
     assert rra.rrs_gemm_form(1, 8192, 4096, 8192) == F
-    assert rra.rrs_gemm_form(64, 1024, 4096, 128) == T      # K < 2048
+    assert rra.rrs_gemm_form(64, 1024, 4096, 128) == F      # 4 waves of one round
+    assert rra.rrs_gemm_form(64, 512, 4096, 128) == T       # 2 rounds: no wave count divides them
+    assert rra.rrs_gemm_form(64, 768, 4096, 64) == T        # 3 rounds
     assert rra.rrs_gemm_form(64, 4096, 4096, 32) == F       # G = 32: two groups per k-step
     # K = m 2^k: a multiple of 2048 with groups nested in the waves' runs of K/8
     assert rra.rrs_gemm_form(64, 14336, 4096, 128) == F     # runs of 1792 codes, groups of 128
@@ -156,8 +158,11 @@ def test_gemm_form():
     assert rra.rrs_gemm_form(64, 14336, 4096, 512) == T     # 512 does not divide 1792
     assert rra.rrs_gemm_form(64, 12288, 4096, 512) == F     # runs of 1536
     assert rra.rrs_gemm_form(64, 10240, 4096, 64) == F
-    assert rra.rrs_gemm_form(64, 3072, 4096, 64) == T       # not a multiple of 2048
-    assert rra.rrs_gemm_form(64, 5120, 4096, 64) == T
+    # other K: 7, 6, 5 or 4 waves of whole rounds (256 codes)
+    assert rra.rrs_gemm_form(64, 3072, 4096, 64) == F       # 12 rounds, 6 waves
+    assert rra.rrs_gemm_form(64, 5120, 4096, 64) == F       # 20 rounds, 5 waves
+    assert rra.rrs_gemm_form(64, 7168, 4096, 256) == F      # 28 rounds, 7 waves
+    assert rra.rrs_gemm_form(64, 3072, 4096, 1024) == F     # groups of two waves' runs
     # K = N = 8192: 2 .. 4 rounds against one tiled round (x 4.8); 5 is too many
     assert rra.rrs_gemm_form(65, 8192, 8192, 128) == F
     assert rra.rrs_gemm_form(256, 8192, 8192, 128) == F

@@ -164,6 +164,9 @@ GEMM_SHAPES = [
     (65, 260, 8192, 128), (200, 33, 2048, 64), (256, 300, 4096, 256), (500, 64, 4096, 128),
     # few-token kernel at G = 32 (two groups per k-step)
     (64, 260, 4096, 32), (130, 64, 8192, 32), (1, 33, 2048, 32),
+    # few-token kernel with 4 .. 7 waves (K not a multiple of 2048)
+    (64, 130, 5120, 128), (1, 96, 3072, 64), (33, 70, 7168, 256), (64, 40, 1024, 128),
+    (130, 64, 2560, 512), (20, 50, 3072, 1024), (7, 33, 1536, 32),
 ]
 
 
