@@ -71,7 +71,7 @@ __device__ __forceinline__ v8i widen(v4u w) {
 // byte offset of 16-byte chunk c of row r in a wave's round buffer
 __device__ __forceinline__ int swz(int r, int c) { return r * kRows + ((c ^ (r & 7)) << 4); }
 
-// TJ: 32-token blocks (1 for M <= 32, 2 for M <= 64); NR: rounds of loads
+// TJ: 32-token blocks per slice (1 for M <= 32, else 2); NR: rounds of loads
 // in flight (1 or 2; divides the wave's round count); KS: min(k-steps per
 // group, kRound), the spacing of possible group starts inside a round, or 0
 // for G = 32 (two groups in every k-step); WV: waves per workgroup.
