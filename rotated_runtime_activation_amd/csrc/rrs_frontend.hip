@@ -922,6 +922,10 @@ hipError_t dispatch_k(int log2K, const FeArgs& a, hipStream_t s, int* grid_out =
 // one row per workgroup), the per-token scale and the packing follow the
 // kernels above with the same arithmetic.
 constexpr int kRowThreads = 512;
+// rowsplit_kernel modes: the one-launch front end (one row per workgroup,
+// grid-wide wait), and the stats and quantise passes of the three launches
+// (rows looped over the grid).
+enum RowMode { kRowOne = 0, kRowStats = 1, kRowQuant = 2 };
 
 __device__ __forceinline__ constexpr int rowpad(int f) { return f + 4 * (f >> 6); }
 
@@ -943,7 +947,7 @@ __device__ __forceinline__ void row_pass8(float* row, int tid) {
   __syncthreads();
 }
 
-template <int LOG2K, bool ROTATE>
+template <int LOG2K, bool ROTATE, int RM>
 __global__ void __launch_bounds__(kRowThreads) rowsplit_kernel(FeArgs a) {
   constexpr int K = 1 << LOG2K;
   constexpr int E = K / kRowThreads;  // 8 or 16
@@ -955,7 +959,6 @@ __global__ void __launch_bounds__(kRowThreads) rowsplit_kernel(FeArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int row = blockIdx.x;
   const int ngroups = K >> a.log2G;
   const int G = 1 << a.log2G;
   const int p0 = E * tid;  // this thread's first element / output position
@@ -970,6 +973,23 @@ __global__ void __launch_bounds__(kRowThreads) rowsplit_kernel(FeArgs a) {
     src[4 * c + 2] = rowpad(q.z);
     src[4 * c + 3] = rowpad(q.w);
   }
+  // one launch: one row per workgroup; passes: rows blockIdx.x,
+  // + gridDim.x, ...
+  const uint32_t epoch = (RM == kRowOne && a.smooth)
+                             ? __hip_atomic_load(&a.sync[kSyncEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u
+                             : 0u;
+  if constexpr (RM == kRowQuant) {
+    // S from the reduce launch; without smoothing S = 1 (written here)
+    for (int g = tid; g < ngroups; g += kRowThreads) {
+      float sg = a.smooth ? a.S_out[g] : 1.f;
+      if (!(sg > 0.f)) sg = 1.f;  // all-zero group over every token
+      if (!a.smooth && blockIdx.x == 0) a.S_out[g] = 1.f;
+      s_grp[g] = 1.f / sg;
+    }
+  } else {
+    for (int g = tid; g < ngroups; g += kRowThreads) s_grp[g] = 0.f;
+  }
+  for (int row = blockIdx.x; row < a.rows; row += gridDim.x) {
   uint4 w[E / 8];
 #pragma unroll
   for (int i = 0; i < E / 8; ++i)
@@ -984,9 +1004,6 @@ __global__ void __launch_bounds__(kRowThreads) rowsplit_kernel(FeArgs a) {
       w[i].w ^= ((b & 64u) << 9) | ((b & 128u) << 24);
     }
   }
-  const uint32_t epoch =
-      a.smooth ? __hip_atomic_load(&a.sync[kSyncEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u : 0u;
-  for (int g = tid; g < ngroups; g += kRowThreads) s_grp[g] = 0.f;
 
   // ---- rotate: E-index bits in registers, the other nine bits in LDS
   float v[E];
@@ -1020,12 +1037,18 @@ __global__ void __launch_bounds__(kRowThreads) rowsplit_kernel(FeArgs a) {
 #pragma unroll
   for (int r = 1; r < E; ++r) m = fmaxf(m, fabsf(v[r]));
   const int g0 = p0 >> a.log2G;
-  if (a.smooth) {
+  if (RM == kRowStats || (RM == kRowOne && a.smooth)) {
     float mg = m;
     for (int d = 1; d * E < G && d < 64; d <<= 1) mg = fmaxf(mg, __shfl_xor(mg, d));
     if ((p0 & (G - 1)) == 0 || (lane == 0)) {
       if (mg > 0.f) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[g0]), __float_as_uint(mg));
     }
+  }
+  if constexpr (RM == kRowStats) {
+    __syncthreads();  // the row buffer is reused by the next row
+    continue;
+  }
+  if (RM == kRowOne && a.smooth) {
     __syncthreads();
 
     // ---- publish this row's maxima, read every row's (as fused_kernel)
@@ -1076,7 +1099,7 @@ __global__ void __launch_bounds__(kRowThreads) rowsplit_kernel(FeArgs a) {
       if (row == 0) a.S_out[g] = sg;
       s_grp[g] = 1.f / sg;
     }
-  } else {
+  } else if (RM == kRowOne) {
     for (int g = tid; g < ngroups; g += kRowThreads) {
       if (row == 0) a.S_out[g] = 1.f;
       s_grp[g] = 1.f;
@@ -1112,6 +1135,16 @@ __global__ void __launch_bounds__(kRowThreads) rowsplit_kernel(FeArgs a) {
   else
     *reinterpret_cast<uint32_t*>(dst) = packed[0];
   if (tid == 0) a.scale[row] = rmax / 7.f;
+  if constexpr (RM == kRowOne) break;  // one row: no loop
+  __syncthreads();                     // s_row and s_red are reused by the next row
+  }
+
+  if constexpr (RM == kRowStats) {
+    // this workgroup's maxima over its rows into its own partial row
+    __syncthreads();
+    for (int g = tid; g < ngroups; g += kRowThreads)
+      a.part[static_cast<size_t>(blockIdx.x) * ngroups + g] = __float_as_uint(s_grp[g]);
+  }
 }
 
 // Workgroups of fused_kernel<LOG2K, ROTATE, R> that the current device holds
@@ -1178,7 +1211,7 @@ bool launch_fused(const FeArgs& a, hipStream_t s, hipError_t* err) {
 }
 
 // Workgroups of rowsplit_kernel the device holds at once (cached per device).
-template <int LOG2K, bool ROTATE>
+template <int LOG2K, bool ROTATE, int RM>
 int rowsplit_capacity() {
   static std::atomic<int> cache[kMaxDevices];
   int dev = 0;
@@ -1186,7 +1219,7 @@ int rowsplit_capacity() {
   int cap = cache[dev].load(std::memory_order_relaxed);
   if (cap == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rowsplit_kernel<LOG2K, ROTATE>, kRowThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rowsplit_kernel<LOG2K, ROTATE, RM>, kRowThreads, 0) !=
             hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu <= 0 ||
         cus <= 0) {
@@ -1206,7 +1239,7 @@ constexpr int kRowSplitMaxRows = 256;
 template <int LOG2K, bool ROTATE>
 bool rowsplit_fits(int rows) {
   if (rows < 1 || rows > kRowSplitMaxRows || rows > kMaxFusedWG) return false;
-  const int cap = rowsplit_capacity<LOG2K, ROTATE>();
+  const int cap = rowsplit_capacity<LOG2K, ROTATE, kRowOne>();
   return cap > 0 && rows <= cap;
 }
 
@@ -1218,8 +1251,26 @@ bool rowsplit_applies(int log2K, bool rotate, int rows) {
 
 template <int LOG2K, bool ROTATE>
 hipError_t launch_rowsplit(const FeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((rowsplit_kernel<LOG2K, ROTATE>), dim3(a.rows), dim3(kRowThreads), 0, s, a);
+  hipLaunchKernelGGL((rowsplit_kernel<LOG2K, ROTATE, kRowOne>), dim3(a.rows), dim3(kRowThreads), 0, s, a);
   return hipGetLastError();
+}
+
+// A stats or quantise pass of the three launches on the row kernel (used at
+// K = 8192): at most one workgroup per resident slot, each looping over its
+// rows. *grid_out receives the launched grid.
+template <int LOG2K, bool ROTATE, int RM>
+hipError_t launch_row_pass(const FeArgs& a, hipStream_t s, int* grid_out) {
+  const int cap = rowsplit_capacity<LOG2K, ROTATE, RM>();
+  const int grid = cap > 0 && a.rows > cap ? cap : a.rows;
+  if (grid_out) *grid_out = grid;
+  hipLaunchKernelGGL((rowsplit_kernel<LOG2K, ROTATE, RM>), dim3(grid), dim3(kRowThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int RM>
+hipError_t row_pass_k(int log2K, bool rotate, const FeArgs& a, hipStream_t s, int* grid_out = nullptr) {
+  if (log2K != 13) return hipErrorInvalidValue;
+  return rotate ? launch_row_pass<13, true, RM>(a, s, grid_out) : launch_row_pass<13, false, RM>(a, s, grid_out);
 }
 
 hipError_t rowsplit_k(int log2K, bool rotate, const FeArgs& a, hipStream_t s) {
@@ -1284,11 +1335,18 @@ hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t
       return hipErrorInvalidValue;
     a.part = reinterpret_cast<uint32_t*>(xq);
     int nrows = 0;
-    e = rotate ? dispatch_k<kStats, true>(log2K, a, s, &nrows) : dispatch_k<kStats, false>(log2K, a, s, &nrows);
+    // K = 8192: the row kernel's passes (24 waves per CU) beat the block
+    // kernel's (3 waves per CU); at K = 4096 the block kernel's passes, with
+    // the rotation on the matrix cores and 8 waves, are faster
+    if (log2K == 13)
+      e = row_pass_k<kRowStats>(log2K, rotate, a, s, &nrows);
+    else
+      e = rotate ? dispatch_k<kStats, true>(log2K, a, s, &nrows) : dispatch_k<kStats, false>(log2K, a, s, &nrows);
     if (e != hipSuccess) return e;
     e = launch_group_max(a.part, nrows, ngroups, S_out, s);
     if (e != hipSuccess) return e;
   }
+  if (log2K == 13) return row_pass_k<kRowQuant>(log2K, rotate, a, s);
   return rotate ? dispatch_k<kQuant, true>(log2K, a, s) : dispatch_k<kQuant, false>(log2K, a, s);
 }
 
