@@ -213,10 +213,11 @@ int rrs_gemm(const uint8_t* xq, const float* dx, const float* S, int M, int K,
  * N output channels and group size G: RRS_GEMM_TILED (256 x 128 output
  * tiles, every shape) or RRS_GEMM_FEW_TOKENS (one workgroup per 32 output
  * channels and 64 tokens, streaming the weights once per 64 tokens; needs
- * K a multiple of 2048 and K/8 and G nested (one a multiple of the other),
- * and serves every M <= 64 and, up
- * to M = 512, the shapes where it needs fewer rounds of workgroups than
- * the tiled kernel, weighted by their measured cost per round). Both apply
+ * K to split into whole 256-code rounds over 8 waves (K a multiple of
+ * 2048) or over 7, 6, 5 or 4 waves, with each wave's run of K and G
+ * nested (one a multiple of the other); it serves every M <= 64 and, up to
+ * M = 512, the shapes where it needs fewer rounds of workgroups than the
+ * tiled kernel, weighted by their measured cost per round). Both apply
  * the same arithmetic (group partials exact, rescaled in fp32). A host-side
  * query; RRS_EINVAL for bad arguments. */
 #define RRS_GEMM_TILED 1
