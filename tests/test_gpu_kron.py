@@ -121,7 +121,9 @@ def test_gemm_kron(M, N, K, G):
     assert err <= gu.Y_TOL
 
 
-@pytest.mark.parametrize("M,K,N,G", [(48, 14336, 130, 128), (7, 1280, 64, 64)])
+@pytest.mark.parametrize("M,K,N,G", [(48, 14336, 130, 128), (7, 1280, 64, 64),
+                                     # one-launch Kronecker front end, few-token GEMM with 5 waves over 4 slices
+                                     (200, 5120, 96, 128)])
 def test_linear_kron(M, K, N, G):
     gu.log(f"[linear kron] M={M} K={K} N={N} G={G}")
     x, w, perm = _case(M, K, N)
