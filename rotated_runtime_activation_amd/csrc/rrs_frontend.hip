@@ -911,17 +911,24 @@ hipError_t dispatch_k(int log2K, const FeArgs& a, hipStream_t s, int* grid_out =
 }
 
 // ------------------------------------------------- one row per workgroup
-// Few tokens (decode-shaped calls, K = 4096 or 8192): the one-wave-per-row
+// Few tokens (decode-shaped calls, K = 1024 .. 8192): the one-wave-per-row
 // kernel above leaves most of the chip idle and runs each row's whole chain
-// on one wave. Here a workgroup of 512 threads owns one row: thread t holds
-// elements E t .. E t + E - 1 (E = K / 512), runs the butterflies over the
-// E-index bits in registers, then three radix-8 passes over the padded row
-// in LDS cover the other nine bits. The reorder reads each output
+// on one wave. Here a workgroup of K / 8 threads (512 at K = 8192) owns one
+// row: thread t holds elements E t .. E t + E - 1 (E = 8, or 16 at
+// K = 8192), runs the butterflies over the E-index bits in registers, then
+// three passes over the padded row in LDS cover the other bits (radix 8;
+// the last pass takes the 2 or 1 bits left at K = 2048 or 1024). The reorder reads each output
 // position's source channel straight from the row buffer through perm.
 // Group maxima, the grid-wide wait (same epoch-tagged rows as fused_kernel,
 // one row per workgroup), the per-token scale and the packing follow the
 // kernels above with the same arithmetic.
-constexpr int kRowThreads = 512;
+constexpr int kRowThreads = 512;  // the most threads of a row workgroup (K = 4096, 8192)
+// Threads of a row workgroup: K / 8 (eight elements each) up to K = 4096,
+// 512 at K = 8192 (sixteen each).
+template <int LOG2K>
+constexpr int row_threads() {
+  return LOG2K >= 12 ? kRowThreads : (1 << LOG2K) / 8;
+}
 // rowsplit_kernel modes: the one-launch front end (one row per workgroup,
 // grid-wide wait), and the stats and quantise passes of the three launches
 // (rows looped over the grid).
@@ -931,31 +938,33 @@ __device__ __forceinline__ constexpr int rowpad(int f) { return f + 4 * (f >> 6)
 
 template <int LOG2K, int B>
 __device__ __forceinline__ void row_pass8(float* row, int tid) {
-  constexpr int K = 1 << LOG2K;
-  for (int t = tid; t < K / 8; t += kRowThreads) {
+  constexpr int K = 1 << LOG2K, T = row_threads<LOG2K>();
+  constexpr int R = LOG2K - B < 3 ? LOG2K - B : 3;  // bits of this pass (the last may take fewer)
+  constexpr int P = 1 << R;
+  for (int t = tid; t < (K >> R); t += T) {
     const int lo = t & ((1 << B) - 1), hi = t >> B;
-    const int base = (hi << (B + 3)) | lo;
-    float v[8];
+    const int base = (hi << (B + R)) | lo;
+    float v[P];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = row[rowpad(base + (u << B))];
-    butterfly<8>(v, 1);
-    butterfly<8>(v, 2);
-    butterfly<8>(v, 4);
+    for (int u = 0; u < P; ++u) v[u] = row[rowpad(base + (u << B))];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) row[rowpad(base + (u << B))] = v[u];
+    for (int h = 1; h < P; h <<= 1) butterfly<P>(v, h);
+#pragma unroll
+    for (int u = 0; u < P; ++u) row[rowpad(base + (u << B))] = v[u];
   }
   __syncthreads();
 }
 
 template <int LOG2K, bool ROTATE, int RM>
-__global__ void __launch_bounds__(kRowThreads) rowsplit_kernel(FeArgs a) {
+__global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a) {
   constexpr int K = 1 << LOG2K;
-  constexpr int E = K / kRowThreads;  // 8 or 16
-  constexpr int LOG2E = LOG2K - 9;
-  static_assert(E == 8 || E == 16, "K = 4096 or 8192");
+  constexpr int T = row_threads<LOG2K>();
+  constexpr int E = K / T;  // 8, or 16 at K = 8192
+  constexpr int LOG2E = E == 16 ? 4 : 3;
+  static_assert(E == 8 || E == 16, "K = 1024 .. 8192");
   __shared__ __attribute__((aligned(16))) float s_row[K + K / 16];
   __shared__ float s_grp[K / 32];
-  __shared__ float s_red[kRowThreads / 64];
+  __shared__ float s_red[T / 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -980,14 +989,14 @@ __global__ void __launch_bounds__(kRowThreads) rowsplit_kernel(FeArgs a) {
                              : 0u;
   if constexpr (RM == kRowQuant) {
     // S from the reduce launch; without smoothing S = 1 (written here)
-    for (int g = tid; g < ngroups; g += kRowThreads) {
+    for (int g = tid; g < ngroups; g += T) {
       float sg = a.smooth ? a.S_out[g] : 1.f;
       if (!(sg > 0.f)) sg = 1.f;  // all-zero group over every token
       if (!a.smooth && blockIdx.x == 0) a.S_out[g] = 1.f;
       s_grp[g] = 1.f / sg;
     }
   } else {
-    for (int g = tid; g < ngroups; g += kRowThreads) s_grp[g] = 0.f;
+    for (int g = tid; g < ngroups; g += T) s_grp[g] = 0.f;
   }
   for (int row = blockIdx.x; row < a.rows; row += gridDim.x) {
   uint4 w[E / 8];
@@ -1054,22 +1063,22 @@ __global__ void __launch_bounds__(kRowThreads) rowsplit_kernel(FeArgs a) {
     // ---- publish this row's maxima, read every row's (as fused_kernel)
     uint64_t* part = reinterpret_cast<uint64_t*>(a.sync + kSyncPartials);
     const uint64_t tag = static_cast<uint64_t>(epoch) << 32;
-    for (int g = tid; g < ngroups; g += kRowThreads)
+    for (int g = tid; g < ngroups; g += T)
       __hip_atomic_store(&part[static_cast<size_t>(row) * ngroups + g], tag | __float_as_uint(s_grp[g]),
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    for (int g = tid; g < ngroups; g += kRowThreads) s_grp[g] = 0.f;
+    for (int g = tid; g < ngroups; g += T) s_grp[g] = 0.f;
     __syncthreads();
     {
       constexpr int kBatch = 8;
       const int n = static_cast<int>(gridDim.x) * ngroups;
-      for (int base = tid; base < n; base += kRowThreads * kBatch) {
+      for (int base = tid; base < n; base += T * kBatch) {
         uint64_t b[kBatch];
         uint32_t it = 0;
         for (;;) {
 #pragma unroll
           for (int k = 0; k < kBatch; ++k) {
-            const int idx = base + k * kRowThreads;
+            const int idx = base + k * T;
             b[k] = idx < n ? __hip_atomic_load(&part[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag;
           }
           bool all = true;
@@ -1085,7 +1094,7 @@ __global__ void __launch_bounds__(kRowThreads) rowsplit_kernel(FeArgs a) {
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
           const uint32_t bits = static_cast<uint32_t>(b[k]);
-          if (bits) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[(base + k * kRowThreads) % ngroups]), bits);
+          if (bits) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[(base + k * T) % ngroups]), bits);
         }
       }
     }
@@ -1093,14 +1102,14 @@ __global__ void __launch_bounds__(kRowThreads) rowsplit_kernel(FeArgs a) {
     // every workgroup has read the old epoch (it tagged its row with old + 1)
     if (row == 0 && tid == 0)
       __hip_atomic_store(&a.sync[kSyncEpoch], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int g = tid; g < ngroups; g += kRowThreads) {
+    for (int g = tid; g < ngroups; g += T) {
       float sg = s_grp[g];
       if (!(sg > 0.f)) sg = 1.f;  // all-zero group over every token
       if (row == 0) a.S_out[g] = sg;
       s_grp[g] = 1.f / sg;
     }
   } else if (RM == kRowOne) {
-    for (int g = tid; g < ngroups; g += kRowThreads) {
+    for (int g = tid; g < ngroups; g += T) {
       if (row == 0) a.S_out[g] = 1.f;
       s_grp[g] = 1.f;
     }
@@ -1115,7 +1124,7 @@ __global__ void __launch_bounds__(kRowThreads) rowsplit_kernel(FeArgs a) {
   __syncthreads();
   rmax = s_red[0];
 #pragma unroll
-  for (int k = 1; k < kRowThreads / 64; ++k) rmax = fmaxf(rmax, s_red[k]);
+  for (int k = 1; k < T / 64; ++k) rmax = fmaxf(rmax, s_red[k]);
   const float k7 = rmax > 0.f ? 7.f / rmax : 0.f;
   const float ks = inv * k7;
   uint32_t packed[E / 8];
@@ -1142,7 +1151,7 @@ __global__ void __launch_bounds__(kRowThreads) rowsplit_kernel(FeArgs a) {
   if constexpr (RM == kRowStats) {
     // this workgroup's maxima over its rows into its own partial row
     __syncthreads();
-    for (int g = tid; g < ngroups; g += kRowThreads)
+    for (int g = tid; g < ngroups; g += T)
       a.part[static_cast<size_t>(blockIdx.x) * ngroups + g] = __float_as_uint(s_grp[g]);
   }
 }
@@ -1219,7 +1228,8 @@ int rowsplit_capacity() {
   int cap = cache[dev].load(std::memory_order_relaxed);
   if (cap == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rowsplit_kernel<LOG2K, ROTATE, RM>, kRowThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rowsplit_kernel<LOG2K, ROTATE, RM>, row_threads<LOG2K>(),
+                                                     0) !=
             hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu <= 0 ||
         cus <= 0) {
@@ -1244,6 +1254,8 @@ bool rowsplit_fits(int rows) {
 }
 
 bool rowsplit_applies(int log2K, bool rotate, int rows) {
+  if (log2K == 10) return rotate ? rowsplit_fits<10, true>(rows) : rowsplit_fits<10, false>(rows);
+  if (log2K == 11) return rotate ? rowsplit_fits<11, true>(rows) : rowsplit_fits<11, false>(rows);
   if (log2K == 12) return rotate ? rowsplit_fits<12, true>(rows) : rowsplit_fits<12, false>(rows);
   if (log2K == 13) return rotate ? rowsplit_fits<13, true>(rows) : rowsplit_fits<13, false>(rows);
   return false;
@@ -1251,7 +1263,7 @@ bool rowsplit_applies(int log2K, bool rotate, int rows) {
 
 template <int LOG2K, bool ROTATE>
 hipError_t launch_rowsplit(const FeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((rowsplit_kernel<LOG2K, ROTATE, kRowOne>), dim3(a.rows), dim3(kRowThreads), 0, s, a);
+  hipLaunchKernelGGL((rowsplit_kernel<LOG2K, ROTATE, kRowOne>), dim3(a.rows), dim3(row_threads<LOG2K>()), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1263,7 +1275,7 @@ hipError_t launch_row_pass(const FeArgs& a, hipStream_t s, int* grid_out) {
   const int cap = rowsplit_capacity<LOG2K, ROTATE, RM>();
   const int grid = cap > 0 && a.rows > cap ? cap : a.rows;
   if (grid_out) *grid_out = grid;
-  hipLaunchKernelGGL((rowsplit_kernel<LOG2K, ROTATE, RM>), dim3(grid), dim3(kRowThreads), 0, s, a);
+  hipLaunchKernelGGL((rowsplit_kernel<LOG2K, ROTATE, RM>), dim3(grid), dim3(row_threads<LOG2K>()), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1274,6 +1286,8 @@ hipError_t row_pass_k(int log2K, bool rotate, const FeArgs& a, hipStream_t s, in
 }
 
 hipError_t rowsplit_k(int log2K, bool rotate, const FeArgs& a, hipStream_t s) {
+  if (log2K == 10) return rotate ? launch_rowsplit<10, true>(a, s) : launch_rowsplit<10, false>(a, s);
+  if (log2K == 11) return rotate ? launch_rowsplit<11, true>(a, s) : launch_rowsplit<11, false>(a, s);
   if (log2K == 12) return rotate ? launch_rowsplit<12, true>(a, s) : launch_rowsplit<12, false>(a, s);
   return rotate ? launch_rowsplit<13, true>(a, s) : launch_rowsplit<13, false>(a, s);
 }

@@ -51,10 +51,12 @@ def test_frontend_capacity(M, K, G):
     gu.check_frontend(x, perm, G)
 
 
-# One row per workgroup (K = 4096 and 8192, up to 256 rows) and the step to
+# One row per workgroup (K = 1024 .. 8192, up to 256 rows) and the step to
 # one row per wave past it; group sizes from 32 to a single group of K.
 @pytest.mark.parametrize("M,K,G", [(1, 8192, 128), (255, 8192, 32), (256, 8192, 8192), (257, 8192, 128),
-                                   (1, 4096, 4096), (256, 4096, 64), (257, 4096, 128)])
+                                   (1, 4096, 4096), (256, 4096, 64), (257, 4096, 128),
+                                   (1, 2048, 64), (256, 2048, 2048), (257, 2048, 128),
+                                   (1, 1024, 1024), (255, 1024, 32), (64, 1024, 128)])
 @pytest.mark.parametrize("flags", [0, rra.RRS_FLAG_NO_SMOOTH, rra.RRS_FLAG_NO_ROTATE])
 def test_frontend_rows_boundary(M, K, G, flags):
     gu.log(f"[frontend rows] M={M} K={K} G={G} flags={flags}: {rra.rrs_frontend_passes(M, K, flags)} launch(es)")
