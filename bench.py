@@ -258,7 +258,7 @@ def main():
         "roofline": gemm_roofline,
         "roofline_frontend": {
             "kernel": (("rowsplit_kernel (one row per workgroup: rotate, reorder, group max, grid-wide wait, "
-                        "quantise, pack)" if M <= 256 and K in (4096, 8192) else
+                        "quantise, pack)" if M <= 256 and K in (1024, 2048, 4096, 8192) else
                         "fused_kernel (rotate, reorder, group max, grid-wide wait, quantise, pack)")
                        if fe_launches == 1 else
                        "stats pass, group-max reduce, quantise pass" if (K & (K - 1)) == 0 else
