@@ -175,7 +175,7 @@ def signs_from_bits(bits: np.ndarray, K: int) -> np.ndarray:
 
 
 # ------------------------------------------------------------------ reorder
-def calibrate_perm(x_cal: np.ndarray, d=None) -> np.ndarray:
+def calibrate_perm(x_cal: np.ndarray, d=None, rotate: bool = True) -> np.ndarray:
     """Fixed channel order from a calibration batch (reading R5/R15).
 
     Rotate the calibration activations (with the layer's sign vector, if
@@ -184,8 +184,13 @@ def calibrate_perm(x_cal: np.ndarray, d=None) -> np.ndarray:
     is the source channel of position j, so outlier channels gather into the
     leading groups and normal channels into the rest ([RRS-rebuttal]
     "Novelty": reorder to collect outliers and normal values).
+    ``rotate=False`` orders the raw channels (Runtime Smooth without the
+    rotation, the ablation of [RRS-rebuttal] "Incomplete ablation study").
     """
-    c = np.max(np.abs(rotate_rows(x_cal, d)), axis=0)
+    if not rotate and d is not None:
+        raise ValueError("the sign vector belongs to the rotation")
+    z = rotate_rows(x_cal, d) if rotate else np.asarray(x_cal, dtype=np.float64)
+    c = np.max(np.abs(z), axis=0)
     return np.argsort(-c, kind="stable").astype(np.int32)
 
 
@@ -201,7 +206,7 @@ def rtn_codes(v: np.ndarray) -> np.ndarray:
     return np.clip(np.rint(v), -QMAX, QMAX).astype(np.int8)
 
 
-def prepare_weights(W: np.ndarray, perm: np.ndarray, d=None) -> Dict[str, np.ndarray]:
+def prepare_weights(W: np.ndarray, perm: np.ndarray, d=None, rotate: bool = True) -> Dict[str, np.ndarray]:
     """Offline weight side for Y = X W with W [K, N].
 
     Output-preserving transform ([AGC-OR] Sec. 3.1): rotating the activations
@@ -214,9 +219,14 @@ def prepare_weights(W: np.ndarray, perm: np.ndarray, d=None) -> Dict[str, np.nda
 
     Returns qw int8 [N, K] (K in permuted order), a = max|Wp| per output
     channel (float64 [N]), dw = a / 7, and the pre-rounding values uw [N, K].
+    ``rotate=False`` skips the transform (Wz = W; the weight side of Runtime
+    Smooth without rotation).
     """
     W = np.asarray(W)
-    Wz_t = rotate_rows(W.T, d)          # [N, K]: row n is (H D W)[:, n]
+    if not rotate and d is not None:
+        raise ValueError("the sign vector belongs to the rotation")
+    # [N, K]: row n is (H D W)[:, n], or W[:, n] without the rotation
+    Wz_t = rotate_rows(W.T, d) if rotate else W.T.astype(np.float64)
     Wp_t = Wz_t[:, perm]                # Wp[j, n] = Wz[perm[j], n]
     a = np.max(np.abs(Wp_t), axis=1)    # per output channel
     safe = np.where(a > 0, a, 1.0)
@@ -249,6 +259,8 @@ def frontend(X: np.ndarray, perm: np.ndarray, G: int, *, rotate: bool = True,
     M, K = X.shape
     if K % G:
         raise ValueError("G must divide K")
+    if not rotate and d is not None:
+        raise ValueError("the sign vector belongs to the rotation")
     Z = rotate_rows(X, d) if rotate else X.astype(np.float64)
     Zp = Z[:, perm]
     c = np.max(np.abs(Zp), axis=0) if M else np.zeros(K)
@@ -298,12 +310,13 @@ def group_partials_int64(q: np.ndarray, qw: np.ndarray, G: int) -> np.ndarray:
 
 
 def linear_out(q: np.ndarray, dx: np.ndarray, S: np.ndarray, qw: np.ndarray,
-               dw: np.ndarray, G: int) -> Dict[str, np.ndarray]:
+               dw: np.ndarray, G: int, rotated: bool = True) -> Dict[str, np.ndarray]:
     """Output of the A4W4 GEMM with group rescale (reading R12):
 
       Y[t, n] = (1/K) * dx_t * dw_n * sum_g S_g * P[t, n, g]
 
-    (1/K is the product of the two 1/sqrt(K) normalisations of H, R3.)
+    (1/K is the product of the two 1/sqrt(K) normalisations of H, R3; codes
+    made without the rotation, ``rotated=False``, carry no such factor.)
     Also returns the cancellation-free magnitude
       C[t, n] = (1/K) * |dx_t| * |dw_n| * sum_g S_g * |P[t, n, g]|
     used by the output tolerance (R13). Accumulates over groups without
@@ -320,16 +333,21 @@ def linear_out(q: np.ndarray, dx: np.ndarray, S: np.ndarray, qw: np.ndarray,
         P = qa[:, g, :] @ qb[:, g, :].T   # exact integers
         acc += S[g] * P
         mag += S[g] * np.abs(P)
-    scale = (dx[:, None] * dw[None, :]) / K
+    scale = (dx[:, None] * dw[None, :]) / (K if rotated else 1)
     return {"Y": scale * acc, "C": np.abs(scale) * mag}
 
 
-def rrs_linear(X: np.ndarray, W: np.ndarray, perm: np.ndarray, G: int, d=None) -> Dict[str, np.ndarray]:
+def rrs_linear(X: np.ndarray, W: np.ndarray, perm: np.ndarray, G: int, d=None, *,
+               rotate: bool = True, smooth: bool = True) -> Dict[str, np.ndarray]:
     """The whole RRS A4W4 linear: weights prepared offline, then the runtime
-    front end and the grouped integer GEMM (signed rotation when d is given)."""
-    wp = prepare_weights(W, perm, d)
-    fe = frontend(X, perm, G, d=d)
-    out = linear_out(fe["q"], fe["dx"], fe["S"], wp["qw"], wp["dw"], G)
+    front end and the grouped integer GEMM (signed rotation when d is given).
+    ``rotate`` and ``smooth`` switch the two components off for the
+    ablations of [RRS-rebuttal] "Incomplete ablation study": Runtime Smooth
+    alone (no rotation on either side) and the rotation alone (S = 1, the
+    per-channel A4W4 baseline)."""
+    wp = prepare_weights(W, perm, d, rotate=rotate)
+    fe = frontend(X, perm, G, rotate=rotate, smooth=smooth, d=d)
+    out = linear_out(fe["q"], fe["dx"], fe["S"], wp["qw"], wp["dw"], G, rotated=rotate)
     return {"fe": fe, "wp": wp, **out}
 
 
@@ -370,7 +388,9 @@ def unpack_codes(bts: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------- parity helpers
 def near_half(v: np.ndarray, window: float = 1e-5) -> np.ndarray:
     """Codes whose pre-rounding value lies within ``window`` of a .5 boundary:
-    either neighbouring integer is an acceptable code there."""
+    either neighbouring integer is an acceptable code there. The distance is
+    taken from |v| to the nearest k + 1/2 (k = floor |v|), so the rule is the
+    same for both signs."""
     a = np.abs(v)
     return np.abs(a - (np.floor(a) + 0.5)) < window
 

@@ -194,3 +194,38 @@ def kron_rotation_matches_explicit(hadamard_rows, hadamard_paley, cases=((12, 64
         if not np.array_equal(hadamard_rows(x), ref):
             return False
     return True
+
+
+# ------------------------------------------------- parity exemption window
+def near_half_window(near_half, w=1e-5) -> bool:
+    """The exemption rule of the code comparisons: a pre-rounding value is
+    exempt exactly when |v| lies within w of k + 1/2 for an integer k (either
+    neighbouring code is then correct). Values are chosen by hand: on both
+    sides of several boundaries and for both signs, just inside the window
+    (exempt), at twice the window and on integers (not exempt)."""
+    inside = [2.5, 2.5 + w / 2, 2.5 - w / 2, -3.5 + w / 2, -3.5 - w / 2, 0.5 + 0.9 * w, 6.5 - 0.9 * w]
+    outside = [3.0, 2.5 + 2 * w, 2.5 - 2 * w, -3.5 - 2 * w, 0.0, 1.0, -7.0, 7.0, 0.5 + 1.5 * w,
+               3.0 - w / 2, -2.0 + w / 2]
+    if w == 1e-5:  # literal values at the window the comparisons use
+        inside += [2.499995, -3.500004]
+        outside += [2.49, 2.5001]
+    a = near_half(np.array(inside, dtype=np.float64), w)
+    b = near_half(np.array(outside, dtype=np.float64), w)
+    return bool(np.all(a) and not np.any(b))
+
+
+def unrounded_output_is_xw_unrotated(frontend, prepare_weights, linear_out, seed=2,
+                                     M=10, K=96, N=12, G=1) -> bool:
+    """Runtime Smooth without the rotation (the ablation): with the
+    pre-rounding values in place of the codes, dx dw sum_g S_g sum_j v uw =
+    Zp Wp = X W exactly up to float64 rounding, with no 1/K (no Hadamard
+    pair). The reorder identity of [RRS-rebuttal] on the raw channels."""
+    g = np.random.default_rng(seed)
+    X = (g.standard_normal((M, K)) * np.where(g.random(K) < 0.1, 20, 1)).astype(np.float16)
+    W = (g.standard_normal((K, N)) * 0.02).astype(np.float16)
+    perm = g.permutation(K).astype(np.int32)
+    fe = frontend(X, perm, G, rotate=False)
+    wp = prepare_weights(W, perm, rotate=False)
+    out = linear_out(fe["v"], fe["dx"], fe["S"], wp["uw"], wp["dw"], G, rotated=False)
+    ref = X.astype(np.float64) @ W.astype(np.float64)
+    return bool(np.allclose(out["Y"], ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max()))

@@ -363,3 +363,88 @@ def test_kron_signed_rotation_explicit():
     d = np.where(g.random(m * n) < 0.5, -1.0, 1.0)
     ref = (x.astype(np.float64) * d) @ np.kron(oracle.hadamard_paley(m), scipy.linalg.hadamard(n).astype(np.float64))
     assert np.array_equal(oracle.rotate_rows(x, d), ref)
+
+
+# ------------------------------------------------------ exemption window
+def test_near_half_window():
+    assert pins.near_half_window(oracle.near_half)
+    assert pins.near_half_window(oracle.near_half, w=1e-3)
+
+
+# ------------------------------------- ablations: RS alone, rotation alone
+def test_unrotated_unrounded_output_equals_xw():
+    for G in (1, 32, 96):
+        assert pins.unrounded_output_is_xw_unrotated(oracle.frontend, oracle.prepare_weights,
+                                                     oracle.linear_out, G=G)
+
+
+def test_unrotated_weights_are_reordered_raw_columns():
+    """Without the rotation the weight side is W's rows in perm order,
+    quantised per output channel: a hand check on a tiny matrix."""
+    W = np.array([[0.5, -1.0], [2.0, 0.25], [-1.0, 0.0], [0.0, 0.5]], dtype=np.float16)
+    perm = np.array([2, 0, 3, 1], dtype=np.int32)
+    wp = oracle.prepare_weights(W, perm, rotate=False)
+    # column 0 reordered: [-1, 0.5, 0, 2], max 2 -> 7 x / 2 = [-3.5, 1.75, 0, 7]
+    # -> rne: [-4, 2, 0, 7]; column 1: [0, -1, 0.5, 0.25], max 1 -> [0, -7, 3.5, 1.75] -> [0, -7, 4, 2]
+    assert np.array_equal(wp["qw"], [[-4, 2, 0, 7], [0, -7, 4, 2]])
+    assert np.array_equal(wp["a"], [2.0, 1.0])
+
+
+def test_calibrate_perm_unrotated_brute_force():
+    g = np.random.default_rng(9)
+    K = 24
+    xc = g.integers(-4, 5, size=(5, K)).astype(np.float16)
+    perm = oracle.calibrate_perm(xc, rotate=False)
+    c = np.abs(xc.astype(np.float64)).max(axis=0)
+    assert list(perm) == sorted(range(K), key=lambda k: (-c[k], k))
+    with pytest.raises(ValueError):
+        oracle.calibrate_perm(xc, d=np.ones(K), rotate=False)
+
+
+def test_G1_is_per_channel_runtime_smooth():
+    """G = 1: every reordered channel has its own scale, its |max| over the
+    call's tokens (per-channel Runtime Smooth); without the rotation the
+    smoothed activations are the raw channels divided by that max."""
+    x, perm, _ = _case(seed=11, M=30, K=256, G=64)
+    x[:, 7] = 0                                   # one all-zero channel -> scale 1
+    fe = oracle.frontend(x, perm, 1, rotate=False)
+    xp = x.astype(np.float64)[:, perm]
+    c = np.abs(xp).max(axis=0)
+    assert np.array_equal(fe["S"], np.where(c > 0, c, 1.0))
+    assert np.array_equal(fe["U"], xp / np.where(c > 0, c, 1.0)[None, :])
+    nz = c > 0
+    assert np.all(np.abs(fe["U"][:, nz]).max(axis=0) == 1.0)
+    fe_r = oracle.frontend(x, perm, 1)
+    assert np.all(np.abs(fe_r["U"]).max(axis=0)[np.abs(fe_r["Zp"]).max(axis=0) > 0] == 1.0)
+
+
+def test_rs_without_rotation_degrades_with_group_size():
+    """Non-gating context check of the pages' qualitative claim that Runtime
+    Smooth without the rotation loses accuracy as the group grows while the
+    rotated form barely moves ([RRS-summary] "Surprising findings" and
+    "Limitations"): ordering only, on the tiny workload."""
+    wl = workloads.WORKLOADS["tiny"]
+    x, w, xc = workloads.runtime_x(wl), workloads.weights(wl), workloads.calib_x(wl)
+    ref = x.astype(np.float64) @ w.astype(np.float64)
+
+    def err(G, rotate):
+        perm = oracle.calibrate_perm(xc, rotate=rotate)
+        y = oracle.rrs_linear(x, w, perm, G, rotate=rotate)["Y"]
+        return np.linalg.norm(y - ref) / np.linalg.norm(ref)
+
+    rs = [err(G, False) for G in (1, 32, 128)]
+    rrs = [err(G, True) for G in (1, 32, 128)]
+    assert rs[0] < rs[1] < rs[2]
+    assert rrs[2] < rs[2]
+    assert max(rrs) - min(rrs) < rs[2] - rs[0]
+
+
+def test_rotation_only_is_per_token_rtn_of_rotated_rows():
+    """smooth=False (S = 1) is the per-channel A4W4 baseline: the codes are
+    per-token round-to-nearest of the rotated, reordered row."""
+    x, perm, G = _case(seed=12)
+    fe = oracle.frontend(x, perm, G, smooth=False)
+    zp = pins.hadamard_popcount(x.shape[1])
+    z = (x.astype(np.float64) @ zp)[:, perm]
+    r = np.abs(z).max(axis=1)
+    assert np.array_equal(fe["q"], np.clip(np.rint(7 * z / r[:, None]), -7, 7).astype(np.int8))

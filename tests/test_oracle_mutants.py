@@ -151,3 +151,25 @@ def test_paley_wrong_character_mutant_fails():
         H[1:, 0] = 1.0
         return H
     assert not pins.paley_is_hadamard(bad, orders=(12,))
+
+
+def test_near_half_mutants_fail():
+    # distance to the nearest integer instead of the nearest half
+    assert not pins.near_half_window(lambda v, w=1e-5: np.abs(np.abs(v) - np.rint(np.abs(v))) < w)
+    # a boundary off by a half step (k instead of k + 1/2 past the floor)
+    assert not pins.near_half_window(lambda v, w=1e-5: np.abs(np.abs(v) - np.floor(np.abs(v))) < w)
+    # window ten times too wide
+    assert not pins.near_half_window(lambda v, w=1e-5: oracle.near_half(v, 10 * w), 1e-5)
+
+
+def test_unrotated_output_with_1_over_K_fails():
+    def linear_out_always_k(q, dx, S, qw, dw, G, rotated=True):
+        return oracle.linear_out(q, dx, S, qw, dw, G, rotated=True)
+    assert not pins.unrounded_output_is_xw_unrotated(oracle.frontend, oracle.prepare_weights, linear_out_always_k)
+
+
+def test_unrotated_weights_still_rotated_fails():
+    def prep_always_rotated(W, perm, d=None, rotate=True):
+        return oracle.prepare_weights(W, perm, d)
+    assert not pins.unrounded_output_is_xw_unrotated(oracle.frontend, prep_always_rotated, oracle.linear_out,
+                                                     K=128)
