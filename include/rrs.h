@@ -16,7 +16,10 @@
  *      and pack two codes per byte;
  *   4. multiply against offline rotated, reordered, per-output-channel 4-bit
  *      weights, rescaling each K-group's integer partial sum by its group
- *      scale before fp32 accumulation.
+ *      scale before fp32 accumulation (the smoothing scales stay out of the
+ *      weights: RRS summary page, "Approach"; the group-wise scales are
+ *      chosen so that the contraction keeps its tiled computation scheme:
+ *      RRS rebuttal page, "Novelty" answer).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -125,6 +128,12 @@ int rrs_calibrate_perm(const void* X_cal_fp16, int T, int K, int32_t* perm,
 int rrs_calibrate_perm_signed(const void* X_cal_fp16, int T, int K,
                               const uint32_t* dsign, int32_t* perm, void* ws,
                               size_t ws_bytes, hipStream_t s);
+/* Either of the above (dsign NULL or not) or, with flags =
+ * RRS_FLAG_NO_ROTATE, the order of the raw channels' maxima (calibration for
+ * Runtime Smooth alone; dsign must be NULL). No other flag is accepted. */
+int rrs_calibrate_perm_ex(const void* X_cal_fp16, int T, int K,
+                          const uint32_t* dsign, int flags, int32_t* perm,
+                          void* ws, size_t ws_bytes, hipStream_t s);
 
 /* Offline weight preparation (output-preserving transform of the AGC-OR page,
  * Sec. 3.1; reorder answer of the RRS rebuttal page; per-output-channel
@@ -138,6 +147,13 @@ int rrs_prepare_weights(const void* W_fp16, int K, int N, const int32_t* perm,
 int rrs_prepare_weights_signed(const void* W_fp16, int K, int N,
                                const int32_t* perm, const uint32_t* dsign,
                                void* wq, hipStream_t s);
+/* Either of the above (dsign NULL or not) or, with flags =
+ * RRS_FLAG_NO_ROTATE, the weight side of Runtime Smooth alone: Wz = W (no
+ * rotation; dsign must be NULL), reordered and quantised the same way. No
+ * other flag is accepted (RRS_EINVAL). */
+int rrs_prepare_weights_ex(const void* W_fp16, int K, int N,
+                           const int32_t* perm, const uint32_t* dsign, int flags,
+                           void* wq, hipStream_t s);
 
 /* The RRS A4W4 linear layer: Y fp32 [M, N] = RRS(X) against prepared weights.
  * `ws` holds rrs_workspace_bytes(M, K, G) bytes, initialised once with
@@ -152,6 +168,27 @@ int rrs_linear(const void* X_fp16, int M, int K, int N, int G,
 int rrs_linear_signed(const void* X_fp16, int M, int K, int N, int G,
                       const int32_t* perm, const uint32_t* dsign, const void* wq,
                       float* Y, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* The layer with the component switches of the RRS rebuttal page
+ * ("Incomplete ablation study": online smoothing, reordering and rotation
+ * as separable parts). `flags` as for rrs_frontend:
+ *   0                  the full method (same as rrs_linear / _signed);
+ *   RRS_FLAG_NO_ROTATE Runtime Smooth alone: no rotation on either side,
+ *                      so wq must come from rrs_prepare_weights_ex with
+ *                      RRS_FLAG_NO_ROTATE (and perm from calibration on
+ *                      the raw channels); Y = dx dw sum_g S_g P_g, with
+ *                      no 1/K (no Hadamard pair to undo);
+ *   RRS_FLAG_NO_SMOOTH the rotation alone (S = 1): per-token 4-bit
+ *                      activations of the rotated rows against the same
+ *                      rotated weights, the per-channel A4W4 baseline;
+ *   RRS_FLAG_TWO_PASS, RRS_FLAG_TEST_GIVE_UP as for rrs_frontend.
+ * dsign: the signed rotation's mask, or NULL (rejected with
+ * RRS_FLAG_NO_ROTATE). Mixing weights prepared for one form with another
+ * form's call is outside the contract (the buffer does not record it). */
+int rrs_linear_ex(const void* X_fp16, int M, int K, int N, int G,
+                  const int32_t* perm, const uint32_t* dsign, int flags,
+                  const void* wq, float* Y, void* ws, size_t ws_bytes,
+                  hipStream_t s);
 
 /* Front end alone (same kernels as rrs_linear): writes xq uint8 [M][K/2],
  * dx fp32 [M] and S fp32 [K/G] (zero groups reported as 1). `ws` holds at
@@ -182,10 +219,25 @@ int rrs_linear_signed(const void* X_fp16, int M, int K, int N, int G,
  * all arrive (for example when another such call on another stream holds
  * part of the device), the kernel still ends, with wrong codes, and sets
  * word 2 of the workspace (the error word) to nonzero; the word stays set
- * until rrs_workspace_init. */
+ * until rrs_workspace_init. A workgroup that gives up also writes NaN into
+ * the token scales dx of its rows (and into S if it is the workgroup that
+ * writes S), so a given-up wait never looks like a result; rrs_linear
+ * additionally writes NaN into all of Y while the error word is set, and a
+ * one-launch front end that finds the error word set gives up at once (no
+ * wait), so every later call on that workspace fails the same visible way
+ * until it is initialised again.
+ * Because of the co-residency requirement, run one-launch calls that share
+ * the device on one stream (calls on two streams can starve each other
+ * until the spin limit, after which both fail visibly as above).
+ *
+ * RRS_FLAG_TEST_GIVE_UP exists for tests of that failure path: the
+ * one-launch wait gives up at once in every workgroup (error word set,
+ * outputs marked), and every kernel still ends normally. It changes
+ * nothing in the three-launch form or without smoothing. */
 #define RRS_FLAG_NO_ROTATE 1
 #define RRS_FLAG_NO_SMOOTH 2
 #define RRS_FLAG_TWO_PASS 4
+#define RRS_FLAG_TEST_GIVE_UP 8
 int rrs_frontend(const void* X_fp16, int M, int K, int G, const int32_t* perm,
                  uint8_t* xq, float* dx, float* S, void* ws, size_t ws_bytes,
                  int flags, hipStream_t s);
@@ -205,7 +257,13 @@ int rrs_frontend_signed(const void* X_fp16, int M, int K, int G,
 int rrs_frontend_passes(int M, int K, int flags);
 
 /* Grouped integer GEMM alone (same kernels as rrs_linear): Y = (1/K) dx dw
- * sum_g S_g P_g with P_g the int32 group partials of the 4-bit codes. */
+ * sum_g S_g P_g with P_g the int32 group partials of the 4-bit codes; each
+ * group's exact partial is multiplied by its smoothing scale S_g before the
+ * fp32 accumulation (RRS summary page, "Approach": the scales are not
+ * migrated into the weights; RRS rebuttal page, "Novelty": group-wise
+ * scales keep the GEMM's tiled scheme). xq uint8 [M][K/2] and dx fp32 [M]
+ * as rrs_frontend writes them, S fp32 [K/G], wq a prepared weight buffer,
+ * Y fp32 [M, N] (fully overwritten). */
 int rrs_gemm(const uint8_t* xq, const float* dx, const float* S, int M, int K,
              int N, int G, const void* wq, float* Y, hipStream_t s);
 
@@ -225,9 +283,15 @@ int rrs_gemm(const uint8_t* xq, const float* dx, const float* S, int M, int K,
 int rrs_gemm_form(int M, int K, int N, int G);
 
 /* The int32 group partials P[t-m0][n-n0][g] = sum_{j in group g} q[t,j]
- * qw[n,j] for m0 <= t < m1, n0 <= n < n1, computed by the main loop of the
- * tiled kernel (for exactness checks; at every M). P is int32
- * [m1-m0][n1-n0][K/G]. */
+ * qw[n,j] for m0 <= t < m1, n0 <= n < n1 (the integer contraction of step 4
+ * before its group scales; RRS rebuttal page, "Novelty"), for exactness
+ * checks. They come from the same kernel instantiation that rrs_gemm runs
+ * for (M, K, N, G) (rrs_gemm_form tells which), with its K split across
+ * waves and its rescale points: where that kernel multiplies the
+ * accumulator by S_{g-1}/S_g this one multiplies it by 0, and each group's
+ * integer sum (or each wave's integer piece of it) is written (added) into
+ * P. P is int32 [m1-m0][n1-n0][K/G] (device); xq and wq as for rrs_gemm.
+ * The few-token kernel clears the window of P on `s` before adding. */
 int rrs_gemm_partials(const uint8_t* xq, int M, int K, int N, int G,
                       const void* wq, int m0, int m1, int n0, int n1,
                       int32_t* P, hipStream_t s);

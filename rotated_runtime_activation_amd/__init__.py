@@ -21,6 +21,7 @@ RRS_OK, RRS_EINVAL, RRS_EUNSUPPORTED, RRS_EHIP = 0, -1, -2, -3
 RRS_FLAG_NO_ROTATE = 1
 RRS_FLAG_NO_SMOOTH = 2
 RRS_FLAG_TWO_PASS = 4
+RRS_FLAG_TEST_GIVE_UP = 8
 
 # every symbol include/rrs.h declares
 EXPORTS = (
@@ -29,7 +30,7 @@ EXPORTS = (
     "rrs_calibrate_perm", "rrs_prepare_weights", "rrs_linear", "rrs_frontend", "rrs_gemm",
     "rrs_gemm_partials", "rrs_frontend_passes", "rrs_gemm_form",
     "rrs_calibrate_perm_signed", "rrs_prepare_weights_signed", "rrs_linear_signed",
-    "rrs_frontend_signed",
+    "rrs_frontend_signed", "rrs_calibrate_perm_ex", "rrs_prepare_weights_ex", "rrs_linear_ex",
 )
 
 
@@ -68,6 +69,9 @@ def _declare(lib):
         "rrs_prepare_weights_signed": (i, [vp, i, i, vp, vp, vp, vp]),
         "rrs_linear_signed": (i, [vp, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]),
         "rrs_frontend_signed": (i, [vp, i, i, i, vp, vp, vp, vp, vp, vp, sz, i, vp]),
+        "rrs_calibrate_perm_ex": (i, [vp, i, i, vp, i, vp, vp, sz, vp]),
+        "rrs_prepare_weights_ex": (i, [vp, i, i, vp, vp, i, vp, vp]),
+        "rrs_linear_ex": (i, [vp, i, i, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -256,6 +260,37 @@ def rrs_frontend_signed(X, G: int, perm, dsign, xq, dx, S, ws, flags: int = 0, s
         _dev(xq, torch.uint8, "xq", (M, K // 2)), _dev(dx, torch.float32, "dx", (M,)),
         _dev(S, torch.float32, "S", (K // G,)), _dev(ws, None, "ws"), _nbytes(ws), flags,
         _stream(stream)))
+
+
+# component switches (flags): dsign is None or the int32 [K/32] sign mask
+def _opt_sign(dsign, K: int) -> int:
+    return 0 if dsign is None else _dev(dsign, _torch().int32, "dsign", (K // 32,))
+
+
+def rrs_calibrate_perm_ex(X_cal, dsign, flags: int, perm, ws, stream=None) -> None:
+    torch = _torch()
+    T, K = X_cal.shape
+    _check("rrs_calibrate_perm_ex", lib().rrs_calibrate_perm_ex(
+        _dev(X_cal, torch.float16, "X_cal"), T, K, _opt_sign(dsign, K), flags,
+        _dev(perm, torch.int32, "perm", (K,)), _dev(ws, None, "ws"), _nbytes(ws), _stream(stream)))
+
+
+def rrs_prepare_weights_ex(W, perm, dsign, flags: int, wq, stream=None) -> None:
+    torch = _torch()
+    K, N = W.shape
+    _check("rrs_prepare_weights_ex", lib().rrs_prepare_weights_ex(
+        _dev(W, torch.float16, "W"), K, N, _dev(perm, torch.int32, "perm", (K,)), _opt_sign(dsign, K), flags,
+        _dev(wq, torch.uint8, "wq", min_numel=rrs_weight_bytes(K, N)), _stream(stream)))
+
+
+def rrs_linear_ex(X, G: int, perm, dsign, flags: int, wq, Y, ws, stream=None) -> None:
+    torch = _torch()
+    M, K = X.shape
+    N = Y.shape[1]
+    _check("rrs_linear_ex", lib().rrs_linear_ex(
+        _dev(X, torch.float16, "X"), M, K, N, G, _dev(perm, torch.int32, "perm", (K,)), _opt_sign(dsign, K),
+        flags, _dev(wq, torch.uint8, "wq", min_numel=rrs_weight_bytes(K, N)),
+        _dev(Y, torch.float32, "Y", (M, N)), _dev(ws, None, "ws"), _nbytes(ws), _stream(stream)))
 
 
 def rrs_gemm(xq, dx, S, G: int, wq, Y, stream=None) -> None:

@@ -104,31 +104,40 @@ RRS_API int rrs_workspace_init(void* ws, size_t ws_bytes, hipStream_t s) {
 
 namespace {
 
-int calibrate_impl(const void* X_cal_fp16, int T, int K, const uint32_t* dsign, int32_t* perm, void* ws,
-                   size_t ws_bytes, hipStream_t s) {
+constexpr int kFrontendFlags = RRS_FLAG_NO_ROTATE | RRS_FLAG_NO_SMOOTH | RRS_FLAG_TWO_PASS | RRS_FLAG_TEST_GIVE_UP;
+static_assert(RRS_FLAG_NO_ROTATE == rrs::kFlagNoRotate && RRS_FLAG_NO_SMOOTH == rrs::kFlagNoSmooth &&
+                  RRS_FLAG_TWO_PASS == rrs::kFlagTwoPass && RRS_FLAG_TEST_GIVE_UP == rrs::kFlagGiveUp,
+              "public and internal flag values agree");
+
+int calibrate_impl(const void* X_cal_fp16, int T, int K, const uint32_t* dsign, int flags, int32_t* perm,
+                   void* ws, size_t ws_bytes, hipStream_t s) {
   if (X_cal_fp16 == nullptr || perm == nullptr || ws == nullptr) return RRS_EINVAL;
   if (T < 1 || !valid_K(K)) return RRS_EINVAL;
+  if (flags & ~RRS_FLAG_NO_ROTATE) return RRS_EINVAL;
+  if (dsign != nullptr && (flags & RRS_FLAG_NO_ROTATE)) return RRS_EINVAL;  // the signs belong to the rotation
   if (ws_bytes < rrs_calibrate_workspace_bytes(K)) return RRS_EINVAL;
   if (!all_a16(X_cal_fp16, perm, ws, dsign)) return RRS_EINVAL;
   return hip_status(rrs::launch_calibrate(static_cast<const uint16_t*>(X_cal_fp16), T, K, dsign, perm,
-                                          static_cast<uint32_t*>(ws), s));
+                                          static_cast<uint32_t*>(ws), s, !(flags & RRS_FLAG_NO_ROTATE)));
 }
 
-int prepare_impl(const void* W_fp16, int K, int N, const int32_t* perm, const uint32_t* dsign, void* wq,
-                 hipStream_t s) {
+int prepare_impl(const void* W_fp16, int K, int N, const int32_t* perm, const uint32_t* dsign, int flags,
+                 void* wq, hipStream_t s) {
   if (W_fp16 == nullptr || perm == nullptr || wq == nullptr) return RRS_EINVAL;
   if (!valid_K(K) || N < 1) return RRS_EINVAL;
+  if (flags & ~RRS_FLAG_NO_ROTATE) return RRS_EINVAL;
+  if (dsign != nullptr && (flags & RRS_FLAG_NO_ROTATE)) return RRS_EINVAL;
   if (!all_a16(W_fp16, perm, wq, dsign)) return RRS_EINVAL;
   uint8_t* codes = static_cast<uint8_t*>(wq);
   float* dw = reinterpret_cast<float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
   return hip_status(rrs::launch_weight_prep(static_cast<const uint16_t*>(W_fp16), K, N, perm, dsign,
-                                            codes, dw, s));
+                                            codes, dw, s, !(flags & RRS_FLAG_NO_ROTATE)));
 }
 
 int frontend_impl(const void* X_fp16, int M, int K, int G, const int32_t* perm, const uint32_t* dsign,
                   uint8_t* xq, float* dx, float* S, void* ws, size_t ws_bytes, int flags, hipStream_t s) {
   if (M < 0 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;
-  if (flags & ~(RRS_FLAG_NO_ROTATE | RRS_FLAG_NO_SMOOTH | RRS_FLAG_TWO_PASS)) return RRS_EINVAL;
+  if (flags & ~kFrontendFlags) return RRS_EINVAL;
   if (dsign != nullptr && (flags & RRS_FLAG_NO_ROTATE)) return RRS_EINVAL;  // the signs belong to the rotation
   if (perm == nullptr || S == nullptr || ws == nullptr) return RRS_EINVAL;
   if (M > 0 && (X_fp16 == nullptr || xq == nullptr || dx == nullptr)) return RRS_EINVAL;
@@ -154,8 +163,10 @@ int frontend_impl(const void* X_fp16, int M, int K, int G, const int32_t* perm, 
 }
 
 int linear_impl(const void* X_fp16, int M, int K, int N, int G, const int32_t* perm, const uint32_t* dsign,
-                const void* wq, float* Y, void* ws, size_t ws_bytes, hipStream_t s) {
+                int flags, const void* wq, float* Y, void* ws, size_t ws_bytes, hipStream_t s) {
   if (M < 0 || N < 1 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;
+  if (flags & ~kFrontendFlags) return RRS_EINVAL;
+  if (dsign != nullptr && (flags & RRS_FLAG_NO_ROTATE)) return RRS_EINVAL;
   if (perm == nullptr || wq == nullptr || ws == nullptr) return RRS_EINVAL;
   if (M > 0 && (X_fp16 == nullptr || Y == nullptr)) return RRS_EINVAL;
   const WsLayout l = ws_layout(M, K, G);
@@ -167,36 +178,51 @@ int linear_impl(const void* X_fp16, int M, int K, int N, int G, const int32_t* p
   float* dx = reinterpret_cast<float*>(base + l.dx);
   float* S = reinterpret_cast<float*>(base + l.S);
   float* zrows = l.rows_bytes ? reinterpret_cast<float*>(base + l.rows) : nullptr;
+  uint32_t* sync = reinterpret_cast<uint32_t*>(base + l.sync);
   hipError_t e = rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, K, G, perm, dsign, xq, dx,
-                                      S, reinterpret_cast<uint32_t*>(base + l.sync), 0, s, zrows);
+                                      S, sync, flags, s, zrows);
   if (e != hipSuccess) return RRS_EHIP;
   const uint8_t* codes = static_cast<const uint8_t*>(wq);
   const float* dw = reinterpret_cast<const float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
-  return hip_status(rrs::launch_gemm(xq, dx, S, M, K, N, G, codes, dw, Y, nullptr, 0, 0, 0, 0, s));
+  // the GEMM reads the workspace's error word: a front end whose grid-wide
+  // wait gave up (now or in an earlier call on this workspace) makes Y NaN
+  const rrs::GemmCall gc{xq, dx, S, M, K, N, G, codes, dw, Y, nullptr, 0, 0, 0, 0,
+                         !(flags & RRS_FLAG_NO_ROTATE), sync + rrs::kSyncError};
+  return hip_status(rrs::launch_gemm(gc, s));
 }
 
 }  // namespace
 
 RRS_API int rrs_calibrate_perm(const void* X_cal_fp16, int T, int K, int32_t* perm, void* ws,
                                size_t ws_bytes, hipStream_t s) {
-  return calibrate_impl(X_cal_fp16, T, K, nullptr, perm, ws, ws_bytes, s);
+  return calibrate_impl(X_cal_fp16, T, K, nullptr, 0, perm, ws, ws_bytes, s);
 }
 
 RRS_API int rrs_calibrate_perm_signed(const void* X_cal_fp16, int T, int K, const uint32_t* dsign, int32_t* perm,
                                       void* ws, size_t ws_bytes, hipStream_t s) {
   if (dsign == nullptr) return RRS_EINVAL;
-  return calibrate_impl(X_cal_fp16, T, K, dsign, perm, ws, ws_bytes, s);
+  return calibrate_impl(X_cal_fp16, T, K, dsign, 0, perm, ws, ws_bytes, s);
+}
+
+RRS_API int rrs_calibrate_perm_ex(const void* X_cal_fp16, int T, int K, const uint32_t* dsign, int flags,
+                                  int32_t* perm, void* ws, size_t ws_bytes, hipStream_t s) {
+  return calibrate_impl(X_cal_fp16, T, K, dsign, flags, perm, ws, ws_bytes, s);
 }
 
 RRS_API int rrs_prepare_weights(const void* W_fp16, int K, int N, const int32_t* perm, void* wq,
                                 hipStream_t s) {
-  return prepare_impl(W_fp16, K, N, perm, nullptr, wq, s);
+  return prepare_impl(W_fp16, K, N, perm, nullptr, 0, wq, s);
 }
 
 RRS_API int rrs_prepare_weights_signed(const void* W_fp16, int K, int N, const int32_t* perm,
                                        const uint32_t* dsign, void* wq, hipStream_t s) {
   if (dsign == nullptr) return RRS_EINVAL;
-  return prepare_impl(W_fp16, K, N, perm, dsign, wq, s);
+  return prepare_impl(W_fp16, K, N, perm, dsign, 0, wq, s);
+}
+
+RRS_API int rrs_prepare_weights_ex(const void* W_fp16, int K, int N, const int32_t* perm, const uint32_t* dsign,
+                                   int flags, void* wq, hipStream_t s) {
+  return prepare_impl(W_fp16, K, N, perm, dsign, flags, wq, s);
 }
 
 RRS_API int rrs_frontend(const void* X_fp16, int M, int K, int G, const int32_t* perm, uint8_t* xq,
@@ -213,7 +239,7 @@ RRS_API int rrs_frontend_signed(const void* X_fp16, int M, int K, int G, const i
 
 RRS_API int rrs_frontend_passes(int M, int K, int flags) {
   if (M < 1 || !valid_K(K)) return RRS_EINVAL;
-  if (flags & ~(RRS_FLAG_NO_ROTATE | RRS_FLAG_NO_SMOOTH | RRS_FLAG_TWO_PASS)) return RRS_EINVAL;
+  if (flags & ~kFrontendFlags) return RRS_EINVAL;
   const int n = rrs::frontend_launches(M, K, flags);
   return n > 0 ? n : RRS_EHIP;
 }
@@ -227,7 +253,8 @@ RRS_API int rrs_gemm(const uint8_t* xq, const float* dx, const float* S, int M, 
   if (M == 0) return RRS_OK;
   const uint8_t* codes = static_cast<const uint8_t*>(wq);
   const float* dw = reinterpret_cast<const float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
-  return hip_status(rrs::launch_gemm(xq, dx, S, M, K, N, G, codes, dw, Y, nullptr, 0, 0, 0, 0, s));
+  const rrs::GemmCall gc{xq, dx, S, M, K, N, G, codes, dw, Y, nullptr, 0, 0, 0, 0, true, nullptr};
+  return hip_status(rrs::launch_gemm(gc, s));
 }
 
 RRS_API int rrs_gemm_form(int M, int K, int N, int G) {
@@ -243,18 +270,24 @@ RRS_API int rrs_gemm_partials(const uint8_t* xq, int M, int K, int N, int G, con
   if (!all_a16(xq, wq, P)) return RRS_EINVAL;
   const uint8_t* codes = static_cast<const uint8_t*>(wq);
   const float* dw = reinterpret_cast<const float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
-  return hip_status(rrs::launch_gemm(xq, nullptr, nullptr, M, K, N, G, codes, dw, nullptr, P, m0,
-                                     m1, n0, n1, s));
+  const rrs::GemmCall gc{xq, nullptr, nullptr, M, K, N, G, codes, dw, nullptr, P, m0, m1, n0, n1, true, nullptr};
+  return hip_status(rrs::launch_gemm(gc, s));
 }
 
 RRS_API int rrs_linear(const void* X_fp16, int M, int K, int N, int G, const int32_t* perm,
                        const void* wq, float* Y, void* ws, size_t ws_bytes, hipStream_t s) {
-  return linear_impl(X_fp16, M, K, N, G, perm, nullptr, wq, Y, ws, ws_bytes, s);
+  return linear_impl(X_fp16, M, K, N, G, perm, nullptr, 0, wq, Y, ws, ws_bytes, s);
 }
 
 RRS_API int rrs_linear_signed(const void* X_fp16, int M, int K, int N, int G, const int32_t* perm,
                               const uint32_t* dsign, const void* wq, float* Y, void* ws, size_t ws_bytes,
                               hipStream_t s) {
   if (dsign == nullptr) return RRS_EINVAL;
-  return linear_impl(X_fp16, M, K, N, G, perm, dsign, wq, Y, ws, ws_bytes, s);
+  return linear_impl(X_fp16, M, K, N, G, perm, dsign, 0, wq, Y, ws, ws_bytes, s);
+}
+
+RRS_API int rrs_linear_ex(const void* X_fp16, int M, int K, int N, int G, const int32_t* perm,
+                          const uint32_t* dsign, int flags, const void* wq, float* Y, void* ws, size_t ws_bytes,
+                          hipStream_t s) {
+  return linear_impl(X_fp16, M, K, N, G, perm, dsign, flags, wq, Y, ws, ws_bytes, s);
 }

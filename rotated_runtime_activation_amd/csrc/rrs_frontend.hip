@@ -78,6 +78,7 @@ struct FeArgs {
   float* S_out;         // [K/G]
   uint32_t* colmax;     // [K] (calibration)
   const uint8_t* dsign; // signed rotation: K-bit mask, bit j set -> channel j negated (nullptr: none)
+  uint32_t spin_limit;  // polls before the one-launch wait gives up (0: after the first)
 };
 
 __device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
@@ -482,7 +483,7 @@ template <int LOG2K>
 __device__ __forceinline__ void quantise_block(const float (&v)[Cfg<LOG2K>::kE],
                                                const float (&m)[Cfg<LOG2K>::kE / 32], const float* s_inv,
                                                int log2G, uint8_t* codes, float* scale, int rows, int row0,
-                                               int lane) {
+                                               int lane, bool bad = false) {
   constexpr int K = 1 << LOG2K, E = Cfg<LOG2K>::kE, NS = E / 32;
   const int rl = (E * lane) >> LOG2K;
   const int j0 = (E * lane) & (K - 1);
@@ -511,7 +512,8 @@ __device__ __forceinline__ void quantise_block(const float (&v)[Cfg<LOG2K>::kE],
 #pragma unroll
     for (int o = 0; o < E / 32; ++o)
       reinterpret_cast<uint4*>(dst)[o] = make_uint4(packed[4 * o], packed[4 * o + 1], packed[4 * o + 2], packed[4 * o + 3]);
-    if (j0 == 0) scale[row0 + rl] = rmax / 7.f;
+    // a workgroup whose wait gave up marks its rows' scales
+    if (j0 == 0) scale[row0 + rl] = bad ? __builtin_nanf("") : rmax / 7.f;
   }
 }
 
@@ -615,8 +617,12 @@ frontend_kernel(FeArgs a) {
       // channel |max| over the block's rows (LDS), folded into global below
 #pragma unroll
       for (int r = 0; r < E; ++r) {
-        const int f = LOG2K >= 12 ? mfma_elem<LOG2K>(lane, r)
-                                  : (lane & 7) | ((r & 63) << 3) | ((lane >> 3) << 9) | ((r >> 6) << 12);
+        // block element in register r of this lane: the rotations' output
+        // layouts, or the load layout (f = 8 lane + 512 i + e in register
+        // 8 i + e) without the rotation
+        const int f = !ROTATE        ? (r & 7) | (lane << 3) | ((r >> 3) << 9)
+                      : LOG2K >= 12 ? mfma_elem<LOG2K>(lane, r)
+                                    : (lane & 7) | ((r & 63) << 3) | ((lane >> 3) << 9) | ((r >> 6) << 12);
         if (row0 + (f >> LOG2K) < a.rows)
           atomicMax(&s_tab[f & (K - 1)], __float_as_uint(fabsf(v[r])));
       }
@@ -720,6 +726,10 @@ fused_kernel(FeArgs a) {
   // see the next call's value
   const uint32_t epoch =
       __hip_atomic_load(&a.sync[kSyncEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  // a workspace whose wait failed before (error word set until it is
+  // initialised again) holds tags of no use: give up at once
+  const uint32_t spin_limit =
+      __hip_atomic_load(&a.sync[kSyncError], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? 0u : a.spin_limit;
 
   table_fill<LOG2K, ROTATE>(s_tab, tl, tid);
   for (int g = tid; g < ngroups; g += C::kThreads) s_grp[g] = 0.f;
@@ -764,6 +774,7 @@ fused_kernel(FeArgs a) {
   __syncthreads();
 
   // ---- S_g = max over the workgroups' rows (all loads of a poll in flight) --
+  bool gave_up = false;
   {
     constexpr int kBatch = 16;
     const int n = nwg * ngroups;
@@ -778,12 +789,12 @@ fused_kernel(FeArgs a) {
           const int idx = base + k * C::kThreads;
           b[k] = idx < n ? __hip_atomic_load(&part[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag;
         }
-        bool all = true;
+        bool all = spin_limit > 0;
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) all &= (b[k] >> 32) == epoch;
         if (all) break;
-        if (++it == kSpinLimit) {
-          atomicOr(&a.sync[kSyncError], 1u);
+        if (++it >= spin_limit) {
+          gave_up = true;
           break;
         }
         __builtin_amdgcn_s_sleep(2);
@@ -800,15 +811,18 @@ fused_kernel(FeArgs a) {
     }
     if (same_group && mx) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[tid % ngroups]), mx);
   }
-  __syncthreads();
-  // every workgroup has read the old epoch (it tagged its row with old + 1)
-  if (blockIdx.x == 0 && tid == 0)
+  // a workgroup that gave up raises the error word and marks its outputs
+  gave_up = __syncthreads_or(gave_up);
+  if (gave_up && tid == 0) atomicOr(&a.sync[kSyncError], 1u);
+  // every workgroup has read the old epoch (it tagged its row with old + 1);
+  // a failed call leaves it
+  if (blockIdx.x == 0 && tid == 0 && !gave_up)
     __hip_atomic_store(&a.sync[kSyncEpoch], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   for (int g = tid; g < ngroups; g += C::kThreads) {
     float sg = s_grp[g];
     if (!(sg > 0.f)) sg = 1.f;  // all-zero group over every token
-    if (blockIdx.x == 0) a.S_out[g] = sg;
+    if (blockIdx.x == 0) a.S_out[g] = gave_up ? __builtin_nanf("") : sg;
     s_grp[g] = 1.f / sg;
   }
   __syncthreads();
@@ -816,7 +830,7 @@ fused_kernel(FeArgs a) {
   // ---- smooth, quantise, pack ------------------------------------------------
 #pragma unroll
   for (int q = 0; q < R; ++q)
-    quantise_block<LOG2K>(v[q], m[q], s_grp, a.log2G, a.codes, a.scale, a.rows, row0[q], lane);
+    quantise_block<LOG2K>(v[q], m[q], s_grp, a.log2G, a.codes, a.scale, a.rows, row0[q], lane, gave_up);
 }
 
 // Stable descending rank: perm[rank(j)] = j with rank(j) = #{i : c_i > c_j}
@@ -987,6 +1001,12 @@ __global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a
   const uint32_t epoch = (RM == kRowOne && a.smooth)
                              ? __hip_atomic_load(&a.sync[kSyncEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u
                              : 0u;
+  // a workspace whose wait failed before gives up at once (as fused_kernel)
+  const uint32_t spin_limit =
+      (RM == kRowOne && a.smooth &&
+       __hip_atomic_load(&a.sync[kSyncError], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+          ? 0u
+          : a.spin_limit;
   if constexpr (RM == kRowQuant) {
     // S from the reduce launch; without smoothing S = 1 (written here)
     for (int g = tid; g < ngroups; g += T) {
@@ -999,6 +1019,7 @@ __global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a
     for (int g = tid; g < ngroups; g += T) s_grp[g] = 0.f;
   }
   for (int row = blockIdx.x; row < a.rows; row += gridDim.x) {
+  bool gave_up = false;  // the one-launch wait gave up (the outputs are marked)
   uint4 w[E / 8];
 #pragma unroll
   for (int i = 0; i < E / 8; ++i)
@@ -1081,12 +1102,12 @@ __global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a
             const int idx = base + k * T;
             b[k] = idx < n ? __hip_atomic_load(&part[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag;
           }
-          bool all = true;
+          bool all = spin_limit > 0;
 #pragma unroll
           for (int k = 0; k < kBatch; ++k) all &= (b[k] >> 32) == epoch;
           if (all) break;
-          if (++it == kSpinLimit) {
-            atomicOr(&a.sync[kSyncError], 1u);
+          if (++it >= spin_limit) {
+            gave_up = true;
             break;
           }
           __builtin_amdgcn_s_sleep(2);
@@ -1098,14 +1119,17 @@ __global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a
         }
       }
     }
-    __syncthreads();
-    // every workgroup has read the old epoch (it tagged its row with old + 1)
-    if (row == 0 && tid == 0)
+    // a workgroup that gave up raises the error word and marks its outputs
+    gave_up = __syncthreads_or(gave_up);
+    if (gave_up && tid == 0) atomicOr(&a.sync[kSyncError], 1u);
+    // every workgroup has read the old epoch (it tagged its row with old + 1);
+    // a failed call leaves it
+    if (row == 0 && tid == 0 && !gave_up)
       __hip_atomic_store(&a.sync[kSyncEpoch], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int g = tid; g < ngroups; g += T) {
       float sg = s_grp[g];
       if (!(sg > 0.f)) sg = 1.f;  // all-zero group over every token
-      if (row == 0) a.S_out[g] = sg;
+      if (row == 0) a.S_out[g] = gave_up ? __builtin_nanf("") : sg;
       s_grp[g] = 1.f / sg;
     }
   } else if (RM == kRowOne) {
@@ -1143,7 +1167,7 @@ __global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a
     *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
   else
     *reinterpret_cast<uint32_t*>(dst) = packed[0];
-  if (tid == 0) a.scale[row] = rmax / 7.f;
+  if (tid == 0) a.scale[row] = gave_up ? __builtin_nanf("") : rmax / 7.f;
   if constexpr (RM == kRowOne) break;  // one row: no loop
   __syncthreads();                     // s_row and s_red are reused by the next row
   }
@@ -1331,6 +1355,7 @@ hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t
   a.codes = xq;
   a.scale = dx;
   a.S_out = S_out;
+  a.spin_limit = (flags & kFlagGiveUp) ? 0u : kSpinLimit;
   const bool rotate = !(flags & 1);
   hipError_t e = hipSuccess;
   // few tokens at K = 4096 / 8192: one row per workgroup, one launch
@@ -1385,8 +1410,8 @@ int frontend_launches(int M, int K, int flags) {
 }
 
 hipError_t launch_weight_prep(const uint16_t* W, int K, int N, const int32_t* perm,
-                              const uint32_t* dsign, uint8_t* wq, float* dw, hipStream_t s) {
-  if (K & (K - 1)) return launch_weight_prep_kron(W, K, N, perm, dsign, wq, dw, s);
+                              const uint32_t* dsign, uint8_t* wq, float* dw, hipStream_t s, bool rotate) {
+  if (K & (K - 1)) return launch_weight_prep_kron(W, K, N, perm, dsign, wq, dw, s, rotate);
   const int log2K = __builtin_ctz(static_cast<unsigned>(K));
   FeArgs a{};
   a.dsign = reinterpret_cast<const uint8_t*>(dsign);
@@ -1398,15 +1423,15 @@ hipError_t launch_weight_prep(const uint16_t* W, int K, int N, const int32_t* pe
   a.perm = perm;
   a.codes = wq;
   a.scale = dw;
-  return dispatch_k<kWeight, true>(log2K, a, s);
+  return rotate ? dispatch_k<kWeight, true>(log2K, a, s) : dispatch_k<kWeight, false>(log2K, a, s);
 }
 
 hipError_t launch_calibrate(const uint16_t* Xc, int T, int K, const uint32_t* dsign, int32_t* perm,
-                            uint32_t* ws, hipStream_t s) {
+                            uint32_t* ws, hipStream_t s, bool rotate) {
   hipError_t e = launch_zero_u32(ws, static_cast<size_t>(K), s);
   if (e != hipSuccess) return e;
   if (K & (K - 1)) {
-    e = launch_colmax_kron(Xc, T, K, dsign, ws, s);
+    e = launch_colmax_kron(Xc, T, K, dsign, ws, s, rotate);
   } else {
     const int log2K = __builtin_ctz(static_cast<unsigned>(K));
     FeArgs a{};
@@ -1415,7 +1440,7 @@ hipError_t launch_calibrate(const uint16_t* Xc, int T, int K, const uint32_t* ds
     a.log2G = log2K;
     a.colmax = ws;
     a.dsign = reinterpret_cast<const uint8_t*>(dsign);
-    e = dispatch_k<kColmax, true>(log2K, a, s);
+    e = rotate ? dispatch_k<kColmax, true>(log2K, a, s) : dispatch_k<kColmax, false>(log2K, a, s);
   }
   if (e != hipSuccess) return e;
   const int grid = (K + 1023) / 1024;

@@ -121,6 +121,7 @@ struct KronArgs {
   uint32_t* colmax;      // [K] (calibration)
   float* zrows;          // stats: [rows][K] rotated, reordered rows, or nullptr
   uint32_t* sync;        // one launch: the synchronisation block (epoch, error word, tagged rows)
+  uint32_t spin_limit;   // polls before the one-launch wait gives up (0: after the first)
 };
 
 __device__ __forceinline__ void bfly(float& x, float& y) {
@@ -363,9 +364,12 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
 
   // one launch: every workgroup reads the epoch before it publishes its row,
   // so none can see the next call's value
-  uint32_t epoch = 0;
-  if constexpr (MODE == kKFused)
+  uint32_t epoch = 0, spin_limit = a.spin_limit;
+  if constexpr (MODE == kKFused) {
     epoch = __hip_atomic_load(&a.sync[kSyncEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    // a workspace whose wait failed before gives up at once
+    if (__hip_atomic_load(&a.sync[kSyncError], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) spin_limit = 0u;
+  }
 
   // rows blockIdx.x, + gridDim.x, ...: the next row's chunks load while this
   // one is processed (one launch: one row per workgroup)
@@ -376,6 +380,7 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
     if (c < W8 && blockIdx.x < a.rows) nxt[s] = load_chunk<MODE, K>(a, blockIdx.x, c);
   }
   for (int row = blockIdx.x; row < a.rows; row += gridDim.x) {
+    bool gave_up = false;  // the one-launch wait gave up (the outputs are marked)
     uint4 cur[SW];
 #pragma unroll
     for (int s = 0; s < SW; ++s) cur[s] = nxt[s];
@@ -478,12 +483,12 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
                 const int idx = base + k * kKT;
                 b[k] = idx < n ? __hip_atomic_load(&part[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag;
               }
-              bool all = true;
+              bool all = spin_limit > 0;
 #pragma unroll
               for (int k = 0; k < kBatch; ++k) all &= (b[k] >> 32) == epoch;
               if (all) break;
-              if (++it == kSpinLimit) {
-                atomicOr(&a.sync[kSyncError], 1u);
+              if (++it >= spin_limit) {
+                gave_up = true;
                 break;
               }
               __builtin_amdgcn_s_sleep(2);
@@ -495,14 +500,17 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
             }
           }
         }
-        __syncthreads();
-        // every workgroup has read the old epoch (it tagged its row with old + 1)
-        if (row == 0 && tid == 0)
+        // a workgroup that gave up raises the error word and marks its outputs
+        gave_up = __syncthreads_or(gave_up);
+        if (gave_up && tid == 0) atomicOr(&a.sync[kSyncError], 1u);
+        // every workgroup has read the old epoch (it tagged its row with old + 1);
+        // a failed call leaves it
+        if (row == 0 && tid == 0 && !gave_up)
           __hip_atomic_store(&a.sync[kSyncEpoch], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         for (int g = tid; g < ngroups; g += kKT) {
           float sg = s_grp[g];
           if (!(sg > 0.f)) sg = 1.f;  // all-zero group over every token
-          if (row == 0) a.S_out[g] = sg;
+          if (row == 0) a.S_out[g] = gave_up ? __builtin_nanf("") : sg;
           s_grp[g] = 1.f / sg;
         }
         __syncthreads();
@@ -536,7 +544,7 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
             dst[w] = pack8(mag, sgn);
           }
         }
-        if (tid == 0) a.scale[row] = r / 7.f;
+        if (tid == 0) a.scale[row] = gave_up ? __builtin_nanf("") : r / 7.f;
       }
     }
     __syncthreads();  // the row buffers are reused by the next row
@@ -719,6 +727,7 @@ hipError_t launch_frontend_kron(const uint16_t* X, int M, int K, int G, const in
   a.scale = dx;
   a.S_out = S_out;
   a.S_in = S_out;
+  a.spin_limit = (flags & kFlagGiveUp) ? 0u : kSpinLimit;
   // the stats pass's partial rows (one per workgroup, K/G words; at most M
   // of them) fit the codes buffer (K/2 bytes per token, G >= 32), which the
   // quantise pass overwrites afterwards
@@ -745,7 +754,7 @@ hipError_t launch_frontend_kron(const uint16_t* X, int M, int K, int G, const in
 }
 
 hipError_t launch_weight_prep_kron(const uint16_t* W, int K, int N, const int32_t* perm, const uint32_t* dsign,
-                                   uint8_t* wq, float* dw, hipStream_t s) {
+                                   uint8_t* wq, float* dw, hipStream_t s, bool rotate) {
   int m = 0, log2n = 0;
   if (!kron_split(K, &m, &log2n)) return hipErrorInvalidValue;
   KronArgs a{};
@@ -754,7 +763,7 @@ hipError_t launch_weight_prep_kron(const uint16_t* W, int K, int N, const int32_
   a.ldw = N;
   a.log2G = __builtin_ctz(static_cast<unsigned>(K & -K));  // one group: no smoothing
   a.smooth = 0;
-  a.rotate = 1;
+  a.rotate = rotate ? 1 : 0;
   a.perm = perm;
   a.dsign = reinterpret_cast<const uint8_t*>(dsign);
   a.codes = wq;
@@ -763,14 +772,14 @@ hipError_t launch_weight_prep_kron(const uint16_t* W, int K, int N, const int32_
 }
 
 hipError_t launch_colmax_kron(const uint16_t* Xc, int T, int K, const uint32_t* dsign, uint32_t* colmax,
-                              hipStream_t s) {
+                              hipStream_t s, bool rotate) {
   int m = 0, log2n = 0;
   if (!kron_split(K, &m, &log2n)) return hipErrorInvalidValue;
   KronArgs a{};
   a.src = Xc;
   a.rows = T;
   a.log2G = 5;
-  a.rotate = 1;
+  a.rotate = rotate ? 1 : 0;
   a.dsign = reinterpret_cast<const uint8_t*>(dsign);
   a.colmax = colmax;
   return dispatch_kron<kKColmax>(m, log2n, a, T < 1024 ? T : 1024, s);

@@ -63,6 +63,8 @@ struct GemmArgs {
   const float* dw;
   float* Y;
   int32_t* P;  // partials window (partials variant)
+  const uint32_t* err;  // nonzero word: write NaN to every output (nullptr: none)
+  float ybase;          // 2^18 / K for rotated codes, 2^18 without the rotation
   int M, N, K, log2G;
   int pm0, pm1, pn0, pn1;
   int tiles_t, tiles_n;
@@ -105,6 +107,10 @@ struct Mma<64> {  // 32 x 32 x 64: 32 codes (16 packed bytes) per lane
     return z;
   }
   __device__ static v4f quad(const acc_t& c, int q) { return v4f{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]}; }
+  __device__ static void set_quad(acc_t& c, int q, v4f v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[4 * q + e] = v[e];
+  }
 };
 
 template <>
@@ -125,6 +131,7 @@ struct Mma<32> {  // 16 x 16 x 32: 8 codes (4 packed bytes) per lane
   }
   __device__ static acc_t zero() { return v4f{0.f, 0.f, 0.f, 0.f}; }
   __device__ static v4f quad(const acc_t& c, int) { return c; }
+  __device__ static void set_quad(acc_t& c, int, v4f v) { c = v; }
 };
 
 // Split K: the workgroup is two sets of 4 waves over the same output tile;
@@ -254,16 +261,16 @@ struct GemmCtx {
 #pragma unroll
       for (int j = 0; j < TJ; ++j) fx[j] = Mm::load(stage + fX + j * Mm::BR * kRowB + koff);
       // Entering a new group rescales the accumulator by S_{g-1} / S_g (the
-      // partials dump clears it instead). With SPG (MFMA k-steps per group)
-      // known at compile time, each block is multiplied just before its
-      // first product of the group: its previous product was issued a full
-      // row of blocks earlier and has retired, so neither the multiplies nor
-      // the matrix core wait on each other. Otherwise (G > 128, one group
-      // over several stages) the whole accumulator is scaled at the group's
-      // first k-step.
-      if constexpr (SPG > 0 && !PARTIALS) {
+      // partials dump multiplies it by 0 instead: the same instructions).
+      // With SPG (MFMA k-steps per group) known at compile time, each block
+      // is multiplied just before its first product of the group: its
+      // previous product was issued a full row of blocks earlier and has
+      // retired, so neither the multiplies nor the matrix core wait on each
+      // other. Otherwise (G > 128, one group over several stages) the whole
+      // accumulator is scaled at the group's first k-step.
+      if constexpr (SPG > 0) {
         if (ks % SPG == 0) {  // folds: ks is an unrolled index
-          const float r = step > st0 * Mm::kSteps ? rat[step >> log2spg] : 1.f;
+          const float r = step > st0 * Mm::kSteps ? (PARTIALS ? 0.f : rat[step >> log2spg]) : 1.f;
           products<true>(stage, next, koff, fx, r, ks, nst);
         } else {
           products<false>(stage, next, koff, fx, 1.f, ks, nst);
@@ -277,7 +284,9 @@ struct GemmCtx {
         }
         products<false>(stage, next, koff, fx, 1.f, ks, nst);
       }
-      if (PARTIALS && gs == (1 << log2spg) - 1) dump(step >> log2spg);
+      // a group that ends inside this set (with one group over all of K the
+      // two sets' integer halves are added first; the epilogue dumps them)
+      if (PARTIALS && ngroups > 1 && gs == (1 << log2spg) - 1) dump(step >> log2spg);
     }
   }
 
@@ -436,13 +445,12 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
   c.nstage = (a.K + 127) / 128;
   c.log2spg = a.log2G - Mma<KM>::kLog2K;  // MFMA k-steps per group
   c.ngroups = a.K >> a.log2G;
-  // K halves (the partials dump keeps whole groups in one set). With two or
-  // more groups the halves meet on a group boundary: half of the groups when
-  // a group spans whole stages (G >= 128; an odd group count, possible for
-  // K = m 2^k, leaves the larger share to set 1), else half of the stages.
+  // K halves. With two or more groups the halves meet on a group boundary:
+  // half of the groups when a group spans whole stages (G >= 128; an odd
+  // group count, possible for K = m 2^k, leaves the larger share to set 1),
+  // else half of the stages. The partials dump splits K the same way.
   int half = (c.nstage + 1) / 2;
   if (c.ngroups > 1 && a.log2G >= 7) half = (c.ngroups / 2) << (a.log2G - 7);
-  if (PARTIALS) half = c.nstage;
   c.st0 = set == 0 ? 0 : half;
   c.st1 = set == 0 ? half : c.nstage;
   const int nsteps = max(half, c.nstage - half);  // both sets step in lockstep
@@ -486,8 +494,11 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
     // s_rat[g] = S[g-1] / S[g]: entering group g rescales the accumulator
     for (int g = tid; g < c.ngroups; g += kThreadsWG) s_rat[g] = g > 0 ? a.S[g - 1] / a.S[g] : 1.f;
     // epilogue operands, read now so their latency hides behind the main
-    // loop (zero past the matrix edge; those outputs are never stored)
-    const float base = kUnit / static_cast<float>(a.K);
+    // loop (zero past the matrix edge; those outputs are never stored).
+    // A set error word (a front end whose grid-wide wait gave up) makes
+    // every output NaN.
+    const bool poison = a.err != nullptr && *a.err != 0u;
+    const float base = poison ? __builtin_nanf("") : a.ybase;
     if (tid < kTT) {
       const int t = c.t0 + tid;
       s_rs[tid] = t < a.M ? a.dx[t] * base : 0.f;
@@ -521,8 +532,9 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
     c.template run<0>(nsteps);
   } else if (c.st1 > c.st0) {
     c.template run<1>(nsteps);
-  }  // else: no second half (K <= 128 or the partials dump)
-  if (PARTIALS) return;
+  }  // else: no second half (K <= 128)
+  const bool one_group = c.ngroups == 1;
+  if (PARTIALS && !one_group) return;  // every group was dumped by its set
 
   // ---- combine the halves ------------------------------------------------
   // With two or more groups the halves meet on a group boundary (K / 2 is a
@@ -531,8 +543,7 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
   // adds its own. With one group (G = K) the two halves are integer parts of
   // the same group partial: they are added exactly first and scaled once,
   // so a partial that cancels to zero stays exactly zero.
-  const bool one_group = c.ngroups == 1;
-  const float s_end = s_send[set];
+  const float s_end = PARTIALS ? 1.f : s_send[set];
   // park chunk of run q of block (i, j) of this wave (32 chunks of 1 KiB)
   auto chunk_of = [&](int i, int j, int q) { return wave * 32 + (i * TJ + j) * NQ + q; };
   __syncthreads();  // all rings idle: park set 1's 4 x 32 tiles of 1 KiB there
@@ -551,6 +562,19 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
   if (set == 1) return;
   const float m0 = one_group ? 1.f : s_end;  // set 0's own last group
   const float fin = one_group ? s_end : 1.f;
+  if constexpr (PARTIALS) {
+    // one group: the exact sum of the two integer halves is the partial
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+          Mma<KM>::set_quad(c.acc[i][j], q, Mma<KM>::quad(c.acc[i][j], q) +
+                                                reinterpret_cast<const v4f*>(park_chunk(chunk_of(i, j, q)))[c.lane]);
+    c.dump(0);
+    return;
+  }
 
   // ---- epilogue: Y[t, n..n+3] = (both halves, absolute) 2^18 / K dx[t] dw[n]
   const bool full = c.t0 + kTT <= a.M && c.n0 + kTN <= a.N && (a.N & 3) == 0;  // uniform
@@ -586,7 +610,7 @@ template <int KM, int SPG>
 hipError_t launch_km(const GemmArgs& a, bool partials, hipStream_t s) {
   const dim3 grid(a.tiles_t * a.tiles_n);
   if (partials)
-    hipLaunchKernelGGL((gemm_kernel<KM, true, 0>), grid, dim3(kThreadsWG), 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<KM, true, SPG>), grid, dim3(kThreadsWG), 0, s, a);
   else
     hipLaunchKernelGGL((gemm_kernel<KM, false, SPG>), grid, dim3(kThreadsWG), 0, s, a);
   return hipGetLastError();
@@ -594,25 +618,27 @@ hipError_t launch_km(const GemmArgs& a, bool partials, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_gemm(const uint8_t* xq, const float* dx, const float* S, int M, int K,
-                       int N, int G, const uint8_t* wq, const float* dw, float* Y, int32_t* P,
-                       int m0, int m1, int n0, int n1, hipStream_t s) {
+hipError_t launch_gemm(const GemmCall& gc, hipStream_t s) {
+  const int M = gc.M, N = gc.N, K = gc.K, G = gc.G;
+  if (M == 0 || N == 0) return hipSuccess;
+  // the partials come from the kernel that would write Y for this shape
+  if (gemm_small_applies(M, K, N, G)) return launch_gemm_small(gc, s);
   GemmArgs a{};
-  a.xq = xq;
-  a.dx = dx;
-  a.S = S;
-  a.wq = wq;
-  a.dw = dw;
-  a.Y = Y;
-  a.P = P;
+  a.xq = gc.xq;
+  a.dx = gc.dx;
+  a.S = gc.S;
+  a.wq = gc.wq;
+  a.dw = gc.dw;
+  a.Y = gc.Y;
+  a.P = gc.P;
+  a.err = gc.err;
+  a.ybase = gc.rotated ? kUnit / static_cast<float>(K) : kUnit;
   a.M = M;
   a.N = N;
   a.K = K;
   a.log2G = __builtin_ctz(static_cast<unsigned>(G));
-  a.pm0 = m0; a.pm1 = m1; a.pn0 = n0; a.pn1 = n1;
-  if (M == 0 || N == 0) return hipSuccess;
-  const bool partials = P != nullptr;
-  if (!partials && gemm_small_applies(M, K, N, G)) return launch_gemm_small(xq, dx, S, M, K, N, G, wq, dw, Y, s);
+  a.pm0 = gc.m0; a.pm1 = gc.m1; a.pn0 = gc.n0; a.pn1 = gc.n1;
+  const bool partials = gc.P != nullptr;
   a.tiles_t = (M + kTT - 1) / kTT;
   a.tiles_n = (N + kTN - 1) / kTN;
   switch (G) {

@@ -28,6 +28,7 @@
 // CU streams its own slice of the weights; further token slices stream them
 // again (from the Infinity Cache when they fit there).
 
+#include <atomic>
 #include <type_traits>
 
 #include "rrs_internal.h"
@@ -57,7 +58,11 @@ struct SmallArgs {
   const uint8_t* wq;
   const float* dw;
   float* Y;
+  int32_t* P;           // partials window (partials variant), zeroed before the launch
+  const uint32_t* err;  // nonzero word: write NaN to every output (nullptr: none)
+  float ybase;          // 2^18 / K for rotated codes, 2^18 without the rotation
   int M, N, K, log2G;
+  int pm0, pm1, pn0, pn1;
 };
 
 // a-codes (even) and b-codes (odd) of a packed word as e4m3 subnormals
@@ -71,23 +76,59 @@ __device__ __forceinline__ v8i widen(v4u w) {
 // byte offset of 16-byte chunk c of row r in a wave's round buffer
 __device__ __forceinline__ int swz(int r, int c) { return r * kRows + ((c ^ (r & 7)) << 4); }
 
+// The partials variant: add an exact integer piece of group g's partial
+// (accumulator units 2^-18; the sum of the NA accumulators given), held by
+// this wave, into P for the window's outputs. Register e of lane l in block
+// j holds token t0 + 32 j + l % 32, channel n0 + 8 (e / 4) + 4 (l / 32) +
+// e % 4.
+template <int TJ>
+__device__ __forceinline__ void dump_piece(const SmallArgs& a, const v16f (&acc)[TJ], const v16f (&acc2)[TJ],
+                                           bool both, int t0, int n0, int lane, int g, int ngroups) {
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int t = t0 + 32 * j + (lane & 31);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int n = n0 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      if (t >= a.pm0 && t < a.pm1 && n >= a.pn0 && n < a.pn1) {
+        const size_t o = (static_cast<size_t>(t - a.pm0) * (a.pn1 - a.pn0) + (n - a.pn0)) * ngroups + g;
+        const float v = both ? acc[j][e] + acc2[j][e] : acc[j][e];
+        atomicAdd(&a.P[o], static_cast<int32_t>(v * kUnit));
+      }
+    }
+  }
+}
+
 // TJ: 32-token blocks per slice (1 for M <= 32, else 2); NR: rounds of loads
 // in flight (1 or 2; divides the wave's round count); KS: min(k-steps per
 // group, kRound), the spacing of possible group starts inside a round, or 0
 // for G = 32 (two groups in every k-step); WV: waves per workgroup.
-template <int TJ, int NR, int KS, int WV>
+// Each wave keeps two accumulators per token block: for G >= 64 one for the
+// even and one for the odd k-steps, for G = 32 one for each group of a
+// k-step's two. Each is rescaled right before its own next MFMA (from the
+// group it last took to the current one), so the rescale never reads the
+// result of the MFMA issued just before it (a VALU read of a 16-pass MFMA's
+// last result registers needs at least 20 issue slots after it on gfx950;
+// the compiler's own padding has been found one short there), and the two
+// MFMAs of a k-step do not depend on each other.
+// PARTIALS: the same main loop with the accumulators multiplied by 0 where
+// they would be rescaled, and every wave's integer piece of a group added
+// into P where the group (or the wave's run) ends; no Y.
+template <int TJ, int NR, int KS, int WV, bool PARTIALS>
 __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
   constexpr int kWaves = WV, kThreads = WV * 64;
-  static_assert(WV <= kMaxWaves && 64 + kTN + WV <= kThreads, "one thread per scale preloaded");
+  static_assert(WV <= kMaxWaves && 64 + kTN + 3 * WV <= kThreads, "one thread per scale preloaded");
   constexpr int kWL = 4;            // W loads per lane per round (32 rows / 8)
   constexpr int kXL = 4 * TJ;       // X loads per lane per round
   constexpr int kBuf = (32 + 32 * TJ) * kRows;  // round buffer bytes per wave
   static_assert(TJ * 16 * 64 * 4 <= kBuf, "a wave's sums fit its round buffer");
   static_assert(kMaxKronK >= (1 << kMaxLog2K), "group ratio table sized by the largest K");
-  __shared__ float s_rat[kMaxKronK / 32];
+  __shared__ float s_rat[kMaxKronK / 32];   // S[g-1] / S[g]
+  __shared__ float s_rat2[kMaxKronK / 32];  // S[g-2] / S[g] (G <= 64)
   __shared__ float s_dx[64];         // dx[t] 2^18 / K (0 past M)
   __shared__ float s_dw[kTN];        // dw of the workgroup's channels (0 past N)
-  __shared__ float s_last[kWaves];   // scale of each wave's last group
+  __shared__ float s_last[kWaves];   // scale of the group of each wave's last code
+  __shared__ float s_lastp[2 * kWaves];  // scale of the last group of each wave's two accumulators
   __shared__ float s_out[64 * (kTN + 1)];  // the summed tile, token-major, rows padded by one word
   __shared__ __attribute__((aligned(16))) uint8_t s_buf[kWaves][kBuf];
 
@@ -113,38 +154,51 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
   // coalesced load i of a round: row 8 i + lane / 8, chunk lane % 8 (rows
   // clamped to the matrix; clamped rows feed outputs that are never stored)
   const int lr = lane >> 3, lc = lane & 7;
-  const uint8_t* wsrc[kWL];
-  const uint8_t* xsrc[kXL];
+  // (a wave-uniform base per operand plus a 32-bit offset per lane and
+  // load: one register per load stream instead of a 64-bit pointer)
+  const uint8_t* wbase = a.wq + static_cast<size_t>(n0) * Kb + ks0 * 32;
+  const uint8_t* xbase = xq + ks0 * 32;
+  uint32_t woff[kWL], xoff[kXL];
 #pragma unroll
   for (int i = 0; i < kWL; ++i)
-    wsrc[i] = a.wq + static_cast<size_t>(min(n0 + 8 * i + lr, a.N - 1)) * Kb + ks0 * 32 + lc * 16;
+    woff[i] = static_cast<uint32_t>((min(n0 + 8 * i + lr, a.N - 1) - n0) * Kb + lc * 16);
 #pragma unroll
-  for (int i = 0; i < kXL; ++i)
-    xsrc[i] = xq + static_cast<size_t>(min(8 * i + lr, Mt - 1)) * Kb + ks0 * 32 + lc * 16;
+  for (int i = 0; i < kXL; ++i) xoff[i] = static_cast<uint32_t>(min(8 * i + lr, Mt - 1) * Kb + lc * 16);
 
   uint8_t* buf = s_buf[wave];
   v4u rw[NR][kWL], rx[NR][kXL];
-  v16f acc[TJ];
+  v16f acc[2][TJ];
 #pragma unroll
-  for (int j = 0; j < TJ; ++j)
+  for (int p = 0; p < 2; ++p)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[p][j][e] = 0.f;
 
 #pragma unroll
   for (int s = 0; s < NR; ++s) {
     const int off = min(s, rounds - 1) * kRows;
 #pragma unroll
-    for (int i = 0; i < kWL; ++i) rw[s][i] = *reinterpret_cast<const v4u*>(wsrc[i] + off);
+    for (int i = 0; i < kWL; ++i) rw[s][i] = *reinterpret_cast<const v4u*>(wbase + off + woff[i]);
 #pragma unroll
-    for (int i = 0; i < kXL; ++i) rx[s][i] = *reinterpret_cast<const v4u*>(xsrc[i] + off);
+    for (int i = 0; i < kXL; ++i) rx[s][i] = *reinterpret_cast<const v4u*>(xbase + off + xoff[i]);
   }
   // the scales the loop and the epilogue need, read up front after the
   // first rounds' loads: their latency then overlaps those loads instead of
   // ending the kernel (as plain loads at the end they cost several
   // microseconds per call)
-  const float base = kUnit / static_cast<float>(a.K);
-  for (int g = tid; g < ngroups; g += kThreads) s_rat[g] = g > 0 ? a.S[g - 1] / a.S[g] : 1.f;
-  if (tid < 64) {
+  // a set error word (a front end whose grid-wide wait gave up) makes every
+  // output NaN
+  const bool poison = !PARTIALS && a.err != nullptr && *a.err != 0u;
+  const float base = poison ? __builtin_nanf("") : a.ybase;
+  if (!PARTIALS) {
+    for (int g = tid; g < ngroups; g += kThreads) {
+      s_rat[g] = g > 0 ? a.S[g - 1] / a.S[g] : 1.f;
+      if (a.log2G <= 6) s_rat2[g] = g > 1 ? a.S[g - 2] / a.S[g] : 1.f;
+    }
+  }
+  if (PARTIALS) {
+  } else if (tid < 64) {
     s_dx[tid] = tid < Mt ? dx[tid] * base : 0.f;
   } else if (tid < 64 + kTN) {
     const int n = n0 + tid - 64;
@@ -152,6 +206,12 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
   } else if (tid < 64 + kTN + kWaves) {
     const int w = tid - 64 - kTN;
     s_last[w] = a.S[(((w + 1) * kpw) * 64 - 1) >> a.log2G];  // group of the wave's last code
+  } else if (tid < 64 + kTN + 3 * kWaves) {
+    // last code of accumulator q of wave w: G = 32, codes 32 q .. 32 q + 31
+    // of the wave's last k-step; else the last k-step of parity q
+    const int i = tid - 64 - kTN - kWaves, w = i >> 1, q = i & 1;
+    const int last = KS == 0 ? ((w + 1) * kpw - 1) * 64 + 32 * q + 31 : ((w + 1) * kpw - 2 + q) * 64 + 63;
+    s_lastp[i] = a.S[last >> a.log2G];
   }
   __syncthreads();
 
@@ -173,56 +233,73 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
       // round again, so every iteration issues the same loads)
       const int off = min(r + NR, rounds - 1) * kRows;
 #pragma unroll
-      for (int i = 0; i < kWL; ++i) rw[s][i] = *reinterpret_cast<const v4u*>(wsrc[i] + off);
+      for (int i = 0; i < kWL; ++i) rw[s][i] = *reinterpret_cast<const v4u*>(wbase + off + woff[i]);
 #pragma unroll
-      for (int i = 0; i < kXL; ++i) rx[s][i] = *reinterpret_cast<const v4u*>(xsrc[i] + off);
+      for (int i = 0; i < kXL; ++i) rx[s][i] = *reinterpret_cast<const v4u*>(xbase + off + xoff[i]);
 #pragma unroll
       for (int u = 0; u < kRound; ++u) {
         const int ks = r * kRound + u;
-        // entering a new group: the accumulator goes from units of S_{g-1}
-        // to units of S_g. Group starts fall only on k-steps with
-        // u % KS == 0; the multiply there is unconditional (by 1 when no
-        // group starts, and at the wave's first k-step, whose sum so far is
-        // empty).
         const int c = 2 * u + (lane >> 5);
         const v8i fw = widen(*reinterpret_cast<const v4u*>(buf + swz(lane & 31, c)));
+        const int kg = ks0 + ks;
         if constexpr (KS == 0) {
           // G = 32: lanes 0-31 carry codes 0-31 of the k-step (group 2 kg)
           // and lanes 32-63 codes 32-63 (group 2 kg + 1), for both operands.
           // Two MFMAs, each with the other lane half of the weights zeroed,
-          // and the rescale into the second group between them.
-          const int kg = ks0 + ks;
-          const float f0 = ks > 0 ? s_rat[2 * kg] : 1.f, f1 = s_rat[2 * kg + 1];
+          // into acc[0] (even groups) and acc[1] (odd groups); each moves
+          // from the group two back to its current one (S_{g-2} / S_g).
+          const float f0 = ks > 0 ? (PARTIALS ? 0.f : s_rat2[2 * kg]) : 1.f;
+          const float f1 = ks > 0 ? (PARTIALS ? 0.f : s_rat2[2 * kg + 1]) : 1.f;
           const bool lo = lane < 32;
           const v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
           const v8i fw0 = lo ? fw : z, fw1 = lo ? z : fw;
-          v8i fx[TJ];
-#pragma unroll
-          for (int j = 0; j < TJ; ++j) fx[j] = widen(*reinterpret_cast<const v4u*>(buf + swz(32 + 32 * j + (lane & 31), c)));
 #pragma unroll
           for (int j = 0; j < TJ; ++j) {
-            acc[j] *= f0;
-            acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw0, fx[j], acc[j], 0, 0, 0, 0, 0, 0);
-            acc[j] *= f1;
-            acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw1, fx[j], acc[j], 0, 0, 0, 0, 0, 0);
+            const v8i fx = widen(*reinterpret_cast<const v4u*>(buf + swz(32 + 32 * j + (lane & 31), c)));
+            acc[0][j] *= f0;
+            acc[0][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw0, fx, acc[0][j], 0, 0, 0, 0, 0, 0);
+            acc[1][j] *= f1;
+            acc[1][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw1, fx, acc[1][j], 0, 0, 0, 0, 0, 0);
+          }
+          if constexpr (PARTIALS) {
+            dump_piece<TJ>(a, acc[0], acc[1], false, t0, n0, lane, 2 * kg, ngroups);
+            dump_piece<TJ>(a, acc[1], acc[0], false, t0, n0, lane, 2 * kg + 1, ngroups);
           }
         } else {
-          if (u % KS == 0) {
-            const int kg = ks0 + ks;
-            const float rg = s_rat[kg >> log2spg];
-            const float f = (ks > 0 && (kg & (kspg - 1)) == 0) ? rg : 1.f;
+          // acc[q] (q = k-step parity, fixed by the unrolled u: a round is 4
+          // k-steps) last took k-step kg - 2. G = 64: one group per k-step,
+          // so that was two groups back (S_{g-2} / S_g); G >= 128: one group
+          // back in the first two k-steps of a group, else the same group.
+          // Group starts fall on k-steps with u % KS == 0, so the multiply
+          // is compiled in only where one can apply (by 1 where none does).
+          const int q = u & 1;
+          if (KS == 1 || u % KS < 2) {
+            float f = 1.f;
+            if (ks >= 2) {
+              if (kspg == 1)
+                f = PARTIALS ? 0.f : s_rat2[kg];
+              else if ((kg & (kspg - 1)) < 2)
+                f = PARTIALS ? 0.f : s_rat[kg >> log2spg];
+            }
 #pragma unroll
-            for (int j = 0; j < TJ; ++j) acc[j] *= f;
+            for (int j = 0; j < TJ; ++j) acc[q][j] *= f;
           }
 #pragma unroll
           for (int j = 0; j < TJ; ++j) {
             const v8i fx = widen(*reinterpret_cast<const v4u*>(buf + swz(32 + 32 * j + (lane & 31), c)));
-            acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw, fx, acc[j], 0, 0, 0, 0, 0, 0);
+            acc[q][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw, fx, acc[q][j], 0, 0, 0, 0, 0, 0);
           }
+          // the group ends here, or the wave's run ends inside it (a piece):
+          // at G = 64 the group is acc[q] alone, else both accumulators
+          // hold pieces of it
+          if (PARTIALS && (((kg + 1) & (kspg - 1)) == 0 || ks == kpw - 1))
+            dump_piece<TJ>(a, acc[q], acc[1 - q], kspg > 1, t0, n0, lane, kg >> log2spg, ngroups);
         }
       }
     }
   }
+
+  if constexpr (PARTIALS) return;
 
   // When a group spans several waves (kpw < kspg), each wave's run lies in
   // one group and its sum is an exact integer piece of that group's
@@ -231,12 +308,12 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
   // absolute with the scale of its last group.
   const bool pieces = kpw < kspg;
   const int wpg = pieces ? kspg / kpw : 1;  // waves per group
-  const float sl = pieces ? 1.f : s_last[wave];
+  const float sl0 = pieces ? 1.f : s_lastp[2 * wave], sl1 = pieces ? 1.f : s_lastp[2 * wave + 1];
   float* part = reinterpret_cast<float*>(buf);
 #pragma unroll
   for (int j = 0; j < TJ; ++j)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) part[(j * 16 + e) * 64 + lane] = acc[j][e] * sl;
+    for (int e = 0; e < 16; ++e) part[(j * 16 + e) * 64 + lane] = acc[0][j][e] * sl0 + acc[1][j][e] * sl1;
   __syncthreads();
 
   // Sum of the 8 waves' sums in their storage order (consecutive threads
@@ -294,10 +371,25 @@ int small_waves(int K) {
   return 0;
 }
 
+// Compute units of the current device (cached per device; 256 if the
+// device cannot be queried).
+int device_cus() {
+  constexpr int kDevs = 64;
+  static std::atomic<int> cache[kDevs];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 256;
+  int cus = cache[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cache[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
+}
+
 // A wave's run and the group must nest (one a multiple of the other), so
 // that no group is cut part-way into a wave. Up to 64 tokens this kernel
 // then always serves. Past that it serves while it needs
-// fewer rounds of resident workgroups (one per CU, 256 CUs) than the tiled
+// fewer rounds of resident workgroups (one per CU) than the tiled
 // kernel, weighted by what one round of each costs at this K (measured with
 // both kernels alone at M = 65 .. 512: a tiled round costs about 4.8 times
 // a few-token round at K = 8192, 3.6 times at K = 4096; 3 is assumed at
@@ -310,44 +402,62 @@ bool gemm_small_applies(int M, int K, int N, int G) {
   if (kpw % kspg != 0 && kspg % kpw != 0) return false;
   if (M <= 64) return true;
   if (M > kSmallMaxTokens) return false;
-  constexpr long kCUs = 256;
+  const long cus = device_cus();
   const long ws = static_cast<long>((N + kTN - 1) / kTN) * ((M + 63) / 64);
   const long wt = static_cast<long>((N + 255) / 256) * ((M + 127) / 128);
-  const long rs = (ws + kCUs - 1) / kCUs, rt = (wt + kCUs - 1) / kCUs;
+  const long rs = (ws + cus - 1) / cus, rt = (wt + cus - 1) / cus;
   const long ratio10 = K >= 8192 ? 48 : K >= 4096 ? 36 : 30;  // tenths
   return rs * 10 < rt * ratio10;
 }
 
-hipError_t launch_gemm_small(const uint8_t* xq, const float* dx, const float* S, int M, int K, int N, int G,
-                             const uint8_t* wq, const float* dw, float* Y, hipStream_t s) {
+hipError_t launch_gemm_small(const GemmCall& gc, hipStream_t s) {
+  const int M = gc.M, K = gc.K, N = gc.N, G = gc.G;
   if (!gemm_small_applies(M, K, N, G)) return hipErrorInvalidValue;
   SmallArgs a{};
-  a.xq = xq;
-  a.dx = dx;
-  a.S = S;
-  a.wq = wq;
-  a.dw = dw;
-  a.Y = Y;
+  a.xq = gc.xq;
+  a.dx = gc.dx;
+  a.S = gc.S;
+  a.wq = gc.wq;
+  a.dw = gc.dw;
+  a.Y = gc.Y;
+  a.P = gc.P;
+  a.err = gc.err;
+  a.ybase = gc.rotated ? kUnit / static_cast<float>(K) : kUnit;
   a.M = M;
   a.N = N;
   a.K = K;
   a.log2G = __builtin_ctz(static_cast<unsigned>(G));
+  a.pm0 = gc.m0; a.pm1 = gc.m1; a.pn0 = gc.n0; a.pn1 = gc.n1;
+  const bool partials = gc.P != nullptr;
+  if (partials) {
+    // the pieces are added into P: clear the window first
+    const size_t words = static_cast<size_t>(gc.m1 - gc.m0) * (gc.n1 - gc.n0) * (K / G);
+    const hipError_t e = launch_zero_u32(reinterpret_cast<uint32_t*>(gc.P), words, s);
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid((N + kTN - 1) / kTN, (M + 63) / 64);
   const int wv = small_waves(K);
   const int rounds = (a.K >> 6) / wv / kRound;  // per wave: 1, 2, 4 for K = 2048, 4096, 8192; 7 for 14336
   const int spg = G >> 6;
   const int ks = G == 32 ? 0 : spg < kRound ? spg : kRound;
   // instantiations: TJ in {1, 2}, NR in {1, 2}, KS in {0 (G = 32), 1, 2, 4},
-  // WV in {4, 5, 6, 7, 8}
-  auto go = [&](auto tj, auto nr, auto w) {
+  // WV in {4, 5, 6, 7, 8}, each with and without the partials dump
+  auto go2 = [&](auto tj, auto nr, auto w, auto pt) {
     constexpr int TJ = decltype(tj)::value, NR = decltype(nr)::value, WV = decltype(w)::value;
+    constexpr bool PT = decltype(pt)::value;
     const dim3 block(WV * 64);
     switch (ks) {
-      case 0: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 0, WV>), grid, block, 0, s, a); break;
-      case 1: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 1, WV>), grid, block, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 2, WV>), grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, kRound, WV>), grid, block, 0, s, a); break;
+      case 0: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 0, WV, PT>), grid, block, 0, s, a); break;
+      case 1: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 1, WV, PT>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 2, WV, PT>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, kRound, WV, PT>), grid, block, 0, s, a); break;
     }
+  };
+  auto go = [&](auto tj, auto nr, auto w) {
+    if (partials)
+      go2(tj, nr, w, std::integral_constant<bool, true>{});
+    else
+      go2(tj, nr, w, std::integral_constant<bool, false>{});
   };
   auto by_waves = [&](auto tj, auto nr) {
     switch (wv) {

@@ -29,9 +29,18 @@ constexpr int kSyncEpoch = 3;
 constexpr int kMaxFusedWG = 512;
 constexpr int kSyncPartials = 17408;
 // Bounded spin of the one-launch forms' grid-wide wait: after this many
-// polls (seconds of polling) a workgroup raises the error word and runs to
-// its end, so every wave exits whatever happens to the other workgroups.
+// polls (seconds of polling) a workgroup gives up: it raises the error word,
+// marks its own outputs (NaN token scales, and NaN group scales from the
+// workgroup that writes them) and runs to its end, so every wave exits
+// whatever happens to the other workgroups. A limit of 0 (the failure-path
+// test flag) gives up after the first poll in every workgroup.
 constexpr uint32_t kSpinLimit = 1u << 22;
+
+// Front-end flags (the public ones of rrs.h, plus the test flag)
+constexpr int kFlagNoRotate = 1;
+constexpr int kFlagNoSmooth = 2;
+constexpr int kFlagTwoPass = 4;
+constexpr int kFlagGiveUp = 8;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -44,6 +53,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 //   zrows: Kronecker K only: room for the M x K fp32 rotated, reordered rows
 //          (the quantise pass then streams them instead of rotating again),
 //          or nullptr.
+//   kFlagGiveUp (bit3): the one-launch forms' wait gives up at once (tests
+//          of the failure path; every kernel still ends normally).
 hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t* perm,
                            const uint32_t* dsign, uint8_t* xq, float* dx, float* S_out, uint32_t* sync,
                            int flags, hipStream_t s, float* zrows = nullptr);
@@ -53,29 +64,47 @@ hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t
 int frontend_launches(int M, int K, int flags);
 
 // Offline weight preparation: W [K, N] row-major fp16 -> wq [N][K/2] + dw [N]
-// (H D W with a sign mask, H W without).
+// (H D W with a sign mask, H W without; W itself, reordered, with
+// rotate = false).
 hipError_t launch_weight_prep(const uint16_t* W, int K, int N, const int32_t* perm,
-                              const uint32_t* dsign, uint8_t* wq, float* dw, hipStream_t s);
+                              const uint32_t* dsign, uint8_t* wq, float* dw, hipStream_t s,
+                              bool rotate = true);
 
-// Calibration permutation: per-channel |max| of the rotated rows, then a
-// stable descending rank. ws holds K uint32.
+// Calibration permutation: per-channel |max| of the rotated rows (the raw
+// rows with rotate = false), then a stable descending rank. ws holds K uint32.
 hipError_t launch_calibrate(const uint16_t* Xc, int T, int K, const uint32_t* dsign, int32_t* perm,
-                            uint32_t* ws, hipStream_t s);
+                            uint32_t* ws, hipStream_t s, bool rotate = true);
 
 // Zero n uint32 words (fill kernel; used instead of hipMemsetAsync).
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
 
-// Grouped INT4 GEMM. Y = (1/K) dx dw sum_g S_g P_g. If P != nullptr the
-// kernel instead writes the int32 partials of the window [m0,m1) x [n0,n1).
-hipError_t launch_gemm(const uint8_t* xq, const float* dx, const float* S, int M, int K,
-                       int N, int G, const uint8_t* wq, const float* dw, float* Y, int32_t* P,
-                       int m0, int m1, int n0, int n1, hipStream_t s);
+// Grouped INT4 GEMM: Y = c dx dw sum_g S_g P_g with c = 1/K for codes of
+// rotated rows (the Hadamard pair's two 1/sqrt(K)) and c = 1 without the
+// rotation (rotated = false). If P != nullptr the kernel that would write Y
+// (the same instantiation, with the accumulator cleared where it would be
+// rescaled) instead writes the int32 partials of the window [m0,m1) x
+// [n0,n1). err: a device word (the workspace's error word) that, when
+// nonzero as the kernel runs, makes it write NaN to every output; nullptr
+// for none.
+struct GemmCall {
+  const uint8_t* xq;
+  const float* dx;
+  const float* S;
+  int M, K, N, G;
+  const uint8_t* wq;
+  const float* dw;
+  float* Y;
+  int32_t* P;
+  int m0, m1, n0, n1;
+  bool rotated;
+  const uint32_t* err;
+};
+hipError_t launch_gemm(const GemmCall& c, hipStream_t s);
 
-// Few-token form of the same product (Y only): whether it serves
-// (M, K, N, G), and its launch. launch_gemm dispatches to it by itself.
+// Few-token form of the same product: whether it serves (M, K, N, G), and
+// its launch. launch_gemm dispatches to it by itself.
 bool gemm_small_applies(int M, int K, int N, int G);
-hipError_t launch_gemm_small(const uint8_t* xq, const float* dx, const float* S, int M, int K, int N, int G,
-                             const uint8_t* wq, const float* dw, float* Y, hipStream_t s);
+hipError_t launch_gemm_small(const GemmCall& c, hipStream_t s);
 
 // Kronecker rotation H_m (x) H_n for K = m n, m in {12, 20, 28}, n = 2^k
 // (64 <= n, K <= kMaxKronK; n <= 1024 for m = 12, n <= 512 otherwise).
@@ -92,8 +121,8 @@ hipError_t launch_frontend_kron(const uint16_t* X, int M, int K, int G, const in
                                 uint8_t* xq, float* dx, float* S_out, uint32_t* sync, int flags, hipStream_t s,
                                 float* zrows);
 hipError_t launch_weight_prep_kron(const uint16_t* W, int K, int N, const int32_t* perm, const uint32_t* dsign,
-                                   uint8_t* wq, float* dw, hipStream_t s);
+                                   uint8_t* wq, float* dw, hipStream_t s, bool rotate);
 hipError_t launch_colmax_kron(const uint16_t* Xc, int T, int K, const uint32_t* dsign, uint32_t* colmax,
-                              hipStream_t s);
+                              hipStream_t s, bool rotate);
 
 }  // namespace rrs

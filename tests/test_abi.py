@@ -99,7 +99,8 @@ def test_frontend_rejects():
         a = {**ok, **kw}
         return L.rrs_frontend(a["X"], a["M"], a["K"], a["G"], a["perm"], a["xq"], a["dx"], a["S"],
                               a["ws"], a["ws_bytes"], a["flags"], NULL)
-    assert call(flags=8) == rra.RRS_EINVAL
+    assert call(flags=16) == rra.RRS_EINVAL
+    assert call(flags=32 | rra.RRS_FLAG_NO_ROTATE) == rra.RRS_EINVAL
     assert call(ws_bytes=255) == rra.RRS_EINVAL
     assert call(S=NULL) == rra.RRS_EINVAL
     assert call(xq=NULL) == rra.RRS_EINVAL
@@ -111,7 +112,7 @@ def test_frontend_passes_rejects():
     L = rra.lib()
     assert L.rrs_frontend_passes(0, 4096, 0) == rra.RRS_EINVAL
     assert L.rrs_frontend_passes(16, 100, 0) == rra.RRS_EINVAL
-    assert L.rrs_frontend_passes(16, 4096, 8) == rra.RRS_EINVAL
+    assert L.rrs_frontend_passes(16, 4096, 16) == rra.RRS_EINVAL
     # answered without a device when the flags fix the form
     assert L.rrs_frontend_passes(16, 4096, rra.RRS_FLAG_NO_SMOOTH) == 1
     assert L.rrs_frontend_passes(16, 4096, rra.RRS_FLAG_TWO_PASS) == 3
@@ -242,3 +243,28 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(rra, "LIB_PATH", "/nonexistent/librrs.so")
     with pytest.raises(rra.RRSLibraryMissing):
         rra.rrs_weight_bytes(256, 4)
+
+
+def test_ablation_entry_points_reject():
+    """The _ex entry points: weights and calibration accept only
+    RRS_FLAG_NO_ROTATE; the layer accepts the front end's flags; a sign mask
+    together with RRS_FLAG_NO_ROTATE is rejected everywhere (the signs belong
+    to the rotation); M = 0 stays a no-op."""
+    L = rra.lib()
+    NR = rra.RRS_FLAG_NO_ROTATE
+    for flags in (rra.RRS_FLAG_NO_SMOOTH, rra.RRS_FLAG_TWO_PASS, rra.RRS_FLAG_TEST_GIVE_UP, 64):
+        assert L.rrs_prepare_weights_ex(DUMMY, 256, 8, DUMMY, NULL, flags, DUMMY, NULL) == rra.RRS_EINVAL
+        assert L.rrs_calibrate_perm_ex(DUMMY, 8, 256, NULL, flags, DUMMY, DUMMY, 1024, NULL) == rra.RRS_EINVAL
+    assert L.rrs_prepare_weights_ex(DUMMY, 256, 8, DUMMY, DUMMY, NR, DUMMY, NULL) == rra.RRS_EINVAL
+    assert L.rrs_calibrate_perm_ex(DUMMY, 8, 256, DUMMY, NR, DUMMY, DUMMY, 1024, NULL) == rra.RRS_EINVAL
+    assert L.rrs_linear_ex(DUMMY, 16, 256, 256, 128, DUMMY, DUMMY, NR, DUMMY, DUMMY, DUMMY, 1 << 20,
+                           NULL) == rra.RRS_EINVAL
+    assert L.rrs_linear_ex(DUMMY, 16, 256, 256, 128, DUMMY, NULL, 64, DUMMY, DUMMY, DUMMY, 1 << 20,
+                           NULL) == rra.RRS_EINVAL
+    assert L.rrs_linear_ex(DUMMY, 16, 256, 256, 96, DUMMY, NULL, NR, DUMMY, DUMMY, DUMMY, 1 << 20,
+                           NULL) == rra.RRS_EINVAL
+    assert L.rrs_linear_ex(NULL, 0, 256, 256, 128, DUMMY, NULL, NR, DUMMY, NULL, DUMMY, 1 << 20,
+                           NULL) == rra.RRS_OK
+    odd = ctypes.c_void_p(0x1004)
+    assert L.rrs_linear_ex(DUMMY, 16, 256, 256, 128, DUMMY, odd, 0, DUMMY, DUMMY, DUMMY, 1 << 20,
+                           NULL) == rra.RRS_EINVAL

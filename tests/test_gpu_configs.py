@@ -82,13 +82,9 @@ def test_workload(name):
         gu.rel_close(S.cpu().numpy(), fe["S"], gu.SCALE_TOL, "S")
 
         ref = oracle.linear_out(fe["q"][rows], fe["dx"][rows], fe["S"], wp["qw"], wp["dw"], G)
-        Yg = Y.cpu().numpy()[np.ix_(rows, cols)].astype(np.float64)
-        bound = gu.Y_TOL * ref["C"] + (1 + 1e-6) * gu.flip_bound(
-            q_gpu[rows], fe["q"][rows], qw_gpu, wp["qw"], fe["dx"][rows], fe["S"], wp["dw"], G)
-        flips = (q_gpu[rows] != fe["q"][rows]).any(axis=1)
-        clean = ~flips
-        err_clean = gu.y_error(Yg[clean], {"Y": ref["Y"][clean], "C": ref["C"][clean]}) if clean.any() else 0.0
-        gu.log(f"  Y: {int(clean.sum())}/{len(rows)} sampled rows without code flips, max err/C {err_clean:.3e}")
-        assert np.all(np.abs(Yg - ref["Y"]) <= bound)
+        Yg = Y.cpu().numpy()[np.ix_(rows, cols)]
+        fe_rows = {"q": fe["q"][rows], "dx": fe["dx"][rows], "S": fe["S"]}
+        gu.check_linear_two_way(Yg, ref, q_gpu[rows], qw_gpu, dx.cpu().numpy()[rows], S.cpu().numpy(),
+                                dw.cpu().numpy()[cols], G, f"{name} G={G}", fe=fe_rows, wp=wp)
         del ws, Y
     torch.cuda.empty_cache()

@@ -56,7 +56,9 @@ def test_frontend_capacity(M, K, G):
 @pytest.mark.parametrize("M,K,G", [(1, 8192, 128), (255, 8192, 32), (256, 8192, 8192), (257, 8192, 128),
                                    (1, 4096, 4096), (256, 4096, 64), (257, 4096, 128),
                                    (1, 2048, 64), (256, 2048, 2048), (257, 2048, 128),
-                                   (1, 1024, 1024), (255, 1024, 32), (64, 1024, 128)])
+                                   (1, 1024, 1024), (255, 1024, 32), (64, 1024, 128),
+                                   # past 256 rows at K = 1024: one row per wave (fused_kernel)
+                                   (257, 1024, 128), (300, 1024, 32)])
 @pytest.mark.parametrize("flags", [0, rra.RRS_FLAG_NO_SMOOTH, rra.RRS_FLAG_NO_ROTATE])
 def test_frontend_rows_boundary(M, K, G, flags):
     gu.log(f"[frontend rows] M={M} K={K} G={G} flags={flags}: {rra.rrs_frontend_passes(M, K, flags)} launch(es)")
@@ -183,7 +185,10 @@ def _random_codes(seed, M, N, K):
 
 @pytest.mark.parametrize("M,N,K,G", GEMM_SHAPES)
 def test_gemm_partials_exact(M, N, K, G):
-    gu.log(f"[gemm partials] M={M} N={N} K={K} G={G}")
+    """rrs_gemm_partials runs the instantiation rrs_gemm runs for the shape
+    (its K split and rescale points, the accumulator multiplied by 0 where
+    it would be rescaled): its partials must equal the int64 brute force."""
+    gu.log(f"[gemm partials] M={M} N={N} K={K} G={G} form={rra.rrs_gemm_form(M, K, N, G)}")
     q, qw = _random_codes(M + N + K, M, N, K)
     xq = gu.to_dev(oracle.pack_codes(q))
     wq = gu.weight_buffer_from_codes(oracle.pack_codes(qw), np.ones(N))
@@ -211,8 +216,51 @@ def test_gemm_output(M, N, K, G):
                  gu.weight_buffer_from_codes(oracle.pack_codes(qw), dw), Y)
     torch.cuda.synchronize()
     err = gu.y_error(Y.cpu().numpy(), ref)
-    gu.log(f"  Y err/C = {err:.3e}")
-    assert err <= gu.Y_TOL
+    gu.log(f"  Y err/C = {err:.3e} (bound {gu.y_tol(K, G):.2e})")
+    assert err <= gu.y_tol(K, G)
+
+
+def _exact_codes(seed, M, N, K):
+    """Random codes whose worst output keeps every partial sum of the
+    product chain below 2^18 units (|q qw| summed over K), so that with the
+    group scales powers of two up to 8 every fp32 value on the chain is an
+    exact multiple of 2^-21 below 8."""
+    q, qw = _random_codes(seed, M, N, K)
+    if 49 * K >= 1 << 18:  # the all-7 rows would exceed it: moderate them
+        q[0, :] = 3
+        qw[0, :] = -3
+    worst = (np.abs(q.astype(np.int64)) @ np.abs(qw.astype(np.int64)).T).max()
+    assert worst < 1 << 18
+    return q, qw
+
+
+@pytest.mark.parametrize("M,N,K,G", GEMM_SHAPES)
+def test_gemm_exact_through_product_kernels(M, N, K, G):
+    """The kernels that produce Y, checked bit for bit: with dx = dw = 1 and
+    group scales that are powers of two (neighbouring groups always
+    different: a product counted in the wrong group changes the sum), every
+    rescale, partial sum and epilogue product is exact in fp32 up to the one
+    product by the output scale: Y = fl32(X fl32(2^18 / K)) with X =
+    2^-18 sum_g S_g P_g exact (for K a power of two, K Y = sum_g S_g P_g
+    exactly). A dropped, doubled or misplaced product anywhere in the main
+    loop, the K split or the epilogue shows as a mismatch."""
+    gu.log(f"[gemm exact Y] M={M} N={N} K={K} G={G} form={rra.rrs_gemm_form(M, K, N, G)}")
+    q, qw = _exact_codes(M * 5 + N + K, M, N, K)
+    ng = K // G
+    S = np.array([2.0 ** ((3 * g + M) % 4) for g in range(ng)], dtype=np.float32)
+    Y = torch.empty(M, N, dtype=torch.float32, device=gu.DEV)
+    rra.rrs_gemm(gu.to_dev(oracle.pack_codes(q)), gu.to_dev(np.ones(M, np.float32)), gu.to_dev(S), G,
+                 gu.weight_buffer_from_codes(oracle.pack_codes(qw), np.ones(N)), Y)
+    torch.cuda.synchronize()
+    total = (oracle.group_partials(q, qw, G) * S.astype(np.int64)[None, None, :]).sum(axis=2)
+    assert np.abs(total).max() < 1 << 24          # X is exact in fp32
+    x32 = (total.astype(np.float64) * 2.0 ** -18).astype(np.float32)
+    want = x32 * (np.float32(2.0 ** 18) / np.float32(K))  # one fp32 rounding
+    if K & (K - 1) == 0:
+        assert np.array_equal(want.astype(np.float64) * K, total)
+    got = Y.cpu().numpy()
+    bad = got != want
+    assert not bad.any(), f"{int(bad.sum())} outputs differ, first {np.argwhere(bad)[:3].tolist()}"
 
 
 @pytest.mark.parametrize("M,K,N,G", [(16, 256, 256, 128), (45, 1024, 300, 64), (3, 8192, 129, 32),
@@ -233,12 +281,8 @@ def test_linear_end_to_end(M, K, N, G):
     codes, dw = rra.weight_views(wq, K, N)
     qw_gpu = oracle.unpack_codes(codes.cpu().numpy())
     gu.compare_codes(qw_gpu, ref["wp"]["qw"], ref["wp"]["uw"], "weight codes")
-    Yg = Y.cpu().numpy().astype(np.float64)
-    err = np.abs(Yg - ref["Y"])
-    bound = gu.Y_TOL * ref["C"] + (1 + 1e-6) * gu.flip_bound(
-        q_gpu, ref["fe"]["q"], qw_gpu, ref["wp"]["qw"], ref["fe"]["dx"], ref["fe"]["S"], ref["wp"]["dw"], G)
-    gu.log(f"  Y max err/C = {gu.y_error(Yg, ref):.3e}")
-    assert np.all(err <= bound)
+    gu.check_linear_two_way(Y.cpu().numpy(), ref, q_gpu, qw_gpu, dx.cpu().numpy(), S.cpu().numpy(),
+                            dw.cpu().numpy(), G, "linear")
 
 
 def test_determinism():

@@ -109,7 +109,9 @@ def test_calibrate_perm_signed(T, K):
 
 
 @pytest.mark.parametrize("M,K,N,G", [(16, 4096, 256, 128), (3, 8192, 129, 128), (130, 1024, 260, 64),
-                                     (64, 8192, 96, 256)])
+                                     (64, 8192, 96, 256),
+                                     # one row per wave past 256 rows (fused_kernel, signed)
+                                     (300, 2048, 64, 128), (260, 1024, 40, 32)])
 def test_linear_signed(M, K, N, G):
     gu.log(f"[linear signed] M={M} K={K} N={N} G={G} form={rra.rrs_gemm_form(M, K, N, G)}")
     x, w, perm, bits, d = _case(M, K, N)
@@ -128,8 +130,5 @@ def test_linear_signed(M, K, N, G):
     codes, dw = rra.weight_views(wq, K, N)
     qw_gpu = oracle.unpack_codes(codes.cpu().numpy())
     gu.compare_codes(qw_gpu, ref["wp"]["qw"], ref["wp"]["uw"], "signed weight codes")
-    Yg = Y.cpu().numpy().astype(np.float64)
-    bound = gu.Y_TOL * ref["C"] + (1 + 1e-6) * gu.flip_bound(
-        q_gpu, ref["fe"]["q"], qw_gpu, ref["wp"]["qw"], ref["fe"]["dx"], ref["fe"]["S"], ref["wp"]["dw"], G)
-    gu.log(f"  Y max err/C = {gu.y_error(Yg, ref):.3e}")
-    assert np.all(np.abs(Yg - ref["Y"]) <= bound)
+    gu.check_linear_two_way(Y.cpu().numpy(), ref, q_gpu, qw_gpu, dx.cpu().numpy(), S.cpu().numpy(),
+                            dw.cpu().numpy(), G, "signed linear")
