@@ -103,14 +103,17 @@ __device__ __forceinline__ void dump_piece(const SmallArgs& a, const v16f (&acc)
 // in flight (1 or 2; divides the wave's round count); KS: min(k-steps per
 // group, kRound), the spacing of possible group starts inside a round, or 0
 // for G = 32 (two groups in every k-step); WV: waves per workgroup.
-// Each wave keeps two accumulators per token block: for G >= 64 one for the
-// even and one for the odd k-steps, for G = 32 one for each group of a
-// k-step's two. Each is rescaled right before its own next MFMA (from the
-// group it last took to the current one), so the rescale never reads the
-// result of the MFMA issued just before it (a VALU read of a 16-pass MFMA's
-// last result registers needs at least 20 issue slots after it on gfx950;
-// the compiler's own padding has been found one short there), and the two
-// MFMAs of a k-step do not depend on each other.
+// A VALU read of a 16-pass MFMA's last result registers needs at least 20
+// issue slots after it on gfx950, and the compiler's own padding has been
+// found one short where a rescale read the MFMA issued just before it (or
+// one block's MFMA before it, at G = 64). So no rescale does: with one
+// token block (TJ = 1), and at G = 64 (a rescale at every k-step), the wave
+// keeps two accumulators per block, for G >= 64 one for the even and one
+// for the odd k-steps, for G = 32 one for each group of a k-step's two,
+// each rescaled right before its own next MFMA from the group it last
+// took; otherwise (two blocks, G = 32 or G >= 128) the other block's MFMA
+// lies between (at G = 32 every block's first-group MFMA is issued before
+// any block's rescale into the second group).
 // PARTIALS: the same main loop with the accumulators multiplied by 0 where
 // they would be rescaled, and every wave's integer piece of a group added
 // into P where the group (or the wave's run) ends; no Y.
@@ -167,9 +170,10 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
 
   uint8_t* buf = s_buf[wave];
   v4u rw[NR][kWL], rx[NR][kXL];
-  v16f acc[2][TJ];
+  constexpr int NA = (TJ == 1 || KS == 1) ? 2 : 1;  // accumulators per token block
+  v16f acc[NA][TJ];
 #pragma unroll
-  for (int p = 0; p < 2; ++p)
+  for (int p = 0; p < NA; ++p)
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
@@ -245,34 +249,55 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
         if constexpr (KS == 0) {
           // G = 32: lanes 0-31 carry codes 0-31 of the k-step (group 2 kg)
           // and lanes 32-63 codes 32-63 (group 2 kg + 1), for both operands.
-          // Two MFMAs, each with the other lane half of the weights zeroed,
-          // into acc[0] (even groups) and acc[1] (odd groups); each moves
-          // from the group two back to its current one (S_{g-2} / S_g).
-          const float f0 = ks > 0 ? (PARTIALS ? 0.f : s_rat2[2 * kg]) : 1.f;
-          const float f1 = ks > 0 ? (PARTIALS ? 0.f : s_rat2[2 * kg + 1]) : 1.f;
+          // Two MFMAs per block, each with the other lane half of the
+          // weights zeroed.
           const bool lo = lane < 32;
           const v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
           const v8i fw0 = lo ? fw : z, fw1 = lo ? z : fw;
+          if constexpr (NA == 2 && TJ == 1) {
+            // acc[0] takes the even groups, acc[1] the odd ones; each moves
+            // from the group two back to its current one (S_{g-2} / S_g)
+            const float f0 = ks > 0 ? (PARTIALS ? 0.f : s_rat2[2 * kg]) : 1.f;
+            const float f1 = ks > 0 ? (PARTIALS ? 0.f : s_rat2[2 * kg + 1]) : 1.f;
+            const v8i fx = widen(*reinterpret_cast<const v4u*>(buf + swz(32 + (lane & 31), c)));
+            acc[0][0] *= f0;
+            acc[0][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw0, fx, acc[0][0], 0, 0, 0, 0, 0, 0);
+            acc[NA - 1][0] *= f1;
+            acc[NA - 1][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw1, fx, acc[NA - 1][0], 0, 0, 0, 0, 0, 0);
+            if constexpr (PARTIALS) {
+              dump_piece<TJ>(a, acc[0], acc[0], false, t0, n0, lane, 2 * kg, ngroups);
+              dump_piece<TJ>(a, acc[NA - 1], acc[0], false, t0, n0, lane, 2 * kg + 1, ngroups);
+            }
+          } else {
+            // one accumulator per block, moved from group 2 kg - 1 to 2 kg
+            // and then to 2 kg + 1; every block's first MFMA goes out before
+            // any block's second rescale
+            const float f0 = ks > 0 ? (PARTIALS ? 0.f : s_rat[2 * kg]) : 1.f;
+            const float f1 = PARTIALS ? 0.f : s_rat[2 * kg + 1];
+            v8i fx[TJ];
 #pragma unroll
-          for (int j = 0; j < TJ; ++j) {
-            const v8i fx = widen(*reinterpret_cast<const v4u*>(buf + swz(32 + 32 * j + (lane & 31), c)));
-            acc[0][j] *= f0;
-            acc[0][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw0, fx, acc[0][j], 0, 0, 0, 0, 0, 0);
-            acc[1][j] *= f1;
-            acc[1][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw1, fx, acc[1][j], 0, 0, 0, 0, 0, 0);
+            for (int j = 0; j < TJ; ++j) fx[j] = widen(*reinterpret_cast<const v4u*>(buf + swz(32 + 32 * j + (lane & 31), c)));
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+              acc[0][j] *= f0;
+              acc[0][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw0, fx[j], acc[0][j], 0, 0, 0, 0, 0, 0);
+            }
+            if constexpr (PARTIALS) dump_piece<TJ>(a, acc[0], acc[0], false, t0, n0, lane, 2 * kg, ngroups);
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+              acc[0][j] *= f1;
+              acc[0][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw1, fx[j], acc[0][j], 0, 0, 0, 0, 0, 0);
+            }
+            if constexpr (PARTIALS) dump_piece<TJ>(a, acc[0], acc[0], false, t0, n0, lane, 2 * kg + 1, ngroups);
           }
-          if constexpr (PARTIALS) {
-            dump_piece<TJ>(a, acc[0], acc[1], false, t0, n0, lane, 2 * kg, ngroups);
-            dump_piece<TJ>(a, acc[1], acc[0], false, t0, n0, lane, 2 * kg + 1, ngroups);
-          }
-        } else {
+        } else if constexpr (NA == 2) {
           // acc[q] (q = k-step parity, fixed by the unrolled u: a round is 4
           // k-steps) last took k-step kg - 2. G = 64: one group per k-step,
           // so that was two groups back (S_{g-2} / S_g); G >= 128: one group
           // back in the first two k-steps of a group, else the same group.
           // Group starts fall on k-steps with u % KS == 0, so the multiply
           // is compiled in only where one can apply (by 1 where none does).
-          const int q = u & 1;
+          const int q = (u & 1) * (NA - 1);
           if (KS == 1 || u % KS < 2) {
             float f = 1.f;
             if (ks >= 2) {
@@ -293,7 +318,27 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
           // at G = 64 the group is acc[q] alone, else both accumulators
           // hold pieces of it
           if (PARTIALS && (((kg + 1) & (kspg - 1)) == 0 || ks == kpw - 1))
-            dump_piece<TJ>(a, acc[q], acc[1 - q], kspg > 1, t0, n0, lane, kg >> log2spg, ngroups);
+            dump_piece<TJ>(a, acc[q], acc[(NA - 1) - q], kspg > 1, t0, n0, lane, kg >> log2spg, ngroups);
+        } else {
+          // entering a new group: the accumulator goes from units of S_{g-1}
+          // to units of S_g. Group starts fall only on k-steps with
+          // u % KS == 0; the multiply there is unconditional (by 1 when no
+          // group starts, and at the wave's first k-step, whose sum so far
+          // is empty).
+          if (u % KS == 0) {
+            const float rg = PARTIALS ? 0.f : s_rat[kg >> log2spg];
+            const float f = (ks > 0 && (kg & (kspg - 1)) == 0) ? rg : 1.f;
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) acc[0][j] *= f;
+          }
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) {
+            const v8i fx = widen(*reinterpret_cast<const v4u*>(buf + swz(32 + 32 * j + (lane & 31), c)));
+            acc[0][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw, fx, acc[0][j], 0, 0, 0, 0, 0, 0);
+          }
+          // the group ends here, or the wave's run ends inside it (a piece)
+          if (PARTIALS && (((kg + 1) & (kspg - 1)) == 0 || ks == kpw - 1))
+            dump_piece<TJ>(a, acc[0], acc[0], false, t0, n0, lane, kg >> log2spg, ngroups);
         }
       }
     }
@@ -308,12 +353,21 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
   // absolute with the scale of its last group.
   const bool pieces = kpw < kspg;
   const int wpg = pieces ? kspg / kpw : 1;  // waves per group
-  const float sl0 = pieces ? 1.f : s_lastp[2 * wave], sl1 = pieces ? 1.f : s_lastp[2 * wave + 1];
   float* part = reinterpret_cast<float*>(buf);
+  if constexpr (NA == 2) {
+    const float sl0 = pieces ? 1.f : s_lastp[2 * wave], sl1 = pieces ? 1.f : s_lastp[2 * wave + 1];
 #pragma unroll
-  for (int j = 0; j < TJ; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) part[(j * 16 + e) * 64 + lane] = acc[0][j][e] * sl0 + acc[1][j][e] * sl1;
+      for (int e = 0; e < 16; ++e)
+        part[(j * 16 + e) * 64 + lane] = acc[0][j][e] * sl0 + acc[NA - 1][j][e] * sl1;
+  } else {
+    const float sl = pieces ? 1.f : s_last[wave];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) part[(j * 16 + e) * 64 + lane] = acc[0][j][e] * sl;
+  }
   __syncthreads();
 
   // Sum of the 8 waves' sums in their storage order (consecutive threads
