@@ -81,7 +81,8 @@ typedef enum {
   RRS_OK = 0,
   RRS_EINVAL = -1,       /* bad argument (shape, null pointer, short buffer) */
   RRS_EUNSUPPORTED = -2, /* legal request the library does not serve */
-  RRS_EHIP = -3          /* a HIP launch or runtime call failed */
+  RRS_EHIP = -3,         /* a HIP launch or runtime call failed */
+  RRS_ETOOBIG = -4       /* rrs_linear_noalloc: the call needs more than its fixed scratch */
 } rrs_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -295,6 +296,29 @@ int rrs_gemm_form(int M, int K, int N, int G);
 int rrs_gemm_partials(const uint8_t* xq, int M, int K, int N, int G,
                       const void* wq, int m0, int m1, int n0, int n1,
                       int32_t* P, hipStream_t s);
+
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): rrs_linear without the
+ * caller's workspace. The workspace (synchronisation block, xq, dx, S) is a
+ * device array of RRS_NOALLOC_SCRATCH_BYTES inside the library, one per GPU
+ * the library runs on, held until the process ends; the call allocates
+ * nothing. A call needs rrs_workspace_bytes(M, K, G) bytes of it, less the
+ * Kronecker row area (for K = m 2^k the three-launch front end rotates
+ * every row twice instead); a larger request returns RRS_ETOOBIG and
+ * launches nothing (at K = 4096 every G fits up to M = 11974 tokens, at
+ * K = 8192 and G = 128 up to M = 6057). X, perm, wq
+ * and Y as for rrs_linear (wq from rrs_prepare_weights).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (it starts zeroed, and the one-launch front end's call count
+ * makes clearing between calls unnecessary): calls that overlap in time on
+ * one GPU (several streams, or several host threads) race and must not be
+ * made. If a one-launch wait ever gives up in it (possible only when other
+ * work holds part of the device), every later call on that GPU returns NaN
+ * in Y until the process ends. */
+#define RRS_NOALLOC_SCRATCH_BYTES ((size_t)24 << 20)
+int rrs_linear_noalloc(const void* X_fp16, int M, int K, int N, int G,
+                       const int32_t* perm, const void* wq, float* Y,
+                       hipStream_t s);
 
 #ifdef __cplusplus
 }

@@ -17,7 +17,8 @@ from typing import Optional
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "lib", "librrs.so")
 
-RRS_OK, RRS_EINVAL, RRS_EUNSUPPORTED, RRS_EHIP = 0, -1, -2, -3
+RRS_OK, RRS_EINVAL, RRS_EUNSUPPORTED, RRS_EHIP, RRS_ETOOBIG = 0, -1, -2, -3, -4
+RRS_NOALLOC_SCRATCH_BYTES = 24 << 20
 RRS_FLAG_NO_ROTATE = 1
 RRS_FLAG_NO_SMOOTH = 2
 RRS_FLAG_TWO_PASS = 4
@@ -31,6 +32,7 @@ EXPORTS = (
     "rrs_gemm_partials", "rrs_frontend_passes", "rrs_gemm_form",
     "rrs_calibrate_perm_signed", "rrs_prepare_weights_signed", "rrs_linear_signed",
     "rrs_frontend_signed", "rrs_calibrate_perm_ex", "rrs_prepare_weights_ex", "rrs_linear_ex",
+    "rrs_linear_noalloc",
 )
 
 
@@ -72,6 +74,7 @@ def _declare(lib):
         "rrs_calibrate_perm_ex": (i, [vp, i, i, vp, i, vp, vp, sz, vp]),
         "rrs_prepare_weights_ex": (i, [vp, i, i, vp, vp, i, vp, vp]),
         "rrs_linear_ex": (i, [vp, i, i, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
+        "rrs_linear_noalloc": (i, [vp, i, i, i, i, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -291,6 +294,17 @@ def rrs_linear_ex(X, G: int, perm, dsign, flags: int, wq, Y, ws, stream=None) ->
         _dev(X, torch.float16, "X"), M, K, N, G, _dev(perm, torch.int32, "perm", (K,)), _opt_sign(dsign, K),
         flags, _dev(wq, torch.uint8, "wq", min_numel=rrs_weight_bytes(K, N)),
         _dev(Y, torch.float32, "Y", (M, N)), _dev(ws, None, "ws"), _nbytes(ws), _stream(stream)))
+
+
+def rrs_linear_noalloc(X, G: int, perm, wq, Y, stream=None) -> None:
+    """rrs_linear on the library's fixed scratch (no workspace argument)."""
+    torch = _torch()
+    M, K = X.shape
+    N = Y.shape[1]
+    _check("rrs_linear_noalloc", lib().rrs_linear_noalloc(
+        _dev(X, torch.float16, "X"), M, K, N, G, _dev(perm, torch.int32, "perm", (K,)),
+        _dev(wq, torch.uint8, "wq", min_numel=rrs_weight_bytes(K, N)),
+        _dev(Y, torch.float32, "Y", (M, N)), _stream(stream)))
 
 
 def rrs_gemm(xq, dx, S, G: int, wq, Y, stream=None) -> None:

@@ -68,6 +68,7 @@ RRS_API const char* rrs_status_string(int status) {
     case RRS_EINVAL: return "RRS_EINVAL: invalid argument";
     case RRS_EUNSUPPORTED: return "RRS_EUNSUPPORTED: unsupported configuration";
     case RRS_EHIP: return "RRS_EHIP: HIP runtime or launch failure";
+    case RRS_ETOOBIG: return "RRS_ETOOBIG: request exceeds the fixed scratch of rrs_linear_noalloc";
     default: return "RRS: unknown status";
   }
 }

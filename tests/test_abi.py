@@ -35,6 +35,7 @@ def test_status_strings_and_version():
     assert "EINVAL" in rra.rrs_status_string(-1)
     assert "EUNSUPPORTED" in rra.rrs_status_string(-2)
     assert "EHIP" in rra.rrs_status_string(-3)
+    assert "ETOOBIG" in rra.rrs_status_string(rra.RRS_ETOOBIG)
     assert "unknown" in rra.rrs_status_string(42)
     assert rra.rrs_version().startswith("rrs-gfx950")
 
@@ -268,3 +269,16 @@ def test_ablation_entry_points_reject():
     odd = ctypes.c_void_p(0x1004)
     assert L.rrs_linear_ex(DUMMY, 16, 256, 256, 128, DUMMY, odd, 0, DUMMY, DUMMY, DUMMY, 1 << 20,
                            NULL) == rra.RRS_EINVAL
+
+
+def test_noalloc_rejects_on_host():
+    """rrs_linear_noalloc checks its arguments and the scratch capacity on the
+    host before touching the device."""
+    L = rra.lib()
+    assert L.rrs_linear_noalloc(DUMMY, 16, 100, 64, 32, DUMMY, DUMMY, DUMMY, NULL) == rra.RRS_EINVAL
+    assert L.rrs_linear_noalloc(DUMMY, 16, 4096, 0, 128, DUMMY, DUMMY, DUMMY, NULL) == rra.RRS_EINVAL
+    assert L.rrs_linear_noalloc(DUMMY, 16, 4096, 64, 128, NULL, DUMMY, DUMMY, NULL) == rra.RRS_EINVAL
+    assert L.rrs_linear_noalloc(ctypes.c_void_p(0x1004), 16, 4096, 64, 128, DUMMY, DUMMY, DUMMY,
+                                NULL) == rra.RRS_EINVAL
+    assert L.rrs_linear_noalloc(DUMMY, 12167, 4096, 64, 128, DUMMY, DUMMY, DUMMY, NULL) == rra.RRS_ETOOBIG
+    assert L.rrs_linear_noalloc(NULL, 0, 4096, 64, 128, DUMMY, DUMMY, NULL, NULL) == rra.RRS_OK
