@@ -11,7 +11,17 @@ the front end's GB/s, a roofline object for the dominant kernel (the GEMM,
 whose int4 x int4 products run on fp8 matrix cores, against the dense fp8
 peak, which equals the dense int8 peak) and one for the front end (against
 HBM peak), each kernel timed alone with HIP events on the stream it runs on,
-and the CPU oracle timed on the host as a reported baseline.
+and the CPU oracle timed on the host as a reported baseline. The oracle leg
+also checks the timed run's own outputs (codes of every token, Y on sampled
+rows) and reports the counts.
+
+Before the counted warm-up steps, steps run for --settle-s seconds so that
+the shader clock reaches its loaded level; the clock levels are sampled
+while the timed loop's work is still running on the GPU.
+
+--ablation times the component switches of the method (Runtime Smooth
+alone, the rotation alone, the full method) on the same workload, each
+with the oracle's output error, in an "ablation" list of the same line.
 
 HBM traffic per launch ("traffic") comes from rocprofv3 FETCH_SIZE and
 WRITE_SIZE counter runs recorded in profiles/traffic.txt, scaled by the
@@ -44,8 +54,13 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=1000,
-                    help="untimed steps first: the shader clock needs tens of milliseconds of load to settle")
+    ap.add_argument("--warmup", type=int, default=1000, help="untimed steps before the timed ones")
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="seconds of untimed steps before the warm-up steps (the shader clock needs tens of "
+                         "milliseconds of load to reach its loaded level)")
+    ap.add_argument("--ablation", action="store_true",
+                    help="also time Runtime Smooth alone and the rotation alone (and report the oracle's error "
+                         "of each variant); every G of the workload")
     ap.add_argument("--workload", default="o_proj")
     ap.add_argument("--G", type=int, default=None)
     ap.add_argument("--signed", action="store_true",
@@ -83,6 +98,21 @@ def recorded_traffic(kernel, source, workload):
                         "bytes": int(parts[3]) + int(parts[4]), "copy_scale": float(parts[5]),
                         "source": f"{source}@{sha}"}
     return None
+
+
+def sample_clocks():
+    """Current shader / memory clock levels from the driver's sysfs tables
+    (the level marked with *); no program is started from this process."""
+    import glob
+    clocks = {}
+    try:
+        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_[sm]clk")):
+            cur = [l.strip() for l in open(path) if "*" in l]
+            if cur:
+                clocks[path.split("/")[-3] + ":" + path.rsplit("_", 1)[-1]] = cur[0]
+    except Exception:
+        pass
+    return clocks or None
 
 
 def copy_probe(mib):
@@ -132,7 +162,6 @@ def main():
     wq0 = torch.empty(rra.rrs_weight_bytes(K, N), dtype=torch.uint8, device=dev)
     dsign = None
     if args.signed:
-        import numpy as np
         bits = np.random.default_rng(1234).integers(0, 2**32, size=K // 32, dtype=np.uint64).astype(np.uint32)
         dsign = torch.from_numpy(bits.view(np.int32)).to(dev)
         rra.rrs_calibrate_perm_signed(torch.from_numpy(xc).to(dev), dsign, perm, cws)
@@ -174,7 +203,9 @@ def main():
         xq, dx, S = s["views"]
         rra.rrs_gemm(xq, dx, S, G, s["wq"], s["Y"], stream)
 
-    def timed(fn, steps, warmup):
+    clock_log = {}
+
+    def timed(fn, steps, warmup, tag=None):
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
@@ -185,17 +216,36 @@ def main():
         for i in range(steps):
             fn(i)
         ev1.record(stream)
+        if tag is not None:
+            # the host has queued the loop; while the GPU still runs it, read
+            # the clock levels (and note whether the work was still in flight)
+            clk = sample_clocks()
+            clock_log[tag] = {"levels": clk, "gpu_busy_at_sample": not ev1.query()}
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         return ev0.elapsed_time(ev1) / steps, wall
 
+    def settle(fn, seconds):
+        """Untimed steps for `seconds` of wall time (the clock-settle phase)."""
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(20):
+                fn(n)
+                n += 1
+            torch.cuda.synchronize()
+        return {"seconds": round(time.perf_counter() - t0, 3), "steps": n}
+
     if args.profile_gemm_only:
+        for i in range(nsets):   # codes and scales in every set's workspace first
+            step(i)
         ms, _ = timed(gemm_step, args.steps, args.warmup)
         print(json.dumps({"gemm_ms": ms}))
         return
 
+    settled = settle(step, args.settle_s)
     # whole layer: the metric
-    ms_step, wall = timed(step, args.steps, args.warmup)
+    ms_step, wall = timed(step, args.steps, args.warmup, tag="layer")
     # each part alone, same kernels, on the same stream
     ms_fe, _ = timed(fe_step, args.steps, args.warmup)
     ms_gemm, _ = timed(gemm_step, args.steps, args.warmup)
@@ -275,53 +325,119 @@ def main():
             "ms_per_call": round(ms_fe, 5),
         },
         "wall_s_timed_region": round(wall, 4),
+        "clock_settle": settled,
     }
 
     out["device"] = device_info(torch)
+    out["device"]["clocks_during_timed_loop"] = clock_log.get("layer")
+    if args.ablation:
+        out["ablation"] = ablation(args, wl, x, w, xc, timed, dev)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(x, w, xc, G)
+        s0 = sets[0]
+        rra.rrs_linear(s0["X"], G, perm, s0["wq"], s0["Y"], s0["ws"], stream) if dsign is None else \
+            rra.rrs_linear_signed(s0["X"], G, perm, dsign, s0["wq"], s0["Y"], s0["ws"], stream)
+        torch.cuda.synchronize()
+        xq, dx, S = s0["views"]
+        codes, dw = rra.weight_views(s0["wq"], K, N)
+        gpu = {"perm": perm.cpu().numpy(), "xq": xq.cpu().numpy(), "dx": dx.cpu().numpy(), "S": S.cpu().numpy(),
+               "codes": codes.cpu().numpy(), "dw": dw.cpu().numpy(), "Y": s0["Y"].cpu().numpy(),
+               "dsign": None if dsign is None else dsign.cpu().numpy().view(np.uint32)}
+        out["cpu_baseline"] = cpu_baseline(x, w, G, gpu)
 
     print(json.dumps(out), flush=True)
 
 
 def device_info(torch):
-    """The device and the clock levels the driver reports right after the
-    timed loops (the shader clock ramps under load; the level marked with *
-    is the one in use). Read from the driver's sysfs tables: no program is
-    started from this GPU process."""
-    import glob
+    """The device; its clock levels are sampled while the timed loop runs
+    (clocks_during_timed_loop) and, for reference, after all loops
+    (clocks_after, usually the idle level)."""
     props = torch.cuda.get_device_properties(0)
-    info = {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
-            "clocks": None}
-    try:
-        clocks = {}
-        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_[sm]clk")):
-            cur = [l.strip() for l in open(path) if "*" in l]
-            if cur:
-                clocks[path.split("/")[-3] + ":" + path.rsplit("_", 1)[-1]] = cur[0]
-        info["clocks"] = clocks or None
-    except Exception:
-        pass
-    return info
+    return {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
+            "clocks_after": sample_clocks()}
 
 
-def cpu_baseline(x, w, xc, G, budget_s=10.0):
+def ablation(args, wl, x, w, xc, timed, dev):
+    """The component switches on the same kernels (RRS rebuttal page,
+    "Incomplete ablation study"): per group size of the workload, the full
+    method, Runtime Smooth alone (no rotation on either side) and the
+    rotation alone (S = 1, the per-channel A4W4 baseline), each timed as a
+    whole layer (rrs_linear_ex), with the oracle's relative output error
+    against the float64 product X W when the CPU leg is on."""
+    import numpy as np
+    import torch
+    import rotated_runtime_activation_amd as rra
+    M, K, N = wl.M, wl.K, wl.N
+    variants = [("rrs", 0), ("rs_only", rra.RRS_FLAG_NO_ROTATE), ("rotation_only", rra.RRS_FLAG_NO_SMOOTH)]
+    Gs = (args.G,) if args.G else tuple(wl.G)
+    X0 = torch.from_numpy(x).to(dev)
+    W0 = torch.from_numpy(w).to(dev)
+    XC = torch.from_numpy(xc).to(dev)
+    stream = torch.cuda.current_stream()
+    ref = None
+    if not args.no_cpu_baseline:
+        ref = x.astype(np.float64) @ w.astype(np.float64)
+    rows = []
+    for G in Gs:
+        for name, flags in variants:
+            nr = flags & rra.RRS_FLAG_NO_ROTATE
+            perm = torch.empty(K, dtype=torch.int32, device=dev)
+            cws = torch.empty(rra.rrs_calibrate_workspace_bytes(K), dtype=torch.uint8, device=dev)
+            rra.rrs_calibrate_perm_ex(XC, None, nr, perm, cws)
+            wq = torch.empty(rra.rrs_weight_bytes(K, N), dtype=torch.uint8, device=dev)
+            rra.rrs_prepare_weights_ex(W0, perm, None, nr, wq)
+            ws_bytes = rra.rrs_workspace_bytes(M, K, G)
+            set_bytes = X0.numel() * 2 + wq.numel() + M * N * 4 + ws_bytes
+            nsets = max(3, -(-2 * MALL_BYTES // set_bytes))
+            sets = []
+            for _ in range(nsets):
+                ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+                rra.rrs_workspace_init(ws)
+                sets.append((X0.clone(), wq.clone(), torch.empty(M, N, dtype=torch.float32, device=dev), ws))
+
+            def step(i, sets=sets, G=G, flags=flags, perm=perm):
+                X, wq_i, Y, ws = sets[i % len(sets)]
+                rra.rrs_linear_ex(X, G, perm, None, flags, wq_i, Y, ws, stream)
+
+            ms, _ = timed(step, args.steps, args.warmup)
+            row = {"variant": name, "G": G, "flags": flags, "ms_per_step": round(ms, 5),
+                   "tops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 3),
+                   "frontend_launches": rra.rrs_frontend_passes(M, K, flags)}
+            if ref is not None:
+                import oracle
+                p_np = perm.cpu().numpy()
+                y = oracle.rrs_linear(x, w, p_np, G, rotate=not nr, smooth=not (flags & rra.RRS_FLAG_NO_SMOOTH))["Y"]
+                row["oracle_rel_fro_error"] = round(float(np.linalg.norm(y - ref) / np.linalg.norm(ref)), 6)
+            rows.append(row)
+            del sets
+            torch.cuda.empty_cache()
+    return rows
+
+
+def cpu_baseline(x, w, G, gpu, budget_s=10.0):
     """The CPU oracle as it stands, on the host cores: full layer steps
     (front end of all tokens + the grouped GEMM output), weights prepared
-    beforehand as on the GPU side, repeated until about ``budget_s`` seconds
-    of CPU work. Reported for context only."""
+    beforehand as on the GPU side, with the GPU's calibration order, repeated
+    until about ``budget_s`` seconds of CPU work. Reported for context only.
+
+    It also checks the GPU's outputs of the timed run against this oracle:
+    every activation and weight code (exempt within 1e-5 of a .5 boundary,
+    reported), and Y on sampled rows, both ways: against the oracle GEMM fed
+    the GPU's own codes and scales, and, on outputs whose row and column
+    carry no code flip, against the oracle's end-to-end result."""
+    import numpy as np
     import oracle
-    perm = oracle.calibrate_perm(xc)
-    wp = oracle.prepare_weights(w, perm)
+    perm = gpu["perm"]
+    d = None if gpu["dsign"] is None else oracle.signs_from_bits(gpu["dsign"], x.shape[1])
+    wp = oracle.prepare_weights(w, perm, d)
     try:
         from threadpoolctl import threadpool_info
-        blas = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         blas = 1
     reps = 0
     t0 = time.perf_counter()
     while True:
-        fe = oracle.frontend(x, perm, G)
+        fe = oracle.frontend(x, perm, G, d=d)
         y = oracle.linear_out(fe["q"], fe["dx"], fe["S"], wp["qw"], wp["dw"], G)["Y"]
         reps += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -330,19 +446,62 @@ def cpu_baseline(x, w, xc, G, budget_s=10.0):
     M, K = x.shape
     N = w.shape[1]
     # the method's own quantisation error on this workload (outside the timing)
-    import numpy as np
     ref = x.astype(np.float64) @ w.astype(np.float64)
     qerr = float(np.linalg.norm(y - ref) / np.linalg.norm(ref))
     return {
         "value": round(2.0 * M * N * K / dt / 1e12, 6),
         "unit": "TOPS",
-        "cores": blas,
+        "cores": len(os.sched_getaffinity(0)),
+        "blas_threads": blas,
         "kind": "oracle",
         "sample": (f"{reps} full steps of the same workload (M={M}, K={K}, N={N}, G={G}) in float64 "
-                   f"NumPy, {dt:.2f} s each; front end single-threaded, group GEMMs on {blas} BLAS threads"),
+                   f"NumPy, {dt:.2f} s each; front end single-threaded, group GEMMs on {blas} BLAS threads "
+                   f"({len(os.sched_getaffinity(0))} cores available)"),
         "quant_error": {"rel_fro": round(qerr, 6),
                         "of": "the oracle's Y against the float64 product X W of the same fp16 inputs"},
+        "parity": parity_of_timed_run(fe, wp, gpu, G),
     }
+
+
+def parity_of_timed_run(fe, wp, gpu, G, rows_sampled=64):
+    """Counts of the GPU's timed-run outputs against the oracle (see
+    cpu_baseline). The Y bound is the fp32 rounding bound of the GEMM chain,
+    gamma_n C with n = K/64 (K/32 at G = 32) + 2 K/G + 8, u = 2^-24, widened
+    for the flip-free check by the GPU scales' relative deviation."""
+    import numpy as np
+    import oracle
+    M, K = fe["q"].shape
+    q = oracle.unpack_codes(gpu["xq"])
+    qw = oracle.unpack_codes(gpu["codes"])
+    out = {}
+    for what, got, want, v in (("activation_codes", q, fe["q"], fe["v"]), ("weight_codes", qw, wp["qw"], wp["uw"])):
+        diff = got.astype(np.int16) != want.astype(np.int16)
+        ex = oracle.near_half(v, 1e-5)
+        out[what] = {"codes": int(want.size), "exempt": int(ex.sum()), "exempt_differ": int((diff & ex).sum()),
+                     "nonexempt_differ": int((diff & ~ex).sum())}
+    n = K // (32 if G == 32 else 64) + 2 * (K // G) + 8
+    tol = n * 2.0 ** -24 / (1 - n * 2.0 ** -24)
+    rows = np.linspace(0, M - 1, min(rows_sampled, M)).astype(np.int64)
+    f64 = lambda a: np.asarray(a, dtype=np.float64)
+    own = oracle.linear_out(q[rows], f64(gpu["dx"][rows]), f64(gpu["S"]), qw, f64(gpu["dw"]), G)
+    Yg = f64(gpu["Y"][rows])
+    C = np.where(own["C"] > 0, own["C"], 1.0)
+    e_own = float((np.abs(Yg - own["Y"]) / C).max())
+    ref = oracle.linear_out(fe["q"][rows], fe["dx"][rows], fe["S"], wp["qw"], wp["dw"], G)
+    rel = lambda g, r: np.abs(f64(g) - f64(r)) / np.where(f64(r) != 0, np.abs(f64(r)), 1.0)
+    dev = (1 + rel(gpu["dx"][rows], fe["dx"][rows])[:, None]) * (1 + rel(gpu["dw"], wp["dw"])[None, :]) * \
+        (1 + float(rel(gpu["S"], fe["S"]).max())) - 1
+    clean = (~(q[rows] != fe["q"][rows]).any(axis=1))[:, None] & (~(qw != wp["qw"]).any(axis=1))[None, :]
+    Cr = np.where(ref["C"] > 0, ref["C"], 1.0)
+    e_ref = np.abs(Yg - ref["Y"]) / Cr
+    out["Y"] = {"rows_sampled": int(rows.size), "tol_over_C": tol,
+                "max_err_over_C_vs_oracle_gemm_of_gpu_codes": e_own,
+                "flip_free_outputs": int(clean.sum()),
+                "max_err_over_C_flip_free_vs_oracle": float(e_ref[clean].max(initial=0.0)),
+                "ok": bool(e_own <= tol and np.all(e_ref[clean] <= (tol + dev[clean]) * (1 + 1e-6)))}
+    out["ok"] = bool(out["Y"]["ok"] and out["activation_codes"]["nonexempt_differ"] == 0
+                     and out["weight_codes"]["nonexempt_differ"] == 0)
+    return out
 
 
 if __name__ == "__main__":
