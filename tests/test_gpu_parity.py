@@ -174,6 +174,35 @@ GEMM_SHAPES = [
 ]
 
 
+# One shape for each few-token GEMM instantiation the shapes above leave
+# out: token blocks (1 up to 32 tokens, else 2) x load rounds in flight (1
+# for an odd, 2 for an even round count per wave) x the G class (32; 64;
+# 128; 256 and up) x waves per workgroup (4 .. 8, fixed by K). The exact
+# and partials tests run them bit for bit.
+FEW_TOKEN_CLASSES = [
+    (20, 41, 1024, 32), (20, 41, 1792, 32), (20, 41, 1024, 64), (20, 41, 1536, 64), (20, 41, 1792, 64),
+    (20, 41, 2048, 64), (20, 41, 1024, 128), (20, 41, 1536, 128), (20, 41, 1792, 128), (20, 41, 2048, 128),
+    (20, 41, 1024, 256), (20, 41, 1536, 256), (20, 41, 1792, 256), (20, 41, 2048, 256), (20, 41, 2560, 32),
+    (20, 41, 3072, 32), (20, 41, 3584, 32), (20, 41, 4096, 32), (20, 41, 2560, 64), (20, 41, 3584, 64),
+    (20, 41, 4096, 64), (20, 41, 2560, 128), (20, 41, 3072, 128), (20, 41, 3584, 128), (20, 41, 2560, 256),
+    (20, 41, 3584, 256), (50, 42, 1024, 32), (50, 42, 1536, 32), (50, 42, 1792, 32), (50, 42, 2048, 32),
+    (50, 42, 1024, 64), (50, 42, 1536, 64), (50, 42, 1792, 64), (50, 42, 1536, 128), (50, 42, 1792, 128),
+    (50, 42, 1536, 256), (50, 42, 1792, 256), (50, 42, 2048, 256), (50, 42, 2560, 32), (50, 42, 3072, 32),
+    (50, 42, 3584, 32), (50, 42, 2560, 64), (50, 42, 3072, 64), (50, 42, 3584, 64), (50, 42, 4096, 64),
+    (50, 42, 3072, 128), (50, 42, 3584, 128), (50, 42, 3072, 256),
+]
+
+# The tiled kernel's instantiations with both sets of waves on K: G = 32
+# (16 x 16 x 32 MFMA), G = 64 and 128 (rescale inside the product loop),
+# G >= 256 (groups over several stages), one group split between the two
+# sets (integer halves added before the scale), and an odd group count at a
+# Kronecker K (set 1 takes the larger share).
+TILED_CLASSES = [
+    (700, 130, 1024, 32), (130, 260, 512, 64), (600, 300, 4096, 128), (130, 300, 512, 256),
+    (700, 64, 2048, 2048), (600, 260, 1792, 256), (515, 257, 8192, 512),
+]
+
+
 def _random_codes(seed, M, N, K):
     g = np.random.default_rng(seed)
     q = g.integers(-7, 8, size=(M, K)).astype(np.int8)
@@ -183,7 +212,7 @@ def _random_codes(seed, M, N, K):
     return q, qw
 
 
-@pytest.mark.parametrize("M,N,K,G", GEMM_SHAPES)
+@pytest.mark.parametrize("M,N,K,G", GEMM_SHAPES + FEW_TOKEN_CLASSES + TILED_CLASSES)
 def test_gemm_partials_exact(M, N, K, G):
     """rrs_gemm_partials runs the instantiation rrs_gemm runs for the shape
     (its K split and rescale points, the accumulator multiplied by 0 where
@@ -234,7 +263,7 @@ def _exact_codes(seed, M, N, K):
     return q, qw
 
 
-@pytest.mark.parametrize("M,N,K,G", GEMM_SHAPES)
+@pytest.mark.parametrize("M,N,K,G", GEMM_SHAPES + FEW_TOKEN_CLASSES + TILED_CLASSES)
 def test_gemm_exact_through_product_kernels(M, N, K, G):
     """The kernels that produce Y, checked bit for bit: with dx = dw = 1 and
     group scales that are powers of two (neighbouring groups always
