@@ -146,6 +146,8 @@ def main():
     wl = workloads.WORKLOADS[args.workload]
     G = args.G or wl.G[len(wl.G) // 2]
     M, K, N = wl.M, wl.K, wl.N
+    # recorded counters are per workload, and per G where it sweeps G
+    tkey = wl.name if len(wl.G) == 1 else f"{wl.name}_G{G}"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -172,7 +174,9 @@ def main():
 
     ws_bytes = rra.rrs_workspace_bytes(M, K, G)
     set_bytes = X0.numel() * 2 + wq0.numel() + M * N * 4 + ws_bytes
-    nsets = max(3, -(-2 * MALL_BYTES // set_bytes))
+    # enough sets to exceed the Infinity Cache twice (at most 64: tiny
+    # shapes would need tens of thousands, and stay cache-resident anyway)
+    nsets = min(64, max(3, -(-2 * MALL_BYTES // set_bytes)))
     sets = []
     for _ in range(nsets):
         ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
@@ -251,6 +255,7 @@ def main():
     ms_gemm, _ = timed(gemm_step, args.steps, args.warmup)
 
     fe_launches = rra.rrs_frontend_passes(M, K, 0)
+    fe_src = "rrs_frontend.hip" if (K & (K - 1)) == 0 else "rrs_frontend_kron.hip"
     ops = 2.0 * M * N * K
     tops = ops / (ms_step * 1e-3) / 1e12
     gemm_tops = ops / (ms_gemm * 1e-3) / 1e12
@@ -268,8 +273,8 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(gemm_gbs / PEAK_HBM_GBS, 4),
-            "traffic": (recorded_traffic("gemm_small", "rrs_gemm_small.hip", wl.name) or {}).get("bytes"),
-            "traffic_detail": recorded_traffic("gemm_small", "rrs_gemm_small.hip", wl.name),
+            "traffic": (recorded_traffic("gemm_small", "rrs_gemm_small.hip", tkey) or {}).get("bytes"),
+            "traffic_detail": recorded_traffic("gemm_small", "rrs_gemm_small.hip", tkey),
             "algorithmic_bytes": gemm_bytes,
             "ms_per_launch": round(ms_gemm, 5),
         }
@@ -282,8 +287,8 @@ def main():
             "unit": "TFLOP/s",
             "op_kind": "2MNK ops of int4 codes on fp8 e4m3 MFMA (exact), against the dense fp8 peak 5.0 PFLOP/s",
             "frac": round(gemm_tops / PEAK_MFMA_TOPS, 4),
-            "traffic": (recorded_traffic("gemm", "rrs_gemm.hip", wl.name) or {}).get("bytes"),
-            "traffic_detail": recorded_traffic("gemm", "rrs_gemm.hip", wl.name),
+            "traffic": (recorded_traffic("gemm", "rrs_gemm.hip", tkey) or {}).get("bytes"),
+            "traffic_detail": recorded_traffic("gemm", "rrs_gemm.hip", tkey),
             "algorithmic_bytes": gemm_bytes,
             "ms_per_launch": round(ms_gemm, 5),
         }
@@ -319,8 +324,8 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(fe_gbs / PEAK_HBM_GBS, 4),
-            "traffic": (recorded_traffic("frontend", "rrs_frontend.hip", wl.name) or {}).get("bytes"),
-            "traffic_detail": recorded_traffic("frontend", "rrs_frontend.hip", wl.name),
+            "traffic": (recorded_traffic("frontend", fe_src, tkey) or {}).get("bytes"),
+            "traffic_detail": recorded_traffic("frontend", fe_src, tkey),
             "algorithmic_bytes": fe_bytes,
             "ms_per_call": round(ms_fe, 5),
         },
@@ -387,7 +392,7 @@ def ablation(args, wl, x, w, xc, timed, dev):
             rra.rrs_prepare_weights_ex(W0, perm, None, nr, wq)
             ws_bytes = rra.rrs_workspace_bytes(M, K, G)
             set_bytes = X0.numel() * 2 + wq.numel() + M * N * 4 + ws_bytes
-            nsets = max(3, -(-2 * MALL_BYTES // set_bytes))
+            nsets = min(64, max(3, -(-2 * MALL_BYTES // set_bytes)))
             sets = []
             for _ in range(nsets):
                 ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
