@@ -205,7 +205,8 @@ struct GemmCtx {
   typename Mm::acc_t acc[TI][TJ];
   const float* rat;
   uint32_t* sbar;   // this set's arrival counter (LDS)
-  uint32_t* sbar_o;  // the other set's arrival counter (LDS)
+  uint32_t* sbar2;   // both sets' counters, set 0's first (LDS)
+  int setid;         // this wave's set
   uint32_t nbar = 0;
 
   __device__ GemmCtx(const GemmArgs& args, const float* s_rat) : a(args), rat(s_rat) {}
@@ -343,20 +344,24 @@ struct GemmCtx {
     const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u32*)sbar));
     const uint32_t one = 1u;
     if (lane == 0) asm volatile("ds_add_u32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(addr), "v"(one) : "memory");
+    // each poll reads both sets' counters (adjacent words) at once: this
+    // set's decides the wait, the other set's the priority below
+    const uint32_t both_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u32*)sbar2));
+    uint32_t no = 0u;
     for (uint32_t it = 0; it < kBarSpinLimit; ++it) {
-      uint32_t n;
-      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(n) : "v"(addr) : "memory");
-      if (__builtin_amdgcn_readfirstlane(n) >= nbar) break;
+      uint64_t both;
+      asm volatile("ds_read2_b32 %0, %1 offset1:1\n\ts_waitcnt lgkmcnt(0)" : "=v"(both) : "v"(both_addr) : "memory");
+      const uint32_t c0 = static_cast<uint32_t>(both), c1 = static_cast<uint32_t>(both >> 32);
+      const uint32_t n = __builtin_amdgcn_readfirstlane(setid ? c1 : c0);
+      no = __builtin_amdgcn_readfirstlane(setid ? c0 : c1);
+      if (n >= nbar) break;
       __builtin_amdgcn_s_sleep(0);
     }
     // Balance the sets: wave w of each set shares a SIMD, and with equal
     // priorities the older wave (set 0) wins every issue conflict, so set 1
     // would finish its half of K several microseconds late. A wave whose set
     // is a stage or more behind the other set raises its priority.
-    const uint32_t addr_o = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u32*)sbar_o));
-    uint32_t no;
-    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(no) : "v"(addr_o) : "memory");
-    if (__builtin_amdgcn_readfirstlane(no) > nbar)
+    if (no > nbar)
       __builtin_amdgcn_s_setprio(2);
     else
       __builtin_amdgcn_s_setprio(0);
@@ -526,7 +531,8 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
 
   if (tid < kSets) s_bar[tid] = 0u;
   c.sbar = &s_bar[set];
-  c.sbar_o = &s_bar[1 - set];
+  c.sbar2 = &s_bar[0];
+  c.setid = set;
   __syncthreads();  // tables and counters published
   if (set == 0) {
     c.template run<0>(nsteps);

@@ -219,7 +219,16 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
   }
   __syncthreads();
 
-  for (int r0 = 0; r0 < rounds; r0 += NR) {
+  // Rounds NR ahead are fetched into the slot just emptied. For G >= 64 the
+  // last NR rounds run as a second pass of the loop that fetches nothing
+  // (at K = N = 8192 these would be a third of a wave's loads). At G = 32
+  // every iteration refills (past the end with the last round again), which
+  // keeps that instantiation's schedule unchanged.
+  constexpr bool kPeel = KS > 0;
+  for (int pass = 0; pass < (kPeel ? 2 : 1); ++pass) {
+  const int rbeg = pass == 0 ? 0 : rounds - NR;
+  const int rend = (kPeel && pass == 0) ? rounds - NR : rounds;
+  for (int r0 = rbeg; r0 < rend; r0 += NR) {
 #pragma unroll
     for (int s = 0; s < NR; ++s) {
       const int r = r0 + s;
@@ -233,13 +242,14 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // refill the slot with the round NR ahead (past the end: the last
-      // round again, so every iteration issues the same loads)
-      const int off = min(r + NR, rounds - 1) * kRows;
+      // refill the slot with the round NR ahead
+      if (!kPeel || pass == 0) {
+        const int off = min(r + NR, rounds - 1) * kRows;
 #pragma unroll
-      for (int i = 0; i < kWL; ++i) rw[s][i] = *reinterpret_cast<const v4u*>(wbase + off + woff[i]);
+        for (int i = 0; i < kWL; ++i) rw[s][i] = *reinterpret_cast<const v4u*>(wbase + off + woff[i]);
 #pragma unroll
-      for (int i = 0; i < kXL; ++i) rx[s][i] = *reinterpret_cast<const v4u*>(xbase + off + xoff[i]);
+        for (int i = 0; i < kXL; ++i) rx[s][i] = *reinterpret_cast<const v4u*>(xbase + off + xoff[i]);
+      }
 #pragma unroll
       for (int u = 0; u < kRound; ++u) {
         const int ks = r * kRound + u;
@@ -342,6 +352,7 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
         }
       }
     }
+  }
   }
 
   if constexpr (PARTIALS) return;
