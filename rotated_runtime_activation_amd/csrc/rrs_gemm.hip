@@ -487,14 +487,6 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
     c.lblk[d] = blk * 1024;
   }
 
-  // the first loads go out before the tables below are read, so the two
-  // latencies overlap
-  if (set == 0) {
-    c.template prologue<0>();
-  } else if (c.st1 > c.st0) {
-    c.template prologue<1>();
-  }
-
   if (!PARTIALS) {
     // s_rat[g] = S[g-1] / S[g]: entering group g rescales the accumulator
     for (int g = tid; g < c.ngroups; g += kThreadsWG) s_rat[g] = g > 0 ? a.S[g - 1] / a.S[g] : 1.f;
@@ -514,6 +506,15 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
       const int st_end = tid - kTT - kTN == 0 ? half : c.nstage;  // end stage of set 0 / set 1
       s_send[tid - kTT - kTN] = a.S[((st_end * 128 > a.K ? a.K : st_end * 128) - 1) >> a.log2G];
     }
+  }
+
+  // the first stages' loads go out after the tables' reads above: loads
+  // complete in order, so tables read after them would hold the first step
+  // until the second stage has landed too
+  if (set == 0) {
+    c.template prologue<0>();
+  } else if (c.st1 > c.st0) {
+    c.template prologue<1>();
   }
 
   // fragment rows: row lane % BR of each BR-row block; the swizzle of the

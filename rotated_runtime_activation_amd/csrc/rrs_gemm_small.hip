@@ -179,6 +179,35 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[p][j][e] = 0.f;
 
+  // The scale operands the loop and the epilogue need are loaded into
+  // registers before the first rounds (clamped indices: every thread loads,
+  // each keeps what its slot below needs). Loads complete in order, so
+  // scales loaded after the rounds would hold the first round until the
+  // second had landed too; loaded first, they are in by the time round 0
+  // is. A set error word (a front end whose grid-wide wait gave up) makes
+  // every output NaN.
+  uint32_t r_err = 0u;
+  float r_s0 = 1.f, r_s1 = 1.f, r_s2 = 1.f, r_dx = 0.f, r_dw = 0.f, r_last = 1.f;
+  if (!PARTIALS) {
+    if (a.err != nullptr) r_err = *a.err;
+    const int g0 = min(tid, ngroups - 1);
+    r_s0 = a.S[g0];
+    r_s1 = a.S[max(g0 - 1, 0)];
+    r_s2 = a.S[max(g0 - 2, 0)];
+    r_dx = dx[min(tid, Mt - 1)];
+    r_dw = a.dw[min(n0 + max(tid - 64, 0), a.N - 1)];
+    int last = 0;  // code whose group scale this thread's s_last / s_lastp slot takes
+    if (tid >= 64 + kTN && tid < 64 + kTN + kWaves) {
+      const int w = tid - 64 - kTN;
+      last = (w + 1) * kpw * 64 - 1;  // the wave's last code
+    } else if (tid >= 64 + kTN + kWaves && tid < 64 + kTN + 3 * kWaves) {
+      // last code of accumulator q of wave w: G = 32, codes 32 q .. 32 q + 31
+      // of the wave's last k-step; else the last k-step of parity q
+      const int i = tid - 64 - kTN - kWaves, w = i >> 1, q = i & 1;
+      last = KS == 0 ? ((w + 1) * kpw - 1) * 64 + 32 * q + 31 : ((w + 1) * kpw - 2 + q) * 64 + 63;
+    }
+    r_last = a.S[last >> a.log2G];
+  }
 #pragma unroll
   for (int s = 0; s < NR; ++s) {
     const int off = min(s, rounds - 1) * kRows;
@@ -187,35 +216,25 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
 #pragma unroll
     for (int i = 0; i < kXL; ++i) rx[s][i] = *reinterpret_cast<const v4u*>(xbase + off + xoff[i]);
   }
-  // the scales the loop and the epilogue need, read up front after the
-  // first rounds' loads: their latency then overlaps those loads instead of
-  // ending the kernel (as plain loads at the end they cost several
-  // microseconds per call)
-  // a set error word (a front end whose grid-wide wait gave up) makes every
-  // output NaN
-  const bool poison = !PARTIALS && a.err != nullptr && *a.err != 0u;
-  const float base = poison ? __builtin_nanf("") : a.ybase;
   if (!PARTIALS) {
-    for (int g = tid; g < ngroups; g += kThreads) {
-      s_rat[g] = g > 0 ? a.S[g - 1] / a.S[g] : 1.f;
-      if (a.log2G <= 6) s_rat2[g] = g > 1 ? a.S[g - 2] / a.S[g] : 1.f;
+    const float base = r_err != 0u ? __builtin_nanf("") : a.ybase;
+    if (tid < ngroups) {
+      s_rat[tid] = tid > 0 ? r_s1 / r_s0 : 1.f;
+      if (a.log2G <= 6) s_rat2[tid] = tid > 1 ? r_s2 / r_s0 : 1.f;
     }
-  }
-  if (PARTIALS) {
-  } else if (tid < 64) {
-    s_dx[tid] = tid < Mt ? dx[tid] * base : 0.f;
-  } else if (tid < 64 + kTN) {
-    const int n = n0 + tid - 64;
-    s_dw[tid - 64] = n < a.N ? a.dw[n] : 0.f;
-  } else if (tid < 64 + kTN + kWaves) {
-    const int w = tid - 64 - kTN;
-    s_last[w] = a.S[(((w + 1) * kpw) * 64 - 1) >> a.log2G];  // group of the wave's last code
-  } else if (tid < 64 + kTN + 3 * kWaves) {
-    // last code of accumulator q of wave w: G = 32, codes 32 q .. 32 q + 31
-    // of the wave's last k-step; else the last k-step of parity q
-    const int i = tid - 64 - kTN - kWaves, w = i >> 1, q = i & 1;
-    const int last = KS == 0 ? ((w + 1) * kpw - 1) * 64 + 32 * q + 31 : ((w + 1) * kpw - 2 + q) * 64 + 63;
-    s_lastp[i] = a.S[last >> a.log2G];
+    for (int g = tid + kThreads; g < ngroups; g += kThreads) {  // more groups than threads
+      s_rat[g] = a.S[g - 1] / a.S[g];
+      if (a.log2G <= 6) s_rat2[g] = a.S[g - 2] / a.S[g];
+    }
+    if (tid < 64) {
+      s_dx[tid] = tid < Mt ? r_dx * base : 0.f;
+    } else if (tid < 64 + kTN) {
+      s_dw[tid - 64] = n0 + tid - 64 < a.N ? r_dw : 0.f;
+    } else if (tid < 64 + kTN + kWaves) {
+      s_last[tid - 64 - kTN] = r_last;
+    } else if (tid < 64 + kTN + 3 * kWaves) {
+      s_lastp[tid - 64 - kTN - kWaves] = r_last;
+    }
   }
   __syncthreads();
 
