@@ -182,7 +182,7 @@ def main():
         ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
         rra.rrs_workspace_init(ws)
         sets.append(dict(X=X0.clone(), wq=wq0.clone(), Y=torch.empty(M, N, dtype=torch.float32, device=dev),
-                         ws=ws, views=rra.workspace_views(ws, M, K, G)))
+                         ws=ws, views=rra.workspace_regions(ws, M, K, G)))
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -342,7 +342,7 @@ def main():
         rra.rrs_linear(s0["X"], G, perm, s0["wq"], s0["Y"], s0["ws"], stream) if dsign is None else \
             rra.rrs_linear_signed(s0["X"], G, perm, dsign, s0["wq"], s0["Y"], s0["ws"], stream)
         torch.cuda.synchronize()
-        xq, dx, S = s0["views"]
+        xq, dx, S = rra.workspace_views(s0["ws"], M, K, G)  # row-major copy of the codes
         codes, dw = rra.weight_views(s0["wq"], K, N)
         gpu = {"perm": perm.cpu().numpy(), "xq": xq.cpu().numpy(), "dx": dx.cpu().numpy(), "S": S.cpu().numpy(),
                "codes": codes.cpu().numpy(), "dw": dw.cpu().numpy(), "Y": s0["Y"].cpu().numpy(),

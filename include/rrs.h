@@ -47,6 +47,14 @@
  *   cores consume directly. A zero code may carry either sign bit (a
  *   negative value that rounds to 0 keeps its sign); readers take any zero
  *   magnitude as 0. The pages fix no storage layout.
+ * - Stored layout of a code matrix (activation codes xq [M rows], prepared
+ *   weight codes [N rows], each row K/2 bytes in reordered K order): rows in
+ *   pairs, each row cut into 64-byte pieces (128 codes), piece c of rows 2p
+ *   and 2p + 1 side by side in one 128-byte line. Byte b of row r lies at
+ *     (r / 2) * 2 rs + (b / 64) * 128 + (r % 2) * 64 + b % 64,
+ *   rs = K/2 rounded up to 64 (for K = 64, 32 bytes of each piece are
+ *   used); rrs_codes_bytes(rows, K) bytes in all (an odd row count leaves
+ *   the last pair half used). The GEMMs then read whole 128-byte lines.
  * - Scales are reported in the unnormalised-Hadamard convention:
  *     dx[t] = r_t / 7 with r_t = max_j |Zp[t,j] / S_g(j)|,
  *     S[g]  = max over tokens and the group's channels of |Zp|,
@@ -91,15 +99,22 @@ const char* rrs_status_string(int status);
 /* Library version string, e.g. "rrs-gfx950 1.0". */
 const char* rrs_version(void);
 
+/* Bytes of a code matrix of `rows` rows of length K in the stored layout
+ * above (the xq buffer rrs_frontend writes for M = rows tokens). Returns 0
+ * for an invalid shape. */
+size_t rrs_codes_bytes(int rows, int K);
+
 /* Bytes of the opaque prepared-weight buffer for a [K, N] weight: the packed
- * codes wq [N][K/2] followed (256-byte aligned) by dw fp32 [N]. Returns 0 for
- * an invalid shape. */
+ * codes of the N output channels (rrs_codes_bytes(N, K) bytes, stored
+ * layout) followed (256-byte aligned) by dw fp32 [N]. Returns 0 for an
+ * invalid shape. */
 size_t rrs_weight_bytes(int K, int N);
 
 /* Bytes of the workspace that rrs_linear needs for M tokens: a
  * synchronisation block (rrs_sync_bytes(K, G): control words, a reserved
  * area, and a row of K/G 64-bit group-maximum words, tagged with the call
- * count, for each of up to 512 workgroups), then xq [M][K/2], dx [M] and
+ * count, for each of up to 512 workgroups), then xq (rrs_codes_bytes(M, K)
+ * bytes, stored layout), dx [M] and
  * S [K/G], each 256-byte aligned; for K = m 2^k (Kronecker rotation) also a
  * row area of M x K fp32 (the rotated, reordered rows, kept between the
  * front end's stats and quantise passes so that each row is rotated once).
@@ -191,7 +206,8 @@ int rrs_linear_ex(const void* X_fp16, int M, int K, int N, int G,
                   const void* wq, float* Y, void* ws, size_t ws_bytes,
                   hipStream_t s);
 
-/* Front end alone (same kernels as rrs_linear): writes xq uint8 [M][K/2],
+/* Front end alone (same kernels as rrs_linear): writes the codes xq
+ * (rrs_codes_bytes(M, K) bytes, stored layout),
  * dx fp32 [M] and S fp32 [K/G] (zero groups reported as 1). `ws` holds at
  * least rrs_sync_bytes(K, G) bytes, initialised once with
  * rrs_workspace_init. `flags` selects the ablations of the RRS rebuttal page
@@ -262,7 +278,7 @@ int rrs_frontend_passes(int M, int K, int flags);
  * group's exact partial is multiplied by its smoothing scale S_g before the
  * fp32 accumulation (RRS summary page, "Approach": the scales are not
  * migrated into the weights; RRS rebuttal page, "Novelty": group-wise
- * scales keep the GEMM's tiled scheme). xq uint8 [M][K/2] and dx fp32 [M]
+ * scales keep the GEMM's tiled scheme). xq (stored layout) and dx fp32 [M]
  * as rrs_frontend writes them, S fp32 [K/G], wq a prepared weight buffer,
  * Y fp32 [M, N] (fully overwritten). */
 int rrs_gemm(const uint8_t* xq, const float* dx, const float* S, int M, int K,

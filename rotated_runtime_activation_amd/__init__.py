@@ -32,7 +32,7 @@ EXPORTS = (
     "rrs_gemm_partials", "rrs_frontend_passes", "rrs_gemm_form",
     "rrs_calibrate_perm_signed", "rrs_prepare_weights_signed", "rrs_linear_signed",
     "rrs_frontend_signed", "rrs_calibrate_perm_ex", "rrs_prepare_weights_ex", "rrs_linear_ex",
-    "rrs_linear_noalloc",
+    "rrs_linear_noalloc", "rrs_codes_bytes",
 )
 
 
@@ -55,6 +55,7 @@ def _declare(lib):
         "rrs_status_string": (ctypes.c_char_p, [i]),
         "rrs_version": (ctypes.c_char_p, []),
         "rrs_weight_bytes": (sz, [i, i]),
+        "rrs_codes_bytes": (sz, [i, i]),
         "rrs_workspace_bytes": (sz, [i, i, i]),
         "rrs_sync_bytes": (sz, [i, i]),
         "rrs_workspace_init": (i, [vp, sz, vp]),
@@ -103,6 +104,13 @@ def _check(fn: str, status: int) -> None:
 @functools.lru_cache(maxsize=256)
 def rrs_weight_bytes(K: int, N: int) -> int:
     return int(lib().rrs_weight_bytes(K, N))
+
+
+@functools.lru_cache(maxsize=256)
+def rrs_codes_bytes(rows: int, K: int) -> int:
+    """Bytes of a code matrix of `rows` rows of length K in the stored
+    layout (include/rrs.h): the xq buffer of rrs_frontend for M = rows."""
+    return int(lib().rrs_codes_bytes(rows, K))
 
 
 def rrs_workspace_bytes(M: int, K: int, G: int) -> int:
@@ -219,7 +227,7 @@ def rrs_frontend(X, G: int, perm, xq, dx, S, ws, flags: int = 0, stream=None) ->
     M, K = X.shape
     _check("rrs_frontend", lib().rrs_frontend(
         _dev(X, torch.float16, "X"), M, K, G, _dev(perm, torch.int32, "perm", (K,)),
-        _dev(xq, torch.uint8, "xq", (M, K // 2)), _dev(dx, torch.float32, "dx", (M,)),
+        _dev(xq, torch.uint8, "xq", min_numel=rrs_codes_bytes(M, K)), _dev(dx, torch.float32, "dx", (M,)),
         _dev(S, torch.float32, "S", (K // G,)), _dev(ws, None, "ws"), _nbytes(ws), flags,
         _stream(stream)))
 
@@ -260,7 +268,7 @@ def rrs_frontend_signed(X, G: int, perm, dsign, xq, dx, S, ws, flags: int = 0, s
     _check("rrs_frontend_signed", lib().rrs_frontend_signed(
         _dev(X, torch.float16, "X"), M, K, G, _dev(perm, torch.int32, "perm", (K,)),
         _dev(dsign, torch.int32, "dsign", (K // 32,)),
-        _dev(xq, torch.uint8, "xq", (M, K // 2)), _dev(dx, torch.float32, "dx", (M,)),
+        _dev(xq, torch.uint8, "xq", min_numel=rrs_codes_bytes(M, K)), _dev(dx, torch.float32, "dx", (M,)),
         _dev(S, torch.float32, "S", (K // G,)), _dev(ws, None, "ws"), _nbytes(ws), flags,
         _stream(stream)))
 
@@ -308,45 +316,94 @@ def rrs_linear_noalloc(X, G: int, perm, wq, Y, stream=None) -> None:
 
 
 def rrs_gemm(xq, dx, S, G: int, wq, Y, stream=None) -> None:
+    """xq: the codes as rrs_frontend writes them (M from Y, K = G * S.numel())."""
     torch = _torch()
-    M, Kh = xq.shape
-    K = 2 * Kh
-    N = Y.shape[1]
+    M, N = Y.shape
+    K = G * S.numel()
     _check("rrs_gemm", lib().rrs_gemm(
-        _dev(xq, torch.uint8, "xq"), _dev(dx, torch.float32, "dx", (M,)),
+        _dev(xq, torch.uint8, "xq", min_numel=rrs_codes_bytes(M, K)), _dev(dx, torch.float32, "dx", (M,)),
         _dev(S, torch.float32, "S", (K // G,)), M, K, N, G,
         _dev(wq, torch.uint8, "wq", min_numel=rrs_weight_bytes(K, N)),
         _dev(Y, torch.float32, "Y", (M, N)), _stream(stream)))
 
 
-def rrs_gemm_partials(xq, N: int, G: int, wq, m0: int, m1: int, n0: int, n1: int, P,
+def rrs_gemm_partials(xq, M: int, K: int, N: int, G: int, wq, m0: int, m1: int, n0: int, n1: int, P,
                       stream=None) -> None:
     torch = _torch()
-    M, Kh = xq.shape
-    K = 2 * Kh
     _check("rrs_gemm_partials", lib().rrs_gemm_partials(
-        _dev(xq, torch.uint8, "xq"), M, K, N, G,
+        _dev(xq, torch.uint8, "xq", min_numel=rrs_codes_bytes(M, K)), M, K, N, G,
         _dev(wq, torch.uint8, "wq", min_numel=rrs_weight_bytes(K, N)), m0, m1, n0, n1,
         _dev(P, torch.int32, "P", (m1 - m0, n1 - n0, K // G)), _stream(stream)))
 
 
 # ----------------------------------------------------------- conveniences
+def codes_stored_view(buf, rows: int, K: int):
+    """Writable [pairs, 2, pieces, piece bytes] view of a code matrix in the
+    stored layout of include/rrs.h (row 2p + h, byte 64 c + e at [p, h, c,
+    e]); `buf` is a uint8 tensor starting at the matrix."""
+    kb = K // 2
+    rs = (kb + 63) // 64 * 64
+    pb = min(kb, 64)
+    pairs = (rows + 1) // 2
+    return buf.reshape(-1).as_strided((pairs, 2, kb // pb, pb), (2 * rs, 64, 128, 1))
+
+
+def codes_matrix(buf, rows: int, K: int):
+    """The code matrix [rows, K/2] (row-major, a copy) held in `buf` in the
+    stored layout."""
+    v = codes_stored_view(buf, rows, K)
+    return v.reshape(v.shape[0] * 2, K // 2)[:rows]
+
+
+def codes_buffer(codes, K: int, out=None):
+    """A buffer holding the row-major code matrix `codes` [rows, K/2] (uint8,
+    device) in the stored layout: `out` (rrs_codes_bytes(rows, K) bytes), or
+    a new zeroed tensor."""
+    torch = _torch()
+    rows = codes.shape[0]
+    if out is None:
+        out = torch.zeros(rrs_codes_bytes(rows, K), dtype=torch.uint8, device=codes.device)
+    v = codes_stored_view(out, rows, K)
+    src = codes if rows % 2 == 0 else torch.cat([codes, torch.zeros_like(codes[:1])])
+    v.copy_(src.reshape(v.shape))
+    return out
+
+
 def weight_views(wq, K: int, N: int):
-    """(codes uint8 [N, K/2], dw float32 [N]) views into a prepared-weight
-    buffer (layout documented in include/rrs.h)."""
-    off = ((N * (K // 2)) + 255) // 256 * 256
-    codes = wq[: N * (K // 2)].view(N, K // 2)
-    dw = wq[off: off + 4 * N].view(_torch().float32)
-    return codes, dw
+    """(codes uint8 [N, K/2] (a copy, row-major), dw float32 [N] (a view))
+    of a prepared-weight buffer (layout documented in include/rrs.h)."""
+    cb = rrs_codes_bytes(N, K)
+    off = (cb + 255) // 256 * 256
+    return codes_matrix(wq[:cb], N, K), wq[off: off + 4 * N].view(_torch().float32)
 
 
-def workspace_views(ws, M: int, K: int, G: int):
-    """(xq [M, K/2], dx [M], S [K/G]) views into an rrs_linear workspace."""
+def weight_codes_region(wq, K: int, N: int):
+    """The codes region of a prepared-weight buffer (stored layout, a view)."""
+    return wq[: rrs_codes_bytes(N, K)]
+
+
+def workspace_codes(ws, M: int, K: int, G: int):
+    """The xq region of an rrs_linear workspace (stored layout, a view), as
+    rrs_gemm takes it."""
+    xq_off = rrs_sync_bytes(K, G)
+    return ws[xq_off: xq_off + rrs_codes_bytes(M, K)]
+
+
+def workspace_regions(ws, M: int, K: int, G: int):
+    """(xq region (stored layout), dx [M], S [K/G]): views into an
+    rrs_linear workspace, as rrs_frontend writes and rrs_gemm reads them."""
     torch = _torch()
     a = lambda x: (x + 255) // 256 * 256
     xq_off = rrs_sync_bytes(K, G)
-    dx_off = xq_off + a(M * (K // 2))
+    dx_off = xq_off + a(rrs_codes_bytes(M, K))
     s_off = dx_off + a(4 * M)
-    return (ws[xq_off: xq_off + M * (K // 2)].view(M, K // 2),
+    return (ws[xq_off: xq_off + rrs_codes_bytes(M, K)],
             ws[dx_off: dx_off + 4 * M].view(torch.float32),
             ws[s_off: s_off + 4 * (K // G)].view(torch.float32))
+
+
+def workspace_views(ws, M: int, K: int, G: int):
+    """(xq [M, K/2] (a row-major copy), dx [M], S [K/G] (views)) of an
+    rrs_linear workspace."""
+    xq, dx, S = workspace_regions(ws, M, K, G)
+    return codes_matrix(xq, M, K), dx, S

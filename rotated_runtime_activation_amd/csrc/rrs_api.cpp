@@ -45,7 +45,7 @@ WsLayout ws_layout(int M, int K, int G) {
   WsLayout l{};
   l.sync = 0;
   l.xq = sync_bytes(K, G);
-  l.dx = l.xq + align256(static_cast<size_t>(M) * (K / 2));
+  l.dx = l.xq + align256(rrs::codes_bytes(static_cast<size_t>(M), K));
   l.S = l.dx + align256(sizeof(float) * static_cast<size_t>(M));
   l.rows = l.S + align256(sizeof(float) * static_cast<size_t>(K / G));
   l.rows_bytes = pow2(K) ? 0 : align256(sizeof(float) * static_cast<size_t>(M) * K);
@@ -77,7 +77,12 @@ RRS_API const char* rrs_version(void) { return "rrs-gfx950 1.0"; }
 
 RRS_API size_t rrs_weight_bytes(int K, int N) {
   if (!valid_K(K) || N < 1) return 0;
-  return align256(static_cast<size_t>(N) * (K / 2)) + align256(sizeof(float) * static_cast<size_t>(N));
+  return align256(rrs::codes_bytes(static_cast<size_t>(N), K)) + align256(sizeof(float) * static_cast<size_t>(N));
+}
+
+RRS_API size_t rrs_codes_bytes(int M, int K) {
+  if (M < 0 || !valid_K(K)) return 0;
+  return rrs::codes_bytes(static_cast<size_t>(M), K);
 }
 
 RRS_API size_t rrs_sync_bytes(int K, int G) {
@@ -130,7 +135,7 @@ int prepare_impl(const void* W_fp16, int K, int N, const int32_t* perm, const ui
   if (dsign != nullptr && (flags & RRS_FLAG_NO_ROTATE)) return RRS_EINVAL;
   if (!all_a16(W_fp16, perm, wq, dsign)) return RRS_EINVAL;
   uint8_t* codes = static_cast<uint8_t*>(wq);
-  float* dw = reinterpret_cast<float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
+  float* dw = reinterpret_cast<float*>(codes + align256(rrs::codes_bytes(static_cast<size_t>(N), K)));
   return hip_status(rrs::launch_weight_prep(static_cast<const uint16_t*>(W_fp16), K, N, perm, dsign,
                                             codes, dw, s, !(flags & RRS_FLAG_NO_ROTATE)));
 }
@@ -152,7 +157,7 @@ int frontend_impl(const void* X_fp16, int M, int K, int G, const int32_t* perm, 
   if (l.rows_bytes && ws_bytes >= l.total) {
     uint8_t* r = static_cast<uint8_t*>(ws) + l.rows;
     const size_t mk = static_cast<size_t>(M) * K;
-    if (!overlap(r, l.rows_bytes, X_fp16, 2 * mk) && !overlap(r, l.rows_bytes, xq, mk / 2) &&
+    if (!overlap(r, l.rows_bytes, X_fp16, 2 * mk) && !overlap(r, l.rows_bytes, xq, rrs::codes_bytes(static_cast<size_t>(M), K)) &&
         !overlap(r, l.rows_bytes, dx, 4 * static_cast<size_t>(M)) &&
         !overlap(r, l.rows_bytes, S, 4 * static_cast<size_t>(K / G)) &&
         !overlap(r, l.rows_bytes, perm, 4 * static_cast<size_t>(K)) &&
@@ -184,7 +189,7 @@ int linear_impl(const void* X_fp16, int M, int K, int N, int G, const int32_t* p
                                       S, sync, flags, s, zrows);
   if (e != hipSuccess) return RRS_EHIP;
   const uint8_t* codes = static_cast<const uint8_t*>(wq);
-  const float* dw = reinterpret_cast<const float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
+  const float* dw = reinterpret_cast<const float*>(codes + align256(rrs::codes_bytes(static_cast<size_t>(N), K)));
   // the GEMM reads the workspace's error word: a front end whose grid-wide
   // wait gave up (now or in an earlier call on this workspace) makes Y NaN
   const rrs::GemmCall gc{xq, dx, S, M, K, N, G, codes, dw, Y, nullptr, 0, 0, 0, 0,
@@ -253,7 +258,7 @@ RRS_API int rrs_gemm(const uint8_t* xq, const float* dx, const float* S, int M, 
   if (!all_a16(xq, dx, S, wq, Y)) return RRS_EINVAL;
   if (M == 0) return RRS_OK;
   const uint8_t* codes = static_cast<const uint8_t*>(wq);
-  const float* dw = reinterpret_cast<const float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
+  const float* dw = reinterpret_cast<const float*>(codes + align256(rrs::codes_bytes(static_cast<size_t>(N), K)));
   const rrs::GemmCall gc{xq, dx, S, M, K, N, G, codes, dw, Y, nullptr, 0, 0, 0, 0, true, nullptr};
   return hip_status(rrs::launch_gemm(gc, s));
 }
@@ -270,7 +275,7 @@ RRS_API int rrs_gemm_partials(const uint8_t* xq, int M, int K, int N, int G, con
   if (m0 < 0 || m1 > M || m0 >= m1 || n0 < 0 || n1 > N || n0 >= n1) return RRS_EINVAL;
   if (!all_a16(xq, wq, P)) return RRS_EINVAL;
   const uint8_t* codes = static_cast<const uint8_t*>(wq);
-  const float* dw = reinterpret_cast<const float*>(codes + align256(static_cast<size_t>(N) * (K / 2)));
+  const float* dw = reinterpret_cast<const float*>(codes + align256(rrs::codes_bytes(static_cast<size_t>(N), K)));
   const rrs::GemmCall gc{xq, nullptr, nullptr, M, K, N, G, codes, dw, nullptr, P, m0, m1, n0, n1, true, nullptr};
   return hip_status(rrs::launch_gemm(gc, s));
 }

@@ -508,7 +508,7 @@ __device__ __forceinline__ void quantise_block(const float (&v)[Cfg<LOG2K>::kE],
     packed[o] = pack8(mag, sgn);
   }
   if (row0 + rl < rows) {
-    uint8_t* dst = codes + static_cast<size_t>(row0 + rl) * (K / 2) + j0 / 2;
+    uint8_t* dst = codes + codes_offset(row0 + rl, j0 / 2, codes_row_stride(K));  // E / 2 bytes in one piece
 #pragma unroll
     for (int o = 0; o < E / 32; ++o)
       reinterpret_cast<uint4*>(dst)[o] = make_uint4(packed[4 * o], packed[4 * o + 1], packed[4 * o + 2], packed[4 * o + 3]);
@@ -1162,7 +1162,7 @@ __global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a
     }
     packed[o] = pack8(mag, sgn);
   }
-  uint8_t* dst = a.codes + static_cast<size_t>(row) * (K / 2) + p0 / 2;
+  uint8_t* dst = a.codes + codes_offset(row, p0 / 2, codes_row_stride(K));  // E / 2 bytes in one piece
   if constexpr (E == 16)
     *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
   else

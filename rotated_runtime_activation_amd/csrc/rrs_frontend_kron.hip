@@ -529,7 +529,7 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
         }
         r = block_max(r, s_red, tid);
         const float k7 = r > 0.f ? 7.f / r : 0.f;
-        uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + static_cast<size_t>(row) * (K / 2));
+        constexpr size_t rs = codes_row_stride(K);
 #pragma unroll
         for (int s = 0; s < SW; ++s) {
           const int w = tid + s * kKT;
@@ -541,7 +541,7 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
               mag[e] = __float_as_uint(fmaf(fabsf(z[s][e]), ks, kMagic));
               sgn[e] = __float_as_uint(z[s][e]);
             }
-            dst[w] = pack8(mag, sgn);
+            *reinterpret_cast<uint32_t*>(a.codes + codes_offset(row, 4 * w, rs)) = pack8(mag, sgn);
           }
         }
         if (tid == 0) a.scale[row] = gave_up ? __builtin_nanf("") : r / 7.f;
@@ -595,7 +595,7 @@ __global__ void __launch_bounds__(kKT) kron_quant_rows_kernel(KronArgs a, int K)
   }
   r = block_max(r, s_red, tid);
   const float k7 = r > 0.f ? 7.f / r : 0.f;
-  uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + static_cast<size_t>(row) * (K / 2));
+  const size_t rs = codes_row_stride(K);
 #pragma unroll
   for (int s = 0; s < SW; ++s) {
     const int w = tid + s * kKT;
@@ -607,7 +607,7 @@ __global__ void __launch_bounds__(kKT) kron_quant_rows_kernel(KronArgs a, int K)
         mag[e] = __float_as_uint(fmaf(fabsf(z[s][e]), ks, kMagic));
         sgn[e] = __float_as_uint(z[s][e]);
       }
-      dst[w] = pack8(mag, sgn);
+      *reinterpret_cast<uint32_t*>(a.codes + codes_offset(row, 4 * w, rs)) = pack8(mag, sgn);
     }
   }
   if (tid == 0) a.scale[row] = r / 7.f;

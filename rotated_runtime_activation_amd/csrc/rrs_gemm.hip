@@ -50,6 +50,7 @@ constexpr int kTN = 256;       // output channels per workgroup tile
 constexpr int kTT = 128;       // tokens per workgroup tile
 constexpr int kThreads = 256;  // 4 waves: 2 (n) x 2 (t), each 128 x 64
 constexpr int kRowB = 64;      // packed bytes per row per stage (128 codes)
+constexpr int kLineB = 128;    // stored bytes per row pair per stage (both rows' pieces)
 constexpr int kWB = kTN * kRowB;
 constexpr int kXB = kTT * kRowB;
 constexpr int kStageB = kWB + kXB;
@@ -231,7 +232,7 @@ struct GemmCtx {
     // result is a signed int: widen through uint32_t, never directly.
     const uint32_t lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
         static_cast<int>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)base)) + lblk[d])));
-    const uint64_t ra = reinterpret_cast<uint64_t>((wave6 + d < 16 ? wbase : xbase) + st * kRowB);
+    const uint64_t ra = reinterpret_cast<uint64_t>((wave6 + d < 16 ? wbase : xbase) + st * kLineB);
     const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(ra))));
     const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(ra >> 32))));
     const uint8_t* rows = reinterpret_cast<const uint8_t*>(static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
@@ -464,16 +465,20 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
   // weight rows, 16..23 the activation rows; wave w moves blocks 6w..6w+5.
   // Lane i fills 16-byte slot i of the block: row 16b + i / 4 of the
   // matrix (clamped to it; clamped rows only feed outputs that are never
-  // stored), 16-byte chunk (i & 3) ^ ((i >> 3) & 3) of that row. The XOR
-  // swizzle spreads the eight rows a fragment read serves at once over all
-  // 32 LDS banks (rows 64 bytes apart would otherwise hit the same banks
-  // every two rows). With K = 64 (one stage of 32 bytes per row) the
-  // chunks past the row's end re-read its first bytes: in bounds, and never
-  // multiplied (only K codes are used). Every other K is a multiple of 128.
-  // The tile's first rows (n0 < N, t0 < M) are the scalar bases; a lane's
-  // offset from them stays below 256 rows, so 32 bits hold it.
-  c.wbase = a.wq + static_cast<size_t>(c.n0) * c.Kb;
-  c.xbase = a.xq + static_cast<size_t>(c.t0) * c.Kb;
+  // stored), 16-byte chunk (i & 3) ^ ((i >> 3) & 3) of that row's stage
+  // piece. The XOR swizzle spreads the eight rows a fragment read serves at
+  // once over all 32 LDS banks (rows 64 bytes apart would otherwise hit the
+  // same banks every two rows). In the stored layout the stage pieces of
+  // rows 2p and 2p + 1 form one 128-byte line, so the eight lanes of a row
+  // pair load a whole line, and a stage advances by a line. With K = 64
+  // (one stage of 32 bytes per row) the chunks past the row's codes re-read
+  // its first bytes: in bounds, and never multiplied (only K codes are
+  // used). Every other K is a multiple of 128. The tile's first rows
+  // (n0 < N, t0 < M; both even) are the scalar bases; a lane's offset from
+  // them stays below 256 rows, so 32 bits hold it.
+  const size_t rs = codes_row_stride(a.K);  // tile bases: n0 and t0 are even rows
+  c.wbase = a.wq + static_cast<size_t>(c.n0) * rs;
+  c.xbase = a.xq + static_cast<size_t>(c.t0) * rs;
   c.wave6 = wave * GemmCtx<KM, PARTIALS, SPG>::kDmaPerWave;
 #pragma unroll
   for (int d = 0; d < GemmCtx<KM, PARTIALS, SPG>::kDmaPerWave; ++d) {
@@ -483,7 +488,8 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
     const int row = min(base_row + (blk & 15) * 16 + (c.lane >> 2), (wrows ? a.N : a.M) - 1);
     int goff = ((c.lane & 3) ^ ((c.lane >> 3) & 3)) * 16;
     if (goff >= c.Kb) goff &= 15;
-    c.voff[d] = static_cast<uint32_t>((row - base_row) * c.Kb + goff);
+    const int rt = row - base_row;  // stored layout: row pairs share each stage's 128-byte line
+    c.voff[d] = static_cast<uint32_t>(codes_offset(rt, goff, rs));
     c.lblk[d] = blk * 1024;
   }
 

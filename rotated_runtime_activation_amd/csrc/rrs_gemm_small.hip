@@ -49,6 +49,7 @@ constexpr int kTN = 32;      // output channels per workgroup
 constexpr int kSmallMaxTokens = 512;  // token count past which the tiled kernel always serves
 constexpr int kRound = 4;    // k-steps per round (128 bytes of a row)
 constexpr int kRows = 128;   // bytes of a row per round
+constexpr int kPairRound = 2 * kRows;  // stored bytes of a row pair per round (two stage lines)
 constexpr float kUnit = 262144.0f;  // 2^18: one integer product in accumulator units
 
 struct SmallArgs {
@@ -139,11 +140,11 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n0 = blockIdx.x * kTN;
-  const int Kb = a.K / 2;
   // this workgroup's token slice: rows t0 .. t0 + Mt - 1 of xq, dx and Y
   const int t0 = blockIdx.y * 64;
   const int Mt = min(64, a.M - t0);
-  const uint8_t* xq = a.xq + static_cast<size_t>(t0) * Kb;
+  const size_t rs = codes_row_stride(a.K);  // stored layout: row pairs, 64-byte pieces side by side
+  const uint8_t* xq = a.xq + static_cast<size_t>(t0) * rs;  // t0 is even
   const float* dx = a.dx + t0;
   float* Y = a.Y + static_cast<size_t>(t0) * a.N;
   const int ngroups = a.K >> a.log2G;
@@ -155,18 +156,22 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
   const int rounds = kpw / kRound;
 
   // coalesced load i of a round: row 8 i + lane / 8, chunk lane % 8 (rows
-  // clamped to the matrix; clamped rows feed outputs that are never stored)
+  // clamped to the matrix; clamped rows feed outputs that are never stored).
+  // In the stored layout a row pair's round is 256 contiguous bytes (the
+  // pair's two stage lines), so each load moves four whole 256-byte runs.
   const int lr = lane >> 3, lc = lane & 7;
   // (a wave-uniform base per operand plus a 32-bit offset per lane and
   // load: one register per load stream instead of a 64-bit pointer)
-  const uint8_t* wbase = a.wq + static_cast<size_t>(n0) * Kb + ks0 * 32;
-  const uint8_t* xbase = xq + ks0 * 32;
+  // the wave's first k-step ks0 starts piece ks0 / 2 of every row (ks0 is
+  // a multiple of a round, so even)
+  const uint8_t* wbase = a.wq + static_cast<size_t>(n0) * rs + (ks0 / 2) * 128;  // n0 is even
+  const uint8_t* xbase = xq + (ks0 / 2) * 128;
   uint32_t woff[kWL], xoff[kXL];
 #pragma unroll
   for (int i = 0; i < kWL; ++i)
-    woff[i] = static_cast<uint32_t>((min(n0 + 8 * i + lr, a.N - 1) - n0) * Kb + lc * 16);
+    woff[i] = static_cast<uint32_t>(codes_offset(min(n0 + 8 * i + lr, a.N - 1) - n0, lc * 16, rs));
 #pragma unroll
-  for (int i = 0; i < kXL; ++i) xoff[i] = static_cast<uint32_t>(min(8 * i + lr, Mt - 1) * Kb + lc * 16);
+  for (int i = 0; i < kXL; ++i) xoff[i] = static_cast<uint32_t>(codes_offset(min(8 * i + lr, Mt - 1), lc * 16, rs));
 
   uint8_t* buf = s_buf[wave];
   v4u rw[NR][kWL], rx[NR][kXL];
@@ -210,7 +215,7 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
   }
 #pragma unroll
   for (int s = 0; s < NR; ++s) {
-    const int off = min(s, rounds - 1) * kRows;
+    const int off = min(s, rounds - 1) * kPairRound;
 #pragma unroll
     for (int i = 0; i < kWL; ++i) rw[s][i] = *reinterpret_cast<const v4u*>(wbase + off + woff[i]);
 #pragma unroll
@@ -263,7 +268,7 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       // refill the slot with the round NR ahead
       if (!kPeel || pass == 0) {
-        const int off = min(r + NR, rounds - 1) * kRows;
+        const int off = min(r + NR, rounds - 1) * kPairRound;
 #pragma unroll
         for (int i = 0; i < kWL; ++i) rw[s][i] = *reinterpret_cast<const v4u*>(wbase + off + woff[i]);
 #pragma unroll

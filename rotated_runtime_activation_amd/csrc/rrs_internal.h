@@ -44,6 +44,22 @@ constexpr int kFlagGiveUp = 8;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Stored layout of a matrix of packed codes (the activation codes xq and the
+// prepared weight codes): rows in pairs, each row's K/2 bytes cut into
+// 64-byte pieces (128 codes, one tiled-GEMM stage), piece c of rows 2p and
+// 2p + 1 side by side in one 128-byte line. Byte b of row r lies at
+//   (r / 2) * 2 rs + (b / 64) * 128 + (r % 2) * 64 + b % 64,
+// with rs = K/2 rounded up to 64 (K = 64 uses 32 bytes of each piece). A
+// stage of a tile's rows then reads whole lines; with one row per line half
+// of every line it fetched went unused until the next stage.
+__host__ __device__ constexpr size_t codes_row_stride(int K) { return (static_cast<size_t>(K / 2) + 63) & ~size_t(63); }
+__host__ __device__ constexpr size_t codes_bytes(size_t rows, int K) {
+  return ((rows + 1) / 2) * 2 * codes_row_stride(K);
+}
+__host__ __device__ inline size_t codes_offset(size_t r, size_t b, size_t rs) {
+  return (r >> 1) * 2 * rs + ((b >> 6) << 7) + ((r & 1) << 6) + (b & 63);
+}
+
 // Front end (activation rows): one launch when its workgroups all fit on
 // the device at once, else a stats pass, a reduce and a quantise pass.
 //   flags: bit0 = skip rotation, bit1 = skip smoothing (S = 1),

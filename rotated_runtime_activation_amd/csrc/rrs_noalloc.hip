@@ -60,7 +60,7 @@ RRS_API int rrs_linear_noalloc(const void* X_fp16, int M, int K, int N, int G, c
   // sync | xq | dx | S, as rrs_linear's workspace (no Kronecker row area:
   // for K = m 2^k the three-launch front end rotates every row twice)
   const size_t xq_off = sync;
-  const size_t dx_off = xq_off + rrs::align256(static_cast<size_t>(M) * (K / 2));
+  const size_t dx_off = xq_off + rrs::align256(rrs::codes_bytes(static_cast<size_t>(M), K));
   const size_t S_off = dx_off + rrs::align256(sizeof(float) * static_cast<size_t>(M));
   const size_t total = S_off + rrs::align256(sizeof(float) * static_cast<size_t>(K / G));
   if (total > kScratchBytes) return RRS_ETOOBIG;
@@ -74,7 +74,7 @@ RRS_API int rrs_linear_noalloc(const void* X_fp16, int M, int K, int N, int G, c
                            nullptr) != hipSuccess)
     return RRS_EHIP;
   const uint8_t* codes = static_cast<const uint8_t*>(wq);
-  const float* dw = reinterpret_cast<const float*>(codes + rrs::align256(static_cast<size_t>(N) * (K / 2)));
+  const float* dw = reinterpret_cast<const float*>(codes + rrs::align256(rrs::codes_bytes(static_cast<size_t>(N), K)));
   const rrs::GemmCall gc{xq, dx, S, M, K, N, G, codes, dw, Y, nullptr, 0, 0, 0, 0, true, sw + rrs::kSyncError};
   return rrs::launch_gemm(gc, s) == hipSuccess ? RRS_OK : RRS_EHIP;
 }

@@ -67,26 +67,44 @@ def prepare_weights(w: np.ndarray, perm: np.ndarray):
 
 def weight_buffer_from_codes(qw_packed: np.ndarray, dw: np.ndarray) -> torch.Tensor:
     """Opaque prepared-weight buffer holding the given packed codes [N, K/2]
-    and scales [N] (the layout include/rrs.h documents)."""
+    (row-major; stored in the layout include/rrs.h documents) and scales
+    [N]."""
     N, Kh = qw_packed.shape
-    buf = torch.zeros(rra.rrs_weight_bytes(2 * Kh, N), dtype=torch.uint8, device=DEV)
-    codes, dwv = rra.weight_views(buf, 2 * Kh, N)
-    codes.copy_(to_dev(qw_packed))
+    K = 2 * Kh
+    buf = torch.zeros(rra.rrs_weight_bytes(K, N), dtype=torch.uint8, device=DEV)
+    rra.codes_buffer(to_dev(qw_packed), K, out=rra.weight_codes_region(buf, K, N))
+    _, dwv = rra.weight_views(buf, K, N)
     dwv.copy_(to_dev(dw.astype(np.float32)))
     return buf
+
+
+def xq_buffer(q_packed: np.ndarray) -> torch.Tensor:
+    """Activation-code buffer (stored layout) holding the row-major packed
+    codes [M, K/2]."""
+    return rra.codes_buffer(to_dev(q_packed), 2 * q_packed.shape[1])
+
+
+def xq_empty(M: int, K: int) -> torch.Tensor:
+    """An uninitialised activation-code buffer for M tokens of length K."""
+    return torch.empty(rra.rrs_codes_bytes(M, K), dtype=torch.uint8, device=DEV)
+
+
+def xq_codes(xq: torch.Tensor, M: int, K: int) -> np.ndarray:
+    """The row-major packed codes [M, K/2] held in an activation-code buffer."""
+    return rra.codes_matrix(xq, M, K).cpu().numpy()
 
 
 def frontend(x: np.ndarray, perm: np.ndarray, G: int, flags: int = 0):
     M, K = x.shape
     X = to_dev(x)
-    xq = torch.empty(M, K // 2, dtype=torch.uint8, device=DEV)
+    xq = xq_empty(M, K)
     dx = torch.empty(M, dtype=torch.float32, device=DEV)
     S = torch.empty(K // G, dtype=torch.float32, device=DEV)
     ws = torch.zeros(rra.rrs_sync_bytes(K, G), dtype=torch.uint8, device=DEV)
     rra.rrs_frontend(X, G, to_dev(perm), xq, dx, S, ws, flags)
     torch.cuda.synchronize()
     check_sync_block(ws, K, G)
-    return xq.cpu().numpy(), dx.cpu().numpy(), S.cpu().numpy()
+    return xq_codes(xq, M, K), dx.cpu().numpy(), S.cpu().numpy()
 
 
 def check_sync_block(ws, K: int, G: int, calls: int = 1):

@@ -131,9 +131,9 @@ def test_kron_shapes_accepted_and_rejected():
     # layout sync | xq | dx | S | rows: a Kronecker K adds the M x K fp32 row area
     a = lambda n: (n + 255) // 256 * 256
     M, K, G = 2048, 14336, 128
-    base = rra.rrs_sync_bytes(K, G) + a(M * K // 2) + a(4 * M) + a(4 * K // G)
+    base = rra.rrs_sync_bytes(K, G) + a(rra.rrs_codes_bytes(M, K)) + a(4 * M) + a(4 * K // G)
     assert rra.rrs_workspace_bytes(M, K, G) == base + a(4 * M * K)
-    assert rra.rrs_workspace_bytes(3, 768, 64) == rra.rrs_sync_bytes(768, 64) + a(3 * 384) + 256 + 256 + a(4 * 3 * 768)
+    assert rra.rrs_workspace_bytes(3, 768, 64) == rra.rrs_sync_bytes(768, 64) + a(2 * 2 * 384) + 256 + 256 + a(4 * 3 * 768)
     assert rra.rrs_gemm_form(8, 14336, 4096, 128) == rra.RRS_GEMM_FEW_TOKENS
     assert rra.rrs_gemm_form(8, 14336, 4096, 2048) == rra.RRS_GEMM_TILED
     assert rra.rrs_frontend_passes(8, 14336, 0) == 3
@@ -282,3 +282,31 @@ def test_noalloc_rejects_on_host():
                                 NULL) == rra.RRS_EINVAL
     assert L.rrs_linear_noalloc(DUMMY, 12167, 4096, 64, 128, DUMMY, DUMMY, DUMMY, NULL) == rra.RRS_ETOOBIG
     assert L.rrs_linear_noalloc(NULL, 0, 4096, 64, 128, DUMMY, DUMMY, NULL, NULL) == rra.RRS_OK
+
+
+def test_code_layout_sizes_and_helpers():
+    """The stored code layout (row pairs, 64-byte pieces side by side): its
+    size query, and the binding's reading and writing helpers against the
+    byte-offset formula the header states."""
+    import numpy as np
+    import torch
+    assert rra.rrs_codes_bytes(4, 4096) == 4 * 2048
+    assert rra.rrs_codes_bytes(3, 4096) == 4 * 2048     # an odd row count rounds up to a pair
+    assert rra.rrs_codes_bytes(5, 64) == 3 * 2 * 64     # K = 64: 32 of each 64-byte piece used
+    assert rra.rrs_codes_bytes(1, 14336) == 2 * 7168
+    assert rra.rrs_codes_bytes(4, 100) == 0 and rra.rrs_codes_bytes(-1, 256) == 0
+    assert rra.rrs_weight_bytes(256, 3) == 512 + 256 and rra.rrs_weight_bytes(64, 5) == 512 + 256  # 384 code bytes, 256-aligned
+
+    def off(r, b, rs):
+        return (r // 2) * 2 * rs + (b // 64) * 128 + (r % 2) * 64 + b % 64
+
+    for rows, K in [(5, 64), (6, 128), (7, 1024), (3, 1792), (4, 4096)]:
+        kb = K // 2
+        rs = (kb + 63) // 64 * 64
+        codes = torch.from_numpy(np.random.default_rng(rows + K).integers(0, 256, (rows, kb), dtype=np.uint8))
+        buf = rra.codes_buffer(codes, K)
+        assert buf.numel() == rra.rrs_codes_bytes(rows, K)
+        b = buf.numpy()
+        idx = np.array([[off(r, c, rs) for c in range(kb)] for r in range(rows)])
+        assert np.array_equal(b[idx], codes.numpy())
+        assert torch.equal(rra.codes_matrix(buf, rows, K), codes)

@@ -135,13 +135,13 @@ def test_wait_give_up_is_visible(M, K, G):
     wq = gu.prepare_weights(w, perm)
     ws = torch.zeros(rra.rrs_workspace_bytes(M, K, G), dtype=torch.uint8, device=gu.DEV)
     rra.rrs_workspace_init(ws)
-    xq, dx, S = rra.workspace_views(ws, M, K, G)
+    _, dx, S = rra.workspace_regions(ws, M, K, G)
     Y = torch.empty(M, N, dtype=torch.float32, device=gu.DEV)
 
     # the front end alone: error word, NaN scales
     sync = torch.zeros(rra.rrs_sync_bytes(K, G), dtype=torch.uint8, device=gu.DEV)
     rra.rrs_workspace_init(sync)
-    xq1 = torch.empty(M, K // 2, dtype=torch.uint8, device=gu.DEV)
+    xq1 = gu.xq_empty(M, K)
     dx1 = torch.empty(M, dtype=torch.float32, device=gu.DEV)
     S1 = torch.empty(K // G, dtype=torch.float32, device=gu.DEV)
     rra.rrs_frontend(X, G, P, xq1, dx1, S1, sync, GU)
@@ -163,7 +163,7 @@ def test_wait_give_up_is_visible(M, K, G):
     torch.cuda.synchronize()
     assert ws[8:12].view(torch.int32).item() == 0
     ref = oracle.rrs_linear(x, w, perm, G)
-    q_gpu = oracle.unpack_codes(xq.cpu().numpy())
+    q_gpu = oracle.unpack_codes(rra.workspace_views(ws, M, K, G)[0].cpu().numpy())
     gu.compare_codes(q_gpu, ref["fe"]["q"], ref["fe"]["v"], "codes after init")
     codes, dw = rra.weight_views(wq, K, N)
     gu.check_linear_two_way(Y.cpu().numpy(), ref, q_gpu, oracle.unpack_codes(codes.cpu().numpy()),

@@ -50,13 +50,13 @@ def test_frontend_kron_signed(M, K, G):
     bits = np.random.default_rng(K).integers(0, 2**32, size=K // 32, dtype=np.uint64).astype(np.uint32)
     d = oracle.signs_from_bits(bits, K)
     fe = oracle.frontend(x, perm, G, d=d)
-    xq = torch.empty(M, K // 2, dtype=torch.uint8, device=gu.DEV)
+    xq = gu.xq_empty(M, K)
     dx = torch.empty(M, dtype=torch.float32, device=gu.DEV)
     S = torch.empty(K // G, dtype=torch.float32, device=gu.DEV)
     ws = torch.zeros(rra.rrs_sync_bytes(K, G), dtype=torch.uint8, device=gu.DEV)
     rra.rrs_frontend_signed(gu.to_dev(x), G, gu.to_dev(perm), gu.to_dev(bits.view(np.int32)), xq, dx, S, ws)
     torch.cuda.synchronize()
-    gu.compare_codes(oracle.unpack_codes(xq.cpu().numpy()), fe["q"], fe["v"], "kron signed codes")
+    gu.compare_codes(oracle.unpack_codes(gu.xq_codes(xq, M, K)), fe["q"], fe["v"], "kron signed codes")
     gu.rel_close(dx.cpu().numpy(), fe["dx"], gu.SCALE_TOL, "kron signed dx")
     gu.rel_close(S.cpu().numpy(), fe["S"], gu.SCALE_TOL, "kron signed S")
 
@@ -107,13 +107,13 @@ def test_gemm_kron(M, N, K, G):
     dx = (g.random(M) + 0.1).astype(np.float32)
     dw = (g.random(N) * 0.01 + 1e-3).astype(np.float32)
     S = (g.random(K // G) * 100 + 1).astype(np.float32)
-    xq = gu.to_dev(oracle.pack_codes(q))
+    xq = gu.xq_buffer(oracle.pack_codes(q))
     wq = gu.weight_buffer_from_codes(oracle.pack_codes(qw), dw)
     ref = oracle.linear_out(q, dx.astype(np.float64), S.astype(np.float64), qw, dw.astype(np.float64), G)
     Y = torch.empty(M, N, dtype=torch.float32, device=gu.DEV)
     rra.rrs_gemm(xq, gu.to_dev(dx), gu.to_dev(S), G, wq, Y)
     P = torch.empty(M, N, K // G, dtype=torch.int32, device=gu.DEV)
-    rra.rrs_gemm_partials(xq, N, G, wq, 0, M, 0, N, P)
+    rra.rrs_gemm_partials(xq, M, K, N, G, wq, 0, M, 0, N, P)
     torch.cuda.synchronize()
     assert np.array_equal(P.cpu().numpy(), oracle.group_partials(q, qw, G))
     err = gu.y_error(Y.cpu().numpy(), ref)
@@ -169,7 +169,7 @@ def test_frontend_kron_row_area(M, K, G, signed):
         torch.cuda.synchronize()
 
     # rotate twice: a workspace of the synchronisation block alone
-    xq_a = torch.empty(M, K // 2, dtype=torch.uint8, device=gu.DEV)
+    xq_a = gu.xq_empty(M, K)
     dx_a = torch.empty(M, dtype=torch.float32, device=gu.DEV)
     S_a = torch.empty(K // G, dtype=torch.float32, device=gu.DEV)
     ws_a = torch.zeros(rra.rrs_sync_bytes(K, G), dtype=torch.uint8, device=gu.DEV)
@@ -178,17 +178,18 @@ def test_frontend_kron_row_area(M, K, G, signed):
     # stored rows: a whole rrs_linear workspace, outputs in its own views
     nbytes = rra.rrs_workspace_bytes(M, K, G)
     ws_b = torch.zeros(nbytes, dtype=torch.uint8, device=gu.DEV)
-    xq_b, dx_b, S_b = rra.workspace_views(ws_b, M, K, G)
+    xq_b, dx_b, S_b = rra.workspace_regions(ws_b, M, K, G)
     run(xq_b, dx_b, S_b, ws_b)
     row_off = nbytes - (4 * M * K + 255) // 256 * 256
     rows = ws_b[row_off:].view(torch.float32).view(M, K).cpu().numpy().astype(np.float64)
 
-    assert torch.equal(xq_a, xq_b), "codes differ between the two forms"
+    codes_a = rra.codes_matrix(xq_a, M, K)
+    assert torch.equal(codes_a, rra.codes_matrix(xq_b, M, K)), "codes differ between the two forms"
     assert torch.equal(dx_a.view(torch.int32), dx_b.view(torch.int32)), "dx differs between the two forms"
     assert torch.equal(S_a.view(torch.int32), S_b.view(torch.int32)), "S differs between the two forms"
 
     fe = oracle.frontend(x, perm, G, d=oracle.signs_from_bits(dsign_np, K)) if signed else oracle.frontend(x, perm, G)
-    gu.compare_codes(oracle.unpack_codes(xq_b.cpu().numpy()), fe["q"], fe["v"], "kron rows codes")
+    gu.compare_codes(oracle.unpack_codes(gu.xq_codes(xq_b, M, K)), fe["q"], fe["v"], "kron rows codes")
     gu.rel_close(dx_b.cpu().numpy(), fe["dx"], gu.SCALE_TOL, "kron rows dx")
     gu.rel_close(S_b.cpu().numpy(), fe["S"], gu.SCALE_TOL, "kron rows S")
     scale = np.maximum(np.abs(fe["Zp"]).max(axis=1, keepdims=True), 1e-30)
@@ -198,18 +199,18 @@ def test_frontend_kron_row_area(M, K, G, signed):
 
     # xq inside the row area: the library must not keep rows there
     ws_c = torch.zeros(nbytes, dtype=torch.uint8, device=gu.DEV)
-    xq_c = ws_c[row_off: row_off + M * (K // 2)].view(M, K // 2)
+    xq_c = ws_c[row_off: row_off + rra.rrs_codes_bytes(M, K)]
     dx_c = torch.empty(M, dtype=torch.float32, device=gu.DEV)
     S_c = torch.empty(K // G, dtype=torch.float32, device=gu.DEV)
     run(xq_c, dx_c, S_c, ws_c)
-    assert torch.equal(xq_a, xq_c) and torch.equal(dx_a, dx_c) and torch.equal(S_a, S_c)
+    assert torch.equal(codes_a, rra.codes_matrix(xq_c, M, K)) and torch.equal(dx_a, dx_c) and torch.equal(S_a, S_c)
 
     # the default form (one launch for up to one row per CU): the same bits
     ws_d = torch.zeros(nbytes, dtype=torch.uint8, device=gu.DEV)
-    xq_d, dx_d, S_d = rra.workspace_views(ws_d, M, K, G)
+    xq_d, dx_d, S_d = rra.workspace_regions(ws_d, M, K, G)
     gu.log(f"  default form: {rra.rrs_frontend_passes(M, K, 0)} launch(es)")
     run(xq_d, dx_d, S_d, ws_d, 0)
-    assert torch.equal(xq_a, xq_d) and torch.equal(dx_a, dx_d) and torch.equal(S_a, S_d)
+    assert torch.equal(codes_a, rra.codes_matrix(xq_d, M, K)) and torch.equal(dx_a, dx_d) and torch.equal(S_a, S_d)
     gu.check_sync_block(ws_d, K, G)
 
 
@@ -226,13 +227,13 @@ def test_frontend_kron_workspace_reuse():
         gu.log(f"[kron workspace reuse] M={M} flags={flags}: {passes} launch(es)")
         x, _, perm = _case(M, K)
         fe = oracle.frontend(x, perm, G)
-        xq = torch.empty(M, K // 2, dtype=torch.uint8, device=gu.DEV)
+        xq = gu.xq_empty(M, K)
         dx = torch.empty(M, dtype=torch.float32, device=gu.DEV)
         S = torch.empty(K // G, dtype=torch.float32, device=gu.DEV)
         rra.rrs_frontend(gu.to_dev(x), G, gu.to_dev(perm), xq, dx, S, ws, flags)
         torch.cuda.synchronize()
         one += passes == 1
-        gu.compare_codes(oracle.unpack_codes(xq.cpu().numpy()), fe["q"], fe["v"], "kron reuse codes")
+        gu.compare_codes(oracle.unpack_codes(gu.xq_codes(xq, M, K)), fe["q"], fe["v"], "kron reuse codes")
         gu.rel_close(dx.cpu().numpy(), fe["dx"], gu.SCALE_TOL, "kron reuse dx")
         gu.rel_close(S.cpu().numpy(), fe["S"], gu.SCALE_TOL, "kron reuse S")
         words = ws.view(torch.int32).cpu().numpy()

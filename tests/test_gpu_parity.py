@@ -79,7 +79,7 @@ def test_frontend_rows_workspace_reuse():
         gu.log(f"[rows workspace reuse] M={M} flags={flags}")
         x, _, perm = _case(M, K)
         fe = oracle.frontend(x, perm, G, smooth=not (flags & 2))
-        xq = torch.empty(M, K // 2, dtype=torch.uint8, device=gu.DEV)
+        xq = gu.xq_empty(M, K)
         dx = torch.empty(M, dtype=torch.float32, device=gu.DEV)
         S = torch.empty(K // G, dtype=torch.float32, device=gu.DEV)
         rra.rrs_frontend(gu.to_dev(x), G, gu.to_dev(perm), xq, dx, S, ws, flags)
@@ -87,7 +87,7 @@ def test_frontend_rows_workspace_reuse():
         if not flags and rra.rrs_frontend_passes(M, K, 0) == 1:
             calls += 1
         gu.check_sync_block(ws, K, G, calls)
-        gu.compare_codes(oracle.unpack_codes(xq.cpu().numpy()), fe["q"], fe["v"], "rows reuse codes")
+        gu.compare_codes(oracle.unpack_codes(gu.xq_codes(xq, M, K)), fe["q"], fe["v"], "rows reuse codes")
         gu.rel_close(S.cpu().numpy(), fe["S"], gu.SCALE_TOL, "rows reuse S")
 
 
@@ -219,12 +219,12 @@ def test_gemm_partials_exact(M, N, K, G):
     it would be rescaled): its partials must equal the int64 brute force."""
     gu.log(f"[gemm partials] M={M} N={N} K={K} G={G} form={rra.rrs_gemm_form(M, K, N, G)}")
     q, qw = _random_codes(M + N + K, M, N, K)
-    xq = gu.to_dev(oracle.pack_codes(q))
+    xq = gu.xq_buffer(oracle.pack_codes(q))
     wq = gu.weight_buffer_from_codes(oracle.pack_codes(qw), np.ones(N))
     ref = oracle.group_partials(q, qw, G)
     for (m0, m1, n0, n1) in {(0, M, 0, N), (M // 2, M, N // 3, N), (M - 1, M, N - 1, N)}:
         P = torch.empty(m1 - m0, n1 - n0, K // G, dtype=torch.int32, device=gu.DEV)
-        rra.rrs_gemm_partials(xq, N, G, wq, m0, m1, n0, n1, P)
+        rra.rrs_gemm_partials(xq, M, K, N, G, wq, m0, m1, n0, n1, P)
         torch.cuda.synchronize()
         got = P.cpu().numpy()
         assert np.array_equal(got, ref[m0:m1, n0:n1]), \
@@ -241,7 +241,7 @@ def test_gemm_output(M, N, K, G):
     S = (g.random(K // G) * 100 + 1).astype(np.float32)
     ref = oracle.linear_out(q, dx.astype(np.float64), S.astype(np.float64), qw, dw.astype(np.float64), G)
     Y = torch.empty(M, N, dtype=torch.float32, device=gu.DEV)
-    rra.rrs_gemm(gu.to_dev(oracle.pack_codes(q)), gu.to_dev(dx), gu.to_dev(S), G,
+    rra.rrs_gemm(gu.xq_buffer(oracle.pack_codes(q)), gu.to_dev(dx), gu.to_dev(S), G,
                  gu.weight_buffer_from_codes(oracle.pack_codes(qw), dw), Y)
     torch.cuda.synchronize()
     err = gu.y_error(Y.cpu().numpy(), ref)
@@ -278,7 +278,7 @@ def test_gemm_exact_through_product_kernels(M, N, K, G):
     ng = K // G
     S = np.array([2.0 ** ((3 * g + M) % 4) for g in range(ng)], dtype=np.float32)
     Y = torch.empty(M, N, dtype=torch.float32, device=gu.DEV)
-    rra.rrs_gemm(gu.to_dev(oracle.pack_codes(q)), gu.to_dev(np.ones(M, np.float32)), gu.to_dev(S), G,
+    rra.rrs_gemm(gu.xq_buffer(oracle.pack_codes(q)), gu.to_dev(np.ones(M, np.float32)), gu.to_dev(S), G,
                  gu.weight_buffer_from_codes(oracle.pack_codes(qw), np.ones(N)), Y)
     torch.cuda.synchronize()
     total = (oracle.group_partials(q, qw, G) * S.astype(np.int64)[None, None, :]).sum(axis=2)
@@ -346,7 +346,7 @@ def test_frontend_workspace_reuse_across_sizes():
         gu.log(f"[workspace reuse] M={M} flags={flags}")
         x, _, perm = _case(M, K)
         fe = oracle.frontend(x, perm, G, smooth=not (flags & 2))
-        xq = torch.empty(M, K // 2, dtype=torch.uint8, device=gu.DEV)
+        xq = gu.xq_empty(M, K)
         dx = torch.empty(M, dtype=torch.float32, device=gu.DEV)
         S = torch.empty(K // G, dtype=torch.float32, device=gu.DEV)
         rra.rrs_frontend(gu.to_dev(x), G, gu.to_dev(perm), xq, dx, S, ws, flags)
@@ -354,7 +354,7 @@ def test_frontend_workspace_reuse_across_sizes():
         if not flags and rra.rrs_frontend_passes(M, K, 0) == 1:
             calls += 1
         gu.check_sync_block(ws, K, G, calls)
-        gu.compare_codes(oracle.unpack_codes(xq.cpu().numpy()), fe["q"], fe["v"], "reuse codes")
+        gu.compare_codes(oracle.unpack_codes(gu.xq_codes(xq, M, K)), fe["q"], fe["v"], "reuse codes")
         gu.rel_close(S.cpu().numpy(), fe["S"], gu.SCALE_TOL, "reuse S")
 
 

@@ -38,14 +38,14 @@ def test_frontend_signed(M, K, G, form):
     gu.log(f"[frontend signed] M={M} K={K} G={G} {form}")
     x, _, perm, bits, d = _case(M, K)
     fe = oracle.frontend(x, perm, G, d=d)
-    xq = torch.empty(M, K // 2, dtype=torch.uint8, device=gu.DEV)
+    xq = gu.xq_empty(M, K)
     dx = torch.empty(M, dtype=torch.float32, device=gu.DEV)
     S = torch.empty(K // G, dtype=torch.float32, device=gu.DEV)
     ws = torch.zeros(rra.rrs_sync_bytes(K, G), dtype=torch.uint8, device=gu.DEV)
     rra.rrs_frontend_signed(gu.to_dev(x), G, gu.to_dev(perm), _dev_bits(bits), xq, dx, S, ws, flags)
     torch.cuda.synchronize()
     gu.check_sync_block(ws, K, G)
-    gu.compare_codes(oracle.unpack_codes(xq.cpu().numpy()), fe["q"], fe["v"], "signed codes")
+    gu.compare_codes(oracle.unpack_codes(gu.xq_codes(xq, M, K)), fe["q"], fe["v"], "signed codes")
     gu.rel_close(dx.cpu().numpy(), fe["dx"], gu.SCALE_TOL, "signed dx")
     gu.rel_close(S.cpu().numpy(), fe["S"], gu.SCALE_TOL, "signed S")
 
@@ -58,7 +58,7 @@ def test_frontend_signed_all_plus_matches_plain():
     zero = torch.zeros(K // 32, dtype=torch.int32, device=gu.DEV)
     outs = []
     for signed in (False, True):
-        xq = torch.empty(M, K // 2, dtype=torch.uint8, device=gu.DEV)
+        xq = gu.xq_empty(M, K)
         dx = torch.empty(M, dtype=torch.float32, device=gu.DEV)
         S = torch.empty(K // G, dtype=torch.float32, device=gu.DEV)
         ws = torch.zeros(rra.rrs_sync_bytes(K, G), dtype=torch.uint8, device=gu.DEV)
@@ -66,7 +66,7 @@ def test_frontend_signed_all_plus_matches_plain():
             rra.rrs_frontend_signed(gu.to_dev(x), G, gu.to_dev(perm), zero, xq, dx, S, ws)
         else:
             rra.rrs_frontend(gu.to_dev(x), G, gu.to_dev(perm), xq, dx, S, ws)
-        outs.append((xq, dx, S))
+        outs.append((rra.codes_matrix(xq, M, K), dx, S))
     torch.cuda.synchronize()
     for a, b in zip(*outs):
         assert torch.equal(a, b)
