@@ -437,14 +437,16 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
 
   // XCD-aware tile order: consecutive workgroup ids land on different XCDs,
   // so give each XCD a contiguous run of the tile sequence; inside bands of
-  // 8 output tiles the token tile runs fastest (neighbours share weights).
+  // 4 output tiles the token tile runs fastest (neighbours share weights).
+  // At M = 2048, N = 4096 an XCD's 32 tiles are then 4 weight tiles x 8
+  // token tiles (4 MiB of codes, its L2's size) rather than 8 x 4 (5 MiB).
   const int ntiles = a.tiles_t * a.tiles_n;
   int wg = blockIdx.x;
   if ((ntiles & 7) == 0) wg = (wg & 7) * (ntiles >> 3) + (wg >> 3);
-  const int band = 8 * a.tiles_t;
+  const int band = 4 * a.tiles_t;
   const int bi = wg / band, bo = wg % band;
-  const int bn = min(8, a.tiles_n - bi * 8);
-  c.n0 = (bi * 8 + bo % bn) * kTN;
+  const int bn = min(4, a.tiles_n - bi * 4);
+  c.n0 = (bi * 4 + bo % bn) * kTN;
   c.t0 = (bo / bn) * kTT;
 
   c.Kb = a.K / 2;
