@@ -268,14 +268,27 @@ struct GemmCtx {
       // is multiplied just before its first product of the group: its
       // previous product was issued a full row of blocks earlier and has
       // retired, so neither the multiplies nor the matrix core wait on each
-      // other. Otherwise (G > 128, one group over several stages) the whole
-      // accumulator is scaled at the group's first k-step.
-      if constexpr (SPG > 0) {
+      // other. When a group is one stage (two k-steps), that would put all
+      // of the rescale in the first k-step (200 vector instructions against
+      // 72 in the second, for 8 matrix instructions each), so the first
+      // half of the rows is rescaled at the end of the previous group
+      // instead, two rows after its last product (same value, same
+      // rounding). Otherwise (G > 128, one group over several stages) the
+      // whole accumulator is scaled at the group's first k-step.
+      if constexpr (SPG == 2 && Mm::kSteps == 2 && !PARTIALS) {
+        if (ks == 0) {
+          const float r = step > st0 * Mm::kSteps ? rat[step >> log2spg] : 1.f;
+          products<kLateHalf>(stage, next, koff, fx, r, ks, nst);
+        } else {  // the next group's ratio, if the next stage is this set's
+          const float r = st + 1 < st1 ? rat[(step + 1) >> log2spg] : 1.f;
+          products<kEarlyHalf>(stage, next, koff, fx, r, ks, nst);
+        }
+      } else if constexpr (SPG > 0) {
         if (ks % SPG == 0) {  // folds: ks is an unrolled index
           const float r = step > st0 * Mm::kSteps ? (PARTIALS ? 0.f : rat[step >> log2spg]) : 1.f;
-          products<true>(stage, next, koff, fx, r, ks, nst);
+          products<kAll>(stage, next, koff, fx, r, ks, nst);
         } else {
-          products<false>(stage, next, koff, fx, 1.f, ks, nst);
+          products<kNone>(stage, next, koff, fx, 1.f, ks, nst);
         }
       } else {
         if (gs == 0 && step > st0 * Mm::kSteps) {
@@ -284,7 +297,7 @@ struct GemmCtx {
 #pragma unroll
             for (int j = 0; j < TJ; ++j) acc[i][j] = PARTIALS ? Mm::zero() : acc[i][j] * rat[step >> log2spg];
         }
-        products<false>(stage, next, koff, fx, 1.f, ks, nst);
+        products<kNone>(stage, next, koff, fx, 1.f, ks, nst);
       }
       // a group that ends inside this set (with one group over all of K the
       // two sets' integer halves are added first; the epilogue dumps them)
@@ -292,17 +305,28 @@ struct GemmCtx {
     }
   }
 
-  // The products of one k-step; RS: multiply each accumulator block by r
-  // right before its product. One DMA block of the next stage goes out after
-  // each row of products.
-  template <bool RS>
+  // Where a k-step multiplies accumulator blocks by r: kNone nowhere; kAll
+  // every block right before its product; kLateHalf the second half of the
+  // rows right before their products; kEarlyHalf the first half of the
+  // rows, row i - TI/2 after the products of row i (its own products were
+  // issued two rows earlier and have retired).
+  enum Rescale { kNone, kAll, kLateHalf, kEarlyHalf };
+
+  // The products of one k-step. One DMA block of the next stage goes out
+  // after each row of products.
+  template <int RS>
   __device__ __forceinline__ void products(const uint8_t* stage, uint8_t* next, int koff,
                                            const typename Mm::frag (&fx)[TJ], float r, int ks, int nst) {
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const typename Mm::frag fw = Mm::load(stage + fW + i * Mm::BR * kRowB + koff);
+      const bool pre = RS == kAll || (RS == kLateHalf && i >= TI / 2);
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) acc[i][j] = Mm::mma(fw, fx[j], RS ? acc[i][j] * r : acc[i][j]);
+      for (int j = 0; j < TJ; ++j) acc[i][j] = Mm::mma(fw, fx[j], pre ? acc[i][j] * r : acc[i][j]);
+      if (RS == kEarlyHalf && i >= TI / 2) {
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i - TI / 2][j] = acc[i - TI / 2][j] * r;
+      }
       const int d = ks * TI + i;
       if (d < kDmaPerWave) issue_one(next, nst, d);
     }
