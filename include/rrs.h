@@ -175,7 +175,11 @@ int rrs_prepare_weights_ex(const void* W_fp16, int K, int N,
  * `ws` holds rrs_workspace_bytes(M, K, G) bytes, initialised once with
  * rrs_workspace_init. Y is fully overwritten. Runs the front end (rotation,
  * reorder, runtime group smoothing, per-token quantise and pack) and the
- * grouped integer GEMM on `s`. */
+ * grouped integer GEMM on `s`. With few tokens (the front end's
+ * one-row-per-workgroup form and the few-token GEMM) the front end's launch
+ * also reads most of wq's codes once, on compute units the rows leave idle,
+ * so that the GEMM finds them in the memory-side cache; it writes nothing
+ * there, and Y is the same bits as rrs_frontend followed by rrs_gemm. */
 int rrs_linear(const void* X_fp16, int M, int K, int N, int G,
                const int32_t* perm, const void* wq, float* Y, void* ws,
                size_t ws_bytes, hipStream_t s);

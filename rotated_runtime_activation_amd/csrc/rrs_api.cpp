@@ -5,6 +5,8 @@
 #include "rrs.h"
 #include "rrs_internal.h"
 
+#include <algorithm>
+
 #define RRS_API extern "C" __attribute__((visibility("default")))
 
 namespace {
@@ -168,6 +170,13 @@ int frontend_impl(const void* X_fp16, int M, int K, int G, const int32_t* perm, 
                                          dx, S, static_cast<uint32_t*>(ws), flags, s, zrows));
 }
 
+// Largest weight stream the front end prefetches (a quarter of MI355X's
+// 256 MB memory-side cache).
+constexpr size_t kPrefetchMaxBytes = size_t(64) << 20;
+#ifndef PF_KEEP4
+#define PF_KEEP4 3
+#endif
+
 int linear_impl(const void* X_fp16, int M, int K, int N, int G, const int32_t* perm, const uint32_t* dsign,
                 int flags, const void* wq, float* Y, void* ws, size_t ws_bytes, hipStream_t s) {
   if (M < 0 || N < 1 || !valid_K(K) || !valid_G(G, K)) return RRS_EINVAL;
@@ -185,10 +194,18 @@ int linear_impl(const void* X_fp16, int M, int K, int N, int G, const int32_t* p
   float* S = reinterpret_cast<float*>(base + l.S);
   float* zrows = l.rows_bytes ? reinterpret_cast<float*>(base + l.rows) : nullptr;
   uint32_t* sync = reinterpret_cast<uint32_t*>(base + l.sync);
-  hipError_t e = rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, K, G, perm, dsign, xq, dx,
-                                      S, sync, flags, s, zrows);
-  if (e != hipSuccess) return RRS_EHIP;
   const uint8_t* codes = static_cast<const uint8_t*>(wq);
+  // the few-token GEMM streams the weights once: the front end's idle
+  // compute units bring them into the memory-side cache meanwhile
+  const size_t wbytes = rrs::codes_bytes(static_cast<size_t>(N), K);
+  const bool pf = rrs::gemm_small_applies(M, K, N, G) && wbytes <= kPrefetchMaxBytes;
+  // the GEMM's waves each stream a run of K / waves codes of a row pair (K / waves
+  // bytes of the stored layout) from its start: the first rounds of every run
+  const int period = pf ? K / rrs::small_waves(K) : 0;
+  const int keep = pf ? std::max(128, period * PF_KEEP4 / 4 / 128 * 128) : 0;
+  hipError_t e = rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, K, G, perm, dsign, xq, dx,
+                                      S, sync, flags, s, zrows, pf ? codes : nullptr, pf ? wbytes : 0, period, keep);
+  if (e != hipSuccess) return RRS_EHIP;
   const float* dw = reinterpret_cast<const float*>(codes + align256(rrs::codes_bytes(static_cast<size_t>(N), K)));
   // the GEMM reads the workspace's error word: a front end whose grid-wide
   // wait gave up (now or in an earlier call on this workspace) makes Y NaN

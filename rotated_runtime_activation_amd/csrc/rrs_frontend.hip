@@ -79,6 +79,12 @@ struct FeArgs {
   uint32_t* colmax;     // [K] (calibration)
   const uint8_t* dsign; // signed rotation: K-bit mask, bit j set -> channel j negated (nullptr: none)
   uint32_t spin_limit;  // polls before the one-launch wait gives up (0: after the first)
+  const uint4* pf;      // one-row-per-workgroup launch: memory for the extra workgroups to read
+  size_t pf_words;      // its 16-byte words
+  int pf_period;        // ... read as the first pf_keep words of every pf_period
+  int pf_keep;
+  int pf_wg;            // extra workgroups (blockIdx.x >= rows)
+  uint32_t* pf_sink;    // nullptr: keeps the reads from being dropped, never written
 };
 
 __device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
@@ -946,6 +952,40 @@ constexpr int row_threads() {
 // rowsplit_kernel modes: the one-launch front end (one row per workgroup,
 // grid-wide wait), and the stats and quantise passes of the three launches
 // (rows looped over the grid).
+#ifndef PF_UNROLL
+#define PF_UNROLL 24
+#endif
+#ifndef PF_DELAY
+#define PF_DELAY 1
+#endif
+// Workgroup `wg` of `nwg` reads its contiguous share of the first `keep`
+// 16-byte words of every `period` words of p[0, words) once, all of a
+// thread's loads in flight together (one batch when the share is at most
+// kU words per thread). The values only feed an XOR that is stored when
+// `sink` is set (never): the reads exist to bring the memory into the
+// memory-side cache for the kernel that follows.
+__device__ __forceinline__ void prefetch_share(const uint4* p, size_t words, int period, int keep, int wg, int nwg,
+                                               int tid, int T, uint32_t* sink) {
+  constexpr int kU = PF_UNROLL;
+  for (int d = 0; d < PF_DELAY; ++d) __builtin_amdgcn_s_sleep(32);
+  const size_t kept = words / period * keep;
+  const size_t per = (kept + nwg - 1) / nwg;
+  const size_t b = static_cast<size_t>(wg) * per;
+  const size_t e = min(kept, b + per);
+  uint32_t x = 0u;
+  for (size_t i = b + tid; i < e; i += static_cast<size_t>(T) * kU) {
+    uint4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const size_t j = i + static_cast<size_t>(u) * T;
+      v[u] = j < e ? p[j / keep * period + j % keep] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (sink) sink[tid] = x;
+}
+
 enum RowMode { kRowOne = 0, kRowStats = 1, kRowQuant = 2 };
 
 __device__ __forceinline__ constexpr int rowpad(int f) { return f + 4 * (f >> 6); }
@@ -981,6 +1021,11 @@ __global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a
   __shared__ float s_red[T / 64];
 
   const int tid = threadIdx.x;
+  if (RM == kRowOne && static_cast<int>(blockIdx.x) >= a.rows) {  // a prefetch workgroup
+    prefetch_share(a.pf, a.pf_words, a.pf_period, a.pf_keep, static_cast<int>(blockIdx.x) - a.rows, a.pf_wg, tid, T,
+                   a.pf_sink);
+    return;
+  }
   const int lane = tid & 63;
   const int ngroups = K >> a.log2G;
   const int G = 1 << a.log2G;
@@ -1092,7 +1137,7 @@ __global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a
     __syncthreads();
     {
       constexpr int kBatch = 8;
-      const int n = static_cast<int>(gridDim.x) * ngroups;
+      const int n = a.rows * ngroups;  // the row workgroups (prefetch ones publish nothing)
       for (int base = tid; base < n; base += T * kBatch) {
         uint64_t b[kBatch];
         uint32_t it = 0;
@@ -1285,9 +1330,17 @@ bool rowsplit_applies(int log2K, bool rotate, int rows) {
   return false;
 }
 
+// Extra workgroups of a one-row-per-workgroup launch that prefetch: the
+// compute units the rows leave idle (0: fewer than 64).
+int prefetch_workgroups(int rows) {
+  const int idle = device_cus() - rows;
+  return idle >= 64 ? idle : 0;
+}
+
 template <int LOG2K, bool ROTATE>
 hipError_t launch_rowsplit(const FeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((rowsplit_kernel<LOG2K, ROTATE, kRowOne>), dim3(a.rows), dim3(row_threads<LOG2K>()), 0, s, a);
+  const int grid = a.rows + (a.pf ? a.pf_wg : 0);
+  hipLaunchKernelGGL((rowsplit_kernel<LOG2K, ROTATE, kRowOne>), dim3(grid), dim3(row_threads<LOG2K>()), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1341,7 +1394,8 @@ hipError_t launch_group_max(const uint32_t* part, int nrows, int ngroups, float*
 
 hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t* perm,
                            const uint32_t* dsign, uint8_t* xq, float* dx, float* S_out, uint32_t* sync,
-                           int flags, hipStream_t s, float* zrows) {
+                           int flags, hipStream_t s, float* zrows, const void* prefetch, size_t prefetch_bytes,
+                           int prefetch_period, int prefetch_keep) {
   if (K & (K - 1)) return launch_frontend_kron(X, M, K, G, perm, dsign, xq, dx, S_out, sync, flags, s, zrows);
   const int log2K = __builtin_ctz(static_cast<unsigned>(K));
   FeArgs a{};
@@ -1359,7 +1413,22 @@ hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t
   const bool rotate = !(flags & 1);
   hipError_t e = hipSuccess;
   // few tokens at K = 4096 / 8192: one row per workgroup, one launch
-  if (!(flags & 4) && rowsplit_applies(log2K, rotate, M)) return rowsplit_k(log2K, rotate, a, s);
+  if (!(flags & 4) && rowsplit_applies(log2K, rotate, M)) {
+    if (prefetch && prefetch_period >= 16 && prefetch_period % 16 == 0 && prefetch_keep >= 16 &&
+        prefetch_keep % 16 == 0 && prefetch_keep <= prefetch_period && prefetch_bytes >= size_t(prefetch_period)) {
+      a.pf = static_cast<const uint4*>(prefetch);
+      a.pf_words = prefetch_bytes / 16;
+      a.pf_period = prefetch_period / 16;
+      a.pf_keep = prefetch_keep / 16;
+      a.pf_wg = prefetch_workgroups(M);
+      // only where one batch of loads per thread covers it: a longer
+      // prefetch would outlast the rows and delay the kernel that follows
+      const int threads = log2K >= 12 ? kRowThreads : (1 << log2K) / 8;
+      const size_t kept = a.pf_words / a.pf_period * a.pf_keep;
+      if (a.pf_wg == 0 || kept > static_cast<size_t>(a.pf_wg) * threads * PF_UNROLL) a.pf = nullptr;
+    }
+    return rowsplit_k(log2K, rotate, a, s);
+  }
   if (a.smooth) {
     // one launch when every workgroup fits on the device at once
     if (!(flags & 4) && (rotate ? fused_k<true>(log2K, a, s, &e) : fused_k<false>(log2K, a, s, &e))) return e;

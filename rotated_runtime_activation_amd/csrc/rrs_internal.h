@@ -71,9 +71,24 @@ __host__ __device__ inline size_t codes_offset(size_t r, size_t b, size_t rs) {
 //          or nullptr.
 //   kFlagGiveUp (bit3): the one-launch forms' wait gives up at once (tests
 //          of the failure path; every kernel still ends normally).
+//   prefetch / prefetch_bytes: device memory the caller reads next (the
+//          layer's weight codes); where the front end leaves most of the
+//          device idle (the one-row-per-workgroup form) extra workgroups of
+//          the same launch read the first prefetch_keep bytes of every
+//          prefetch_period bytes of it once (both multiples of 16), so that
+//          they sit in the memory-side cache when the next kernel starts.
+//          nullptr: none.
 hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t* perm,
                            const uint32_t* dsign, uint8_t* xq, float* dx, float* S_out, uint32_t* sync,
-                           int flags, hipStream_t s, float* zrows = nullptr);
+                           int flags, hipStream_t s, float* zrows = nullptr, const void* prefetch = nullptr,
+                           size_t prefetch_bytes = 0, int prefetch_period = 0, int prefetch_keep = 0);
+
+// Compute units of the current device (cached per device).
+int device_cus();
+
+// Waves per workgroup of the few-token GEMM at K (0: not served); each wave
+// runs K / waves consecutive codes of every row.
+int small_waves(int K);
 
 // Launches the front end would use for M rows on the current device (1 or
 // 3), -1 for an unsupported K.

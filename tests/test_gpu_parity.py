@@ -332,6 +332,40 @@ def test_determinism():
     assert torch.equal(xq1, rra.workspace_views(ws, M, K, G)[0])
 
 
+@pytest.mark.parametrize("M,K,N,G", [(64, 8192, 8192, 128), (1, 8192, 4096, 32), (16, 4096, 4096, 128),
+                                     (100, 2048, 4096, 64), (192, 8192, 8192, 128), (200, 1024, 2048, 128)])
+def test_linear_prefetch_same_bits(M, K, N, G):
+    """With few tokens rrs_linear's front end launches extra workgroups that
+    read the weight codes ahead of the GEMM (where enough compute units are
+    idle; at M = 192, K = N = 8192 it does not). The layer's outputs must be
+    the bits of rrs_frontend followed by rrs_gemm, which never prefetch,
+    and the grid-wide wait must not give up."""
+    gu.log(f"[linear prefetch] M={M} K={K} N={N} G={G}")
+    x, w, perm = _case(M, K, N)
+    wq = gu.prepare_weights(w, perm)
+    X, P = gu.to_dev(x), gu.to_dev(perm)
+    ws = torch.zeros(rra.rrs_workspace_bytes(M, K, G), dtype=torch.uint8, device=gu.DEV)
+    rra.rrs_workspace_init(ws)
+    Y1 = torch.empty(M, N, dtype=torch.float32, device=gu.DEV)
+    rra.rrs_linear(X, G, P, wq, Y1, ws)
+    torch.cuda.synchronize()
+    gu.check_sync_block(ws, K, G, calls=1 if rra.rrs_frontend_passes(M, K, 0) == 1 else 0)
+    xq1, dx1, S1 = (t.clone() for t in rra.workspace_regions(ws, M, K, G))
+    sw = torch.zeros(rra.rrs_sync_bytes(K, G), dtype=torch.uint8, device=gu.DEV)
+    rra.rrs_workspace_init(sw)
+    xq2 = gu.xq_empty(M, K)
+    dx2 = torch.empty(M, dtype=torch.float32, device=gu.DEV)
+    S2 = torch.empty(K // G, dtype=torch.float32, device=gu.DEV)
+    rra.rrs_frontend(X, G, P, xq2, dx2, S2, sw)
+    Y2 = torch.empty_like(Y1)
+    rra.rrs_gemm(xq2, dx2, S2, G, wq, Y2)
+    torch.cuda.synchronize()
+    # the codes of the M rows (an odd M leaves the pad row of the last pair unwritten)
+    assert torch.equal(rra.codes_matrix(xq1, M, K), rra.codes_matrix(xq2, M, K))
+    assert torch.equal(dx1, dx2) and torch.equal(S1, S2)
+    assert torch.equal(Y1, Y2)
+
+
 def test_frontend_workspace_reuse_across_sizes():
     """One synchronisation block serves calls of different token counts in a
     row (the one-launch form's grid changes size between calls: rows of
