@@ -173,9 +173,9 @@ int frontend_impl(const void* X_fp16, int M, int K, int G, const int32_t* perm, 
 // Largest weight stream the front end prefetches (a quarter of MI355X's
 // 256 MB memory-side cache).
 constexpr size_t kPrefetchMaxBytes = size_t(64) << 20;
-#ifndef PF_KEEP4
-#define PF_KEEP4 3
-#endif
+// Share of each wave's run of weight codes the front end reads ahead, in
+// quarters (the rounds the GEMM's waves fetch first).
+constexpr int kPrefetchQuarters = 3;
 
 int linear_impl(const void* X_fp16, int M, int K, int N, int G, const int32_t* perm, const uint32_t* dsign,
                 int flags, const void* wq, float* Y, void* ws, size_t ws_bytes, hipStream_t s) {
@@ -202,7 +202,7 @@ int linear_impl(const void* X_fp16, int M, int K, int N, int G, const int32_t* p
   // the GEMM's waves each stream a run of K / waves codes of a row pair (K / waves
   // bytes of the stored layout) from its start: the first rounds of every run
   const int period = pf ? K / rrs::small_waves(K) : 0;
-  const int keep = pf ? std::max(128, period * PF_KEEP4 / 4 / 128 * 128) : 0;
+  const int keep = pf ? std::max(128, period * kPrefetchQuarters / 4 / 128 * 128) : 0;
   hipError_t e = rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, K, G, perm, dsign, xq, dx,
                                       S, sync, flags, s, zrows, pf ? codes : nullptr, pf ? wbytes : 0, period, keep);
   if (e != hipSuccess) return RRS_EHIP;

@@ -952,12 +952,12 @@ constexpr int row_threads() {
 // rowsplit_kernel modes: the one-launch front end (one row per workgroup,
 // grid-wide wait), and the stats and quantise passes of the three launches
 // (rows looped over the grid).
-#ifndef PF_UNROLL
-#define PF_UNROLL 24
-#endif
-#ifndef PF_DELAY
-#define PF_DELAY 1
-#endif
+// Weight read-ahead: loads a thread keeps in flight (its whole share in one
+// batch), and how long a prefetch workgroup sleeps first (s_sleep 32 is
+// about 2048 cycles, 0.85 us at 2.4 GHz) so that the rows' own loads go
+// out ahead of it.
+constexpr int kPrefetchLoads = 24;
+constexpr int kPrefetchSleeps = 1;
 // Workgroup `wg` of `nwg` reads its contiguous share of the first `keep`
 // 16-byte words of every `period` words of p[0, words) once, all of a
 // thread's loads in flight together (one batch when the share is at most
@@ -966,8 +966,8 @@ constexpr int row_threads() {
 // memory-side cache for the kernel that follows.
 __device__ __forceinline__ void prefetch_share(const uint4* p, size_t words, int period, int keep, int wg, int nwg,
                                                int tid, int T, uint32_t* sink) {
-  constexpr int kU = PF_UNROLL;
-  for (int d = 0; d < PF_DELAY; ++d) __builtin_amdgcn_s_sleep(32);
+  constexpr int kU = kPrefetchLoads;
+  for (int d = 0; d < kPrefetchSleeps; ++d) __builtin_amdgcn_s_sleep(32);
   const size_t kept = words / period * keep;
   const size_t per = (kept + nwg - 1) / nwg;
   const size_t b = static_cast<size_t>(wg) * per;
@@ -1425,7 +1425,7 @@ hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t
       // prefetch would outlast the rows and delay the kernel that follows
       const int threads = log2K >= 12 ? kRowThreads : (1 << log2K) / 8;
       const size_t kept = a.pf_words / a.pf_period * a.pf_keep;
-      if (a.pf_wg == 0 || kept > static_cast<size_t>(a.pf_wg) * threads * PF_UNROLL) a.pf = nullptr;
+      if (a.pf_wg == 0 || kept > static_cast<size_t>(a.pf_wg) * threads * kPrefetchLoads) a.pf = nullptr;
     }
     return rowsplit_k(log2K, rotate, a, s);
   }

@@ -132,3 +132,34 @@ def test_linear_signed(M, K, N, G):
     gu.compare_codes(qw_gpu, ref["wp"]["qw"], ref["wp"]["uw"], "signed weight codes")
     gu.check_linear_two_way(Y.cpu().numpy(), ref, q_gpu, qw_gpu, dx.cpu().numpy(), S.cpu().numpy(),
                             dw.cpu().numpy(), G, "signed linear")
+
+
+@pytest.mark.parametrize("M,K,N,G", [(64, 8192, 4096, 128), (7, 4096, 4096, 64)])
+def test_linear_signed_prefetch_same_bits(M, K, N, G):
+    """The signed layer with few tokens (its front end reads the weight codes
+    ahead of the GEMM) gives the bits of rrs_frontend_signed followed by
+    rrs_gemm."""
+    gu.log(f"[signed linear prefetch] M={M} K={K} N={N} G={G}")
+    x, w, perm, bits, _ = _case(M, K, N)
+    X, P, db = gu.to_dev(x), gu.to_dev(perm), _dev_bits(bits)
+    wq = torch.empty(rra.rrs_weight_bytes(K, N), dtype=torch.uint8, device=gu.DEV)
+    rra.rrs_prepare_weights_signed(gu.to_dev(w), P, db, wq)
+    ws = torch.zeros(rra.rrs_workspace_bytes(M, K, G), dtype=torch.uint8, device=gu.DEV)
+    rra.rrs_workspace_init(ws)
+    Y1 = torch.empty(M, N, dtype=torch.float32, device=gu.DEV)
+    rra.rrs_linear_signed(X, G, P, db, wq, Y1, ws)
+    torch.cuda.synchronize()
+    gu.check_sync_block(ws, K, G, calls=1)
+    xq1, dx1, S1 = (t.clone() for t in rra.workspace_regions(ws, M, K, G))
+    sw = torch.zeros(rra.rrs_sync_bytes(K, G), dtype=torch.uint8, device=gu.DEV)
+    rra.rrs_workspace_init(sw)
+    xq2 = gu.xq_empty(M, K)
+    dx2 = torch.empty(M, dtype=torch.float32, device=gu.DEV)
+    S2 = torch.empty(K // G, dtype=torch.float32, device=gu.DEV)
+    rra.rrs_frontend_signed(X, G, P, db, xq2, dx2, S2, sw)
+    Y2 = torch.empty_like(Y1)
+    rra.rrs_gemm(xq2, dx2, S2, G, wq, Y2)
+    torch.cuda.synchronize()
+    assert torch.equal(rra.codes_matrix(xq1, M, K), rra.codes_matrix(xq2, M, K))
+    assert torch.equal(dx1, dx2) and torch.equal(S1, S2)
+    assert torch.equal(Y1, Y2)
