@@ -32,9 +32,11 @@
 // quantised. The one-launch form (fused_kernel) keeps each wave's rotated,
 // reordered rows in registers across one grid-wide wait on the group
 // maxima, so X is read from memory once; it is used whenever all its
-// workgroups fit on the device together. For few tokens at K = 4096 and
+// workgroups fit on the device together. For few tokens at K = 1024 ..
 // 8192 (up to 256 rows) rowsplit_kernel gives each row a whole workgroup
-// instead (one launch as well). Otherwise a stats launch (per-workgroup
+// instead (one launch as well); called from rrs_linear its launch can also
+// carry workgroups that read the GEMM's weight codes ahead, on the compute
+// units the rows leave idle. Otherwise a stats launch (per-workgroup
 // maxima rows), a reduce launch and a quantise launch; the stats and
 // quantise launches each rotate the rows (X is read twice).
 
@@ -949,9 +951,6 @@ template <int LOG2K>
 constexpr int row_threads() {
   return LOG2K >= 12 ? kRowThreads : (1 << LOG2K) / 8;
 }
-// rowsplit_kernel modes: the one-launch front end (one row per workgroup,
-// grid-wide wait), and the stats and quantise passes of the three launches
-// (rows looped over the grid).
 // Weight read-ahead: loads a thread keeps in flight (its whole share in one
 // batch), and how long a prefetch workgroup sleeps first (s_sleep 32 is
 // about 2048 cycles, 0.85 us at 2.4 GHz) so that the rows' own loads go
@@ -961,7 +960,7 @@ constexpr int kPrefetchSleeps = 1;
 // Workgroup `wg` of `nwg` reads its contiguous share of the first `keep`
 // 16-byte words of every `period` words of p[0, words) once, all of a
 // thread's loads in flight together (one batch when the share is at most
-// kU words per thread). The values only feed an XOR that is stored when
+// kPrefetchLoads words per thread). The values only feed an XOR that is stored when
 // `sink` is set (never): the reads exist to bring the memory into the
 // memory-side cache for the kernel that follows.
 __device__ __forceinline__ void prefetch_share(const uint4* p, size_t words, int period, int keep, int wg, int nwg,
@@ -986,6 +985,9 @@ __device__ __forceinline__ void prefetch_share(const uint4* p, size_t words, int
   if (sink) sink[tid] = x;
 }
 
+// rowsplit_kernel modes: the one-launch front end (one row per workgroup,
+// grid-wide wait), and the stats and quantise passes of the three launches
+// (rows looped over the grid).
 enum RowMode { kRowOne = 0, kRowStats = 1, kRowQuant = 2 };
 
 __device__ __forceinline__ constexpr int rowpad(int f) { return f + 4 * (f >> 6); }
