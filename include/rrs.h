@@ -175,11 +175,12 @@ int rrs_prepare_weights_ex(const void* W_fp16, int K, int N,
  * `ws` holds rrs_workspace_bytes(M, K, G) bytes, initialised once with
  * rrs_workspace_init. Y is fully overwritten. Runs the front end (rotation,
  * reorder, runtime group smoothing, per-token quantise and pack) and the
- * grouped integer GEMM on `s`. With few tokens (the front end's
- * one-row-per-workgroup form and the few-token GEMM) the front end's launch
- * also reads most of wq's codes once, on compute units the rows leave idle,
- * so that the GEMM finds them in the memory-side cache; it writes nothing
- * there, and Y is the same bits as rrs_frontend followed by rrs_gemm. */
+ * grouped integer GEMM on `s`. The front end's launch may also read wq's
+ * codes once ahead of the GEMM (most of them with few tokens, on compute
+ * units its rows leave idle; all of them, up to 8 MiB, in its one-launch
+ * form before the tiled GEMM) so that the GEMM finds them in the memory-side
+ * cache; it writes nothing there, and Y is the same bits as rrs_frontend
+ * followed by rrs_gemm. */
 int rrs_linear(const void* X_fp16, int M, int K, int N, int G,
                const int32_t* perm, const void* wq, float* Y, void* ws,
                size_t ws_bytes, hipStream_t s);

@@ -195,14 +195,17 @@ int linear_impl(const void* X_fp16, int M, int K, int N, int G, const int32_t* p
   float* zrows = l.rows_bytes ? reinterpret_cast<float*>(base + l.rows) : nullptr;
   uint32_t* sync = reinterpret_cast<uint32_t*>(base + l.sync);
   const uint8_t* codes = static_cast<const uint8_t*>(wq);
-  // the few-token GEMM streams the weights once: the front end's idle
-  // compute units bring them into the memory-side cache meanwhile
+  // The front end reads the GEMM's weight codes ahead into the memory-side
+  // cache where its launch can (it decides by its form). The few-token GEMM
+  // streams the weights once: its waves each stream a run of K / waves codes
+  // of a row pair (K / waves bytes of the stored layout) from its start, so
+  // the first rounds of every run are read. Before the tiled GEMM, all of
+  // them (period = keep).
   const size_t wbytes = rrs::codes_bytes(static_cast<size_t>(N), K);
-  const bool pf = rrs::gemm_small_applies(M, K, N, G) && wbytes <= kPrefetchMaxBytes;
-  // the GEMM's waves each stream a run of K / waves codes of a row pair (K / waves
-  // bytes of the stored layout) from its start: the first rounds of every run
-  const int period = pf ? K / rrs::small_waves(K) : 0;
-  const int keep = pf ? std::max(128, period * kPrefetchQuarters / 4 / 128 * 128) : 0;
+  const bool small = rrs::gemm_small_applies(M, K, N, G);
+  const bool pf = wbytes <= kPrefetchMaxBytes;
+  const int period = !pf ? 0 : small ? K / rrs::small_waves(K) : 16;
+  const int keep = !pf ? 0 : small ? std::max(128, period * kPrefetchQuarters / 4 / 128 * 128) : 16;
   hipError_t e = rrs::launch_frontend(static_cast<const uint16_t*>(X_fp16), M, K, G, perm, dsign, xq, dx,
                                       S, sync, flags, s, zrows, pf ? codes : nullptr, pf ? wbytes : 0, period, keep);
   if (e != hipSuccess) return RRS_EHIP;

@@ -700,6 +700,10 @@ __global__ void __launch_bounds__(256) group_max_kernel(const uint32_t* part, in
 // update the same word (same-address atomics from every XCD serialise).
 // All workgroups must be resident at once; the launcher checks the grid
 // against the device's occupancy.
+// Weight codes a thread of the one-launch form reads ahead for the tiled
+// GEMM, in 16-byte loads: 256 workgroups of 512 threads cover 8 MiB.
+constexpr int kFusedPrefetchLoads = 4;
+
 template <int LOG2K, bool ROTATE, int R>
 __global__ void __launch_bounds__(Cfg<LOG2K>::kThreads)
 fused_kernel(FeArgs a) {
@@ -734,10 +738,18 @@ fused_kernel(FeArgs a) {
   // see the next call's value
   const uint32_t epoch =
       __hip_atomic_load(&a.sync[kSyncEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-  // a workspace whose wait failed before (error word set until it is
-  // initialised again) holds tags of no use: give up at once
-  const uint32_t spin_limit =
-      __hip_atomic_load(&a.sync[kSyncError], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? 0u : a.spin_limit;
+  // Weight read-ahead (rrs_linear before the tiled GEMM, one block per
+  // wave): this workgroup's share of the weight codes, issued once the row
+  // is rotated (HBM is idle from there to the wait; issued with the row's
+  // own loads they competed with them, 0.7 us slower at M = 2048) and
+  // consumed before the maxima are published, so none of the front end's
+  // other waits includes them; the lines sit in the memory-side cache when
+  // the GEMM starts. The loads are unconditional (without a read-ahead
+  // every thread reads the first 16 bytes of the synchronisation block, and
+  // an index past the end reads the last word): the compiler counts loads
+  // in flight per path, and a conditional load made the waits for the
+  // rows' own loads also wait for the read-ahead.
+  uint4 pfv[kFusedPrefetchLoads];
 
   table_fill<LOG2K, ROTATE>(s_tab, tl, tid);
   for (int g = tid; g < ngroups; g += C::kThreads) s_grp[g] = 0.f;
@@ -758,9 +770,24 @@ fused_kernel(FeArgs a) {
       widen_block<LOG2K>(v[q], w[q]);
       if constexpr (ROTATE) rotate_block<LOG2K>(v[q], wb, lane);
     }
+    if constexpr (R == 1) {
+      const uint4* src = a.pf ? a.pf : reinterpret_cast<const uint4*>(a.sync);
+      const size_t words = a.pf ? a.pf_words : 1;
+      const size_t per = (words + nwg - 1) / nwg;
+      const size_t b = static_cast<size_t>(blockIdx.x) * per;
+#pragma unroll
+      for (int u = 0; u < kFusedPrefetchLoads; ++u)
+        pfv[u] = src[min(b + tid + static_cast<size_t>(u) * C::kThreads, words - 1)];
+    }
     reorder_block<LOG2K>(v[q], wb, s_tab, lane);
     group_max<LOG2K>(v[q], m[q], 1 << a.log2G);
     fold_group_max<LOG2K>(m[q], s_grp, a.log2G, a.rows, row0[q], lane);
+  }
+  if constexpr (R == 1) {  // the read-ahead's values only feed an XOR stored when pf_sink is set (never)
+    uint32_t x = 0u;
+#pragma unroll
+    for (int u = 0; u < kFusedPrefetchLoads; ++u) x ^= pfv[u].x ^ pfv[u].y ^ pfv[u].z ^ pfv[u].w;
+    if (a.pf_sink) a.pf_sink[tid] = x;
   }
   __syncthreads();
 
@@ -783,6 +810,13 @@ fused_kernel(FeArgs a) {
 
   // ---- S_g = max over the workgroups' rows (all loads of a poll in flight) --
   bool gave_up = false;
+  // a workspace whose wait failed before (error word set until it is
+  // initialised again) holds tags of no use: give up at once. Read here,
+  // with the first poll: read at the start, its value (uniform, moved to a
+  // scalar register at once) made the workgroup wait for every load issued
+  // before it, the rows' own included.
+  const uint32_t spin_limit =
+      __hip_atomic_load(&a.sync[kSyncError], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? 0u : a.spin_limit;
   {
     constexpr int kBatch = 16;
     const int n = nwg * ngroups;
@@ -1259,7 +1293,13 @@ bool try_fused(const FeArgs& a, hipStream_t s, hipError_t* err) {
   const int grid = (nblk + C::kWaves * R - 1) / (C::kWaves * R);
   const int cap = fused_capacity<LOG2K, ROTATE, R>();
   if (cap <= 0 || grid > cap || grid > kMaxFusedWG) return false;
-  hipLaunchKernelGGL((fused_kernel<LOG2K, ROTATE, R>), dim3(grid), dim3(C::kThreads), 0, s, a);
+  FeArgs b = a;
+  // the read-ahead rides along only where one batch of loads per thread
+  // covers all of it (and with one block per wave)
+  if (R != 1 || b.pf_period != b.pf_keep ||
+      b.pf_words > static_cast<size_t>(grid) * C::kThreads * kFusedPrefetchLoads)
+    b.pf = nullptr;
+  hipLaunchKernelGGL((fused_kernel<LOG2K, ROTATE, R>), dim3(grid), dim3(C::kThreads), 0, s, b);
   *err = hipGetLastError();
   return true;
 }
@@ -1415,13 +1455,17 @@ hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t
   const bool rotate = !(flags & 1);
   hipError_t e = hipSuccess;
   // few tokens at K = 4096 / 8192: one row per workgroup, one launch
+  const bool pf_ok = prefetch && prefetch_period >= 16 && prefetch_period % 16 == 0 && prefetch_keep >= 16 &&
+                     prefetch_keep % 16 == 0 && prefetch_keep <= prefetch_period &&
+                     prefetch_bytes >= size_t(prefetch_period);
+  if (pf_ok) {
+    a.pf = static_cast<const uint4*>(prefetch);
+    a.pf_words = prefetch_bytes / 16;
+    a.pf_period = prefetch_period / 16;
+    a.pf_keep = prefetch_keep / 16;
+  }
   if (!(flags & 4) && rowsplit_applies(log2K, rotate, M)) {
-    if (prefetch && prefetch_period >= 16 && prefetch_period % 16 == 0 && prefetch_keep >= 16 &&
-        prefetch_keep % 16 == 0 && prefetch_keep <= prefetch_period && prefetch_bytes >= size_t(prefetch_period)) {
-      a.pf = static_cast<const uint4*>(prefetch);
-      a.pf_words = prefetch_bytes / 16;
-      a.pf_period = prefetch_period / 16;
-      a.pf_keep = prefetch_keep / 16;
+    if (pf_ok) {
       a.pf_wg = prefetch_workgroups(M);
       // only where one batch of loads per thread covers it: a longer
       // prefetch would outlast the rows and delay the kernel that follows
@@ -1434,6 +1478,7 @@ hipError_t launch_frontend(const uint16_t* X, int M, int K, int G, const int32_t
   if (a.smooth) {
     // one launch when every workgroup fits on the device at once
     if (!(flags & 4) && (rotate ? fused_k<true>(log2K, a, s, &e) : fused_k<false>(log2K, a, s, &e))) return e;
+    a.pf = nullptr;  // the passes carry no read-ahead
     // else stats, reduce, quantise. The stats rows (one per workgroup) sit
     // in the codes buffer, which the quantise pass overwrites after the
     // reduce has read them: at most pass_grid(log2K, M) rows of K/G words

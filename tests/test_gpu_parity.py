@@ -333,13 +333,16 @@ def test_determinism():
 
 
 @pytest.mark.parametrize("M,K,N,G", [(64, 8192, 8192, 128), (1, 8192, 4096, 32), (16, 4096, 4096, 128),
-                                     (100, 2048, 4096, 64), (192, 8192, 8192, 128), (200, 1024, 2048, 128)])
+                                     (100, 2048, 4096, 64), (192, 8192, 8192, 128), (200, 1024, 2048, 128),
+                                     (2048, 4096, 4096, 128), (700, 1024, 1000, 64), (4096, 4096, 512, 128)])
 def test_linear_prefetch_same_bits(M, K, N, G):
-    """With few tokens rrs_linear's front end launches extra workgroups that
-    read the weight codes ahead of the GEMM (where enough compute units are
-    idle; at M = 192, K = N = 8192 it does not). The layer's outputs must be
-    the bits of rrs_frontend followed by rrs_gemm, which never prefetch,
-    and the grid-wide wait must not give up."""
+    """rrs_linear's front end reads the GEMM's weight codes ahead: with few
+    tokens on extra workgroups where enough compute units are idle (at
+    M = 192, K = N = 8192 it does not), before the tiled GEMM in the
+    one-launch form's own threads (with one block per wave: not at M = 4096,
+    K = 4096). The layer's outputs must be the bits of rrs_frontend followed
+    by rrs_gemm, which never read ahead, and the grid-wide wait must not give
+    up."""
     gu.log(f"[linear prefetch] M={M} K={K} N={N} G={G}")
     x, w, perm = _case(M, K, N)
     wq = gu.prepare_weights(w, perm)
