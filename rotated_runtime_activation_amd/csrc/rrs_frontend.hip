@@ -992,11 +992,15 @@ constexpr int row_threads() {
 constexpr int kPrefetchLoads = 24;
 constexpr int kPrefetchSleeps = 1;
 // Workgroup `wg` of `nwg` reads its contiguous share of the first `keep`
-// 16-byte words of every `period` words of p[0, words) once, all of a
-// thread's loads in flight together (one batch when the share is at most
-// kPrefetchLoads words per thread). The values only feed an XOR that is stored when
-// `sink` is set (never): the reads exist to bring the memory into the
-// memory-side cache for the kernel that follows.
+// 16-byte words of every `period` words of p[0, words) once (one batch of
+// loads per thread when the share is at most kPrefetchLoads words per
+// thread). Each load's address takes a 64-bit division, which spreads a
+// thread's loads over a few microseconds; computed incrementally (one
+// division per thread) they went out back to back and the row workgroups'
+// latency-bound chain queued behind the burst: M = 1, K = N = 8192
+// 16.9 -> 19.0 us, M = 16, K = N = 4096 14.3 -> 16.5 us. The values only
+// feed an XOR that is stored when `sink` is set (never): the reads exist to
+// bring the memory into the memory-side cache for the kernel that follows.
 __device__ __forceinline__ void prefetch_share(const uint4* p, size_t words, int period, int keep, int wg, int nwg,
                                                int tid, int T, uint32_t* sink) {
   constexpr int kU = kPrefetchLoads;
@@ -1077,17 +1081,11 @@ __global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a
     src[4 * c + 2] = rowpad(q.z);
     src[4 * c + 3] = rowpad(q.w);
   }
-  // one launch: one row per workgroup; passes: rows blockIdx.x,
-  // + gridDim.x, ...
-  const uint32_t epoch = (RM == kRowOne && a.smooth)
-                             ? __hip_atomic_load(&a.sync[kSyncEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u
-                             : 0u;
-  // a workspace whose wait failed before gives up at once (as fused_kernel)
-  const uint32_t spin_limit =
-      (RM == kRowOne && a.smooth &&
-       __hip_atomic_load(&a.sync[kSyncError], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-          ? 0u
-          : a.spin_limit;
+  // one launch: one row per workgroup, whose epoch is read after the row's
+  // loads are issued (its value goes to a scalar register at once, and the
+  // wait for it covers every load issued before it); passes: rows
+  // blockIdx.x, + gridDim.x, ...
+  uint32_t epoch = 0u;
   if constexpr (RM == kRowQuant) {
     // S from the reduce launch; without smoothing S = 1 (written here)
     for (int g = tid; g < ngroups; g += T) {
@@ -1115,6 +1113,8 @@ __global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a
       w[i].w ^= ((b & 64u) << 9) | ((b & 128u) << 24);
     }
   }
+  if (RM == kRowOne && a.smooth)
+    epoch = __hip_atomic_load(&a.sync[kSyncEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
 
   // ---- rotate: E-index bits in registers, the other nine bits in LDS
   float v[E];
@@ -1172,6 +1172,10 @@ __global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a
     for (int g = tid; g < ngroups; g += T) s_grp[g] = 0.f;
     __syncthreads();
     {
+      // a workspace whose wait failed before gives up at once (as
+      // fused_kernel; read here with the first poll for the same reason)
+      const uint32_t spin_limit =
+          __hip_atomic_load(&a.sync[kSyncError], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? 0u : a.spin_limit;
       constexpr int kBatch = 8;
       const int n = a.rows * ngroups;  // the row workgroups (prefetch ones publish nothing)
       for (int base = tid; base < n; base += T * kBatch) {
