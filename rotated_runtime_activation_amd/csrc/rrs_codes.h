@@ -14,6 +14,39 @@ namespace {
 // code magnitude (<= 7) the low 3 bits of the result are the magnitude.
 constexpr float kMagic = 12582912.0f;
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over aligned groups of `lanes` lanes (1, 2, 4, ..., 64; the same
+// in every lane, every lane active), left in every lane of its group, for
+// non-negative floats as their bit patterns (whose integer order is the
+// values' order, so an integer maximum gives the bits fmaxf would). Group
+// widths 2 and 4 are quad permutes, 8 and 16 the half-row and row mirrors
+// (once the smaller groups are reduced each pairs a lane with one of the
+// other half of its group), 32 and 64 the gfx950 row swaps: VALU moves,
+// where a lane shuffle is an LDS round trip per level.
+__device__ __forceinline__ uint32_t lanes_max_u32(uint32_t x, int lanes) {
+  if (lanes >= 2) x = max(x, dpp_u32<0xB1>(x));   // quad_perm [1, 0, 3, 2]
+  if (lanes >= 4) x = max(x, dpp_u32<0x4E>(x));   // quad_perm [2, 3, 0, 1]
+  if (lanes >= 8) x = max(x, dpp_u32<0x141>(x));  // row_half_mirror
+  if (lanes >= 16) x = max(x, dpp_u32<0x140>(x)); // row_mirror
+  if (lanes >= 32) {
+    const auto s = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = max(static_cast<uint32_t>(s[0]), static_cast<uint32_t>(s[1]));
+  }
+  if (lanes >= 64) {
+    const auto s = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    x = max(static_cast<uint32_t>(s[0]), static_cast<uint32_t>(s[1]));
+  }
+  return x;
+}
+
+__device__ __forceinline__ float lanes_max(float x, int lanes) {
+  return __uint_as_float(lanes_max_u32(__float_as_uint(x), lanes));
+}
+
 __device__ __forceinline__ float h2f(uint32_t bits16) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
 }

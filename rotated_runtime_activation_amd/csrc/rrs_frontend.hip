@@ -463,9 +463,9 @@ __device__ __forceinline__ void group_max(const float (&v)[Cfg<LOG2K>::kE], floa
       for (int s = 0; s < NS; ++s) m[s] = t[s];
     }
   }
-  for (int d = 1; d * E < G; d <<= 1) {
+  if (G > E) {  // a group spans G / E lanes (at most 64)
 #pragma unroll
-    for (int s = 0; s < NS; ++s) m[s] = fmaxf(m[s], __shfl_xor(m[s], d));
+    for (int s = 0; s < NS; ++s) m[s] = lanes_max(m[s], min(G / E, 64));
   }
 }
 
@@ -501,7 +501,7 @@ __device__ __forceinline__ void quantise_block(const float (&v)[Cfg<LOG2K>::kE],
   float rmax = 0.f;
 #pragma unroll
   for (int s = 0; s < NS; ++s) rmax = fmaxf(rmax, m[s] * inv[s]);
-  for (int d = 1; d * E < K; d <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, d));
+  if (K > E) rmax = lanes_max(rmax, min(K / E, 64));  // a row spans K / E lanes
   const float k7 = rmax > 0.f ? 7.f / rmax : 0.f;
   uint32_t packed[E / 8];
 #pragma unroll
@@ -680,7 +680,7 @@ __global__ void __launch_bounds__(256) group_max_kernel(const uint32_t* part, in
   const int g = blockIdx.x, tid = threadIdx.x;
   uint32_t m = 0u;
   for (int r = tid; r < nrows; r += 256) m = max(m, part[static_cast<size_t>(r) * ngroups + g]);
-  for (int d = 32; d >= 1; d >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), d)));
+  m = lanes_max_u32(m, 64);
   if ((tid & 63) == 0) s_m[tid >> 6] = m;
   __syncthreads();
   if (tid == 0) {
@@ -1150,7 +1150,7 @@ __global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a
   const int g0 = p0 >> a.log2G;
   if (RM == kRowStats || (RM == kRowOne && a.smooth)) {
     float mg = m;
-    for (int d = 1; d * E < G && d < 64; d <<= 1) mg = fmaxf(mg, __shfl_xor(mg, d));
+    if (G > E) mg = lanes_max(mg, min(G / E, 64));
     if ((p0 & (G - 1)) == 0 || (lane == 0)) {
       if (mg > 0.f) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[g0]), __float_as_uint(mg));
     }
@@ -1228,7 +1228,7 @@ __global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a
   // ---- per-token scale (max over the row of |Zp| / S_g), codes, packing
   const float inv = s_grp[g0];
   float rmax = m * inv;
-  for (int d = 1; d < 64; d <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, d));
+  rmax = lanes_max(rmax, 64);
   if (lane == 0) s_red[tid >> 6] = rmax;
   __syncthreads();
   rmax = s_red[0];

@@ -293,7 +293,7 @@ __device__ __forceinline__ void hm_mfma(const uint16_t* x16, float* row, const H
 }
 
 __device__ __forceinline__ float block_max(float v, float* s_red, int tid) {
-  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d));
+  v = lanes_max(v, 64);  // v >= 0
   if ((tid & 63) == 0) s_red[tid >> 6] = v;
   __syncthreads();
   float m = s_red[0];
