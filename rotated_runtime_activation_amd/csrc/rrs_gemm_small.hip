@@ -220,6 +220,9 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
     for (int i = 0; i < kWL; ++i) rw[s][i] = *reinterpret_cast<const v4u*>(wbase + off + woff[i]);
 #pragma unroll
     for (int i = 0; i < kXL; ++i) rx[s][i] = *reinterpret_cast<const v4u*>(xbase + off + xoff[i]);
+    // round s's loads all go out before round s + 1's: loads complete in
+    // order, so interleaved they would hold round s until s + 1 had landed
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (!PARTIALS) {
     const float base = r_err != 0u ? __builtin_nanf("") : a.ybase;
