@@ -262,34 +262,181 @@ __device__ __forceinline__ HmFrag<M> hm_frags(int lane) {
   return h;
 }
 
+// The row as the matrix cores take it. Wave w owns columns
+// w * 32 * CP .. (w + 1) * 32 * CP - 1 (CP = N / 256 columns per lane, at
+// least 1; at N < 256 only N / 32 waves hold columns). Lane l loads, for
+// each 16-deep k-step ks and e = 0 .. 7, the CP adjacent halves
+// x[i][j0 .. j0 + CP - 1], i = 16 ks + 8 (l / 32) + e, j0 = w 32 CP +
+// CP (l % 32): consecutive lanes read consecutive 2 CP-byte pieces of a run
+// (whole lines for CP >= 2), and no fp16 copy of the row goes through LDS.
+// Tile c (c < CP) of the wave is the 32 columns j0 + c of its lanes: its B
+// operand holds x[i][j0 + c] for the lane's eight i, two halves per dword,
+// put together from the loaded pieces with byte permutes. Rows i >= m read
+// as 0.
 template <int M, int LOG2N>
-__device__ __forceinline__ void hm_mfma(const uint16_t* x16, float* row, const HmFrag<M>& h, int tid) {
-  constexpr int N = 1 << LOG2N;
-  const int lane = tid & 63, wave = tid >> 6;
-  for (int jt = wave; jt < N / 32; jt += kKT / 64) {
-    const int j = jt * 32 + (lane & 31);
+struct HmRow {
+  static constexpr int N = 1 << LOG2N;
+  static constexpr int CP = N >= 1024 ? 4 : N >= 512 ? 2 : 1;
+  static constexpr int CW = CP == 4 ? 2 : 1;   // dwords per loaded piece
+  static constexpr int NW = N / (32 * CP);     // waves that hold columns (<= 8)
+  static constexpr int KS = HmFrag<M>::KS;
+  static_assert(NW >= 1 && NW <= kKT / 64, "columns per wave");
+  uint32_t v[KS][8][CW];
+};
+
+// Column j0 of this lane (first of CP), and whether its wave holds columns.
+template <int M, int LOG2N>
+__device__ __forceinline__ int hm_col(int tid) {
+  using R = HmRow<M, LOG2N>;
+  return (tid >> 6) * 32 * R::CP + R::CP * (tid & 31);
+}
+
+// Element f = i n + j of row `row`, fp16 bits: X [rows][K], or column `row`
+// of W [K][ldw] (weights).
+template <int MODE, int K>
+__device__ __forceinline__ uint32_t load_half(const KronArgs& a, int row, int f) {
+  if constexpr (MODE == kKWeight)
+    return static_cast<uint32_t>(a.src[static_cast<size_t>(f) * a.ldw + row]);
+  else
+    return static_cast<uint32_t>(a.src[static_cast<size_t>(row) * K + f]);
+}
+
+template <int M, int LOG2N, int MODE>
+__device__ __forceinline__ void hm_load(HmRow<M, LOG2N>& r, const KronArgs& a, int row, int tid) {
+  using R = HmRow<M, LOG2N>;
+  constexpr int N = R::N, K = M * N;
+  const int lane = tid & 63;
+  const int j0 = hm_col<M, LOG2N>(tid);
+  const bool cols = (tid >> 6) < R::NW;
+#pragma unroll
+  for (int ks = 0; ks < R::KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = 16 * ks + 8 * (lane >> 5) + e;
+      const int f = i * N + j0;
+      const bool ok = cols && i < M;
+      if constexpr (MODE == kKWeight) {
+        uint32_t h[R::CP];
+#pragma unroll
+        for (int c = 0; c < R::CP; ++c) h[c] = ok ? load_half<MODE, K>(a, row, f + c) : 0u;
+#pragma unroll
+        for (int d = 0; d < R::CW; ++d)
+          r.v[ks][e][d] = R::CP == 1 ? h[0] : (h[2 * d] | (h[2 * d + 1] << 16));
+      } else {
+        const uint16_t* p = a.src + static_cast<size_t>(row) * K + f;
+        if constexpr (R::CP == 1) {
+          r.v[ks][e][0] = ok ? static_cast<uint32_t>(*p) : 0u;
+        } else if constexpr (R::CP == 2) {
+          r.v[ks][e][0] = ok ? *reinterpret_cast<const uint32_t*>(p) : 0u;
+        } else {
+          const uint2 q = ok ? *reinterpret_cast<const uint2*>(p) : make_uint2(0u, 0u);
+          r.v[ks][e][0] = q.x;
+          r.v[ks][e][1] = q.y;
+        }
+      }
+    }
+}
+
+// Sign-mask bits of the lane's loaded elements, bit (ks 8 + e) CP + c for
+// x[i][j0 + c]; at most 32 (KS 8 CP <= 32 for every instantiated m, n).
+template <int M, int LOG2N>
+__device__ __forceinline__ uint32_t hm_sign_bits(const uint8_t* dsign, int tid) {
+  using R = HmRow<M, LOG2N>;
+  static_assert(R::KS * 8 * R::CP <= 32, "sign bits per lane");
+  if (!dsign || (tid >> 6) >= R::NW) return 0u;
+  const int lane = tid & 63;
+  const int j0 = hm_col<M, LOG2N>(tid);
+  uint32_t bits = 0u;
+#pragma unroll
+  for (int ks = 0; ks < R::KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = 16 * ks + 8 * (lane >> 5) + e;
+      if (i < M) {
+#pragma unroll
+        for (int c = 0; c < R::CP; ++c) {
+          const int f = i * R::N + j0 + c;
+          bits |= ((static_cast<uint32_t>(dsign[f >> 3]) >> (f & 7)) & 1u) << ((ks * 8 + e) * R::CP + c);
+        }
+      }
+    }
+  return bits;
+}
+
+// Flip the fp16 sign bits the mask selects (the signed rotation x D).
+template <int M, int LOG2N>
+__device__ __forceinline__ void hm_apply_signs(HmRow<M, LOG2N>& r, uint32_t bits) {
+  using R = HmRow<M, LOG2N>;
+#pragma unroll
+  for (int ks = 0; ks < R::KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t b = bits >> ((ks * 8 + e) * R::CP);
+#pragma unroll
+      for (int d = 0; d < R::CW; ++d) {
+        const uint32_t bd = R::CP == 1 ? (b & 1u) : (b >> (2 * d)) & 3u;
+        r.v[ks][e][d] ^= ((bd & 1u) << 15) | ((bd & 2u) << 30);
+      }
+    }
+}
+
+// H_m on the matrix cores from the loaded pieces: Z1[a][j] = sum_i H_m[i][a]
+// x[i][j], written to the fp32 row buffer (rows a >= m are padding, not
+// written). Products are exact, sums fp32.
+template <int M, int LOG2N>
+__device__ __forceinline__ void hm_mfma(const HmRow<M, LOG2N>& r, float* row, const HmFrag<M>& h, int tid) {
+  using R = HmRow<M, LOG2N>;
+  if ((tid >> 6) >= R::NW) return;  // wave-uniform
+  const int lane = tid & 63;
+  const int j0 = hm_col<M, LOG2N>(tid);
+#pragma unroll
+  for (int c = 0; c < R::CP; ++c) {
     v16f acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < HmFrag<M>::KS; ++ks) {
-      // B[i][j] for i = i0 .. i0 + 7: halves n apart in the natural row
-      // (consecutive lanes read consecutive j); rows i >= m read as 0
-      const int i0 = 16 * ks + 8 * (lane >> 5);
-      uint32_t hv[8];
+    for (int ks = 0; ks < R::KS; ++ks) {
+      // halves (i0 + 2d, i0 + 2d + 1) of column j0 + c: half c % 2 of dword
+      // c / 2 of each piece
+      constexpr uint32_t kSel[2] = {0x05040100u, 0x07060302u};
+      v4u b;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) hv[e] = (i0 + e < M) ? x16[(i0 + e) * N + j] : 0u;
-      const v4u b = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16)};
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t lo = r.v[ks][2 * d][c / 2], hi = r.v[ks][2 * d + 1][c / 2];
+        b[d] = R::CP == 1 ? (lo | (hi << 16)) : __builtin_amdgcn_perm(hi, lo, kSel[c & 1]);
+      }
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, h.a[ks]), __builtin_bit_cast(v8h, b), acc,
                                                    0, 0, 0);
     }
-    // register r of lane l: row a = 8 (r / 4) + 4 (l / 32) + r % 4, column j
+    // register q of lane l: row a = 8 (q / 4) + 4 (l / 32) + q % 4, column j0 + c
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int ar = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (ar < M) row[rpad(ar * N + j)] = acc[r];
+    for (int q = 0; q < 16; ++q) {
+      const int ar = 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+      if (ar < M) row[rpad(ar * R::N + j0 + c)] = acc[q];
     }
   }
+}
+
+// Without the rotation: the loaded elements widened into the row buffer.
+template <int M, int LOG2N>
+__device__ __forceinline__ void hm_store_plain(const HmRow<M, LOG2N>& r, float* row, int tid) {
+  using R = HmRow<M, LOG2N>;
+  if ((tid >> 6) >= R::NW) return;
+  const int lane = tid & 63;
+  const int j0 = hm_col<M, LOG2N>(tid);
+#pragma unroll
+  for (int ks = 0; ks < R::KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = 16 * ks + 8 * (lane >> 5) + e;
+      if (i < M) {
+#pragma unroll
+        for (int c = 0; c < R::CP; ++c) {
+          const uint32_t w = r.v[ks][e][c / 2];
+          row[rpad(i * R::N + j0 + c)] = h2f(R::CP == 1 || (c & 1) == 0 ? (w & 0xffffu) : (w >> 16));
+        }
+      }
+    }
 }
 
 __device__ __forceinline__ float block_max(float v, float* s_red, int tid) {
@@ -303,30 +450,12 @@ __device__ __forceinline__ float block_max(float v, float* s_red, int tid) {
   return m;
 }
 
-// 16-byte chunk c (elements 8c .. 8c+7) of row `row`, fp16 bits
-template <int MODE, int K>
-__device__ __forceinline__ uint4 load_chunk(const KronArgs& a, int row, int c) {
-  if constexpr (MODE == kKWeight) {
-    // column `row` of W [K][ldw], channels 8c .. 8c+7
-    const uint16_t* p = a.src + static_cast<size_t>(8 * c) * a.ldw + row;
-    uint32_t q[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      q[e] = static_cast<uint32_t>(p[(2 * e) * static_cast<size_t>(a.ldw)]) |
-             (static_cast<uint32_t>(p[(2 * e + 1) * static_cast<size_t>(a.ldw)]) << 16);
-    return make_uint4(q[0], q[1], q[2], q[3]);
-  } else {
-    return *reinterpret_cast<const uint4*>(a.src + static_cast<size_t>(row) * K + 8 * c);
-  }
-}
-
 template <int M, int LOG2N, int MODE>
 __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
   constexpr int N = 1 << LOG2N, K = M * N;
   constexpr int W8 = K / 8;                      // 16-byte chunks = packed words (8 positions) per row
   constexpr int SW = (W8 + kKT - 1) / kKT;       // chunks / words per thread
   __shared__ __attribute__((aligned(16))) float s_row[kRowFloats<K>];
-  __shared__ __attribute__((aligned(16))) uint16_t s_x16[K];  // the fp16 row (matrix-core input)
   __shared__ float s_grp[K / 32];                // group maxima, or inverse scales
   __shared__ float s_red[kKT / 64];
   const int tid = threadIdx.x;
@@ -344,13 +473,12 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
   }
 
   // the permutation is the same for every row: its row buffer indices stay
-  // in registers; sign-mask bytes likewise
+  // in registers; the sign bits of the lane's elements likewise
   int pp[SW][8];
-  uint32_t sb[SW];
+  const uint32_t sbits = hm_sign_bits<M, LOG2N>(a.dsign, tid);
 #pragma unroll
   for (int s = 0; s < SW; ++s) {
     const int w = tid + s * kKT;
-    sb[s] = (a.dsign && w < W8) ? static_cast<uint32_t>(a.dsign[w]) : 0u;
     if constexpr (MODE != kKColmax) {
       if (w < W8) {
         const int4 p0 = *reinterpret_cast<const int4*>(a.perm + 8 * w);
@@ -371,53 +499,25 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
     if (__hip_atomic_load(&a.sync[kSyncError], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) spin_limit = 0u;
   }
 
-  // rows blockIdx.x, + gridDim.x, ...: the next row's chunks load while this
+  // rows blockIdx.x, + gridDim.x, ...: the next row's pieces load while this
   // one is processed (one launch: one row per workgroup)
-  uint4 nxt[SW];
-#pragma unroll
-  for (int s = 0; s < SW; ++s) {
-    const int c = tid + s * kKT;
-    if (c < W8 && blockIdx.x < a.rows) nxt[s] = load_chunk<MODE, K>(a, blockIdx.x, c);
-  }
+  HmRow<M, LOG2N> nxt;
+  if (blockIdx.x < a.rows) hm_load<M, LOG2N, MODE>(nxt, a, blockIdx.x, tid);
   for (int row = blockIdx.x; row < a.rows; row += gridDim.x) {
     bool gave_up = false;  // the one-launch wait gave up (the outputs are marked)
-    uint4 cur[SW];
-#pragma unroll
-    for (int s = 0; s < SW; ++s) cur[s] = nxt[s];
+    HmRow<M, LOG2N> cur = nxt;
     const int nrow = row + gridDim.x;
-#pragma unroll
-    for (int s = 0; s < SW; ++s) {
-      const int c = tid + s * kKT;
-      if (c < W8 && nrow < a.rows) nxt[s] = load_chunk<MODE, K>(a, nrow, c);
-    }
-    // ---- signs (fp16 sign bits), then the row into LDS
-#pragma unroll
-    for (int s = 0; s < SW; ++s) {
-      const int c = tid + s * kKT;
-      if (c < W8) {
-        uint4 q = cur[s];
-        const uint32_t b = sb[s];
-        q.x ^= ((b & 1u) << 15) | ((b & 2u) << 30);
-        q.y ^= ((b & 4u) << 13) | ((b & 8u) << 28);
-        q.z ^= ((b & 16u) << 11) | ((b & 32u) << 26);
-        q.w ^= ((b & 64u) << 9) | ((b & 128u) << 24);
-        if (a.rotate) {
-          *reinterpret_cast<uint4*>(s_x16 + 8 * c) = q;
-        } else {
-          const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            s_row[rpad(8 * c + 2 * e)] = h2f(qq[e] & 0xffffu);
-            s_row[rpad(8 * c + 2 * e + 1)] = h2f(qq[e] >> 16);
-          }
-        }
-      }
-    }
-    __syncthreads();
+    if (nrow < a.rows) hm_load<M, LOG2N, MODE>(nxt, a, nrow, tid);
+    // ---- signs (fp16 sign bits), then H_m on the matrix cores into the row
+    // buffer (or the plain row without the rotation)
+    if (a.dsign) hm_apply_signs<M, LOG2N>(cur, sbits);
     if (a.rotate) {
-      hm_mfma<M, LOG2N>(s_x16, s_row, hf, tid);  // H_m across the runs
+      hm_mfma<M, LOG2N>(cur, s_row, hf, tid);  // H_m across the runs
       __syncthreads();
       lds_passes<K, 0, LOG2N>(s_row, tid);       // H_n along each run
+    } else {
+      hm_store_plain<M, LOG2N>(cur, s_row, tid);
+      __syncthreads();
     }
 
     if constexpr (MODE == kKColmax) {
