@@ -208,6 +208,33 @@ __device__ __forceinline__ void lds_pass_vec(float* row, int tid) {
   __syncthreads();
 }
 
+// Passes with B >= 1 whose items are pairs: f bit 0 takes no part, so each
+// thread carries 2 adjacent elements (one 8-byte word) through its R
+// levels, 2^R words 2^B apart (32 floats per item at R = 4).
+template <int K, int B, int R>
+__device__ __forceinline__ void lds_pass_pair(float* row, int tid) {
+  static_assert(B >= 1, "bit 0 stays inside an 8-byte word");
+  constexpr int P = 1 << R;
+  for (int t = tid; t < (K >> (R + 1)); t += kKT) {
+    const int lo = t & ((1 << (B - 1)) - 1), hi = t >> (B - 1);
+    const int base = (hi << (B + R)) | (lo << 1);
+    float2 v[P];
+#pragma unroll
+    for (int u = 0; u < P; ++u) v[u] = *reinterpret_cast<const float2*>(row + rpad(base + (u << B)));
+#pragma unroll
+    for (int h = 1; h < P; h <<= 1)
+#pragma unroll
+      for (int u = 0; u < P; ++u)
+        if (!(u & h)) {
+          bfly(v[u].x, v[u + h].x);
+          bfly(v[u].y, v[u + h].y);
+        }
+#pragma unroll
+    for (int u = 0; u < P; ++u) *reinterpret_cast<float2*>(row + rpad(base + (u << B))) = v[u];
+  }
+  __syncthreads();
+}
+
 template <int K, int B, int LOG2N>
 __device__ __forceinline__ void lds_passes(float* row, int tid) {
   if constexpr (B < LOG2N) {
@@ -389,11 +416,11 @@ __device__ __forceinline__ void hm_mfma(const HmRow<M, LOG2N>& r, float* row, co
   if ((tid >> 6) >= R::NW) return;  // wave-uniform
   const int lane = tid & 63;
   const int j0 = hm_col<M, LOG2N>(tid);
+  v16f acc[R::CP];
 #pragma unroll
   for (int c = 0; c < R::CP; ++c) {
-    v16f acc;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < R::KS; ++ks) {
       // halves (i0 + 2d, i0 + 2d + 1) of column j0 + c: half c % 2 of dword
@@ -405,15 +432,43 @@ __device__ __forceinline__ void hm_mfma(const HmRow<M, LOG2N>& r, float* row, co
         const uint32_t lo = r.v[ks][2 * d][c / 2], hi = r.v[ks][2 * d + 1][c / 2];
         b[d] = R::CP == 1 ? (lo | (hi << 16)) : __builtin_amdgcn_perm(hi, lo, kSel[c & 1]);
       }
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, h.a[ks]), __builtin_bit_cast(v8h, b), acc,
-                                                   0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, h.a[ks]), __builtin_bit_cast(v8h, b),
+                                                      acc[c], 0, 0, 0);
     }
-    // register q of lane l: row a = 8 (q / 4) + 4 (l / 32) + q % 4, column j0 + c
+  }
+  // register q of lane l: row a = 8 (q / 4) + 4 (l / 32) + q % 4, column j0 + c
+  if constexpr (R::CP == 2) {
+    // columns j0 and j0 + 1 (j0 even) differ in f bit 0: H_n's first level
+    // here, and each pair goes to the row buffer as one 8-byte word
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int ar = 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-      if (ar < M) row[rpad(ar * R::N + j0 + c)] = acc[q];
+      float x = acc[0][q], y = acc[1][q];
+      bfly(x, y);
+      if (ar < M) *reinterpret_cast<float2*>(row + rpad(ar * R::N + j0)) = make_float2(x, y);
     }
+  } else {
+#pragma unroll
+    for (int c = 0; c < R::CP; ++c)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int ar = 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        if (ar < M) row[rpad(ar * R::N + j0 + c)] = acc[c][q];
+      }
+  }
+}
+
+// H_n along every run of the row buffer. With two columns per lane (n = 512)
+// its first level ran in hm_mfma; the other eight bits take two radix-16
+// passes over pairs. Otherwise radix-8 passes from bit 0.
+template <int M, int LOG2N>
+__device__ __forceinline__ void hn_passes(float* row, int tid) {
+  constexpr int K = M << LOG2N;
+  if constexpr (HmRow<M, LOG2N>::CP == 2 && LOG2N == 9) {
+    lds_pass_pair<K, 1, 4>(row, tid);
+    lds_pass_pair<K, 5, 4>(row, tid);
+  } else {
+    lds_passes<K, 0, LOG2N>(row, tid);
   }
 }
 
@@ -501,20 +556,29 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
 
   // rows blockIdx.x, + gridDim.x, ...: the next row's pieces load while this
   // one is processed (one launch: one row per workgroup)
+  // (the offline weight preparation reads columns of W in 2-byte loads, one
+  // address each: it loads its row at the top of the loop instead, which
+  // keeps those addresses out of the live set)
+  constexpr bool kAhead = MODE != kKWeight;
   HmRow<M, LOG2N> nxt;
-  if (blockIdx.x < a.rows) hm_load<M, LOG2N, MODE>(nxt, a, blockIdx.x, tid);
+  if (kAhead && blockIdx.x < a.rows) hm_load<M, LOG2N, MODE>(nxt, a, blockIdx.x, tid);
   for (int row = blockIdx.x; row < a.rows; row += gridDim.x) {
     bool gave_up = false;  // the one-launch wait gave up (the outputs are marked)
-    HmRow<M, LOG2N> cur = nxt;
-    const int nrow = row + gridDim.x;
-    if (nrow < a.rows) hm_load<M, LOG2N, MODE>(nxt, a, nrow, tid);
+    HmRow<M, LOG2N> cur;
+    if constexpr (kAhead) {
+      cur = nxt;
+      const int nrow = row + gridDim.x;
+      if (nrow < a.rows) hm_load<M, LOG2N, MODE>(nxt, a, nrow, tid);
+    } else {
+      hm_load<M, LOG2N, MODE>(cur, a, row, tid);
+    }
     // ---- signs (fp16 sign bits), then H_m on the matrix cores into the row
     // buffer (or the plain row without the rotation)
     if (a.dsign) hm_apply_signs<M, LOG2N>(cur, sbits);
     if (a.rotate) {
       hm_mfma<M, LOG2N>(cur, s_row, hf, tid);  // H_m across the runs
       __syncthreads();
-      lds_passes<K, 0, LOG2N>(s_row, tid);       // H_n along each run
+      hn_passes<M, LOG2N>(s_row, tid);           // H_n along each run
     } else {
       hm_store_plain<M, LOG2N>(cur, s_row, tid);
       __syncthreads();
