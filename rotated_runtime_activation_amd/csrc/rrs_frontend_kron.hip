@@ -179,6 +179,29 @@ __device__ __forceinline__ void lds_pass_low3(float* row, int tid) {
   __syncthreads();
 }
 
+// A first pass over f bits 0-3: each thread's 16 elements are consecutive,
+// read and written as four 16-byte words.
+template <int K>
+__device__ __forceinline__ void lds_pass_low4(float* row, int tid) {
+  for (int t = tid; t < K / 16; t += kKT) {
+    float4* p = reinterpret_cast<float4*>(row + rpad(16 * t));
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 w = p[q];
+      v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+    }
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (!(u & h)) bfly(v[u], v[u + h]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) p[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  }
+  __syncthreads();
+}
+
 // Later passes (B >= 2): f bits 0-1 take no part, so each thread carries 4
 // adjacent elements (one 16-byte word) through its R levels, 2^R words
 // 2^B apart.
@@ -447,6 +470,19 @@ __device__ __forceinline__ void hm_mfma(const HmRow<M, LOG2N>& r, float* row, co
       bfly(x, y);
       if (ar < M) *reinterpret_cast<float2*>(row + rpad(ar * R::N + j0)) = make_float2(x, y);
     }
+  } else if constexpr (R::CP == 4) {
+    // columns j0 .. j0 + 3 (j0 a multiple of 4) span f bits 0 and 1: both
+    // levels here, in that order, and each quad goes out as one 16-byte word
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int ar = 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+      float x0 = acc[0][q], x1 = acc[1][q], x2 = acc[2][q], x3 = acc[3][q];
+      bfly(x0, x1);
+      bfly(x2, x3);
+      bfly(x0, x2);
+      bfly(x1, x3);
+      if (ar < M) *reinterpret_cast<float4*>(row + rpad(ar * R::N + j0)) = make_float4(x0, x1, x2, x3);
+    }
   } else {
 #pragma unroll
     for (int c = 0; c < R::CP; ++c)
@@ -458,16 +494,26 @@ __device__ __forceinline__ void hm_mfma(const HmRow<M, LOG2N>& r, float* row, co
   }
 }
 
-// H_n along every run of the row buffer. With two columns per lane (n = 512)
-// its first level ran in hm_mfma; the other eight bits take two radix-16
-// passes over pairs. Otherwise radix-8 passes from bit 0.
+// H_n along every run of the row buffer, levels in the order of the bits.
+// With two or four columns per lane (n = 512, 1024) hm_mfma ran the first
+// one or two levels; the remaining eight bits take two radix-16 passes over
+// pairs. At n = 256 and 128 a radix-16 pass over 16 consecutive elements
+// comes first, then one pass over pairs; n = 64 keeps two radix-8 passes.
 template <int M, int LOG2N>
 __device__ __forceinline__ void hn_passes(float* row, int tid) {
   constexpr int K = M << LOG2N;
-  if constexpr (HmRow<M, LOG2N>::CP == 2 && LOG2N == 9) {
+  constexpr int CP = HmRow<M, LOG2N>::CP;
+  if constexpr (CP == 2 && LOG2N == 9) {
     lds_pass_pair<K, 1, 4>(row, tid);
     lds_pass_pair<K, 5, 4>(row, tid);
+  } else if constexpr (CP == 4 && LOG2N == 10) {
+    lds_pass_pair<K, 2, 4>(row, tid);
+    lds_pass_pair<K, 6, 4>(row, tid);
+  } else if constexpr (CP == 1 && (LOG2N == 8 || LOG2N == 7)) {
+    lds_pass_low4<K>(row, tid);
+    lds_pass_pair<K, 4, LOG2N - 4>(row, tid);
   } else {
+    static_assert(CP == 1, "in-register levels only where the passes above expect them");
     lds_passes<K, 0, LOG2N>(row, tid);
   }
 }
