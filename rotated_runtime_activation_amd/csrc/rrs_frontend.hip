@@ -799,8 +799,17 @@ fused_kernel(FeArgs a) {
   // Every cross-workgroup word is written and read with relaxed agent-scope
   // atomics, which go to the device-coherent level directly (no L2
   // write-back or invalidate, which acquire/release would add per access).
+  // A grid of one workgroup already holds every token's maxima: it skips
+  // the exchange (a round trip) and reads the error word alone; it still
+  // advances the epoch, so the count of one-launch calls stays exact.
+  const bool alone = nwg == 1;
+  bool gave_up = false;
   uint64_t* part = reinterpret_cast<uint64_t*>(a.sync + kSyncPartials);
   const uint64_t tag = static_cast<uint64_t>(epoch) << 32;
+  if (alone) {
+    gave_up = __hip_atomic_load(&a.sync[kSyncError], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
+              a.spin_limit == 0u;
+  } else {
   for (int g = tid; g < ngroups; g += C::kThreads)
     __hip_atomic_store(&part[blockIdx.x * ngroups + g], tag | __float_as_uint(s_grp[g]), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
@@ -809,7 +818,6 @@ fused_kernel(FeArgs a) {
   __syncthreads();
 
   // ---- S_g = max over the workgroups' rows (all loads of a poll in flight) --
-  bool gave_up = false;
   // a workspace whose wait failed before (error word set until it is
   // initialised again) holds tags of no use: give up at once. Read here,
   // with the first poll: read at the start, its value (uniform, moved to a
@@ -852,6 +860,7 @@ fused_kernel(FeArgs a) {
       }
     }
     if (same_group && mx) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[tid % ngroups]), mx);
+  }
   }
   // a workgroup that gave up raises the error word and marks its outputs
   gave_up = __syncthreads_or(gave_up);
@@ -1113,8 +1122,13 @@ __global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a
       w[i].w ^= ((b & 64u) << 9) | ((b & 128u) << 24);
     }
   }
-  if (RM == kRowOne && a.smooth)
+  // (a lone row workgroup, which exchanges nothing, reads the error word
+  // here too: its wait covers the same loads)
+  uint32_t err_alone = 0u;
+  if (RM == kRowOne && a.smooth) {
     epoch = __hip_atomic_load(&a.sync[kSyncEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    if (a.rows == 1) err_alone = __hip_atomic_load(&a.sync[kSyncError], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   // ---- rotate: E-index bits in registers, the other nine bits in LDS
   float v[E];
@@ -1162,9 +1176,16 @@ __global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a
   if (RM == kRowOne && a.smooth) {
     __syncthreads();
 
-    // ---- publish this row's maxima, read every row's (as fused_kernel)
+    // ---- publish this row's maxima, read every row's (as fused_kernel);
+    // the only row workgroup already holds every token's maxima: it skips
+    // the exchange (a round trip) and reads the error word alone; it still
+    // advances the epoch, so the count of one-launch calls stays exact
+    const bool alone = a.rows == 1;
     uint64_t* part = reinterpret_cast<uint64_t*>(a.sync + kSyncPartials);
     const uint64_t tag = static_cast<uint64_t>(epoch) << 32;
+    if (alone) {
+      gave_up = err_alone != 0u || a.spin_limit == 0u;
+    } else {
     for (int g = tid; g < ngroups; g += T)
       __hip_atomic_store(&part[static_cast<size_t>(row) * ngroups + g], tag | __float_as_uint(s_grp[g]),
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1203,6 +1224,7 @@ __global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a
           if (bits) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[(base + k * T) % ngroups]), bits);
         }
       }
+    }
     }
     // a workgroup that gave up raises the error word and marks its outputs
     gave_up = __syncthreads_or(gave_up);

@@ -673,8 +673,16 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
         // epoch (single-copy atomic stores), poll every row until all carry
         // it, reduce them here; the reordered row stays in registers
         __syncthreads();
+        // the only workgroup (one row) already holds every token's maxima:
+        // it skips the exchange (a round trip) (the error word was read at
+        // the start); it still advances the epoch, so the count of
+        // one-launch calls stays exact
+        const bool alone = gridDim.x == 1;
         uint64_t* part = reinterpret_cast<uint64_t*>(a.sync + kSyncPartials);
         const uint64_t tag = static_cast<uint64_t>(epoch) << 32;
+        if (alone) {
+          gave_up = spin_limit == 0u;  // the error word was read at the start
+        } else {
         for (int g = tid; g < ngroups; g += kKT)
           __hip_atomic_store(&part[static_cast<size_t>(row) * ngroups + g], tag | __float_as_uint(s_grp[g]),
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -709,6 +717,7 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
               if (bits) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[(base + k * kKT) % ngroups]), bits);
             }
           }
+        }
         }
         // a workgroup that gave up raises the error word and marks its outputs
         gave_up = __syncthreads_or(gave_up);

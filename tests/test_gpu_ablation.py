@@ -114,8 +114,11 @@ def test_ablation_ex_entry_points_match_plain():
 # ------------------------------------------------------ failure path
 # Shapes taking each one-launch form: one row per workgroup (K = 4096,
 # M <= 256), one row per wave (fused_kernel), and the Kronecker one-launch
-# form (K = 1792, few rows).
-GIVE_UP_CASES = [(64, 4096, 128), (1000, 4096, 128), (40, 1024, 64), (16, 1792, 64)]
+# form (K = 1792, few rows); each also as a grid of a single workgroup,
+# which exchanges no maxima but honours the test flag and the error word
+# the same way (M = 1 at K = 4096 and 1792, M = 16 at K = 256).
+GIVE_UP_CASES = [(64, 4096, 128), (1000, 4096, 128), (40, 1024, 64), (16, 1792, 64),
+                 (1, 4096, 128), (16, 256, 64), (1, 1792, 64)]
 
 
 @pytest.mark.parametrize("M,K,G", GIVE_UP_CASES)
