@@ -10,11 +10,14 @@
 // Sylvester matrices; QuaRot-style rotations use such Kronecker products for
 // hidden sizes like 14336.
 //
-// One workgroup of 512 threads rotates one row at a time in LDS (loading
-// its next row meanwhile): H_m runs first on the matrix cores
-// (fp16 32 x 32 x 16 MFMA against +-1 H_m^T: exact products, fp32 sums),
-// then H_n runs as radix-8 butterfly passes over the fp32 row. The two
-// factors commute (H_m (x) H_n = (H_m (x) I)(I (x) H_n)). Then the row is
+// One workgroup of 512 threads rotates one row at a time (loading its next
+// row meanwhile): H_m runs first on the matrix cores (fp16 32 x 32 x 16
+// MFMA against +-1 H_m^T: exact products, fp32 sums), its operands loaded
+// from memory straight into the matrix-core layout; then H_n runs as
+// butterfly levels, the lowest in registers where a lane holds adjacent
+// columns and the rest as two radix-16 passes over the fp32 row in LDS
+// (two radix-8 passes at n = 64). The two factors commute
+// (H_m (x) H_n = (H_m (x) I)(I (x) H_n)). Then the row is
 // gathered in reordered order through perm, eight positions (one packed
 // word) per thread and step.
 //
