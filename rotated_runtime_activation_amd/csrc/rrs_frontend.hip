@@ -810,57 +810,57 @@ fused_kernel(FeArgs a) {
     gave_up = __hip_atomic_load(&a.sync[kSyncError], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
               a.spin_limit == 0u;
   } else {
-  for (int g = tid; g < ngroups; g += C::kThreads)
-    __hip_atomic_store(&part[blockIdx.x * ngroups + g], tag | __float_as_uint(s_grp[g]), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  for (int g = tid; g < ngroups; g += C::kThreads) s_grp[g] = 0.f;
-  __syncthreads();
+    for (int g = tid; g < ngroups; g += C::kThreads)
+      __hip_atomic_store(&part[blockIdx.x * ngroups + g], tag | __float_as_uint(s_grp[g]), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    for (int g = tid; g < ngroups; g += C::kThreads) s_grp[g] = 0.f;
+    __syncthreads();
 
-  // ---- S_g = max over the workgroups' rows (all loads of a poll in flight) --
-  // a workspace whose wait failed before (error word set until it is
-  // initialised again) holds tags of no use: give up at once. Read here,
-  // with the first poll: read at the start, its value (uniform, moved to a
-  // scalar register at once) made the workgroup wait for every load issued
-  // before it, the rows' own included.
-  const uint32_t spin_limit =
-      __hip_atomic_load(&a.sync[kSyncError], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? 0u : a.spin_limit;
-  {
-    constexpr int kBatch = 16;
-    const int n = nwg * ngroups;
-    const bool same_group = C::kThreads % ngroups == 0;  // thread always on group tid % ngroups
-    uint32_t mx = 0u;
-    for (int base = tid; base < n; base += C::kThreads * kBatch) {
-      uint64_t b[kBatch];
-      uint32_t it = 0;
-      for (;;) {
-#pragma unroll
+    // ---- S_g = max over the workgroups' rows (all loads of a poll in flight) --
+    // a workspace whose wait failed before (error word set until it is
+    // initialised again) holds tags of no use: give up at once. Read here,
+    // with the first poll: read at the start, its value (uniform, moved to a
+    // scalar register at once) made the workgroup wait for every load issued
+    // before it, the rows' own included.
+    const uint32_t spin_limit =
+        __hip_atomic_load(&a.sync[kSyncError], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? 0u : a.spin_limit;
+    {
+      constexpr int kBatch = 16;
+      const int n = nwg * ngroups;
+      const bool same_group = C::kThreads % ngroups == 0;  // thread always on group tid % ngroups
+      uint32_t mx = 0u;
+      for (int base = tid; base < n; base += C::kThreads * kBatch) {
+        uint64_t b[kBatch];
+        uint32_t it = 0;
+        for (;;) {
+  #pragma unroll
+          for (int k = 0; k < kBatch; ++k) {
+            const int idx = base + k * C::kThreads;
+            b[k] = idx < n ? __hip_atomic_load(&part[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag;
+          }
+          bool all = spin_limit > 0;
+  #pragma unroll
+          for (int k = 0; k < kBatch; ++k) all &= (b[k] >> 32) == epoch;
+          if (all) break;
+          if (++it >= spin_limit) {
+            gave_up = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+  #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
-          const int idx = base + k * C::kThreads;
-          b[k] = idx < n ? __hip_atomic_load(&part[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag;
-        }
-        bool all = spin_limit > 0;
-#pragma unroll
-        for (int k = 0; k < kBatch; ++k) all &= (b[k] >> 32) == epoch;
-        if (all) break;
-        if (++it >= spin_limit) {
-          gave_up = true;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        const uint32_t v = static_cast<uint32_t>(b[k]);
-        if (same_group) {
-          mx = max(mx, v);
-        } else if (v) {
-          atomicMax(reinterpret_cast<uint32_t*>(&s_grp[(base + k * C::kThreads) % ngroups]), v);
+          const uint32_t v = static_cast<uint32_t>(b[k]);
+          if (same_group) {
+            mx = max(mx, v);
+          } else if (v) {
+            atomicMax(reinterpret_cast<uint32_t*>(&s_grp[(base + k * C::kThreads) % ngroups]), v);
+          }
         }
       }
+      if (same_group && mx) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[tid % ngroups]), mx);
     }
-    if (same_group && mx) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[tid % ngroups]), mx);
-  }
   }
   // a workgroup that gave up raises the error word and marks its outputs
   gave_up = __syncthreads_or(gave_up);
@@ -1127,7 +1127,8 @@ __global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a
   uint32_t err_alone = 0u;
   if (RM == kRowOne && a.smooth) {
     epoch = __hip_atomic_load(&a.sync[kSyncEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-    if (a.rows == 1) err_alone = __hip_atomic_load(&a.sync[kSyncError], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.rows == 1)
+      err_alone = __hip_atomic_load(&a.sync[kSyncError], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- rotate: E-index bits in registers, the other nine bits in LDS
@@ -1186,45 +1187,45 @@ __global__ void __launch_bounds__(row_threads<LOG2K>()) rowsplit_kernel(FeArgs a
     if (alone) {
       gave_up = err_alone != 0u || a.spin_limit == 0u;
     } else {
-    for (int g = tid; g < ngroups; g += T)
-      __hip_atomic_store(&part[static_cast<size_t>(row) * ngroups + g], tag | __float_as_uint(s_grp[g]),
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    for (int g = tid; g < ngroups; g += T) s_grp[g] = 0.f;
-    __syncthreads();
-    {
-      // a workspace whose wait failed before gives up at once (as
-      // fused_kernel; read here with the first poll for the same reason)
-      const uint32_t spin_limit =
-          __hip_atomic_load(&a.sync[kSyncError], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? 0u : a.spin_limit;
-      constexpr int kBatch = 8;
-      const int n = a.rows * ngroups;  // the row workgroups (prefetch ones publish nothing)
-      for (int base = tid; base < n; base += T * kBatch) {
-        uint64_t b[kBatch];
-        uint32_t it = 0;
-        for (;;) {
-#pragma unroll
+      for (int g = tid; g < ngroups; g += T)
+        __hip_atomic_store(&part[static_cast<size_t>(row) * ngroups + g], tag | __float_as_uint(s_grp[g]),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      for (int g = tid; g < ngroups; g += T) s_grp[g] = 0.f;
+      __syncthreads();
+      {
+        // a workspace whose wait failed before gives up at once (as
+        // fused_kernel; read here with the first poll for the same reason)
+        const uint32_t spin_limit =
+            __hip_atomic_load(&a.sync[kSyncError], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? 0u : a.spin_limit;
+        constexpr int kBatch = 8;
+        const int n = a.rows * ngroups;  // the row workgroups (prefetch ones publish nothing)
+        for (int base = tid; base < n; base += T * kBatch) {
+          uint64_t b[kBatch];
+          uint32_t it = 0;
+          for (;;) {
+  #pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+              const int idx = base + k * T;
+              b[k] = idx < n ? __hip_atomic_load(&part[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag;
+            }
+            bool all = spin_limit > 0;
+  #pragma unroll
+            for (int k = 0; k < kBatch; ++k) all &= (b[k] >> 32) == epoch;
+            if (all) break;
+            if (++it >= spin_limit) {
+              gave_up = true;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+          }
+  #pragma unroll
           for (int k = 0; k < kBatch; ++k) {
-            const int idx = base + k * T;
-            b[k] = idx < n ? __hip_atomic_load(&part[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag;
+            const uint32_t bits = static_cast<uint32_t>(b[k]);
+            if (bits) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[(base + k * T) % ngroups]), bits);
           }
-          bool all = spin_limit > 0;
-#pragma unroll
-          for (int k = 0; k < kBatch; ++k) all &= (b[k] >> 32) == epoch;
-          if (all) break;
-          if (++it >= spin_limit) {
-            gave_up = true;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-        }
-#pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-          const uint32_t bits = static_cast<uint32_t>(b[k]);
-          if (bits) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[(base + k * T) % ngroups]), bits);
         }
       }
-    }
     }
     // a workgroup that gave up raises the error word and marks its outputs
     gave_up = __syncthreads_or(gave_up);

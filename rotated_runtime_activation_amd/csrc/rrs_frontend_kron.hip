@@ -686,41 +686,41 @@ __global__ void __launch_bounds__(kKT) kron_kernel(KronArgs a) {
         if (alone) {
           gave_up = spin_limit == 0u;  // the error word was read at the start
         } else {
-        for (int g = tid; g < ngroups; g += kKT)
-          __hip_atomic_store(&part[static_cast<size_t>(row) * ngroups + g], tag | __float_as_uint(s_grp[g]),
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        for (int g = tid; g < ngroups; g += kKT) s_grp[g] = 0.f;
-        __syncthreads();
-        {
-          constexpr int kBatch = 8;
-          const int n = static_cast<int>(gridDim.x) * ngroups;
-          for (int base = tid; base < n; base += kKT * kBatch) {
-            uint64_t b[kBatch];
-            uint32_t it = 0;
-            for (;;) {
-#pragma unroll
+          for (int g = tid; g < ngroups; g += kKT)
+            __hip_atomic_store(&part[static_cast<size_t>(row) * ngroups + g], tag | __float_as_uint(s_grp[g]),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __syncthreads();
+          for (int g = tid; g < ngroups; g += kKT) s_grp[g] = 0.f;
+          __syncthreads();
+          {
+            constexpr int kBatch = 8;
+            const int n = static_cast<int>(gridDim.x) * ngroups;
+            for (int base = tid; base < n; base += kKT * kBatch) {
+              uint64_t b[kBatch];
+              uint32_t it = 0;
+              for (;;) {
+  #pragma unroll
+                for (int k = 0; k < kBatch; ++k) {
+                  const int idx = base + k * kKT;
+                  b[k] = idx < n ? __hip_atomic_load(&part[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag;
+                }
+                bool all = spin_limit > 0;
+  #pragma unroll
+                for (int k = 0; k < kBatch; ++k) all &= (b[k] >> 32) == epoch;
+                if (all) break;
+                if (++it >= spin_limit) {
+                  gave_up = true;
+                  break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+              }
+  #pragma unroll
               for (int k = 0; k < kBatch; ++k) {
-                const int idx = base + k * kKT;
-                b[k] = idx < n ? __hip_atomic_load(&part[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag;
+                const uint32_t bits = static_cast<uint32_t>(b[k]);
+                if (bits) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[(base + k * kKT) % ngroups]), bits);
               }
-              bool all = spin_limit > 0;
-#pragma unroll
-              for (int k = 0; k < kBatch; ++k) all &= (b[k] >> 32) == epoch;
-              if (all) break;
-              if (++it >= spin_limit) {
-                gave_up = true;
-                break;
-              }
-              __builtin_amdgcn_s_sleep(2);
-            }
-#pragma unroll
-            for (int k = 0; k < kBatch; ++k) {
-              const uint32_t bits = static_cast<uint32_t>(b[k]);
-              if (bits) atomicMax(reinterpret_cast<uint32_t*>(&s_grp[(base + k * kKT) % ngroups]), bits);
             }
           }
-        }
         }
         // a workgroup that gave up raises the error word and marks its outputs
         gave_up = __syncthreads_or(gave_up);
