@@ -25,6 +25,7 @@ def _case(M, K, N=8):
 KRON_FE = [
     (16, 768, 64), (5, 1280, 256), (33, 1792, 128), (7, 3072, 1024), (40, 5120, 32),
     (3, 14336, 128), (130, 14336, 2048), (9, 12288, 4096), (2, 10240, 512), (300, 1536, 64),
+    (300, 12288, 128), (270, 5120, 64),
 ]
 
 
@@ -62,7 +63,7 @@ def test_frontend_kron_signed(M, K, G):
     gu.rel_close(S.cpu().numpy(), fe["S"], gu.SCALE_TOL, "kron signed S")
 
 
-@pytest.mark.parametrize("K,N", [(768, 40), (1792, 7), (14336, 96), (12288, 33)])
+@pytest.mark.parametrize("K,N", [(768, 40), (1792, 7), (14336, 96), (12288, 33), (5120, 24), (1536, 17)])
 def test_prepare_weights_kron(K, N):
     gu.log(f"[weights kron] K={K} N={N}")
     _, w, perm = _case(4, K, N)
@@ -74,7 +75,7 @@ def test_prepare_weights_kron(K, N):
     gu.rel_close(dw.cpu().numpy(), ref["dw"], gu.SCALE_TOL, "kron dw")
 
 
-@pytest.mark.parametrize("T,K", [(64, 768), (200, 14336)])
+@pytest.mark.parametrize("T,K", [(64, 768), (200, 14336), (100, 12288), (50, 3072)])
 def test_calibrate_perm_kron(T, K):
     gu.log(f"[calibrate kron] T={T} K={K}")
     wl = workloads.Workload(40_000 + K, "cal", T, K, 8, (K,), 8, 20.0, "count", 3, 500.0, 0.02, T)
