@@ -45,7 +45,7 @@ def test_frontend_kron_ablations(flags):
 
 
 @pytest.mark.parametrize("M,K,G", [(11, 1792, 64), (6, 14336, 256), (9, 12288, 128), (5, 5120, 64),
-                                   (3, 1536, 32), (300, 14336, 128)])
+                                   (3, 1536, 32), (300, 14336, 128), (1, 14336, 128)])
 def test_frontend_kron_signed(M, K, G):
     gu.log(f"[frontend kron signed] M={M} K={K} G={G}")
     x, _, perm = _case(M, K)
