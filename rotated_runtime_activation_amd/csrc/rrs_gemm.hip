@@ -25,7 +25,10 @@
 // Tiles: 256 output channels x 128 tokens per workgroup, 4 waves of
 // 128 x 64. The MFMA A operand is the weight tile (rows n), the B operand the
 // activation tile (rows t), so runs of four accumulator registers are four
-// consecutive output channels of one token: 16-byte stores.
+// consecutive output channels of one token. A tile inside Y goes out
+// through the idle rings: set 0 writes the finished tile there as token
+// rows, and all eight waves store whole 1-KiB rows of Y (a ragged tile
+// stores its 16-byte runs directly).
 // K advances in stages of 128 codes (64 packed bytes per row): direct
 // global -> LDS loads into 3-slot rings (two stages in flight), then
 // per-wave widening of the packed fragments -> MFMA. Two sets of 4 waves
@@ -292,6 +295,13 @@ struct GemmCtx {
         }
       } else {
         if (gs == 0 && step > st0 * Mm::kSteps) {
+          // the previous k-step's last products were issued just before:
+          // two more issue slots keep the multiplies past their results
+          // (the compiler's own padding can fall one short across the
+          // branch into this block)
+          __builtin_amdgcn_sched_barrier(0);
+          asm volatile("s_nop 1");
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -598,7 +608,11 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
           reinterpret_cast<v4f*>(park_chunk(chunk_of(i, j, q)))[c.lane] = Mma<KM>::quad(c.acc[i][j], q) * m1;
   }
   __syncthreads();
-  if (set == 1) return;
+  // whole tile in range: Y leaves through the idle rings as token rows
+  const bool rings = s_r01 == s_r00 + kStageB && s_r02 == s_r00 + 2 * kStageB && s_r10 == s_r00 + 3 * kStageB &&
+                     s_r11 == s_r00 + 4 * kStageB && s_r12 == s_r00 + 5 * kStageB;  // back to back
+  const bool full = rings && c.t0 + kTT <= a.M && c.n0 + kTN <= a.N && (a.N & 3) == 0;  // uniform
+  if (set == 1 && (PARTIALS || !full)) return;
   const float m0 = one_group ? 1.f : s_end;  // set 0's own last group
   const float fin = one_group ? s_end : 1.f;
   if constexpr (PARTIALS) {
@@ -616,7 +630,52 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
   }
 
   // ---- epilogue: Y[t, n..n+3] = (both halves, absolute) 2^18 / K dx[t] dw[n]
-  const bool full = c.t0 + kTT <= a.M && c.n0 + kTN <= a.N && (a.N & 3) == 0;  // uniform
+  if (full) {
+    // row t of the tile at t * kYRow bytes of the rings (16 bytes of
+    // padding per row: a 16-lane group's rows fall in distinct banks)
+    constexpr int kYRow = kTN * 4 + 16;
+    static_assert(kTT * kYRow <= 6 * kStageB, "Y tile exceeds the rings");
+    uint8_t* yl = s_r00;
+    if (set == 0) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int tl = c.wt * 64 + j * BR + (c.lane % BR);
+          const float rs = fin * s_rs[tl];
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) {
+            const int nl = c.wn * 128 + i * BR + Mma<KM>::qrow(q, c.lane);
+            const v4f dwv = *reinterpret_cast<const v4f*>(s_dw + nl);
+            const v4f v = (Mma<KM>::quad(c.acc[i][j], q) * m0 +
+                           reinterpret_cast<const v4f*>(park_chunk(chunk_of(i, j, q)))[c.lane]) * rs;
+            Mma<KM>::set_quad(c.acc[i][j], q, v * dwv);
+          }
+        }
+    }
+    __syncthreads();  // every parked sum read before the rows overwrite them
+    if (set == 0) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int tl = c.wt * 64 + j * BR + (c.lane % BR);
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) {
+            const int nl = c.wn * 128 + i * BR + Mma<KM>::qrow(q, c.lane);
+            *reinterpret_cast<v4f*>(yl + tl * kYRow + nl * 4) = Mma<KM>::quad(c.acc[i][j], q);
+          }
+        }
+    }
+    __syncthreads();
+    // eight waves, one token row (1 KiB) per store
+    const int gw = set * (kThreads / 64) + wave;
+    for (int r = gw; r < kTT; r += kSets * (kThreads / 64)) {
+      const v4f v = *reinterpret_cast<const v4f*>(yl + r * kYRow + c.lane * 16);
+      *reinterpret_cast<v4f*>(a.Y + static_cast<size_t>(c.t0 + r) * a.N + c.n0 + c.lane * 4) = v;
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
