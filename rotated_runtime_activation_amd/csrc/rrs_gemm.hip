@@ -27,8 +27,8 @@
 // activation tile (rows t), so runs of four accumulator registers are four
 // consecutive output channels of one token. A tile inside Y goes out
 // through the idle rings: set 0 writes the finished tile there as token
-// rows, and all eight waves store whole 1-KiB rows of Y (a ragged tile
-// stores its 16-byte runs directly).
+// rows, and all eight waves store whole 1-KiB rows of Y with streaming
+// (non-temporal) stores (a ragged tile stores its 16-byte runs directly).
 // K advances in stages of 128 codes (64 packed bytes per row): direct
 // global -> LDS loads into 3-slot rings (two stages in flight), then
 // per-wave widening of the packed fragments -> MFMA. Two sets of 4 waves
@@ -670,10 +670,18 @@ __global__ void __launch_bounds__(kThreadsWG) gemm_kernel(GemmArgs a) {
     __syncthreads();
     // eight waves, one token row (1 KiB) per store
     const int gw = set * (kThreads / 64) + wave;
-    for (int r = gw; r < kTT; r += kSets * (kThreads / 64)) {
-      const v4f v = *reinterpret_cast<const v4f*>(yl + r * kYRow + c.lane * 16);
-      *reinterpret_cast<v4f*>(a.Y + static_cast<size_t>(c.t0 + r) * a.N + c.n0 + c.lane * 4) = v;
-    }
+    // all of a wave's rows read first, then stored; the stores stream
+    // (non-temporal): Y is not read back here, and 32 MiB of dirty lines
+    // left in the caches would be written back under the next kernel
+    constexpr int kWaves = kSets * (kThreads / 64);
+    v4f rows[kTT / kWaves];
+#pragma unroll
+    for (int k = 0; k < kTT / kWaves; ++k)
+      rows[k] = *reinterpret_cast<const v4f*>(yl + (gw + k * kWaves) * kYRow + c.lane * 16);
+#pragma unroll
+    for (int k = 0; k < kTT / kWaves; ++k)
+      __builtin_nontemporal_store(rows[k], reinterpret_cast<v4f*>(a.Y + static_cast<size_t>(c.t0 + gw + k * kWaves) * a.N +
+                                                                  c.n0 + c.lane * 4));
     return;
   }
 #pragma unroll
