@@ -69,6 +69,16 @@ struct SmallArgs {
 // a-codes (even) and b-codes (odd) of a packed word as e4m3 subnormals
 __device__ __forceinline__ uint32_t ecodes(uint32_t w) { return w & 0x87878787u; }
 __device__ __forceinline__ uint32_t ocodes(uint32_t w) { return __builtin_amdgcn_alignbit(w, w, 4) & 0x87878787u; }
+// A weight stream much larger than the caches is read once per call: with
+// WSTREAM its loads are non-temporal, so they do not push the activation
+// codes (read by every workgroup of an XCD) out of L2.
+template <bool WSTREAM>
+__device__ __forceinline__ v4u wload(const v4u* p) {
+  if constexpr (WSTREAM)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
 __device__ __forceinline__ v8i widen(v4u w) {
   return v8i{(int)ecodes(w.x), (int)ocodes(w.x), (int)ecodes(w.y), (int)ocodes(w.y),
              (int)ecodes(w.z), (int)ocodes(w.z), (int)ecodes(w.w), (int)ocodes(w.w)};
@@ -118,7 +128,7 @@ __device__ __forceinline__ void dump_piece(const SmallArgs& a, const v16f (&acc)
 // PARTIALS: the same main loop with the accumulators multiplied by 0 where
 // they would be rescaled, and every wave's integer piece of a group added
 // into P where the group (or the wave's run) ends; no Y.
-template <int TJ, int NR, int KS, int WV, bool PARTIALS>
+template <int TJ, int NR, int KS, int WV, bool PARTIALS, bool WSTREAM>
 __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
   constexpr int kWaves = WV, kThreads = WV * 64;
   static_assert(WV <= kMaxWaves && 64 + kTN + 3 * WV <= kThreads, "one thread per scale preloaded");
@@ -217,7 +227,7 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
   for (int s = 0; s < NR; ++s) {
     const int off = min(s, rounds - 1) * kPairRound;
 #pragma unroll
-    for (int i = 0; i < kWL; ++i) rw[s][i] = *reinterpret_cast<const v4u*>(wbase + off + woff[i]);
+    for (int i = 0; i < kWL; ++i) rw[s][i] = wload<WSTREAM>(reinterpret_cast<const v4u*>(wbase + off + woff[i]));
 #pragma unroll
     for (int i = 0; i < kXL; ++i) rx[s][i] = *reinterpret_cast<const v4u*>(xbase + off + xoff[i]);
     // round s's loads all go out before round s + 1's: loads complete in
@@ -273,7 +283,7 @@ __global__ void __launch_bounds__(WV * 64) gemm_small_kernel(SmallArgs a) {
       if (!kPeel || pass == 0) {
         const int off = min(r + NR, rounds - 1) * kPairRound;
 #pragma unroll
-        for (int i = 0; i < kWL; ++i) rw[s][i] = *reinterpret_cast<const v4u*>(wbase + off + woff[i]);
+        for (int i = 0; i < kWL; ++i) rw[s][i] = wload<WSTREAM>(reinterpret_cast<const v4u*>(wbase + off + woff[i]));
 #pragma unroll
         for (int i = 0; i < kXL; ++i) rx[s][i] = *reinterpret_cast<const v4u*>(xbase + off + xoff[i]);
       }
@@ -528,28 +538,36 @@ hipError_t launch_gemm_small(const GemmCall& gc, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const dim3 grid((N + kTN - 1) / kTN, (M + 63) / 64);
+  // one 64-token slice (the weights are read once) and more weight codes than
+  // half the L2s hold (each XCD streams an eighth of them through its 4 MiB)
+  const bool wstream = !partials && grid.y == 1 && static_cast<size_t>(K) * N / 2 > (size_t(16) << 20);
   const int wv = small_waves(K);
   const int rounds = (a.K >> 6) / wv / kRound;  // per wave: 1, 2, 4 for K = 2048, 4096, 8192; 7 for 14336
   const int spg = G >> 6;
   const int ks = G == 32 ? 0 : spg < kRound ? spg : kRound;
   // instantiations: TJ in {1, 2}, NR in {1, 2}, KS in {0 (G = 32), 1, 2, 4},
-  // WV in {4, 5, 6, 7, 8}, each with and without the partials dump
-  auto go2 = [&](auto tj, auto nr, auto w, auto pt) {
+  // WV in {4, 5, 6, 7, 8}, each with and without the partials dump, and
+  // without the dump also with streaming weight loads
+  auto go2 = [&](auto tj, auto nr, auto w, auto pt, auto ws) {
     constexpr int TJ = decltype(tj)::value, NR = decltype(nr)::value, WV = decltype(w)::value;
-    constexpr bool PT = decltype(pt)::value;
+    constexpr bool PT = decltype(pt)::value, WS = decltype(ws)::value;
     const dim3 block(WV * 64);
     switch (ks) {
-      case 0: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 0, WV, PT>), grid, block, 0, s, a); break;
-      case 1: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 1, WV, PT>), grid, block, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 2, WV, PT>), grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, kRound, WV, PT>), grid, block, 0, s, a); break;
+      case 0: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 0, WV, PT, WS>), grid, block, 0, s, a); break;
+      case 1: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 1, WV, PT, WS>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, 2, WV, PT, WS>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((gemm_small_kernel<TJ, NR, kRound, WV, PT, WS>), grid, block, 0, s, a); break;
     }
   };
   auto go = [&](auto tj, auto nr, auto w) {
+    using T = std::integral_constant<bool, true>;
+    using F = std::integral_constant<bool, false>;
     if (partials)
-      go2(tj, nr, w, std::integral_constant<bool, true>{});
+      go2(tj, nr, w, T{}, F{});
+    else if (wstream)
+      go2(tj, nr, w, F{}, T{});
     else
-      go2(tj, nr, w, std::integral_constant<bool, false>{});
+      go2(tj, nr, w, F{}, F{});
   };
   auto by_waves = [&](auto tj, auto nr) {
     switch (wv) {
