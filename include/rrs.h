@@ -285,7 +285,11 @@ int rrs_frontend_passes(int M, int K, int flags);
  * migrated into the weights; RRS rebuttal page, "Novelty": group-wise
  * scales keep the GEMM's tiled scheme). xq (stored layout) and dx fp32 [M]
  * as rrs_frontend writes them, S fp32 [K/G], wq a prepared weight buffer,
- * Y fp32 [M, N] (fully overwritten). */
+ * Y fp32 [M, N] (fully overwritten). The tiled kernel writes the tiles
+ * that lie inside Y with streaming (non-temporal) stores, so Y is not left
+ * in the caches for a consumer that follows; the few-token kernel loads
+ * the weight codes the same way when one 64-token slice streams more than
+ * 16 MiB of them. */
 int rrs_gemm(const uint8_t* xq, const float* dx, const float* S, int M, int K,
              int N, int G, const void* wq, float* Y, hipStream_t s);
 
